@@ -1,0 +1,45 @@
+"""Independent NumPy brute force used to pin the oracle on small inputs.
+
+Written separately from oracle.c on purpose: the blocks are decoded with
+vectorised bit operations and numpy's own binary16 conversion, and products
+are formed as one dense fp64 matrix product (a different summation order
+from the oracle's sequential sums).
+"""
+import numpy as np
+
+
+def dequant(fmt: str, W: np.ndarray, N: int, K: int) -> np.ndarray:
+    """Dense fp64 weights [N][K] from interchange bytes."""
+    nb = K // 32
+    bb = 18 if fmt == "q4_0" else 34
+    blk = np.asarray(W, np.uint8).reshape(N, nb, bb)
+    d = blk[:, :, 0:2].copy().view(np.float16)[:, :, 0].astype(np.float64)  # little endian
+    qs = blk[:, :, 2:]
+    if fmt == "q4_0":
+        codes = np.concatenate([qs & 0x0F, qs >> 4], axis=2).astype(np.int64) - 8
+    else:
+        codes = qs.view(np.int8).astype(np.int64)
+    return (codes * d[:, :, None]).reshape(N, K)
+
+
+def qmv(fmt, W, X, N, K):
+    Wd = dequant(fmt, W, N, K)
+    X64 = np.asarray(X, np.float32).astype(np.float64).reshape(-1, K)
+    Y = X64 @ Wd.T
+    S = np.abs(X64) @ np.abs(Wd).T
+    return Y, S
+
+
+def qmm_isum(Wq8, Xq, N, K):
+    """Exact int64 block sums [M][N][nb] by a dense integer product per block."""
+    nb = K // 32
+    blk = np.asarray(Wq8, np.uint8).reshape(N, nb, 34)
+    qw = blk[:, :, 2:].view(np.int8).astype(np.int64)             # [N][nb][32]
+    qx = np.asarray(Xq, np.int8).astype(np.int64).reshape(-1, nb, 32)  # [M][nb][32]
+    return np.einsum("mbj,nbj->mnb", qx, qw)
+
+
+def q8_scales(Wq8, N, K):
+    nb = K // 32
+    blk = np.asarray(Wq8, np.uint8).reshape(N, nb, 34)
+    return blk[:, :, 0:2].copy().view(np.float16)[:, :, 0].astype(np.float64)

@@ -1,0 +1,367 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-quantized decode weight stream on one MI355X.
+
+One step = one decoded token's pass over a 27B-dense model's GEMV weight stream: 64 layers,
+each q|k|v (7168 x 5120, the three projections stacked since they read the same input),
+o (5120 x 5120), gate|up (34816 x 5120, stacked likewise) and down (5120 x 17408), all
+Q4_0, batch 1, launched in layer order on one stream and replayed as a HIP graph.  Weights
+are seeded N(0, 0.02) draws quantized to Q4_0, inputs N(0, 1), all resident in HBM before
+the timed region.  The headline is achieved HBM GB/s over the algorithmic bytes of the
+stream (packed codes and scales read once, fp32 inputs read, outputs written) and the
+equivalent decode tokens/s (1 / time per pass).
+
+Other workloads (--workload): the single 4096 x 4096 GEMV, the Q8_0 stream at M = 1/4/8,
+the 128-expert MoE layer through qmv_id, and the 512 x 5120 x 17408 prefill GEMM.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+INT8_PEAK_TOPS = 5000.0         # MI355X dense int8 MFMA, published (POP/s = 5.0e15)
+VALU_FP32_PEAK = 157.3         # MI355X fp32 vector TFLOP/s, published (with packed fp32)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="dense27b_q4_0",
+                    choices=["dense27b_q4_0", "dense27b_q8_0", "gemv4096", "moe", "prefill"])
+    ap.add_argument("--M", type=int, default=1, help="batch for dense27b_q8_0 (1, 4 or 8)")
+    ap.add_argument("--layers", type=int, default=64)
+    ap.add_argument("--no-graph", action="store_true", help="eager launches instead of a graph")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# --------------------------------------------------------------------- inputs
+
+def make_matrix(fmt, N, K, key, torch, gen, bqm):
+    """Seeded Gaussian weights -> interchange blocks -> packed layout, all on the GPU."""
+    w = gen.normal((N, K), key, std=0.02, device="cuda")
+    wi = gen.encode_q4_0(w) if fmt == "q4_0" else gen.encode_q8_0(w)
+    del w
+    wp = bqm.repack(fmt, wi.reshape(-1), N, K)
+    return wp
+
+
+def weight_bytes(fmt, N, K):
+    return N * (K // 32) * (18 if fmt == "q4_0" else 34)   # codes + scales, no padding
+
+
+# --------------------------------------------------------------------- timing
+
+def time_steps(run, steps, warmup, torch, use_graph):
+    """Warm up, then time exactly `steps` steps between two synchronizations."""
+    if use_graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            run()                      # eager once (sets kernel attributes)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            run()
+        step = g.replay
+    else:
+        step = run
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps   # ms per step
+
+
+def per_launch_ms(launches, torch, reps=3):
+    """Average duration of each launch, bracketed by events on the stream it runs on."""
+    cur = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in launches]
+    tot = np.zeros(len(launches))
+    for _ in range(reps):
+        for (a, b), fn in zip(ev, launches):
+            a.record(cur)
+            fn()
+            b.record(cur)
+        torch.cuda.synchronize()
+        tot += [a.elapsed_time(b) for a, b in ev]
+    return tot / reps
+
+
+def traffic_from_profiles(kernel_key):
+    """HBM bytes per launch from the committed counter summary, if it was taken on the
+    current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+        ent = d[kernel_key]
+        src = os.path.join(ROOT, "block_quantized_matrix_amd", "csrc", ent["source"])
+        if hashlib.sha256(open(src, "rb").read()).hexdigest() != ent["source_sha256"]:
+            return None
+        return float(ent["hbm_bytes_per_launch"])
+    except Exception:
+        return None
+
+
+# --------------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(fmt, shapes, key_of, seconds, torch, gen, unit="GB/s", M=1):
+    """The oracle (never tuned) on the host cores, on whole layers of the same stream until
+    about `seconds` of work is done; rate in the metric's unit over the same bytes."""
+    import oracle
+    oracle.build(force=False)
+    done_bytes, t_used, layers = 0, 0.0, 0
+    while t_used < seconds and layers < 64:
+        for name, N, K in shapes:
+            wi = (gen.encode_q4_0 if fmt == "q4_0" else gen.encode_q8_0)(
+                gen.normal((N, K), key_of(layers, name), std=0.02, device="cuda"))
+            wh = wi.cpu().numpy()
+            x = gen.normal((M, K), key_of(layers, name) + ("x",), device="cuda").cpu().numpy()
+            t = time.perf_counter()
+            oracle.qmv(fmt, wh, x, N, K)
+            t_used += time.perf_counter() - t
+            done_bytes += weight_bytes(fmt, N, K) + 4 * M * (K + N)
+        layers += 1
+    return {"value": round(done_bytes / t_used / 1e9, 4), "unit": unit, "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"{layers} of the 64 layers ({len(shapes)} GEMVs each), full rows, "
+                      f"{t_used:.1f} s of oracle time"}
+
+
+# --------------------------------------------------------------------- workloads
+
+def run_dense(args, torch, gen, bqm, fmt="q4_0"):
+    M = args.M if fmt == "q8_0" else 1
+    shapes = gen.DENSE27B_FUSED_SHAPES
+    qmv = bqm.qmv_q4_0 if fmt == "q4_0" else bqm.qmv_q8_0
+    say(f"generating {args.layers} layers of {fmt} weights on the GPU ...")
+    t = time.time()
+    mats, xs, ys = [], [], []
+    for l in range(args.layers):
+        for name, N, K in shapes:
+            mats.append((make_matrix(fmt, N, K, ("dense27b", fmt, l, name), torch, gen, bqm), N, K))
+            xs.append(gen.normal((M, K), ("dense27b-x", l, name, M), device="cuda"))
+            ys.append(torch.empty((M, N), device="cuda"))
+    torch.cuda.synchronize()
+    say(f"  done in {time.time() - t:.1f} s; {torch.cuda.memory_allocated() / 2**30:.2f} GiB resident")
+    wbytes = sum(weight_bytes(fmt, N, K) for _, N, K in mats)
+    abytes = sum(4 * M * (K + N) for _, N, K in mats)
+    launches = [(lambda w=w, x=x, y=y, N=N, K=K: qmv(w, x, y, M, N, K))
+                for (w, N, K), x, y in zip(mats, xs, ys)]
+
+    def run():
+        for f in launches:
+            f()
+
+    ms = time_steps(run, args.steps, args.warmup, torch, not args.no_graph)
+    total = wbytes + abytes
+    gbs = total / (ms * 1e-3) / 1e9
+    say(f"step {ms:.3f} ms, {gbs:.1f} GB/s, {1e3 / ms:.1f} passes/s")
+    # eager timing of the same pass, for reference
+    ms_eager = time_steps(run, max(2, args.steps // 4), 1, torch, False) if not args.no_graph else ms
+    # per-launch durations of the dominant kernel (the GEMV; every launch of the step)
+    dur = per_launch_ms(launches, torch)
+    per_bytes = np.array([weight_bytes(fmt, N, K) + 4 * M * (K + N) for _, N, K in mats])
+    achieved = per_bytes.sum() / (dur.sum() * 1e-3) / 1e9
+    by_shape = {}
+    for (name, N, K), i in zip(shapes * args.layers, range(len(mats))):
+        by_shape.setdefault(name, []).append((per_bytes[i], dur[i]))
+    shape_gbs = {k: round(sum(b for b, _ in v) / (sum(d for _, d in v) * 1e-3) / 1e9, 1)
+                 for k, v in by_shape.items()}
+    shape_us = {k: round(1e3 * float(np.mean([d for _, d in v])), 2) for k, v in by_shape.items()}
+    kkey = f"qmv_{fmt}_m{M}_dense27b"
+    traffic = traffic_from_profiles(kkey)
+    res = {
+        "metric": "Q4_0 GEMV achieved HBM GB/s (% of peak) + equiv 27B decode tok/s"
+        if fmt == "q4_0" else f"Q8_0 GEMV (M={M}) achieved HBM GB/s + equiv 27B decode tok/s",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"27B-dense decode weight stream, {fmt.upper()}, batch {M}: "
+                               f"{args.layers} layers x (qkv 7168x5120, o 5120x5120, "
+                               f"gate_up 34816x5120, down 5120x17408)",
+                   "layers": args.layers, "gemv_launches_per_step": len(mats),
+                   "weight_bytes": wbytes, "activation_bytes": abytes, "hip_graph": not args.no_graph},
+        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "equiv_tok_s": round(1e3 / ms * (1 if fmt == "q4_0" else 1), 2),
+        "eager_ms_per_step": round(ms_eager, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": f"k_qmv (Q4_0 M=1)" if fmt == "q4_0" else f"k_qmv (Q8_0 M={M})",
+                     "avg_launch_us": round(1e3 * float(dur.mean()), 3),
+                     "per_shape_gbs": shape_gbs, "per_shape_us": shape_us},
+    }
+    if fmt == "q8_0":
+        res["equiv_tok_s_aggregate"] = round(M * 1e3 / ms, 2)
+    if not args.no_cpu:
+        say("timing the oracle on the host ...")
+        res["cpu_baseline"] = cpu_baseline(fmt, shapes, lambda l, n: ("dense27b", fmt, l, n),
+                                           args.cpu_seconds, torch, gen, M=M)
+    return res
+
+
+def run_gemv4096(args, torch, gen, bqm):
+    N = K = 4096
+    copies = 64   # distinct weight copies (604 MB) so that repeated launches stream HBM
+    mats = [make_matrix("q4_0", N, K, ("gemv4096", c), torch, gen, bqm) for c in range(copies)]
+    x = gen.normal((1, K), ("gemv4096-x", 0), device="cuda")
+    y = torch.empty((1, N), device="cuda")
+    launches = [(lambda w=w: bqm.qmv_q4_0(w, x, y, 1, N, K)) for w in mats]
+
+    def run():
+        for f in launches:
+            f()
+
+    ms = time_steps(run, args.steps, args.warmup, torch, not args.no_graph)
+    per = weight_bytes("q4_0", N, K) + 4 * (N + K)
+    gbs = per * copies / (ms * 1e-3) / 1e9
+    dur = per_launch_ms(launches, torch)
+    return {"metric": "Q4_0 GEMV 4096x4096 sustained GB/s", "value": round(gbs, 2), "unit": "GB/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic",
+            "config": {"workload": "Q4_0 GEMV 4096x4096 batch 1, 64 distinct weight copies per step"},
+            "roofline": {"bound": "hbm", "achieved": round(per / (dur.mean() * 1e-3) / 1e9, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(per / (dur.mean() * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "traffic": traffic_from_profiles("qmv_q4_0_m1_gemv4096"),
+                         "avg_launch_us": round(1e3 * float(dur.mean()), 3)}}
+
+
+def run_moe(args, torch, gen, bqm):
+    sh = gen.MOE_SHAPE
+    E, top_k, H, F = sh["E"], sh["top_k"], sh["hidden"], sh["ffn"]
+    n_layers = 8   # distinct MoE layers (8 x 1.36 GB) cycled so the expert weights stream HBM
+    out = []
+    for T in (1, 16):
+        layers = []
+        for l in range(n_layers):
+            gate = make_matrix("q4_0", E * F, H, ("moe", l, "gate"), torch, gen, bqm)
+            up = make_matrix("q4_0", E * F, H, ("moe", l, "up"), torch, gen, bqm)
+            down = make_matrix("q4_0", E * H, F, ("moe", l, "down"), torch, gen, bqm)
+            ids = torch.from_numpy(gen.router_ids(T, E, top_k, ("moe-ids", l, T))).cuda()
+            x = gen.normal((T, H), ("moe-x", l, T), device="cuda")
+            xd = gen.normal((T, top_k, F), ("moe-xd", l, T), device="cuda")
+            yg = torch.empty((T, top_k, F), device="cuda")
+            yu = torch.empty((T, top_k, F), device="cuda")
+            yd = torch.empty((T, top_k, H), device="cuda")
+            uniq = len(np.unique(ids.cpu().numpy()))
+            layers.append((gate, up, down, ids, x, xd, yg, yu, yd, uniq))
+
+        def run():
+            for gate, up, down, ids, x, xd, yg, yu, yd, _ in layers:
+                bqm.qmv_id("q4_0", gate, E, F, H, ids, T, top_k, x, H, 0, yg)
+                bqm.qmv_id("q4_0", up, E, F, H, ids, T, top_k, x, H, 0, yu)
+                bqm.qmv_id("q4_0", down, E, H, F, ids, T, top_k, xd, top_k * F, F, yd)
+
+        ms = time_steps(run, args.steps, args.warmup, torch, not args.no_graph)
+        per_expert = 3 * weight_bytes("q4_0", F, H)
+        ubytes = sum(L[-1] for L in layers) * per_expert
+        abytes = n_layers * 4 * (2 * T * H + 2 * T * top_k * F + T * top_k * F + T * top_k * H)
+        gbs = (ubytes + abytes) / (ms * 1e-3) / 1e9
+        out.append({"T": T, "ms_per_layer": round(ms / n_layers, 4),
+                    "unique_experts_per_layer": [L[-1] for L in layers],
+                    "gbs_unique_bytes": round(gbs, 1), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+                    "layer_tok_s": round(T * n_layers / (ms * 1e-3), 1)})
+        del layers
+        torch.cuda.empty_cache()
+    return {"metric": "MoE qmv_id achieved HBM GB/s over unique-expert bytes", "value": out[0]["gbs_unique_bytes"],
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": out[0]["ms_per_layer"] * n_layers, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "128-expert MoE layer (gate/up 4096->1536, down 1536->4096, Q4_0, top-8), "
+                                   "8 distinct layers per step"},
+            "by_T": out}
+
+
+def run_prefill(args, torch, gen, bqm):
+    sh = gen.PREFILL_SHAPE
+    M, N, K = sh["M"], sh["N"], sh["K"]
+    copies = 8
+    mats = [make_matrix("q8_0", N, K, ("prefill", c), torch, gen, bqm) for c in range(copies)]
+    X = gen.normal((M, K), ("prefill-x", 0), device="cuda")
+    Xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    dx = torch.empty((M, K // 32), device="cuda")
+    Y = torch.empty((M, N), device="cuda")
+    bqm.bqm_quantize_q8_act(X, Xq, dx, M, K)
+    launches = [(lambda w=w: bqm.qmm_q8_0(w, Xq, dx, Y, M, N, K)) for w in mats]
+    qlaunch = [lambda: bqm.bqm_quantize_q8_act(X, Xq, dx, M, K)]
+
+    def run():
+        bqm.bqm_quantize_q8_act(X, Xq, dx, M, K)
+        for f in launches:
+            f()
+
+    ms = time_steps(run, args.steps, args.warmup, torch, not args.no_graph)
+    dur = per_launch_ms(launches, torch)
+    qdur = per_launch_ms(qlaunch, torch)
+    ops = 2.0 * M * N * K
+    tops = ops / (dur.mean() * 1e-3) / 1e12
+    return {"metric": "prefill qmm_q8_0 int8 TOP/s", "value": round(tops, 2), "unit": "TOP/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8/f32",
+            "data": "synthetic",
+            "config": {"workload": "prefill GEMM M=512 K=5120 N=17408, Q8_0 weights, 8 weight copies"},
+            "roofline": {"bound": "mfma", "achieved": round(tops, 2), "peak": INT8_PEAK_TOPS,
+                         "unit": "TOP/s", "frac": round(tops / INT8_PEAK_TOPS, 4),
+                         "traffic": traffic_from_profiles("qmm_q8_0_prefill"),
+                         "avg_launch_us": round(1e3 * float(dur.mean()), 3)},
+            "quantize_us": round(1e3 * float(qdur.mean()), 3)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU sharding "
+              f"is a design note, not built", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import gen
+    from block_quantized_matrix_amd import bqm
+    bqm.lib()   # fail loudly if the HIP library is missing
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    say(f"device: {torch.cuda.get_device_name(0)}")
+    wl = args.workload
+    if wl == "dense27b_q4_0":
+        res = run_dense(args, torch, gen, bqm, "q4_0")
+    elif wl == "dense27b_q8_0":
+        res = run_dense(args, torch, gen, bqm, "q8_0")
+    elif wl == "gemv4096":
+        res = run_gemv4096(args, torch, gen, bqm)
+    elif wl == "moe":
+        res = run_moe(args, torch, gen, bqm)
+    else:
+        res = run_prefill(args, torch, gen, bqm)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,130 @@
+"""Thin Python binding of libbqm.so (the C ABI in include/bqm.h).
+
+Argument marshalling only: every function passes device pointers (``tensor.data_ptr()``),
+sizes and the current HIP stream of torch to the C entry point of the same name and
+raises ``BqmError`` on a non-zero status.  All computation happens in the HIP kernels;
+there is no fallback of any kind: if the library is missing, importing the functions
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbqm.so")
+
+Q4_0 = 2
+Q8_0 = 8
+FMT = {"q4_0": Q4_0, "q8_0": Q8_0}
+QMV_MAX_M = 8
+QMV_ID_MAX_T = 64
+QMV_ID_MAX_TOPK = 32
+QMV_ID_MAX_E = 4096
+
+_lib = None
+
+
+class BqmError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn}: {strerror(status)} (status {status})")
+        self.status = status
+
+
+def lib():
+    """Load libbqm.so (raises OSError if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise OSError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+        L.bqm_packed_bytes.argtypes = [I, I64, I64]
+        L.bqm_packed_bytes.restype = SZ
+        L.bqm_repack.argtypes = [I, P, P, I64, I64, P]
+        L.bqm_unpack.argtypes = [I, P, P, I64, I64, P]
+        L.qmv_q4_0.argtypes = [P, P, P, I, I64, I64, P]
+        L.qmv_q8_0.argtypes = [P, P, P, I, I64, I64, P]
+        L.qmv_id.argtypes = [I, P, I, I64, I64, P, I, I, P, I64, I64, P, P]
+        L.bqm_quantize_q8_act.argtypes = [P, P, P, I64, I64, P]
+        L.qmm_q8_0.argtypes = [P, P, P, P, I64, I64, I64, P]
+        L.bqm_strerror.argtypes = [I]
+        L.bqm_strerror.restype = ctypes.c_char_p
+        for f in ("bqm_repack", "bqm_unpack", "qmv_q4_0", "qmv_q8_0", "qmv_id",
+                  "bqm_quantize_q8_act", "qmm_q8_0"):
+            getattr(L, f).restype = I
+        _lib = L
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().bqm_strerror(int(status)).decode()
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return ctypes.c_void_p(t)
+    return ctypes.c_void_p(t.data_ptr()) if t.numel() > 0 else ctypes.c_void_p(t.data_ptr() or None)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _call(name, *args):
+    st = getattr(lib(), name)(*args)
+    if st != 0:
+        raise BqmError(name, st)
+
+
+def _fmt(fmt):
+    return FMT[fmt] if isinstance(fmt, str) else int(fmt)
+
+
+def packed_bytes(fmt, rows: int, K: int) -> int:
+    return int(lib().bqm_packed_bytes(_fmt(fmt), rows, K))
+
+
+def bqm_repack(fmt, w_interchange, w_packed, rows: int, K: int, stream=None):
+    _call("bqm_repack", _fmt(fmt), _ptr(w_interchange), _ptr(w_packed), rows, K, _stream(stream))
+
+
+def bqm_unpack(fmt, w_packed, w_interchange, rows: int, K: int, stream=None):
+    _call("bqm_unpack", _fmt(fmt), _ptr(w_packed), _ptr(w_interchange), rows, K, _stream(stream))
+
+
+def qmv_q4_0(w_packed, X, Y, M: int, N: int, K: int, stream=None):
+    _call("qmv_q4_0", _ptr(w_packed), _ptr(X), _ptr(Y), M, N, K, _stream(stream))
+
+
+def qmv_q8_0(w_packed, X, Y, M: int, N: int, K: int, stream=None):
+    _call("qmv_q8_0", _ptr(w_packed), _ptr(X), _ptr(Y), M, N, K, _stream(stream))
+
+
+def qmv_id(fmt, w_packed, E: int, N: int, K: int, ids, T: int, top_k: int, X,
+           x_tok_stride: int, x_slot_stride: int, Y, stream=None):
+    _call("qmv_id", _fmt(fmt), _ptr(w_packed), E, N, K, _ptr(ids), T, top_k, _ptr(X),
+          x_tok_stride, x_slot_stride, _ptr(Y), _stream(stream))
+
+
+def bqm_quantize_q8_act(X, Xq, dx, M: int, K: int, stream=None):
+    _call("bqm_quantize_q8_act", _ptr(X), _ptr(Xq), _ptr(dx), M, K, _stream(stream))
+
+
+def qmm_q8_0(w_packed, Xq, dx, Y, M: int, N: int, K: int, stream=None):
+    _call("qmm_q8_0", _ptr(w_packed), _ptr(Xq), _ptr(dx), _ptr(Y), M, N, K, _stream(stream))
+
+
+# ---- conveniences built only from the calls above (allocation through torch) ----
+
+def repack(fmt, w_interchange: torch.Tensor, rows: int, K: int, stream=None) -> torch.Tensor:
+    """Device interchange bytes -> a new packed uint8 tensor."""
+    out = torch.empty(packed_bytes(fmt, rows, K), dtype=torch.uint8, device=w_interchange.device)
+    bqm_repack(fmt, w_interchange, out, rows, K, stream)
+    return out

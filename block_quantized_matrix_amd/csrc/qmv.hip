@@ -1,0 +1,598 @@
+// Decode GEMV / small-batch GEMV over packed Q4_0 and Q8_0 weights, gfx950.
+//
+// Y[m][n] = sum_k dequant(W)[n][k] * X[m][k]. Decode reads every weight once per token
+// ("V100跑Qwen 27B：量化与KV Cache调优" (lmnt.cn), section 1.2), so the kernels are built
+// around streaming the packed codes from HBM once, at full 16-byte load width, and doing as
+// little VALU work per weight as the format allows.
+//
+// Work mapping.  A row of the matrix is handled by a lane group of G lanes (G = 16, 32 or
+// 64, picked so that K/32 divides evenly where possible); lane g of the group owns blocks
+// g, g+G, g+2G, ... of the row, one whole 32-weight block per 16-byte (Q4_0) or 2x16-byte
+// (Q8_0) load.  A group handles R rows at once, so the activations a lane holds for one
+// block are reused R times.  A 256-thread workgroup therefore covers (256/G)*R rows.
+//
+// Activations.  X is staged once per workgroup into LDS, 128 bytes (one block) per lane
+// read; the eight 16-byte chunks of block b are stored XOR-swizzled by (b & 7) so that
+// eight neighbouring lanes (eight consecutive blocks) hit eight different bank groups.
+// Long rows are staged in chunks of blocks that fit the LDS budget.
+//
+// Arithmetic, M = 1 (the bandwidth-critical case).  A Q4_0 weight is (n - 8) d.  Per
+// block the kernel accumulates sum n_j x_j with v_cvt_f32_ubyte + FMA (the high nibbles
+// are taken in place, as 16 n, and scaled by 1/16 once per block), and then subtracts
+// 8 * sum_j x_j, a per-block sum computed once in LDS in the *same order* as the FMA
+// chains.  Because 8 (and 1/16) are powers of two the subtraction is exact for an all-8
+// block, so neutral codes give exactly zero, as the definition requires.  Q8_0 does the
+// same with the bias 128 (q ^ 0x80 makes the code an unsigned byte q + 128).
+//
+// Arithmetic, M > 1.  Each weight is dequantized once into a register, exactly:
+// fma(n, d, -8d) has at most 4 + 11 significant bits, and then used for M FMAs.
+//
+// Reduction: a butterfly of cross-lane shuffles inside the lane group, then one lane
+// stores the row.  No atomics; the summation order is fixed for a given launch shape.
+#include "bqm_internal.h"
+
+namespace bqm {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kLdsBudget = 80 * 1024;  // bytes of LDS per workgroup (two per CU fit)
+
+__device__ __forceinline__ float h2f(uint32_t bits) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+__device__ __forceinline__ float ub(uint32_t v, int k) {
+  return (float)((v >> (8 * k)) & 0xffu);  // v_cvt_f32_ubyte{k}
+}
+
+enum { FQ4 = 0, FQ8 = 1 };
+
+template <int FMT> struct Codes;
+template <> struct Codes<FQ4> { u32x4 a; };
+template <> struct Codes<FQ8> { u32x4 a, b; };
+
+template <int FMT>
+__device__ __forceinline__ Codes<FMT> load_codes(const uint8_t* __restrict__ codes, size_t blk) {
+  Codes<FMT> c;
+  if constexpr (FMT == FQ4) {
+    c.a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(codes) + blk);
+  } else {
+    const u32x4* p = reinterpret_cast<const u32x4*>(codes) + 2 * blk;
+    c.a = __builtin_nontemporal_load(p);
+    c.b = __builtin_nontemporal_load(p + 1);
+  }
+  return c;
+}
+
+template <int FMT>
+__device__ __forceinline__ Codes<FMT> zero_codes() {
+  Codes<FMT> c;
+  if constexpr (FMT == FQ4) {
+    c.a = u32x4{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
+  } else {
+    c.a = u32x4{0u, 0u, 0u, 0u};
+    c.b = u32x4{0u, 0u, 0u, 0u};
+  }
+  return c;
+}
+
+// Per-block x sum in the order the M = 1 FMA chains use.
+template <int FMT>
+__device__ __forceinline__ float block_xsum(const float4 (&v)[8]) {
+  if constexpr (FMT == FQ4) {
+    float lo = 0.f, hi = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      lo = lo + v[i].x; lo = lo + v[i].y; lo = lo + v[i].z; lo = lo + v[i].w;
+    }
+#pragma unroll
+    for (int i = 4; i < 8; i++) {
+      hi = hi + v[i].x; hi = hi + v[i].y; hi = hi + v[i].z; hi = hi + v[i].w;
+    }
+    return lo + hi;
+  } else {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      s = s + v[i].x; s = s + v[i].y; s = s + v[i].z; s = s + v[i].w;
+    }
+    return s;
+  }
+}
+
+// M = 1: sum_j (w_j / d) x_j for one block, with the offset removed via the block x sum.
+template <int FMT>
+__device__ __forceinline__ float block_dot_m1(const Codes<FMT>& q, const float4 (&x)[8],
+                                              float sx) {
+  if constexpr (FMT == FQ4) {
+    const uint32_t w[4] = {q.a.x, q.a.y, q.a.z, q.a.w};
+    float lo = 0.f, hi = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      const uint32_t l = w[k] & 0x0F0F0F0Fu;
+      lo = fmaf(ub(l, 0), x[k].x, lo); lo = fmaf(ub(l, 1), x[k].y, lo);
+      lo = fmaf(ub(l, 2), x[k].z, lo); lo = fmaf(ub(l, 3), x[k].w, lo);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      const uint32_t h = w[k] & 0xF0F0F0F0u;  // 16 * high nibble, in place
+      hi = fmaf(ub(h, 0), x[k + 4].x, hi); hi = fmaf(ub(h, 1), x[k + 4].y, hi);
+      hi = fmaf(ub(h, 2), x[k + 4].z, hi); hi = fmaf(ub(h, 3), x[k + 4].w, hi);
+    }
+    const float r = fmaf(hi, 0.0625f, lo);
+    return fmaf(-8.0f, sx, r);
+  } else {
+    const uint32_t w[8] = {q.a.x, q.a.y, q.a.z, q.a.w, q.b.x, q.b.y, q.b.z, q.b.w};
+    float a = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      const uint32_t u = w[k] ^ 0x80808080u;  // q + 128 as unsigned bytes
+      a = fmaf(ub(u, 0), x[k].x, a); a = fmaf(ub(u, 1), x[k].y, a);
+      a = fmaf(ub(u, 2), x[k].z, a); a = fmaf(ub(u, 3), x[k].w, a);
+    }
+    return fmaf(-128.0f, sx, a);
+  }
+}
+
+// M > 1: the 32 weights of one block, dequantized exactly.
+template <int FMT>
+__device__ __forceinline__ void block_dequant(const Codes<FMT>& q, uint32_t dbits, float (&w)[32]) {
+  const float d = h2f(dbits);
+  if constexpr (FMT == FQ4) {
+    const float d16 = d * 0.0625f, m8d = -8.0f * d;
+    const uint32_t c[4] = {q.a.x, q.a.y, q.a.z, q.a.w};
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      const uint32_t l = c[k] & 0x0F0F0F0Fu, h = c[k] & 0xF0F0F0F0u;
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        w[4 * k + e] = fmaf(ub(l, e), d, m8d);
+        w[16 + 4 * k + e] = fmaf(ub(h, e), d16, m8d);
+      }
+    }
+  } else {
+    const float m128d = -128.0f * d;
+    const uint32_t c[8] = {q.a.x, q.a.y, q.a.z, q.a.w, q.b.x, q.b.y, q.b.z, q.b.w};
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      const uint32_t u = c[k] ^ 0x80808080u;
+#pragma unroll
+      for (int e = 0; e < 4; e++) w[4 * k + e] = fmaf(ub(u, e), d, m128d);
+    }
+  }
+}
+
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int off = G / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Per-workgroup pointers of the M inputs / outputs of the current tile.  It lives in LDS:
+// the caller's threads 0..7 fill it before tile_qmv, whose first barrier publishes it.
+// Offsets (in floats) rather than pointers, so that every access is derived from a kernel
+// argument and stays a global (not flat) memory access.
+struct TileIO {
+  int64_t x[8];  // X + x[m]: the K inputs of slot m
+  int64_t y[8];  // Y + y[m] + row: output of tile row `row` for slot m
+};
+
+// Rows [row_base, row_base + nrows) of the packed matrix (nrows <= RPW) times M <= MM
+// inputs.  All threads of the workgroup take part.  smem holds M * kcb * 8 float4 of
+// staged x plus kcb floats of block sums.
+template <int FMT, int MM, int G, int R>
+__device__ __forceinline__ void tile_qmv(const uint8_t* __restrict__ codes,
+                                         const uint16_t* __restrict__ scales, int nb,
+                                         int64_t row_base, int nrows, const float* __restrict__ X,
+                                         float* __restrict__ Y, const TileIO* io, int M,
+                                         float4* smem, int kcb) {
+  const int tid = threadIdx.x;
+  const int g = tid % G;
+  const int lr0 = (tid / G) * R;  // first tile row of this lane group
+  float* sxs = reinterpret_cast<float*>(smem + (size_t)M * kcb * 8);
+
+  bool row_ok[R];
+#pragma unroll
+  for (int r = 0; r < R; r++) row_ok[r] = lr0 + r < nrows;
+
+  float acc[R][MM];
+#pragma unroll
+  for (int r = 0; r < R; r++)
+#pragma unroll
+    for (int m = 0; m < MM; m++) acc[r][m] = 0.f;
+
+  for (int c0 = 0; c0 < nb; c0 += kcb) {
+    const int cn = min(kcb, nb - c0);
+    __syncthreads();  // LDS from the previous chunk / tile is no longer read
+    // ---- stage x[:, chunk] into LDS (swizzled), and the block sums for M = 1 ----
+    for (int idx = tid; idx < M * cn; idx += kThreads) {
+      const int m = idx / cn, bl = idx - m * cn;
+      const float4* src = reinterpret_cast<const float4*>(X + io->x[m] + (int64_t)(c0 + bl) * kQK);
+      float4* dst = smem + ((size_t)m * kcb + bl) * 8;
+      const int sw = bl & 7;
+      float4 v[8];
+      if constexpr (MM == 1) {
+#pragma unroll
+        for (int i = 0; i < 8; i++) v[i] = src[i];
+#pragma unroll
+        for (int i = 0; i < 8; i++) dst[i ^ sw] = v[i];
+        sxs[bl] = block_xsum<FMT>(v);
+      } else {
+        // swizzle on the load side: slot i of the LDS block holds chunk i ^ sw
+#pragma unroll
+        for (int i = 0; i < 8; i++) v[i] = src[i ^ sw];
+#pragma unroll
+        for (int i = 0; i < 8; i++) dst[i] = v[i];
+      }
+    }
+    __syncthreads();
+
+    // ---- stream the weights of this chunk ----
+    Codes<FMT> qn[R];
+    uint32_t dn[R];
+    auto issue = [&](int bl) {
+#pragma unroll
+      for (int r = 0; r < R; r++) {
+        if (row_ok[r] && bl < cn) {
+          const size_t blk = (size_t)(row_base + lr0 + r) * nb + (c0 + bl);
+          qn[r] = load_codes<FMT>(codes, blk);
+          dn[r] = scales[blk];
+        } else {
+          qn[r] = zero_codes<FMT>();
+          dn[r] = 0;
+        }
+      }
+    };
+    issue(g);
+    for (int bl = g; bl < cn; bl += G) {
+      Codes<FMT> q[R];
+      uint32_t d[R];
+#pragma unroll
+      for (int r = 0; r < R; r++) { q[r] = qn[r]; d[r] = dn[r]; }
+      issue(bl + G);  // prefetch the next block while this one is computed
+      const float4* xb = smem + (size_t)bl * 8;
+      const int sw = bl & 7;
+      if constexpr (MM == 1) {
+        float4 xv[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) xv[i] = xb[i ^ sw];
+        const float sx = sxs[bl];
+#pragma unroll
+        for (int r = 0; r < R; r++)
+          acc[r][0] = fmaf(h2f(d[r]), block_dot_m1<FMT>(q[r], xv, sx), acc[r][0]);
+      } else {
+        float w[R][32];
+#pragma unroll
+        for (int r = 0; r < R; r++) block_dequant<FMT>(q[r], d[r], w[r]);
+#pragma unroll
+        for (int m = 0; m < MM; m++) {
+          if (m < M) {
+            const float4* xm = xb + (size_t)m * kcb * 8;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+              const float4 xv = xm[i ^ sw];
+#pragma unroll
+              for (int r = 0; r < R; r++) {
+                float a = acc[r][m];
+                a = fmaf(w[r][4 * i + 0], xv.x, a);
+                a = fmaf(w[r][4 * i + 1], xv.y, a);
+                a = fmaf(w[r][4 * i + 2], xv.z, a);
+                a = fmaf(w[r][4 * i + 3], xv.w, a);
+                acc[r][m] = a;
+              }
+            }
+          }
+        }
+      }
+    }
+  }
+
+  // ---- reduce across the lane group and store ----
+#pragma unroll
+  for (int r = 0; r < R; r++) {
+#pragma unroll
+    for (int m = 0; m < MM; m++) {
+      const float v = group_sum<G>(acc[r][m]);
+      if (g == 0 && row_ok[r] && m < M) Y[io->y[m] + lr0 + r] = v;
+    }
+  }
+}
+
+// Dense GEMV: workgroup b computes rows [b * RPW, +RPW) for all M inputs.
+template <int FMT, int MM, int G, int R>
+__global__ __launch_bounds__(kThreads) void k_qmv(const uint8_t* __restrict__ codes,
+                                                  const uint16_t* __restrict__ scales,
+                                                  const float* __restrict__ X,
+                                                  float* __restrict__ Y, int M, int N, int nb,
+                                                  int kcb) {
+  extern __shared__ float4 smem[];
+  constexpr int RPW = (kThreads / G) * R;
+  const int64_t row_base = (int64_t)blockIdx.x * RPW;
+  const int nrows = (int)min((int64_t)RPW, (int64_t)N - row_base);
+  __shared__ TileIO io;
+  if (threadIdx.x < 8) {
+    const int m = threadIdx.x < M ? threadIdx.x : 0;
+    io.x[threadIdx.x] = (int64_t)m * nb * kQK;
+    io.y[threadIdx.x] = (int64_t)m * N + row_base;
+  }
+  // (nb >= 1 here: the first chunk barrier inside tile_qmv publishes io)
+  tile_qmv<FMT, MM, G, R>(codes, scales, nb, row_base, nrows, X, Y, &io, M, smem, kcb);
+}
+
+// ---- expert-indexed GEMV -----------------------------------------------------------
+// Every workgroup first turns the T x top_k ids into per-expert slot lists in LDS (experts
+// ascending, slots ascending within an expert), split into passes of at most 8 slots.
+// The work items are (pass, row tile) pairs, pass-major; workgroup w takes a contiguous
+// range of them.  Each work item stages its slots' inputs and streams the tile's rows of
+// the expert once for all of them.  Slots with a negative id are
+// zero-filled, slots with an id >= E NaN-filled, each by exactly one workgroup.
+struct IdLds {
+  int* ids;        // [TS]
+  int* cnt;        // [E]   slots routed to expert e
+  int* off;        // [E]   start of e's slots in list
+  int* poff;       // [E]   first pass of e
+  int* list;       // [TS]  slot indices grouped by expert
+  int* pass_e;     // [TS]  expert of pass p
+  int* pass_lo;    // [TS]  list offset of pass p
+  int* pass_m;     // [TS]  slots in pass p (1..8)
+  int* totals;     // [2]   number of passes, scratch
+};
+
+template <int FMT, int G, int R>
+__global__ __launch_bounds__(kThreads) void k_qmv_id(const uint8_t* __restrict__ codes,
+                                                     const uint16_t* __restrict__ scales,
+                                                     const int32_t* __restrict__ ids, int E,
+                                                     int N, int nb, int TS, int top_k,
+                                                     const float* __restrict__ X, int64_t xts,
+                                                     int64_t xss, float* __restrict__ Y,
+                                                     int kcb1, int kcb8, int x_floats) {
+  extern __shared__ float4 smem[];
+  constexpr int RPW = (kThreads / G) * R;  // rows per tile
+  const int tid = threadIdx.x;
+  int* ib = reinterpret_cast<int*>(smem + x_floats / 4);
+  IdLds L;
+  L.ids = ib;
+  L.cnt = L.ids + TS;
+  L.off = L.cnt + E;
+  L.poff = L.off + E;
+  L.list = L.poff + E;
+  L.pass_e = L.list + TS;
+  L.pass_lo = L.pass_e + TS;
+  L.pass_m = L.pass_lo + TS;
+  L.totals = L.pass_m + TS;
+  __shared__ TileIO io;
+
+  for (int i = tid; i < TS; i += kThreads) L.ids[i] = ids[i];
+  __syncthreads();
+  for (int e = tid; e < E; e += kThreads) {
+    int c = 0;
+    for (int i = 0; i < TS; i++) c += L.ids[i] == e;
+    L.cnt[e] = c;
+  }
+  __syncthreads();
+  // exclusive scans over experts (slot offsets and pass offsets), by wave 0
+  if (tid < 64) {
+    const int per = (E + 63) / 64;
+    const int e0 = tid * per, e1 = min(E, e0 + per);
+    int s_slots = 0, s_pass = 0;
+    for (int e = e0; e < e1; e++) { s_slots += L.cnt[e]; s_pass += (L.cnt[e] + 7) / 8; }
+    int inc_slots = s_slots, inc_pass = s_pass;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int a = __shfl_up(inc_slots, o, 64), b = __shfl_up(inc_pass, o, 64);
+      if (tid >= o) { inc_slots += a; inc_pass += b; }
+    }
+    int run_slots = inc_slots - s_slots, run_pass = inc_pass - s_pass;
+    for (int e = e0; e < e1; e++) {
+      L.off[e] = run_slots;
+      L.poff[e] = run_pass;
+      run_slots += L.cnt[e];
+      run_pass += (L.cnt[e] + 7) / 8;
+    }
+    if (tid == 63) L.totals[0] = inc_pass;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kThreads) {
+    const int c = L.cnt[e];
+    if (c == 0) continue;
+    int j = L.off[e];
+    for (int i = 0; i < TS; i++)
+      if (L.ids[i] == e) L.list[j++] = i;
+    for (int p = 0; p < (c + 7) / 8; p++) {
+      L.pass_e[L.poff[e] + p] = e;
+      L.pass_lo[L.poff[e] + p] = L.off[e] + 8 * p;
+      L.pass_m[L.poff[e] + p] = min(8, c - 8 * p);
+    }
+  }
+  __syncthreads();
+  const int P = L.totals[0];
+
+  // padding / out-of-range slots
+  for (int ts = blockIdx.x; ts < TS; ts += gridDim.x) {
+    const int e = L.ids[ts];
+    if (e >= 0 && e < E) continue;
+    const float v = e < 0 ? 0.0f : __builtin_nanf("");
+    for (int n = tid; n < N; n += kThreads) Y[(size_t)ts * N + n] = v;
+  }
+
+  // work items: (pass, tile) of RPW rows
+  const int ntiles = (N + RPW - 1) / RPW;
+  const int64_t n_items = (int64_t)P * ntiles;
+  const int64_t per_wg = (n_items + gridDim.x - 1) / gridDim.x;
+  const int64_t it0 = (int64_t)blockIdx.x * per_wg;
+  const int64_t it1 = min(n_items, it0 + per_wg);
+  for (int64_t it = it0; it < it1; it++) {
+    const int p = (int)(it / ntiles), tile = (int)(it % ntiles);
+    const int e = L.pass_e[p], lo = L.pass_lo[p], M = L.pass_m[p];
+    __syncthreads();  // io of the previous item is no longer read
+    if (tid < 8) {
+      const int mm = tid < M ? tid : 0;
+      const int ts = L.list[lo + mm];
+      const int t = ts / top_k, s = ts - t * top_k;
+      io.x[tid] = t * xts + s * xss;
+      io.y[tid] = (int64_t)ts * N + (int64_t)tile * RPW;
+    }
+    __syncthreads();
+    const int64_t row_base = (int64_t)e * N + (int64_t)tile * RPW;
+    const int nrows = min(RPW, N - tile * RPW);
+    if (M == 1)
+      tile_qmv<FMT, 1, G, R>(codes, scales, nb, row_base, nrows, X, Y, &io, 1, smem, kcb1);
+    else
+      tile_qmv<FMT, 8, G, R>(codes, scales, nb, row_base, nrows, X, Y, &io, M, smem, kcb8);
+  }
+}
+
+__global__ void k_fill(float* __restrict__ y, int64_t n, float v) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    y[i] = v;
+}
+
+// ---------------------------------------------------------------- host side ----
+
+int pick_group(int64_t nb) {
+  int best = 64;
+  int64_t best_waste = (nb + 63) / 64 * 64 - nb;
+  for (int G : {32, 16}) {
+    const int64_t waste = (nb + G - 1) / G * G - nb;
+    if (waste < best_waste) { best = G; best_waste = waste; }
+  }
+  return best;
+}
+
+#ifndef BQM_QMV_MIN_WGS
+#define BQM_QMV_MIN_WGS 512  // aim for at least two workgroups per CU
+#endif
+
+int pick_rows(int64_t N, int G, int M) {
+  const int rmax = M == 1 ? 4 : 2;
+  for (int R = rmax; R > 1; R >>= 1) {
+    const int64_t rpw = (kThreads / G) * R;
+    if ((N + rpw - 1) / rpw >= BQM_QMV_MIN_WGS) return R;
+  }
+  return 1;
+}
+
+// Blocks of x staged per LDS chunk for M inputs within `budget` bytes.
+int chunk_blocks(int64_t nb, int M, int budget) {
+  const int per_block = M * 128 + (M == 1 ? 4 : 0);
+  int64_t kcb = budget / per_block;
+  if (kcb >= nb) return (int)(nb > 0 ? nb : 1);
+  return (int)(kcb & ~int64_t(7));
+}
+
+size_t x_lds_bytes(int M, int kcb) { return (size_t)M * kcb * 128 + (M == 1 ? (size_t)kcb * 4 : 0); }
+
+// Kernels using more than 64 KB of dynamic LDS must say so once.
+template <typename Kern>
+void allow_lds(Kern k, size_t bytes) {
+  if (bytes > 64 * 1024)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+using QmvKernel = void (*)(const uint8_t*, const uint16_t*, const float*, float*, int, int, int,
+                           int);
+
+template <int FMT, int MM, int G>
+QmvKernel select_r(int R) {
+  if constexpr (MM == 1) {
+    if (R == 4) return k_qmv<FMT, MM, G, 4>;
+  }
+  if (R == 2) return k_qmv<FMT, MM, G, 2>;
+  return k_qmv<FMT, MM, G, 1>;
+}
+
+template <int FMT, int MM>
+QmvKernel select_g(int G, int R) {
+  if (G == 64) return select_r<FMT, MM, 64>(R);
+  if (G == 32) return select_r<FMT, MM, 32>(R);
+  return select_r<FMT, MM, 16>(R);
+}
+
+template <int FMT>
+QmvKernel select_m(int M, int G, int R) {
+  if (M == 1) return select_g<FMT, 1>(G, R);
+  if (M == 2) return select_g<FMT, 2>(G, R);
+  if (M <= 4) return select_g<FMT, 4>(G, R);
+  return select_g<FMT, 8>(G, R);
+}
+
+using QmvIdKernel = void (*)(const uint8_t*, const uint16_t*, const int32_t*, int, int, int, int,
+                             int, const float*, int64_t, int64_t, float*, int, int, int);
+
+template <int FMT, int G>
+QmvIdKernel select_id_r(int R) {
+  if (R == 2) return k_qmv_id<FMT, G, 2>;
+  return k_qmv_id<FMT, G, 1>;
+}
+
+template <int FMT>
+QmvIdKernel select_id(int G, int R) {
+  if (G == 64) return select_id_r<FMT, 64>(R);
+  if (G == 32) return select_id_r<FMT, 32>(R);
+  return select_id_r<FMT, 16>(R);
+}
+
+}  // namespace
+
+int launch_fill(float* y, int64_t n, float v, hipStream_t s) {
+  if (n <= 0) return BQM_OK;
+  const int64_t blocks = (n + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(k_fill, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(kThreads), 0, s,
+                     y, n, v);
+  return launch_status();
+}
+
+int launch_qmv(int fmt, const void* w, const float* X, float* Y, int M, int64_t N, int64_t K,
+               hipStream_t s) {
+  if (M == 0 || N == 0) return BQM_OK;
+  if (K == 0) return launch_fill(Y, (int64_t)M * N, 0.0f, s);
+  Layout L;
+  layout_of(fmt, N, K, &L);
+  const uint8_t* codes = static_cast<const uint8_t*>(w);
+  const uint16_t* scales = reinterpret_cast<const uint16_t*>(codes + L.scales_off);
+  const int G = pick_group(L.nb);
+  const int R = pick_rows(N, G, M);
+  const int kcb = chunk_blocks(L.nb, M, kLdsBudget);
+  const int64_t rpw = (kThreads / G) * R;
+  const int64_t grid = (N + rpw - 1) / rpw;
+  const size_t lds = x_lds_bytes(M, kcb);
+  QmvKernel k = fmt == BQM_Q4_0 ? select_m<FQ4>(M, G, R) : select_m<FQ8>(M, G, R);
+  allow_lds(k, lds);
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kThreads), lds, s, codes, scales, X, Y, M,
+                     (int)N, (int)L.nb, kcb);
+  return launch_status();
+}
+
+int launch_qmv_id(int fmt, const void* w, int E, int64_t N, int64_t K, const int32_t* ids, int T,
+                  int top_k, const float* X, int64_t xts, int64_t xss, float* Y, hipStream_t s) {
+  const int TS = T * top_k;
+  // K == 0 and E == 0 need no special path: the kernel then streams nothing, writes the
+  // empty sums (0) and marks every non-negative id of an empty expert set out of range.
+  Layout L;
+  layout_of(fmt, (int64_t)E * N, K, &L);
+  const uint8_t* codes = static_cast<const uint8_t*>(w);
+  const uint16_t* scales = reinterpret_cast<const uint16_t*>(codes + L.scales_off);
+  const int G = pick_group(L.nb);
+  const int R = 2;
+  const int budget = 48 * 1024;
+  const int kcb1 = chunk_blocks(L.nb, 1, budget), kcb8 = chunk_blocks(L.nb, 8, budget);
+  size_t xb = x_lds_bytes(1, kcb1) > x_lds_bytes(8, kcb8) ? x_lds_bytes(1, kcb1) : x_lds_bytes(8, kcb8);
+  xb = (xb + 15) & ~size_t(15);
+  const int x_floats = (int)(xb / 4);
+  const size_t lds = xb + (size_t)(3 * E + 5 * TS + 2) * 4;
+  const int64_t rpw = (kThreads / G) * R;
+  const int64_t ntiles = (N + rpw - 1) / rpw;
+  int64_t grid = (int64_t)TS * ntiles;
+  if (grid > 1024) grid = 1024;
+  QmvIdKernel k = fmt == BQM_Q4_0 ? select_id<FQ4>(G, R) : select_id<FQ8>(G, R);
+  allow_lds(k, lds);
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kThreads), lds, s, codes, scales, ids, E, (int)N,
+                     (int)L.nb, TS, top_k, X, xts, xss, Y, kcb1, kcb8, x_floats);
+  return launch_status();
+}
+
+}  // namespace bqm

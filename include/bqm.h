@@ -1,0 +1,136 @@
+/*
+ * bqm.h - block-quantized matrix products on AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * What the library computes.  Decode streams every weight once per token, so its
+ * speed is set by how many weight bytes cross HBM ("V100跑Qwen 27B：量化与KV Cache调优，
+ * 从4到64 tok/s", lmnt.cn, section 1.2); the compact block formats Q4_0 and Q8_0 named
+ * in that page's format table (section 4.1) cut those bytes.  Every product here is
+ *     y = dequant(W) . x
+ * with W stored in 32-weight blocks that each carry one binary16 scale d:
+ *     Q4_0 weight = (nibble - 8) * d        Q8_0 weight = int8 * d.
+ *
+ * Interchange block layout (host or device bytes, what bqm_repack reads):
+ *     Q4_0: 18 bytes per block = binary16 d (little endian), then 16 bytes; byte j
+ *           holds weight j in its low nibble and weight j+16 in its high nibble.
+ *     Q8_0: 34 bytes per block = binary16 d, then 32 signed bytes (weight j = byte j).
+ *     A matrix W[N][K] is N rows of K/32 consecutive blocks.
+ * The pages name the formats but do not print their bytes; this is the ggml layout.
+ *
+ * Packed (device) layout, what the products read: produced by bqm_repack, opaque to
+ * callers except for its size, bqm_packed_bytes().  It separates the 16-byte aligned
+ * code bytes from the scales so that every code load is a full 16-byte load.
+ *
+ * Conventions shared by every call:
+ *   - Pointers are DEVICE pointers unless stated; the caller owns all memory.  The
+ *     library allocates nothing, frees nothing and never synchronizes: work is queued
+ *     on `stream` (a HIP stream; 0 = the null stream) and the call returns.
+ *   - Argument errors are found on the host before anything is launched: the call
+ *     returns a non-zero bqm_status and leaves every output untouched.  A failed launch
+ *     returns BQM_E_LAUNCH.  Faults inside a kernel surface at the caller's next
+ *     synchronization, as for any HIP kernel.
+ *   - Sizes may be zero (nothing is launched, except that N > 0 with K = 0 writes
+ *     zeros, the value of an empty sum).  K must be a multiple of 32.
+ *   - Pointers passed to the products must be 16-byte aligned (torch allocations are).
+ *   - Outputs must not alias inputs.  Results are deterministic: no atomics, a fixed
+ *     summation order, the same bits on every run with the same launch.
+ *   - Floating-point outputs are fp32 and satisfy, per output,
+ *         |y - y_exact| <= 1e-3 * sum_i |w_i * x_i|
+ *     (y_exact in exact arithmetic); integer and byte outputs are exact.
+ */
+#ifndef BQM_H
+#define BQM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BQM_OK = 0,
+  BQM_E_NULL = 1,        /* a required pointer is NULL                          */
+  BQM_E_SHAPE = 2,       /* negative size, K % 32 != 0, or a size over a limit  */
+  BQM_E_ALIGN = 3,       /* a pointer is not 16-byte aligned                    */
+  BQM_E_UNSUPPORTED = 4, /* unknown format code                                 */
+  BQM_E_LAUNCH = 5       /* the HIP runtime refused a launch                    */
+} bqm_status;
+
+typedef enum { BQM_Q4_0 = 2, BQM_Q8_0 = 8 } bqm_fmt;
+
+/* Largest M accepted by qmv_q4_0 / qmv_q8_0, the small-batch decode width. */
+#define BQM_QMV_MAX_M 8
+/* Limits of qmv_id: token count, experts per token, number of experts (the per-expert
+ * slot tables are built in LDS). */
+#define BQM_QMV_ID_MAX_T 64
+#define BQM_QMV_ID_MAX_TOPK 32
+#define BQM_QMV_ID_MAX_E 4096
+
+/* Bytes of the packed layout of a rows x K matrix in format fmt (0 for an unknown
+ * format or a K that is not a multiple of 32).  Host function, no device work. */
+size_t bqm_packed_bytes(int fmt, int64_t rows, int64_t K);
+
+/* One-time layout transform: interchange blocks (w_interchange, rows x K/32 blocks,
+ * 2-byte aligned) -> packed layout (w_packed, bqm_packed_bytes(fmt, rows, K) bytes,
+ * 16-byte aligned).  Every byte of the packed buffer is written.  Precedent: weights
+ * re-laid out once for the unit that runs them, like the interleaved repack on the page
+ * "ik_llama.cpp 老工作站多 GPU 部署 Qwen3-235B-A22B 实战指南" (nxmr.cn), section on -rtr. */
+int bqm_repack(int fmt, const void* w_interchange, void* w_packed, int64_t rows, int64_t K,
+               hipStream_t stream);
+
+/* Inverse of bqm_repack (packed -> interchange), byte exact.  For tests and export. */
+int bqm_unpack(int fmt, const void* w_packed, void* w_interchange, int64_t rows, int64_t K,
+               hipStream_t stream);
+
+/* Decode GEMV and small-batch GEMV ("V100跑Qwen 27B" page, section 1.2: every weight read
+ * once per token):
+ *     Y[m][n] = sum_k dequant(W)[n][k] * X[m][k],   0 <= m < M <= 8, 0 <= n < N.
+ * w_packed: packed N x K matrix.  X: fp32 [M][K] row-major.  Y: fp32 [M][N] row-major.
+ * M = 0 or N = 0: nothing to do.  M > 8: BQM_E_SHAPE. */
+int qmv_q4_0(const void* w_packed, const float* X, float* Y, int M, int64_t N, int64_t K,
+             hipStream_t stream);
+int qmv_q8_0(const void* w_packed, const float* X, float* Y, int M, int64_t N, int64_t K,
+             hipStream_t stream);
+
+/* Expert-indexed GEMV, the mul_mat_id of the page "ik_llama.cpp 老工作站多 GPU 部署
+ * Qwen3-235B-A22B 实战指南" (nxmr.cn), background and split-mode sections: a 3D expert
+ * tensor W[E][N][K] and per-token expert ids.
+ *     e = ids[t][s];  Y[t][s][n] = sum_k dequant(W)[e][n][k] * x_ts[k]
+ *     x_ts = X + t * x_tok_stride + s * x_slot_stride      (strides in floats)
+ * x_slot_stride = 0 broadcasts one input per token (gate/up projections); = K gives each
+ * slot its own input (down projection).  A negative id marks a padding slot: its Y row is
+ * written with zeros.  An id >= E is a contract violation: its Y row is filled with NaN
+ * and nothing outside the arrays is read.  Each selected expert's rows are streamed once
+ * for all the tokens routed to it.
+ * w_packed: the expert tensor packed as ONE matrix of E*N rows (bqm_repack with
+ * rows = E*N).  ids: int32 [T][top_k], device memory.  Y: fp32 [T][top_k][N].
+ * fmt: BQM_Q4_0 or BQM_Q8_0.  Limits: T <= 64, top_k <= 32, E <= 4096. */
+int qmv_id(int fmt, const void* w_packed, int E, int64_t N, int64_t K, const int32_t* ids, int T,
+           int top_k, const float* X, int64_t x_tok_stride, int64_t x_slot_stride, float* Y,
+           hipStream_t stream);
+
+/* Activation quantizer for the prefill product, per row m and 32-wide block b, in IEEE
+ * single precision:  a = max_j |x_j|;  dx = a / 127 (correctly rounded);  dx == 0 gives
+ * all-zero codes and dx = +0; otherwise Xq_j = round_half_away_from_zero(x_j / dx) clamped
+ * to [-127, 127].  X: fp32 [M][K];  Xq: int8 [M][K];  dx: fp32 [M][K/32].  Bit exact. */
+int bqm_quantize_q8_act(const float* X, int8_t* Xq, float* dx, int64_t M, int64_t K,
+                        hipStream_t stream);
+
+/* Prefill product with Q8_0 weights (the llama-bench pp512 shape of the page "llama.cpp
+ * 0.9.0" analysis (ai-v5 LLMNews), section 2 table):
+ *     isum[m][n][b] = sum_{j<32} qw[n][32b+j] * Xq[m][32b+j]        exact int32 (int8 MFMA)
+ *     Y[m][n]       = sum_b (d_w[n][b] * dx[m][b]) * isum[m][n][b]    fp32
+ * w_packed: packed Q8_0 N x K matrix.  Xq, dx: from bqm_quantize_q8_act.  Y: fp32 [M][N]. */
+int qmm_q8_0(const void* w_packed, const int8_t* Xq, const float* dx, float* Y, int64_t M,
+             int64_t N, int64_t K, hipStream_t stream);
+
+/* Static English text for a status code. */
+const char* bqm_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BQM_H */

@@ -1,0 +1,105 @@
+"""The C-ABI library on the host: it loads, exports every symbol include/bqm.h declares,
+and rejects bad arguments on the host before anything is launched.  No GPU needed: every
+call below fails validation and returns before touching the HIP runtime."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_quantized_matrix_amd import bqm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bqm.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([A-Za-z_]\w*)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "defined")))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("bqm_packed_bytes", "bqm_repack", "bqm_unpack", "qmv_q4_0", "qmv_q8_0", "qmv_id",
+              "bqm_quantize_q8_act", "qmm_q8_0", "bqm_strerror"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(bqm.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), f"libbqm.so does not export {n}"
+
+
+def test_packed_bytes():
+    # Q4_0 4096 x 4096: 16 B of codes + 2 B of scale per block, sections 256-aligned
+    nb = 4096 * 4096 // 32
+    assert bqm.packed_bytes("q4_0", 4096, 4096) == nb * 16 + nb * 2
+    assert bqm.packed_bytes("q8_0", 17408, 5120) == 17408 * 5120 + 17408 * 160 * 2
+    assert bqm.packed_bytes("q4_0", 3, 32) == 256 + 256    # 48 B codes -> 256, 6 B scales -> 256
+    assert bqm.packed_bytes("q4_0", 0, 64) == 0
+    assert bqm.packed_bytes("q4_0", 5, 33) == 0             # K not a multiple of 32
+    assert bqm.packed_bytes(3, 5, 32) == 0                  # unknown format
+
+
+def test_strerror():
+    assert bqm.strerror(0) == "success"
+    assert "multiple of 32" in bqm.strerror(2)
+    assert bqm.strerror(99) == "unknown status"
+
+
+def _st(fn, *args):
+    return getattr(bqm.lib(), fn)(*args)
+
+
+P = ctypes.c_void_p
+GOOD = P(0x100000)      # 16-byte aligned fake addresses: never dereferenced on these paths
+ODD = P(0x100008)
+
+
+def test_host_validation_before_launch():
+    L = bqm.lib()
+    # K not a multiple of 32
+    assert L.qmv_q4_0(GOOD, GOOD, GOOD, 1, 64, 48, None) == 2
+    assert L.qmv_q8_0(GOOD, GOOD, GOOD, 1, 64, 33, None) == 2
+    # M out of range
+    assert L.qmv_q4_0(GOOD, GOOD, GOOD, 9, 64, 64, None) == 2
+    assert L.qmv_q4_0(GOOD, GOOD, GOOD, -1, 64, 64, None) == 2
+    # null pointers
+    assert L.qmv_q4_0(None, GOOD, GOOD, 1, 64, 64, None) == 1
+    assert L.qmv_q4_0(GOOD, None, GOOD, 1, 64, 64, None) == 1
+    assert L.qmv_q4_0(GOOD, GOOD, None, 1, 64, 64, None) == 1
+    # misaligned
+    assert L.qmv_q4_0(ODD, GOOD, GOOD, 1, 64, 64, None) == 3
+    assert L.qmv_q4_0(GOOD, ODD, GOOD, 1, 64, 64, None) == 3
+    # unknown format
+    assert L.bqm_repack(3, GOOD, GOOD, 4, 64, None) == 4
+    assert L.qmv_id(5, GOOD, 4, 8, 64, GOOD, 1, 2, GOOD, 64, 0, GOOD, None) == 4
+    # qmv_id limits and strides
+    assert L.qmv_id(2, GOOD, 4, 8, 64, GOOD, 65, 2, GOOD, 64, 0, GOOD, None) == 2
+    assert L.qmv_id(2, GOOD, 4097, 8, 64, GOOD, 1, 2, GOOD, 64, 0, GOOD, None) == 2
+    assert L.qmv_id(2, GOOD, 4, 8, 64, GOOD, 1, 33, GOOD, 64, 0, GOOD, None) == 2
+    assert L.qmv_id(2, GOOD, 4, 8, 64, GOOD, 1, 2, GOOD, 66, 0, GOOD, None) == 3
+    assert L.qmv_id(2, GOOD, 4, 8, 64, None, 1, 2, GOOD, 64, 0, GOOD, None) == 1
+    # quantizer and qmm
+    assert L.bqm_quantize_q8_act(GOOD, GOOD, GOOD, 4, 40, None) == 2
+    assert L.bqm_quantize_q8_act(GOOD, None, GOOD, 4, 64, None) == 1
+    assert L.qmm_q8_0(GOOD, GOOD, GOOD, GOOD, 4, 8, 48, None) == 2
+    assert L.qmm_q8_0(GOOD, ODD, GOOD, GOOD, 4, 8, 64, None) == 3
+    # repack alignment: interchange needs 2-byte alignment, packed 16
+    assert L.bqm_repack(2, P(0x100001), GOOD, 4, 64, None) == 3
+    assert L.bqm_repack(2, GOOD, ODD, 4, 64, None) == 3
+
+
+def test_empty_sizes_are_no_ops():
+    L = bqm.lib()
+    # nothing to compute: success without any launch (null pointers are fine then)
+    assert L.qmv_q4_0(None, None, None, 0, 64, 64, None) == 0
+    assert L.qmv_q4_0(None, None, None, 1, 0, 64, None) == 0
+    assert L.qmv_id(2, None, 4, 8, 64, None, 0, 8, None, 64, 0, None, None) == 0
+    assert L.bqm_quantize_q8_act(None, None, None, 0, 64, None) == 0
+    assert L.qmm_q8_0(None, None, None, None, 0, 8, 64, None) == 0
+    assert L.bqm_repack(2, None, None, 0, 64, None) == 0
+    assert L.bqm_unpack(8, None, None, 4, 0, None) == 0

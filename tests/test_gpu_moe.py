@@ -1,0 +1,100 @@
+"""GPU parity of the expert-indexed GEMV (qmv_id) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle
+from block_quantized_matrix_amd import bqm
+from tests._gpu import DEV, check_close, host, packed, say, weights
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _oracle():
+    oracle.build(force=False)
+
+
+def run_id(fmt, E, N, K, ids_np, X, xts, xss, key):
+    T, top_k = ids_np.shape
+    Wi = weights(fmt, E * N, K, key)
+    Wp = packed(fmt, Wi, E * N, K)
+    ids = torch.from_numpy(ids_np).to(DEV)
+    Y = torch.full((T, top_k, N), -7.0, device=DEV)
+    bqm.qmv_id(fmt, Wp, E, N, K, ids, T, top_k, X, xts, xss, Y)
+    Yr, S = oracle.qmv_id(fmt, host(Wi), E, N, K, ids_np, host(X).reshape(-1), xts, xss)
+    return host(Y), Yr, S
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0"])
+@pytest.mark.parametrize("slots", ["broadcast", "per_slot"])
+@pytest.mark.parametrize("E,N,K", [(5, 37, 96), (3, 300, 1536), (9, 64, 4096)])
+def test_qmv_id_small(fmt, slots, E, N, K):
+    say("qmv_id small", fmt, slots, E, N, K)
+    ids = np.array([[3, 0, 4], [-1, 4, 2], [1, 3, -1], [0, 2, 4]], np.int32) % max(E, 1)
+    ids[1, 0] = -1
+    ids[2, 2] = -1
+    T, top_k = ids.shape
+    if slots == "broadcast":
+        X = gen.normal((T, K), ("id-x", K), device=DEV)
+        xts, xss = K, 0
+    else:
+        X = gen.normal((T, top_k, K), ("id-x2", K), device=DEV)
+        xts, xss = top_k * K, K
+    y, Yr, S = run_id(fmt, E, N, K, ids, X, xts, xss, ("id", fmt, E, N, K))
+    check_close(y, Yr, S, f"qmv_id {fmt} {slots}")
+    assert np.all(y[1, 0] == 0) and np.all(y[2, 2] == 0)
+
+
+def test_qmv_id_many_tokens_per_expert():
+    """20 tokens all routed to experts 0 and 1: passes of 8, 8 and 4 slots per expert."""
+    E, N, K, T = 4, 80, 512, 20
+    ids = np.tile(np.array([[1, 0]], np.int32), (T, 1))
+    X = gen.normal((T, K), ("many-x",), device=DEV)
+    y, Yr, S = run_id("q4_0", E, N, K, ids, X, K, 0, ("many",))
+    check_close(y, Yr, S, "many tokens per expert")
+
+
+def test_qmv_id_out_of_range_ids_give_nan():
+    E, N, K = 3, 40, 64
+    ids = np.array([[0, 3], [7, -1]], np.int32)
+    X = gen.normal((2, K), ("oor-x",), device=DEV)
+    y, Yr, S = run_id("q4_0", E, N, K, ids, X, K, 0, ("oor",))
+    assert np.all(np.isnan(y[0, 1])) and np.all(np.isnan(y[1, 0]))
+    assert np.all(y[1, 1] == 0)
+    check_close(y[0, 0], Yr[0, 0], S[0, 0], "valid slot next to bad ids")
+
+
+@pytest.mark.parametrize("T", [1, 16])
+@pytest.mark.parametrize("proj", ["gate", "down"])
+def test_qmv_id_moe_layer(T, proj):
+    """128 experts, top-8, hidden 4096, expert FFN 1536, Q4_0; ids from the skewed router;
+    gate/up take one input per token (broadcast), down one input per (token, slot)."""
+    sh = gen.MOE_SHAPE
+    E, top_k = sh["E"], sh["top_k"]
+    ids = gen.router_ids(T, E, top_k, ("moe-router", T))
+    if proj == "gate":
+        N, K = sh["ffn"], sh["hidden"]
+        X = gen.normal((T, K), ("moe-x", T, proj), device=DEV)
+        xts, xss = K, 0
+    else:
+        N, K = sh["hidden"], sh["ffn"]
+        X = gen.normal((T, top_k, K), ("moe-x", T, proj), device=DEV)
+        xts, xss = top_k * K, K
+    say("qmv_id moe", T, proj, "unique experts", len(np.unique(ids)))
+    y, Yr, S = run_id("q4_0", E, N, K, ids, X, xts, xss, ("moe", proj))
+    check_close(y, Yr, S, f"moe T={T} {proj}")
+
+
+def test_qmv_id_deterministic():
+    E, N, K, T = 16, 256, 1024, 12
+    ids = gen.router_ids(T, E, 4, ("det-router",))
+    Wp = packed("q4_0", weights("q4_0", E * N, K, ("det-id",)), E * N, K)
+    X = gen.normal((T, K), ("det-id-x",), device=DEV)
+    idd = torch.from_numpy(ids).to(DEV)
+    Y1 = torch.empty((T, 4, N), device=DEV)
+    Y2 = torch.empty((T, 4, N), device=DEV)
+    bqm.qmv_id("q4_0", Wp, E, N, K, idd, T, 4, X, K, 0, Y1)
+    bqm.qmv_id("q4_0", Wp, E, N, K, idd, T, 4, X, K, 0, Y2)
+    assert torch.equal(Y1, Y2)

@@ -1,0 +1,122 @@
+"""GPU parity of the activation quantizer (bit exact) and the int8-MFMA prefill product."""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle
+from block_quantized_matrix_amd import bqm
+from tests._gpu import DEV, check_close, host, packed, say, weights
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _oracle():
+    oracle.build(force=False)
+
+
+def quantize(X, M, K):
+    Xq = torch.empty((M, K), dtype=torch.int8, device=DEV)
+    dx = torch.empty((M, K // 32), dtype=torch.float32, device=DEV)
+    bqm.bqm_quantize_q8_act(X, Xq, dx, M, K)
+    return Xq, dx
+
+
+@pytest.mark.parametrize("M,K", [(1, 32), (7, 96), (512, 5120)])
+def test_quantize_q8_act_bitwise(M, K):
+    say("quantize", M, K)
+    X = gen.normal((M, K), ("qa", M, K), device=DEV)
+    Xq, dx = quantize(X, M, K)
+    Xq_r, dx_r = oracle.quantize_q8_act(host(X), K)
+    assert np.array_equal(host(Xq), Xq_r)
+    assert np.array_equal(host(dx).view(np.uint32), dx_r.view(np.uint32))
+
+
+def test_quantize_q8_act_special_blocks():
+    """Ties (x/dx exactly k + 1/2), zero blocks, subnormal blocks, the largest float below 1/2."""
+    K = 256
+    X = torch.zeros((4, K))
+    X[0, :32] = torch.arange(-16, 16) * 0.5
+    X[0, 31] = 127.0                                       # dx = 1: every half is a tie
+    X[0, 32:38] = torch.tensor([127.0, 63.5, -0.5, 2.5, -2.5, 0.49999997])
+    X[1, 64:96] = torch.arange(-16, 16) * 2.0 ** -149      # dx underflows to 0
+    X[2, 96:128] = torch.arange(1, 33) * 2.0 ** -140       # subnormal dx
+    X[3] = gen.normal((K,), ("qa-special",)) * 1e30
+    Xd = X.to(DEV)
+    Xq, dx = quantize(Xd, 4, K)
+    Xq_r, dx_r = oracle.quantize_q8_act(X.numpy(), K)
+    assert np.array_equal(host(Xq), Xq_r)
+    assert np.array_equal(host(dx).view(np.uint32), dx_r.view(np.uint32))
+    assert list(host(Xq)[0, 32:38]) == [127, 64, -1, 3, -3, 0]
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (5, 37, 96), (130, 129, 160), (256, 300, 1056)])
+def test_qmm_parity_small(M, N, K):
+    say("qmm small", M, N, K)
+    Wi = weights("q8_0", N, K, ("qmm", M, N, K))
+    X = gen.normal((M, K), ("qmm-x", M, N, K), device=DEV)
+    Xq, dx = quantize(X, M, K)
+    Y = torch.full((M, N), float("nan"), device=DEV)
+    bqm.qmm_q8_0(packed("q8_0", Wi, N, K), Xq, dx, Y, M, N, K)
+    Yr, S = oracle.qmm_q8_0(host(Wi), host(Xq), host(dx), N, K)
+    check_close(host(Y), Yr, S, f"qmm {M}x{N}x{K}")
+
+
+def _exact_probe(M, N, K, rows=None):
+    """qw, qx in [-8, 8], dw, dx in {0.5, 1, 2}: the block sums are exact integers and so is
+    every fp32 step after them, so the output equals the oracle bit for bit; a single
+    wrong integer block sum changes it."""
+    Wi = gen.raw_q8_0(N, K, ("qmm-probe", N, K), codes=(-8, 8), device=DEV)
+    Xq = gen.small_int((M, K), ("qmm-probe-x", M, K), device=DEV, dtype=torch.int32).to(torch.int8)
+    pick = gen.small_int((M, K // 32), ("qmm-probe-dx", M, K), 0, 2, device=DEV, dtype=torch.int32)
+    dx = torch.tensor([0.5, 1.0, 2.0], device=DEV)[pick.long()]
+    Y = torch.empty((M, N), device=DEV)
+    bqm.qmm_q8_0(packed("q8_0", Wi, N, K), Xq, dx, Y, M, N, K)
+    Wh = host(Wi).reshape(N, -1)
+    if rows is not None:
+        Wh = Wh[rows]
+    Yr, _ = oracle.qmm_q8_0(Wh, host(Xq), host(dx), Wh.shape[0], K)
+    yg = host(Y) if rows is None else host(Y)[:, rows]
+    assert np.array_equal(yg.astype(np.float64), Yr)
+
+
+@pytest.mark.parametrize("M,N,K", [(3, 5, 64), (130, 129, 544), (128, 256, 5120)])
+def test_qmm_exact_probe(M, N, K):
+    say("qmm exact", M, N, K)
+    _exact_probe(M, N, K)
+
+
+def test_qmm_exact_probe_prefill_shape():
+    """The full 512 x 17408 x 5120 prefill shape, sampled output columns, bit exact."""
+    say("qmm exact full shape")
+    sh = gen.PREFILL_SHAPE
+    rows = np.unique(np.random.default_rng(1).integers(0, sh["N"], 48))
+    _exact_probe(sh["M"], sh["N"], sh["K"], rows)
+
+
+def test_qmm_prefill_shape():
+    """Prefill GEMM: M=512 tokens, K=5120, N=17408, Q8_0 weights from N(0, 0.02), activations
+    N(0, 1) quantized per block; sampled output columns against the oracle."""
+    sh = gen.PREFILL_SHAPE
+    M, N, K = sh["M"], sh["N"], sh["K"]
+    say("qmm prefill shape")
+    Wi = weights("q8_0", N, K, ("prefill", 0))
+    X = gen.normal((M, K), ("prefill-x", 0), device=DEV)
+    Xq, dx = quantize(X, M, K)
+    Y = torch.empty((M, N), device=DEV)
+    bqm.qmm_q8_0(packed("q8_0", Wi, N, K), Xq, dx, Y, M, N, K)
+    rows = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(2).integers(0, N, 64)]))
+    Yr, S = oracle.qmm_q8_0(host(Wi).reshape(N, -1)[rows], host(Xq), host(dx), len(rows), K)
+    check_close(host(Y)[:, rows], Yr, S, "prefill")
+
+
+def test_qmm_deterministic():
+    M, N, K = 256, 384, 2048
+    Wp = packed("q8_0", weights("q8_0", N, K, ("qmm-det",)), N, K)
+    Xq, dx = quantize(gen.normal((M, K), ("qmm-det-x",), device=DEV), M, K)
+    Y1 = torch.empty((M, N), device=DEV)
+    Y2 = torch.empty((M, N), device=DEV)
+    bqm.qmm_q8_0(Wp, Xq, dx, Y1, M, N, K)
+    bqm.qmm_q8_0(Wp, Xq, dx, Y2, M, N, K)
+    assert torch.equal(Y1, Y2)

@@ -23,7 +23,9 @@ def run_id(fmt, E, N, K, ids_np, X, xts, xss, key):
     ids = torch.from_numpy(ids_np).to(DEV)
     Y = torch.full((T, top_k, N), -7.0, device=DEV)
     bqm.qmv_id(fmt, Wp, E, N, K, ids, T, top_k, X, xts, xss, Y)
-    Yr, S = oracle.qmv_id(fmt, host(Wi), E, N, K, ids_np, host(X).reshape(-1), xts, xss)
+    # the oracle rejects ids >= E (a contract violation); give it those slots as padding
+    ids_ok = np.where(ids_np >= E, -1, ids_np).astype(np.int32)
+    Yr, S = oracle.qmv_id(fmt, host(Wi), E, N, K, ids_ok, host(X).reshape(-1), xts, xss)
     return host(Y), Yr, S
 
 

@@ -35,6 +35,7 @@ namespace bqm {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kLdsBudget = 80 * 1024;  // bytes of LDS per workgroup (two per CU fit)
@@ -321,6 +322,232 @@ __global__ __launch_bounds__(kThreads) void k_qmv(const uint8_t* __restrict__ co
   tile_qmv<FMT, MM, G, R>(codes, scales, nb, row_base, nrows, X, Y, &io, M, smem, kcb);
 }
 
+// ---- persistent batch-1 GEMV ------------------------------------------------------
+// The batch-1 product is the bandwidth-critical one, so it gets its own kernel shaped
+// around the VALU budget (Q4_0 at 8 TB/s delivers 14.2 T weights/s against 39.3 T fp32
+// lane-ops/s, about 2.8 ops per weight):
+//  - One 1024-thread workgroup per CU (grid = CU count) owns a contiguous range of rows
+//    and stages x into LDS once.  Blocks are 144 bytes apart in LDS: 128 bytes of x,
+//    then the block's x sum; with that stride eight neighbouring blocks start in eight
+//    different 16-byte bank groups, so the per-lane block reads are conflict-free with
+//    immediate offsets.  For Q4_0 the x values that meet the high nibbles are stored
+//    divided by 16 (exact), so one FMA chain takes the nibbles in place (16 n * x / 16).
+//  - Codes and scales come through buffer loads: the per-lane part of the offset is a
+//    constant register, the per-step part a scalar, so a load costs no VALU address
+//    arithmetic.  Lanes past the workgroup's last row (or past K in a ragged last step)
+//    use an offset beyond the descriptor and read zeros.
+//  - Each lane keeps P blocks (per row) in flight in a register ring that is consumed in
+//    place (the loop is unrolled by P).
+//  - The waves of the workgroup take tiles of (64/G)*R rows round-robin; a lane group
+//    reduces and stores a row when its last block is done.
+// Arithmetic per block and row: 8 ANDs, 32 v_cvt_f32_ubyte, 32 FMAs, then
+// r = chain - 8 * sum(x) (Q8_0: - 128 * sum(x)) and acc += d * r (v_fma_mix: d stays fp16).
+// The chain and the block sum follow the same order and 8, 128 and 1/16 are powers of
+// two, so neutral codes give exactly zero.
+constexpr int kP1Threads = 1024;
+constexpr int kP1Waves = kP1Threads / 64;
+constexpr int kBlkLds = 144;  // LDS bytes per staged block
+
+template <int FMT>
+__device__ __forceinline__ float chain_m1(const Codes<FMT>& q, const f32x4* __restrict__ xl) {
+  // xl: the staged block (8 chunks of 4 floats), Q4_0 chunks 4..7 already divided by 16
+  float acc;
+  if constexpr (FMT == FQ4) {
+    const uint32_t w[4] = {q.a.x, q.a.y, q.a.z, q.a.w};
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      uint32_t l = w[k] & 0x0F0F0F0Fu, h = w[k] & 0xF0F0F0F0u;
+      asm("" : "+v"(l), "+v"(h));  // keep the byte conversions as v_cvt_f32_ubyte{0..3}
+      const f32x4 a = xl[k], b = xl[k + 4];
+      if (k == 0) acc = ub(l, 0) * a.x; else acc = fmaf(ub(l, 0), a.x, acc);
+      acc = fmaf(ub(l, 1), a.y, acc); acc = fmaf(ub(l, 2), a.z, acc); acc = fmaf(ub(l, 3), a.w, acc);
+      acc = fmaf(ub(h, 0), b.x, acc); acc = fmaf(ub(h, 1), b.y, acc);
+      acc = fmaf(ub(h, 2), b.z, acc); acc = fmaf(ub(h, 3), b.w, acc);
+    }
+  } else {
+    const uint32_t w[8] = {q.a.x, q.a.y, q.a.z, q.a.w, q.b.x, q.b.y, q.b.z, q.b.w};
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      uint32_t u = w[k] ^ 0x80808080u;
+      asm("" : "+v"(u));
+      const f32x4 a = xl[k];
+      if (k == 0) acc = ub(u, 0) * a.x; else acc = fmaf(ub(u, 0), a.x, acc);
+      acc = fmaf(ub(u, 1), a.y, acc); acc = fmaf(ub(u, 2), a.z, acc); acc = fmaf(ub(u, 3), a.w, acc);
+    }
+  }
+  return acc;
+}
+
+// Block sum of the staged x in the order chain_m1 consumes it.
+template <int FMT>
+__device__ __forceinline__ float chain_xsum(const f32x4* __restrict__ xl) {
+  float s;
+  if constexpr (FMT == FQ4) {
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      const f32x4 a = xl[k], b = xl[k + 4];
+      if (k == 0) s = a.x; else s = s + a.x;
+      s = s + a.y; s = s + a.z; s = s + a.w;
+      s = s + b.x * 16.0f; s = s + b.y * 16.0f; s = s + b.z * 16.0f; s = s + b.w * 16.0f;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      const f32x4 a = xl[k];
+      if (k == 0) s = a.x; else s = s + a.x;
+      s = s + a.y; s = s + a.z; s = s + a.w;
+    }
+  }
+  return s;
+}
+
+struct P1Args {
+  const uint8_t* codes;     // packed code section of the whole matrix
+  const uint16_t* scales;   // packed scale section
+  const float* X;           // [K]
+  float* Y;                 // [N]
+  int N, nb;
+};
+
+template <int FMT, int G, int R, int P, bool RAGGED>
+__global__ __launch_bounds__(kP1Threads) void k_qmv1p(P1Args a) {
+  extern __shared__ float4 smem[];
+  constexpr int CB = FMT == FQ4 ? 16 : 32;     // code bytes per block
+  constexpr int GPW = 64 / G;                  // lane groups per wave
+  constexpr int RW = GPW * R;                  // rows per wave tile
+  const int nb = a.nb;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep in SGPRs
+  const int g = lane % G, lg = lane / G;
+  const int64_t row_begin = (int64_t)blockIdx.x * a.N / gridDim.x;
+  const int64_t row_end = (int64_t)(blockIdx.x + 1) * a.N / gridDim.x;
+  const int nrows = (int)(row_end - row_begin);
+  const int ntiles = (nrows + RW - 1) / RW;
+  const int ns = (nb + G - 1) / G;                       // steps per tile
+  const int my_tiles = wave < ntiles ? (ntiles - 1 - wave) / kP1Waves + 1 : 0;
+  const int F = my_tiles * ns;                           // steps of this wave
+
+  // buffer descriptors over this workgroup's rows
+  const uint32_t cbytes = (uint32_t)((int64_t)nrows * nb * CB);
+  const uint32_t sbytes = (uint32_t)((int64_t)nrows * nb * 2);
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.codes + row_begin * nb * CB), (short)0, (int)cbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.scales + row_begin * nb), (short)0, (int)sbytes, 0x00020000);
+  // lane part of the offsets (constant), per row r of the tile
+  uint32_t voc[R], vos[R];
+#pragma unroll
+  for (int r = 0; r < R; r++) {
+    voc[r] = ((uint32_t)lg * nb + g) * CB;  // the row r * GPW goes in the scalar offset
+    vos[r] = ((uint32_t)lg * nb + g) * 2;
+  }
+
+  Codes<FMT> ring_q[P][R];
+  uint32_t ring_d[P][R];
+  // Issue state (uniform): tile counter and step within the tile.  The lane offsets of the
+  // current tile (rows past the workgroup's range masked out) change once per tile.
+  int it = 0, ij = 0;
+  uint32_t vc[R], vs[R];
+  auto tile_offsets = [&]() {
+    const int trow = (wave + it * kP1Waves) * RW;
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+      const bool ok = trow + r * GPW + lg < nrows;  // out of range: reads 0
+      vc[r] = ok ? voc[r] : 0x80000000u;
+      vs[r] = ok ? vos[r] : 0x80000000u;
+    }
+  };
+  tile_offsets();
+  // Always loads: steps past this wave's last tile fall on rows past the workgroup's
+  // range, which are masked like any row past the end (they read zeros, unused).
+  auto issue = [&](Codes<FMT> (&q)[R], uint32_t (&d)[R]) {
+    const uint32_t trow = (uint32_t)((wave + it * kP1Waves) * RW);
+    const uint32_t sb = (uint32_t)(ij * G);
+    const uint32_t so = trow * nb + sb;
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+      uint32_t c = vc[r], e = vs[r];
+      if constexpr (RAGGED) {
+        if ((int)sb + g >= nb) { c = 0x80000000u; e = 0x80000000u; }
+      }
+      const uint32_t sr = so + (uint32_t)(r * GPW * nb);
+      if constexpr (FMT == FQ4) {
+        q[r].a = __builtin_amdgcn_raw_buffer_load_b128(rc, c, sr * CB, 0);
+      } else {
+        q[r].a = __builtin_amdgcn_raw_buffer_load_b128(rc, c, sr * CB, 0);
+        q[r].b = __builtin_amdgcn_raw_buffer_load_b128(rc, c + 16, sr * CB, 0);
+      }
+      d[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, e, sr * 2, 0);
+    }
+    if (++ij == ns) {
+      ij = 0;
+      ++it;
+      tile_offsets();
+    }
+  };
+
+  // start streaming before x is staged
+#pragma unroll
+  for (int p = 0; p < P; p++) issue(ring_q[p], ring_d[p]);
+
+  // ---- stage x (coalesced), then the block sums ----
+  {
+    char* lds = reinterpret_cast<char*>(smem);
+    const f32x4* x4 = reinterpret_cast<const f32x4*>(a.X);
+    for (int c = tid; c < nb * 8; c += kP1Threads) {
+      f32x4 v = x4[c];
+      const int b = c >> 3, i = c & 7;
+      if (FMT == FQ4 && i >= 4) v = v * 0.0625f;
+      *reinterpret_cast<f32x4*>(lds + b * kBlkLds + i * 16) = v;
+    }
+    __syncthreads();
+    for (int b = tid; b < nb; b += kP1Threads) {
+      const f32x4* xl = reinterpret_cast<const f32x4*>(lds + b * kBlkLds);
+      *reinterpret_cast<float*>(lds + b * kBlkLds + 128) = chain_xsum<FMT>(xl);
+    }
+    __syncthreads();
+  }
+
+  const char* lds_lane = reinterpret_cast<const char*>(smem) + g * kBlkLds;
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; r++) acc[r] = 0.f;
+  int ct = 0, cj = 0;  // consume state
+  for (int f0 = 0; f0 < F; f0 += P) {
+#pragma unroll
+    for (int p = 0; p < P; p++) {
+      if (f0 + p < F) {
+        const char* xb = lds_lane + cj * (G * kBlkLds);
+        if constexpr (RAGGED) {  // past K: reuse the last block; its d is 0, it adds exactly 0
+          if (cj * G + g >= nb) xb = reinterpret_cast<const char*>(smem) + (nb - 1) * kBlkLds;
+        }
+        const f32x4* xl = reinterpret_cast<const f32x4*>(xb);
+        const float sx = *reinterpret_cast<const float*>(xb + 128);
+#pragma unroll
+        for (int r = 0; r < R; r++) {
+          const float c = chain_m1<FMT>(ring_q[p][r], xl);
+          const float rr = fmaf(FMT == FQ4 ? -8.0f : -128.0f, sx, c);
+          acc[r] = fmaf(h2f(ring_d[p][r]), rr, acc[r]);
+        }
+        if (++cj == ns) {
+          // tile done: reduce over the lane group and store its rows
+          const int64_t trow = row_begin + (int64_t)(wave + ct * kP1Waves) * RW;
+#pragma unroll
+          for (int r = 0; r < R; r++) {
+            const float v = group_sum<G>(acc[r]);
+            const int64_t row = trow + r * GPW + lg;
+            if (g == 0 && row < row_end) a.Y[row] = v;
+            acc[r] = 0.f;
+          }
+          cj = 0;
+          ++ct;
+        }
+      }
+      issue(ring_q[p], ring_d[p]);  // refill the slot just consumed
+    }
+  }
+}
+
 // ---- expert-indexed GEMV -----------------------------------------------------------
 // Every workgroup first turns the T x top_k ids into per-expert slot lists in LDS (experts
 // ascending, slots ascending within an expert), split into passes of at most 8 slots.
@@ -536,6 +763,37 @@ QmvIdKernel select_id(int G, int R) {
   return select_id_r<FMT, 16>(R);
 }
 
+#ifndef BQM_P1_R
+#define BQM_P1_R 1  // rows per lane group in the persistent batch-1 kernel
+#endif
+#ifndef BQM_P1_P
+#define BQM_P1_P 4  // blocks in flight per lane and row (best of 4, 8, 12 measured)
+#endif
+constexpr int kP1MaxLds = 150 * 1024;
+
+using P1Kernel = void (*)(P1Args);
+
+template <int FMT, int G>
+P1Kernel select_p1(bool ragged) {
+  // same bytes in flight per lane for both formats (a Q8_0 block is twice as long)
+  constexpr int P = FMT == FQ4 ? BQM_P1_P : BQM_P1_P / 2;
+  if (ragged) return k_qmv1p<FMT, G, BQM_P1_R, P, true>;
+  return k_qmv1p<FMT, G, BQM_P1_R, P, false>;
+}
+
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 }  // namespace
 
 int launch_fill(float* y, int64_t n, float v, hipStream_t s) {
@@ -543,6 +801,27 @@ int launch_fill(float* y, int64_t n, float v, hipStream_t s) {
   const int64_t blocks = (n + kThreads - 1) / kThreads;
   hipLaunchKernelGGL(k_fill, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(kThreads), 0, s,
                      y, n, v);
+  return launch_status();
+}
+
+// Batch-1 product through the persistent kernel, when x fits in LDS; returns -1 if not.
+static int launch_qmv1p(int fmt, const uint8_t* codes, const uint16_t* scales, const float* X,
+                        float* Y, int64_t N, int64_t nb, hipStream_t s) {
+  const size_t lds = (size_t)nb * kBlkLds;
+  if (lds > (size_t)kP1MaxLds) return -1;
+  const int64_t grid = N < cu_count() ? N : cu_count();
+  const int64_t rows_per_wg = (N + grid - 1) / grid;
+  if (rows_per_wg * nb * (fmt == BQM_Q4_0 ? 16 : 32) >= ((int64_t)1 << 31)) return -1;
+  const int G = pick_group(nb);
+  const bool ragged = nb % G != 0;
+  P1Kernel k;
+  if (fmt == BQM_Q4_0)
+    k = G == 64 ? select_p1<FQ4, 64>(ragged) : G == 32 ? select_p1<FQ4, 32>(ragged) : select_p1<FQ4, 16>(ragged);
+  else
+    k = G == 64 ? select_p1<FQ8, 64>(ragged) : G == 32 ? select_p1<FQ8, 32>(ragged) : select_p1<FQ8, 16>(ragged);
+  allow_lds(k, lds);
+  P1Args a{codes, scales, X, Y, (int)N, (int)nb};
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kP1Threads), lds, s, a);
   return launch_status();
 }
 
@@ -554,6 +833,10 @@ int launch_qmv(int fmt, const void* w, const float* X, float* Y, int M, int64_t 
   layout_of(fmt, N, K, &L);
   const uint8_t* codes = static_cast<const uint8_t*>(w);
   const uint16_t* scales = reinterpret_cast<const uint16_t*>(codes + L.scales_off);
+  if (M == 1) {
+    const int st = launch_qmv1p(fmt, codes, scales, X, Y, N, L.nb, s);
+    if (st >= 0) return st;
+  }
   const int G = pick_group(L.nb);
   const int R = pick_rows(N, G, M);
   const int kcb = chunk_blocks(L.nb, M, kLdsBudget);

@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--M", type=int, default=1, help="batch for dense27b_q8_0 (1, 4 or 8)")
     ap.add_argument("--layers", type=int, default=64)
     ap.add_argument("--no-graph", action="store_true", help="eager launches instead of a graph")
+    ap.add_argument("--separate", action="store_true",
+                    help="one launch per GEMV (graph replay) instead of one chain launch per token")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     return ap.parse_args()
@@ -174,27 +176,45 @@ def run_dense(args, torch, gen, bqm, fmt="q4_0"):
     launches = [(lambda w=w, x=x, y=y, N=N, K=K: qmv(w, x, y, M, N, K))
                 for (w, N, K), x, y in zip(mats, xs, ys)]
 
-    def run():
+    def run_separate():
         for f in launches:
             f()
 
-    ms = time_steps(run, args.steps, args.warmup, torch, not args.no_graph)
     total = wbytes + abytes
+    per_bytes = np.array([weight_bytes(fmt, N, K) + 4 * M * (K + N) for _, N, K in mats])
+    use_chain = M == 1 and not args.separate
+    if use_chain:
+        # one launch per token: the 256 GEMVs in layer order, each waiting (device-wide)
+        # for all earlier ones, as a decode step's data dependencies require
+        descs = [bqm.gemv(fmt, w, x, y, N, K, wait=i > 0)
+                 for i, ((w, N, K), x, y) in enumerate(zip(mats, xs, ys))]
+        ws = torch.zeros(bqm.chain_workspace_bytes(len(descs)), dtype=torch.uint8, device="cuda")
+        bqm.bqm_chain_prepare(descs, ws)
+
+        def run():
+            bqm.qmv_chain(fmt, ws, len(descs))
+
+        ms = time_steps(run, args.steps, args.warmup, torch, False)
+        status = bqm.bqm_chain_status(ws)
+        if status != 0:
+            raise RuntimeError(f"chain reported error {status}")
+        dur = per_launch_ms([run], torch, reps=max(3, args.steps // 2))
+        achieved = total / (float(dur.mean()) * 1e-3) / 1e9
+        kernel = f"k_qmv_chain ({fmt.upper()}, {len(descs)} GEMVs per launch)"
+        launch_us = round(1e3 * float(dur.mean()), 3)
+        kkey = f"qmv_chain_{fmt}_dense27b"
+    else:
+        ms = time_steps(run_separate, args.steps, args.warmup, torch, not args.no_graph)
+        dur = per_launch_ms(launches, torch)
+        achieved = per_bytes.sum() / (dur.sum() * 1e-3) / 1e9
+        kernel = f"k_qmv ({fmt.upper()} M={M})"
+        launch_us = round(1e3 * float(dur.mean()), 3)
+        kkey = f"qmv_{fmt}_m{M}_dense27b"
     gbs = total / (ms * 1e-3) / 1e9
     say(f"step {ms:.3f} ms, {gbs:.1f} GB/s, {1e3 / ms:.1f} passes/s")
-    # eager timing of the same pass, for reference
-    ms_eager = time_steps(run, max(2, args.steps // 4), 1, torch, False) if not args.no_graph else ms
-    # per-launch durations of the dominant kernel (the GEMV; every launch of the step)
-    dur = per_launch_ms(launches, torch)
-    per_bytes = np.array([weight_bytes(fmt, N, K) + 4 * M * (K + N) for _, N, K in mats])
-    achieved = per_bytes.sum() / (dur.sum() * 1e-3) / 1e9
-    by_shape = {}
-    for (name, N, K), i in zip(shapes * args.layers, range(len(mats))):
-        by_shape.setdefault(name, []).append((per_bytes[i], dur[i]))
-    shape_gbs = {k: round(sum(b for b, _ in v) / (sum(d for _, d in v) * 1e-3) / 1e9, 1)
-                 for k, v in by_shape.items()}
-    shape_us = {k: round(1e3 * float(np.mean([d for _, d in v])), 2) for k, v in by_shape.items()}
-    kkey = f"qmv_{fmt}_m{M}_dense27b"
+    # the same pass as separate launches (graph replay), for reference
+    ms_sep = time_steps(run_separate, max(3, args.steps // 2), 1, torch, not args.no_graph) \
+        if use_chain else ms
     traffic = traffic_from_profiles(kkey)
     res = {
         "metric": "Q4_0 GEMV achieved HBM GB/s (% of peak) + equiv 27B decode tok/s"
@@ -206,16 +226,15 @@ def run_dense(args, torch, gen, bqm, fmt="q4_0"):
                                f"{args.layers} layers x (qkv 7168x5120, o 5120x5120, "
                                f"gate_up 34816x5120, down 5120x17408)",
                    "layers": args.layers, "gemv_launches_per_step": len(mats),
-                   "weight_bytes": wbytes, "activation_bytes": abytes, "hip_graph": not args.no_graph},
+                   "weight_bytes": wbytes, "activation_bytes": abytes,
+                   "launch": "one chain launch per token" if use_chain else
+                   ("HIP graph of separate launches" if not args.no_graph else "separate launches")},
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-        "equiv_tok_s": round(1e3 / ms * (1 if fmt == "q4_0" else 1), 2),
-        "eager_ms_per_step": round(ms_eager, 4),
+        "equiv_tok_s": round(1e3 / ms, 2),
+        "separate_launches_ms_per_step": round(ms_sep, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic,
-                     "kernel": f"k_qmv (Q4_0 M=1)" if fmt == "q4_0" else f"k_qmv (Q8_0 M={M})",
-                     "avg_launch_us": round(1e3 * float(dur.mean()), 3),
-                     "per_shape_gbs": shape_gbs, "per_shape_us": shape_us},
+                     "traffic": traffic, "kernel": kernel, "avg_launch_us": launch_us},
     }
     if fmt == "q8_0":
         res["equiv_tok_s_aggregate"] = round(M * 1e3 / ms, 2)

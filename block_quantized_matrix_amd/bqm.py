@@ -50,6 +50,13 @@ def lib():
         L.qmv_id.argtypes = [I, P, I, I64, I64, P, I, I, P, I64, I64, P, P]
         L.bqm_quantize_q8_act.argtypes = [P, P, P, I64, I64, P]
         L.qmm_q8_0.argtypes = [P, P, P, P, I64, I64, I64, P]
+        L.bqm_chain_workspace_bytes.argtypes = [I]
+        L.bqm_chain_workspace_bytes.restype = SZ
+        L.bqm_chain_prepare.argtypes = [P, I, P, P]
+        L.qmv_chain.argtypes = [I, P, I, P]
+        L.bqm_chain_status.argtypes = [P, P]
+        for f in ("bqm_chain_prepare", "qmv_chain", "bqm_chain_status"):
+            getattr(L, f).restype = I
         L.bqm_strerror.argtypes = [I]
         L.bqm_strerror.restype = ctypes.c_char_p
         for f in ("bqm_repack", "bqm_unpack", "qmv_q4_0", "qmv_q8_0", "qmv_id",
@@ -119,6 +126,40 @@ def bqm_quantize_q8_act(X, Xq, dx, M: int, K: int, stream=None):
 
 def qmm_q8_0(w_packed, Xq, dx, Y, M: int, N: int, K: int, stream=None):
     _call("qmm_q8_0", _ptr(w_packed), _ptr(Xq), _ptr(dx), _ptr(Y), M, N, K, _stream(stream))
+
+
+class Gemv(ctypes.Structure):
+    """One GEMV of a chain (the C struct bqm_gemv)."""
+    _fields_ = [("w_packed", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("fmt", ctypes.c_int32),
+                ("wait", ctypes.c_int32)]
+
+
+CHAIN_MAX_K = 32768
+
+
+def chain_workspace_bytes(n: int) -> int:
+    return int(lib().bqm_chain_workspace_bytes(n))
+
+
+def bqm_chain_prepare(descs, workspace, stream=None):
+    """descs: a sequence of Gemv (host memory); workspace: device tensor of
+    chain_workspace_bytes(len(descs)) bytes.  Synchronizes the stream."""
+    arr = (Gemv * len(descs))(*descs)
+    _call("bqm_chain_prepare", ctypes.cast(arr, ctypes.c_void_p), len(descs), _ptr(workspace),
+          _stream(stream))
+
+
+def qmv_chain(fmt, workspace, n: int, stream=None):
+    _call("qmv_chain", _fmt(fmt), _ptr(workspace), n, _stream(stream))
+
+
+def bqm_chain_status(workspace, stream=None) -> int:
+    return int(lib().bqm_chain_status(_ptr(workspace), _stream(stream)))
+
+
+def gemv(fmt, w_packed, x, y, N: int, K: int, wait: bool) -> Gemv:
+    return Gemv(w_packed.data_ptr(), x.data_ptr(), y.data_ptr(), N, K, _fmt(fmt), 1 if wait else 0)
 
 
 # ---- conveniences built only from the calls above (allocation through torch) ----

@@ -126,6 +126,28 @@ int qmm_q8_0(const void* w_packed, const int8_t* Xq, const float* dx, float* Y, 
   return launch_qmm_q8_0(w_packed, Xq, dx, Y, M, N, K, stream);
 }
 
+size_t bqm_chain_workspace_bytes(int n) { return chain_workspace_bytes(n); }
+
+int bqm_chain_prepare(const bqm_gemv* descs, int n, void* workspace, hipStream_t stream) {
+  if (n < 1 || n > (1 << 20)) return BQM_E_SHAPE;
+  if (!descs || !workspace) return BQM_E_NULL;
+  if (!aligned16(workspace)) return BQM_E_ALIGN;
+  return chain_prepare(descs, n, workspace, stream);
+}
+
+int qmv_chain(int fmt, void* workspace, int n, hipStream_t stream) {
+  if (!valid_fmt(fmt)) return BQM_E_UNSUPPORTED;
+  if (n < 1 || n > (1 << 20)) return BQM_E_SHAPE;
+  if (!workspace) return BQM_E_NULL;
+  if (!aligned16(workspace)) return BQM_E_ALIGN;
+  return chain_launch(fmt, workspace, n, stream);
+}
+
+int bqm_chain_status(const void* workspace, hipStream_t stream) {
+  if (!workspace) return -1;
+  return chain_status(workspace, stream);
+}
+
 const char* bqm_strerror(int status) {
   switch (status) {
     case BQM_OK: return "success";

@@ -322,13 +322,14 @@ __global__ __launch_bounds__(kThreads) void k_qmv(const uint8_t* __restrict__ co
   tile_qmv<FMT, MM, G, R>(codes, scales, nb, row_base, nrows, X, Y, &io, M, smem, kcb);
 }
 
-// ---- persistent batch-1 GEMV ------------------------------------------------------
+// ---- persistent batch-1 GEMV chain ------------------------------------------------
 // The batch-1 product is the bandwidth-critical one, so it gets its own kernel shaped
-// around the VALU budget (Q4_0 at 8 TB/s delivers 14.2 T weights/s against 39.3 T fp32
-// lane-ops/s, about 2.8 ops per weight):
-//  - One 1024-thread workgroup per CU (grid = CU count) owns a contiguous range of rows
-//    and stages x into LDS once.  Blocks are 144 bytes apart in LDS: 128 bytes of x,
-//    then the block's x sum; with that stride eight neighbouring blocks start in eight
+// around the VALU budget and around the cost of starting a kernel (Q4_0 at 8 TB/s delivers
+// 14.2 T weights/s against 39.3 T fp32 lane-ops/s, about 2.8 ops per weight).  One launch
+// runs a chain of GEMVs in order (a single GEMV is a chain of one):
+//  - One 1024-thread workgroup per CU owns, for each GEMV, a contiguous range of rows and
+//    stages that GEMV's x into LDS once.  Blocks are 144 bytes apart in LDS: 128 bytes of
+//    x, then the block's x sum; with that stride eight neighbouring blocks start in eight
 //    different 16-byte bank groups, so the per-lane block reads are conflict-free with
 //    immediate offsets.  For Q4_0 the x values that meet the high nibbles are stored
 //    divided by 16 (exact), so one FMA chain takes the nibbles in place (16 n * x / 16).
@@ -336,11 +337,13 @@ __global__ __launch_bounds__(kThreads) void k_qmv(const uint8_t* __restrict__ co
 //    constant register, the per-step part a scalar, so a load costs no VALU address
 //    arithmetic.  Lanes past the workgroup's last row (or past K in a ragged last step)
 //    use an offset beyond the descriptor and read zeros.
-//  - Each lane keeps P blocks (per row) in flight in a register ring that is consumed in
-//    place (the loop is unrolled by P).
-//  - The waves of the workgroup take tiles of (64/G)*R rows round-robin; a lane group
-//    reduces and stores a row when its last block is done.
-// Arithmetic per block and row: 8 ANDs, 32 v_cvt_f32_ubyte, 32 FMAs, then
+//  - Each lane keeps P blocks in flight in a register ring consumed in place (the loop is
+//    unrolled by P).  The ring runs ahead across GEMV boundaries: the weights of the next
+//    GEMV do not depend on its input, so they stream while the workgroup waits for the
+//    previous GEMV's outputs (device-wide barrier) and stages the new x.
+//  - The waves of a workgroup take tiles of 64/G rows round-robin; a lane group reduces
+//    and stores a row when its last block is done.
+// Arithmetic per block and row: 8 ANDs, 32 v_cvt_f32_ubyte, 32 FMAs in one chain, then
 // r = chain - 8 * sum(x) (Q8_0: - 128 * sum(x)) and acc += d * r (v_fma_mix: d stays fp16).
 // The chain and the block sum follow the same order and 8, 128 and 1/16 are powers of
 // two, so neutral codes give exactly zero.
@@ -348,27 +351,37 @@ constexpr int kP1Threads = 1024;
 constexpr int kP1Waves = kP1Threads / 64;
 constexpr int kBlkLds = 144;  // LDS bytes per staged block
 
+// Chain order of one block: positions 0..15 (low nibbles / first 16 bytes), then 16..31.
 template <int FMT>
 __device__ __forceinline__ float chain_m1(const Codes<FMT>& q, const f32x4* __restrict__ xl) {
   // xl: the staged block (8 chunks of 4 floats), Q4_0 chunks 4..7 already divided by 16
   float acc;
   if constexpr (FMT == FQ4) {
+    uint32_t l[4], h[4];
     const uint32_t w[4] = {q.a.x, q.a.y, q.a.z, q.a.w};
 #pragma unroll
     for (int k = 0; k < 4; k++) {
-      uint32_t l = w[k] & 0x0F0F0F0Fu, h = w[k] & 0xF0F0F0F0u;
-      asm("" : "+v"(l), "+v"(h));  // keep the byte conversions as v_cvt_f32_ubyte{0..3}
-      const f32x4 a = xl[k], b = xl[k + 4];
-      if (k == 0) acc = ub(l, 0) * a.x; else acc = fmaf(ub(l, 0), a.x, acc);
-      acc = fmaf(ub(l, 1), a.y, acc); acc = fmaf(ub(l, 2), a.z, acc); acc = fmaf(ub(l, 3), a.w, acc);
-      acc = fmaf(ub(h, 0), b.x, acc); acc = fmaf(ub(h, 1), b.y, acc);
-      acc = fmaf(ub(h, 2), b.z, acc); acc = fmaf(ub(h, 3), b.w, acc);
+      l[k] = w[k] & 0x0F0F0F0Fu;
+      h[k] = w[k] & 0xF0F0F0F0u;  // 16 * high nibble, in place
+      asm("" : "+v"(l[k]), "+v"(h[k]));  // keep the conversions as v_cvt_f32_ubyte{0..3}
+    }
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      const f32x4 a = xl[k];
+      if (k == 0) acc = ub(l[k], 0) * a.x; else acc = fmaf(ub(l[k], 0), a.x, acc);
+      acc = fmaf(ub(l[k], 1), a.y, acc); acc = fmaf(ub(l[k], 2), a.z, acc); acc = fmaf(ub(l[k], 3), a.w, acc);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      const f32x4 b = xl[k + 4];
+      acc = fmaf(ub(h[k], 0), b.x, acc); acc = fmaf(ub(h[k], 1), b.y, acc);
+      acc = fmaf(ub(h[k], 2), b.z, acc); acc = fmaf(ub(h[k], 3), b.w, acc);
     }
   } else {
     const uint32_t w[8] = {q.a.x, q.a.y, q.a.z, q.a.w, q.b.x, q.b.y, q.b.z, q.b.w};
 #pragma unroll
     for (int k = 0; k < 8; k++) {
-      uint32_t u = w[k] ^ 0x80808080u;
+      uint32_t u = w[k] ^ 0x80808080u;  // q + 128 as unsigned bytes
       asm("" : "+v"(u));
       const f32x4 a = xl[k];
       if (k == 0) acc = ub(u, 0) * a.x; else acc = fmaf(ub(u, 0), a.x, acc);
@@ -378,172 +391,306 @@ __device__ __forceinline__ float chain_m1(const Codes<FMT>& q, const f32x4* __re
   return acc;
 }
 
-// Block sum of the staged x in the order chain_m1 consumes it.
-template <int FMT>
-__device__ __forceinline__ float chain_xsum(const f32x4* __restrict__ xl) {
-  float s;
-  if constexpr (FMT == FQ4) {
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-      const f32x4 a = xl[k], b = xl[k + 4];
-      if (k == 0) s = a.x; else s = s + a.x;
-      s = s + a.y; s = s + a.z; s = s + a.w;
-      s = s + b.x * 16.0f; s = s + b.y * 16.0f; s = s + b.z * 16.0f; s = s + b.w * 16.0f;
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < 8; k++) {
-      const f32x4 a = xl[k];
-      if (k == 0) s = a.x; else s = s + a.x;
-      s = s + a.y; s = s + a.z; s = s + a.w;
-    }
-  }
-  return s;
-}
+// Description of one GEMV of a chain (the device image of bqm_gemv).
+struct GemvDesc {
+  const uint8_t* w;
+  const float* x;
+  float* y;
+  int64_t N, K;
+  int32_t fmt, wait;
+};
+static_assert(sizeof(GemvDesc) == sizeof(bqm_gemv), "bqm_gemv layout");
 
-struct P1Args {
-  const uint8_t* codes;     // packed code section of the whole matrix
-  const uint16_t* scales;   // packed scale section
-  const float* X;           // [K]
-  float* Y;                 // [N]
-  int N, nb;
+struct ChainArgs {
+  const GemvDesc* descs;  // n descriptors in device memory, or null: use `one`
+  GemvDesc one;
+  int n;
+  uint32_t* sync;         // device-wide barrier words {count, generation, error}; null if n == 1
 };
 
-template <int FMT, int G, int R, int P, bool RAGGED>
-__global__ __launch_bounds__(kP1Threads) void k_qmv1p(P1Args a) {
+// Per-GEMV values of one workgroup, computed once at kernel start (one thread per GEMV)
+// into a table in LDS, so moving to the next GEMV costs a few LDS reads.
+struct StageRow {
+  const uint8_t* codes;     // this workgroup's first row of codes
+  const uint16_t* scales;   // ... and of scales
+  const float* x;
+  float* y;                 // this workgroup's first output row
+  int32_t nrows;            // rows of this workgroup
+  int32_t nb;               // blocks per row
+  int32_t info;             // lg2(G) | ragged << 8 | wait << 9
+  int32_t ns;               // steps per tile (blocks per lane)
+};
+static_assert(sizeof(StageRow) == 48, "stage table row");
+
+template <int FMT>
+__device__ __forceinline__ StageRow make_stage(const GemvDesc& d) {
+  constexpr int CB = FMT == FQ4 ? 16 : 32;
+  const int nb = (int)(d.K >> 5);
+  const int N = (int)d.N;
+  // lane group: the width among 64/32/16 that leaves the fewest idle lanes in a row
+  const int w64 = (-nb) & 63, w32 = (-nb) & 31, w16 = (-nb) & 15;
+  int lg2 = 6;
+  if (w32 < w64) lg2 = 5;
+  if (w16 < (lg2 == 6 ? w64 : w32)) lg2 = 4;
+  const int G = 1 << lg2;
+  // rows split as evenly as possible: the first N % grid workgroups get one more
+  const int grid = (int)gridDim.x, b = (int)blockIdx.x;
+  const int base = N / grid, extra = N - base * grid;
+  const int r0 = b * base + (b < extra ? b : extra);
+  const int64_t code_bytes = (int64_t)N * nb * CB;
+  StageRow st;
+  st.codes = d.w + (int64_t)r0 * nb * CB;
+  st.scales = reinterpret_cast<const uint16_t*>(d.w + ((code_bytes + 255) & ~int64_t(255))) +
+              (int64_t)r0 * nb;
+  st.x = d.x;
+  st.y = d.y + r0;
+  st.nrows = base + (b < extra ? 1 : 0);
+  st.nb = nb;
+  st.info = lg2 | ((nb & (G - 1)) != 0 ? 1 << 8 : 0) | (d.wait ? 1 << 9 : 0);
+  st.ns = (nb + G - 1) >> lg2;
+  return st;
+}
+
+// Uniform copy of a table row (LDS reads made scalar).
+struct Stage {
+  const uint8_t* codes;
+  const uint16_t* scales;
+  const float* x;
+  float* y;
+  int nrows, nb, lg2G, G, gpw, ns, my_tiles;
+  bool ragged, wait;
+};
+
+// __builtin_amdgcn_readfirstlane is 32 bits wide: a 64-bit value takes two.
+__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ void load_stage(const StageRow* t, int i, int wave, Stage& s) {
+  const StageRow r = t[i];
+  s.codes = reinterpret_cast<const uint8_t*>(uniform64(reinterpret_cast<uint64_t>(r.codes)));
+  s.scales = reinterpret_cast<const uint16_t*>(uniform64(reinterpret_cast<uint64_t>(r.scales)));
+  s.x = reinterpret_cast<const float*>(uniform64(reinterpret_cast<uint64_t>(r.x)));
+  s.y = reinterpret_cast<float*>(uniform64(reinterpret_cast<uint64_t>(r.y)));
+  s.nrows = __builtin_amdgcn_readfirstlane(r.nrows);
+  s.nb = __builtin_amdgcn_readfirstlane(r.nb);
+  const int info = __builtin_amdgcn_readfirstlane(r.info);
+  s.ns = __builtin_amdgcn_readfirstlane(r.ns);
+  s.lg2G = info & 0xff;
+  s.G = 1 << s.lg2G;
+  s.gpw = 64 >> s.lg2G;
+  s.ragged = (info >> 8) & 1;
+  s.wait = (info >> 9) & 1;
+  const int ntiles = (s.nrows + s.gpw - 1) >> (6 - s.lg2G);
+  s.my_tiles = wave < ntiles ? ((ntiles - 1 - wave) >> 4) + 1 : 0;  // 16 waves
+}
+
+// Device-wide barrier; thread 0 of each workgroup arrives.  The spin is bounded: on timeout
+// the error word is set and every workgroup leaves (the chain's results are then invalid).
+__device__ __forceinline__ bool grid_barrier(uint32_t* sync, bool* lds_ok) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    bool ok = true;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // this workgroup's outputs, visible
+    const uint32_t gen0 = __hip_atomic_load(sync + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t arrived =
+        __hip_atomic_fetch_add(sync, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (arrived == gridDim.x - 1) {
+      __hip_atomic_store(sync, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(sync + 1, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      uint32_t spins = 0;
+      // relaxed polls (an acquire per poll would invalidate this XCD's L2 every time);
+      // the acquire fence below orders the reads that follow
+      while (__hip_atomic_load(sync + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen0) {
+        if (++spins > (1u << 24) ||
+            __hip_atomic_load(sync + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+          __hip_atomic_store(sync + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ok = false;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // other workgroups' outputs
+    *lds_ok = ok;
+  }
+  __syncthreads();
+  return *lds_ok;
+}
+
+template <int FMT, int P>
+__global__ __launch_bounds__(kP1Threads) void k_qmv_chain(ChainArgs a) {
   extern __shared__ float4 smem[];
   constexpr int CB = FMT == FQ4 ? 16 : 32;     // code bytes per block
-  constexpr int GPW = 64 / G;                  // lane groups per wave
-  constexpr int RW = GPW * R;                  // rows per wave tile
-  const int nb = a.nb;
+  __shared__ bool lds_ok;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep in SGPRs
-  const int g = lane % G, lg = lane / G;
-  const int64_t row_begin = (int64_t)blockIdx.x * a.N / gridDim.x;
-  const int64_t row_end = (int64_t)(blockIdx.x + 1) * a.N / gridDim.x;
-  const int nrows = (int)(row_end - row_begin);
-  const int ntiles = (nrows + RW - 1) / RW;
-  const int ns = (nb + G - 1) / G;                       // steps per tile
-  const int my_tiles = wave < ntiles ? (ntiles - 1 - wave) / kP1Waves + 1 : 0;
-  const int F = my_tiles * ns;                           // steps of this wave
-
-  // buffer descriptors over this workgroup's rows
-  const uint32_t cbytes = (uint32_t)((int64_t)nrows * nb * CB);
-  const uint32_t sbytes = (uint32_t)((int64_t)nrows * nb * 2);
-  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.codes + row_begin * nb * CB), (short)0, (int)cbytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.scales + row_begin * nb), (short)0, (int)sbytes, 0x00020000);
-  // lane part of the offsets (constant), per row r of the tile
-  uint32_t voc[R], vos[R];
-#pragma unroll
-  for (int r = 0; r < R; r++) {
-    voc[r] = ((uint32_t)lg * nb + g) * CB;  // the row r * GPW goes in the scalar offset
-    vos[r] = ((uint32_t)lg * nb + g) * 2;
+  if (a.sync && (a.sync[3] != (uint32_t)a.n || a.sync[4] != (uint32_t)(FMT == FQ4 ? BQM_Q4_0 : BQM_Q8_0))) {
+    // the workspace was prepared for another chain: flag it, compute nothing
+    if (blockIdx.x == 0 && tid == 0)
+      __hip_atomic_store(a.sync + 2, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
   }
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep in SGPRs
+  // LDS: the stage table, then the staged x
+  StageRow* table = reinterpret_cast<StageRow*>(smem);
+  char* xlds = reinterpret_cast<char*>(smem) + ((a.n * (int)sizeof(StageRow) + 15) & ~15);
+  for (int i = tid; i < a.n; i += kP1Threads) table[i] = make_stage<FMT>(a.descs ? a.descs[i] : a.one);
+  __syncthreads();
 
-  Codes<FMT> ring_q[P][R];
-  uint32_t ring_d[P][R];
-  // Issue state (uniform): tile counter and step within the tile.  The lane offsets of the
-  // current tile (rows past the workgroup's range masked out) change once per tile.
-  int it = 0, ij = 0;
-  uint32_t vc[R], vs[R];
-  auto tile_offsets = [&]() {
-    const int trow = (wave + it * kP1Waves) * RW;
-#pragma unroll
-    for (int r = 0; r < R; r++) {
-      const bool ok = trow + r * GPW + lg < nrows;  // out of range: reads 0
-      vc[r] = ok ? voc[r] : 0x80000000u;
-      vs[r] = ok ? vos[r] : 0x80000000u;
+  // ---------------- issue side: runs P steps ahead, across GEMVs ----------------
+  int gi = 0, it = 0, ij = 0;
+  Stage si;
+  __amdgpu_buffer_rsrc_t rc, rs;
+  uint32_t vc = 0x80000000u, vs = 0x80000000u;
+  int ig = 0, ilg = 0;
+  // next (gi, tile) with work for this wave; sets up descriptors and lane offsets
+  auto issue_tile = [&]() {
+    while (gi < a.n && it >= si.my_tiles) {
+      if (++gi < a.n) {
+        load_stage(table, gi, wave, si);
+        it = 0;
+        rc = __builtin_amdgcn_make_buffer_rsrc((void*)si.codes, (short)0,
+                                               (int)((uint32_t)si.nrows * si.nb * CB), 0x00020000);
+        rs = __builtin_amdgcn_make_buffer_rsrc((void*)si.scales, (short)0,
+                                               (int)((uint32_t)si.nrows * si.nb * 2), 0x00020000);
+        ig = lane & (si.G - 1);
+        ilg = lane >> si.lg2G;
+      }
+    }
+    if (gi < a.n) {
+      const int trow = (wave + it * kP1Waves) * si.gpw;
+      const bool ok = trow + ilg < si.nrows;  // rows past the range read zeros
+      vc = ok ? ((uint32_t)ilg * si.nb + ig) * CB : 0x80000000u;
+      vs = ok ? ((uint32_t)ilg * si.nb + ig) * 2 : 0x80000000u;
     }
   };
-  tile_offsets();
-  // Always loads: steps past this wave's last tile fall on rows past the workgroup's
-  // range, which are masked like any row past the end (they read zeros, unused).
-  auto issue = [&](Codes<FMT> (&q)[R], uint32_t (&d)[R]) {
-    const uint32_t trow = (uint32_t)((wave + it * kP1Waves) * RW);
-    const uint32_t sb = (uint32_t)(ij * G);
-    const uint32_t so = trow * nb + sb;
-#pragma unroll
-    for (int r = 0; r < R; r++) {
-      uint32_t c = vc[r], e = vs[r];
-      if constexpr (RAGGED) {
-        if ((int)sb + g >= nb) { c = 0x80000000u; e = 0x80000000u; }
-      }
-      const uint32_t sr = so + (uint32_t)(r * GPW * nb);
+  gi = -1;
+  si.my_tiles = 0;
+  issue_tile();
+
+  auto issue = [&](Codes<FMT>& q, uint32_t& d) {
+    if (gi < a.n) {
+      const uint32_t trow = (uint32_t)((wave + it * kP1Waves) * si.gpw);
+      const uint32_t so = trow * si.nb + (uint32_t)(ij << si.lg2G);
+      uint32_t c = vc, e = vs;
+      if (si.ragged && (ij << si.lg2G) + ig >= si.nb) { c = 0x80000000u; e = 0x80000000u; }
       if constexpr (FMT == FQ4) {
-        q[r].a = __builtin_amdgcn_raw_buffer_load_b128(rc, c, sr * CB, 0);
+        q.a = __builtin_amdgcn_raw_buffer_load_b128(rc, c, so * CB, 0);
       } else {
-        q[r].a = __builtin_amdgcn_raw_buffer_load_b128(rc, c, sr * CB, 0);
-        q[r].b = __builtin_amdgcn_raw_buffer_load_b128(rc, c + 16, sr * CB, 0);
+        q.a = __builtin_amdgcn_raw_buffer_load_b128(rc, c, so * CB, 0);
+        q.b = __builtin_amdgcn_raw_buffer_load_b128(rc, c + 16, so * CB, 0);
       }
-      d[r] = __builtin_amdgcn_raw_buffer_load_b16(rs, e, sr * 2, 0);
-    }
-    if (++ij == ns) {
-      ij = 0;
-      ++it;
-      tile_offsets();
+      d = __builtin_amdgcn_raw_buffer_load_b16(rs, e, so * 2, 0);
+      if (++ij == si.ns) {
+        ij = 0;
+        ++it;
+        issue_tile();
+      }
     }
   };
 
-  // start streaming before x is staged
+  Codes<FMT> ring_q[P];
+  uint32_t ring_d[P];
 #pragma unroll
   for (int p = 0; p < P; p++) issue(ring_q[p], ring_d[p]);
 
-  // ---- stage x (coalesced), then the block sums ----
-  {
-    char* lds = reinterpret_cast<char*>(smem);
-    const f32x4* x4 = reinterpret_cast<const f32x4*>(a.X);
-    for (int c = tid; c < nb * 8; c += kP1Threads) {
+  // ---------------- consume side ----------------
+  int gc = -1, ct = 0, cj = 0, csteps = 0;  // GEMV, tile, step in tile, steps left
+  Stage sc;
+  const char* lds_lane = xlds;
+  int cg = 0, clg = 0;
+  float acc = 0.f;
+  bool alive = true;
+  // Enter the next GEMV: all waves finished reading the staged x, wait for earlier outputs
+  // if asked, stage the new x.  Every wave calls this once per GEMV, in order.
+  auto enter = [&]() {
+    ++gc;
+    load_stage(table, gc, wave, sc);
+    ct = 0;
+    cj = 0;
+    csteps = sc.my_tiles * sc.ns;
+    cg = lane & (sc.G - 1);
+    clg = lane >> sc.lg2G;
+    __syncthreads();
+    if (sc.wait && gc > 0 && a.sync) alive = grid_barrier(a.sync, &lds_ok);
+    const f32x4* x4 = reinterpret_cast<const f32x4*>(sc.x);
+    for (int c = tid; c < sc.nb * 8; c += kP1Threads) {
       f32x4 v = x4[c];
-      const int b = c >> 3, i = c & 7;
+      const int blk = c >> 3, i = c & 7;
       if (FMT == FQ4 && i >= 4) v = v * 0.0625f;
-      *reinterpret_cast<f32x4*>(lds + b * kBlkLds + i * 16) = v;
+      *reinterpret_cast<f32x4*>(xlds + blk * kBlkLds + i * 16) = v;
     }
     __syncthreads();
-    for (int b = tid; b < nb; b += kP1Threads) {
-      const f32x4* xl = reinterpret_cast<const f32x4*>(lds + b * kBlkLds);
-      *reinterpret_cast<float*>(lds + b * kBlkLds + 128) = chain_xsum<FMT>(xl);
-    }
-    __syncthreads();
-  }
-
-  const char* lds_lane = reinterpret_cast<const char*>(smem) + g * kBlkLds;
-  float acc[R];
+    // block sums in chain order (positions 0..31; Q4_0 positions 16..31 are stored / 16)
+    for (int blk = tid; blk < sc.nb; blk += kP1Threads) {
+      const f32x4* xl = reinterpret_cast<const f32x4*>(xlds + blk * kBlkLds);
+      float s = xl[0].x;
+      s = s + xl[0].y; s = s + xl[0].z; s = s + xl[0].w;
 #pragma unroll
-  for (int r = 0; r < R; r++) acc[r] = 0.f;
-  int ct = 0, cj = 0;  // consume state
-  for (int f0 = 0; f0 < F; f0 += P) {
+      for (int k = 1; k < 4; k++) { s = s + xl[k].x; s = s + xl[k].y; s = s + xl[k].z; s = s + xl[k].w; }
+      const float m = FMT == FQ4 ? 16.0f : 1.0f;
+#pragma unroll
+      for (int k = 4; k < 8; k++) {
+        s = s + xl[k].x * m; s = s + xl[k].y * m; s = s + xl[k].z * m; s = s + xl[k].w * m;
+      }
+      *reinterpret_cast<float*>(xlds + blk * kBlkLds + 128) = s;
+    }
+    __syncthreads();
+    lds_lane = xlds + cg * kBlkLds;
+  };
+
+  // Rotate the ring so that slot k becomes slot 0 (at a GEMV boundary, where the steps of
+  // the finished GEMV ended in the middle of the unrolled group).
+  auto rotate = [&](int k) {
+    Codes<FMT> tq[P];
+    uint32_t td[P];
+#pragma unroll
+    for (int r = 1; r < P; r++) {
+      if (k == r) {
+#pragma unroll
+        for (int i = 0; i < P; i++) { tq[i] = ring_q[(i + r) % P]; td[i] = ring_d[(i + r) % P]; }
+#pragma unroll
+        for (int i = 0; i < P; i++) { ring_q[i] = tq[i]; ring_d[i] = td[i]; }
+      }
+    }
+  };
+
+  enter();
+  while (alive) {
+    int used = P;
 #pragma unroll
     for (int p = 0; p < P; p++) {
-      if (f0 + p < F) {
-        const char* xb = lds_lane + cj * (G * kBlkLds);
-        if constexpr (RAGGED) {  // past K: reuse the last block; its d is 0, it adds exactly 0
-          if (cj * G + g >= nb) xb = reinterpret_cast<const char*>(smem) + (nb - 1) * kBlkLds;
-        }
+      if (csteps == 0) {  // uniform: this GEMV is done for this wave
+        if (used == P) used = p;
+      } else {
+        const char* xb = lds_lane + cj * (sc.G * kBlkLds);
+        if (sc.ragged && cj * sc.G + cg >= sc.nb)  // past K: reuse the last block; its d is 0
+          xb = xlds + (sc.nb - 1) * kBlkLds;
         const f32x4* xl = reinterpret_cast<const f32x4*>(xb);
         const float sx = *reinterpret_cast<const float*>(xb + 128);
-#pragma unroll
-        for (int r = 0; r < R; r++) {
-          const float c = chain_m1<FMT>(ring_q[p][r], xl);
-          const float rr = fmaf(FMT == FQ4 ? -8.0f : -128.0f, sx, c);
-          acc[r] = fmaf(h2f(ring_d[p][r]), rr, acc[r]);
-        }
-        if (++cj == ns) {
-          // tile done: reduce over the lane group and store its rows
-          const int64_t trow = row_begin + (int64_t)(wave + ct * kP1Waves) * RW;
-#pragma unroll
-          for (int r = 0; r < R; r++) {
-            const float v = group_sum<G>(acc[r]);
-            const int64_t row = trow + r * GPW + lg;
-            if (g == 0 && row < row_end) a.Y[row] = v;
-            acc[r] = 0.f;
-          }
+        const float c = chain_m1<FMT>(ring_q[p], xl);
+        const float rr = fmaf(FMT == FQ4 ? -8.0f : -128.0f, sx, c);
+        acc = fmaf(h2f(ring_d[p]), rr, acc);
+        --csteps;
+        if (++cj == sc.ns) {  // tile done: reduce over the lane group, store its row
+          float v = acc;
+          for (int off = sc.G >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+          const int row = (wave + ct * kP1Waves) * sc.gpw + clg;
+          if (cg == 0 && row < sc.nrows) sc.y[row] = v;
+          acc = 0.f;
           cj = 0;
           ++ct;
         }
+        issue(ring_q[p], ring_d[p]);  // refill the slot just consumed
       }
-      issue(ring_q[p], ring_d[p]);  // refill the slot just consumed
+    }
+    if (csteps == 0) {
+      if (used != P && used != 0) rotate(used);
+      if (gc + 1 >= a.n) break;
+      enter();
     }
   }
 }
@@ -763,22 +910,15 @@ QmvIdKernel select_id(int G, int R) {
   return select_id_r<FMT, 16>(R);
 }
 
-#ifndef BQM_P1_R
-#define BQM_P1_R 1  // rows per lane group in the persistent batch-1 kernel
-#endif
 #ifndef BQM_P1_P
-#define BQM_P1_P 4  // blocks in flight per lane and row (best of 4, 8, 12 measured)
+#define BQM_P1_P 4  // blocks in flight per lane (Q4_0; Q8_0 blocks are twice as long: half)
 #endif
-constexpr int kP1MaxLds = 150 * 1024;
+constexpr int kP1MaxLds = 160 * 1024 - 256;  // a CU's LDS, less the kernel's static LDS
 
-using P1Kernel = void (*)(P1Args);
+using ChainKernel = void (*)(ChainArgs);
 
-template <int FMT, int G>
-P1Kernel select_p1(bool ragged) {
-  // same bytes in flight per lane for both formats (a Q8_0 block is twice as long)
-  constexpr int P = FMT == FQ4 ? BQM_P1_P : BQM_P1_P / 2;
-  if (ragged) return k_qmv1p<FMT, G, BQM_P1_R, P, true>;
-  return k_qmv1p<FMT, G, BQM_P1_R, P, false>;
+ChainKernel chain_kernel(int fmt) {
+  return fmt == BQM_Q4_0 ? k_qmv_chain<FQ4, BQM_P1_P> : k_qmv_chain<FQ8, BQM_P1_P / 2>;
 }
 
 int cu_count() {
@@ -804,25 +944,84 @@ int launch_fill(float* y, int64_t n, float v, hipStream_t s) {
   return launch_status();
 }
 
-// Batch-1 product through the persistent kernel, when x fits in LDS; returns -1 if not.
-static int launch_qmv1p(int fmt, const uint8_t* codes, const uint16_t* scales, const float* X,
-                        float* Y, int64_t N, int64_t nb, hipStream_t s) {
-  const size_t lds = (size_t)nb * kBlkLds;
-  if (lds > (size_t)kP1MaxLds) return -1;
-  const int64_t grid = N < cu_count() ? N : cu_count();
-  const int64_t rows_per_wg = (N + grid - 1) / grid;
-  if (rows_per_wg * nb * (fmt == BQM_Q4_0 ? 16 : 32) >= ((int64_t)1 << 31)) return -1;
-  const int G = pick_group(nb);
-  const bool ragged = nb % G != 0;
-  P1Kernel k;
-  if (fmt == BQM_Q4_0)
-    k = G == 64 ? select_p1<FQ4, 64>(ragged) : G == 32 ? select_p1<FQ4, 32>(ragged) : select_p1<FQ4, 16>(ragged);
-  else
-    k = G == 64 ? select_p1<FQ8, 64>(ragged) : G == 32 ? select_p1<FQ8, 32>(ragged) : select_p1<FQ8, 16>(ragged);
-  allow_lds(k, lds);
-  P1Args a{codes, scales, X, Y, (int)N, (int)nb};
-  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kP1Threads), lds, s, a);
+// Largest K a chain GEMV may have: its staged x must fit the LDS of one workgroup.
+int64_t chain_max_k() { return 32768; }
+
+// LDS a chain of n GEMVs needs: its stage table, then x of its longest GEMV.
+int64_t chain_lds_bytes(int n, int64_t max_k) {
+  return (((int64_t)n * (int64_t)sizeof(StageRow) + 15) & ~int64_t(15)) + (max_k / kQK) * kBlkLds;
+}
+
+// Launch a chain (descriptors in device memory, or `one` when descs is null).
+int launch_chain(int fmt, const GemvDesc* descs, const GemvDesc* one, int n, uint32_t* sync,
+                 hipStream_t s) {
+  ChainArgs a;
+  a.descs = descs;
+  if (one) a.one = *one; else a.one = GemvDesc{nullptr, nullptr, nullptr, 0, 0, fmt, 0};
+  a.n = n;
+  a.sync = sync;
+  ChainKernel k = chain_kernel(fmt);
+  allow_lds(k, kP1MaxLds);
+  const int grid = cu_count();
+  if (sync) {
+    // workgroups wait for each other: they must all be resident at once
+    void* args[] = {&a};
+    if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k), dim3(grid), dim3(kP1Threads), args,
+                                   kP1MaxLds, s) != hipSuccess)
+      return BQM_E_LAUNCH;
+    return launch_status();
+  }
+  hipLaunchKernelGGL(k, dim3(grid), dim3(kP1Threads), kP1MaxLds, s, a);
   return launch_status();
+}
+
+// ---- chain API: workspace = {count, generation, error, n, fmt} words, then descriptors
+constexpr int64_t kChainHeader = 256;
+
+size_t chain_workspace_bytes(int n) {
+  return n < 1 ? 0 : (size_t)(kChainHeader + (int64_t)n * (int64_t)sizeof(GemvDesc));
+}
+
+int chain_prepare(const bqm_gemv* descs, int n, void* ws, hipStream_t s) {
+  const int fmt = descs[0].fmt;
+  if (fmt != BQM_Q4_0 && fmt != BQM_Q8_0) return BQM_E_UNSUPPORTED;
+  const int CB = fmt == BQM_Q4_0 ? 16 : 32;
+  const int cus = cu_count();
+  int64_t max_k = 0;
+  for (int i = 0; i < n; i++) max_k = descs[i].K > max_k ? descs[i].K : max_k;
+  if (chain_lds_bytes(n, max_k) > kP1MaxLds) return BQM_E_SHAPE;
+  for (int i = 0; i < n; i++) {
+    const bqm_gemv& d = descs[i];
+    if (d.fmt != fmt) return BQM_E_UNSUPPORTED;
+    if (d.N < 1 || d.N > ((int64_t)1 << 30) || d.K < kQK || d.K % kQK != 0 || d.K > chain_max_k())
+      return BQM_E_SHAPE;
+    if (((d.N + cus - 1) / cus + 1) * (d.K / kQK) * CB >= ((int64_t)1 << 31)) return BQM_E_SHAPE;
+    if (!d.w_packed || !d.x || !d.y) return BQM_E_NULL;
+    if (((uintptr_t)d.w_packed & 15) || ((uintptr_t)d.x & 15) || ((uintptr_t)d.y & 3))
+      return BQM_E_ALIGN;
+  }
+  static const uint32_t zero_words[kChainHeader / 4] = {0};
+  uint32_t head[8] = {0, 0, 0, (uint32_t)n, (uint32_t)fmt, 0, 0, 0};
+  if (hipMemcpyAsync(ws, zero_words, kChainHeader, hipMemcpyHostToDevice, s) != hipSuccess ||
+      hipMemcpyAsync(ws, head, sizeof(head), hipMemcpyHostToDevice, s) != hipSuccess ||
+      hipMemcpyAsync(static_cast<char*>(ws) + kChainHeader, descs, (size_t)n * sizeof(GemvDesc),
+                     hipMemcpyHostToDevice, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return BQM_E_LAUNCH;
+  return BQM_OK;
+}
+
+int chain_launch(int fmt, void* ws, int n, hipStream_t s) {
+  const GemvDesc* d = reinterpret_cast<const GemvDesc*>(static_cast<char*>(ws) + kChainHeader);
+  return launch_chain(fmt, d, nullptr, n, static_cast<uint32_t*>(ws), s);
+}
+
+int chain_status(const void* ws, hipStream_t s) {
+  uint32_t err = 0;
+  if (hipMemcpyAsync(&err, static_cast<const uint32_t*>(ws) + 2, 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return -1;
+  return (int)err;
 }
 
 int launch_qmv(int fmt, const void* w, const float* X, float* Y, int M, int64_t N, int64_t K,
@@ -833,9 +1032,9 @@ int launch_qmv(int fmt, const void* w, const float* X, float* Y, int M, int64_t 
   layout_of(fmt, N, K, &L);
   const uint8_t* codes = static_cast<const uint8_t*>(w);
   const uint16_t* scales = reinterpret_cast<const uint16_t*>(codes + L.scales_off);
-  if (M == 1) {
-    const int st = launch_qmv1p(fmt, codes, scales, X, Y, N, L.nb, s);
-    if (st >= 0) return st;
+  if (M == 1 && K <= chain_max_k()) {  // batch 1: a chain of one GEMV
+    const GemvDesc d{codes, X, Y, N, K, fmt, 0};
+    return launch_chain(fmt, nullptr, &d, 1, nullptr, s);
   }
   const int G = pick_group(L.nb);
   const int R = pick_rows(N, G, M);

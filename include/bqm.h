@@ -111,6 +111,48 @@ int qmv_id(int fmt, const void* w_packed, int E, int64_t N, int64_t K, const int
            int top_k, const float* X, int64_t x_tok_stride, int64_t x_slot_stride, float* Y,
            hipStream_t stream);
 
+/* ---- chains of batch-1 GEMVs in one launch -------------------------------------------
+ * Decode runs one GEMV after another, each reading the previous one's output (through
+ * the layers' other operations); launching them one by one pays a kernel start and drain
+ * per GEMV.  A chain runs a list of batch-1 GEMVs in order in ONE launch: a GEMV marked
+ * `wait` starts only after every earlier GEMV of the chain has finished and its outputs
+ * are visible device-wide (so its x may be an earlier GEMV's y); the weights of the next
+ * GEMV are already streaming while the previous one finishes.  Same arithmetic and
+ * tolerance as qmv_q4_0 / qmv_q8_0 with M = 1. */
+typedef struct bqm_gemv {
+  const void* w_packed;  /* packed N x K matrix (device)                              */
+  const float* x;        /* [K] fp32 input (device), 16-byte aligned                  */
+  float* y;              /* [N] fp32 output (device)                                  */
+  int64_t N, K;          /* 1 <= N <= 2^30; 32 <= K <= BQM_CHAIN_MAX_K, K % 32 == 0   */
+  int32_t fmt;           /* BQM_Q4_0 or BQM_Q8_0, the same for every GEMV of a chain  */
+  int32_t wait;          /* nonzero: start after all earlier GEMVs of the chain       */
+} bqm_gemv;
+
+/* Largest K of a chain GEMV (its x is staged in the LDS of one workgroup).  A chain of n
+ * GEMVs also needs 48 * n + 4.5 * max(K) <= 163584 bytes of LDS (about 1700 GEMVs at
+ * K = 5120); bqm_chain_prepare returns BQM_E_SHAPE otherwise. */
+#define BQM_CHAIN_MAX_K 32768
+
+/* Device bytes of the workspace of an n-GEMV chain (0 if n < 1). */
+size_t bqm_chain_workspace_bytes(int n);
+
+/* Validates the n host-side descriptors, then writes them and a zeroed synchronization
+ * header into `workspace` (device memory, bqm_chain_workspace_bytes(n) bytes, 16-byte
+ * aligned, owned by the caller).  A set-up call: it synchronizes `stream` before it
+ * returns, so `descs` may be freed afterwards.  Errors: BQM_E_SHAPE, BQM_E_NULL,
+ * BQM_E_ALIGN, BQM_E_UNSUPPORTED (mixed or unknown formats), BQM_E_LAUNCH. */
+int bqm_chain_prepare(const bqm_gemv* descs, int n, void* workspace, hipStream_t stream);
+
+/* Runs a prepared chain in one (cooperative) launch on `stream`; fmt and n must be those
+ * it was prepared with (the kernel checks them against the workspace and otherwise
+ * computes nothing and records error 2).  The workspace is left ready for the next call;
+ * calls sharing one workspace must not overlap in time. */
+int qmv_chain(int fmt, void* workspace, int n, hipStream_t stream);
+
+/* Synchronizes `stream` and returns the chain's error word: 0 = ok, 1 = a device-wide
+ * wait timed out (results invalid; prepare again), 2 = fmt/n mismatch, -1 = copy failed. */
+int bqm_chain_status(const void* workspace, hipStream_t stream);
+
 /* Activation quantizer for the prefill product, per row m and 32-wide block b, in IEEE
  * single precision:  a = max_j |x_j|;  dx = a / 127 (correctly rounded);  dx == 0 gives
  * all-zero codes and dx = +0; otherwise Xq_j = round_half_away_from_zero(x_j / dx) clamped

@@ -1,0 +1,114 @@
+"""GPU parity of GEMV chains (qmv_chain): one launch, device-wide waits between GEMVs."""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle
+from block_quantized_matrix_amd import bqm
+from tests._gpu import DEV, check_close, host, packed, say, weights
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _oracle():
+    oracle.build(force=False)
+
+
+def make_chain(fmt, shapes, key, dependent=True):
+    """GEMVs i = 0..n-1 with W_i [N_i][K_i]; if dependent, x_{i+1} is y_i (N_i == K_{i+1})."""
+    Ws, Wps, xs, ys, descs = [], [], [], [], []
+    x = gen.normal((shapes[0][1],), key + ("x0",), device=DEV)
+    for i, (N, K) in enumerate(shapes):
+        Wi = weights(fmt, N, K, key + (i,))
+        Wp = packed(fmt, Wi, N, K)
+        if not dependent and i > 0:
+            x = gen.normal((K,), key + ("x", i), device=DEV)
+        y = torch.full((N,), float("nan"), device=DEV)
+        Ws.append(Wi); Wps.append(Wp); xs.append(x); ys.append(y)
+        descs.append(bqm.gemv(fmt, Wp, x, y, N, K, wait=i > 0))
+        if dependent:
+            x = y
+    ws = torch.zeros(bqm.chain_workspace_bytes(len(descs)), dtype=torch.uint8, device=DEV)
+    bqm.bqm_chain_prepare(descs, ws)
+    return Ws, Wps, xs, ys, descs, ws
+
+
+def check_stages(fmt, shapes, Ws, xs, ys):
+    for i, (N, K) in enumerate(shapes):
+        xi = host(xs[i]).reshape(1, K)
+        assert np.all(np.isfinite(xi)), f"stage {i} read an input that was never written"
+        Yr, S = oracle.qmv(fmt, host(Ws[i]), xi, N, K)
+        check_close(host(ys[i]).reshape(1, N), Yr, S, f"chain stage {i} ({N}x{K})")
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0"])
+def test_chain_dependent_stages(fmt):
+    """Each GEMV reads the previous one's output: a missing device-wide wait would read the
+    NaN the output buffers start with."""
+    shapes = [(5120, 4096), (17408, 5120), (5120, 17408), (1536, 5120), (4096, 1536), (96, 4096)]
+    say("chain dependent", fmt)
+    Ws, Wps, xs, ys, descs, ws = make_chain(fmt, shapes, ("chain-dep", fmt))
+    bqm.qmv_chain(fmt, ws, len(descs))
+    assert bqm.bqm_chain_status(ws) == 0
+    check_stages(fmt, shapes, Ws, xs, ys)
+
+
+def test_chain_ragged_and_tiny_shapes():
+    """Ragged K (K/32 not a multiple of the lane group), rows fewer than CUs, tiny shapes."""
+    say("chain ragged")
+    shapes = [(37, 96), (3, 1184), (300, 96), (1, 9600), (65, 32), (2049, 1536)]
+    Ws, Wps, xs, ys, descs, ws = make_chain("q4_0", shapes, ("chain-ragged",), dependent=False)
+    bqm.qmv_chain("q4_0", ws, len(descs))
+    assert bqm.bqm_chain_status(ws) == 0
+    check_stages("q4_0", shapes, Ws, xs, ys)
+
+
+def test_chain_equals_separate_launches_and_replays():
+    """A chain gives the same bits as the batch-1 calls one by one, on every replay."""
+    shapes = [(7168, 5120), (5120, 5120), (34816, 5120), (5120, 17408)]
+    say("chain vs separate")
+    Ws, Wps, xs, ys, descs, ws = make_chain("q4_0", shapes, ("chain-eq",), dependent=False)
+    sep = []
+    for (N, K), Wp, x in zip(shapes, Wps, xs):
+        y = torch.empty((N,), device=DEV)
+        bqm.qmv_q4_0(Wp, x, y, 1, N, K)
+        sep.append(y)
+    for rep in range(3):
+        for y in ys:
+            y.fill_(float("nan"))
+        bqm.qmv_chain("q4_0", ws, len(descs))
+        assert bqm.bqm_chain_status(ws) == 0
+        for y, ys_ in zip(sep, ys):
+            assert torch.equal(y, ys_), f"replay {rep}"
+
+
+def test_chain_mismatch_is_reported_and_computes_nothing():
+    shapes = [(64, 512), (64, 64)]
+    Ws, Wps, xs, ys, descs, ws = make_chain("q4_0", shapes, ("chain-mis",))
+    bqm.qmv_chain("q4_0", ws, 3)           # wrong n
+    assert bqm.bqm_chain_status(ws) == 2
+    assert torch.all(torch.isnan(ys[0]))
+    bqm.bqm_chain_prepare(descs, ws)       # prepare again: clean state
+    bqm.qmv_chain("q8_0", ws, 2)           # wrong format
+    assert bqm.bqm_chain_status(ws) == 2
+    bqm.bqm_chain_prepare(descs, ws)
+    bqm.qmv_chain("q4_0", ws, 2)
+    assert bqm.bqm_chain_status(ws) == 0
+    check_stages("q4_0", shapes, Ws, xs, ys)
+
+
+def test_chain_prepare_rejects_bad_descriptors():
+    W = torch.zeros(4096, dtype=torch.uint8, device=DEV)
+    x = torch.zeros(64, device=DEV)
+    y = torch.zeros(64, device=DEV)
+    ws = torch.zeros(bqm.chain_workspace_bytes(2), dtype=torch.uint8, device=DEV)
+    good = bqm.gemv("q4_0", W, x, y, 64, 64, False)
+    for bad in (bqm.Gemv(W.data_ptr(), x.data_ptr(), y.data_ptr(), 64, 48, 2, 0),     # K % 32
+                bqm.Gemv(W.data_ptr(), x.data_ptr(), y.data_ptr(), 64, 0, 2, 0),      # K = 0
+                bqm.Gemv(W.data_ptr(), x.data_ptr(), y.data_ptr(), 64, 32800, 2, 0),     # K too long
+                bqm.Gemv(W.data_ptr(), x.data_ptr(), y.data_ptr(), 64, 64, 8, 0),     # mixed fmt
+                bqm.Gemv(0, x.data_ptr(), y.data_ptr(), 64, 64, 2, 0)):
+        with pytest.raises(bqm.BqmError):
+            bqm.bqm_chain_prepare([good, bad], ws)

@@ -487,35 +487,53 @@ __device__ __forceinline__ void load_stage(const StageRow* t, int i, int wave, S
   s.my_tiles = wave < ntiles ? ((ntiles - 1 - wave) >> 4) + 1 : 0;  // 16 waves
 }
 
-// Device-wide barrier; thread 0 of each workgroup arrives.  The spin is bounded: on timeout
-// the error word is set and every workgroup leaves (the chain's results are then invalid).
-__device__ __forceinline__ bool grid_barrier(uint32_t* sync, bool* lds_ok) {
+// Device-wide barrier between the GEMVs of a chain.  Workspace words: [0] release epoch,
+// [2] error, [3] n, [4] format; then one arrival flag per workgroup, each on its own
+// 128-byte line (no contended atomic).  Workgroup 0 waits for every flag to reach the
+// barrier's epoch and then publishes it in the release word, which the others wait for.
+// Data crossing the barrier (the outputs y and the next inputs x) is written and read with
+// agent-coherent (sc1) accesses, so no L2-wide write-back or invalidation is needed; the
+// outputs must only have landed before a workgroup arrives (see the wait below).  Every
+// wait is bounded: on timeout the error word is set and all workgroups leave.
+constexpr int kChainHeaderWords = 64;      // 256 bytes
+constexpr int kFlagStrideWords = 32;       // 128 bytes
+constexpr int kChainMaxWorkgroups = 512;
+constexpr uint32_t kSpinLimit = 1u << 22;
+
+__device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ bool grid_barrier(uint32_t* ws, uint32_t epoch, bool* lds_ok) {
+  // Each wave's last output store of this GEMV is followed by at most 3 loads (one ring
+  // refill), and vector memory operations complete in issue order: vmcnt <= 3 means the
+  // stores have landed, while the prefetched weights of the next GEMV stay in flight.
+  __builtin_amdgcn_s_waitcnt(0x0F73);  // vmcnt(3); expcnt, lgkmcnt: no wait
   __syncthreads();
-  if (threadIdx.x == 0) {
-    bool ok = true;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // this workgroup's outputs, visible
-    const uint32_t gen0 = __hip_atomic_load(sync + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t arrived =
-        __hip_atomic_fetch_add(sync, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    if (arrived == gridDim.x - 1) {
-      __hip_atomic_store(sync, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_fetch_add(sync + 1, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
+  uint32_t* flags = ws + kChainHeaderWords;
+  if (threadIdx.x == 0) st_agent(flags + blockIdx.x * kFlagStrideWords, epoch);
+  if (blockIdx.x == 0) {
+    for (uint32_t b = threadIdx.x; b < gridDim.x; b += blockDim.x) {
       uint32_t spins = 0;
-      // relaxed polls (an acquire per poll would invalidate this XCD's L2 every time);
-      // the acquire fence below orders the reads that follow
-      while (__hip_atomic_load(sync + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen0) {
-        if (++spins > (1u << 24) ||
-            __hip_atomic_load(sync + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
-          __hip_atomic_store(sync + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          ok = false;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
+      while (ld_agent(flags + b * kFlagStrideWords) != epoch) {
+        if (++spins > kSpinLimit || ld_agent(ws + 2) != 0) { st_agent(ws + 2, 1u); break; }
+        __builtin_amdgcn_s_sleep(1);
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // other workgroups' outputs
-    *lds_ok = ok;
+    __syncthreads();
+    if (threadIdx.x == 0) st_agent(ws, epoch);
+  }
+  if (threadIdx.x == 0) {
+    uint32_t spins = 0;
+    bool ok = true;
+    while (ld_agent(ws) != epoch) {
+      if (++spins > kSpinLimit || ld_agent(ws + 2) != 0) { st_agent(ws + 2, 1u); ok = false; break; }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    *lds_ok = ok && ld_agent(ws + 2) == 0;
   }
   __syncthreads();
   return *lds_ok;
@@ -538,7 +556,10 @@ __global__ __launch_bounds__(kP1Threads) void k_qmv_chain(ChainArgs a) {
   StageRow* table = reinterpret_cast<StageRow*>(smem);
   char* xlds = reinterpret_cast<char*>(smem) + ((a.n * (int)sizeof(StageRow) + 15) & ~15);
   for (int i = tid; i < a.n; i += kP1Threads) table[i] = make_stage<FMT>(a.descs ? a.descs[i] : a.one);
+  __shared__ uint32_t lds_epoch;
+  if (tid == 0 && a.sync) lds_epoch = ld_agent(a.sync);  // stable until all have arrived once
   __syncthreads();
+  uint32_t epoch = a.sync ? lds_epoch : 0u;
 
   // ---------------- issue side: runs P steps ahead, across GEMVs ----------------
   int gi = 0, it = 0, ij = 0;
@@ -614,11 +635,13 @@ __global__ __launch_bounds__(kP1Threads) void k_qmv_chain(ChainArgs a) {
     csteps = sc.my_tiles * sc.ns;
     cg = lane & (sc.G - 1);
     clg = lane >> sc.lg2G;
-    __syncthreads();
-    if (sc.wait && gc > 0 && a.sync) alive = grid_barrier(a.sync, &lds_ok);
-    const f32x4* x4 = reinterpret_cast<const f32x4*>(sc.x);
+    if (sc.wait && gc > 0 && a.sync) alive = grid_barrier(a.sync, ++epoch, &lds_ok);
+    else __syncthreads();
+    // x through agent-coherent loads: it may have been written by other workgroups
+    const __amdgpu_buffer_rsrc_t rx =
+        __builtin_amdgcn_make_buffer_rsrc((void*)sc.x, (short)0, sc.nb * 128, 0x00020000);
     for (int c = tid; c < sc.nb * 8; c += kP1Threads) {
-      f32x4 v = x4[c];
+      f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, c * 16, 0, 16));
       const int blk = c >> 3, i = c & 7;
       if (FMT == FQ4 && i >= 4) v = v * 0.0625f;
       *reinterpret_cast<f32x4*>(xlds + blk * kBlkLds + i * 16) = v;
@@ -679,7 +702,10 @@ __global__ __launch_bounds__(kP1Threads) void k_qmv_chain(ChainArgs a) {
           float v = acc;
           for (int off = sc.G >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
           const int row = (wave + ct * kP1Waves) * sc.gpw + clg;
-          if (cg == 0 && row < sc.nrows) sc.y[row] = v;
+          if (cg == 0 && row < sc.nrows)  // agent-coherent global store: a later GEMV may read it
+            __hip_atomic_store((__attribute__((address_space(1))) float*)sc.y + row, v,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          asm volatile("" ::: "memory");  // keep the store ahead of the refill loads
           acc = 0.f;
           cj = 0;
           ++ct;
@@ -975,11 +1001,12 @@ int launch_chain(int fmt, const GemvDesc* descs, const GemvDesc* one, int n, uin
   return launch_status();
 }
 
-// ---- chain API: workspace = {count, generation, error, n, fmt} words, then descriptors
-constexpr int64_t kChainHeader = 256;
+// ---- chain API.  Workspace: 64 header words {release epoch, -, error, n, fmt, ...}, one
+// 128-byte arrival flag per workgroup (at most kChainMaxWorkgroups), then the descriptors.
+constexpr int64_t kChainSyncBytes = (kChainHeaderWords + kChainMaxWorkgroups * kFlagStrideWords) * 4;
 
 size_t chain_workspace_bytes(int n) {
-  return n < 1 ? 0 : (size_t)(kChainHeader + (int64_t)n * (int64_t)sizeof(GemvDesc));
+  return n < 1 ? 0 : (size_t)(kChainSyncBytes + (int64_t)n * (int64_t)sizeof(GemvDesc));
 }
 
 int chain_prepare(const bqm_gemv* descs, int n, void* ws, hipStream_t s) {
@@ -1000,11 +1027,11 @@ int chain_prepare(const bqm_gemv* descs, int n, void* ws, hipStream_t s) {
     if (((uintptr_t)d.w_packed & 15) || ((uintptr_t)d.x & 15) || ((uintptr_t)d.y & 3))
       return BQM_E_ALIGN;
   }
-  static const uint32_t zero_words[kChainHeader / 4] = {0};
+  if (cus > kChainMaxWorkgroups) return BQM_E_UNSUPPORTED;
   uint32_t head[8] = {0, 0, 0, (uint32_t)n, (uint32_t)fmt, 0, 0, 0};
-  if (hipMemcpyAsync(ws, zero_words, kChainHeader, hipMemcpyHostToDevice, s) != hipSuccess ||
+  if (hipMemsetAsync(ws, 0, kChainSyncBytes, s) != hipSuccess ||
       hipMemcpyAsync(ws, head, sizeof(head), hipMemcpyHostToDevice, s) != hipSuccess ||
-      hipMemcpyAsync(static_cast<char*>(ws) + kChainHeader, descs, (size_t)n * sizeof(GemvDesc),
+      hipMemcpyAsync(static_cast<char*>(ws) + kChainSyncBytes, descs, (size_t)n * sizeof(GemvDesc),
                      hipMemcpyHostToDevice, s) != hipSuccess ||
       hipStreamSynchronize(s) != hipSuccess)
     return BQM_E_LAUNCH;
@@ -1012,7 +1039,7 @@ int chain_prepare(const bqm_gemv* descs, int n, void* ws, hipStream_t s) {
 }
 
 int chain_launch(int fmt, void* ws, int n, hipStream_t s) {
-  const GemvDesc* d = reinterpret_cast<const GemvDesc*>(static_cast<char*>(ws) + kChainHeader);
+  const GemvDesc* d = reinterpret_cast<const GemvDesc*>(static_cast<char*>(ws) + kChainSyncBytes);
   return launch_chain(fmt, d, nullptr, n, static_cast<uint32_t*>(ws), s);
 }
 

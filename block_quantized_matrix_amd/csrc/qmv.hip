@@ -507,11 +507,14 @@ __device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// LOADS: the loads of one step.  Every output store is followed by at least that many
+// loads (the same step's refill), and vector memory operations complete in issue order, so
+// vmcnt <= LOADS means every store of the wave has landed, while the weights prefetched
+// for the next GEMV may stay in flight.
+template <int LOADS>
 __device__ __forceinline__ bool grid_barrier(uint32_t* ws, uint32_t epoch, bool* lds_ok) {
-  // Each wave's last output store of this GEMV is followed by at most 3 loads (one ring
-  // refill), and vector memory operations complete in issue order: vmcnt <= 3 means the
-  // stores have landed, while the prefetched weights of the next GEMV stay in flight.
-  __builtin_amdgcn_s_waitcnt(0x0F73);  // vmcnt(3); expcnt, lgkmcnt: no wait
+  static_assert(LOADS >= 0 && LOADS <= 15, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | LOADS);  // vmcnt(LOADS); expcnt, lgkmcnt: no wait
   __syncthreads();
   uint32_t* flags = ws + kChainHeaderWords;
   if (threadIdx.x == 0) st_agent(flags + blockIdx.x * kFlagStrideWords, epoch);
@@ -543,7 +546,9 @@ template <int FMT, int P>
 __global__ __launch_bounds__(kP1Threads) void k_qmv_chain(ChainArgs a) {
   extern __shared__ float4 smem[];
   constexpr int CB = FMT == FQ4 ? 16 : 32;     // code bytes per block
+  constexpr uint32_t kOob = 0x80000000u;       // lane offset past every descriptor: reads 0
   __shared__ bool lds_ok;
+  __shared__ uint32_t lds_epoch;
   const int tid = threadIdx.x, lane = tid & 63;
   if (a.sync && (a.sync[3] != (uint32_t)a.n || a.sync[4] != (uint32_t)(FMT == FQ4 ? BQM_Q4_0 : BQM_Q8_0))) {
     // the workspace was prepared for another chain: flag it, compute nothing
@@ -556,108 +561,131 @@ __global__ __launch_bounds__(kP1Threads) void k_qmv_chain(ChainArgs a) {
   StageRow* table = reinterpret_cast<StageRow*>(smem);
   char* xlds = reinterpret_cast<char*>(smem) + ((a.n * (int)sizeof(StageRow) + 15) & ~15);
   for (int i = tid; i < a.n; i += kP1Threads) table[i] = make_stage<FMT>(a.descs ? a.descs[i] : a.one);
-  __shared__ uint32_t lds_epoch;
   if (tid == 0 && a.sync) lds_epoch = ld_agent(a.sync);  // stable until all have arrived once
   __syncthreads();
   uint32_t epoch = a.sync ? lds_epoch : 0u;
 
-  // ---------------- issue side: runs P steps ahead, across GEMVs ----------------
-  int gi = 0, it = 0, ij = 0;
+  // Both sides walk the same sequence of steps: for each GEMV in which this wave has
+  // tiles, its steps padded to a multiple of P (padding steps load nothing useful and
+  // compute nothing), so a GEMV always ends at the end of an unrolled group.  Every step
+  // issues its loads, real or past the descriptor, so the number of loads in flight is
+  // the same on every path through the loop.
+
+  // ---------------- issue side: P steps ahead ----------------
+  int gi = -1;               // GEMV being issued
   Stage si;
-  __amdgpu_buffer_rsrc_t rc, rs;
-  uint32_t vc = 0x80000000u, vs = 0x80000000u;
+  si.my_tiles = 0;
+  int it = 0, ij = 0;        // this wave's tile, step in tile
+  int ireal = 0, ipad = 0;   // real steps left; steps left with padding
+  __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(nullptr, (short)0, 0, 0x00020000);
+  __amdgpu_buffer_rsrc_t rs = rc;
+  uint32_t vc = kOob, vs = kOob;
   int ig = 0, ilg = 0;
-  // next (gi, tile) with work for this wave; sets up descriptors and lane offsets
-  auto issue_tile = [&]() {
-    while (gi < a.n && it >= si.my_tiles) {
-      if (++gi < a.n) {
-        load_stage(table, gi, wave, si);
-        it = 0;
-        rc = __builtin_amdgcn_make_buffer_rsrc((void*)si.codes, (short)0,
-                                               (int)((uint32_t)si.nrows * si.nb * CB), 0x00020000);
-        rs = __builtin_amdgcn_make_buffer_rsrc((void*)si.scales, (short)0,
-                                               (int)((uint32_t)si.nrows * si.nb * 2), 0x00020000);
-        ig = lane & (si.G - 1);
-        ilg = lane >> si.lg2G;
-      }
+  auto tile_offsets = [&]() {
+    const int trow = (wave + it * kP1Waves) * si.gpw;
+    const bool ok = trow + ilg < si.nrows;  // rows past the range read zeros
+    vc = ok ? ((uint32_t)ilg * si.nb + ig) * CB : kOob;
+    vs = ok ? ((uint32_t)ilg * si.nb + ig) * 2 : kOob;
+  };
+  auto next_issue_gemv = [&]() {  // the next GEMV with steps for this wave, if any
+    while (ipad == 0 && gi + 1 < a.n) {
+      ++gi;
+      load_stage(table, gi, wave, si);
+      ireal = si.my_tiles * si.ns;
+      ipad = (ireal + P - 1) / P * P;
     }
-    if (gi < a.n) {
-      const int trow = (wave + it * kP1Waves) * si.gpw;
-      const bool ok = trow + ilg < si.nrows;  // rows past the range read zeros
-      vc = ok ? ((uint32_t)ilg * si.nb + ig) * CB : 0x80000000u;
-      vs = ok ? ((uint32_t)ilg * si.nb + ig) * 2 : 0x80000000u;
+    if (ipad > 0) {
+      rc = __builtin_amdgcn_make_buffer_rsrc((void*)si.codes, (short)0,
+                                             (int)((uint32_t)si.nrows * si.nb * CB), 0x00020000);
+      rs = __builtin_amdgcn_make_buffer_rsrc((void*)si.scales, (short)0,
+                                             (int)((uint32_t)si.nrows * si.nb * 2), 0x00020000);
+      ig = lane & (si.G - 1);
+      ilg = lane >> si.lg2G;
+      it = 0;
+      ij = 0;
+      tile_offsets();
     }
   };
-  gi = -1;
-  si.my_tiles = 0;
-  issue_tile();
+  next_issue_gemv();
 
-  auto issue = [&](Codes<FMT>& q, uint32_t& d) {
-    if (gi < a.n) {
-      const uint32_t trow = (uint32_t)((wave + it * kP1Waves) * si.gpw);
-      const uint32_t so = trow * si.nb + (uint32_t)(ij << si.lg2G);
-      uint32_t c = vc, e = vs;
-      if (si.ragged && (ij << si.lg2G) + ig >= si.nb) { c = 0x80000000u; e = 0x80000000u; }
-      if constexpr (FMT == FQ4) {
-        q.a = __builtin_amdgcn_raw_buffer_load_b128(rc, c, so * CB, 0);
-      } else {
-        q.a = __builtin_amdgcn_raw_buffer_load_b128(rc, c, so * CB, 0);
-        q.b = __builtin_amdgcn_raw_buffer_load_b128(rc, c + 16, so * CB, 0);
-      }
-      d = __builtin_amdgcn_raw_buffer_load_b16(rs, e, so * 2, 0);
+  auto issue = [&](Codes<FMT>& q, uint16_t& d) {
+    // arithmetic, not branches: one load sequence for real and padding steps (a lane
+    // offset with bit 31 set is past every descriptor)
+    const uint32_t live = ireal > 0 ? 1u : 0u;
+    const uint32_t trow = (uint32_t)((wave + it * kP1Waves) * si.gpw);
+    const uint32_t so = (trow * si.nb + (uint32_t)(ij << si.lg2G)) * live;
+    const uint32_t past_k = (uint32_t)si.ragged & (uint32_t)((ij << si.lg2G) + ig >= si.nb);
+    const uint32_t off = ((1u - live) | past_k) << 31;
+    const uint32_t c = vc | off;
+    const uint32_t e = vs | off;
+    if constexpr (FMT == FQ4) {
+      q.a = __builtin_amdgcn_raw_buffer_load_b128(rc, c, so * CB, 0);
+    } else {
+      q.a = __builtin_amdgcn_raw_buffer_load_b128(rc, c, so * CB, 0);
+      q.b = __builtin_amdgcn_raw_buffer_load_b128(rc, c + 16, so * CB, 0);
+    }
+    d = __builtin_amdgcn_raw_buffer_load_b16(rs, e, so * 2, 0);
+    if (ireal > 0) {
+      --ireal;
       if (++ij == si.ns) {
         ij = 0;
         ++it;
-        issue_tile();
+        tile_offsets();
       }
     }
+    if (ipad > 0 && --ipad == 0) next_issue_gemv();
   };
 
   Codes<FMT> ring_q[P];
-  uint32_t ring_d[P];
+  uint16_t ring_d[P];  // scales stay 16-bit: a widening at the loop edge would wait for them
 #pragma unroll
   for (int p = 0; p < P; p++) issue(ring_q[p], ring_d[p]);
 
   // ---------------- consume side ----------------
-  int gc = -1, ct = 0, cj = 0, csteps = 0;  // GEMV, tile, step in tile, steps left
+  int gc = -1, ct = 0, cj = 0, creal = 0, cpad = 0;  // GEMV, tile, step in tile, steps left
   Stage sc;
   const char* lds_lane = xlds;
   int cg = 0, clg = 0;
   float acc = 0.f;
   bool alive = true;
   // Enter the next GEMV: all waves finished reading the staged x, wait for earlier outputs
-  // if asked, stage the new x.  Every wave calls this once per GEMV, in order.
+  // if asked, stage the new x and its block sums.  Every wave enters every GEMV, in order.
   auto enter = [&]() {
     ++gc;
     load_stage(table, gc, wave, sc);
     ct = 0;
     cj = 0;
-    csteps = sc.my_tiles * sc.ns;
+    creal = sc.my_tiles * sc.ns;
+    cpad = (creal + P - 1) / P * P;
     cg = lane & (sc.G - 1);
     clg = lane >> sc.lg2G;
-    if (sc.wait && gc > 0 && a.sync) alive = grid_barrier(a.sync, ++epoch, &lds_ok);
+    if (sc.wait && gc > 0 && a.sync) alive = grid_barrier<FMT == FQ4 ? 2 : 3>(a.sync, ++epoch, &lds_ok);
     else __syncthreads();
-    // x through agent-coherent loads: it may have been written by other workgroups
+    // One thread per block.  x comes through agent-coherent loads: other workgroups may
+    // have written it.  The block sum runs in chain order over the values as staged
+    // (Q4_0 positions 16..31 divided by 16, multiplied back exactly).
     const __amdgpu_buffer_rsrc_t rx =
         __builtin_amdgcn_make_buffer_rsrc((void*)sc.x, (short)0, sc.nb * 128, 0x00020000);
-    for (int c = tid; c < sc.nb * 8; c += kP1Threads) {
-      f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, c * 16, 0, 16));
-      const int blk = c >> 3, i = c & 7;
-      if (FMT == FQ4 && i >= 4) v = v * 0.0625f;
-      *reinterpret_cast<f32x4*>(xlds + blk * kBlkLds + i * 16) = v;
-    }
-    __syncthreads();
-    // block sums in chain order (positions 0..31; Q4_0 positions 16..31 are stored / 16)
     for (int blk = tid; blk < sc.nb; blk += kP1Threads) {
-      const f32x4* xl = reinterpret_cast<const f32x4*>(xlds + blk * kBlkLds);
-      float s = xl[0].x;
-      s = s + xl[0].y; s = s + xl[0].z; s = s + xl[0].w;
+      f32x4 v[8];
 #pragma unroll
-      for (int k = 1; k < 4; k++) { s = s + xl[k].x; s = s + xl[k].y; s = s + xl[k].z; s = s + xl[k].w; }
+      for (int i = 0; i < 8; i++)
+        v[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, blk * 128 + i * 16, 0, 16));
+      if (FMT == FQ4) {
+#pragma unroll
+        for (int i = 4; i < 8; i++) v[i] = v[i] * 0.0625f;
+      }
+      f32x4* dst = reinterpret_cast<f32x4*>(xlds + blk * kBlkLds);
+#pragma unroll
+      for (int i = 0; i < 8; i++) dst[i] = v[i];
+      float s = v[0].x;
+      s = s + v[0].y; s = s + v[0].z; s = s + v[0].w;
+#pragma unroll
+      for (int i = 1; i < 4; i++) { s = s + v[i].x; s = s + v[i].y; s = s + v[i].z; s = s + v[i].w; }
       const float m = FMT == FQ4 ? 16.0f : 1.0f;
 #pragma unroll
-      for (int k = 4; k < 8; k++) {
-        s = s + xl[k].x * m; s = s + xl[k].y * m; s = s + xl[k].z * m; s = s + xl[k].w * m;
+      for (int i = 4; i < 8; i++) {
+        s = s + v[i].x * m; s = s + v[i].y * m; s = s + v[i].z * m; s = s + v[i].w * m;
       }
       *reinterpret_cast<float*>(xlds + blk * kBlkLds + 128) = s;
     }
@@ -665,56 +693,39 @@ __global__ __launch_bounds__(kP1Threads) void k_qmv_chain(ChainArgs a) {
     lds_lane = xlds + cg * kBlkLds;
   };
 
-  // Rotate the ring so that slot k becomes slot 0 (at a GEMV boundary, where the steps of
-  // the finished GEMV ended in the middle of the unrolled group).
-  auto rotate = [&](int k) {
-    Codes<FMT> tq[P];
-    uint32_t td[P];
-#pragma unroll
-    for (int r = 1; r < P; r++) {
-      if (k == r) {
-#pragma unroll
-        for (int i = 0; i < P; i++) { tq[i] = ring_q[(i + r) % P]; td[i] = ring_d[(i + r) % P]; }
-#pragma unroll
-        for (int i = 0; i < P; i++) { ring_q[i] = tq[i]; ring_d[i] = td[i]; }
-      }
-    }
-  };
-
   enter();
   while (alive) {
-    int used = P;
+    if (cpad > 0) {
 #pragma unroll
-    for (int p = 0; p < P; p++) {
-      if (csteps == 0) {  // uniform: this GEMV is done for this wave
-        if (used == P) used = p;
-      } else {
-        const char* xb = lds_lane + cj * (sc.G * kBlkLds);
-        if (sc.ragged && cj * sc.G + cg >= sc.nb)  // past K: reuse the last block; its d is 0
-          xb = xlds + (sc.nb - 1) * kBlkLds;
-        const f32x4* xl = reinterpret_cast<const f32x4*>(xb);
-        const float sx = *reinterpret_cast<const float*>(xb + 128);
-        const float c = chain_m1<FMT>(ring_q[p], xl);
-        const float rr = fmaf(FMT == FQ4 ? -8.0f : -128.0f, sx, c);
-        acc = fmaf(h2f(ring_d[p]), rr, acc);
-        --csteps;
-        if (++cj == sc.ns) {  // tile done: reduce over the lane group, store its row
-          float v = acc;
-          for (int off = sc.G >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-          const int row = (wave + ct * kP1Waves) * sc.gpw + clg;
-          if (cg == 0 && row < sc.nrows)  // agent-coherent global store: a later GEMV may read it
-            __hip_atomic_store((__attribute__((address_space(1))) float*)sc.y + row, v,
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          asm volatile("" ::: "memory");  // keep the store ahead of the refill loads
-          acc = 0.f;
-          cj = 0;
-          ++ct;
+      for (int p = 0; p < P; p++) {
+        if (creal > 0) {  // uniform: a real step of this wave
+          const char* xb = lds_lane + cj * (sc.G * kBlkLds);
+          if (sc.ragged && cj * sc.G + cg >= sc.nb)  // past K: reuse the last block; its d is 0
+            xb = xlds + (sc.nb - 1) * kBlkLds;
+          const f32x4* xl = reinterpret_cast<const f32x4*>(xb);
+          const float sx = *reinterpret_cast<const float*>(xb + 128);
+          const float c = chain_m1<FMT>(ring_q[p], xl);
+          const float rr = fmaf(FMT == FQ4 ? -8.0f : -128.0f, sx, c);
+          acc = fmaf(h2f(ring_d[p]), rr, acc);
+          --creal;
+          if (++cj == sc.ns) {  // tile done: reduce over the lane group, store its row
+            float v = acc;
+            for (int off = sc.G >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+            const int row = (wave + ct * kP1Waves) * sc.gpw + clg;
+            if (cg == 0 && row < sc.nrows)  // agent-coherent global store: a later GEMV may read it
+              __hip_atomic_store((__attribute__((address_space(1))) float*)sc.y + row, v,
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            asm volatile("" ::: "memory");  // keep the store ahead of this step's loads
+            acc = 0.f;
+            cj = 0;
+            ++ct;
+          }
         }
         issue(ring_q[p], ring_d[p]);  // refill the slot just consumed
       }
+      cpad -= P;
     }
-    if (csteps == 0) {
-      if (used != P && used != 0) rotate(used);
+    if (cpad == 0) {
       if (gc + 1 >= a.n) break;
       enter();
     }

@@ -17,7 +17,9 @@ constexpr int kQK = 32;  // weights per block
 //                                       order (byte j: weight j low, weight j+16 high)
 //                                 Q8_0: 32 bytes per block = the int8 matrix [rows][K]
 //   [scales_off, +rows*nb*2)    binary16 scales, [rows][nb]
-// Both sections start on a 256-byte boundary; the total is rounded up to 256 bytes.
+// Both sections start on a 256-byte boundary.  At least 16 zero bytes follow the scales
+// (so a 4-byte read at any scale stays inside the buffer), and the total is rounded up to
+// 256 bytes; an empty matrix takes 0 bytes.
 struct Layout {
   int64_t nb;
   int64_t code_bytes_per_block;
@@ -34,7 +36,7 @@ inline bool layout_of(int fmt, int64_t rows, int64_t K, Layout* L) {
   L->code_bytes_per_block = fmt == BQM_Q4_0 ? 16 : 32;
   L->codes_bytes = rows * L->nb * L->code_bytes_per_block;
   L->scales_off = align256(L->codes_bytes);
-  L->total = align256(L->scales_off + rows * L->nb * 2);
+  L->total = rows * L->nb == 0 ? 0 : align256(L->scales_off + rows * L->nb * 2 + 16);
   return true;
 }
 

@@ -457,7 +457,8 @@ struct Stage {
   const uint16_t* scales;
   const float* x;
   float* y;
-  int nrows, nb, lg2G, G, gpw, ns, my_tiles;
+  int nrows, nb, lg2G, G, gpw, ns;
+  int S, start, end;  // the workgroup's steps (tiles x steps per tile); this wave's range
   bool ragged, wait;
 };
 
@@ -483,8 +484,12 @@ __device__ __forceinline__ void load_stage(const StageRow* t, int i, int wave, S
   s.gpw = 64 >> s.lg2G;
   s.ragged = (info >> 8) & 1;
   s.wait = (info >> 9) & 1;
+  // tiles of gpw rows, ns steps each, in row order; the 16 waves take equal contiguous
+  // ranges of the tile-major step sequence (a tile may be split between waves)
   const int ntiles = (s.nrows + s.gpw - 1) >> (6 - s.lg2G);
-  s.my_tiles = wave < ntiles ? ((ntiles - 1 - wave) >> 4) + 1 : 0;  // 16 waves
+  s.S = ntiles * s.ns;
+  s.start = (wave * s.S) >> 4;
+  s.end = ((wave + 1) * s.S) >> 4;
 }
 
 // Device-wide barrier between the GEMVs of a chain.  Workspace words: [0] release epoch,
@@ -507,13 +512,13 @@ __device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// LOADS: the loads of one step.  Every output store is followed by at least that many
-// loads (the same step's refill), and vector memory operations complete in issue order, so
-// vmcnt <= LOADS means every store of the wave has landed, while the weights prefetched
-// for the next GEMV may stay in flight.
+// Before a wave arrives, its output stores must have landed.  Every store is followed by
+// at least LOADS loads (its step's refill), and vector memory operations complete in issue
+// order, so vmcnt <= LOADS suffices, while the weights prefetched for the next GEMV may
+// stay in flight.
 template <int LOADS>
 __device__ __forceinline__ bool grid_barrier(uint32_t* ws, uint32_t epoch, bool* lds_ok) {
-  static_assert(LOADS >= 0 && LOADS <= 15, "vmcnt field");
+  static_assert(LOADS >= 1 && LOADS <= 15, "vmcnt field");
   __builtin_amdgcn_s_waitcnt(0x0F70 | LOADS);  // vmcnt(LOADS); expcnt, lgkmcnt: no wait
   __syncthreads();
   uint32_t* flags = ws + kChainHeaderWords;
@@ -547,6 +552,7 @@ __global__ __launch_bounds__(kP1Threads) void k_qmv_chain(ChainArgs a) {
   extern __shared__ float4 smem[];
   constexpr int CB = FMT == FQ4 ? 16 : 32;     // code bytes per block
   constexpr uint32_t kOob = 0x80000000u;       // lane offset past every descriptor: reads 0
+  constexpr int LOADS = FMT == FQ4 ? 2 : 3;    // loads per step
   __shared__ bool lds_ok;
   __shared__ uint32_t lds_epoch;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -574,60 +580,66 @@ __global__ __launch_bounds__(kP1Threads) void k_qmv_chain(ChainArgs a) {
   // ---------------- issue side: P steps ahead ----------------
   int gi = -1;               // GEMV being issued
   Stage si;
-  si.my_tiles = 0;
   int it = 0, ij = 0;        // this wave's tile, step in tile
   int ireal = 0, ipad = 0;   // real steps left; steps left with padding
   __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(nullptr, (short)0, 0, 0x00020000);
   __amdgpu_buffer_rsrc_t rs = rc;
-  uint32_t vc = kOob, vs = kOob;
+  uint32_t vc = kOob, vs = kOob;          // lane offsets in the current tile
+  uint32_t vc_last = kOob, vs_last = kOob;  // ... at its last step (past K in a ragged row: zeros)
   int ig = 0, ilg = 0;
   auto tile_offsets = [&]() {
-    const int trow = (wave + it * kP1Waves) * si.gpw;
+    const int trow = it * si.gpw;
     const bool ok = trow + ilg < si.nrows;  // rows past the range read zeros
     vc = ok ? ((uint32_t)ilg * si.nb + ig) * CB : kOob;
     vs = ok ? ((uint32_t)ilg * si.nb + ig) * 2 : kOob;
+    const bool past_k = ((si.ns - 1) << si.lg2G) + ig >= si.nb;
+    vc_last = past_k ? kOob : vc;
+    vs_last = past_k ? kOob : vs;
   };
   auto next_issue_gemv = [&]() {  // the next GEMV with steps for this wave, if any
     while (ipad == 0 && gi + 1 < a.n) {
       ++gi;
       load_stage(table, gi, wave, si);
-      ireal = si.my_tiles * si.ns;
+      ireal = si.end - si.start;
       ipad = (ireal + P - 1) / P * P;
     }
     if (ipad > 0) {
       rc = __builtin_amdgcn_make_buffer_rsrc((void*)si.codes, (short)0,
                                              (int)((uint32_t)si.nrows * si.nb * CB), 0x00020000);
+      // +2: a scale is read as 4 bytes (the packed layout leaves slack after the scales)
       rs = __builtin_amdgcn_make_buffer_rsrc((void*)si.scales, (short)0,
-                                             (int)((uint32_t)si.nrows * si.nb * 2), 0x00020000);
+                                             (int)((uint32_t)si.nrows * si.nb * 2 + 2), 0x00020000);
       ig = lane & (si.G - 1);
       ilg = lane >> si.lg2G;
-      it = 0;
-      ij = 0;
+      it = si.start / si.ns;
+      ij = si.start - it * si.ns;
       tile_offsets();
     }
   };
   next_issue_gemv();
 
-  auto issue = [&](Codes<FMT>& q, uint16_t& d) {
-    // arithmetic, not branches: one load sequence for real and padding steps (a lane
-    // offset with bit 31 set is past every descriptor)
+  auto issue = [&](Codes<FMT>& q, uint32_t& d) {
+    // arithmetic, not branches or selects (which the compiler may turn into branches with
+    // the loads duplicated): one load sequence for real and padding steps.  Once the range
+    // is done the lane offsets are past the descriptor: zeros, no memory traffic.
     const uint32_t live = ireal > 0 ? 1u : 0u;
-    const uint32_t trow = (uint32_t)((wave + it * kP1Waves) * si.gpw);
-    const uint32_t so = (trow * si.nb + (uint32_t)(ij << si.lg2G)) * live;
-    const uint32_t past_k = (uint32_t)si.ragged & (uint32_t)((ij << si.lg2G) + ig >= si.nb);
-    const uint32_t off = ((1u - live) | past_k) << 31;
-    const uint32_t c = vc | off;
-    const uint32_t e = vs | off;
+    const uint32_t so = ((uint32_t)(it * si.gpw) * si.nb + (uint32_t)(ij << si.lg2G)) * live;
+    const uint32_t lm = 0u - (uint32_t)(ij == si.ns - 1);  // all ones at a tile's last step
+    const uint32_t c = (vc_last & lm) | (vc & ~lm);
+    const uint32_t e = (vs_last & lm) | (vs & ~lm);
     if constexpr (FMT == FQ4) {
       q.a = __builtin_amdgcn_raw_buffer_load_b128(rc, c, so * CB, 0);
     } else {
       q.a = __builtin_amdgcn_raw_buffer_load_b128(rc, c, so * CB, 0);
       q.b = __builtin_amdgcn_raw_buffer_load_b128(rc, c + 16, so * CB, 0);
     }
-    d = __builtin_amdgcn_raw_buffer_load_b16(rs, e, so * 2, 0);
+    // the scale and the next 2 bytes (ignored): a whole-register load, which the compiler
+    // neither widens nor merges, so the ring is waited on per slot
+    d = __builtin_amdgcn_raw_buffer_load_b32(rs, e, so * 2, 0);
     if (ireal > 0) {
-      --ireal;
-      if (++ij == si.ns) {
+      if (--ireal == 0) {  // padding steps follow: read nothing
+        vc = vs = vc_last = vs_last = kOob;
+      } else if (++ij == si.ns) {
         ij = 0;
         ++it;
         tile_offsets();
@@ -637,60 +649,85 @@ __global__ __launch_bounds__(kP1Threads) void k_qmv_chain(ChainArgs a) {
   };
 
   Codes<FMT> ring_q[P];
-  uint16_t ring_d[P];  // scales stay 16-bit: a widening at the loop edge would wait for them
+  uint32_t ring_d[P];  // low 16 bits: the scale
 #pragma unroll
   for (int p = 0; p < P; p++) issue(ring_q[p], ring_d[p]);
 
   // ---------------- consume side ----------------
+  // A tile within one wave's range is reduced and stored by that wave.  A tile split
+  // between waves w0..wl: each part leaves its row sums in `part` (slot 1: the part that
+  // holds the tile's first step, slot 0: later parts) and counts itself in done[w0]; the
+  // part that completes the count adds the parts in wave order, stores the rows and resets
+  // the count.  Every store is followed by its step's loads.
+  __shared__ float part[kP1Waves * 2 * 4];
+  __shared__ int done[kP1Waves];
   int gc = -1, ct = 0, cj = 0, creal = 0, cpad = 0;  // GEMV, tile, step in tile, steps left
   Stage sc;
-  const char* lds_lane = xlds;
+  const char* lds_lane = xlds;   // this lane's first block of a tile
+  const char* lds_last = xlds;   // ... its block at the tile's last step (past K: the last block)
   int cg = 0, clg = 0;
   float acc = 0.f;
   bool alive = true;
+  if (tid < kP1Waves) done[tid] = 0;
   // Enter the next GEMV: all waves finished reading the staged x, wait for earlier outputs
   // if asked, stage the new x and its block sums.  Every wave enters every GEMV, in order.
   auto enter = [&]() {
     ++gc;
     load_stage(table, gc, wave, sc);
-    ct = 0;
-    cj = 0;
-    creal = sc.my_tiles * sc.ns;
+    creal = sc.end - sc.start;
     cpad = (creal + P - 1) / P * P;
+    ct = sc.start / sc.ns;
+    cj = sc.start - ct * sc.ns;
     cg = lane & (sc.G - 1);
     clg = lane >> sc.lg2G;
-    if (sc.wait && gc > 0 && a.sync) alive = grid_barrier<FMT == FQ4 ? 2 : 3>(a.sync, ++epoch, &lds_ok);
+    if (sc.wait && gc > 0 && a.sync) alive = grid_barrier<LOADS>(a.sync, ++epoch, &lds_ok);
     else __syncthreads();
-    // One thread per block.  x comes through agent-coherent loads: other workgroups may
-    // have written it.  The block sum runs in chain order over the values as staged
-    // (Q4_0 positions 16..31 divided by 16, multiplied back exactly).
+    // x comes through agent-coherent loads (other workgroups may have written it), 16
+    // bytes per lane: a pass of a wave stages 8 whole blocks.  Up to 4 passes' loads are
+    // issued before any is used.  Then 8 lanes form the blocks' sums in chain order over
+    // the values as staged (Q4_0 positions 16..31 divided by 16, multiplied back exactly);
+    // a wave's LDS accesses complete in order, so its own stores are visible to its reads.
     const __amdgpu_buffer_rsrc_t rx =
         __builtin_amdgcn_make_buffer_rsrc((void*)sc.x, (short)0, sc.nb * 128, 0x00020000);
-    for (int blk = tid; blk < sc.nb; blk += kP1Threads) {
-      f32x4 v[8];
+    const int nch = sc.nb * 8;
+    for (int c00 = wave * 64; c00 < nch; c00 += 4 * kP1Threads) {
+      f32x4 v[4];
 #pragma unroll
-      for (int i = 0; i < 8; i++)
-        v[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, blk * 128 + i * 16, 0, 16));
-      if (FMT == FQ4) {
+      for (int q = 0; q < 4; q++)  // past the end reads zeros
+        v[q] = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (c00 + q * kP1Threads + lane) * 16, 0, 16));
 #pragma unroll
-        for (int i = 4; i < 8; i++) v[i] = v[i] * 0.0625f;
+      for (int q = 0; q < 4; q++) {
+        const int c0 = c00 + q * kP1Threads;
+        if (c0 < nch) {
+          const int c = c0 + lane;
+          const int blk = c >> 3, i = c & 7;
+          f32x4 w = v[q];
+          if (FMT == FQ4 && i >= 4) w = w * 0.0625f;
+          if (c < nch) *reinterpret_cast<f32x4*>(xlds + blk * kBlkLds + i * 16) = w;
+          asm volatile("" ::: "memory");
+          const int b = (c0 >> 3) + lane;
+          if (lane < 8 && b < sc.nb) {
+            const f32x4* xl = reinterpret_cast<const f32x4*>(xlds + b * kBlkLds);
+            float s = xl[0].x;
+            s = s + xl[0].y; s = s + xl[0].z; s = s + xl[0].w;
+#pragma unroll
+            for (int k = 1; k < 4; k++) { s = s + xl[k].x; s = s + xl[k].y; s = s + xl[k].z; s = s + xl[k].w; }
+            const float m = FMT == FQ4 ? 16.0f : 1.0f;
+#pragma unroll
+            for (int k = 4; k < 8; k++) {
+              s = s + xl[k].x * m; s = s + xl[k].y * m; s = s + xl[k].z * m; s = s + xl[k].w * m;
+            }
+            *reinterpret_cast<float*>(xlds + b * kBlkLds + 128) = s;
+          }
+          asm volatile("" ::: "memory");
+        }
       }
-      f32x4* dst = reinterpret_cast<f32x4*>(xlds + blk * kBlkLds);
-#pragma unroll
-      for (int i = 0; i < 8; i++) dst[i] = v[i];
-      float s = v[0].x;
-      s = s + v[0].y; s = s + v[0].z; s = s + v[0].w;
-#pragma unroll
-      for (int i = 1; i < 4; i++) { s = s + v[i].x; s = s + v[i].y; s = s + v[i].z; s = s + v[i].w; }
-      const float m = FMT == FQ4 ? 16.0f : 1.0f;
-#pragma unroll
-      for (int i = 4; i < 8; i++) {
-        s = s + v[i].x * m; s = s + v[i].y * m; s = s + v[i].z * m; s = s + v[i].w * m;
-      }
-      *reinterpret_cast<float*>(xlds + blk * kBlkLds + 128) = s;
     }
     __syncthreads();
     lds_lane = xlds + cg * kBlkLds;
+    lds_last = ((sc.ns - 1) << sc.lg2G) + cg < sc.nb ? lds_lane + (sc.ns - 1) * (sc.G * kBlkLds)
+                                                     : xlds + (sc.nb - 1) * kBlkLds;  // its d is 0
   };
 
   enter();
@@ -699,26 +736,50 @@ __global__ __launch_bounds__(kP1Threads) void k_qmv_chain(ChainArgs a) {
 #pragma unroll
       for (int p = 0; p < P; p++) {
         if (creal > 0) {  // uniform: a real step of this wave
-          const char* xb = lds_lane + cj * (sc.G * kBlkLds);
-          if (sc.ragged && cj * sc.G + cg >= sc.nb)  // past K: reuse the last block; its d is 0
-            xb = xlds + (sc.nb - 1) * kBlkLds;
+          const char* xb = cj == sc.ns - 1 ? lds_last : lds_lane + cj * (sc.G * kBlkLds);
           const f32x4* xl = reinterpret_cast<const f32x4*>(xb);
           const float sx = *reinterpret_cast<const float*>(xb + 128);
           const float c = chain_m1<FMT>(ring_q[p], xl);
           const float rr = fmaf(FMT == FQ4 ? -8.0f : -128.0f, sx, c);
           acc = fmaf(h2f(ring_d[p]), rr, acc);
           --creal;
-          if (++cj == sc.ns) {  // tile done: reduce over the lane group, store its row
+          ++cj;
+          if (cj == sc.ns || creal == 0) {  // this wave's part of the tile is done
             float v = acc;
             for (int off = sc.G >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-            const int row = (wave + ct * kP1Waves) * sc.gpw + clg;
-            if (cg == 0 && row < sc.nrows)  // agent-coherent global store: a later GEMV may read it
+            // waves holding the tile: the wave of step s is (16 s + 15) / S; when S < 16 each
+            // non-empty wave holds one step
+            const int t0 = ct * sc.ns, t1 = t0 + sc.ns;
+            const int w0 = (16 * t0 + 15) / sc.S, wl = (16 * (t1 - 1) + 15) / sc.S;
+            const int parts = sc.S >= 16 ? wl - w0 + 1 : sc.ns;
+            const int row = ct * sc.gpw + clg;
+            bool put = parts == 1;
+            if (!put) {
+              if (cg == 0) part[(wave * 2 + (t0 >= sc.start ? 1 : 0)) * 4 + clg] = v;
+              asm volatile("" ::: "memory");
+              int before = 0;
+              if (lane == 0)
+                before = __hip_atomic_fetch_add(&done[w0], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+              before = __builtin_amdgcn_readfirstlane(before);
+              asm volatile("" ::: "memory");
+              if (before == parts - 1) {  // the last part in: every part is in `part`
+                v = part[(w0 * 2 + 1) * 4 + clg];
+                for (int u = w0 + 1; u <= wl; u++)
+                  if (sc.S >= 16 || ((u * sc.S) >> 4) < (((u + 1) * sc.S) >> 4))
+                    v = v + part[(u * 2) * 4 + clg];
+                if (lane == 0) done[w0] = 0;
+                put = true;
+              }
+            }
+            if (put && cg == 0 && row < sc.nrows)  // agent-coherent: a later GEMV may read it
               __hip_atomic_store((__attribute__((address_space(1))) float*)sc.y + row, v,
                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             asm volatile("" ::: "memory");  // keep the store ahead of this step's loads
             acc = 0.f;
-            cj = 0;
-            ++ct;
+            if (cj == sc.ns) {
+              cj = 0;
+              ++ct;
+            }
           }
         }
         issue(ring_q[p], ring_d[p]);  // refill the slot just consumed
@@ -950,7 +1011,8 @@ QmvIdKernel select_id(int G, int R) {
 #ifndef BQM_P1_P
 #define BQM_P1_P 4  // blocks in flight per lane (Q4_0; Q8_0 blocks are twice as long: half)
 #endif
-constexpr int kP1MaxLds = 160 * 1024 - 256;  // a CU's LDS, less the kernel's static LDS
+constexpr int kP1StaticLds = 1024;                   // reserved for the kernel's own __shared__
+constexpr int kP1MaxLds = 160 * 1024 - kP1StaticLds;  // dynamic LDS of a chain launch
 
 using ChainKernel = void (*)(ChainArgs);
 
@@ -998,6 +1060,14 @@ int launch_chain(int fmt, const GemvDesc* descs, const GemvDesc* one, int n, uin
   a.n = n;
   a.sync = sync;
   ChainKernel k = chain_kernel(fmt);
+  static int static_ok[2] = {0, 0};  // per format: 1 = the kernel's static LDS fits the reserve
+  int& ok = static_ok[fmt == BQM_Q4_0 ? 0 : 1];
+  if (ok == 0) {
+    hipFuncAttributes fa;
+    ok = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(k)) == hipSuccess &&
+                 fa.sharedSizeBytes <= (size_t)kP1StaticLds ? 1 : -1;
+  }
+  if (ok < 0) return BQM_E_LAUNCH;
   allow_lds(k, kP1MaxLds);
   const int grid = cu_count();
   if (sync) {
@@ -1024,21 +1094,29 @@ int chain_prepare(const bqm_gemv* descs, int n, void* ws, hipStream_t s) {
   const int fmt = descs[0].fmt;
   if (fmt != BQM_Q4_0 && fmt != BQM_Q8_0) return BQM_E_UNSUPPORTED;
   const int CB = fmt == BQM_Q4_0 ? 16 : 32;
-  const int cus = cu_count();
+  // checks of the descriptors alone first (no HIP call before they pass)
   int64_t max_k = 0;
-  for (int i = 0; i < n; i++) max_k = descs[i].K > max_k ? descs[i].K : max_k;
-  if (chain_lds_bytes(n, max_k) > kP1MaxLds) return BQM_E_SHAPE;
   for (int i = 0; i < n; i++) {
     const bqm_gemv& d = descs[i];
     if (d.fmt != fmt) return BQM_E_UNSUPPORTED;
     if (d.N < 1 || d.N > ((int64_t)1 << 30) || d.K < kQK || d.K % kQK != 0 || d.K > chain_max_k())
       return BQM_E_SHAPE;
-    if (((d.N + cus - 1) / cus + 1) * (d.K / kQK) * CB >= ((int64_t)1 << 31)) return BQM_E_SHAPE;
+    max_k = d.K > max_k ? d.K : max_k;
+  }
+  if (chain_lds_bytes(n, max_k) > kP1MaxLds) return BQM_E_SHAPE;
+  for (int i = 0; i < n; i++) {
+    const bqm_gemv& d = descs[i];
     if (!d.w_packed || !d.x || !d.y) return BQM_E_NULL;
     if (((uintptr_t)d.w_packed & 15) || ((uintptr_t)d.x & 15) || ((uintptr_t)d.y & 3))
       return BQM_E_ALIGN;
   }
+  // then the ones that depend on the device: one workgroup's rows must stay below 2 GiB
+  const int cus = cu_count();
   if (cus > kChainMaxWorkgroups) return BQM_E_UNSUPPORTED;
+  for (int i = 0; i < n; i++) {
+    const bqm_gemv& d = descs[i];
+    if (((d.N + cus - 1) / cus + 1) * (d.K / kQK) * CB >= ((int64_t)1 << 31)) return BQM_E_SHAPE;
+  }
   uint32_t head[8] = {0, 0, 0, (uint32_t)n, (uint32_t)fmt, 0, 0, 0};
   if (hipMemsetAsync(ws, 0, kChainSyncBytes, s) != hipSuccess ||
       hipMemcpyAsync(ws, head, sizeof(head), hipMemcpyHostToDevice, s) != hipSuccess ||

@@ -129,8 +129,8 @@ typedef struct bqm_gemv {
 } bqm_gemv;
 
 /* Largest K of a chain GEMV (its x is staged in the LDS of one workgroup).  A chain of n
- * GEMVs also needs 48 * n + 4.5 * max(K) <= 163584 bytes of LDS (about 1700 GEMVs at
- * K = 5120); bqm_chain_prepare returns BQM_E_SHAPE otherwise. */
+ * GEMVs also needs 48 * n + 4.5 * max(K) <= 162816 bytes of LDS (about 2900 GEMVs when the
+ * longest K is 5120, 1760 when it is 17408); bqm_chain_prepare returns BQM_E_SHAPE otherwise. */
 #define BQM_CHAIN_MAX_K 32768
 
 /* Device bytes of the workspace of an n-GEMV chain (0 if n < 1). */

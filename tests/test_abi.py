@@ -34,11 +34,14 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_packed_bytes():
-    # Q4_0 4096 x 4096: 16 B of codes + 2 B of scale per block, sections 256-aligned
+    # Q4_0 4096 x 4096: 16 B of codes + 2 B of scale per block, sections 256-aligned, at
+    # least 16 bytes of slack after the scales
     nb = 4096 * 4096 // 32
-    assert bqm.packed_bytes("q4_0", 4096, 4096) == nb * 16 + nb * 2
-    assert bqm.packed_bytes("q8_0", 17408, 5120) == 17408 * 5120 + 17408 * 160 * 2
-    assert bqm.packed_bytes("q4_0", 3, 32) == 256 + 256    # 48 B codes -> 256, 6 B scales -> 256
+    assert bqm.packed_bytes("q4_0", 4096, 4096) == nb * 16 + nb * 2 + 256
+    assert bqm.packed_bytes("q8_0", 17408, 5120) == 17408 * 5120 + 17408 * 160 * 2 + 256
+    assert bqm.packed_bytes("q4_0", 3, 32) == 256 + 256    # 48 B codes -> 256, 6 + 16 B -> 256
+    assert bqm.packed_bytes("q4_0", 1, 32 * 120) == 2048 + 256   # 240 B scales + 16 -> 256
+    assert bqm.packed_bytes("q4_0", 1, 32 * 128) == 2048 + 512   # 256 B scales + 16 -> 512
     assert bqm.packed_bytes("q4_0", 0, 64) == 0
     assert bqm.packed_bytes("q4_0", 5, 33) == 0             # K not a multiple of 32
     assert bqm.packed_bytes(3, 5, 32) == 0                  # unknown format
@@ -103,3 +106,38 @@ def test_empty_sizes_are_no_ops():
     assert L.qmm_q8_0(None, None, None, None, 0, 8, 64, None) == 0
     assert L.bqm_repack(2, None, None, 0, 64, None) == 0
     assert L.bqm_unpack(8, None, None, 4, 0, None) == 0
+
+
+def _gemv(N, K, fmt="q4_0", ptr=0x10000, wait=0):
+    return bqm.Gemv(ptr, ptr, ptr, N, K, bqm.FMT[fmt], wait)
+
+
+def test_chain_host_validation():
+    """bqm_chain_prepare rejects bad descriptor lists before any device work (the
+    descriptor checks run before the runtime is queried); host addresses stand in for
+    device pointers since nothing is dereferenced."""
+    ws = 0x20000  # 16-byte aligned stand-in
+    L = bqm.lib()
+
+    def prep(descs, n=None, w=ws):
+        arr = (bqm.Gemv * max(1, len(descs)))(*descs)
+        return L.bqm_chain_prepare(ctypes.cast(arr, ctypes.c_void_p), len(descs) if n is None else n,
+                                   ctypes.c_void_p(w), None)
+
+    assert bqm.chain_workspace_bytes(0) == 0
+    assert bqm.chain_workspace_bytes(2) - bqm.chain_workspace_bytes(1) == ctypes.sizeof(bqm.Gemv) == 48
+    assert prep([], n=0) == 2                                    # empty chain
+    assert prep([_gemv(64, 64)], w=0) == 1                       # no workspace
+    assert prep([_gemv(64, 64)], w=ws + 8) == 3                  # misaligned workspace
+    assert prep([_gemv(64, 64), _gemv(64, 64, "q8_0")]) == 4     # mixed formats
+    assert prep([_gemv(64, 48)]) == 2                            # K % 32 != 0
+    assert prep([_gemv(64, 32800)]) == 2                         # K over the chain limit
+    assert prep([_gemv(0, 64)]) == 2                             # empty GEMV
+    assert prep([_gemv(64, 64, ptr=0)]) == 1                     # null matrix
+    assert prep([_gemv(64, 64, ptr=0x10008)]) == 3               # misaligned matrix
+    # LDS: 48 n + 4.5 max(K) <= 162816 bytes.  At K = 17408 the largest chain is 1760
+    # GEMVs: one more is rejected for LDS (before the null-pointer check of the stand-ins)
+    assert prep([_gemv(64, 17408, ptr=0)] * 1761) == 2
+    assert prep([_gemv(64, 17408, ptr=0)] * 1760) == 1
+    assert prep([_gemv(64, 32768, ptr=0)] * 320) == 1
+    assert prep([_gemv(64, 32768, ptr=0)] * 321) == 2

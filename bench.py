@@ -184,17 +184,17 @@ def run_dense(args, torch, gen, bqm, fmt="q4_0"):
 
     total = wbytes + abytes
     per_bytes = np.array([weight_bytes(fmt, N, K) + 4 * M * (K + N) for _, N, K in mats])
-    use_chain = M == 1 and not args.separate
+    use_chain = not args.separate
     if use_chain:
         # one launch per token: the 256 GEMVs in layer order, each waiting (device-wide)
         # for all earlier ones, as a decode step's data dependencies require
-        descs = [bqm.gemv(fmt, w, x, y, N, K, wait=i > 0)
+        descs = [bqm.gemv(fmt, w, x, y, N, K, wait=i > 0, M=M)
                  for i, ((w, N, K), x, y) in enumerate(zip(mats, xs, ys))]
         ws = torch.zeros(bqm.chain_workspace_bytes(len(descs)), dtype=torch.uint8, device="cuda")
         bqm.bqm_chain_prepare(descs, ws)
 
         def run():
-            bqm.qmv_chain(fmt, ws, len(descs))
+            bqm.qmv_chain(fmt, M, ws, len(descs))
 
         ms = time_steps(run, args.steps, args.warmup, torch, False)
         status = bqm.bqm_chain_status(ws)
@@ -202,9 +202,9 @@ def run_dense(args, torch, gen, bqm, fmt="q4_0"):
             raise RuntimeError(f"chain reported error {status}")
         dur = per_launch_ms([run], torch, reps=max(3, args.steps // 2))
         achieved = total / (float(dur.mean()) * 1e-3) / 1e9
-        kernel = f"k_qmv_chain ({fmt.upper()}, {len(descs)} GEMVs per launch)"
+        kernel = f"k_qmv_chain ({fmt.upper()}, M={M}, {len(descs)} GEMVs per launch)"
         launch_us = round(1e3 * float(dur.mean()), 3)
-        kkey = f"qmv_chain_{fmt}_dense27b"
+        kkey = f"qmv_chain_{fmt}_dense27b" if M == 1 else f"qmv_chain_{fmt}_m{M}_dense27b"
     else:
         ms = time_steps(run_separate, args.steps, args.warmup, torch, not args.no_graph)
         dur = per_launch_ms(launches, torch)

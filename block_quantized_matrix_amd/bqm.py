@@ -53,7 +53,7 @@ def lib():
         L.bqm_chain_workspace_bytes.argtypes = [I]
         L.bqm_chain_workspace_bytes.restype = SZ
         L.bqm_chain_prepare.argtypes = [P, I, P, P]
-        L.qmv_chain.argtypes = [I, P, I, P]
+        L.qmv_chain.argtypes = [I, I, P, I, P]
         L.bqm_chain_status.argtypes = [P, P]
         for f in ("bqm_chain_prepare", "qmv_chain", "bqm_chain_status"):
             getattr(L, f).restype = I
@@ -132,7 +132,7 @@ class Gemv(ctypes.Structure):
     """One GEMV of a chain (the C struct bqm_gemv)."""
     _fields_ = [("w_packed", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
                 ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("fmt", ctypes.c_int32),
-                ("wait", ctypes.c_int32)]
+                ("wait", ctypes.c_int32), ("M", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 CHAIN_MAX_K = 32768
@@ -150,16 +150,17 @@ def bqm_chain_prepare(descs, workspace, stream=None):
           _stream(stream))
 
 
-def qmv_chain(fmt, workspace, n: int, stream=None):
-    _call("qmv_chain", _fmt(fmt), _ptr(workspace), n, _stream(stream))
+def qmv_chain(fmt, M: int, workspace, n: int, stream=None):
+    _call("qmv_chain", _fmt(fmt), M, _ptr(workspace), n, _stream(stream))
 
 
 def bqm_chain_status(workspace, stream=None) -> int:
     return int(lib().bqm_chain_status(_ptr(workspace), _stream(stream)))
 
 
-def gemv(fmt, w_packed, x, y, N: int, K: int, wait: bool) -> Gemv:
-    return Gemv(w_packed.data_ptr(), x.data_ptr(), y.data_ptr(), N, K, _fmt(fmt), 1 if wait else 0)
+def gemv(fmt, w_packed, x, y, N: int, K: int, wait: bool, M: int = 1) -> Gemv:
+    """Descriptor of one GEMV of a chain: x [M][K], y [M][N] (torch tensors on the device)."""
+    return Gemv(w_packed.data_ptr(), x.data_ptr(), y.data_ptr(), N, K, _fmt(fmt), 1 if wait else 0, M, 0)
 
 
 # ---- conveniences built only from the calls above (allocation through torch) ----

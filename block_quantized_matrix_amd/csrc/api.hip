@@ -135,12 +135,12 @@ int bqm_chain_prepare(const bqm_gemv* descs, int n, void* workspace, hipStream_t
   return chain_prepare(descs, n, workspace, stream);
 }
 
-int qmv_chain(int fmt, void* workspace, int n, hipStream_t stream) {
+int qmv_chain(int fmt, int M, void* workspace, int n, hipStream_t stream) {
   if (!valid_fmt(fmt)) return BQM_E_UNSUPPORTED;
-  if (n < 1 || n > (1 << 20)) return BQM_E_SHAPE;
+  if (n < 1 || n > (1 << 20) || M < 1 || M > BQM_QMV_MAX_M) return BQM_E_SHAPE;
   if (!workspace) return BQM_E_NULL;
   if (!aligned16(workspace)) return BQM_E_ALIGN;
-  return chain_launch(fmt, workspace, n, stream);
+  return chain_launch(fmt, M, workspace, n, stream);
 }
 
 int bqm_chain_status(const void* workspace, hipStream_t stream) {

@@ -61,7 +61,7 @@ int launch_fill(float* y, int64_t n, float v, hipStream_t s);
 int64_t chain_max_k();
 size_t chain_workspace_bytes(int n);
 int chain_prepare(const bqm_gemv* descs, int n, void* ws, hipStream_t s);
-int chain_launch(int fmt, void* ws, int n, hipStream_t s);
+int chain_launch(int fmt, int M, void* ws, int n, hipStream_t s);
 int chain_status(const void* ws, hipStream_t s);
 
 }  // namespace bqm

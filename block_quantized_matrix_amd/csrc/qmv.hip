@@ -301,61 +301,42 @@ __device__ __forceinline__ void tile_qmv(const uint8_t* __restrict__ codes,
   }
 }
 
-// Dense GEMV: workgroup b computes rows [b * RPW, +RPW) for all M inputs.
-template <int FMT, int MM, int G, int R>
-__global__ __launch_bounds__(kThreads) void k_qmv(const uint8_t* __restrict__ codes,
-                                                  const uint16_t* __restrict__ scales,
-                                                  const float* __restrict__ X,
-                                                  float* __restrict__ Y, int M, int N, int nb,
-                                                  int kcb) {
-  extern __shared__ float4 smem[];
-  constexpr int RPW = (kThreads / G) * R;
-  const int64_t row_base = (int64_t)blockIdx.x * RPW;
-  const int nrows = (int)min((int64_t)RPW, (int64_t)N - row_base);
-  __shared__ TileIO io;
-  if (threadIdx.x < 8) {
-    const int m = threadIdx.x < M ? threadIdx.x : 0;
-    io.x[threadIdx.x] = (int64_t)m * nb * kQK;
-    io.y[threadIdx.x] = (int64_t)m * N + row_base;
-  }
-  // (nb >= 1 here: the first chunk barrier inside tile_qmv publishes io)
-  tile_qmv<FMT, MM, G, R>(codes, scales, nb, row_base, nrows, X, Y, &io, M, smem, kcb);
-}
-
-// ---- persistent batch-1 GEMV chain ------------------------------------------------
-// The batch-1 product is the bandwidth-critical one, so it gets its own kernel shaped
+// ---- persistent GEMV chain ------------------------------------------------------------
+// Decode is bandwidth-critical, so the batch-M (M <= 8) product gets its own kernel shaped
 // around the VALU budget and around the cost of starting a kernel (Q4_0 at 8 TB/s delivers
 // 14.2 T weights/s against 39.3 T fp32 lane-ops/s, about 2.8 ops per weight).  One launch
 // runs a chain of GEMVs in order (a single GEMV is a chain of one):
 //  - One 1024-thread workgroup per CU owns, for each GEMV, a contiguous range of rows and
-//    stages that GEMV's x into LDS once.  Blocks are 144 bytes apart in LDS: 128 bytes of
+//    stages that GEMV's M inputs into LDS.  Blocks are 144 bytes apart in LDS: 128 bytes of
 //    x, then the block's x sum; with that stride eight neighbouring blocks start in eight
 //    different 16-byte bank groups, so the per-lane block reads are conflict-free with
 //    immediate offsets.  For Q4_0 the x values that meet the high nibbles are stored
 //    divided by 16 (exact), so one FMA chain takes the nibbles in place (16 n * x / 16).
+//  - When M inputs of K do not fit, a GEMV is walked in chunks of kc blocks of K: the
+//    workgroup stages one chunk of x at a time and keeps each row's partial sums in LDS,
+//    adding the chunks in order.
 //  - Codes and scales come through buffer loads: the per-lane part of the offset is a
 //    constant register, the per-step part a scalar, so a load costs no VALU address
 //    arithmetic.  Lanes past the workgroup's last row (or past K in a ragged last step)
 //    use an offset beyond the descriptor and read zeros.
 //  - Each lane keeps P blocks in flight in a register ring consumed in place (the loop is
-//    unrolled by P).  The ring runs ahead across GEMV boundaries: the weights of the next
-//    GEMV do not depend on its input, so they stream while the workgroup waits for the
-//    previous GEMV's outputs (device-wide barrier) and stages the new x.
-//  - The waves of a workgroup take tiles of 64/G rows round-robin; a lane group reduces
-//    and stores a row when its last block is done.
-// Arithmetic per block and row: 8 ANDs, 32 v_cvt_f32_ubyte, 32 FMAs in one chain, then
-// r = chain - 8 * sum(x) (Q8_0: - 128 * sum(x)) and acc += d * r (v_fma_mix: d stays fp16).
-// The chain and the block sum follow the same order and 8, 128 and 1/16 are powers of
-// two, so neutral codes give exactly zero.
-constexpr int kP1Threads = 1024;
-constexpr int kP1Waves = kP1Threads / 64;
+//    unrolled by P).  The ring runs ahead across GEMV and chunk boundaries: the weights of
+//    the next GEMV do not depend on its input, so they stream while the workgroup waits for
+//    the previous GEMV's outputs (device-wide barrier) and stages the new x.
+// Arithmetic per block and row: 8 ANDs (Q8_0: XORs) and 32 v_cvt_f32_ubyte, shared by the
+// M inputs; per input 32 FMAs in one chain, then r = chain - 8 * sum(x) (Q8_0: - 128 *
+// sum(x)) and acc += d * r (v_fma_mix: d stays fp16).  The chain and the block sum follow
+// the same order and 8, 128 and 1/16 are powers of two, so neutral codes give exactly zero.
+constexpr int kP1Waves = 16;  // waves of a workgroup (8 for the widest batch: registers)
 constexpr int kBlkLds = 144;  // LDS bytes per staged block
+constexpr int kChainMaxM = 8;
 
-// Chain order of one block: positions 0..15 (low nibbles / first 16 bytes), then 16..31.
-template <int FMT>
-__device__ __forceinline__ float chain_m1(const Codes<FMT>& q, const f32x4* __restrict__ xl) {
-  // xl: the staged block (8 chunks of 4 floats), Q4_0 chunks 4..7 already divided by 16
-  float acc;
+// One block of codes against MM staged input blocks (input m at xb + m * mstride bytes):
+// c[m] = sum_j code_j * x_mj in chain order (positions 0..15, then 16..31).
+template <int FMT, int MM>
+__device__ __forceinline__ void chain_block(const Codes<FMT>& q, const char* xb, int mstride,
+                                            float (&c)[MM]) {
+  auto xm = [&](int m, int k) { return *reinterpret_cast<const f32x4*>(xb + m * mstride + k * 16); };
   if constexpr (FMT == FQ4) {
     uint32_t l[4], h[4];
     const uint32_t w[4] = {q.a.x, q.a.y, q.a.z, q.a.w};
@@ -367,15 +348,23 @@ __device__ __forceinline__ float chain_m1(const Codes<FMT>& q, const f32x4* __re
     }
 #pragma unroll
     for (int k = 0; k < 4; k++) {
-      const f32x4 a = xl[k];
-      if (k == 0) acc = ub(l[k], 0) * a.x; else acc = fmaf(ub(l[k], 0), a.x, acc);
-      acc = fmaf(ub(l[k], 1), a.y, acc); acc = fmaf(ub(l[k], 2), a.z, acc); acc = fmaf(ub(l[k], 3), a.w, acc);
+      const float v0 = ub(l[k], 0), v1 = ub(l[k], 1), v2 = ub(l[k], 2), v3 = ub(l[k], 3);
+#pragma unroll
+      for (int m = 0; m < MM; m++) {
+        const f32x4 a = xm(m, k);
+        if (k == 0) c[m] = v0 * a.x; else c[m] = fmaf(v0, a.x, c[m]);
+        c[m] = fmaf(v1, a.y, c[m]); c[m] = fmaf(v2, a.z, c[m]); c[m] = fmaf(v3, a.w, c[m]);
+      }
     }
 #pragma unroll
     for (int k = 0; k < 4; k++) {
-      const f32x4 b = xl[k + 4];
-      acc = fmaf(ub(h[k], 0), b.x, acc); acc = fmaf(ub(h[k], 1), b.y, acc);
-      acc = fmaf(ub(h[k], 2), b.z, acc); acc = fmaf(ub(h[k], 3), b.w, acc);
+      const float v0 = ub(h[k], 0), v1 = ub(h[k], 1), v2 = ub(h[k], 2), v3 = ub(h[k], 3);
+#pragma unroll
+      for (int m = 0; m < MM; m++) {
+        const f32x4 b = xm(m, k + 4);
+        c[m] = fmaf(v0, b.x, c[m]); c[m] = fmaf(v1, b.y, c[m]);
+        c[m] = fmaf(v2, b.z, c[m]); c[m] = fmaf(v3, b.w, c[m]);
+      }
     }
   } else {
     const uint32_t w[8] = {q.a.x, q.a.y, q.a.z, q.a.w, q.b.x, q.b.y, q.b.z, q.b.w};
@@ -383,12 +372,34 @@ __device__ __forceinline__ float chain_m1(const Codes<FMT>& q, const f32x4* __re
     for (int k = 0; k < 8; k++) {
       uint32_t u = w[k] ^ 0x80808080u;  // q + 128 as unsigned bytes
       asm("" : "+v"(u));
-      const f32x4 a = xl[k];
-      if (k == 0) acc = ub(u, 0) * a.x; else acc = fmaf(ub(u, 0), a.x, acc);
-      acc = fmaf(ub(u, 1), a.y, acc); acc = fmaf(ub(u, 2), a.z, acc); acc = fmaf(ub(u, 3), a.w, acc);
+      const float v0 = ub(u, 0), v1 = ub(u, 1), v2 = ub(u, 2), v3 = ub(u, 3);
+#pragma unroll
+      for (int m = 0; m < MM; m++) {
+        const f32x4 a = xm(m, k);
+        if (k == 0) c[m] = v0 * a.x; else c[m] = fmaf(v0, a.x, c[m]);
+        c[m] = fmaf(v1, a.y, c[m]); c[m] = fmaf(v2, a.z, c[m]); c[m] = fmaf(v3, a.w, c[m]);
+      }
     }
   }
-  return acc;
+}
+
+// Sum over the lane group of 16, 32 or 64 lanes holding one row (every lane gets the sum):
+// DPP exchanges within 16-lane rows, then cross-row exchanges.  The partners of each step
+// add the same two values, so all lanes hold bitwise the same result.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v),
+                                                               __builtin_bit_cast(int, v), CTRL, 0xF,
+                                                               0xF, false));
+}
+__device__ __forceinline__ float group_sum_rt(float v, int lg2G) {
+  v = v + dpp<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
+  v = v + dpp<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
+  v = v + dpp<0x141>(v);  // row_half_mirror: the other quad of the 8
+  v = v + dpp<0x140>(v);  // row_mirror: the other 8 of the 16
+  if (lg2G >= 5) v = v + __shfl_xor(v, 16, 64);
+  if (lg2G >= 6) v = v + __shfl_xor(v, 32, 64);
+  return v;
 }
 
 // Description of one GEMV of a chain (the device image of bqm_gemv).
@@ -397,7 +408,7 @@ struct GemvDesc {
   const float* x;
   float* y;
   int64_t N, K;
-  int32_t fmt, wait;
+  int32_t fmt, wait, M, reserved;
 };
 static_assert(sizeof(GemvDesc) == sizeof(bqm_gemv), "bqm_gemv layout");
 
@@ -405,7 +416,9 @@ struct ChainArgs {
   const GemvDesc* descs;  // n descriptors in device memory, or null: use `one`
   GemvDesc one;
   int n;
-  uint32_t* sync;         // device-wide barrier words {count, generation, error}; null if n == 1
+  int kc;                 // K blocks staged at a time (`one` only; else in the workspace)
+  int pacc_rows;          // rows per workgroup of the partial-sum buffer (likewise)
+  uint32_t* sync;         // workspace words (see grid_barrier); null for a chain of one
 };
 
 // Per-GEMV values of one workgroup, computed once at kernel start (one thread per GEMV)
@@ -413,26 +426,20 @@ struct ChainArgs {
 struct StageRow {
   const uint8_t* codes;     // this workgroup's first row of codes
   const uint16_t* scales;   // ... and of scales
-  const float* x;
-  float* y;                 // this workgroup's first output row
-  int32_t nrows;            // rows of this workgroup
-  int32_t nb;               // blocks per row
-  int32_t info;             // lg2(G) | ragged << 8 | wait << 9
-  int32_t ns;               // steps per tile (blocks per lane)
+  const float* x;           // input row 0
+  float* y;                 // output row 0, this workgroup's first row
+  int32_t nrows, nb;        // rows of this workgroup; blocks per row
+  int32_t wait, M;
+  int32_t xstride, ystride; // floats between input rows (K) and between output rows (N)
+  int32_t nchunks, pad;     // chunks of kc blocks
 };
-static_assert(sizeof(StageRow) == 48, "stage table row");
+static_assert(sizeof(StageRow) == 64, "stage table row");
 
 template <int FMT>
-__device__ __forceinline__ StageRow make_stage(const GemvDesc& d) {
+__device__ __forceinline__ StageRow make_stage(const GemvDesc& d, int kc) {
   constexpr int CB = FMT == FQ4 ? 16 : 32;
   const int nb = (int)(d.K >> 5);
   const int N = (int)d.N;
-  // lane group: the width among 64/32/16 that leaves the fewest idle lanes in a row
-  const int w64 = (-nb) & 63, w32 = (-nb) & 31, w16 = (-nb) & 15;
-  int lg2 = 6;
-  if (w32 < w64) lg2 = 5;
-  if (w16 < (lg2 == 6 ? w64 : w32)) lg2 = 4;
-  const int G = 1 << lg2;
   // rows split as evenly as possible: the first N % grid workgroups get one more
   const int grid = (int)gridDim.x, b = (int)blockIdx.x;
   const int base = N / grid, extra = N - base * grid;
@@ -446,20 +453,23 @@ __device__ __forceinline__ StageRow make_stage(const GemvDesc& d) {
   st.y = d.y + r0;
   st.nrows = base + (b < extra ? 1 : 0);
   st.nb = nb;
-  st.info = lg2 | ((nb & (G - 1)) != 0 ? 1 << 8 : 0) | (d.wait ? 1 << 9 : 0);
-  st.ns = (nb + G - 1) >> lg2;
+  st.wait = d.wait ? 1 : 0;
+  st.M = d.M;
+  st.xstride = (int)d.K;
+  st.ystride = N;
+  st.nchunks = (nb + kc - 1) / kc;
+  st.pad = 0;
   return st;
 }
 
-// Uniform copy of a table row (LDS reads made scalar).
+// Uniform values of one chunk of one GEMV for one wave.
 struct Stage {
   const uint8_t* codes;
   const uint16_t* scales;
   const float* x;
   float* y;
-  int nrows, nb, lg2G, G, gpw, ns;
-  int S, start, end;  // the workgroup's steps (tiles x steps per tile); this wave's range
-  bool ragged, wait;
+  int nrows, nb, nbc, kb0, lg2G, G, gpw, ns, S, start, end, M, xstride, ystride, nchunks;
+  bool ragged, wait, first, last;
 };
 
 // __builtin_amdgcn_readfirstlane is 32 bits wide: a 64-bit value takes two.
@@ -469,7 +479,8 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t v) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-__device__ __forceinline__ void load_stage(const StageRow* t, int i, int wave, Stage& s) {
+template <int LGW>  // log2 of the waves of the workgroup
+__device__ __forceinline__ void load_stage(const StageRow* t, int i, int c, int kc, int wave, Stage& s) {
   const StageRow r = t[i];
   s.codes = reinterpret_cast<const uint8_t*>(uniform64(reinterpret_cast<uint64_t>(r.codes)));
   s.scales = reinterpret_cast<const uint16_t*>(uniform64(reinterpret_cast<uint64_t>(r.scales)));
@@ -477,29 +488,43 @@ __device__ __forceinline__ void load_stage(const StageRow* t, int i, int wave, S
   s.y = reinterpret_cast<float*>(uniform64(reinterpret_cast<uint64_t>(r.y)));
   s.nrows = __builtin_amdgcn_readfirstlane(r.nrows);
   s.nb = __builtin_amdgcn_readfirstlane(r.nb);
-  const int info = __builtin_amdgcn_readfirstlane(r.info);
-  s.ns = __builtin_amdgcn_readfirstlane(r.ns);
-  s.lg2G = info & 0xff;
-  s.G = 1 << s.lg2G;
-  s.gpw = 64 >> s.lg2G;
-  s.ragged = (info >> 8) & 1;
-  s.wait = (info >> 9) & 1;
-  // tiles of gpw rows, ns steps each, in row order; the 16 waves take equal contiguous
+  s.M = __builtin_amdgcn_readfirstlane(r.M);
+  s.xstride = __builtin_amdgcn_readfirstlane(r.xstride);
+  s.ystride = __builtin_amdgcn_readfirstlane(r.ystride);
+  s.nchunks = __builtin_amdgcn_readfirstlane(r.nchunks);
+  const int wait = __builtin_amdgcn_readfirstlane(r.wait);
+  s.kb0 = c * kc;
+  s.nbc = min(kc, s.nb - s.kb0);
+  s.first = c == 0;
+  s.last = c == s.nchunks - 1;
+  s.wait = wait != 0 && c == 0;
+  // lane group: the width among 64/32/16 that leaves the fewest idle lanes in a row
+  const int w64 = (-s.nbc) & 63, w32 = (-s.nbc) & 31, w16 = (-s.nbc) & 15;
+  int lg2 = 6;
+  if (w32 < w64) lg2 = 5;
+  if (w16 < (lg2 == 6 ? w64 : w32)) lg2 = 4;
+  s.lg2G = lg2;
+  s.G = 1 << lg2;
+  s.gpw = 64 >> lg2;
+  s.ragged = (s.nbc & (s.G - 1)) != 0;
+  s.ns = (s.nbc + s.G - 1) >> lg2;
+  // tiles of gpw rows, ns steps each, in row order; the waves take equal contiguous
   // ranges of the tile-major step sequence (a tile may be split between waves)
-  const int ntiles = (s.nrows + s.gpw - 1) >> (6 - s.lg2G);
+  const int ntiles = (s.nrows + s.gpw - 1) >> (6 - lg2);
   s.S = ntiles * s.ns;
-  s.start = (wave * s.S) >> 4;
-  s.end = ((wave + 1) * s.S) >> 4;
+  s.start = (wave * s.S) >> LGW;
+  s.end = ((wave + 1) * s.S) >> LGW;
 }
 
 // Device-wide barrier between the GEMVs of a chain.  Workspace words: [0] release epoch,
-// [2] error, [3] n, [4] format; then one arrival flag per workgroup, each on its own
-// 128-byte line (no contended atomic).  Workgroup 0 waits for every flag to reach the
-// barrier's epoch and then publishes it in the release word, which the others wait for.
-// Data crossing the barrier (the outputs y and the next inputs x) is written and read with
-// agent-coherent (sc1) accesses, so no L2-wide write-back or invalidation is needed; the
-// outputs must only have landed before a workgroup arrives (see the wait below).  Every
-// wait is bounded: on timeout the error word is set and all workgroups leave.
+// [2] error, [3] n, [4] format, [5] kc, [6] partial-sum rows, [7] M class; then one arrival
+// flag per workgroup, each on its own 128-byte line (no contended atomic).  Workgroup 0
+// waits for every flag to reach the barrier's epoch and then publishes it in the release
+// word, which the others wait for.  Data crossing the barrier (the outputs y and the next
+// inputs x) is written and read with agent-coherent (sc1) accesses, so no L2-wide
+// write-back or invalidation is needed; the outputs must only have landed before a
+// workgroup arrives (see the wait below).  Every wait is bounded: on timeout the error
+// word is set and all workgroups leave.
 constexpr int kChainHeaderWords = 64;      // 256 bytes
 constexpr int kFlagStrideWords = 32;       // 128 bytes
 constexpr int kChainMaxWorkgroups = 512;
@@ -547,8 +572,24 @@ __device__ __forceinline__ bool grid_barrier(uint32_t* ws, uint32_t epoch, bool*
   return *lds_ok;
 }
 
-template <int FMT, int P>
-__global__ __launch_bounds__(kP1Threads) void k_qmv_chain(ChainArgs a) {
+// Dynamic LDS of a chain launch, in bytes from the start: the stage table, the split-tile
+// parts, their counters, the per-row partial sums of chunked GEMVs, the staged inputs.
+struct ChainLds {
+  int part, done, pacc, x, total;
+};
+__host__ __device__ inline ChainLds chain_lds(int n, int mm, int pacc_rows, int kc) {
+  ChainLds L;
+  L.part = (n * 64 + 15) & ~15;
+  L.done = L.part + kP1Waves * 2 * 4 * mm * 4;
+  L.pacc = L.done + kP1Waves * 4;
+  L.x = L.pacc + ((pacc_rows * mm * 4 + 15) & ~15);
+  L.total = L.x + mm * kc * kBlkLds;
+  return L;
+}
+
+template <int FMT, int P, int MM, int LGW>
+__global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
+  constexpr int NW = 1 << LGW, NT = 64 << LGW;  // waves, threads
   extern __shared__ float4 smem[];
   constexpr int CB = FMT == FQ4 ? 16 : 32;     // code bytes per block
   constexpr uint32_t kOob = 0x80000000u;       // lane offset past every descriptor: reads 0
@@ -556,35 +597,45 @@ __global__ __launch_bounds__(kP1Threads) void k_qmv_chain(ChainArgs a) {
   __shared__ bool lds_ok;
   __shared__ uint32_t lds_epoch;
   const int tid = threadIdx.x, lane = tid & 63;
-  if (a.sync && (a.sync[3] != (uint32_t)a.n || a.sync[4] != (uint32_t)(FMT == FQ4 ? BQM_Q4_0 : BQM_Q8_0))) {
+  if (a.sync && (a.sync[3] != (uint32_t)a.n || a.sync[4] != (uint32_t)(FMT == FQ4 ? BQM_Q4_0 : BQM_Q8_0) ||
+                 a.sync[7] != (uint32_t)MM)) {
     // the workspace was prepared for another chain: flag it, compute nothing
     if (blockIdx.x == 0 && tid == 0)
       __hip_atomic_store(a.sync + 2, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep in SGPRs
-  // LDS: the stage table, then the staged x
-  StageRow* table = reinterpret_cast<StageRow*>(smem);
-  char* xlds = reinterpret_cast<char*>(smem) + ((a.n * (int)sizeof(StageRow) + 15) & ~15);
-  for (int i = tid; i < a.n; i += kP1Threads) table[i] = make_stage<FMT>(a.descs ? a.descs[i] : a.one);
+  const int kc = a.sync ? (int)a.sync[5] : a.kc;
+  const int pacc_rows = a.sync ? (int)a.sync[6] : a.pacc_rows;
+  const ChainLds ly = chain_lds(a.n, MM, pacc_rows, kc);
+  char* lds = reinterpret_cast<char*>(smem);
+  StageRow* table = reinterpret_cast<StageRow*>(lds);
+  float* part = reinterpret_cast<float*>(lds + ly.part);
+  int* done = reinterpret_cast<int*>(lds + ly.done);
+  float* pacc = reinterpret_cast<float*>(lds + ly.pacc);
+  char* xlds = lds + ly.x;
+  const int mstride = kc * kBlkLds;  // bytes between the staged inputs
+  for (int i = tid; i < a.n; i += NT) table[i] = make_stage<FMT>(a.descs ? a.descs[i] : a.one, kc);
+  if (tid < NW) done[tid] = 0;
   if (tid == 0 && a.sync) lds_epoch = ld_agent(a.sync);  // stable until all have arrived once
   __syncthreads();
   uint32_t epoch = a.sync ? lds_epoch : 0u;
 
-  // Both sides walk the same sequence of steps: for each GEMV in which this wave has
-  // tiles, its steps padded to a multiple of P (padding steps load nothing useful and
-  // compute nothing), so a GEMV always ends at the end of an unrolled group.  Every step
-  // issues its loads, real or past the descriptor, so the number of loads in flight is
-  // the same on every path through the loop.
+  // Both sides walk the same sequence of steps: for each (GEMV, chunk) in which this wave
+  // has steps, its steps padded to a multiple of P (padding steps load nothing useful and
+  // compute nothing), so a chunk always ends at the end of an unrolled group.  Every step
+  // issues its loads, real or past the descriptor, so the number of loads in flight is the
+  // same on every path through the loop.
 
   // ---------------- issue side: P steps ahead ----------------
-  int gi = -1;               // GEMV being issued
+  int gi = -1, ci = 0;       // GEMV and chunk being issued
   Stage si;
+  si.nchunks = 0;
   int it = 0, ij = 0;        // this wave's tile, step in tile
   int ireal = 0, ipad = 0;   // real steps left; steps left with padding
   __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(nullptr, (short)0, 0, 0x00020000);
   __amdgpu_buffer_rsrc_t rs = rc;
-  uint32_t vc = kOob, vs = kOob;          // lane offsets in the current tile
+  uint32_t vc = kOob, vs = kOob;            // lane offsets in the current tile
   uint32_t vc_last = kOob, vs_last = kOob;  // ... at its last step (past K in a ragged row: zeros)
   int ig = 0, ilg = 0;
   auto tile_offsets = [&]() {
@@ -592,14 +643,22 @@ __global__ __launch_bounds__(kP1Threads) void k_qmv_chain(ChainArgs a) {
     const bool ok = trow + ilg < si.nrows;  // rows past the range read zeros
     vc = ok ? ((uint32_t)ilg * si.nb + ig) * CB : kOob;
     vs = ok ? ((uint32_t)ilg * si.nb + ig) * 2 : kOob;
-    const bool past_k = ((si.ns - 1) << si.lg2G) + ig >= si.nb;
+    const bool past_k = ((si.ns - 1) << si.lg2G) + ig >= si.nbc;
     vc_last = past_k ? kOob : vc;
     vs_last = past_k ? kOob : vs;
   };
-  auto next_issue_gemv = [&]() {  // the next GEMV with steps for this wave, if any
-    while (ipad == 0 && gi + 1 < a.n) {
-      ++gi;
-      load_stage(table, gi, wave, si);
+  auto next_issue = [&]() {  // the next (GEMV, chunk) with steps for this wave, if any
+    ireal = 0;
+    ipad = 0;
+    while (ipad == 0) {
+      if (ci + 1 < si.nchunks) {
+        ++ci;
+      } else {
+        if (gi + 1 >= a.n) break;
+        ++gi;
+        ci = 0;
+      }
+      load_stage<LGW>(table, gi, ci, kc, wave, si);
       ireal = si.end - si.start;
       ipad = (ireal + P - 1) / P * P;
     }
@@ -616,14 +675,14 @@ __global__ __launch_bounds__(kP1Threads) void k_qmv_chain(ChainArgs a) {
       tile_offsets();
     }
   };
-  next_issue_gemv();
+  next_issue();
 
   auto issue = [&](Codes<FMT>& q, uint32_t& d) {
     // arithmetic, not branches or selects (which the compiler may turn into branches with
     // the loads duplicated): one load sequence for real and padding steps.  Once the range
     // is done the lane offsets are past the descriptor: zeros, no memory traffic.
     const uint32_t live = ireal > 0 ? 1u : 0u;
-    const uint32_t so = ((uint32_t)(it * si.gpw) * si.nb + (uint32_t)(ij << si.lg2G)) * live;
+    const uint32_t so = ((uint32_t)(it * si.gpw) * si.nb + (uint32_t)si.kb0 + (uint32_t)(ij << si.lg2G)) * live;
     const uint32_t lm = 0u - (uint32_t)(ij == si.ns - 1);  // all ones at a tile's last step
     const uint32_t c = (vc_last & lm) | (vc & ~lm);
     const uint32_t e = (vs_last & lm) | (vs & ~lm);
@@ -645,7 +704,7 @@ __global__ __launch_bounds__(kP1Threads) void k_qmv_chain(ChainArgs a) {
         tile_offsets();
       }
     }
-    if (ipad > 0 && --ipad == 0) next_issue_gemv();
+    if (ipad > 0 && --ipad == 0) next_issue();
   };
 
   Codes<FMT> ring_q[P];
@@ -658,22 +717,30 @@ __global__ __launch_bounds__(kP1Threads) void k_qmv_chain(ChainArgs a) {
   // between waves w0..wl: each part leaves its row sums in `part` (slot 1: the part that
   // holds the tile's first step, slot 0: later parts) and counts itself in done[w0]; the
   // part that completes the count adds the parts in wave order, stores the rows and resets
-  // the count.  Every store is followed by its step's loads.
-  __shared__ float part[kP1Waves * 2 * 4];
-  __shared__ int done[kP1Waves];
-  int gc = -1, ct = 0, cj = 0, creal = 0, cpad = 0;  // GEMV, tile, step in tile, steps left
+  // the count.  A chunked GEMV adds each chunk's row sums into `pacc` and stores at its last
+  // chunk.  Every store is followed by its step's loads.
+  int gc = -1, cc = 0;                               // GEMV and chunk being consumed
+  int ct = 0, cj = 0, creal = 0, cpad = 0;           // tile, step in tile, steps left
   Stage sc;
+  sc.nchunks = 0;
   const char* lds_lane = xlds;   // this lane's first block of a tile
   const char* lds_last = xlds;   // ... its block at the tile's last step (past K: the last block)
   int cg = 0, clg = 0;
-  float acc = 0.f;
+  float acc[MM];
+#pragma unroll
+  for (int m = 0; m < MM; m++) acc[m] = 0.f;
   bool alive = true;
-  if (tid < kP1Waves) done[tid] = 0;
-  // Enter the next GEMV: all waves finished reading the staged x, wait for earlier outputs
-  // if asked, stage the new x and its block sums.  Every wave enters every GEMV, in order.
+  // Enter the next (GEMV, chunk): all waves finished reading the staged x, wait for earlier
+  // outputs if asked, stage the new x and its block sums.  Every wave enters every
+  // (GEMV, chunk), in order.
   auto enter = [&]() {
-    ++gc;
-    load_stage(table, gc, wave, sc);
+    if (cc + 1 < sc.nchunks) {
+      ++cc;
+    } else {
+      ++gc;
+      cc = 0;
+    }
+    load_stage<LGW>(table, gc, cc, kc, wave, sc);
     creal = sc.end - sc.start;
     cpad = (creal + P - 1) / P * P;
     ct = sc.start / sc.ns;
@@ -683,51 +750,57 @@ __global__ __launch_bounds__(kP1Threads) void k_qmv_chain(ChainArgs a) {
     if (sc.wait && gc > 0 && a.sync) alive = grid_barrier<LOADS>(a.sync, ++epoch, &lds_ok);
     else __syncthreads();
     // x comes through agent-coherent loads (other workgroups may have written it), 16
-    // bytes per lane: a pass of a wave stages 8 whole blocks.  Up to 4 passes' loads are
-    // issued before any is used.  Then 8 lanes form the blocks' sums in chain order over
-    // the values as staged (Q4_0 positions 16..31 divided by 16, multiplied back exactly);
-    // a wave's LDS accesses complete in order, so its own stores are visible to its reads.
-    const __amdgpu_buffer_rsrc_t rx =
-        __builtin_amdgcn_make_buffer_rsrc((void*)sc.x, (short)0, sc.nb * 128, 0x00020000);
-    const int nch = sc.nb * 8;
-    for (int c00 = wave * 64; c00 < nch; c00 += 4 * kP1Threads) {
-      f32x4 v[4];
+    // bytes per lane: a pass of a wave stages 8 whole blocks of one input.  Up to 4 passes'
+    // loads are issued before any is used.  Then 8 lanes form the blocks' sums in chain
+    // order over the values as staged (Q4_0 positions 16..31 divided by 16, multiplied back
+    // exactly); a wave's LDS accesses complete in order, so its own stores are visible to
+    // its reads.  Inputs m >= M are staged as zeros (their results are not stored).
+    const int nch = sc.nbc * 8;
 #pragma unroll
-      for (int q = 0; q < 4; q++)  // past the end reads zeros
-        v[q] = __builtin_bit_cast(
-            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (c00 + q * kP1Threads + lane) * 16, 0, 16));
+    for (int m = 0; m < MM; m++) {
+      const float* xrow = sc.x + (int64_t)(m < sc.M ? m : 0) * sc.xstride + (int64_t)sc.kb0 * kQK;
+      const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)xrow, (short)0, m < sc.M ? sc.nbc * 128 : 0, 0x00020000);
+      char* xm = xlds + m * mstride;
+      for (int c00 = wave * 64; c00 < nch; c00 += 4 * NT) {
+        f32x4 v[4];
 #pragma unroll
-      for (int q = 0; q < 4; q++) {
-        const int c0 = c00 + q * kP1Threads;
-        if (c0 < nch) {
-          const int c = c0 + lane;
-          const int blk = c >> 3, i = c & 7;
-          f32x4 w = v[q];
-          if (FMT == FQ4 && i >= 4) w = w * 0.0625f;
-          if (c < nch) *reinterpret_cast<f32x4*>(xlds + blk * kBlkLds + i * 16) = w;
-          asm volatile("" ::: "memory");
-          const int b = (c0 >> 3) + lane;
-          if (lane < 8 && b < sc.nb) {
-            const f32x4* xl = reinterpret_cast<const f32x4*>(xlds + b * kBlkLds);
-            float s = xl[0].x;
-            s = s + xl[0].y; s = s + xl[0].z; s = s + xl[0].w;
+        for (int q = 0; q < 4; q++)  // past the end reads zeros
+          v[q] = __builtin_bit_cast(
+              f32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (c00 + q * NT + lane) * 16, 0, 16));
 #pragma unroll
-            for (int k = 1; k < 4; k++) { s = s + xl[k].x; s = s + xl[k].y; s = s + xl[k].z; s = s + xl[k].w; }
-            const float m = FMT == FQ4 ? 16.0f : 1.0f;
+        for (int q = 0; q < 4; q++) {
+          const int c0 = c00 + q * NT;
+          if (c0 < nch) {
+            const int c = c0 + lane;
+            const int blk = c >> 3, i = c & 7;
+            f32x4 w = v[q];
+            if (FMT == FQ4 && i >= 4) w = w * 0.0625f;
+            if (c < nch) *reinterpret_cast<f32x4*>(xm + blk * kBlkLds + i * 16) = w;
+            asm volatile("" ::: "memory");
+            const int b = (c0 >> 3) + lane;
+            if (lane < 8 && b < sc.nbc) {
+              const f32x4* xl = reinterpret_cast<const f32x4*>(xm + b * kBlkLds);
+              float s = xl[0].x;
+              s = s + xl[0].y; s = s + xl[0].z; s = s + xl[0].w;
 #pragma unroll
-            for (int k = 4; k < 8; k++) {
-              s = s + xl[k].x * m; s = s + xl[k].y * m; s = s + xl[k].z * m; s = s + xl[k].w * m;
+              for (int k = 1; k < 4; k++) { s = s + xl[k].x; s = s + xl[k].y; s = s + xl[k].z; s = s + xl[k].w; }
+              const float mu = FMT == FQ4 ? 16.0f : 1.0f;
+#pragma unroll
+              for (int k = 4; k < 8; k++) {
+                s = s + xl[k].x * mu; s = s + xl[k].y * mu; s = s + xl[k].z * mu; s = s + xl[k].w * mu;
+              }
+              *reinterpret_cast<float*>(xm + b * kBlkLds + 128) = s;
             }
-            *reinterpret_cast<float*>(xlds + b * kBlkLds + 128) = s;
+            asm volatile("" ::: "memory");
           }
-          asm volatile("" ::: "memory");
         }
       }
     }
     __syncthreads();
     lds_lane = xlds + cg * kBlkLds;
-    lds_last = ((sc.ns - 1) << sc.lg2G) + cg < sc.nb ? lds_lane + (sc.ns - 1) * (sc.G * kBlkLds)
-                                                     : xlds + (sc.nb - 1) * kBlkLds;  // its d is 0
+    lds_last = ((sc.ns - 1) << sc.lg2G) + cg < sc.nbc ? lds_lane + (sc.ns - 1) * (sc.G * kBlkLds)
+                                                      : xlds + (sc.nbc - 1) * kBlkLds;  // its d is 0
   };
 
   enter();
@@ -737,25 +810,33 @@ __global__ __launch_bounds__(kP1Threads) void k_qmv_chain(ChainArgs a) {
       for (int p = 0; p < P; p++) {
         if (creal > 0) {  // uniform: a real step of this wave
           const char* xb = cj == sc.ns - 1 ? lds_last : lds_lane + cj * (sc.G * kBlkLds);
-          const f32x4* xl = reinterpret_cast<const f32x4*>(xb);
-          const float sx = *reinterpret_cast<const float*>(xb + 128);
-          const float c = chain_m1<FMT>(ring_q[p], xl);
-          const float rr = fmaf(FMT == FQ4 ? -8.0f : -128.0f, sx, c);
-          acc = fmaf(h2f(ring_d[p]), rr, acc);
+          float c[MM];
+          chain_block<FMT, MM>(ring_q[p], xb, mstride, c);
+#pragma unroll
+          for (int m = 0; m < MM; m++) {
+            const float sx = *reinterpret_cast<const float*>(xb + m * mstride + 128);
+            const float rr = fmaf(FMT == FQ4 ? -8.0f : -128.0f, sx, c[m]);
+            acc[m] = fmaf(h2f(ring_d[p]), rr, acc[m]);
+          }
           --creal;
           ++cj;
           if (cj == sc.ns || creal == 0) {  // this wave's part of the tile is done
-            float v = acc;
-            for (int off = sc.G >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-            // waves holding the tile: the wave of step s is (16 s + 15) / S; when S < 16 each
-            // non-empty wave holds one step
+            float v[MM];
+#pragma unroll
+            for (int m = 0; m < MM; m++) v[m] = group_sum_rt(acc[m], sc.lg2G);
+            // waves holding the tile: the wave of step s is (NW s + NW - 1) / S; when S < NW
+            // each non-empty wave holds one step
             const int t0 = ct * sc.ns, t1 = t0 + sc.ns;
-            const int w0 = (16 * t0 + 15) / sc.S, wl = (16 * (t1 - 1) + 15) / sc.S;
-            const int parts = sc.S >= 16 ? wl - w0 + 1 : sc.ns;
+            const int w0 = (NW * t0 + NW - 1) / sc.S, wl = (NW * (t1 - 1) + NW - 1) / sc.S;
+            const int parts = sc.S >= NW ? wl - w0 + 1 : sc.ns;
             const int row = ct * sc.gpw + clg;
             bool put = parts == 1;
             if (!put) {
-              if (cg == 0) part[(wave * 2 + (t0 >= sc.start ? 1 : 0)) * 4 + clg] = v;
+              float* mine = part + ((wave * 2 + (t0 >= sc.start ? 1 : 0)) * 4 + clg) * MM;
+              if (cg == 0) {
+#pragma unroll
+                for (int m = 0; m < MM; m++) mine[m] = v[m];
+              }
               asm volatile("" ::: "memory");
               int before = 0;
               if (lane == 0)
@@ -763,19 +844,42 @@ __global__ __launch_bounds__(kP1Threads) void k_qmv_chain(ChainArgs a) {
               before = __builtin_amdgcn_readfirstlane(before);
               asm volatile("" ::: "memory");
               if (before == parts - 1) {  // the last part in: every part is in `part`
-                v = part[(w0 * 2 + 1) * 4 + clg];
+                const float* p0 = part + ((w0 * 2 + 1) * 4 + clg) * MM;
+#pragma unroll
+                for (int m = 0; m < MM; m++) v[m] = p0[m];
                 for (int u = w0 + 1; u <= wl; u++)
-                  if (sc.S >= 16 || ((u * sc.S) >> 4) < (((u + 1) * sc.S) >> 4))
-                    v = v + part[(u * 2) * 4 + clg];
+                  if (sc.S >= NW || ((u * sc.S) >> LGW) < (((u + 1) * sc.S) >> LGW)) {
+                    const float* pu = part + ((u * 2) * 4 + clg) * MM;
+#pragma unroll
+                    for (int m = 0; m < MM; m++) v[m] = v[m] + pu[m];
+                  }
                 if (lane == 0) done[w0] = 0;
                 put = true;
               }
             }
-            if (put && cg == 0 && row < sc.nrows)  // agent-coherent: a later GEMV may read it
-              __hip_atomic_store((__attribute__((address_space(1))) float*)sc.y + row, v,
-                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (put && cg == 0 && row < sc.nrows) {
+              bool store = true;
+              if (sc.nchunks > 1) {  // chunk sums, added in chunk order
+                float* pa = pacc + row * MM;
+#pragma unroll
+                for (int m = 0; m < MM; m++) {
+                  if (!sc.first) v[m] = pa[m] + v[m];
+                  pa[m] = v[m];
+                }
+                store = sc.last;
+              }
+              if (store) {
+#pragma unroll
+                for (int m = 0; m < MM; m++)
+                  if (m < sc.M)  // agent-coherent: a later GEMV may read it
+                    __hip_atomic_store((__attribute__((address_space(1))) float*)sc.y +
+                                           (int64_t)m * sc.ystride + row,
+                                       v[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              }
+            }
             asm volatile("" ::: "memory");  // keep the store ahead of this step's loads
-            acc = 0.f;
+#pragma unroll
+            for (int m = 0; m < MM; m++) acc[m] = 0.f;
             if (cj == sc.ns) {
               cj = 0;
               ++ct;
@@ -787,7 +891,7 @@ __global__ __launch_bounds__(kP1Threads) void k_qmv_chain(ChainArgs a) {
       cpad -= P;
     }
     if (cpad == 0) {
-      if (gc + 1 >= a.n) break;
+      if (cc + 1 >= sc.nchunks && gc + 1 >= a.n) break;
       enter();
     }
   }
@@ -934,20 +1038,6 @@ int pick_group(int64_t nb) {
   return best;
 }
 
-#ifndef BQM_QMV_MIN_WGS
-#define BQM_QMV_MIN_WGS 512  // aim for at least two workgroups per CU
-#endif
-
-int pick_rows(int64_t N, int G, int M) {
-  const int rmax = M == 1 ? 4 : 2;
-  for (int R = rmax; R > 1; R >>= 1) {
-    const int64_t rpw = (kThreads / G) * R;
-    if ((N + rpw - 1) / rpw >= BQM_QMV_MIN_WGS) return R;
-  }
-  return 1;
-}
-
-// Blocks of x staged per LDS chunk for M inputs within `budget` bytes.
 int chunk_blocks(int64_t nb, int M, int budget) {
   const int per_block = M * 128 + (M == 1 ? 4 : 0);
   int64_t kcb = budget / per_block;
@@ -963,33 +1053,6 @@ void allow_lds(Kern k, size_t bytes) {
   if (bytes > 64 * 1024)
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-}
-
-using QmvKernel = void (*)(const uint8_t*, const uint16_t*, const float*, float*, int, int, int,
-                           int);
-
-template <int FMT, int MM, int G>
-QmvKernel select_r(int R) {
-  if constexpr (MM == 1) {
-    if (R == 4) return k_qmv<FMT, MM, G, 4>;
-  }
-  if (R == 2) return k_qmv<FMT, MM, G, 2>;
-  return k_qmv<FMT, MM, G, 1>;
-}
-
-template <int FMT, int MM>
-QmvKernel select_g(int G, int R) {
-  if (G == 64) return select_r<FMT, MM, 64>(R);
-  if (G == 32) return select_r<FMT, MM, 32>(R);
-  return select_r<FMT, MM, 16>(R);
-}
-
-template <int FMT>
-QmvKernel select_m(int M, int G, int R) {
-  if (M == 1) return select_g<FMT, 1>(G, R);
-  if (M == 2) return select_g<FMT, 2>(G, R);
-  if (M <= 4) return select_g<FMT, 4>(G, R);
-  return select_g<FMT, 8>(G, R);
 }
 
 using QmvIdKernel = void (*)(const uint8_t*, const uint16_t*, const int32_t*, int, int, int, int,
@@ -1016,8 +1079,29 @@ constexpr int kP1MaxLds = 160 * 1024 - kP1StaticLds;  // dynamic LDS of a chain 
 
 using ChainKernel = void (*)(ChainArgs);
 
-ChainKernel chain_kernel(int fmt) {
-  return fmt == BQM_Q4_0 ? k_qmv_chain<FQ4, BQM_P1_P> : k_qmv_chain<FQ8, BQM_P1_P / 2>;
+// M class: the kernel instantiation that takes M inputs (1, 2, 4 or 8).
+int m_class(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
+
+// Ring depth: a step of a wider batch computes longer, so fewer steps in flight cover the
+// memory latency, and its registers go to the batch's sums.
+template <int FMT, int MM>
+constexpr int chain_ring() {
+  return (FMT == FQ4 ? BQM_P1_P : BQM_P1_P / 2) / (MM >= 4 && FMT == FQ4 ? 2 : 1);
+}
+// log2 of the waves per workgroup: 16 waves, or 8 for the widest batch, whose sums need
+// more than the 128 registers a lane has when 16 waves share a CU
+constexpr int chain_lgw(int mm) { return mm >= 8 ? 3 : 4; }
+template <int FMT>
+ChainKernel chain_kernel_f(int mm) {
+  switch (mm) {
+    case 1: return k_qmv_chain<FMT, chain_ring<FMT, 1>(), 1, chain_lgw(1)>;
+    case 2: return k_qmv_chain<FMT, chain_ring<FMT, 2>(), 2, chain_lgw(2)>;
+    case 4: return k_qmv_chain<FMT, chain_ring<FMT, 4>(), 4, chain_lgw(4)>;
+    default: return k_qmv_chain<FMT, chain_ring<FMT, 8>(), 8, chain_lgw(8)>;
+  }
+}
+ChainKernel chain_kernel(int fmt, int mm) {
+  return fmt == BQM_Q4_0 ? chain_kernel_f<FQ4>(mm) : chain_kernel_f<FQ8>(mm);
 }
 
 int cu_count() {
@@ -1043,25 +1127,43 @@ int launch_fill(float* y, int64_t n, float v, hipStream_t s) {
   return launch_status();
 }
 
-// Largest K a chain GEMV may have: its staged x must fit the LDS of one workgroup.
+// Largest K a chain GEMV may have.
 int64_t chain_max_k() { return 32768; }
 
-// LDS a chain of n GEMVs needs: its stage table, then x of its longest GEMV.
-int64_t chain_lds_bytes(int n, int64_t max_k) {
-  return (((int64_t)n * (int64_t)sizeof(StageRow) + 15) & ~int64_t(15)) + (max_k / kQK) * kBlkLds;
+// Staging plan of a chain: kc (K blocks staged at a time) and the rows of the per-row
+// partial-sum buffer (0 when no GEMV is walked in chunks).  Whole GEMVs are staged when
+// the table, the split-tile parts and M inputs of the longest K fit; otherwise every GEMV
+// longer than kc goes in chunks.  Returns false when even 32-block chunks do not fit.
+bool chain_plan(int n, int mm, int64_t max_nb, int64_t max_rows, int* kc, int* pacc_rows) {
+  const int64_t fixed = chain_lds(n, mm, 0, 0).total;
+  if (fixed + (int64_t)mm * max_nb * kBlkLds <= kP1MaxLds) {
+    *kc = (int)max_nb;
+    *pacc_rows = 0;
+    return true;
+  }
+  const int64_t pacc = (max_rows * mm * 4 + 15) & ~int64_t(15);
+  const int64_t room = kP1MaxLds - fixed - pacc;
+  const int64_t k = room / ((int64_t)mm * kBlkLds);
+  if (room <= 0 || k < 32) return false;
+  *kc = (int)(k & ~int64_t(15));  // a multiple of the lane group widths' common factor
+  *pacc_rows = (int)max_rows;
+  return true;
 }
 
 // Launch a chain (descriptors in device memory, or `one` when descs is null).
-int launch_chain(int fmt, const GemvDesc* descs, const GemvDesc* one, int n, uint32_t* sync,
-                 hipStream_t s) {
+int launch_chain(int fmt, int mm, const GemvDesc* descs, const GemvDesc* one, int n, int kc,
+                 int pacc_rows, uint32_t* sync, hipStream_t s) {
   ChainArgs a;
   a.descs = descs;
-  if (one) a.one = *one; else a.one = GemvDesc{nullptr, nullptr, nullptr, 0, 0, fmt, 0};
+  if (one) a.one = *one; else a.one = GemvDesc{nullptr, nullptr, nullptr, 0, 0, fmt, 0, 1, 0};
   a.n = n;
+  a.kc = kc;
+  a.pacc_rows = pacc_rows;
   a.sync = sync;
-  ChainKernel k = chain_kernel(fmt);
-  static int static_ok[2] = {0, 0};  // per format: 1 = the kernel's static LDS fits the reserve
-  int& ok = static_ok[fmt == BQM_Q4_0 ? 0 : 1];
+  ChainKernel k = chain_kernel(fmt, mm);
+  // per kernel: 1 = its static LDS fits the reserve, -1 = it does not
+  static int static_ok[2][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+  int& ok = static_ok[fmt == BQM_Q4_0 ? 0 : 1][mm == 1 ? 0 : mm == 2 ? 1 : mm == 4 ? 2 : 3];
   if (ok == 0) {
     hipFuncAttributes fa;
     ok = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(k)) == hipSuccess &&
@@ -1070,20 +1172,22 @@ int launch_chain(int fmt, const GemvDesc* descs, const GemvDesc* one, int n, uin
   if (ok < 0) return BQM_E_LAUNCH;
   allow_lds(k, kP1MaxLds);
   const int grid = cu_count();
+  const int threads = 64 << chain_lgw(mm);
   if (sync) {
     // workgroups wait for each other: they must all be resident at once
     void* args[] = {&a};
-    if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k), dim3(grid), dim3(kP1Threads), args,
+    if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k), dim3(grid), dim3(threads), args,
                                    kP1MaxLds, s) != hipSuccess)
       return BQM_E_LAUNCH;
     return launch_status();
   }
-  hipLaunchKernelGGL(k, dim3(grid), dim3(kP1Threads), kP1MaxLds, s, a);
+  hipLaunchKernelGGL(k, dim3(grid), dim3(threads), kP1MaxLds, s, a);
   return launch_status();
 }
 
-// ---- chain API.  Workspace: 64 header words {release epoch, -, error, n, fmt, ...}, one
-// 128-byte arrival flag per workgroup (at most kChainMaxWorkgroups), then the descriptors.
+// ---- chain API.  Workspace: 64 header words {release epoch, -, error, n, fmt, kc,
+// partial-sum rows, M class, ...}, one 128-byte arrival flag per workgroup (at most
+// kChainMaxWorkgroups), then the descriptors.
 constexpr int64_t kChainSyncBytes = (kChainHeaderWords + kChainMaxWorkgroups * kFlagStrideWords) * 4;
 
 size_t chain_workspace_bytes(int n) {
@@ -1091,19 +1195,19 @@ size_t chain_workspace_bytes(int n) {
 }
 
 int chain_prepare(const bqm_gemv* descs, int n, void* ws, hipStream_t s) {
-  const int fmt = descs[0].fmt;
+  const int fmt = descs[0].fmt, M = descs[0].M;
   if (fmt != BQM_Q4_0 && fmt != BQM_Q8_0) return BQM_E_UNSUPPORTED;
   const int CB = fmt == BQM_Q4_0 ? 16 : 32;
   // checks of the descriptors alone first (no HIP call before they pass)
-  int64_t max_k = 0;
+  int64_t max_nb = 0;
   for (int i = 0; i < n; i++) {
     const bqm_gemv& d = descs[i];
     if (d.fmt != fmt) return BQM_E_UNSUPPORTED;
+    if (d.M != M || M < 1 || M > kChainMaxM) return BQM_E_SHAPE;
     if (d.N < 1 || d.N > ((int64_t)1 << 30) || d.K < kQK || d.K % kQK != 0 || d.K > chain_max_k())
       return BQM_E_SHAPE;
-    max_k = d.K > max_k ? d.K : max_k;
+    max_nb = d.K / kQK > max_nb ? d.K / kQK : max_nb;
   }
-  if (chain_lds_bytes(n, max_k) > kP1MaxLds) return BQM_E_SHAPE;
   for (int i = 0; i < n; i++) {
     const bqm_gemv& d = descs[i];
     if (!d.w_packed || !d.x || !d.y) return BQM_E_NULL;
@@ -1113,11 +1217,17 @@ int chain_prepare(const bqm_gemv* descs, int n, void* ws, hipStream_t s) {
   // then the ones that depend on the device: one workgroup's rows must stay below 2 GiB
   const int cus = cu_count();
   if (cus > kChainMaxWorkgroups) return BQM_E_UNSUPPORTED;
+  int64_t max_rows = 0;
   for (int i = 0; i < n; i++) {
     const bqm_gemv& d = descs[i];
-    if (((d.N + cus - 1) / cus + 1) * (d.K / kQK) * CB >= ((int64_t)1 << 31)) return BQM_E_SHAPE;
+    const int64_t rows = (d.N + cus - 1) / cus;
+    if ((rows + 1) * (d.K / kQK) * CB >= ((int64_t)1 << 31)) return BQM_E_SHAPE;
+    max_rows = rows > max_rows ? rows : max_rows;
   }
-  uint32_t head[8] = {0, 0, 0, (uint32_t)n, (uint32_t)fmt, 0, 0, 0};
+  const int mm = m_class(M);
+  int kc = 0, pacc_rows = 0;
+  if (!chain_plan(n, mm, max_nb, max_rows, &kc, &pacc_rows)) return BQM_E_SHAPE;
+  uint32_t head[8] = {0, 0, 0, (uint32_t)n, (uint32_t)fmt, (uint32_t)kc, (uint32_t)pacc_rows, (uint32_t)mm};
   if (hipMemsetAsync(ws, 0, kChainSyncBytes, s) != hipSuccess ||
       hipMemcpyAsync(ws, head, sizeof(head), hipMemcpyHostToDevice, s) != hipSuccess ||
       hipMemcpyAsync(static_cast<char*>(ws) + kChainSyncBytes, descs, (size_t)n * sizeof(GemvDesc),
@@ -1127,9 +1237,9 @@ int chain_prepare(const bqm_gemv* descs, int n, void* ws, hipStream_t s) {
   return BQM_OK;
 }
 
-int chain_launch(int fmt, void* ws, int n, hipStream_t s) {
+int chain_launch(int fmt, int M, void* ws, int n, hipStream_t s) {
   const GemvDesc* d = reinterpret_cast<const GemvDesc*>(static_cast<char*>(ws) + kChainSyncBytes);
-  return launch_chain(fmt, d, nullptr, n, static_cast<uint32_t*>(ws), s);
+  return launch_chain(fmt, m_class(M), d, nullptr, n, 0, 0, static_cast<uint32_t*>(ws), s);
 }
 
 int chain_status(const void* ws, hipStream_t s) {
@@ -1140,29 +1250,21 @@ int chain_status(const void* ws, hipStream_t s) {
   return (int)err;
 }
 
+// Batch-M GEMV: a chain of one (no device-wide barrier), chunked along K when the M inputs
+// do not fit the LDS.
 int launch_qmv(int fmt, const void* w, const float* X, float* Y, int M, int64_t N, int64_t K,
                hipStream_t s) {
   if (M == 0 || N == 0) return BQM_OK;
   if (K == 0) return launch_fill(Y, (int64_t)M * N, 0.0f, s);
-  Layout L;
-  layout_of(fmt, N, K, &L);
-  const uint8_t* codes = static_cast<const uint8_t*>(w);
-  const uint16_t* scales = reinterpret_cast<const uint16_t*>(codes + L.scales_off);
-  if (M == 1 && K <= chain_max_k()) {  // batch 1: a chain of one GEMV
-    const GemvDesc d{codes, X, Y, N, K, fmt, 0};
-    return launch_chain(fmt, nullptr, &d, 1, nullptr, s);
-  }
-  const int G = pick_group(L.nb);
-  const int R = pick_rows(N, G, M);
-  const int kcb = chunk_blocks(L.nb, M, kLdsBudget);
-  const int64_t rpw = (kThreads / G) * R;
-  const int64_t grid = (N + rpw - 1) / rpw;
-  const size_t lds = x_lds_bytes(M, kcb);
-  QmvKernel k = fmt == BQM_Q4_0 ? select_m<FQ4>(M, G, R) : select_m<FQ8>(M, G, R);
-  allow_lds(k, lds);
-  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kThreads), lds, s, codes, scales, X, Y, M,
-                     (int)N, (int)L.nb, kcb);
-  return launch_status();
+  const int mm = m_class(M);
+  const int cus = cu_count();
+  const int64_t rows = (N + cus - 1) / cus;
+  const int CB = fmt == BQM_Q4_0 ? 16 : 32;
+  if ((rows + 1) * (K / kQK) * CB >= ((int64_t)1 << 31)) return BQM_E_SHAPE;
+  int kc = 0, pacc_rows = 0;
+  if (!chain_plan(1, mm, K / kQK, rows, &kc, &pacc_rows)) return BQM_E_SHAPE;
+  const GemvDesc d{static_cast<const uint8_t*>(w), X, Y, N, K, fmt, 0, M, 0};
+  return launch_chain(fmt, mm, nullptr, &d, 1, kc, pacc_rows, nullptr, s);
 }
 
 int launch_qmv_id(int fmt, const void* w, int E, int64_t N, int64_t K, const int32_t* ids, int T,

@@ -88,7 +88,8 @@ int bqm_unpack(int fmt, const void* w_packed, void* w_interchange, int64_t rows,
  * once per token):
  *     Y[m][n] = sum_k dequant(W)[n][k] * X[m][k],   0 <= m < M <= 8, 0 <= n < N.
  * w_packed: packed N x K matrix.  X: fp32 [M][K] row-major.  Y: fp32 [M][N] row-major.
- * M = 0 or N = 0: nothing to do.  M > 8: BQM_E_SHAPE. */
+ * M = 0 or N = 0: nothing to do.  M > 8, or one workgroup's share of the rows reaching
+ * 2 GiB of codes: BQM_E_SHAPE.  (A chain of one GEMV: see qmv_chain.) */
 int qmv_q4_0(const void* w_packed, const float* X, float* Y, int M, int64_t N, int64_t K,
              hipStream_t stream);
 int qmv_q8_0(const void* w_packed, const float* X, float* Y, int M, int64_t N, int64_t K,
@@ -111,46 +112,50 @@ int qmv_id(int fmt, const void* w_packed, int E, int64_t N, int64_t K, const int
            int top_k, const float* X, int64_t x_tok_stride, int64_t x_slot_stride, float* Y,
            hipStream_t stream);
 
-/* ---- chains of batch-1 GEMVs in one launch -------------------------------------------
+/* ---- chains of GEMVs in one launch ----------------------------------------------------
  * Decode runs one GEMV after another, each reading the previous one's output (through
  * the layers' other operations); launching them one by one pays a kernel start and drain
- * per GEMV.  A chain runs a list of batch-1 GEMVs in order in ONE launch: a GEMV marked
- * `wait` starts only after every earlier GEMV of the chain has finished and its outputs
- * are visible device-wide (so its x may be an earlier GEMV's y); the weights of the next
- * GEMV are already streaming while the previous one finishes.  Same arithmetic and
- * tolerance as qmv_q4_0 / qmv_q8_0 with M = 1. */
+ * per GEMV.  A chain runs a list of GEMVs in order in ONE launch: a GEMV marked `wait`
+ * starts only after every earlier GEMV of the chain has finished and its outputs are
+ * visible device-wide (so its x may be an earlier GEMV's y); the weights of the next GEMV
+ * are already streaming while the previous one finishes.  Every GEMV of a chain has the
+ * same batch M (1..8).  Same arithmetic and tolerance as qmv_q4_0 / qmv_q8_0. */
 typedef struct bqm_gemv {
   const void* w_packed;  /* packed N x K matrix (device)                              */
-  const float* x;        /* [K] fp32 input (device), 16-byte aligned                  */
-  float* y;              /* [N] fp32 output (device)                                  */
+  const float* x;        /* [M][K] fp32 inputs (device), row-major, 16-byte aligned   */
+  float* y;              /* [M][N] fp32 outputs (device), row-major                   */
   int64_t N, K;          /* 1 <= N <= 2^30; 32 <= K <= BQM_CHAIN_MAX_K, K % 32 == 0   */
   int32_t fmt;           /* BQM_Q4_0 or BQM_Q8_0, the same for every GEMV of a chain  */
   int32_t wait;          /* nonzero: start after all earlier GEMVs of the chain       */
+  int32_t M;             /* batch, 1..8, the same for every GEMV of a chain           */
+  int32_t reserved;      /* set to 0                                                  */
 } bqm_gemv;
 
-/* Largest K of a chain GEMV (its x is staged in the LDS of one workgroup).  A chain of n
- * GEMVs also needs 48 * n + 4.5 * max(K) <= 162816 bytes of LDS (about 2900 GEMVs when the
- * longest K is 5120, 1760 when it is 17408); bqm_chain_prepare returns BQM_E_SHAPE otherwise. */
+/* Largest K of a chain GEMV.  The chain keeps a 64-byte table row per GEMV and the staged
+ * inputs in the LDS of each workgroup: bqm_chain_prepare returns BQM_E_SHAPE when the table
+ * leaves no room for 32 blocks of K per input row (about 1900 GEMVs at M = 1; the inputs of
+ * a long K are then staged in chunks). */
 #define BQM_CHAIN_MAX_K 32768
 
 /* Device bytes of the workspace of an n-GEMV chain (0 if n < 1). */
 size_t bqm_chain_workspace_bytes(int n);
 
-/* Validates the n host-side descriptors, then writes them and a zeroed synchronization
- * header into `workspace` (device memory, bqm_chain_workspace_bytes(n) bytes, 16-byte
- * aligned, owned by the caller).  A set-up call: it synchronizes `stream` before it
- * returns, so `descs` may be freed afterwards.  Errors: BQM_E_SHAPE, BQM_E_NULL,
- * BQM_E_ALIGN, BQM_E_UNSUPPORTED (mixed or unknown formats), BQM_E_LAUNCH. */
+/* Validates the n host-side descriptors, then writes them, the staging plan and a zeroed
+ * synchronization header into `workspace` (device memory, bqm_chain_workspace_bytes(n)
+ * bytes, 16-byte aligned, owned by the caller).  A set-up call: it synchronizes `stream`
+ * before it returns, so `descs` may be freed afterwards.  Errors: BQM_E_SHAPE (sizes, M
+ * differing between GEMVs, a chain too long for the LDS), BQM_E_NULL, BQM_E_ALIGN,
+ * BQM_E_UNSUPPORTED (mixed or unknown formats), BQM_E_LAUNCH. */
 int bqm_chain_prepare(const bqm_gemv* descs, int n, void* workspace, hipStream_t stream);
 
-/* Runs a prepared chain in one (cooperative) launch on `stream`; fmt and n must be those
- * it was prepared with (the kernel checks them against the workspace and otherwise
- * computes nothing and records error 2).  The workspace is left ready for the next call;
- * calls sharing one workspace must not overlap in time. */
-int qmv_chain(int fmt, void* workspace, int n, hipStream_t stream);
+/* Runs a prepared chain in one (cooperative) launch on `stream`; fmt, M and n must be those
+ * it was prepared with (the kernel checks fmt, n and the class of M against the workspace
+ * and otherwise computes nothing and records error 2).  The workspace is left ready for
+ * the next call; calls sharing one workspace must not overlap in time. */
+int qmv_chain(int fmt, int M, void* workspace, int n, hipStream_t stream);
 
 /* Synchronizes `stream` and returns the chain's error word: 0 = ok, 1 = a device-wide
- * wait timed out (results invalid; prepare again), 2 = fmt/n mismatch, -1 = copy failed. */
+ * wait timed out (results invalid; prepare again), 2 = fmt/M/n mismatch, -1 = copy failed. */
 int bqm_chain_status(const void* workspace, hipStream_t stream);
 
 /* Activation quantizer for the prefill product, per row m and 32-wide block b, in IEEE

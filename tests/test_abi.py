@@ -108,14 +108,14 @@ def test_empty_sizes_are_no_ops():
     assert L.bqm_unpack(8, None, None, 4, 0, None) == 0
 
 
-def _gemv(N, K, fmt="q4_0", ptr=0x10000, wait=0):
-    return bqm.Gemv(ptr, ptr, ptr, N, K, bqm.FMT[fmt], wait)
+def _gemv(N, K, fmt="q4_0", ptr=0x10000, wait=0, M=1):
+    return bqm.Gemv(ptr, ptr, ptr, N, K, bqm.FMT[fmt], wait, M, 0)
 
 
 def test_chain_host_validation():
-    """bqm_chain_prepare rejects bad descriptor lists before any device work (the
-    descriptor checks run before the runtime is queried); host addresses stand in for
-    device pointers since nothing is dereferenced."""
+    """bqm_chain_prepare rejects bad descriptor lists on the host.  Host addresses stand in
+    for device pointers: every case below is rejected before any device work (at most the
+    CU count is queried), so nothing is dereferenced."""
     ws = 0x20000  # 16-byte aligned stand-in
     L = bqm.lib()
 
@@ -125,19 +125,21 @@ def test_chain_host_validation():
                                    ctypes.c_void_p(w), None)
 
     assert bqm.chain_workspace_bytes(0) == 0
-    assert bqm.chain_workspace_bytes(2) - bqm.chain_workspace_bytes(1) == ctypes.sizeof(bqm.Gemv) == 48
+    assert bqm.chain_workspace_bytes(2) - bqm.chain_workspace_bytes(1) == ctypes.sizeof(bqm.Gemv) == 56
     assert prep([], n=0) == 2                                    # empty chain
     assert prep([_gemv(64, 64)], w=0) == 1                       # no workspace
     assert prep([_gemv(64, 64)], w=ws + 8) == 3                  # misaligned workspace
     assert prep([_gemv(64, 64), _gemv(64, 64, "q8_0")]) == 4     # mixed formats
+    assert prep([_gemv(64, 64), _gemv(64, 64, M=2)]) == 2        # mixed batch
+    assert prep([_gemv(64, 64, M=0)]) == 2                       # batch 0
+    assert prep([_gemv(64, 64, M=9)]) == 2                       # batch over 8
     assert prep([_gemv(64, 48)]) == 2                            # K % 32 != 0
     assert prep([_gemv(64, 32800)]) == 2                         # K over the chain limit
     assert prep([_gemv(0, 64)]) == 2                             # empty GEMV
     assert prep([_gemv(64, 64, ptr=0)]) == 1                     # null matrix
     assert prep([_gemv(64, 64, ptr=0x10008)]) == 3               # misaligned matrix
-    # LDS: 48 n + 4.5 max(K) <= 162816 bytes.  At K = 17408 the largest chain is 1760
-    # GEMVs: one more is rejected for LDS (before the null-pointer check of the stand-ins)
-    assert prep([_gemv(64, 17408, ptr=0)] * 1761) == 2
-    assert prep([_gemv(64, 17408, ptr=0)] * 1760) == 1
-    assert prep([_gemv(64, 32768, ptr=0)] * 320) == 1
-    assert prep([_gemv(64, 32768, ptr=0)] * 321) == 2
+    # LDS: a 64-byte table row per GEMV, the split-tile parts (512 M bytes), 64 bytes of
+    # counters, per-row partial sums and at least 32 staged blocks per input row must fit
+    # 162816 bytes.  With 64 rows (one per workgroup) at M = 1 that allows 2462 GEMVs.
+    assert prep([_gemv(64, 17408)] * 2463) == 2
+    assert prep([_gemv(64, 17408, M=8)] * 2463) == 2

@@ -16,18 +16,19 @@ def _oracle():
     oracle.build(force=False)
 
 
-def make_chain(fmt, shapes, key, dependent=True):
-    """GEMVs i = 0..n-1 with W_i [N_i][K_i]; if dependent, x_{i+1} is y_i (N_i == K_{i+1})."""
+def make_chain(fmt, shapes, key, dependent=True, M=1):
+    """GEMVs i = 0..n-1 with W_i [N_i][K_i], inputs [M][K_i], outputs [M][N_i]; if
+    dependent, x_{i+1} is y_i (N_i == K_{i+1})."""
     Ws, Wps, xs, ys, descs = [], [], [], [], []
-    x = gen.normal((shapes[0][1],), key + ("x0",), device=DEV)
+    x = gen.normal((M, shapes[0][1]), key + ("x0",), device=DEV)
     for i, (N, K) in enumerate(shapes):
         Wi = weights(fmt, N, K, key + (i,))
         Wp = packed(fmt, Wi, N, K)
         if not dependent and i > 0:
-            x = gen.normal((K,), key + ("x", i), device=DEV)
-        y = torch.full((N,), float("nan"), device=DEV)
+            x = gen.normal((M, K), key + ("x", i), device=DEV)
+        y = torch.full((M, N), float("nan"), device=DEV)
         Ws.append(Wi); Wps.append(Wp); xs.append(x); ys.append(y)
-        descs.append(bqm.gemv(fmt, Wp, x, y, N, K, wait=i > 0))
+        descs.append(bqm.gemv(fmt, Wp, x, y, N, K, wait=i > 0, M=M))
         if dependent:
             x = y
     ws = torch.zeros(bqm.chain_workspace_bytes(len(descs)), dtype=torch.uint8, device=DEV)
@@ -35,12 +36,12 @@ def make_chain(fmt, shapes, key, dependent=True):
     return Ws, Wps, xs, ys, descs, ws
 
 
-def check_stages(fmt, shapes, Ws, xs, ys):
+def check_stages(fmt, shapes, Ws, xs, ys, M=1):
     for i, (N, K) in enumerate(shapes):
-        xi = host(xs[i]).reshape(1, K)
+        xi = host(xs[i]).reshape(M, K)
         assert np.all(np.isfinite(xi)), f"stage {i} read an input that was never written"
         Yr, S = oracle.qmv(fmt, host(Ws[i]), xi, N, K)
-        check_close(host(ys[i]).reshape(1, N), Yr, S, f"chain stage {i} ({N}x{K})")
+        check_close(host(ys[i]).reshape(M, N), Yr, S, f"chain stage {i} ({N}x{K}, M={M})")
 
 
 @pytest.mark.parametrize("fmt", ["q4_0", "q8_0"])
@@ -50,9 +51,38 @@ def test_chain_dependent_stages(fmt):
     shapes = [(5120, 4096), (17408, 5120), (5120, 17408), (1536, 5120), (4096, 1536), (96, 4096)]
     say("chain dependent", fmt)
     Ws, Wps, xs, ys, descs, ws = make_chain(fmt, shapes, ("chain-dep", fmt))
-    bqm.qmv_chain(fmt, ws, len(descs))
+    bqm.qmv_chain(fmt, 1, ws, len(descs))
     assert bqm.bqm_chain_status(ws) == 0
     check_stages(fmt, shapes, Ws, xs, ys)
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0"])
+@pytest.mark.parametrize("M", [2, 4, 8])
+def test_chain_batched_dependent_stages(fmt, M):
+    """Batch M through dependent GEMVs; K = 17408 with M >= 4 does not fit the LDS at once,
+    so that GEMV is walked in chunks of K with per-row partial sums."""
+    shapes = [(4096, 1536), (17408, 4096), (1536, 17408), (520, 1536)]
+    say("chain batched", fmt, M)
+    Ws, Wps, xs, ys, descs, ws = make_chain(fmt, shapes, ("chain-bat", fmt, M), M=M)
+    bqm.qmv_chain(fmt, M, ws, len(descs))
+    assert bqm.bqm_chain_status(ws) == 0
+    check_stages(fmt, shapes, Ws, xs, ys, M=M)
+
+
+@pytest.mark.parametrize("M", [3, 8])
+def test_chain_batched_equals_qmv_and_ragged(M):
+    """A batched chain gives the same bits as qmv_q8_0 with the same M, one call per GEMV,
+    on ragged and tiny shapes."""
+    shapes = [(37, 96), (300, 1184), (1, 9600), (2049, 32768)]
+    say("chain batched vs qmv", M)
+    Ws, Wps, xs, ys, descs, ws = make_chain("q8_0", shapes, ("chain-bq", M), dependent=False, M=M)
+    bqm.qmv_chain("q8_0", M, ws, len(descs))
+    assert bqm.bqm_chain_status(ws) == 0
+    for (N, K), Wp, x, y in zip(shapes, Wps, xs, ys):
+        ref = torch.empty((M, N), device=DEV)
+        bqm.qmv_q8_0(Wp, x, ref, M, N, K)
+        assert torch.equal(ref, y), f"{N}x{K}"
+    check_stages("q8_0", shapes[:3], Ws[:3], xs[:3], ys[:3], M=M)
 
 
 def test_chain_ragged_and_tiny_shapes():
@@ -60,7 +90,7 @@ def test_chain_ragged_and_tiny_shapes():
     say("chain ragged")
     shapes = [(37, 96), (3, 1184), (300, 96), (1, 9600), (65, 32), (2049, 1536)]
     Ws, Wps, xs, ys, descs, ws = make_chain("q4_0", shapes, ("chain-ragged",), dependent=False)
-    bqm.qmv_chain("q4_0", ws, len(descs))
+    bqm.qmv_chain("q4_0", 1, ws, len(descs))
     assert bqm.bqm_chain_status(ws) == 0
     check_stages("q4_0", shapes, Ws, xs, ys)
 
@@ -72,13 +102,13 @@ def test_chain_equals_separate_launches_and_replays():
     Ws, Wps, xs, ys, descs, ws = make_chain("q4_0", shapes, ("chain-eq",), dependent=False)
     sep = []
     for (N, K), Wp, x in zip(shapes, Wps, xs):
-        y = torch.empty((N,), device=DEV)
+        y = torch.empty((1, N), device=DEV)
         bqm.qmv_q4_0(Wp, x, y, 1, N, K)
         sep.append(y)
     for rep in range(3):
         for y in ys:
             y.fill_(float("nan"))
-        bqm.qmv_chain("q4_0", ws, len(descs))
+        bqm.qmv_chain("q4_0", 1, ws, len(descs))
         assert bqm.bqm_chain_status(ws) == 0
         for y, ys_ in zip(sep, ys):
             assert torch.equal(y, ys_), f"replay {rep}"
@@ -87,14 +117,18 @@ def test_chain_equals_separate_launches_and_replays():
 def test_chain_mismatch_is_reported_and_computes_nothing():
     shapes = [(64, 512), (64, 64)]
     Ws, Wps, xs, ys, descs, ws = make_chain("q4_0", shapes, ("chain-mis",))
-    bqm.qmv_chain("q4_0", ws, 3)           # wrong n
+    bqm.qmv_chain("q4_0", 1, ws, 3)        # wrong n
     assert bqm.bqm_chain_status(ws) == 2
     assert torch.all(torch.isnan(ys[0]))
     bqm.bqm_chain_prepare(descs, ws)       # prepare again: clean state
-    bqm.qmv_chain("q8_0", ws, 2)           # wrong format
+    bqm.qmv_chain("q8_0", 1, ws, 2)        # wrong format
     assert bqm.bqm_chain_status(ws) == 2
     bqm.bqm_chain_prepare(descs, ws)
-    bqm.qmv_chain("q4_0", ws, 2)
+    bqm.qmv_chain("q4_0", 4, ws, 2)        # wrong batch
+    assert bqm.bqm_chain_status(ws) == 2
+    assert torch.all(torch.isnan(ys[0]))
+    bqm.bqm_chain_prepare(descs, ws)
+    bqm.qmv_chain("q4_0", 1, ws, 2)
     assert bqm.bqm_chain_status(ws) == 0
     check_stages("q4_0", shapes, Ws, xs, ys)
 
@@ -105,10 +139,19 @@ def test_chain_prepare_rejects_bad_descriptors():
     y = torch.zeros(64, device=DEV)
     ws = torch.zeros(bqm.chain_workspace_bytes(2), dtype=torch.uint8, device=DEV)
     good = bqm.gemv("q4_0", W, x, y, 64, 64, False)
-    for bad in (bqm.Gemv(W.data_ptr(), x.data_ptr(), y.data_ptr(), 64, 48, 2, 0),     # K % 32
-                bqm.Gemv(W.data_ptr(), x.data_ptr(), y.data_ptr(), 64, 0, 2, 0),      # K = 0
-                bqm.Gemv(W.data_ptr(), x.data_ptr(), y.data_ptr(), 64, 32800, 2, 0),     # K too long
-                bqm.Gemv(W.data_ptr(), x.data_ptr(), y.data_ptr(), 64, 64, 8, 0),     # mixed fmt
-                bqm.Gemv(0, x.data_ptr(), y.data_ptr(), 64, 64, 2, 0)):
+    def g(w=W.data_ptr(), K=64, fmt=2, M=1):
+        return bqm.Gemv(w, x.data_ptr(), y.data_ptr(), 64, K, fmt, 0, M, 0)
+    for bad in (g(K=48), g(K=0), g(K=32800),  # K % 32, K = 0, K too long
+                g(fmt=8), g(M=2), g(w=0)):    # mixed format, mixed batch, null matrix
         with pytest.raises(bqm.BqmError):
             bqm.bqm_chain_prepare([good, bad], ws)
+
+
+def test_chain_prepare_rejects_bad_batch():
+    W = torch.zeros(4096, dtype=torch.uint8, device=DEV)
+    x = torch.zeros(64 * 9, device=DEV)
+    y = torch.zeros(64 * 9, device=DEV)
+    ws = torch.zeros(bqm.chain_workspace_bytes(1), dtype=torch.uint8, device=DEV)
+    for M in (0, 9):
+        with pytest.raises(bqm.BqmError):
+            bqm.bqm_chain_prepare([bqm.Gemv(W.data_ptr(), x.data_ptr(), y.data_ptr(), 64, 64, 2, 0, M, 0)], ws)

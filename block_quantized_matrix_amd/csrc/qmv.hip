@@ -479,7 +479,7 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t v) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-template <int LGW>  // log2 of the waves of the workgroup
+template <int LGW, int R>  // log2 of the waves of the workgroup; rows per lane
 __device__ __forceinline__ void load_stage(const StageRow* t, int i, int c, int kc, int wave, Stage& s) {
   const StageRow r = t[i];
   s.codes = reinterpret_cast<const uint8_t*>(uniform64(reinterpret_cast<uint64_t>(r.codes)));
@@ -508,9 +508,9 @@ __device__ __forceinline__ void load_stage(const StageRow* t, int i, int c, int 
   s.gpw = 64 >> lg2;
   s.ragged = (s.nbc & (s.G - 1)) != 0;
   s.ns = (s.nbc + s.G - 1) >> lg2;
-  // tiles of gpw rows, ns steps each, in row order; the waves take equal contiguous
+  // tiles of R * gpw rows, ns steps each, in row order; the waves take equal contiguous
   // ranges of the tile-major step sequence (a tile may be split between waves)
-  const int ntiles = (s.nrows + s.gpw - 1) >> (6 - lg2);
+  const int ntiles = (s.nrows + R * s.gpw - 1) / (R * s.gpw);
   s.S = ntiles * s.ns;
   s.start = (wave * s.S) >> LGW;
   s.end = ((wave + 1) * s.S) >> LGW;
@@ -577,23 +577,23 @@ __device__ __forceinline__ bool grid_barrier(uint32_t* ws, uint32_t epoch, bool*
 struct ChainLds {
   int part, done, pacc, x, total;
 };
-__host__ __device__ inline ChainLds chain_lds(int n, int mm, int pacc_rows, int kc) {
+__host__ __device__ inline ChainLds chain_lds(int n, int mm, int r, int pacc_rows, int kc) {
   ChainLds L;
   L.part = (n * 64 + 15) & ~15;
-  L.done = L.part + kP1Waves * 2 * 4 * mm * 4;
+  L.done = L.part + kP1Waves * 2 * 4 * r * mm * 4;
   L.pacc = L.done + kP1Waves * 4;
   L.x = L.pacc + ((pacc_rows * mm * 4 + 15) & ~15);
   L.total = L.x + mm * kc * kBlkLds;
   return L;
 }
 
-template <int FMT, int P, int MM, int LGW>
+template <int FMT, int P, int MM, int LGW, int R>
 __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
   constexpr int NW = 1 << LGW, NT = 64 << LGW;  // waves, threads
   extern __shared__ float4 smem[];
   constexpr int CB = FMT == FQ4 ? 16 : 32;     // code bytes per block
   constexpr uint32_t kOob = 0x80000000u;       // lane offset past every descriptor: reads 0
-  constexpr int LOADS = FMT == FQ4 ? 2 : 3;    // loads per step
+  constexpr int LOADS = R * (FMT == FQ4 ? 2 : 3);  // loads per step (R rows)
   __shared__ bool lds_ok;
   __shared__ uint32_t lds_epoch;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -607,7 +607,7 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep in SGPRs
   const int kc = a.sync ? (int)a.sync[5] : a.kc;
   const int pacc_rows = a.sync ? (int)a.sync[6] : a.pacc_rows;
-  const ChainLds ly = chain_lds(a.n, MM, pacc_rows, kc);
+  const ChainLds ly = chain_lds(a.n, MM, R, pacc_rows, kc);
   char* lds = reinterpret_cast<char*>(smem);
   StageRow* table = reinterpret_cast<StageRow*>(lds);
   float* part = reinterpret_cast<float*>(lds + ly.part);
@@ -635,17 +635,27 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
   int ireal = 0, ipad = 0;   // real steps left; steps left with padding
   __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(nullptr, (short)0, 0, 0x00020000);
   __amdgpu_buffer_rsrc_t rs = rc;
-  uint32_t vc = kOob, vs = kOob;            // lane offsets in the current tile
-  uint32_t vc_last = kOob, vs_last = kOob;  // ... at its last step (past K in a ragged row: zeros)
+  // lane offsets of its rows (ilg, and ilg + gpw when R = 2, in the tile) in the current
+  // tile, and at the tile's last step (past K in a ragged row: zeros).  Named scalars, not
+  // arrays: an array shared by the lambdas may be kept in scratch memory.
+  uint32_t vc0 = kOob, vs0 = kOob, vcl0 = kOob, vsl0 = kOob;
+  uint32_t vc1 = kOob, vs1 = kOob, vcl1 = kOob, vsl1 = kOob;
   int ig = 0, ilg = 0;
   auto tile_offsets = [&]() {
-    const int trow = it * si.gpw;
-    const bool ok = trow + ilg < si.nrows;  // rows past the range read zeros
-    vc = ok ? ((uint32_t)ilg * si.nb + ig) * CB : kOob;
-    vs = ok ? ((uint32_t)ilg * si.nb + ig) * 2 : kOob;
     const bool past_k = ((si.ns - 1) << si.lg2G) + ig >= si.nbc;
-    vc_last = past_k ? kOob : vc;
-    vs_last = past_k ? kOob : vs;
+    const int row = it * R * si.gpw + ilg;
+    const bool ok0 = row < si.nrows;  // rows past the range read zeros
+    vc0 = ok0 ? ((uint32_t)ilg * si.nb + ig) * CB : kOob;
+    vs0 = ok0 ? ((uint32_t)ilg * si.nb + ig) * 2 : kOob;
+    vcl0 = past_k ? kOob : vc0;
+    vsl0 = past_k ? kOob : vs0;
+    if constexpr (R == 2) {
+      const bool ok1 = row + si.gpw < si.nrows;
+      vc1 = ok1 ? ((uint32_t)(si.gpw + ilg) * si.nb + ig) * CB : kOob;
+      vs1 = ok1 ? ((uint32_t)(si.gpw + ilg) * si.nb + ig) * 2 : kOob;
+      vcl1 = past_k ? kOob : vc1;
+      vsl1 = past_k ? kOob : vs1;
+    }
   };
   auto next_issue = [&]() {  // the next (GEMV, chunk) with steps for this wave, if any
     ireal = 0;
@@ -658,7 +668,7 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
         ++gi;
         ci = 0;
       }
-      load_stage<LGW>(table, gi, ci, kc, wave, si);
+      load_stage<LGW, R>(table, gi, ci, kc, wave, si);
       ireal = si.end - si.start;
       ipad = (ireal + P - 1) / P * P;
     }
@@ -677,27 +687,30 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
   };
   next_issue();
 
-  auto issue = [&](Codes<FMT>& q, uint32_t& d) {
+  auto issue = [&](Codes<FMT> (&q)[R], uint32_t (&d)[R]) {
     // arithmetic, not branches or selects (which the compiler may turn into branches with
     // the loads duplicated): one load sequence for real and padding steps.  Once the range
     // is done the lane offsets are past the descriptor: zeros, no memory traffic.
     const uint32_t live = ireal > 0 ? 1u : 0u;
-    const uint32_t so = ((uint32_t)(it * si.gpw) * si.nb + (uint32_t)si.kb0 + (uint32_t)(ij << si.lg2G)) * live;
+    const uint32_t so = ((uint32_t)(it * R * si.gpw) * si.nb + (uint32_t)si.kb0 + (uint32_t)(ij << si.lg2G)) * live;
     const uint32_t lm = 0u - (uint32_t)(ij == si.ns - 1);  // all ones at a tile's last step
-    const uint32_t c = (vc_last & lm) | (vc & ~lm);
-    const uint32_t e = (vs_last & lm) | (vs & ~lm);
-    if constexpr (FMT == FQ4) {
-      q.a = __builtin_amdgcn_raw_buffer_load_b128(rc, c, so * CB, 0);
-    } else {
-      q.a = __builtin_amdgcn_raw_buffer_load_b128(rc, c, so * CB, 0);
-      q.b = __builtin_amdgcn_raw_buffer_load_b128(rc, c + 16, so * CB, 0);
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+      const uint32_t c = r == 0 ? (vcl0 & lm) | (vc0 & ~lm) : (vcl1 & lm) | (vc1 & ~lm);
+      const uint32_t e = r == 0 ? (vsl0 & lm) | (vs0 & ~lm) : (vsl1 & lm) | (vs1 & ~lm);
+      if constexpr (FMT == FQ4) {
+        q[r].a = __builtin_amdgcn_raw_buffer_load_b128(rc, c, so * CB, 0);
+      } else {
+        q[r].a = __builtin_amdgcn_raw_buffer_load_b128(rc, c, so * CB, 0);
+        q[r].b = __builtin_amdgcn_raw_buffer_load_b128(rc, c + 16, so * CB, 0);
+      }
+      // the scale and the next 2 bytes (ignored): a whole-register load, which the compiler
+      // neither widens nor merges, so the ring is waited on per slot
+      d[r] = __builtin_amdgcn_raw_buffer_load_b32(rs, e, so * 2, 0);
     }
-    // the scale and the next 2 bytes (ignored): a whole-register load, which the compiler
-    // neither widens nor merges, so the ring is waited on per slot
-    d = __builtin_amdgcn_raw_buffer_load_b32(rs, e, so * 2, 0);
     if (ireal > 0) {
       if (--ireal == 0) {  // padding steps follow: read nothing
-        vc = vs = vc_last = vs_last = kOob;
+        vc0 = vs0 = vcl0 = vsl0 = vc1 = vs1 = vcl1 = vsl1 = kOob;
       } else if (++ij == si.ns) {
         ij = 0;
         ++it;
@@ -707,8 +720,8 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
     if (ipad > 0 && --ipad == 0) next_issue();
   };
 
-  Codes<FMT> ring_q[P];
-  uint32_t ring_d[P];  // low 16 bits: the scale
+  Codes<FMT> ring_q[P][R];
+  uint32_t ring_d[P][R];  // low 16 bits: the scale
 #pragma unroll
   for (int p = 0; p < P; p++) issue(ring_q[p], ring_d[p]);
 
@@ -726,9 +739,11 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
   const char* lds_lane = xlds;   // this lane's first block of a tile
   const char* lds_last = xlds;   // ... its block at the tile's last step (past K: the last block)
   int cg = 0, clg = 0;
-  float acc[MM];
+  float acc[R][MM];
 #pragma unroll
-  for (int m = 0; m < MM; m++) acc[m] = 0.f;
+  for (int r = 0; r < R; r++)
+#pragma unroll
+    for (int m = 0; m < MM; m++) acc[r][m] = 0.f;
   bool alive = true;
   // Enter the next (GEMV, chunk): all waves finished reading the staged x, wait for earlier
   // outputs if asked, stage the new x and its block sums.  Every wave enters every
@@ -740,7 +755,7 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
       ++gc;
       cc = 0;
     }
-    load_stage<LGW>(table, gc, cc, kc, wave, sc);
+    load_stage<LGW, R>(table, gc, cc, kc, wave, sc);
     creal = sc.end - sc.start;
     cpad = (creal + P - 1) / P * P;
     ct = sc.start / sc.ns;
@@ -810,32 +825,40 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
       for (int p = 0; p < P; p++) {
         if (creal > 0) {  // uniform: a real step of this wave
           const char* xb = cj == sc.ns - 1 ? lds_last : lds_lane + cj * (sc.G * kBlkLds);
-          float c[MM];
-          chain_block<FMT, MM>(ring_q[p], xb, mstride, c);
+          float sxm[MM];
 #pragma unroll
-          for (int m = 0; m < MM; m++) {
-            const float sx = *reinterpret_cast<const float*>(xb + m * mstride + 128);
-            const float rr = fmaf(FMT == FQ4 ? -8.0f : -128.0f, sx, c[m]);
-            acc[m] = fmaf(h2f(ring_d[p]), rr, acc[m]);
+          for (int m = 0; m < MM; m++) sxm[m] = *reinterpret_cast<const float*>(xb + m * mstride + 128);
+#pragma unroll
+          for (int r = 0; r < R; r++) {
+            float c[MM];
+            chain_block<FMT, MM>(ring_q[p][r], xb, mstride, c);
+#pragma unroll
+            for (int m = 0; m < MM; m++) {
+              const float rr = fmaf(FMT == FQ4 ? -8.0f : -128.0f, sxm[m], c[m]);
+              acc[r][m] = fmaf(h2f(ring_d[p][r]), rr, acc[r][m]);
+            }
           }
           --creal;
           ++cj;
           if (cj == sc.ns || creal == 0) {  // this wave's part of the tile is done
-            float v[MM];
+            float v[R][MM];
 #pragma unroll
-            for (int m = 0; m < MM; m++) v[m] = group_sum_rt(acc[m], sc.lg2G);
+            for (int r = 0; r < R; r++)
+#pragma unroll
+              for (int m = 0; m < MM; m++) v[r][m] = group_sum_rt(acc[r][m], sc.lg2G);
             // waves holding the tile: the wave of step s is (NW s + NW - 1) / S; when S < NW
             // each non-empty wave holds one step
             const int t0 = ct * sc.ns, t1 = t0 + sc.ns;
             const int w0 = (NW * t0 + NW - 1) / sc.S, wl = (NW * (t1 - 1) + NW - 1) / sc.S;
             const int parts = sc.S >= NW ? wl - w0 + 1 : sc.ns;
-            const int row = ct * sc.gpw + clg;
             bool put = parts == 1;
-            if (!put) {
-              float* mine = part + ((wave * 2 + (t0 >= sc.start ? 1 : 0)) * 4 + clg) * MM;
+            if (!put) {  // rows of the tile: r * gpw + clg, fewer than 4 R
+              float* mine = part + ((wave * 2 + (t0 >= sc.start ? 1 : 0)) * 4 * R + clg) * MM;
               if (cg == 0) {
 #pragma unroll
-                for (int m = 0; m < MM; m++) mine[m] = v[m];
+                for (int r = 0; r < R; r++)
+#pragma unroll
+                  for (int m = 0; m < MM; m++) mine[r * sc.gpw * MM + m] = v[r][m];
               }
               asm volatile("" ::: "memory");
               int before = 0;
@@ -844,42 +867,54 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
               before = __builtin_amdgcn_readfirstlane(before);
               asm volatile("" ::: "memory");
               if (before == parts - 1) {  // the last part in: every part is in `part`
-                const float* p0 = part + ((w0 * 2 + 1) * 4 + clg) * MM;
 #pragma unroll
-                for (int m = 0; m < MM; m++) v[m] = p0[m];
+                for (int r = 0; r < R; r++) {
+                  const float* p0 = part + ((w0 * 2 + 1) * 4 * R + r * sc.gpw + clg) * MM;
+#pragma unroll
+                  for (int m = 0; m < MM; m++) v[r][m] = p0[m];
+                }
                 for (int u = w0 + 1; u <= wl; u++)
                   if (sc.S >= NW || ((u * sc.S) >> LGW) < (((u + 1) * sc.S) >> LGW)) {
-                    const float* pu = part + ((u * 2) * 4 + clg) * MM;
 #pragma unroll
-                    for (int m = 0; m < MM; m++) v[m] = v[m] + pu[m];
+                    for (int r = 0; r < R; r++) {
+                      const float* pu = part + ((u * 2) * 4 * R + r * sc.gpw + clg) * MM;
+#pragma unroll
+                      for (int m = 0; m < MM; m++) v[r][m] = v[r][m] + pu[m];
+                    }
                   }
                 if (lane == 0) done[w0] = 0;
                 put = true;
               }
             }
-            if (put && cg == 0 && row < sc.nrows) {
-              bool store = true;
-              if (sc.nchunks > 1) {  // chunk sums, added in chunk order
-                float* pa = pacc + row * MM;
 #pragma unroll
-                for (int m = 0; m < MM; m++) {
-                  if (!sc.first) v[m] = pa[m] + v[m];
-                  pa[m] = v[m];
+            for (int r = 0; r < R; r++) {
+              const int row = ct * R * sc.gpw + r * sc.gpw + clg;
+              if (put && cg == 0 && row < sc.nrows) {
+                bool store = true;
+                if (sc.nchunks > 1) {  // chunk sums, added in chunk order
+                  float* pa = pacc + row * MM;
+#pragma unroll
+                  for (int m = 0; m < MM; m++) {
+                    if (!sc.first) v[r][m] = pa[m] + v[r][m];
+                    pa[m] = v[r][m];
+                  }
+                  store = sc.last;
                 }
-                store = sc.last;
-              }
-              if (store) {
+                if (store) {
 #pragma unroll
-                for (int m = 0; m < MM; m++)
-                  if (m < sc.M)  // agent-coherent: a later GEMV may read it
-                    __hip_atomic_store((__attribute__((address_space(1))) float*)sc.y +
-                                           (int64_t)m * sc.ystride + row,
-                                       v[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                  for (int m = 0; m < MM; m++)
+                    if (m < sc.M)  // agent-coherent: a later GEMV may read it
+                      __hip_atomic_store((__attribute__((address_space(1))) float*)sc.y +
+                                             (int64_t)m * sc.ystride + row,
+                                         v[r][m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
               }
             }
             asm volatile("" ::: "memory");  // keep the store ahead of this step's loads
 #pragma unroll
-            for (int m = 0; m < MM; m++) acc[m] = 0.f;
+            for (int r = 0; r < R; r++)
+#pragma unroll
+              for (int m = 0; m < MM; m++) acc[r][m] = 0.f;
             if (cj == sc.ns) {
               cj = 0;
               ++ct;
@@ -1074,6 +1109,9 @@ QmvIdKernel select_id(int G, int R) {
 #ifndef BQM_P1_P
 #define BQM_P1_P 4  // blocks in flight per lane (Q4_0; Q8_0 blocks are twice as long: half)
 #endif
+#ifndef BQM_CHAIN_MM_WIDE
+#define BQM_CHAIN_MM_WIDE 8  // batch classes from this one up: 2 rows per lane, 8 waves
+#endif
 constexpr int kP1StaticLds = 1024;                   // reserved for the kernel's own __shared__
 constexpr int kP1MaxLds = 160 * 1024 - kP1StaticLds;  // dynamic LDS of a chain launch
 
@@ -1089,15 +1127,19 @@ constexpr int chain_ring() {
   return (FMT == FQ4 ? BQM_P1_P : BQM_P1_P / 2) / (MM >= 4 && FMT == FQ4 ? 2 : 1);
 }
 // log2 of the waves per workgroup: 16 waves, or 8 for the widest batch, whose sums need
-// more than the 128 registers a lane has when 16 waves share a CU
-constexpr int chain_lgw(int mm) { return mm >= 8 ? 3 : 4; }
+// more than the 128 registers a lane has when 16 waves share a CU (measured on the 27B
+// Q8_0 pass: M = 4 is fastest with 16 waves and one row per lane, M = 8 with 8 waves and
+// two rows per lane)
+constexpr int chain_lgw(int mm) { return mm >= BQM_CHAIN_MM_WIDE ? 3 : 4; }
+// rows per lane: for the widest batch one read of the staged inputs serves two rows' codes
+constexpr int chain_r(int mm) { return mm >= BQM_CHAIN_MM_WIDE ? 2 : 1; }
 template <int FMT>
 ChainKernel chain_kernel_f(int mm) {
   switch (mm) {
-    case 1: return k_qmv_chain<FMT, chain_ring<FMT, 1>(), 1, chain_lgw(1)>;
-    case 2: return k_qmv_chain<FMT, chain_ring<FMT, 2>(), 2, chain_lgw(2)>;
-    case 4: return k_qmv_chain<FMT, chain_ring<FMT, 4>(), 4, chain_lgw(4)>;
-    default: return k_qmv_chain<FMT, chain_ring<FMT, 8>(), 8, chain_lgw(8)>;
+    case 1: return k_qmv_chain<FMT, chain_ring<FMT, 1>(), 1, chain_lgw(1), chain_r(1)>;
+    case 2: return k_qmv_chain<FMT, chain_ring<FMT, 2>(), 2, chain_lgw(2), chain_r(2)>;
+    case 4: return k_qmv_chain<FMT, chain_ring<FMT, 4>(), 4, chain_lgw(4), chain_r(4)>;
+    default: return k_qmv_chain<FMT, chain_ring<FMT, 8>(), 8, chain_lgw(8), chain_r(8)>;
   }
 }
 ChainKernel chain_kernel(int fmt, int mm) {
@@ -1135,7 +1177,7 @@ int64_t chain_max_k() { return 32768; }
 // the table, the split-tile parts and M inputs of the longest K fit; otherwise every GEMV
 // longer than kc goes in chunks.  Returns false when even 32-block chunks do not fit.
 bool chain_plan(int n, int mm, int64_t max_nb, int64_t max_rows, int* kc, int* pacc_rows) {
-  const int64_t fixed = chain_lds(n, mm, 0, 0).total;
+  const int64_t fixed = chain_lds(n, mm, chain_r(mm), 0, 0).total;
   if (fixed + (int64_t)mm * max_nb * kBlkLds <= kP1MaxLds) {
     *kc = (int)max_nb;
     *pacc_rows = 0;

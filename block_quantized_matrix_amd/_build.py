@@ -18,6 +18,9 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-ffp-contract=off",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
+    # matrix-core results go to ordinary registers: the prefill epilogue works on every
+    # result with vector ops, which would otherwise first copy it out of the accumulators
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-function",
 ]
 SOURCES = ["api.hip", "repack.hip", "qmv.hip", "qmm.hip"]

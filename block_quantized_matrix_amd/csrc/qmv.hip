@@ -31,6 +31,8 @@
 // stores the row.  No atomics; the summation order is fixed for a given launch shape.
 #include "bqm_internal.h"
 
+#include <vector>
+
 namespace bqm {
 namespace {
 
@@ -38,7 +40,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kLdsBudget = 80 * 1024;  // bytes of LDS per workgroup (two per CU fit)
 
 __device__ __forceinline__ float h2f(uint32_t bits) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
@@ -52,254 +53,6 @@ enum { FQ4 = 0, FQ8 = 1 };
 template <int FMT> struct Codes;
 template <> struct Codes<FQ4> { u32x4 a; };
 template <> struct Codes<FQ8> { u32x4 a, b; };
-
-template <int FMT>
-__device__ __forceinline__ Codes<FMT> load_codes(const uint8_t* __restrict__ codes, size_t blk) {
-  Codes<FMT> c;
-  if constexpr (FMT == FQ4) {
-    c.a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(codes) + blk);
-  } else {
-    const u32x4* p = reinterpret_cast<const u32x4*>(codes) + 2 * blk;
-    c.a = __builtin_nontemporal_load(p);
-    c.b = __builtin_nontemporal_load(p + 1);
-  }
-  return c;
-}
-
-template <int FMT>
-__device__ __forceinline__ Codes<FMT> zero_codes() {
-  Codes<FMT> c;
-  if constexpr (FMT == FQ4) {
-    c.a = u32x4{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
-  } else {
-    c.a = u32x4{0u, 0u, 0u, 0u};
-    c.b = u32x4{0u, 0u, 0u, 0u};
-  }
-  return c;
-}
-
-// Per-block x sum in the order the M = 1 FMA chains use.
-template <int FMT>
-__device__ __forceinline__ float block_xsum(const float4 (&v)[8]) {
-  if constexpr (FMT == FQ4) {
-    float lo = 0.f, hi = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      lo = lo + v[i].x; lo = lo + v[i].y; lo = lo + v[i].z; lo = lo + v[i].w;
-    }
-#pragma unroll
-    for (int i = 4; i < 8; i++) {
-      hi = hi + v[i].x; hi = hi + v[i].y; hi = hi + v[i].z; hi = hi + v[i].w;
-    }
-    return lo + hi;
-  } else {
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-      s = s + v[i].x; s = s + v[i].y; s = s + v[i].z; s = s + v[i].w;
-    }
-    return s;
-  }
-}
-
-// M = 1: sum_j (w_j / d) x_j for one block, with the offset removed via the block x sum.
-template <int FMT>
-__device__ __forceinline__ float block_dot_m1(const Codes<FMT>& q, const float4 (&x)[8],
-                                              float sx) {
-  if constexpr (FMT == FQ4) {
-    const uint32_t w[4] = {q.a.x, q.a.y, q.a.z, q.a.w};
-    float lo = 0.f, hi = 0.f;
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-      const uint32_t l = w[k] & 0x0F0F0F0Fu;
-      lo = fmaf(ub(l, 0), x[k].x, lo); lo = fmaf(ub(l, 1), x[k].y, lo);
-      lo = fmaf(ub(l, 2), x[k].z, lo); lo = fmaf(ub(l, 3), x[k].w, lo);
-    }
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-      const uint32_t h = w[k] & 0xF0F0F0F0u;  // 16 * high nibble, in place
-      hi = fmaf(ub(h, 0), x[k + 4].x, hi); hi = fmaf(ub(h, 1), x[k + 4].y, hi);
-      hi = fmaf(ub(h, 2), x[k + 4].z, hi); hi = fmaf(ub(h, 3), x[k + 4].w, hi);
-    }
-    const float r = fmaf(hi, 0.0625f, lo);
-    return fmaf(-8.0f, sx, r);
-  } else {
-    const uint32_t w[8] = {q.a.x, q.a.y, q.a.z, q.a.w, q.b.x, q.b.y, q.b.z, q.b.w};
-    float a = 0.f;
-#pragma unroll
-    for (int k = 0; k < 8; k++) {
-      const uint32_t u = w[k] ^ 0x80808080u;  // q + 128 as unsigned bytes
-      a = fmaf(ub(u, 0), x[k].x, a); a = fmaf(ub(u, 1), x[k].y, a);
-      a = fmaf(ub(u, 2), x[k].z, a); a = fmaf(ub(u, 3), x[k].w, a);
-    }
-    return fmaf(-128.0f, sx, a);
-  }
-}
-
-// M > 1: the 32 weights of one block, dequantized exactly.
-template <int FMT>
-__device__ __forceinline__ void block_dequant(const Codes<FMT>& q, uint32_t dbits, float (&w)[32]) {
-  const float d = h2f(dbits);
-  if constexpr (FMT == FQ4) {
-    const float d16 = d * 0.0625f, m8d = -8.0f * d;
-    const uint32_t c[4] = {q.a.x, q.a.y, q.a.z, q.a.w};
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-      const uint32_t l = c[k] & 0x0F0F0F0Fu, h = c[k] & 0xF0F0F0F0u;
-#pragma unroll
-      for (int e = 0; e < 4; e++) {
-        w[4 * k + e] = fmaf(ub(l, e), d, m8d);
-        w[16 + 4 * k + e] = fmaf(ub(h, e), d16, m8d);
-      }
-    }
-  } else {
-    const float m128d = -128.0f * d;
-    const uint32_t c[8] = {q.a.x, q.a.y, q.a.z, q.a.w, q.b.x, q.b.y, q.b.z, q.b.w};
-#pragma unroll
-    for (int k = 0; k < 8; k++) {
-      const uint32_t u = c[k] ^ 0x80808080u;
-#pragma unroll
-      for (int e = 0; e < 4; e++) w[4 * k + e] = fmaf(ub(u, e), d, m128d);
-    }
-  }
-}
-
-template <int G>
-__device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int off = G / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
-
-// Per-workgroup pointers of the M inputs / outputs of the current tile.  It lives in LDS:
-// the caller's threads 0..7 fill it before tile_qmv, whose first barrier publishes it.
-// Offsets (in floats) rather than pointers, so that every access is derived from a kernel
-// argument and stays a global (not flat) memory access.
-struct TileIO {
-  int64_t x[8];  // X + x[m]: the K inputs of slot m
-  int64_t y[8];  // Y + y[m] + row: output of tile row `row` for slot m
-};
-
-// Rows [row_base, row_base + nrows) of the packed matrix (nrows <= RPW) times M <= MM
-// inputs.  All threads of the workgroup take part.  smem holds M * kcb * 8 float4 of
-// staged x plus kcb floats of block sums.
-template <int FMT, int MM, int G, int R>
-__device__ __forceinline__ void tile_qmv(const uint8_t* __restrict__ codes,
-                                         const uint16_t* __restrict__ scales, int nb,
-                                         int64_t row_base, int nrows, const float* __restrict__ X,
-                                         float* __restrict__ Y, const TileIO* io, int M,
-                                         float4* smem, int kcb) {
-  const int tid = threadIdx.x;
-  const int g = tid % G;
-  const int lr0 = (tid / G) * R;  // first tile row of this lane group
-  float* sxs = reinterpret_cast<float*>(smem + (size_t)M * kcb * 8);
-
-  bool row_ok[R];
-#pragma unroll
-  for (int r = 0; r < R; r++) row_ok[r] = lr0 + r < nrows;
-
-  float acc[R][MM];
-#pragma unroll
-  for (int r = 0; r < R; r++)
-#pragma unroll
-    for (int m = 0; m < MM; m++) acc[r][m] = 0.f;
-
-  for (int c0 = 0; c0 < nb; c0 += kcb) {
-    const int cn = min(kcb, nb - c0);
-    __syncthreads();  // LDS from the previous chunk / tile is no longer read
-    // ---- stage x[:, chunk] into LDS (swizzled), and the block sums for M = 1 ----
-    for (int idx = tid; idx < M * cn; idx += kThreads) {
-      const int m = idx / cn, bl = idx - m * cn;
-      const float4* src = reinterpret_cast<const float4*>(X + io->x[m] + (int64_t)(c0 + bl) * kQK);
-      float4* dst = smem + ((size_t)m * kcb + bl) * 8;
-      const int sw = bl & 7;
-      float4 v[8];
-      if constexpr (MM == 1) {
-#pragma unroll
-        for (int i = 0; i < 8; i++) v[i] = src[i];
-#pragma unroll
-        for (int i = 0; i < 8; i++) dst[i ^ sw] = v[i];
-        sxs[bl] = block_xsum<FMT>(v);
-      } else {
-        // swizzle on the load side: slot i of the LDS block holds chunk i ^ sw
-#pragma unroll
-        for (int i = 0; i < 8; i++) v[i] = src[i ^ sw];
-#pragma unroll
-        for (int i = 0; i < 8; i++) dst[i] = v[i];
-      }
-    }
-    __syncthreads();
-
-    // ---- stream the weights of this chunk ----
-    Codes<FMT> qn[R];
-    uint32_t dn[R];
-    auto issue = [&](int bl) {
-#pragma unroll
-      for (int r = 0; r < R; r++) {
-        if (row_ok[r] && bl < cn) {
-          const size_t blk = (size_t)(row_base + lr0 + r) * nb + (c0 + bl);
-          qn[r] = load_codes<FMT>(codes, blk);
-          dn[r] = scales[blk];
-        } else {
-          qn[r] = zero_codes<FMT>();
-          dn[r] = 0;
-        }
-      }
-    };
-    issue(g);
-    for (int bl = g; bl < cn; bl += G) {
-      Codes<FMT> q[R];
-      uint32_t d[R];
-#pragma unroll
-      for (int r = 0; r < R; r++) { q[r] = qn[r]; d[r] = dn[r]; }
-      issue(bl + G);  // prefetch the next block while this one is computed
-      const float4* xb = smem + (size_t)bl * 8;
-      const int sw = bl & 7;
-      if constexpr (MM == 1) {
-        float4 xv[8];
-#pragma unroll
-        for (int i = 0; i < 8; i++) xv[i] = xb[i ^ sw];
-        const float sx = sxs[bl];
-#pragma unroll
-        for (int r = 0; r < R; r++)
-          acc[r][0] = fmaf(h2f(d[r]), block_dot_m1<FMT>(q[r], xv, sx), acc[r][0]);
-      } else {
-        float w[R][32];
-#pragma unroll
-        for (int r = 0; r < R; r++) block_dequant<FMT>(q[r], d[r], w[r]);
-#pragma unroll
-        for (int m = 0; m < MM; m++) {
-          if (m < M) {
-            const float4* xm = xb + (size_t)m * kcb * 8;
-#pragma unroll
-            for (int i = 0; i < 8; i++) {
-              const float4 xv = xm[i ^ sw];
-#pragma unroll
-              for (int r = 0; r < R; r++) {
-                float a = acc[r][m];
-                a = fmaf(w[r][4 * i + 0], xv.x, a);
-                a = fmaf(w[r][4 * i + 1], xv.y, a);
-                a = fmaf(w[r][4 * i + 2], xv.z, a);
-                a = fmaf(w[r][4 * i + 3], xv.w, a);
-                acc[r][m] = a;
-              }
-            }
-          }
-        }
-      }
-    }
-  }
-
-  // ---- reduce across the lane group and store ----
-#pragma unroll
-  for (int r = 0; r < R; r++) {
-#pragma unroll
-    for (int m = 0; m < MM; m++) {
-      const float v = group_sum<G>(acc[r][m]);
-      if (g == 0 && row_ok[r] && m < M) Y[io->y[m] + lr0 + r] = v;
-    }
-  }
-}
 
 // ---- persistent GEMV chain ------------------------------------------------------------
 // Decode is bandwidth-critical, so the batch-M (M <= 8) product gets its own kernel shaped
@@ -412,13 +165,24 @@ struct GemvDesc {
 };
 static_assert(sizeof(GemvDesc) == sizeof(bqm_gemv), "bqm_gemv layout");
 
+// The expert-indexed form (qmv_id): `one` is the expert tensor as one matrix of E * N rows
+// (N = rows per expert), its x and y the bases of X and Y.
+struct IdxArgs {
+  const int32_t* ids;      // [T][top_k]
+  const uint16_t* scales;  // the scales of all E * N rows
+  int E, TS, top_k;        // experts; slots T * top_k; slots per token
+  int64_t xts, xss;        // input strides (floats) per token and per slot
+};
+
 struct ChainArgs {
   const GemvDesc* descs;  // n descriptors in device memory, or null: use `one`
+  const int64_t* seg;     // per GEMV {blocks before it in its segment, blocks of the segment}
   GemvDesc one;
   int n;
   int kc;                 // K blocks staged at a time (`one` only; else in the workspace)
   int pacc_rows;          // rows per workgroup of the partial-sum buffer (likewise)
   uint32_t* sync;         // workspace words (see grid_barrier); null for a chain of one
+  IdxArgs ix;             // the expert-indexed form only
 };
 
 // Per-GEMV values of one workgroup, computed once at kernel start (one thread per GEMV)
@@ -435,15 +199,27 @@ struct StageRow {
 };
 static_assert(sizeof(StageRow) == 64, "stage table row");
 
+// Rows of a GEMV before flattened position v of its segment, whose rows (nb blocks each)
+// start at position sbase.
+__device__ __forceinline__ int rows_before(int64_t v, int64_t sbase, int nb, int N) {
+  if (v <= sbase) return 0;
+  const int64_t r = (v - sbase + nb - 1) / nb;
+  return r < N ? (int)r : N;
+}
+
+// A segment is a run of GEMVs that starts with a waiting one (or the chain's first) and
+// holds no other: its GEMVs may run at once.  The weight blocks of a segment, its GEMVs'
+// rows one after another, are split evenly between the workgroups at row boundaries: a
+// row belongs to the workgroup whose share holds its first block.  A workgroup thus works
+// on the few GEMVs its share touches, and meets the others only at the waits.
 template <int FMT>
-__device__ __forceinline__ StageRow make_stage(const GemvDesc& d, int kc) {
+__device__ __forceinline__ StageRow make_stage(const GemvDesc& d, int64_t sbase, int64_t sblocks, int kc) {
   constexpr int CB = FMT == FQ4 ? 16 : 32;
   const int nb = (int)(d.K >> 5);
   const int N = (int)d.N;
-  // rows split as evenly as possible: the first N % grid workgroups get one more
   const int grid = (int)gridDim.x, b = (int)blockIdx.x;
-  const int base = N / grid, extra = N - base * grid;
-  const int r0 = b * base + (b < extra ? b : extra);
+  const int r0 = rows_before(b * sblocks / grid, sbase, nb, N);
+  const int r1 = rows_before((b + 1) * sblocks / grid, sbase, nb, N);
   const int64_t code_bytes = (int64_t)N * nb * CB;
   StageRow st;
   st.codes = d.w + (int64_t)r0 * nb * CB;
@@ -451,7 +227,7 @@ __device__ __forceinline__ StageRow make_stage(const GemvDesc& d, int kc) {
               (int64_t)r0 * nb;
   st.x = d.x;
   st.y = d.y + r0;
-  st.nrows = base + (b < extra ? 1 : 0);
+  st.nrows = r1 - r0;
   st.nb = nb;
   st.wait = d.wait ? 1 : 0;
   st.M = d.M;
@@ -468,7 +244,7 @@ struct Stage {
   const uint16_t* scales;
   const float* x;
   float* y;
-  int nrows, nb, nbc, kb0, lg2G, G, gpw, ns, S, start, end, M, xstride, ystride, nchunks;
+  int nrows, nb, nbc, kb0, lg2G, G, gpw, ns, S, start, end, M, xstride, ystride, nchunks, lo;
   bool ragged, wait, first, last;
 };
 
@@ -479,20 +255,9 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t v) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// The chunk-dependent values of a stage whose GEMV-level values are set.
 template <int LGW, int R>  // log2 of the waves of the workgroup; rows per lane
-__device__ __forceinline__ void load_stage(const StageRow* t, int i, int c, int kc, int wave, Stage& s) {
-  const StageRow r = t[i];
-  s.codes = reinterpret_cast<const uint8_t*>(uniform64(reinterpret_cast<uint64_t>(r.codes)));
-  s.scales = reinterpret_cast<const uint16_t*>(uniform64(reinterpret_cast<uint64_t>(r.scales)));
-  s.x = reinterpret_cast<const float*>(uniform64(reinterpret_cast<uint64_t>(r.x)));
-  s.y = reinterpret_cast<float*>(uniform64(reinterpret_cast<uint64_t>(r.y)));
-  s.nrows = __builtin_amdgcn_readfirstlane(r.nrows);
-  s.nb = __builtin_amdgcn_readfirstlane(r.nb);
-  s.M = __builtin_amdgcn_readfirstlane(r.M);
-  s.xstride = __builtin_amdgcn_readfirstlane(r.xstride);
-  s.ystride = __builtin_amdgcn_readfirstlane(r.ystride);
-  s.nchunks = __builtin_amdgcn_readfirstlane(r.nchunks);
-  const int wait = __builtin_amdgcn_readfirstlane(r.wait);
+__device__ __forceinline__ void stage_chunk(int c, int kc, int wave, int wait, Stage& s) {
   s.kb0 = c * kc;
   s.nbc = min(kc, s.nb - s.kb0);
   s.first = c == 0;
@@ -514,6 +279,45 @@ __device__ __forceinline__ void load_stage(const StageRow* t, int i, int c, int 
   s.S = ntiles * s.ns;
   s.start = (wave * s.S) >> LGW;
   s.end = ((wave + 1) * s.S) >> LGW;
+}
+
+template <int LGW, int R>
+__device__ __forceinline__ void load_stage(const StageRow* t, int i, int c, int kc, int wave, Stage& s) {
+  const StageRow r = t[i];
+  s.codes = reinterpret_cast<const uint8_t*>(uniform64(reinterpret_cast<uint64_t>(r.codes)));
+  s.scales = reinterpret_cast<const uint16_t*>(uniform64(reinterpret_cast<uint64_t>(r.scales)));
+  s.x = reinterpret_cast<const float*>(uniform64(reinterpret_cast<uint64_t>(r.x)));
+  s.y = reinterpret_cast<float*>(uniform64(reinterpret_cast<uint64_t>(r.y)));
+  s.nrows = __builtin_amdgcn_readfirstlane(r.nrows);
+  s.nb = __builtin_amdgcn_readfirstlane(r.nb);
+  s.M = __builtin_amdgcn_readfirstlane(r.M);
+  s.xstride = __builtin_amdgcn_readfirstlane(r.xstride);
+  s.ystride = __builtin_amdgcn_readfirstlane(r.ystride);
+  s.nchunks = __builtin_amdgcn_readfirstlane(r.nchunks);
+  s.lo = 0;
+  stage_chunk<LGW, R>(c, kc, wave, __builtin_amdgcn_readfirstlane(r.wait), s);
+}
+
+// Expert-indexed form: unit i is a group of up to MM slots routed to one expert (`groups`:
+// expert, first slot in the sorted list, slots).  The units' rows, N each, one unit after
+// another, are split evenly between the workgroups; this one holds flattened rows
+// [flo, fhi).  `base`: expert 0's row 0 (codes, scales), x and y bases, nb, nchunks.
+template <int LGW, int R, int CB>
+__device__ __forceinline__ void load_unit(const int* groups, const Stage& base, int i, int c, int kc,
+                                          int wave, int N, int64_t flo, int64_t fhi, Stage& s) {
+  const int e = __builtin_amdgcn_readfirstlane(groups[3 * i]);
+  const int64_t u0 = (int64_t)i * N;
+  const int r0 = (int)(flo - u0 < 0 ? 0 : flo - u0 > N ? N : flo - u0);
+  const int r1 = (int)(fhi - u0 < 0 ? 0 : fhi - u0 > N ? N : fhi - u0);
+  const int64_t row = (int64_t)e * N + r0;
+  s = base;
+  s.codes = base.codes + row * base.nb * CB;
+  s.scales = base.scales + row * base.nb;
+  s.y = base.y + r0;
+  s.nrows = r1 - r0;
+  s.lo = __builtin_amdgcn_readfirstlane(groups[3 * i + 1]);
+  s.M = __builtin_amdgcn_readfirstlane(groups[3 * i + 2]);
+  stage_chunk<LGW, R>(c, kc, wave, 0, s);
 }
 
 // Device-wide barrier between the GEMVs of a chain.  Workspace words: [0] release epoch,
@@ -572,6 +376,12 @@ __device__ __forceinline__ bool grid_barrier(uint32_t* ws, uint32_t epoch, bool*
   return *lds_ok;
 }
 
+// Slots of the indexed form, at most (its tables are built in LDS).
+constexpr int kIdMaxSlots = BQM_QMV_ID_MAX_T * BQM_QMV_ID_MAX_TOPK;
+// LDS rows (64 bytes) the indexed form's tables take: per-expert counts (E + 1), the slots
+// grouped by expert (TS) and the groups (3 ints each, at most TS).
+__host__ __device__ inline int idx_table_rows(int E, int TS) { return (4 * (E + 1) + 16 * TS + 63) / 64; }
+
 // Dynamic LDS of a chain launch, in bytes from the start: the stage table, the split-tile
 // parts, their counters, the per-row partial sums of chunked GEMVs, the staged inputs.
 struct ChainLds {
@@ -587,7 +397,7 @@ __host__ __device__ inline ChainLds chain_lds(int n, int mm, int r, int pacc_row
   return L;
 }
 
-template <int FMT, int P, int MM, int LGW, int R>
+template <int FMT, int P, int MM, int LGW, int R, bool IDX>
 __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
   constexpr int NW = 1 << LGW, NT = 64 << LGW;  // waves, threads
   extern __shared__ float4 smem[];
@@ -607,7 +417,8 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep in SGPRs
   const int kc = a.sync ? (int)a.sync[5] : a.kc;
   const int pacc_rows = a.sync ? (int)a.sync[6] : a.pacc_rows;
-  const ChainLds ly = chain_lds(a.n, MM, R, pacc_rows, kc);
+  const int TS = IDX ? a.ix.TS : 0;
+  const ChainLds ly = chain_lds(IDX ? idx_table_rows(a.ix.E, TS) : a.n, MM, R, pacc_rows, kc);
   char* lds = reinterpret_cast<char*>(smem);
   StageRow* table = reinterpret_cast<StageRow*>(lds);
   float* part = reinterpret_cast<float*>(lds + ly.part);
@@ -615,11 +426,164 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
   float* pacc = reinterpret_cast<float*>(lds + ly.pacc);
   char* xlds = lds + ly.x;
   const int mstride = kc * kBlkLds;  // bytes between the staged inputs
-  for (int i = tid; i < a.n; i += NT) table[i] = make_stage<FMT>(a.descs ? a.descs[i] : a.one, kc);
+  // indexed form: per-expert counts, then starts; the valid slots grouped by expert; the
+  // groups (expert, first position in srt, slots)
+  int* cnt = reinterpret_cast<int*>(lds);
+  int* srt = cnt + (IDX ? a.ix.E + 1 : 0);
+  int* groups = srt + TS;
+  __shared__ int lds_units;
+  __shared__ int scan_w[2 * NW];
+  Stage ibase;  // indexed form: expert 0, bases
+  if constexpr (IDX) {
+    // Counting sort of the slots by expert (bucket E: invalid ids), stable: within an
+    // expert's run the slots are in index order, so every workgroup forms the same groups
+    // (the workgroups split a group's rows between them).  Each run is cut into groups of
+    // at most MM slots.
+    const int E = a.ix.E;
+    for (int e = tid; e <= E; e += NT) cnt[e] = 0;
+    __syncthreads();
+    constexpr int SPT = (kIdMaxSlots + NT - 1) / NT;
+    int key[SPT], pos[SPT];
+#pragma unroll
+    for (int k = 0; k < SPT; k++) {
+      const int i = tid + k * NT;
+      key[k] = E;
+      pos[k] = 0;
+      if (i < TS) {
+        const int e = a.ix.ids[i];
+        key[k] = e >= 0 && e < E ? e : E;
+        pos[k] = atomicAdd(&cnt[key[k]], 1);
+      }
+    }
+    __syncthreads();
+    // exclusive scans over e = 0..E of the slot counts and of the group counts; thread t
+    // owns entries [t * per, (t + 1) * per)
+    const int per = (E + 1 + NT - 1) / NT;
+    const int e0 = min(E + 1, tid * per), e1 = min(E + 1, e0 + per);
+    int ls = 0, lg = 0;
+    for (int e = e0; e < e1; e++) {
+      const int c = cnt[e];
+      ls += c;
+      lg += e < E ? (c + MM - 1) / MM : 0;
+    }
+    int is = ls, ig = lg;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(is, o, 64), v = __shfl_up(ig, o, 64);
+      if (lane >= o) {
+        is += u;
+        ig += v;
+      }
+    }
+    if (lane == 63) {
+      scan_w[2 * wave] = is;
+      scan_w[2 * wave + 1] = ig;
+    }
+    __syncthreads();
+    int s0 = is - ls, g0 = ig - lg;
+    for (int w = 0; w < wave; w++) {
+      s0 += scan_w[2 * w];
+      g0 += scan_w[2 * w + 1];
+    }
+    for (int e = e0; e < e1; e++) {
+      const int c = cnt[e];
+      cnt[e] = s0;
+      if (e < E)
+        for (int j = 0; j < c; j += MM) {
+          groups[3 * g0] = e;
+          groups[3 * g0 + 1] = s0 + j;
+          groups[3 * g0 + 2] = min(MM, c - j);
+          g0++;
+        }
+      s0 += c;
+    }
+    if (tid == NT - 1) lds_units = g0;
+    __syncthreads();
+    // each slot at the place its counting atomic returned (an order that differs between
+    // workgroups), then at its rank by index within its run
+#pragma unroll
+    for (int k = 0; k < SPT; k++) {
+      const int i = tid + k * NT;
+      if (i < TS && key[k] < E) srt[cnt[key[k]] + pos[k]] = i;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < SPT; k++) {
+      const int i = tid + k * NT;
+      if (i < TS && key[k] < E) {
+        const int q0 = cnt[key[k]], q1 = cnt[key[k] + 1];
+        int r = q0;
+        for (int q = q0; q < q1; q++) r += srt[q] < i;
+        pos[k] = r;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < SPT; k++) {
+      const int i = tid + k * NT;
+      if (i < TS && key[k] < E) srt[pos[k]] = i;
+    }
+    const int N = (int)a.one.N, nb = (int)(a.one.K >> 5);
+    ibase.codes = a.one.w;
+    ibase.scales = a.ix.scales;
+    ibase.x = a.one.x;
+    ibase.y = a.one.y;
+    ibase.nrows = 0;
+    ibase.nb = nb;
+    ibase.xstride = nb * kQK;
+    ibase.ystride = N;
+    ibase.nchunks = (nb + kc - 1) / kc;
+    ibase.M = 1;
+    ibase.lo = 0;
+  } else {
+    for (int i = tid; i < a.n; i += NT) {
+      const GemvDesc d = a.descs ? a.descs[i] : a.one;
+      table[i] = a.seg ? make_stage<FMT>(d, a.seg[2 * i], a.seg[2 * i + 1], kc)
+                       : make_stage<FMT>(d, 0, d.N * (d.K >> 5), kc);
+    }
+  }
   if (tid < NW) done[tid] = 0;
   if (tid == 0 && a.sync) lds_epoch = ld_agent(a.sync);  // stable until all have arrived once
   __syncthreads();
   uint32_t epoch = a.sync ? lds_epoch : 0u;
+  // units of work: the GEMVs, or (indexed form) the groups; none when K = 0
+  const int n_units = IDX ? (a.one.K > 0 ? __builtin_amdgcn_readfirstlane(lds_units) : 0) : a.n;
+  // this workgroup's units [u_begin, u_end) and (indexed form) flattened rows [flo, fhi)
+  int u_begin = 0, u_end = n_units;
+  int64_t flo = 0, fhi = 0;
+  if constexpr (IDX) {
+    const int64_t rows = (int64_t)n_units * a.one.N;
+    flo = (int64_t)blockIdx.x * rows / gridDim.x;
+    fhi = (int64_t)(blockIdx.x + 1) * rows / gridDim.x;
+    if (fhi > flo) {
+      u_begin = (int)(flo / a.one.N);
+      u_end = (int)((fhi - 1) / a.one.N) + 1;
+    } else {
+      u_end = 0;
+    }
+  }
+  if constexpr (IDX) {
+    // rows of slots that no group computes, each by one workgroup: a negative id gives
+    // zeros, an id >= E NaN; with K = 0 every valid slot's sums are empty (zeros)
+    const int N = (int)a.one.N;
+    for (int ts = blockIdx.x; ts < TS; ts += gridDim.x) {
+      const int e = a.ix.ids[ts];
+      const bool valid = e >= 0 && e < a.ix.E;
+      if (valid && n_units > 0) continue;
+      const float v = valid || e < 0 ? 0.0f : __builtin_nanf("");
+      for (int n = tid; n < N; n += NT) a.one.y[(int64_t)ts * N + n] = v;
+    }
+    if (n_units == 0) return;
+  }
+  auto load = [&](int i, int c, Stage& st) {
+    if constexpr (IDX) load_unit<LGW, R, CB>(groups, ibase, i, c, kc, wave, (int)a.one.N, flo, fhi, st);
+    else load_stage<LGW, R>(table, i, c, kc, wave, st);
+  };
+  // input and output row of batch entry m of the current unit: m itself, or (indexed form)
+  // the m-th slot of the group
+  auto slot_of = [&](const Stage& st, int m) {
+    return IDX ? __builtin_amdgcn_readfirstlane(srt[st.lo + m]) : m;
+  };
 
   // Both sides walk the same sequence of steps: for each (GEMV, chunk) in which this wave
   // has steps, its steps padded to a multiple of P (padding steps load nothing useful and
@@ -628,7 +592,7 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
   // same on every path through the loop.
 
   // ---------------- issue side: P steps ahead ----------------
-  int gi = -1, ci = 0;       // GEMV and chunk being issued
+  int gi = u_begin - 1, ci = 0;  // unit and chunk being issued
   Stage si;
   si.nchunks = 0;
   int it = 0, ij = 0;        // this wave's tile, step in tile
@@ -664,11 +628,12 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
       if (ci + 1 < si.nchunks) {
         ++ci;
       } else {
-        if (gi + 1 >= a.n) break;
+        if (gi + 1 >= u_end) break;
         ++gi;
         ci = 0;
       }
-      load_stage<LGW, R>(table, gi, ci, kc, wave, si);
+      load(gi, ci, si);
+      if (si.nrows == 0) ci = si.nchunks - 1;  // none of its rows here: skip its chunks
       ireal = si.end - si.start;
       ipad = (ireal + P - 1) / P * P;
     }
@@ -732,7 +697,7 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
   // part that completes the count adds the parts in wave order, stores the rows and resets
   // the count.  A chunked GEMV adds each chunk's row sums into `pacc` and stores at its last
   // chunk.  Every store is followed by its step's loads.
-  int gc = -1, cc = 0;                               // GEMV and chunk being consumed
+  int gc = u_begin - 1, cc = 0;                      // unit and chunk being consumed
   int ct = 0, cj = 0, creal = 0, cpad = 0;           // tile, step in tile, steps left
   Stage sc;
   sc.nchunks = 0;
@@ -745,25 +710,35 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
 #pragma unroll
     for (int m = 0; m < MM; m++) acc[r][m] = 0.f;
   bool alive = true;
-  // Enter the next (GEMV, chunk): all waves finished reading the staged x, wait for earlier
-  // outputs if asked, stage the new x and its block sums.  Every wave enters every
-  // (GEMV, chunk), in order.
-  auto enter = [&]() {
-    if (cc + 1 < sc.nchunks) {
-      ++cc;
-    } else {
-      ++gc;
-      cc = 0;
+  // Enter the next (unit, chunk) with rows in this workgroup: wait for earlier outputs
+  // where a unit asks (also for a unit with none of its rows here: every workgroup takes
+  // part in every wait), then, once all waves finished reading the staged x, stage the new
+  // x and its block sums.  Every wave enters the same (unit, chunk)s, in order.  False when
+  // no unit is left or a wait failed.
+  auto enter = [&]() -> bool {
+    for (;;) {
+      if (cc + 1 < sc.nchunks) {
+        ++cc;
+      } else {
+        if (gc + 1 >= u_end) return false;
+        ++gc;
+        cc = 0;
+      }
+      load(gc, cc, sc);
+      if (sc.wait && gc > 0 && a.sync) {
+        alive = grid_barrier<LOADS>(a.sync, ++epoch, &lds_ok);
+        if (!alive) return false;
+      }
+      if (sc.nrows > 0) break;
+      cc = sc.nchunks - 1;  // none of its rows here: skip its chunks
     }
-    load_stage<LGW, R>(table, gc, cc, kc, wave, sc);
     creal = sc.end - sc.start;
     cpad = (creal + P - 1) / P * P;
     ct = sc.start / sc.ns;
     cj = sc.start - ct * sc.ns;
     cg = lane & (sc.G - 1);
     clg = lane >> sc.lg2G;
-    if (sc.wait && gc > 0 && a.sync) alive = grid_barrier<LOADS>(a.sync, ++epoch, &lds_ok);
-    else __syncthreads();
+    __syncthreads();
     // x comes through agent-coherent loads (other workgroups may have written it), 16
     // bytes per lane: a pass of a wave stages 8 whole blocks of one input.  Up to 4 passes'
     // loads are issued before any is used.  Then 8 lanes form the blocks' sums in chain
@@ -773,7 +748,16 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
     const int nch = sc.nbc * 8;
 #pragma unroll
     for (int m = 0; m < MM; m++) {
-      const float* xrow = sc.x + (int64_t)(m < sc.M ? m : 0) * sc.xstride + (int64_t)sc.kb0 * kQK;
+      int64_t xo = 0;  // input row of entry m (entries m >= M read nothing)
+      if (m < sc.M) {
+        if constexpr (IDX) {
+          const int ts = slot_of(sc, m), t = ts / a.ix.top_k;
+          xo = t * a.ix.xts + (ts - t * a.ix.top_k) * a.ix.xss;
+        } else {
+          xo = (int64_t)m * sc.xstride;
+        }
+      }
+      const float* xrow = sc.x + xo + (int64_t)sc.kb0 * kQK;
       const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
           (void*)xrow, (short)0, m < sc.M ? sc.nbc * 128 : 0, 0x00020000);
       char* xm = xlds + m * mstride;
@@ -816,10 +800,11 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
     lds_lane = xlds + cg * kBlkLds;
     lds_last = ((sc.ns - 1) << sc.lg2G) + cg < sc.nbc ? lds_lane + (sc.ns - 1) * (sc.G * kBlkLds)
                                                       : xlds + (sc.nbc - 1) * kBlkLds;  // its d is 0
+    return true;
   };
 
-  enter();
-  while (alive) {
+  bool more = enter();
+  while (more) {
     if (cpad > 0) {
 #pragma unroll
       for (int p = 0; p < P; p++) {
@@ -905,7 +890,7 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
                   for (int m = 0; m < MM; m++)
                     if (m < sc.M)  // agent-coherent: a later GEMV may read it
                       __hip_atomic_store((__attribute__((address_space(1))) float*)sc.y +
-                                             (int64_t)m * sc.ystride + row,
+                                             (int64_t)slot_of(sc, m) * sc.ystride + row,
                                          v[r][m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
               }
@@ -925,133 +910,7 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
       }
       cpad -= P;
     }
-    if (cpad == 0) {
-      if (cc + 1 >= sc.nchunks && gc + 1 >= a.n) break;
-      enter();
-    }
-  }
-}
-
-// ---- expert-indexed GEMV -----------------------------------------------------------
-// Every workgroup first turns the T x top_k ids into per-expert slot lists in LDS (experts
-// ascending, slots ascending within an expert), split into passes of at most 8 slots.
-// The work items are (pass, row tile) pairs, pass-major; workgroup w takes a contiguous
-// range of them.  Each work item stages its slots' inputs and streams the tile's rows of
-// the expert once for all of them.  Slots with a negative id are
-// zero-filled, slots with an id >= E NaN-filled, each by exactly one workgroup.
-struct IdLds {
-  int* ids;        // [TS]
-  int* cnt;        // [E]   slots routed to expert e
-  int* off;        // [E]   start of e's slots in list
-  int* poff;       // [E]   first pass of e
-  int* list;       // [TS]  slot indices grouped by expert
-  int* pass_e;     // [TS]  expert of pass p
-  int* pass_lo;    // [TS]  list offset of pass p
-  int* pass_m;     // [TS]  slots in pass p (1..8)
-  int* totals;     // [2]   number of passes, scratch
-};
-
-template <int FMT, int G, int R>
-__global__ __launch_bounds__(kThreads) void k_qmv_id(const uint8_t* __restrict__ codes,
-                                                     const uint16_t* __restrict__ scales,
-                                                     const int32_t* __restrict__ ids, int E,
-                                                     int N, int nb, int TS, int top_k,
-                                                     const float* __restrict__ X, int64_t xts,
-                                                     int64_t xss, float* __restrict__ Y,
-                                                     int kcb1, int kcb8, int x_floats) {
-  extern __shared__ float4 smem[];
-  constexpr int RPW = (kThreads / G) * R;  // rows per tile
-  const int tid = threadIdx.x;
-  int* ib = reinterpret_cast<int*>(smem + x_floats / 4);
-  IdLds L;
-  L.ids = ib;
-  L.cnt = L.ids + TS;
-  L.off = L.cnt + E;
-  L.poff = L.off + E;
-  L.list = L.poff + E;
-  L.pass_e = L.list + TS;
-  L.pass_lo = L.pass_e + TS;
-  L.pass_m = L.pass_lo + TS;
-  L.totals = L.pass_m + TS;
-  __shared__ TileIO io;
-
-  for (int i = tid; i < TS; i += kThreads) L.ids[i] = ids[i];
-  __syncthreads();
-  for (int e = tid; e < E; e += kThreads) {
-    int c = 0;
-    for (int i = 0; i < TS; i++) c += L.ids[i] == e;
-    L.cnt[e] = c;
-  }
-  __syncthreads();
-  // exclusive scans over experts (slot offsets and pass offsets), by wave 0
-  if (tid < 64) {
-    const int per = (E + 63) / 64;
-    const int e0 = tid * per, e1 = min(E, e0 + per);
-    int s_slots = 0, s_pass = 0;
-    for (int e = e0; e < e1; e++) { s_slots += L.cnt[e]; s_pass += (L.cnt[e] + 7) / 8; }
-    int inc_slots = s_slots, inc_pass = s_pass;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int a = __shfl_up(inc_slots, o, 64), b = __shfl_up(inc_pass, o, 64);
-      if (tid >= o) { inc_slots += a; inc_pass += b; }
-    }
-    int run_slots = inc_slots - s_slots, run_pass = inc_pass - s_pass;
-    for (int e = e0; e < e1; e++) {
-      L.off[e] = run_slots;
-      L.poff[e] = run_pass;
-      run_slots += L.cnt[e];
-      run_pass += (L.cnt[e] + 7) / 8;
-    }
-    if (tid == 63) L.totals[0] = inc_pass;
-  }
-  __syncthreads();
-  for (int e = tid; e < E; e += kThreads) {
-    const int c = L.cnt[e];
-    if (c == 0) continue;
-    int j = L.off[e];
-    for (int i = 0; i < TS; i++)
-      if (L.ids[i] == e) L.list[j++] = i;
-    for (int p = 0; p < (c + 7) / 8; p++) {
-      L.pass_e[L.poff[e] + p] = e;
-      L.pass_lo[L.poff[e] + p] = L.off[e] + 8 * p;
-      L.pass_m[L.poff[e] + p] = min(8, c - 8 * p);
-    }
-  }
-  __syncthreads();
-  const int P = L.totals[0];
-
-  // padding / out-of-range slots
-  for (int ts = blockIdx.x; ts < TS; ts += gridDim.x) {
-    const int e = L.ids[ts];
-    if (e >= 0 && e < E) continue;
-    const float v = e < 0 ? 0.0f : __builtin_nanf("");
-    for (int n = tid; n < N; n += kThreads) Y[(size_t)ts * N + n] = v;
-  }
-
-  // work items: (pass, tile) of RPW rows
-  const int ntiles = (N + RPW - 1) / RPW;
-  const int64_t n_items = (int64_t)P * ntiles;
-  const int64_t per_wg = (n_items + gridDim.x - 1) / gridDim.x;
-  const int64_t it0 = (int64_t)blockIdx.x * per_wg;
-  const int64_t it1 = min(n_items, it0 + per_wg);
-  for (int64_t it = it0; it < it1; it++) {
-    const int p = (int)(it / ntiles), tile = (int)(it % ntiles);
-    const int e = L.pass_e[p], lo = L.pass_lo[p], M = L.pass_m[p];
-    __syncthreads();  // io of the previous item is no longer read
-    if (tid < 8) {
-      const int mm = tid < M ? tid : 0;
-      const int ts = L.list[lo + mm];
-      const int t = ts / top_k, s = ts - t * top_k;
-      io.x[tid] = t * xts + s * xss;
-      io.y[tid] = (int64_t)ts * N + (int64_t)tile * RPW;
-    }
-    __syncthreads();
-    const int64_t row_base = (int64_t)e * N + (int64_t)tile * RPW;
-    const int nrows = min(RPW, N - tile * RPW);
-    if (M == 1)
-      tile_qmv<FMT, 1, G, R>(codes, scales, nb, row_base, nrows, X, Y, &io, 1, smem, kcb1);
-    else
-      tile_qmv<FMT, 8, G, R>(codes, scales, nb, row_base, nrows, X, Y, &io, M, smem, kcb8);
+    if (cpad == 0) more = enter();
   }
 }
 
@@ -1063,47 +922,12 @@ __global__ void k_fill(float* __restrict__ y, int64_t n, float v) {
 
 // ---------------------------------------------------------------- host side ----
 
-int pick_group(int64_t nb) {
-  int best = 64;
-  int64_t best_waste = (nb + 63) / 64 * 64 - nb;
-  for (int G : {32, 16}) {
-    const int64_t waste = (nb + G - 1) / G * G - nb;
-    if (waste < best_waste) { best = G; best_waste = waste; }
-  }
-  return best;
-}
-
-int chunk_blocks(int64_t nb, int M, int budget) {
-  const int per_block = M * 128 + (M == 1 ? 4 : 0);
-  int64_t kcb = budget / per_block;
-  if (kcb >= nb) return (int)(nb > 0 ? nb : 1);
-  return (int)(kcb & ~int64_t(7));
-}
-
-size_t x_lds_bytes(int M, int kcb) { return (size_t)M * kcb * 128 + (M == 1 ? (size_t)kcb * 4 : 0); }
-
 // Kernels using more than 64 KB of dynamic LDS must say so once.
 template <typename Kern>
 void allow_lds(Kern k, size_t bytes) {
   if (bytes > 64 * 1024)
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-}
-
-using QmvIdKernel = void (*)(const uint8_t*, const uint16_t*, const int32_t*, int, int, int, int,
-                             int, const float*, int64_t, int64_t, float*, int, int, int);
-
-template <int FMT, int G>
-QmvIdKernel select_id_r(int R) {
-  if (R == 2) return k_qmv_id<FMT, G, 2>;
-  return k_qmv_id<FMT, G, 1>;
-}
-
-template <int FMT>
-QmvIdKernel select_id(int G, int R) {
-  if (G == 64) return select_id_r<FMT, 64>(R);
-  if (G == 32) return select_id_r<FMT, 32>(R);
-  return select_id_r<FMT, 16>(R);
 }
 
 #ifndef BQM_P1_P
@@ -1133,17 +957,18 @@ constexpr int chain_ring() {
 constexpr int chain_lgw(int mm) { return mm >= BQM_CHAIN_MM_WIDE ? 3 : 4; }
 // rows per lane: for the widest batch one read of the staged inputs serves two rows' codes
 constexpr int chain_r(int mm) { return mm >= BQM_CHAIN_MM_WIDE ? 2 : 1; }
-template <int FMT>
+template <int FMT, bool IDX>
 ChainKernel chain_kernel_f(int mm) {
   switch (mm) {
-    case 1: return k_qmv_chain<FMT, chain_ring<FMT, 1>(), 1, chain_lgw(1), chain_r(1)>;
-    case 2: return k_qmv_chain<FMT, chain_ring<FMT, 2>(), 2, chain_lgw(2), chain_r(2)>;
-    case 4: return k_qmv_chain<FMT, chain_ring<FMT, 4>(), 4, chain_lgw(4), chain_r(4)>;
-    default: return k_qmv_chain<FMT, chain_ring<FMT, 8>(), 8, chain_lgw(8), chain_r(8)>;
+    case 1: return k_qmv_chain<FMT, chain_ring<FMT, 1>(), 1, chain_lgw(1), chain_r(1), IDX>;
+    case 2: return k_qmv_chain<FMT, chain_ring<FMT, 2>(), 2, chain_lgw(2), chain_r(2), IDX>;
+    case 4: return k_qmv_chain<FMT, chain_ring<FMT, 4>(), 4, chain_lgw(4), chain_r(4), IDX>;
+    default: return k_qmv_chain<FMT, chain_ring<FMT, 8>(), 8, chain_lgw(8), chain_r(8), IDX>;
   }
 }
-ChainKernel chain_kernel(int fmt, int mm) {
-  return fmt == BQM_Q4_0 ? chain_kernel_f<FQ4>(mm) : chain_kernel_f<FQ8>(mm);
+ChainKernel chain_kernel(int fmt, int mm, bool idx) {
+  if (idx) return fmt == BQM_Q4_0 ? chain_kernel_f<FQ4, true>(mm) : chain_kernel_f<FQ8, true>(mm);
+  return fmt == BQM_Q4_0 ? chain_kernel_f<FQ4, false>(mm) : chain_kernel_f<FQ8, false>(mm);
 }
 
 int cu_count() {
@@ -1192,20 +1017,24 @@ bool chain_plan(int n, int mm, int64_t max_nb, int64_t max_rows, int* kc, int* p
   return true;
 }
 
-// Launch a chain (descriptors in device memory, or `one` when descs is null).
-int launch_chain(int fmt, int mm, const GemvDesc* descs, const GemvDesc* one, int n, int kc,
-                 int pacc_rows, uint32_t* sync, hipStream_t s) {
+// Launch a chain (descriptors in device memory, or `one` when descs is null), or with
+// `ix` the expert-indexed form of `one`.
+int launch_chain(int fmt, int mm, const GemvDesc* descs, const int64_t* seg, const GemvDesc* one,
+                 int n, int kc, int pacc_rows, uint32_t* sync, hipStream_t s,
+                 const IdxArgs* ix = nullptr) {
   ChainArgs a;
   a.descs = descs;
+  a.seg = seg;
   if (one) a.one = *one; else a.one = GemvDesc{nullptr, nullptr, nullptr, 0, 0, fmt, 0, 1, 0};
   a.n = n;
   a.kc = kc;
   a.pacc_rows = pacc_rows;
   a.sync = sync;
-  ChainKernel k = chain_kernel(fmt, mm);
+  if (ix) a.ix = *ix; else a.ix = IdxArgs{nullptr, nullptr, 0, 0, 0, 0, 0};
+  ChainKernel k = chain_kernel(fmt, mm, ix != nullptr);
   // per kernel: 1 = its static LDS fits the reserve, -1 = it does not
-  static int static_ok[2][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
-  int& ok = static_ok[fmt == BQM_Q4_0 ? 0 : 1][mm == 1 ? 0 : mm == 2 ? 1 : mm == 4 ? 2 : 3];
+  static int static_ok[2][2][4] = {};
+  int& ok = static_ok[ix ? 1 : 0][fmt == BQM_Q4_0 ? 0 : 1][mm == 1 ? 0 : mm == 2 ? 1 : mm == 4 ? 2 : 3];
   if (ok == 0) {
     hipFuncAttributes fa;
     ok = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(k)) == hipSuccess &&
@@ -1229,11 +1058,13 @@ int launch_chain(int fmt, int mm, const GemvDesc* descs, const GemvDesc* one, in
 
 // ---- chain API.  Workspace: 64 header words {release epoch, -, error, n, fmt, kc,
 // partial-sum rows, M class, ...}, one 128-byte arrival flag per workgroup (at most
-// kChainMaxWorkgroups), then the descriptors.
+// kChainMaxWorkgroups), then the descriptors, then per descriptor its segment's split
+// {blocks before it in its segment, blocks of the segment}.
 constexpr int64_t kChainSyncBytes = (kChainHeaderWords + kChainMaxWorkgroups * kFlagStrideWords) * 4;
+constexpr int64_t kSegBytes = 2 * sizeof(int64_t);
 
 size_t chain_workspace_bytes(int n) {
-  return n < 1 ? 0 : (size_t)(kChainSyncBytes + (int64_t)n * (int64_t)sizeof(GemvDesc));
+  return n < 1 ? 0 : (size_t)(kChainSyncBytes + (int64_t)n * (int64_t)(sizeof(GemvDesc) + kSegBytes));
 }
 
 int chain_prepare(const bqm_gemv* descs, int n, void* ws, hipStream_t s) {
@@ -1256,32 +1087,51 @@ int chain_prepare(const bqm_gemv* descs, int n, void* ws, hipStream_t s) {
     if (((uintptr_t)d.w_packed & 15) || ((uintptr_t)d.x & 15) || ((uintptr_t)d.y & 3))
       return BQM_E_ALIGN;
   }
-  // then the ones that depend on the device: one workgroup's rows must stay below 2 GiB
+  // segments: each waiting GEMV (and the first) starts one; its GEMVs' blocks are split
+  // between the workgroups (see make_stage)
+  std::vector<int64_t> seg(2 * (size_t)n);
+  for (int i = 0, j; i < n; i = j) {
+    int64_t blocks = 0;
+    for (j = i; j < n && (j == i || !descs[j].wait); j++) {
+      seg[2 * j] = blocks;
+      blocks += descs[j].N * (descs[j].K / kQK);
+    }
+    for (int k = i; k < j; k++) seg[2 * k + 1] = blocks;
+  }
+  // then the checks that depend on the device: a workgroup's rows of one GEMV (at most
+  // ceil(share / nb) for a share of ceil(blocks / workgroups) blocks) stay below 2 GiB
   const int cus = cu_count();
   if (cus > kChainMaxWorkgroups) return BQM_E_UNSUPPORTED;
   int64_t max_rows = 0;
   for (int i = 0; i < n; i++) {
     const bqm_gemv& d = descs[i];
-    const int64_t rows = (d.N + cus - 1) / cus;
-    if ((rows + 1) * (d.K / kQK) * CB >= ((int64_t)1 << 31)) return BQM_E_SHAPE;
+    const int64_t nb = d.K / kQK, share = (seg[2 * i + 1] + cus - 1) / cus;
+    int64_t rows = (share + nb - 1) / nb;
+    rows = rows < d.N ? rows : d.N;
+    if ((rows + 1) * nb * CB >= ((int64_t)1 << 31)) return BQM_E_SHAPE;
     max_rows = rows > max_rows ? rows : max_rows;
   }
   const int mm = m_class(M);
   int kc = 0, pacc_rows = 0;
   if (!chain_plan(n, mm, max_nb, max_rows, &kc, &pacc_rows)) return BQM_E_SHAPE;
   uint32_t head[8] = {0, 0, 0, (uint32_t)n, (uint32_t)fmt, (uint32_t)kc, (uint32_t)pacc_rows, (uint32_t)mm};
+  char* wsb = static_cast<char*>(ws);
   if (hipMemsetAsync(ws, 0, kChainSyncBytes, s) != hipSuccess ||
       hipMemcpyAsync(ws, head, sizeof(head), hipMemcpyHostToDevice, s) != hipSuccess ||
-      hipMemcpyAsync(static_cast<char*>(ws) + kChainSyncBytes, descs, (size_t)n * sizeof(GemvDesc),
+      hipMemcpyAsync(wsb + kChainSyncBytes, descs, (size_t)n * sizeof(GemvDesc),
                      hipMemcpyHostToDevice, s) != hipSuccess ||
+      hipMemcpyAsync(wsb + kChainSyncBytes + (int64_t)n * sizeof(GemvDesc), seg.data(),
+                     (size_t)n * kSegBytes, hipMemcpyHostToDevice, s) != hipSuccess ||
       hipStreamSynchronize(s) != hipSuccess)
     return BQM_E_LAUNCH;
   return BQM_OK;
 }
 
 int chain_launch(int fmt, int M, void* ws, int n, hipStream_t s) {
-  const GemvDesc* d = reinterpret_cast<const GemvDesc*>(static_cast<char*>(ws) + kChainSyncBytes);
-  return launch_chain(fmt, m_class(M), d, nullptr, n, 0, 0, static_cast<uint32_t*>(ws), s);
+  char* wsb = static_cast<char*>(ws);
+  const GemvDesc* d = reinterpret_cast<const GemvDesc*>(wsb + kChainSyncBytes);
+  const int64_t* seg = reinterpret_cast<const int64_t*>(wsb + kChainSyncBytes + (int64_t)n * sizeof(GemvDesc));
+  return launch_chain(fmt, m_class(M), d, seg, nullptr, n, 0, 0, static_cast<uint32_t*>(ws), s);
 }
 
 int chain_status(const void* ws, hipStream_t s) {
@@ -1306,35 +1156,32 @@ int launch_qmv(int fmt, const void* w, const float* X, float* Y, int M, int64_t 
   int kc = 0, pacc_rows = 0;
   if (!chain_plan(1, mm, K / kQK, rows, &kc, &pacc_rows)) return BQM_E_SHAPE;
   const GemvDesc d{static_cast<const uint8_t*>(w), X, Y, N, K, fmt, 0, M, 0};
-  return launch_chain(fmt, mm, nullptr, &d, 1, kc, pacc_rows, nullptr, s);
+  return launch_chain(fmt, mm, nullptr, nullptr, &d, 1, kc, pacc_rows, nullptr, s);
 }
 
+// Expert-indexed GEMV: the chain kernel's indexed form, with E * N rows as one matrix.  The
+// batch class is that of min(T, 8): one token usually adds at most one slot to an expert,
+// so up to 8 tokens stream each selected expert once; an expert with more slots is
+// streamed once per group of 8.
 int launch_qmv_id(int fmt, const void* w, int E, int64_t N, int64_t K, const int32_t* ids, int T,
                   int top_k, const float* X, int64_t xts, int64_t xss, float* Y, hipStream_t s) {
   const int TS = T * top_k;
-  // K == 0 and E == 0 need no special path: the kernel then streams nothing, writes the
-  // empty sums (0) and marks every non-negative id of an empty expert set out of range.
   Layout L;
   layout_of(fmt, (int64_t)E * N, K, &L);
+  const int CB = fmt == BQM_Q4_0 ? 16 : 32;
+  const int mm = m_class(T < kChainMaxM ? T : kChainMaxM);
+  const int cus = cu_count();
+  // a workgroup's rows of one group: its share of the groups' rows (at most TS groups of N)
+  int64_t rows = ((int64_t)TS * N + cus - 1) / cus;
+  rows = rows < N ? rows : N;
+  if ((rows + 1) * L.nb * CB >= ((int64_t)1 << 31)) return BQM_E_SHAPE;
+  int kc = 0, pacc_rows = 0;
+  if (!chain_plan(idx_table_rows(E, TS), mm, L.nb, rows, &kc, &pacc_rows)) return BQM_E_SHAPE;
+  if (kc < 1) kc = 1;  // K = 0: nothing is staged, but chunk counts divide by kc
   const uint8_t* codes = static_cast<const uint8_t*>(w);
-  const uint16_t* scales = reinterpret_cast<const uint16_t*>(codes + L.scales_off);
-  const int G = pick_group(L.nb);
-  const int R = 2;
-  const int budget = 48 * 1024;
-  const int kcb1 = chunk_blocks(L.nb, 1, budget), kcb8 = chunk_blocks(L.nb, 8, budget);
-  size_t xb = x_lds_bytes(1, kcb1) > x_lds_bytes(8, kcb8) ? x_lds_bytes(1, kcb1) : x_lds_bytes(8, kcb8);
-  xb = (xb + 15) & ~size_t(15);
-  const int x_floats = (int)(xb / 4);
-  const size_t lds = xb + (size_t)(3 * E + 5 * TS + 2) * 4;
-  const int64_t rpw = (kThreads / G) * R;
-  const int64_t ntiles = (N + rpw - 1) / rpw;
-  int64_t grid = (int64_t)TS * ntiles;
-  if (grid > 1024) grid = 1024;
-  QmvIdKernel k = fmt == BQM_Q4_0 ? select_id<FQ4>(G, R) : select_id<FQ8>(G, R);
-  allow_lds(k, lds);
-  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kThreads), lds, s, codes, scales, ids, E, (int)N,
-                     (int)L.nb, TS, top_k, X, xts, xss, Y, kcb1, kcb8, x_floats);
-  return launch_status();
+  const IdxArgs ix{ids, reinterpret_cast<const uint16_t*>(codes + L.scales_off), E, TS, top_k, xts, xss};
+  const GemvDesc d{codes, X, Y, N, K, fmt, 0, 1, 0};
+  return launch_chain(fmt, mm, nullptr, nullptr, &d, 1, kc, pacc_rows, nullptr, s, &ix);
 }
 
 }  // namespace bqm

@@ -125,7 +125,8 @@ def test_chain_host_validation():
                                    ctypes.c_void_p(w), None)
 
     assert bqm.chain_workspace_bytes(0) == 0
-    assert bqm.chain_workspace_bytes(2) - bqm.chain_workspace_bytes(1) == ctypes.sizeof(bqm.Gemv) == 56
+    # per GEMV: its descriptor (56 bytes) and its segment's split (two int64)
+    assert bqm.chain_workspace_bytes(2) - bqm.chain_workspace_bytes(1) == ctypes.sizeof(bqm.Gemv) + 16 == 72
     assert prep([], n=0) == 2                                    # empty chain
     assert prep([_gemv(64, 64)], w=0) == 1                       # no workspace
     assert prep([_gemv(64, 64)], w=ws + 8) == 3                  # misaligned workspace

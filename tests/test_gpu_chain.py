@@ -70,19 +70,45 @@ def test_chain_batched_dependent_stages(fmt, M):
 
 
 @pytest.mark.parametrize("M", [3, 8])
-def test_chain_batched_equals_qmv_and_ragged(M):
-    """A batched chain gives the same bits as qmv_q8_0 with the same M, one call per GEMV,
-    on ragged and tiny shapes."""
+def test_chain_batched_ragged_one_segment(M):
+    """Independent GEMVs of a batched chain form one segment, whose rows of all GEMVs are
+    split between the workgroups together: ragged and tiny shapes, and one long K."""
     shapes = [(37, 96), (300, 1184), (1, 9600), (2049, 32768)]
-    say("chain batched vs qmv", M)
+    say("chain batched one segment", M)
     Ws, Wps, xs, ys, descs, ws = make_chain("q8_0", shapes, ("chain-bq", M), dependent=False, M=M)
     bqm.qmv_chain("q8_0", M, ws, len(descs))
     assert bqm.bqm_chain_status(ws) == 0
-    for (N, K), Wp, x, y in zip(shapes, Wps, xs, ys):
-        ref = torch.empty((M, N), device=DEV)
-        bqm.qmv_q8_0(Wp, x, ref, M, N, K)
-        assert torch.equal(ref, y), f"{N}x{K}"
-    check_stages("q8_0", shapes[:3], Ws[:3], xs[:3], ys[:3], M=M)
+    check_stages("q8_0", shapes, Ws, xs, ys, M=M)
+
+
+def test_chain_segments_with_mixed_waits():
+    """Segments of several GEMVs with different K: A and B read x0; C (waits) reads A's
+    output and D (same segment) B's; E (waits) reads C's.  A workgroup whose share of a
+    segment misses a GEMV still takes part in that segment's wait."""
+    fmt = "q4_0"
+    say("chain mixed waits")
+    sh = {"A": (5120, 4096), "B": (320, 4096), "C": (96, 5120), "D": (2000, 320), "E": (4096, 96)}
+    Wi = {k: weights(fmt, N, K, ("chain-mix", k)) for k, (N, K) in sh.items()}
+    Wp = {k: packed(fmt, Wi[k], *sh[k]) for k in sh}
+    y = {k: torch.full((1, N), float("nan"), device=DEV) for k, (N, K) in sh.items()}
+    x0 = gen.normal((1, 4096), ("chain-mix-x",), device=DEV)
+    xin = {"A": x0, "B": x0, "C": y["A"], "D": y["B"], "E": y["C"]}
+    wait = {"A": False, "B": False, "C": True, "D": False, "E": True}
+    order = ["A", "B", "C", "D", "E"]
+    descs = [bqm.gemv(fmt, Wp[k], xin[k], y[k], *sh[k], wait=wait[k]) for k in order]
+    ws = torch.zeros(bqm.chain_workspace_bytes(len(descs)), dtype=torch.uint8, device=DEV)
+    bqm.bqm_chain_prepare(descs, ws)
+    for rep in range(2):
+        for k in order:
+            y[k].fill_(float("nan"))
+        bqm.qmv_chain(fmt, 1, ws, len(descs))
+        assert bqm.bqm_chain_status(ws) == 0
+        for k in order:
+            N, K = sh[k]
+            xi = host(xin[k]).reshape(1, K)
+            assert np.all(np.isfinite(xi)), f"{k} read an input that was never written"
+            Yr, S = oracle.qmv(fmt, host(Wi[k]), xi, N, K)
+            check_close(host(y[k]).reshape(1, N), Yr, S, f"mixed waits {k} (replay {rep})")
 
 
 def test_chain_ragged_and_tiny_shapes():
@@ -95,23 +121,22 @@ def test_chain_ragged_and_tiny_shapes():
     check_stages("q4_0", shapes, Ws, xs, ys)
 
 
-def test_chain_equals_separate_launches_and_replays():
-    """A chain gives the same bits as the batch-1 calls one by one, on every replay."""
+def test_chain_replays_are_bit_identical():
+    """Every replay of a chain gives the same bits (and matches the oracle)."""
     shapes = [(7168, 5120), (5120, 5120), (34816, 5120), (5120, 17408)]
-    say("chain vs separate")
+    say("chain replays")
     Ws, Wps, xs, ys, descs, ws = make_chain("q4_0", shapes, ("chain-eq",), dependent=False)
-    sep = []
-    for (N, K), Wp, x in zip(shapes, Wps, xs):
-        y = torch.empty((1, N), device=DEV)
-        bqm.qmv_q4_0(Wp, x, y, 1, N, K)
-        sep.append(y)
+    first = None
     for rep in range(3):
         for y in ys:
             y.fill_(float("nan"))
         bqm.qmv_chain("q4_0", 1, ws, len(descs))
         assert bqm.bqm_chain_status(ws) == 0
-        for y, ys_ in zip(sep, ys):
-            assert torch.equal(y, ys_), f"replay {rep}"
+        if first is None:
+            first = [y.clone() for y in ys]
+            check_stages("q4_0", shapes, Ws, xs, ys)
+        for y, y0 in zip(ys, first):
+            assert torch.equal(y, y0), f"replay {rep}"
 
 
 def test_chain_mismatch_is_reported_and_computes_nothing():

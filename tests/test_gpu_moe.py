@@ -100,3 +100,77 @@ def test_qmv_id_deterministic():
     bqm.qmv_id("q4_0", Wp, E, N, K, idd, T, 4, X, K, 0, Y1)
     bqm.qmv_id("q4_0", Wp, E, N, K, idd, T, 4, X, K, 0, Y2)
     assert torch.equal(Y1, Y2)
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0"])
+@pytest.mark.parametrize("T", [2, 3, 5, 8])
+def test_qmv_id_batch_classes(fmt, T):
+    """T tokens run in the batch class of min(T, 8) (2, 4, 8, 8): groups of every size,
+    some shorter than the class, with padding slots among them."""
+    E, N, K, top_k = 6, 130, 1184, 3
+    ids = gen.router_ids(T, E, top_k, ("cls-router", T))
+    ids[0, 1] = -1
+    X = gen.normal((T, top_k, K), ("cls-x", T, fmt), device=DEV)
+    say("qmv_id classes", fmt, T)
+    y, Yr, S = run_id(fmt, E, N, K, ids, X, top_k * K, K, ("cls", fmt, T))
+    check_close(y, Yr, S, f"qmv_id {fmt} T={T}")
+    assert np.all(y[0, 1] == 0)
+
+
+@pytest.mark.parametrize("T,K", [(16, 16384), (4, 32768), (1, 32768)])
+def test_qmv_id_long_k_is_chunked(T, K):
+    """Inputs of a long K do not fit the LDS at once: each group is walked in chunks of K
+    with per-row partial sums."""
+    E, N, top_k = 8, 100, 4
+    ids = gen.router_ids(T, E, top_k, ("long-router", T))
+    X = gen.normal((T, top_k, K), ("long-x", T, K), device=DEV)
+    say("qmv_id long K", T, K)
+    y, Yr, S = run_id("q8_0", E, N, K, ids, X, top_k * K, K, ("long", T, K))
+    check_close(y, Yr, S, f"qmv_id long K T={T}")
+
+
+def test_qmv_id_maximum_slots_and_experts():
+    """T = 64 tokens x top_k = 32 slots over E = 4096 experts (the limits), with padding and
+    out-of-range ids mixed in: the grouping tables at their largest."""
+    from block_quantized_matrix_amd import bqm as b
+    E, N, K, T, top_k = b.QMV_ID_MAX_E, 8, 64, b.QMV_ID_MAX_T, b.QMV_ID_MAX_TOPK
+    rng = np.random.default_rng(7)
+    ids = rng.integers(0, 64, size=(T, top_k)).astype(np.int32) * 64  # crowd 64 experts
+    ids[::3, 5] = rng.integers(0, E, size=ids[::3, 5].shape)
+    ids[1::7, 2] = -1
+    ids[2::9, 9] = E + 5
+    X = gen.normal((T, K), ("max-x",), device=DEV)
+    say("qmv_id max slots")
+    y, Yr, S = run_id("q4_0", E, N, K, ids, X, K, 0, ("max",))
+    bad = ids >= E
+    assert np.all(np.isnan(y[bad]))
+    check_close(y[~bad], Yr[~bad], S[~bad], "qmv_id max slots")
+
+
+def test_qmv_id_empty_k_and_no_experts():
+    """K = 0: every valid slot's sum is empty (zeros); E = 0: every id is out of range."""
+    ids = torch.tensor([[0, -1], [2, 5]], dtype=torch.int32, device=DEV)
+    W = torch.zeros(256, dtype=torch.uint8, device=DEV)
+    X = torch.zeros(64, device=DEV)
+    Y = torch.full((2, 2, 24), -7.0, device=DEV)
+    bqm.qmv_id("q4_0", W, 3, 24, 0, ids, 2, 2, X, 0, 0, Y)
+    y = host(Y)
+    assert np.all(y[0, 0] == 0) and np.all(y[0, 1] == 0) and np.all(y[1, 0] == 0)
+    assert np.all(np.isnan(y[1, 1]))
+    Y.fill_(-7.0)
+    bqm.qmv_id("q4_0", W, 0, 24, 32, ids, 2, 2, X, 0, 0, Y)
+    y = host(Y)
+    assert np.all(y[0, 1] == 0)
+    assert np.all(np.isnan(y[0, 0])) and np.all(np.isnan(y[1]))
+
+
+def test_qmv_id_groups_split_between_workgroups():
+    """Experts with more slots than one group holds, and groups whose rows are split between
+    workgroups: every workgroup must form the same groups (slot order within an expert's
+    run is by slot index), or some rows of a slot are never computed."""
+    E, N, K, T, top_k = 3, 2048, 256, 16, 2
+    ids = np.stack([np.zeros(T, np.int32), (np.arange(T) % 2 + 1).astype(np.int32)], axis=1)
+    X = gen.normal((T, K), ("split-x",), device=DEV)
+    say("qmv_id groups split between workgroups")
+    y, Yr, S = run_id("q4_0", E, N, K, ids, X, K, 0, ("split",))
+    check_close(y, Yr, S, "groups split between workgroups")

@@ -16,6 +16,8 @@ namespace {
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kThreads = 256;
 
@@ -57,11 +59,48 @@ __global__ __launch_bounds__(kThreads) void k_quantize_q8_act(const float4* __re
 
 // ---------------------------------------------------------------- qmm ----
 // Workgroup tile 128 (m) x 128 (n), four waves as 2 x 2 of 64 x 64, each wave 2 x 2 MFMA
-// tiles of 32 x 32.  K advances four blocks (128 bytes of codes per row) per LDS stage.
+// tiles of 32 x 32.  K advances four blocks (128 bytes of codes per row) per LDS stage;
+// the next stage's codes and scales are loaded into registers while the current one is
+// computed.
+//
+// The block-scale epilogue, not the integer products, bounds this kernel: per 32 x 32 tile
+// and block one int8 MFMA (32 cycles) meets 1024 fp32 rescales.  The scale product
+// dx[m][b] * dw[n][b] of a tile is an outer product, so it goes to the matrix cores too:
+// one bf16 MFMA with K = 6 used terms, dx split exactly into three truncated bf16 parts
+// and dw (fp16, 11 significant bits) into two, every partial product exact in fp32.
+// Per element and block the vector units then do one conversion and one FMA.
 constexpr int BM = 128, BN = 128, BKB = 4;     // BKB blocks of 32 per stage
 constexpr int ROWB = BKB * 32 + 16;            // LDS row stride in bytes (padding vs conflicts)
 
-__global__ __launch_bounds__(kThreads) void k_qmm_q8_0(const int8_t* __restrict__ Wc,   // [N][K]
+// v = hi + mid + lo exactly, each a truncated bf16 (returned as its 16 bits)
+__device__ __forceinline__ void split3(float v, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  const uint32_t h = __float_as_uint(v) & 0xFFFF0000u;
+  const float r1 = v - __uint_as_float(h);
+  const uint32_t m = __float_as_uint(r1) & 0xFFFF0000u;
+  const float r2 = r1 - __uint_as_float(m);
+  hi = h >> 16;
+  mid = m >> 16;
+  lo = __float_as_uint(r2) >> 16;
+}
+
+// MFMA operand rows of the scale outer product (k = 0..5 used, 6..15 zero):
+//   A (row m): dx parts  {hi, hi, mid, mid, lo, lo}
+//   B (col n): dw parts  {hi, lo, hi, lo, hi, lo}
+// so that sum_k A[m][k] B[k][n] = (dx_hi + dx_mid + dx_lo) (dw_hi + dw_lo).
+__device__ __forceinline__ u32x4 dx_operand(float dx) {
+  uint32_t h, m, l;
+  split3(dx, h, m, l);
+  return u32x4{h | (h << 16), m | (m << 16), l | (l << 16), 0u};
+}
+__device__ __forceinline__ u32x4 dw_operand(uint32_t dw_bits) {
+  const float d = h2f(dw_bits);
+  const uint32_t h = __float_as_uint(d) & 0xFFFF0000u;
+  const uint32_t l = __float_as_uint(d - __uint_as_float(h)) >> 16;
+  const uint32_t w = (h >> 16) | (l << 16);
+  return u32x4{w, w, w, 0u};
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_qmm_q8_0(const int8_t* __restrict__ Wc,   // [N][K]
                                                        const uint16_t* __restrict__ Wd,  // [N][nb]
                                                        const int8_t* __restrict__ Xq,    // [M][K]
                                                        const float* __restrict__ dx,     // [M][nb]
@@ -69,8 +108,8 @@ __global__ __launch_bounds__(kThreads) void k_qmm_q8_0(const int8_t* __restrict_
                                                        int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(16))) int8_t sA[BM * ROWB];
   __shared__ __attribute__((aligned(16))) int8_t sB[BN * ROWB];
-  __shared__ float sdx[BKB][BM];
-  __shared__ float sdw[BKB][BN];
+  __shared__ u32x4 sXs[BKB * BM + 1];  // dx operands per (block, m); the last: zeros
+  __shared__ u32x4 sWs[BKB * BN];      // dw operands per (block, n)
 
   // Workgroups are dealt round-robin to the eight XCDs; give the workgroups of one XCD
   // neighbouring tiles (all m-tiles of a few n-tiles) so they share W rows in that L2.
@@ -85,73 +124,101 @@ __global__ __launch_bounds__(kThreads) void k_qmm_q8_0(const int8_t* __restrict_
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = (wave & 1) * 64, wn = (wave >> 1) * 64;
   const int l32 = lane & 31, lh = lane >> 5;
+  if (tid == 0) sXs[BKB * BM] = u32x4{0u, 0u, 0u, 0u};
 
-  float acc[2][2][16];
+  f32x16 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; i++)
 #pragma unroll
-    for (int j = 0; j < 2; j++)
-#pragma unroll
-      for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+    for (int j = 0; j < 2; j++) acc[i][j] = f32x16{};
 
-  // staging assignment: 128 rows x 128 bytes per operand = 1024 16-byte pieces, 4/thread
-  for (int b0 = 0; b0 < nb; b0 += BKB) {
-    const int bn = min(BKB, nb - b0);
-    __syncthreads();
-#pragma unroll
-    for (int p = 0; p < 4; p++) {
-      const int piece = tid + p * kThreads;   // 0..1023
-      const int row = piece >> 3, c16 = piece & 7;   // 8 pieces of 16 B per row
-      const bool kin = (c16 >> 1) < bn;             // 2 pieces per block
-      u32x4 va = {0u, 0u, 0u, 0u}, vb = {0u, 0u, 0u, 0u};
-      if (kin && m0 + row < M)
-        va = *reinterpret_cast<const u32x4*>(Xq + (size_t)(m0 + row) * K + (size_t)b0 * 32 + c16 * 16);
-      if (kin && n0 + row < N)
-        vb = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(Wc + (size_t)(n0 + row) * K + (size_t)b0 * 32 + c16 * 16));
-      *reinterpret_cast<u32x4*>(sA + row * ROWB + c16 * 16) = va;
-      *reinterpret_cast<u32x4*>(sB + row * ROWB + c16 * 16) = vb;
-    }
-    for (int e = tid; e < BKB * BM; e += kThreads) {
-      const int kb = e / BM, r = e % BM;
-      const bool kin = kb < bn;
-      sdx[kb][r] = (kin && m0 + r < M) ? dx[(size_t)(m0 + r) * nb + b0 + kb] : 0.f;
-      sdw[kb][r] = (kin && n0 + r < N) ? h2f(Wd[(size_t)(n0 + r) * nb + b0 + kb]) : 0.f;
-    }
-    __syncthreads();
-
-    for (int kb = 0; kb < bn; kb++) {
-      i32x4 a[2], bfrag[2];
-#pragma unroll
-      for (int i = 0; i < 2; i++)
-        a[i] = *reinterpret_cast<const i32x4*>(sA + (wm + i * 32 + l32) * ROWB + kb * 32 + lh * 16);
-#pragma unroll
-      for (int j = 0; j < 2; j++)
-        bfrag[j] = *reinterpret_cast<const i32x4*>(sB + (wn + j * 32 + l32) * ROWB + kb * 32 + lh * 16);
-      float dwv[2];
-#pragma unroll
-      for (int j = 0; j < 2; j++) dwv[j] = sdw[kb][wn + j * 32 + l32];
-#pragma unroll
-      for (int i = 0; i < 2; i++) {
-        // the 16 rows this lane holds in a 32x32 tile: 8*(r/4) + 4*lh + r%4
-        float dxv[16];
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-          const float4 t = *reinterpret_cast<const float4*>(&sdx[kb][wm + i * 32 + 8 * q + 4 * lh]);
-          dxv[4 * q + 0] = t.x; dxv[4 * q + 1] = t.y; dxv[4 * q + 2] = t.z; dxv[4 * q + 3] = t.w;
-        }
-#pragma unroll
-        for (int j = 0; j < 2; j++) {
-          const i32x16 zero = {};
-          const i32x16 isum = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], bfrag[j], zero, 0, 0, 0);
-#pragma unroll
-          for (int r = 0; r < 16; r++)
-            acc[i][j][r] = fmaf(dxv[r] * dwv[j], (float)isum[r], acc[i][j][r]);
-        }
-      }
-    }
+  // staging: 128 rows x 128 bytes per operand = 1024 16-byte pieces, 4 per thread; 512
+  // scales per operand, 2 per thread
+  u32x4 pa0, pa1, pa2, pa3, pb0, pb1, pb2, pb3;
+  float px0, px1;
+  uint32_t pw0, pw1;
+#define BQM_FETCH(B0)                                                                          \
+  {                                                                                            \
+    const int bn_ = min(BKB, nb - (B0));                                                       \
+    u32x4* pa_[4] = {&pa0, &pa1, &pa2, &pa3};                                                  \
+    u32x4* pb_[4] = {&pb0, &pb1, &pb2, &pb3};                                                  \
+    _Pragma("unroll") for (int p = 0; p < 4; p++) {                                            \
+      const int piece = tid + p * kThreads, row = piece >> 3, c16 = piece & 7;                 \
+      const bool kin = (c16 >> 1) < bn_;                                                       \
+      u32x4 va = {0u, 0u, 0u, 0u}, vb = {0u, 0u, 0u, 0u};                                     \
+      if (kin && m0 + row < M)                                                                 \
+        va = *reinterpret_cast<const u32x4*>(Xq + (size_t)(m0 + row) * K + (size_t)(B0) * 32 + c16 * 16); \
+      if (kin && n0 + row < N)                                                                 \
+        vb = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(                       \
+            Wc + (size_t)(n0 + row) * K + (size_t)(B0) * 32 + c16 * 16));                      \
+      *pa_[p] = va;                                                                            \
+      *pb_[p] = vb;                                                                            \
+    }                                                                                          \
+    float* px_[2] = {&px0, &px1};                                                              \
+    uint32_t* pw_[2] = {&pw0, &pw1};                                                           \
+    _Pragma("unroll") for (int q = 0; q < 2; q++) {                                            \
+      const int e = tid + q * kThreads, kb = e >> 7, r = e & 127;                              \
+      const bool kin = kb < bn_;                                                               \
+      *px_[q] = (kin && m0 + r < M) ? dx[(size_t)(m0 + r) * nb + (B0) + kb] : 0.f;             \
+      *pw_[q] = (kin && n0 + r < N) ? (uint32_t)Wd[(size_t)(n0 + r) * nb + (B0) + kb] : 0u;   \
+    }                                                                                          \
   }
 
+  BQM_FETCH(0)
+  for (int b0 = 0; b0 < nb; b0 += BKB) {
+    const int bn = min(BKB, nb - b0);
+    __syncthreads();  // every wave is done with the previous stage
+    {
+      const u32x4 pa_[4] = {pa0, pa1, pa2, pa3};
+      const u32x4 pb_[4] = {pb0, pb1, pb2, pb3};
+#pragma unroll
+      for (int p = 0; p < 4; p++) {
+        const int piece = tid + p * kThreads, row = piece >> 3, c16 = piece & 7;
+        *reinterpret_cast<u32x4*>(sA + row * ROWB + c16 * 16) = pa_[p];
+        *reinterpret_cast<u32x4*>(sB + row * ROWB + c16 * 16) = pb_[p];
+      }
+      const float px_[2] = {px0, px1};
+      const uint32_t pw_[2] = {pw0, pw1};
+#pragma unroll
+      for (int q = 0; q < 2; q++) {
+        const int e = tid + q * kThreads;  // = kb * 128 + r
+        sXs[e] = dx_operand(px_[q]);
+        sWs[e] = dw_operand(pw_[q]);
+      }
+    }
+    __syncthreads();
+    if (b0 + BKB < nb) BQM_FETCH(b0 + BKB)  // in flight while this stage is computed
+
+    for (int kb = 0; kb < bn; kb++) {
+      i32x4 a[2], bq[2];
+      bf16x8 as[2], bs[2];
+#pragma unroll
+      for (int i = 0; i < 2; i++) {
+        a[i] = *reinterpret_cast<const i32x4*>(sA + (wm + i * 32 + l32) * ROWB + kb * 32 + lh * 16);
+        // lanes 32..63 hold k = 8..15 of the scale product: zeros
+        const u32x4* p = lh ? &sXs[BKB * BM] : &sXs[kb * BM + wm + i * 32 + l32];
+        as[i] = __builtin_bit_cast(bf16x8, *p);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; j++) {
+        bq[j] = *reinterpret_cast<const i32x4*>(sB + (wn + j * 32 + l32) * ROWB + kb * 32 + lh * 16);
+        const u32x4* p = lh ? &sXs[BKB * BM] : &sWs[kb * BN + wn + j * 32 + l32];
+        bs[j] = __builtin_bit_cast(bf16x8, *p);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+          const i32x16 isum = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], bq[j], i32x16{}, 0, 0, 0);
+          const f32x16 sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as[i], bs[j], f32x16{}, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 16; r++) acc[i][j][r] = fmaf(sc[r], (float)isum[r], acc[i][j][r]);
+        }
+    }
+  }
+#undef BQM_FETCH
+
+  // a lane's 16 results of a 32 x 32 tile: rows 8 (r / 4) + 4 lh + r % 4, column l32
 #pragma unroll
   for (int i = 0; i < 2; i++)
 #pragma unroll

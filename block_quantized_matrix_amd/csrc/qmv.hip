@@ -31,6 +31,8 @@
 // stores the row.  No atomics; the summation order is fixed for a given launch shape.
 #include "bqm_internal.h"
 
+#include <mutex>
+#include <unordered_map>
 #include <vector>
 
 namespace bqm {
@@ -1018,9 +1020,10 @@ bool chain_plan(int n, int mm, int64_t max_nb, int64_t max_rows, int* kc, int* p
 }
 
 // Launch a chain (descriptors in device memory, or `one` when descs is null), or with
-// `ix` the expert-indexed form of `one`.
+// `ix` the expert-indexed form of `one`.  `coop`: some GEMV waits for the others, so all
+// workgroups must be resident at once (a cooperative launch, which costs 15-20 us more).
 int launch_chain(int fmt, int mm, const GemvDesc* descs, const int64_t* seg, const GemvDesc* one,
-                 int n, int kc, int pacc_rows, uint32_t* sync, hipStream_t s,
+                 int n, int kc, int pacc_rows, uint32_t* sync, bool coop, hipStream_t s,
                  const IdxArgs* ix = nullptr) {
   ChainArgs a;
   a.descs = descs;
@@ -1044,7 +1047,7 @@ int launch_chain(int fmt, int mm, const GemvDesc* descs, const int64_t* seg, con
   allow_lds(k, kP1MaxLds);
   const int grid = cu_count();
   const int threads = 64 << chain_lgw(mm);
-  if (sync) {
+  if (coop) {
     // workgroups wait for each other: they must all be resident at once
     void* args[] = {&a};
     if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k), dim3(grid), dim3(threads), args,
@@ -1066,6 +1069,11 @@ constexpr int64_t kSegBytes = 2 * sizeof(int64_t);
 size_t chain_workspace_bytes(int n) {
   return n < 1 ? 0 : (size_t)(kChainSyncBytes + (int64_t)n * (int64_t)(sizeof(GemvDesc) + kSegBytes));
 }
+
+// Whether a prepared workspace's chain has a waiting GEMV (set by chain_prepare; a
+// workspace this process did not prepare is taken to have one).
+static std::mutex g_waits_mutex;
+static std::unordered_map<const void*, bool> g_chain_waits;
 
 int chain_prepare(const bqm_gemv* descs, int n, void* ws, hipStream_t s) {
   const int fmt = descs[0].fmt, M = descs[0].M;
@@ -1124,6 +1132,10 @@ int chain_prepare(const bqm_gemv* descs, int n, void* ws, hipStream_t s) {
                      (size_t)n * kSegBytes, hipMemcpyHostToDevice, s) != hipSuccess ||
       hipStreamSynchronize(s) != hipSuccess)
     return BQM_E_LAUNCH;
+  bool waits = false;
+  for (int i = 1; i < n; i++) waits = waits || descs[i].wait != 0;
+  std::lock_guard<std::mutex> lock(g_waits_mutex);
+  g_chain_waits[ws] = waits;
   return BQM_OK;
 }
 
@@ -1131,7 +1143,13 @@ int chain_launch(int fmt, int M, void* ws, int n, hipStream_t s) {
   char* wsb = static_cast<char*>(ws);
   const GemvDesc* d = reinterpret_cast<const GemvDesc*>(wsb + kChainSyncBytes);
   const int64_t* seg = reinterpret_cast<const int64_t*>(wsb + kChainSyncBytes + (int64_t)n * sizeof(GemvDesc));
-  return launch_chain(fmt, m_class(M), d, seg, nullptr, n, 0, 0, static_cast<uint32_t*>(ws), s);
+  bool coop = true;
+  {
+    std::lock_guard<std::mutex> lock(g_waits_mutex);
+    auto it = g_chain_waits.find(ws);
+    if (it != g_chain_waits.end()) coop = it->second;
+  }
+  return launch_chain(fmt, m_class(M), d, seg, nullptr, n, 0, 0, static_cast<uint32_t*>(ws), coop, s);
 }
 
 int chain_status(const void* ws, hipStream_t s) {
@@ -1156,7 +1174,7 @@ int launch_qmv(int fmt, const void* w, const float* X, float* Y, int M, int64_t 
   int kc = 0, pacc_rows = 0;
   if (!chain_plan(1, mm, K / kQK, rows, &kc, &pacc_rows)) return BQM_E_SHAPE;
   const GemvDesc d{static_cast<const uint8_t*>(w), X, Y, N, K, fmt, 0, M, 0};
-  return launch_chain(fmt, mm, nullptr, nullptr, &d, 1, kc, pacc_rows, nullptr, s);
+  return launch_chain(fmt, mm, nullptr, nullptr, &d, 1, kc, pacc_rows, nullptr, false, s);
 }
 
 // Expert-indexed GEMV: the chain kernel's indexed form, with E * N rows as one matrix.  The
@@ -1181,7 +1199,7 @@ int launch_qmv_id(int fmt, const void* w, int E, int64_t N, int64_t K, const int
   const uint8_t* codes = static_cast<const uint8_t*>(w);
   const IdxArgs ix{ids, reinterpret_cast<const uint16_t*>(codes + L.scales_off), E, TS, top_k, xts, xss};
   const GemvDesc d{codes, X, Y, N, K, fmt, 0, 1, 0};
-  return launch_chain(fmt, mm, nullptr, nullptr, &d, 1, kc, pacc_rows, nullptr, s, &ix);
+  return launch_chain(fmt, mm, nullptr, nullptr, &d, 1, kc, pacc_rows, nullptr, false, s, &ix);
 }
 
 }  // namespace bqm

@@ -148,10 +148,12 @@ size_t bqm_chain_workspace_bytes(int n);
  * BQM_E_UNSUPPORTED (mixed or unknown formats), BQM_E_LAUNCH. */
 int bqm_chain_prepare(const bqm_gemv* descs, int n, void* workspace, hipStream_t stream);
 
-/* Runs a prepared chain in one (cooperative) launch on `stream`; fmt, M and n must be those
- * it was prepared with (the kernel checks fmt, n and the class of M against the workspace
- * and otherwise computes nothing and records error 2).  The workspace is left ready for
- * the next call; calls sharing one workspace must not overlap in time. */
+/* Runs a prepared chain in one launch on `stream`; fmt, M and n must be those it was
+ * prepared with (the kernel checks fmt, n and the class of M against the workspace and
+ * otherwise computes nothing and records error 2).  A chain with a waiting GEMV runs as a
+ * cooperative launch (all workgroups resident at once); one without (independent GEMVs,
+ * split between the workgroups together) as an ordinary launch.  The workspace is left
+ * ready for the next call; calls sharing one workspace must not overlap in time. */
 int qmv_chain(int fmt, int M, void* workspace, int n, hipStream_t stream);
 
 /* Synchronizes `stream` and returns the chain's error word: 0 = ok, 1 = a device-wide
@@ -168,7 +170,10 @@ int bqm_quantize_q8_act(const float* X, int8_t* Xq, float* dx, int64_t M, int64_
 /* Prefill product with Q8_0 weights (the llama-bench pp512 shape of the page "llama.cpp
  * 0.9.0" analysis (ai-v5 LLMNews), section 2 table):
  *     isum[m][n][b] = sum_{j<32} qw[n][32b+j] * Xq[m][32b+j]        exact int32 (int8 MFMA)
- *     Y[m][n]       = sum_b (d_w[n][b] * dx[m][b]) * isum[m][n][b]    fp32
+ *     Y[m][n]       = sum_b (d_w[n][b] * dx[m][b]) * isum[m][n][b]    fp32, b ascending
+ * The scale product d_w * dx comes from the matrix cores as an fp32 sum of six exact
+ * partial products (d_w and dx split into bf16 parts); it may differ from the correctly
+ * rounded product in the last bits, well within the float tolerance.
  * w_packed: packed Q8_0 N x K matrix.  Xq, dx: from bqm_quantize_q8_act.  Y: fp32 [M][N]. */
 int qmm_q8_0(const void* w_packed, const int8_t* Xq, const float* dx, float* Y, int64_t M,
              int64_t N, int64_t K, hipStream_t stream);

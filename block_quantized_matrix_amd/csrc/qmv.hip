@@ -701,6 +701,7 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
   // chunk.  Every store is followed by its step's loads.
   int gc = u_begin - 1, cc = 0;                      // unit and chunk being consumed
   int ct = 0, cj = 0, creal = 0, cpad = 0;           // tile, step in tile, steps left
+  int creal0 = 1;                                    // steps of this wave in the chunk
   Stage sc;
   sc.nchunks = 0;
   const char* lds_lane = xlds;   // this lane's first block of a tile
@@ -735,6 +736,8 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
       cc = sc.nchunks - 1;  // none of its rows here: skip its chunks
     }
     creal = sc.end - sc.start;
+    creal0 = creal > 0 ? creal : 1;
+    __builtin_amdgcn_s_setprio(3);
     cpad = (creal + P - 1) / P * P;
     ct = sc.start / sc.ns;
     cj = sc.start - ct * sc.ns;
@@ -827,6 +830,17 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
           }
           --creal;
           ++cj;
+          // A SIMD issues from its oldest wave first, so with equal step counts the younger
+          // waves of a workgroup finish microseconds later and the whole workgroup waits
+          // for them.  Each wave's issue priority follows the share of its steps still
+          // left: a wave that falls behind keeps a higher priority than those ahead of it.
+          {
+            const int lvl = (4 * creal) / creal0;
+            if (lvl >= 3) __builtin_amdgcn_s_setprio(3);
+            else if (lvl == 2) __builtin_amdgcn_s_setprio(2);
+            else if (lvl == 1) __builtin_amdgcn_s_setprio(1);
+            else __builtin_amdgcn_s_setprio(0);
+          }
           if (cj == sc.ns || creal == 0) {  // this wave's part of the tile is done
             float v[R][MM];
 #pragma unroll

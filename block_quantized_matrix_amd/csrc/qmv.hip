@@ -964,9 +964,12 @@ using ChainKernel = void (*)(ChainArgs);
 int m_class(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
 
 // Ring depth: a step of a wider batch computes longer, so fewer steps in flight cover the
-// memory latency, and its registers go to the batch's sums.
+// memory latency, and its registers go to the batch's sums.  Batch 1 takes two rows per
+// lane (two blocks per step), where a shallower ring is best (measured: also less padding
+// at the end of each GEMV's share).
 template <int FMT, int MM>
 constexpr int chain_ring() {
+  if (MM == 1) return FMT == FQ4 ? 2 : 1;
   return (FMT == FQ4 ? BQM_P1_P : BQM_P1_P / 2) / (MM >= 4 && FMT == FQ4 ? 2 : 1);
 }
 // log2 of the waves per workgroup: 16 waves, or 8 for the widest batch, whose sums need
@@ -974,8 +977,11 @@ constexpr int chain_ring() {
 // Q8_0 pass: M = 4 is fastest with 16 waves and one row per lane, M = 8 with 8 waves and
 // two rows per lane)
 constexpr int chain_lgw(int mm) { return mm >= BQM_CHAIN_MM_WIDE ? 3 : 4; }
-// rows per lane: for the widest batch one read of the staged inputs serves two rows' codes
-constexpr int chain_r(int mm) { return mm >= BQM_CHAIN_MM_WIDE ? 2 : 1; }
+// rows per lane: one read of the staged inputs serves the codes of two rows, halving the
+// LDS reads per weight byte (batch 1: 8 bytes of x per Q4_0 code byte otherwise; measured
+// +6% on the 27B Q4_0 pass) and, for the widest batch, sharing the input reads of eight
+// sums; batches 2 and 4 keep one row per lane
+constexpr int chain_r(int mm) { return mm >= BQM_CHAIN_MM_WIDE || mm == 1 ? 2 : 1; }
 template <int FMT, bool IDX>
 ChainKernel chain_kernel_f(int mm) {
   switch (mm) {

@@ -964,12 +964,13 @@ using ChainKernel = void (*)(ChainArgs);
 int m_class(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
 
 // Ring depth: a step of a wider batch computes longer, so fewer steps in flight cover the
-// memory latency, and its registers go to the batch's sums.  Batch 1 takes two rows per
-// lane (two blocks per step), where a shallower ring is best (measured: also less padding
-// at the end of each GEMV's share).
+// memory latency, and its registers go to the batch's sums.  Batches 1 and 4 take two
+// rows per lane (two blocks per step), where a shallower ring is best (measured: also less
+// padding at the end of each GEMV's share; batch 4 with two steps would spill).
 template <int FMT, int MM>
 constexpr int chain_ring() {
   if (MM == 1) return FMT == FQ4 ? 2 : 1;
+  if (MM == 4) return 1;
   return (FMT == FQ4 ? BQM_P1_P : BQM_P1_P / 2) / (MM >= 4 && FMT == FQ4 ? 2 : 1);
 }
 // log2 of the waves per workgroup: 16 waves, or 8 for the widest batch, whose sums need
@@ -979,9 +980,9 @@ constexpr int chain_ring() {
 constexpr int chain_lgw(int mm) { return mm >= BQM_CHAIN_MM_WIDE ? 3 : 4; }
 // rows per lane: one read of the staged inputs serves the codes of two rows, halving the
 // LDS reads per weight byte (batch 1: 8 bytes of x per Q4_0 code byte otherwise; measured
-// +6% on the 27B Q4_0 pass) and, for the widest batch, sharing the input reads of eight
-// sums; batches 2 and 4 keep one row per lane
-constexpr int chain_r(int mm) { return mm >= BQM_CHAIN_MM_WIDE || mm == 1 ? 2 : 1; }
+// +6% on the 27B Q4_0 pass, +6% on the 27B Q8_0 pass at M = 4) and, for the widest batch,
+// sharing the input reads of eight sums; batch 2 keeps one row per lane
+constexpr int chain_r(int mm) { return mm == 2 ? 1 : 2; }
 template <int FMT, bool IDX>
 ChainKernel chain_kernel_f(int mm) {
   switch (mm) {

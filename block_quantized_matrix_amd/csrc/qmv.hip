@@ -837,11 +837,11 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
           // left: a wave that falls behind keeps a higher priority than those ahead of it.
           // (Measured: 8% faster on the dependent batch-1 chain; far slower for wider
           // batches and the indexed form, which keep the default.)
-          if constexpr (kPrioFeedback) {
-            const int lvl = (4 * creal) / creal0;
-            if (lvl >= 3) __builtin_amdgcn_s_setprio(3);
-            else if (lvl == 2) __builtin_amdgcn_s_setprio(2);
-            else if (lvl == 1) __builtin_amdgcn_s_setprio(1);
+          if constexpr (kPrioFeedback) {  // quarter of the steps left: 3 .. 0 (no division)
+            const int c4 = 4 * creal;
+            if (c4 >= 3 * creal0) __builtin_amdgcn_s_setprio(3);
+            else if (c4 >= 2 * creal0) __builtin_amdgcn_s_setprio(2);
+            else if (c4 >= creal0) __builtin_amdgcn_s_setprio(1);
             else __builtin_amdgcn_s_setprio(0);
           }
           if (cj == sc.ns || creal == 0) {  // this wave's part of the tile is done

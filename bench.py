@@ -337,6 +337,24 @@ def run_moe(args, torch, gen, bqm):
             lbytes += [uniq * mat + 4 * (T * top_k * F + T * top_k * H)]   # down
         dur = per_launch_ms(launches, torch)
         achieved = sum(lbytes) / (dur.sum() * 1e-3) / 1e9
+
+        # the same layer with gate and up fused (one pass over both, silu(gate) * up out):
+        # two launches per layer
+        def run_fused():
+            for gate, up, down, ids, x, xd, yg, yu, yd, _ in layers:
+                bqm.qmv_id_gate_up("q4_0", gate, up, E, F, H, ids, T, top_k, x, H, 0, yg)
+                bqm.qmv_id("q4_0", down, E, H, F, ids, T, top_k, xd, top_k * F, F, yd)
+
+        ms_f = time_steps(run_fused, args.steps, args.warmup, torch, not args.no_graph)
+        abytes_f = n_layers * 4 * (T * H + T * top_k * F + T * top_k * F + T * top_k * H)
+        gbs_f = (ubytes + abytes_f) / (ms_f * 1e-3) / 1e9
+        flaunch, fbytes = [], []
+        for gate, up, down, ids, x, xd, yg, yu, yd, uniq in layers:
+            flaunch.append(lambda g=gate, u=up, i=ids, x=x, y=yg:
+                           bqm.qmv_id_gate_up("q4_0", g, u, E, F, H, i, T, top_k, x, H, 0, y))
+            fbytes.append(2 * uniq * weight_bytes("q4_0", F, H) + 4 * (T * H + T * top_k * F))
+        fdur = per_launch_ms(flaunch, torch)
+        f_achieved = sum(fbytes) / (fdur.sum() * 1e-3) / 1e9
         out.append({"T": T, "ms_per_layer": round(ms / n_layers, 4),
                     "unique_experts_per_layer": [L[-1] for L in layers],
                     "gbs_unique_bytes": round(gbs, 1), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
@@ -345,7 +363,16 @@ def run_moe(args, torch, gen, bqm):
                                  "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                                  "traffic": traffic_from_profiles(f"qmv_id_q4_0_moe_t{T}"),
                                  "kernel": f"k_qmv_chain indexed form (Q4_0, batch class {1 if T == 1 else 8})",
-                                 "avg_launch_us": round(1e3 * float(dur.mean()), 3)}})
+                                 "avg_launch_us": round(1e3 * float(dur.mean()), 3)},
+                    "fused_gate_up": {
+                        "ms_per_layer": round(ms_f / n_layers, 4), "gbs_unique_bytes": round(gbs_f, 1),
+                        "pct_of_hbm_peak": round(100 * gbs_f / HBM_PEAK_GBS, 2),
+                        "layer_tok_s": round(T * n_layers / (ms_f * 1e-3), 1),
+                        "roofline": {"bound": "hbm", "achieved": round(f_achieved, 1), "peak": HBM_PEAK_GBS,
+                                     "unit": "GB/s", "frac": round(f_achieved / HBM_PEAK_GBS, 4),
+                                     "traffic": traffic_from_profiles(f"qmv_id_gate_up_q4_0_moe_t{T}"),
+                                     "kernel": "k_qmv_chain gate+up form (qmv_id_gate_up)",
+                                     "avg_launch_us": round(1e3 * float(fdur.mean()), 3)}}})
         del layers
         torch.cuda.empty_cache()
     return {"metric": "MoE qmv_id achieved HBM GB/s over unique-expert bytes", "value": out[0]["gbs_unique_bytes"],

@@ -48,6 +48,7 @@ def lib():
         L.qmv_q4_0.argtypes = [P, P, P, I, I64, I64, P]
         L.qmv_q8_0.argtypes = [P, P, P, I, I64, I64, P]
         L.qmv_id.argtypes = [I, P, I, I64, I64, P, I, I, P, I64, I64, P, P]
+        L.qmv_id_gate_up.argtypes = [I, P, P, I, I64, I64, P, I, I, P, I64, I64, P, P]
         L.bqm_quantize_q8_act.argtypes = [P, P, P, I64, I64, P]
         L.qmm_q8_0.argtypes = [P, P, P, P, I64, I64, I64, P]
         L.bqm_chain_workspace_bytes.argtypes = [I]
@@ -118,6 +119,12 @@ def qmv_id(fmt, w_packed, E: int, N: int, K: int, ids, T: int, top_k: int, X,
            x_tok_stride: int, x_slot_stride: int, Y, stream=None):
     _call("qmv_id", _fmt(fmt), _ptr(w_packed), E, N, K, _ptr(ids), T, top_k, _ptr(X),
           x_tok_stride, x_slot_stride, _ptr(Y), _stream(stream))
+
+
+def qmv_id_gate_up(fmt, w_gate, w_up, E: int, N: int, K: int, ids, T: int, top_k: int, X,
+                   x_tok_stride: int, x_slot_stride: int, Y, stream=None):
+    _call("qmv_id_gate_up", _fmt(fmt), _ptr(w_gate), _ptr(w_up), E, N, K, _ptr(ids), T, top_k,
+          _ptr(X), x_tok_stride, x_slot_stride, _ptr(Y), _stream(stream))
 
 
 def bqm_quantize_q8_act(X, Xq, dx, M: int, K: int, stream=None):

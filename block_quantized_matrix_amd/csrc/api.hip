@@ -27,6 +27,34 @@ int check_ptr(const void* w) {
   return BQM_OK;
 }
 
+
+// Argument checks shared by qmv_id and qmv_id_gate_up (w2: the up tensor, or null).
+int check_id(int fmt, const void* w, const void* w2, bool pair, int E, int64_t N, int64_t K,
+             const int32_t* ids, int T, int top_k, const float* X, int64_t x_tok_stride,
+             int64_t x_slot_stride, float* Y, bool* nothing) {
+  *nothing = false;
+  if (E < 0 || T < 0 || top_k < 0 || T > BQM_QMV_ID_MAX_T || top_k > BQM_QMV_ID_MAX_TOPK ||
+      E > BQM_QMV_ID_MAX_E)
+    return BQM_E_SHAPE;
+  if (N < 0 || (int64_t)E * N > kMaxRows) return BQM_E_SHAPE;
+  if (int st = check_shape(fmt, (int64_t)E * N, K)) return st;
+  if (x_tok_stride < 0 || x_slot_stride < 0) return BQM_E_SHAPE;
+  if (T == 0 || top_k == 0 || N == 0) {
+    *nothing = true;
+    return BQM_OK;
+  }
+  if (!Y || !ids) return BQM_E_NULL;
+  if (!aligned16(Y) || !aligned16(ids)) return BQM_E_ALIGN;
+  if (K > 0 && E > 0) {
+    if (int st = check_ptr(w)) return st;
+    if (pair)
+      if (int st = check_ptr(w2)) return st;
+    if (int st = check_ptr(X)) return st;
+    // every (t, s) input row must start 16-byte aligned
+    if ((x_tok_stride & 3) != 0 || (x_slot_stride & 3) != 0) return BQM_E_ALIGN;
+  }
+  return BQM_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -84,23 +112,25 @@ int qmv_q8_0(const void* w_packed, const float* X, float* Y, int M, int64_t N, i
 int qmv_id(int fmt, const void* w_packed, int E, int64_t N, int64_t K, const int32_t* ids, int T,
            int top_k, const float* X, int64_t x_tok_stride, int64_t x_slot_stride, float* Y,
            hipStream_t stream) {
-  if (E < 0 || T < 0 || top_k < 0 || T > BQM_QMV_ID_MAX_T || top_k > BQM_QMV_ID_MAX_TOPK ||
-      E > BQM_QMV_ID_MAX_E)
-    return BQM_E_SHAPE;
-  if (N < 0 || (int64_t)E * N > kMaxRows) return BQM_E_SHAPE;
-  if (int st = check_shape(fmt, (int64_t)E * N, K)) return st;
-  if (x_tok_stride < 0 || x_slot_stride < 0) return BQM_E_SHAPE;
-  if (T == 0 || top_k == 0 || N == 0) return BQM_OK;
-  if (!Y || !ids) return BQM_E_NULL;
-  if (!aligned16(Y) || !aligned16(ids)) return BQM_E_ALIGN;
-  if (K > 0 && E > 0) {
-    if (int st = check_ptr(w_packed)) return st;
-    if (int st = check_ptr(X)) return st;
-    // every (t, s) input row must start 16-byte aligned
-    if ((x_tok_stride & 3) != 0 || (x_slot_stride & 3) != 0) return BQM_E_ALIGN;
-  }
+  bool nothing = false;
+  if (int st = check_id(fmt, w_packed, nullptr, false, E, N, K, ids, T, top_k, X, x_tok_stride,
+                        x_slot_stride, Y, &nothing))
+    return st;
+  if (nothing) return BQM_OK;
   return launch_qmv_id(fmt, w_packed, E, N, K, ids, T, top_k, X, x_tok_stride, x_slot_stride, Y,
                        stream);
+}
+
+int qmv_id_gate_up(int fmt, const void* w_gate, const void* w_up, int E, int64_t N, int64_t K,
+                   const int32_t* ids, int T, int top_k, const float* X, int64_t x_tok_stride,
+                   int64_t x_slot_stride, float* Y, hipStream_t stream) {
+  bool nothing = false;
+  if (int st = check_id(fmt, w_gate, w_up, true, E, N, K, ids, T, top_k, X, x_tok_stride,
+                        x_slot_stride, Y, &nothing))
+    return st;
+  if (nothing) return BQM_OK;
+  return launch_qmv_id_gate_up(fmt, w_gate, w_up, E, N, K, ids, T, top_k, X, x_tok_stride,
+                               x_slot_stride, Y, stream);
 }
 
 int bqm_quantize_q8_act(const float* X, int8_t* Xq, float* dx, int64_t M, int64_t K,

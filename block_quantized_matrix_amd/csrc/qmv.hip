@@ -172,6 +172,8 @@ static_assert(sizeof(GemvDesc) == sizeof(bqm_gemv), "bqm_gemv layout");
 struct IdxArgs {
   const int32_t* ids;      // [T][top_k]
   const uint16_t* scales;  // the scales of all E * N rows
+  const uint8_t* up;       // gate+up form: the up tensor's codes (E * N rows) ...
+  const uint16_t* up_scales;  // ... and scales; the gate tensor is `one.w`
   int E, TS, top_k;        // experts; slots T * top_k; slots per token
   int64_t xts, xss;        // input strides (floats) per token and per slot
 };
@@ -244,6 +246,8 @@ __device__ __forceinline__ StageRow make_stage(const GemvDesc& d, int64_t sbase,
 struct Stage {
   const uint8_t* codes;
   const uint16_t* scales;
+  const uint8_t* codes2;    // gate+up form: the up rows (the gate rows are `codes`)
+  const uint16_t* scales2;
   const float* x;
   float* y;
   int nrows, nb, nbc, kb0, lg2G, G, gpw, ns, S, start, end, M, xstride, ystride, nchunks, lo;
@@ -258,7 +262,7 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t v) {
 }
 
 // The chunk-dependent values of a stage whose GEMV-level values are set.
-template <int LGW, int R>  // log2 of the waves of the workgroup; rows per lane
+template <int LGW, int R, int RT = R>  // log2 of the waves; rows per lane; distinct rows per lane
 __device__ __forceinline__ void stage_chunk(int c, int kc, int wave, int wait, Stage& s) {
   s.kb0 = c * kc;
   s.nbc = min(kc, s.nb - s.kb0);
@@ -275,9 +279,9 @@ __device__ __forceinline__ void stage_chunk(int c, int kc, int wave, int wait, S
   s.gpw = 64 >> lg2;
   s.ragged = (s.nbc & (s.G - 1)) != 0;
   s.ns = (s.nbc + s.G - 1) >> lg2;
-  // tiles of R * gpw rows, ns steps each, in row order; the waves take equal contiguous
+  // tiles of RT * gpw rows, ns steps each, in row order; the waves take equal contiguous
   // ranges of the tile-major step sequence (a tile may be split between waves)
-  const int ntiles = (s.nrows + R * s.gpw - 1) / (R * s.gpw);
+  const int ntiles = (s.nrows + RT * s.gpw - 1) / (RT * s.gpw);
   s.S = ntiles * s.ns;
   s.start = (wave * s.S) >> LGW;
   s.end = ((wave + 1) * s.S) >> LGW;
@@ -304,7 +308,7 @@ __device__ __forceinline__ void load_stage(const StageRow* t, int i, int c, int 
 // expert, first slot in the sorted list, slots).  The units' rows, N each, one unit after
 // another, are split evenly between the workgroups; this one holds flattened rows
 // [flo, fhi).  `base`: expert 0's row 0 (codes, scales), x and y bases, nb, nchunks.
-template <int LGW, int R, int CB>
+template <int LGW, int R, int CB, bool GU>
 __device__ __forceinline__ void load_unit(const int* groups, const Stage& base, int i, int c, int kc,
                                           int wave, int N, int64_t flo, int64_t fhi, Stage& s) {
   const int e = __builtin_amdgcn_readfirstlane(groups[3 * i]);
@@ -315,11 +319,15 @@ __device__ __forceinline__ void load_unit(const int* groups, const Stage& base, 
   s = base;
   s.codes = base.codes + row * base.nb * CB;
   s.scales = base.scales + row * base.nb;
+  if constexpr (GU) {
+    s.codes2 = base.codes2 + row * base.nb * CB;
+    s.scales2 = base.scales2 + row * base.nb;
+  }
   s.y = base.y + r0;
   s.nrows = r1 - r0;
   s.lo = __builtin_amdgcn_readfirstlane(groups[3 * i + 1]);
   s.M = __builtin_amdgcn_readfirstlane(groups[3 * i + 2]);
-  stage_chunk<LGW, R>(c, kc, wave, 0, s);
+  stage_chunk<LGW, R, GU ? 1 : R>(c, kc, wave, 0, s);
 }
 
 // Device-wide barrier between the GEMVs of a chain.  Workspace words: [0] release epoch,
@@ -399,8 +407,13 @@ __host__ __device__ inline ChainLds chain_lds(int n, int mm, int r, int pacc_row
   return L;
 }
 
-template <int FMT, int P, int MM, int LGW, int R, bool IDX>
+// MODE 0: chains of GEMVs; 1: the expert-indexed form; 2: the expert-indexed gate+up form
+// (a lane's two rows are gate row n and up row n of one expert; outputs silu(g) * u).
+template <int FMT, int P, int MM, int LGW, int R, int MODE>
 __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
+  constexpr bool IDX = MODE != 0, GU = MODE == 2;
+  static_assert(!GU || R == 2, "gate+up pairs take the two rows of a lane");
+  constexpr int RT = GU ? 1 : R;  // distinct output rows per lane
   constexpr int NW = 1 << LGW, NT = 64 << LGW;  // waves, threads
   extern __shared__ float4 smem[];
   constexpr int CB = FMT == FQ4 ? 16 : 32;     // code bytes per block
@@ -529,6 +542,8 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
     const int N = (int)a.one.N, nb = (int)(a.one.K >> 5);
     ibase.codes = a.one.w;
     ibase.scales = a.ix.scales;
+    ibase.codes2 = a.ix.up;
+    ibase.scales2 = a.ix.up_scales;
     ibase.x = a.one.x;
     ibase.y = a.one.y;
     ibase.nrows = 0;
@@ -579,7 +594,7 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
     if (n_units == 0) return;
   }
   auto load = [&](int i, int c, Stage& st) {
-    if constexpr (IDX) load_unit<LGW, R, CB>(groups, ibase, i, c, kc, wave, (int)a.one.N, flo, fhi, st);
+    if constexpr (IDX) load_unit<LGW, R, CB, GU>(groups, ibase, i, c, kc, wave, (int)a.one.N, flo, fhi, st);
     else load_stage<LGW, R>(table, i, c, kc, wave, st);
   };
   // input and output row of batch entry m of the current unit: m itself, or (indexed form)
@@ -602,6 +617,7 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
   int ireal = 0, ipad = 0;   // real steps left; steps left with padding
   __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(nullptr, (short)0, 0, 0x00020000);
   __amdgpu_buffer_rsrc_t rs = rc;
+  __amdgpu_buffer_rsrc_t rc2 = rc, rs2 = rc;  // gate+up form: the up rows
   // lane offsets of its rows (ilg, and ilg + gpw when R = 2, in the tile) in the current
   // tile, and at the tile's last step (past K in a ragged row: zeros).  Named scalars, not
   // arrays: an array shared by the lambdas may be kept in scratch memory.
@@ -610,13 +626,18 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
   int ig = 0, ilg = 0;
   auto tile_offsets = [&]() {
     const bool past_k = ((si.ns - 1) << si.lg2G) + ig >= si.nbc;
-    const int row = it * R * si.gpw + ilg;
+    const int row = it * RT * si.gpw + ilg;
     const bool ok0 = row < si.nrows;  // rows past the range read zeros
     vc0 = ok0 ? ((uint32_t)ilg * si.nb + ig) * CB : kOob;
     vs0 = ok0 ? ((uint32_t)ilg * si.nb + ig) * 2 : kOob;
     vcl0 = past_k ? kOob : vc0;
     vsl0 = past_k ? kOob : vs0;
-    if constexpr (R == 2) {
+    if constexpr (GU) {  // the up row: same row, other tensor
+      vc1 = vc0;
+      vs1 = vs0;
+      vcl1 = vcl0;
+      vsl1 = vsl0;
+    } else if constexpr (R == 2) {
       const bool ok1 = row + si.gpw < si.nrows;
       vc1 = ok1 ? ((uint32_t)(si.gpw + ilg) * si.nb + ig) * CB : kOob;
       vs1 = ok1 ? ((uint32_t)(si.gpw + ilg) * si.nb + ig) * 2 : kOob;
@@ -646,6 +667,12 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
       // +2: a scale is read as 4 bytes (the packed layout leaves slack after the scales)
       rs = __builtin_amdgcn_make_buffer_rsrc((void*)si.scales, (short)0,
                                              (int)((uint32_t)si.nrows * si.nb * 2 + 2), 0x00020000);
+      if constexpr (GU) {
+        rc2 = __builtin_amdgcn_make_buffer_rsrc((void*)si.codes2, (short)0,
+                                                (int)((uint32_t)si.nrows * si.nb * CB), 0x00020000);
+        rs2 = __builtin_amdgcn_make_buffer_rsrc((void*)si.scales2, (short)0,
+                                                (int)((uint32_t)si.nrows * si.nb * 2 + 2), 0x00020000);
+      }
       ig = lane & (si.G - 1);
       ilg = lane >> si.lg2G;
       it = si.start / si.ns;
@@ -660,21 +687,23 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
     // the loads duplicated): one load sequence for real and padding steps.  Once the range
     // is done the lane offsets are past the descriptor: zeros, no memory traffic.
     const uint32_t live = ireal > 0 ? 1u : 0u;
-    const uint32_t so = ((uint32_t)(it * R * si.gpw) * si.nb + (uint32_t)si.kb0 + (uint32_t)(ij << si.lg2G)) * live;
+    const uint32_t so = ((uint32_t)(it * RT * si.gpw) * si.nb + (uint32_t)si.kb0 + (uint32_t)(ij << si.lg2G)) * live;
     const uint32_t lm = 0u - (uint32_t)(ij == si.ns - 1);  // all ones at a tile's last step
 #pragma unroll
     for (int r = 0; r < R; r++) {
       const uint32_t c = r == 0 ? (vcl0 & lm) | (vc0 & ~lm) : (vcl1 & lm) | (vc1 & ~lm);
       const uint32_t e = r == 0 ? (vsl0 & lm) | (vs0 & ~lm) : (vsl1 & lm) | (vs1 & ~lm);
+      const __amdgpu_buffer_rsrc_t rcr = GU && r == 1 ? rc2 : rc;
+      const __amdgpu_buffer_rsrc_t rsr = GU && r == 1 ? rs2 : rs;
       if constexpr (FMT == FQ4) {
-        q[r].a = __builtin_amdgcn_raw_buffer_load_b128(rc, c, so * CB, 0);
+        q[r].a = __builtin_amdgcn_raw_buffer_load_b128(rcr, c, so * CB, 0);
       } else {
-        q[r].a = __builtin_amdgcn_raw_buffer_load_b128(rc, c, so * CB, 0);
-        q[r].b = __builtin_amdgcn_raw_buffer_load_b128(rc, c + 16, so * CB, 0);
+        q[r].a = __builtin_amdgcn_raw_buffer_load_b128(rcr, c, so * CB, 0);
+        q[r].b = __builtin_amdgcn_raw_buffer_load_b128(rcr, c + 16, so * CB, 0);
       }
       // the scale and the next 2 bytes (ignored): a whole-register load, which the compiler
       // neither widens nor merges, so the ring is waited on per slot
-      d[r] = __builtin_amdgcn_raw_buffer_load_b32(rs, e, so * 2, 0);
+      d[r] = __builtin_amdgcn_raw_buffer_load_b32(rsr, e, so * 2, 0);
     }
     if (ireal > 0) {
       if (--ireal == 0) {  // padding steps follow: read nothing
@@ -892,11 +921,12 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
             }
 #pragma unroll
             for (int r = 0; r < R; r++) {
-              const int row = ct * R * sc.gpw + r * sc.gpw + clg;
+              // the output row (gate+up form: both of the lane's rows are row n)
+              const int row = GU ? ct * sc.gpw + clg : ct * R * sc.gpw + r * sc.gpw + clg;
               if (put && cg == 0 && row < sc.nrows) {
                 bool store = true;
                 if (sc.nchunks > 1) {  // chunk sums, added in chunk order
-                  float* pa = pacc + row * MM;
+                  float* pa = pacc + (GU ? 2 * row + r : row) * MM;
 #pragma unroll
                   for (int m = 0; m < MM; m++) {
                     if (!sc.first) v[r][m] = pa[m] + v[r][m];
@@ -904,13 +934,19 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
                   }
                   store = sc.last;
                 }
-                if (store) {
+                if (store && (!GU || r == 1)) {
 #pragma unroll
                   for (int m = 0; m < MM; m++)
-                    if (m < sc.M)  // agent-coherent: a later GEMV may read it
+                    if (m < sc.M) {  // agent-coherent: a later GEMV may read it
+                      float out = v[r][m];
+                      if constexpr (GU) {  // silu(g) * u, g the gate row's sum
+                        const float g = v[0][m];
+                        out = g / (1.0f + expf(-g)) * v[1][m];
+                      }
                       __hip_atomic_store((__attribute__((address_space(1))) float*)sc.y +
                                              (int64_t)slot_of(sc, m) * sc.ystride + row,
-                                         v[r][m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                                         out, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
                 }
               }
             }
@@ -983,18 +1019,24 @@ constexpr int chain_lgw(int mm) { return mm >= BQM_CHAIN_MM_WIDE ? 3 : 4; }
 // +6% on the 27B Q4_0 pass, +6% on the 27B Q8_0 pass at M = 4) and, for the widest batch,
 // sharing the input reads of eight sums; batch 2 keeps one row per lane
 constexpr int chain_r(int mm) { return mm == 2 ? 1 : 2; }
-template <int FMT, bool IDX>
+// rows per lane of a mode: the gate+up form always pairs two rows
+constexpr int mode_r(int mm, int mode) { return mode == 2 ? 2 : chain_r(mm); }
+template <int FMT, int MODE>
 ChainKernel chain_kernel_f(int mm) {
   switch (mm) {
-    case 1: return k_qmv_chain<FMT, chain_ring<FMT, 1>(), 1, chain_lgw(1), chain_r(1), IDX>;
-    case 2: return k_qmv_chain<FMT, chain_ring<FMT, 2>(), 2, chain_lgw(2), chain_r(2), IDX>;
-    case 4: return k_qmv_chain<FMT, chain_ring<FMT, 4>(), 4, chain_lgw(4), chain_r(4), IDX>;
-    default: return k_qmv_chain<FMT, chain_ring<FMT, 8>(), 8, chain_lgw(8), chain_r(8), IDX>;
+    case 1: return k_qmv_chain<FMT, chain_ring<FMT, 1>(), 1, chain_lgw(1), mode_r(1, MODE), MODE>;
+    // two rows per lane: the ring of batch 1 (that of batch 2 would spill)
+    case 2: return k_qmv_chain<FMT, chain_ring<FMT, MODE == 2 ? 1 : 2>(), 2, chain_lgw(2), mode_r(2, MODE), MODE>;
+    case 4: return k_qmv_chain<FMT, chain_ring<FMT, 4>(), 4, chain_lgw(4), mode_r(4, MODE), MODE>;
+    default: return k_qmv_chain<FMT, chain_ring<FMT, 8>(), 8, chain_lgw(8), mode_r(8, MODE), MODE>;
   }
 }
-ChainKernel chain_kernel(int fmt, int mm, bool idx) {
-  if (idx) return fmt == BQM_Q4_0 ? chain_kernel_f<FQ4, true>(mm) : chain_kernel_f<FQ8, true>(mm);
-  return fmt == BQM_Q4_0 ? chain_kernel_f<FQ4, false>(mm) : chain_kernel_f<FQ8, false>(mm);
+template <int MODE>
+ChainKernel chain_kernel_m(int fmt, int mm) {
+  return fmt == BQM_Q4_0 ? chain_kernel_f<FQ4, MODE>(mm) : chain_kernel_f<FQ8, MODE>(mm);
+}
+ChainKernel chain_kernel(int fmt, int mm, int mode) {
+  return mode == 2 ? chain_kernel_m<2>(fmt, mm) : mode == 1 ? chain_kernel_m<1>(fmt, mm) : chain_kernel_m<0>(fmt, mm);
 }
 
 int cu_count() {
@@ -1057,11 +1099,12 @@ int launch_chain(int fmt, int mm, const GemvDesc* descs, const int64_t* seg, con
   a.kc = kc;
   a.pacc_rows = pacc_rows;
   a.sync = sync;
-  if (ix) a.ix = *ix; else a.ix = IdxArgs{nullptr, nullptr, 0, 0, 0, 0, 0};
-  ChainKernel k = chain_kernel(fmt, mm, ix != nullptr);
+  if (ix) a.ix = *ix; else a.ix = IdxArgs{nullptr, nullptr, nullptr, nullptr, 0, 0, 0, 0, 0};
+  const int mode = ix ? (ix->up ? 2 : 1) : 0;
+  ChainKernel k = chain_kernel(fmt, mm, mode);
   // per kernel: 1 = its static LDS fits the reserve, -1 = it does not
-  static int static_ok[2][2][4] = {};
-  int& ok = static_ok[ix ? 1 : 0][fmt == BQM_Q4_0 ? 0 : 1][mm == 1 ? 0 : mm == 2 ? 1 : mm == 4 ? 2 : 3];
+  static int static_ok[3][2][4] = {};
+  int& ok = static_ok[mode][fmt == BQM_Q4_0 ? 0 : 1][mm == 1 ? 0 : mm == 2 ? 1 : mm == 4 ? 2 : 3];
   if (ok == 0) {
     hipFuncAttributes fa;
     ok = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(k)) == hipSuccess &&
@@ -1204,9 +1247,11 @@ int launch_qmv(int fmt, const void* w, const float* X, float* Y, int M, int64_t 
 // Expert-indexed GEMV: the chain kernel's indexed form, with E * N rows as one matrix.  The
 // batch class is that of min(T, 8): one token usually adds at most one slot to an expert,
 // so up to 8 tokens stream each selected expert once; an expert with more slots is
-// streamed once per group of 8.
-int launch_qmv_id(int fmt, const void* w, int E, int64_t N, int64_t K, const int32_t* ids, int T,
-                  int top_k, const float* X, int64_t xts, int64_t xss, float* Y, hipStream_t s) {
+// streamed once per group of 8.  With `w_up`, the gate+up form: each lane takes gate row n
+// and up row n of the expert, and the output is silu(gate) * up.
+static int launch_id(int fmt, const void* w, const void* w_up, int E, int64_t N, int64_t K,
+              const int32_t* ids, int T, int top_k, const float* X, int64_t xts, int64_t xss,
+              float* Y, hipStream_t s) {
   const int TS = T * top_k;
   Layout L;
   layout_of(fmt, (int64_t)E * N, K, &L);
@@ -1218,12 +1263,28 @@ int launch_qmv_id(int fmt, const void* w, int E, int64_t N, int64_t K, const int
   rows = rows < N ? rows : N;
   if ((rows + 1) * L.nb * CB >= ((int64_t)1 << 31)) return BQM_E_SHAPE;
   int kc = 0, pacc_rows = 0;
-  if (!chain_plan(idx_table_rows(E, TS), mm, L.nb, rows, &kc, &pacc_rows)) return BQM_E_SHAPE;
+  // the gate+up form keeps two partial sums per output row
+  if (!chain_plan(idx_table_rows(E, TS), mm, L.nb, w_up ? 2 * rows : rows, &kc, &pacc_rows))
+    return BQM_E_SHAPE;
   if (kc < 1) kc = 1;  // K = 0: nothing is staged, but chunk counts divide by kc
   const uint8_t* codes = static_cast<const uint8_t*>(w);
-  const IdxArgs ix{ids, reinterpret_cast<const uint16_t*>(codes + L.scales_off), E, TS, top_k, xts, xss};
+  const uint8_t* up = static_cast<const uint8_t*>(w_up);
+  const IdxArgs ix{ids, reinterpret_cast<const uint16_t*>(codes + L.scales_off), up,
+                   up ? reinterpret_cast<const uint16_t*>(up + L.scales_off) : nullptr,
+                   E, TS, top_k, xts, xss};
   const GemvDesc d{codes, X, Y, N, K, fmt, 0, 1, 0};
   return launch_chain(fmt, mm, nullptr, nullptr, &d, 1, kc, pacc_rows, nullptr, false, s, &ix);
+}
+
+int launch_qmv_id(int fmt, const void* w, int E, int64_t N, int64_t K, const int32_t* ids, int T,
+                  int top_k, const float* X, int64_t xts, int64_t xss, float* Y, hipStream_t s) {
+  return launch_id(fmt, w, nullptr, E, N, K, ids, T, top_k, X, xts, xss, Y, s);
+}
+
+int launch_qmv_id_gate_up(int fmt, const void* w_gate, const void* w_up, int E, int64_t N, int64_t K,
+                          const int32_t* ids, int T, int top_k, const float* X, int64_t xts,
+                          int64_t xss, float* Y, hipStream_t s) {
+  return launch_id(fmt, w_gate, w_up, E, N, K, ids, T, top_k, X, xts, xss, Y, s);
 }
 
 }  // namespace bqm

@@ -112,6 +112,20 @@ int qmv_id(int fmt, const void* w_packed, int E, int64_t N, int64_t K, const int
            int top_k, const float* X, int64_t x_tok_stride, int64_t x_slot_stride, float* Y,
            hipStream_t stream);
 
+/* Fused expert gate+up, the fused MoE path (`-fmoe`, `fused_moe 1`) of the page
+ * "ik_llama.cpp 老工作站多 GPU 部署 Qwen3-235B-A22B 实战指南" (nxmr.cn), recommended-command
+ * section.  The page names the path without defining it; read as the SwiGLU feed-forward
+ * of the models it runs:
+ *     g = W_gate[e] x_ts,  u = W_up[e] x_ts,  Y[t][s][n] = silu(g[n]) * u[n],
+ *     silu(z) = z / (1 + exp(-z))
+ * One pass: each selected expert's gate and up rows are streamed once for all its slots
+ * (in groups of up to 8), both sums share every input read.  w_gate and w_up: two expert
+ * tensors of the same format and shape, each packed as one matrix of E*N rows.  Everything
+ * else (ids, strides, padding and out-of-range ids, limits, errors) as qmv_id. */
+int qmv_id_gate_up(int fmt, const void* w_gate, const void* w_up, int E, int64_t N, int64_t K,
+                   const int32_t* ids, int T, int top_k, const float* X, int64_t x_tok_stride,
+                   int64_t x_slot_stride, float* Y, hipStream_t stream);
+
 /* ---- chains of GEMVs in one launch ----------------------------------------------------
  * Decode runs one GEMV after another, each reading the previous one's output (through
  * the layers' other operations); launching them one by one pays a kernel start and drain

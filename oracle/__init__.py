@@ -53,12 +53,15 @@ def _load():
         lib.oracle_decode_row.argtypes = [I32, P, I64, P]
         lib.oracle_qmv.argtypes = [I32, P, P, I64, I64, I64, P, P]
         lib.oracle_qmv_id.argtypes = [I32, P, I64, I64, I64, P, I64, I64, P, I64, I64, P, P]
+        lib.oracle_qmv_id_gate_up.argtypes = [I32, P, P, I64, I64, I64, P, I64, I64, P, I64, I64, P, P]
+        lib.oracle_silu.argtypes = [ctypes.c_double]
+        lib.oracle_silu.restype = ctypes.c_double
         lib.oracle_quantize_q8_act.argtypes = [P, I64, I64, P, P]
         lib.oracle_qmm_q8_0.argtypes = [P, P, P, I64, I64, I64, P, P, P]
         lib.oracle_threads.restype = I32
         lib.oracle_set_threads.argtypes = [I32]
-        for f in ("oracle_decode_row", "oracle_qmv", "oracle_qmv_id", "oracle_quantize_q8_act",
-                  "oracle_qmm_q8_0"):
+        for f in ("oracle_decode_row", "oracle_qmv", "oracle_qmv_id", "oracle_qmv_id_gate_up",
+                  "oracle_quantize_q8_act", "oracle_qmm_q8_0"):
             getattr(lib, f).restype = I32
         _lib = lib
     return _lib
@@ -119,6 +122,27 @@ def qmv_id(fmt: str, W, E: int, N: int, K: int, ids, X, x_tok_stride: int, x_slo
     S = np.empty((T, top_k, N), np.float64)
     _check(_load().oracle_qmv_id(FMT[fmt], _p(Wb), E, N, K, _p(ids32), T, top_k, _p(Xf),
                                  x_tok_stride, x_slot_stride, _p(Y), _p(S)), "qmv_id")
+    return Y, S
+
+
+def silu(z):
+    """silu(z) = z / (1 + e^-z) in double precision (the oracle's own, from C)."""
+    return _load().oracle_silu(float(z))
+
+
+def qmv_id_gate_up(fmt: str, Wg, Wu, E: int, N: int, K: int, ids, X, x_tok_stride: int,
+                   x_slot_stride: int):
+    """Y, S [T][top_k][N] of the fused gate+up product silu(Wg x) * (Wu x) (padding -> 0)."""
+    Wgb, Wub = _c(Wg, np.uint8), _c(Wu, np.uint8)
+    ids32 = _c(ids, np.int32)
+    T, top_k = ids32.shape
+    Xf = _c(X, np.float32).reshape(-1)
+    assert Wgb.size == Wub.size == E * N * (K // 32) * BLOCK_BYTES[fmt]
+    Y = np.empty((T, top_k, N), np.float64)
+    S = np.empty((T, top_k, N), np.float64)
+    _check(_load().oracle_qmv_id_gate_up(FMT[fmt], _p(Wgb), _p(Wub), E, N, K, _p(ids32), T, top_k,
+                                         _p(Xf), x_tok_stride, x_slot_stride, _p(Y), _p(S)),
+           "qmv_id_gate_up")
     return Y, S
 
 

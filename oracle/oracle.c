@@ -159,6 +159,60 @@ int oracle_qmv_id(int fmt, const uint8_t* W, int64_t E, int64_t N, int64_t K,
   return err;
 }
 
+/* silu(z) = z / (1 + e^-z), in double precision. */
+double oracle_silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* Fused expert gate+up (the fused MoE path of the ik_llama.cpp MoE page, recommended-
+ * command section, read as the SwiGLU feed-forward): per slot (t, s) with expert
+ * e = ids[t][s] >= 0 and row n,
+ *     g = sum_k Wg[e][n][k] x[k],  u = sum_k Wu[e][n][k] x[k],  Y = silu(g) * u,
+ * each sum in double over the exactly dequantized weights in index order.  A padding slot
+ * gives 0.  S is the tolerance scale for |y - Y| <= 1e-3 S: with |dg| <= 1e-3 Sg and
+ * |du| <= 1e-3 Su (the bar of each sum, Sg = sum |wg x|, Su = sum |wu x|) and |silu'| <= 1.1,
+ *     |silu(g + dg)(u + du) - silu(g) u| <= 1.1 |dg| (|u| + |du|) + |silu(g)| |du|,
+ * so S = 1.1 Sg (|u| + 1e-3 Su) + |silu(g)| Su, plus 1e-3 |Y| for the single-precision
+ * evaluation of silu and the product. */
+int oracle_qmv_id_gate_up(int fmt, const uint8_t* Wg, const uint8_t* Wu, int64_t E, int64_t N,
+                          int64_t K, const int32_t* ids, int64_t T, int64_t top_k,
+                          const float* X, int64_t x_tok_stride, int64_t x_slot_stride,
+                          double* Y, double* S) {
+  if (K % 32 != 0 || (fmt != ORACLE_Q4_0 && fmt != ORACLE_Q8_0)) return -1;
+  const int64_t row_bytes = (K / 32) * block_bytes(fmt);
+  for (int64_t i = 0; i < T * top_k; i++)
+    if (ids[i] >= E) return -3;
+  int err = 0;
+#pragma omp parallel for collapse(2) schedule(dynamic, 4)
+  for (int64_t ts = 0; ts < T * top_k; ts++) {
+    for (int64_t n = 0; n < N; n++) {
+      const int64_t t = ts / top_k, s = ts % top_k;
+      const int32_t e = ids[ts];
+      double y = 0.0, sy = 0.0;
+      if (e >= 0) {
+        double* w = (double*)malloc((size_t)2 * K * sizeof(double));
+        if (!w) { err = -2; continue; }
+        oracle_decode_row(fmt, Wg + ((int64_t)e * N + n) * row_bytes, K, w);
+        oracle_decode_row(fmt, Wu + ((int64_t)e * N + n) * row_bytes, K, w + K);
+        const float* x = X + t * x_tok_stride + s * x_slot_stride;
+        double g = 0.0, u = 0.0, sg = 0.0, su = 0.0;
+        for (int64_t k = 0; k < K; k++) {
+          const double pg = w[k] * (double)x[k], pu = w[K + k] * (double)x[k];
+          g += pg;
+          u += pu;
+          sg += fabs(pg);
+          su += fabs(pu);
+        }
+        free(w);
+        const double sl = oracle_silu(g);
+        y = sl * u;
+        sy = 1.1 * sg * (fabs(u) + 1e-3 * su) + fabs(sl) * su + 1e-3 * fabs(y);
+      }
+      Y[ts * N + n] = y;
+      if (S) S[ts * N + n] = sy;
+    }
+  }
+  return err;
+}
+
 /* Activation quantizer for the prefill product, per row m and 32-wide block b, in
  * IEEE single precision:
  *   a  = max_j |x_j|;  dx = a / 127 (correctly rounded division);

@@ -174,3 +174,88 @@ def test_qmv_id_groups_split_between_workgroups():
     say("qmv_id groups split between workgroups")
     y, Yr, S = run_id("q4_0", E, N, K, ids, X, K, 0, ("split",))
     check_close(y, Yr, S, "groups split between workgroups")
+
+
+# --- fused gate+up ------------------------------------------------------------------------
+
+def run_gate_up(fmt, E, N, K, ids_np, X, xts, xss, key):
+    T, top_k = ids_np.shape
+    Wg = weights(fmt, E * N, K, key + ("g",), std=0.05)
+    Wu = weights(fmt, E * N, K, key + ("u",), std=0.05)
+    Gp, Up = packed(fmt, Wg, E * N, K), packed(fmt, Wu, E * N, K)
+    ids = torch.from_numpy(ids_np).to(DEV)
+    Y = torch.full((T, top_k, N), -7.0, device=DEV)
+    bqm.qmv_id_gate_up(fmt, Gp, Up, E, N, K, ids, T, top_k, X, xts, xss, Y)
+    ids_ok = np.where(ids_np >= E, -1, ids_np).astype(np.int32)
+    Yr, S = oracle.qmv_id_gate_up(fmt, host(Wg), host(Wu), E, N, K, ids_ok, host(X).reshape(-1), xts, xss)
+    return host(Y), Yr, S
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0"])
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 16])
+def test_gate_up_batch_classes(fmt, T):
+    """silu(gate) * up for every batch class (1, 2, 4, 8), groups of one expert split over
+    workgroups, a padding slot and an out-of-range id."""
+    E, N, K, top_k = 6, 300, 1184, 3
+    ids = gen.router_ids(T, E, top_k, ("gu-router", T))
+    ids[0, 1] = -1
+    if T > 1:
+        ids[1, 2] = E + 2
+    X = gen.normal((T, K), ("gu-x", T, fmt), device=DEV)
+    say("gate_up classes", fmt, T)
+    y, Yr, S = run_gate_up(fmt, E, N, K, ids, X, K, 0, ("gu", fmt, T))
+    bad = ids >= E
+    assert np.all(np.isnan(y[bad]))
+    assert np.all(y[0, 1] == 0)
+    check_close(y[~bad], Yr[~bad], S[~bad], f"gate_up {fmt} T={T}")
+
+
+@pytest.mark.parametrize("T,K", [(16, 16384), (1, 32768)])
+def test_gate_up_long_k_is_chunked(T, K):
+    """Chunked K: each output row keeps two partial sums (gate and up) across the chunks."""
+    E, N, top_k = 8, 100, 4
+    ids = gen.router_ids(T, E, top_k, ("gu-long-router", T))
+    X = gen.normal((T, top_k, K), ("gu-long-x", T, K), device=DEV)
+    say("gate_up long K", T, K)
+    y, Yr, S = run_gate_up("q8_0", E, N, K, ids, X, top_k * K, K, ("gu-long", T, K))
+    check_close(y, Yr, S, f"gate_up long K T={T}")
+
+
+@pytest.mark.parametrize("T", [1, 16])
+def test_gate_up_moe_layer(T):
+    """The MoE layer's gate/up shapes (1536 x 4096 per expert, 128 experts, top-8)."""
+    sh = gen.MOE_SHAPE
+    E, top_k, N, K = sh["E"], sh["top_k"], sh["ffn"], sh["hidden"]
+    ids = gen.router_ids(T, E, top_k, ("moe-router", T))
+    X = gen.normal((T, K), ("gu-moe-x", T), device=DEV)
+    say("gate_up moe", T)
+    y, Yr, S = run_gate_up("q4_0", E, N, K, ids, X, K, 0, ("gu-moe",))
+    check_close(y, Yr, S, f"gate_up moe T={T}")
+
+
+def test_gate_up_empty_k_and_matches_separate_calls():
+    """K = 0 gives zeros for valid slots; with K > 0 the fused result equals silu of one
+    qmv_id call times the other's, to the tolerance of the fused bound."""
+    ids = torch.tensor([[0, -1], [2, 5]], dtype=torch.int32, device=DEV)
+    W = torch.zeros(256, dtype=torch.uint8, device=DEV)
+    X = torch.zeros(64, device=DEV)
+    Y = torch.full((2, 2, 24), -7.0, device=DEV)
+    bqm.qmv_id_gate_up("q4_0", W, W, 3, 24, 0, ids, 2, 2, X, 0, 0, Y)
+    y = host(Y)
+    assert np.all(y[0] == 0) and np.all(y[1, 0] == 0) and np.all(np.isnan(y[1, 1]))
+    E, N, K, T, top_k = 5, 200, 2048, 4, 2
+    idn = gen.router_ids(T, E, top_k, ("gu-sep",))
+    Wg, Wu = weights("q4_0", E * N, K, ("gu-sep", "g")), weights("q4_0", E * N, K, ("gu-sep", "u"))
+    Gp, Up = packed("q4_0", Wg, E * N, K), packed("q4_0", Wu, E * N, K)
+    X = gen.normal((T, K), ("gu-sep-x",), device=DEV)
+    idd = torch.from_numpy(idn).to(DEV)
+    Yf = torch.empty((T, top_k, N), device=DEV)
+    Yg = torch.empty((T, top_k, N), device=DEV)
+    Yu = torch.empty((T, top_k, N), device=DEV)
+    bqm.qmv_id_gate_up("q4_0", Gp, Up, E, N, K, idd, T, top_k, X, K, 0, Yf)
+    bqm.qmv_id("q4_0", Gp, E, N, K, idd, T, top_k, X, K, 0, Yg)
+    bqm.qmv_id("q4_0", Up, E, N, K, idd, T, top_k, X, K, 0, Yu)
+    Yr, S = oracle.qmv_id_gate_up("q4_0", host(Wg), host(Wu), E, N, K, idn, host(X).reshape(-1), K, 0)
+    sep = host(torch.nn.functional.silu(Yg) * Yu).astype(np.float64)
+    check_close(host(Yf), sep, S, "fused vs separate")
+    check_close(host(Yf), Yr, S, "fused vs oracle")

@@ -23,6 +23,8 @@ MUTANTS = {
     "act_signed_max": [("float v = fabsf(x[j]);", "float v = x[j];")],
     "id_slot_stride": [("s * x_slot_stride", "t * x_slot_stride")],
     "id_padding_ignored": [("if (e >= 0) {", "if (1) { const int32_t ee = e < 0 ? 0 : e; (void)ee;")],
+    "silu_sign": [("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));")],
+    "gate_up_swapped": [("y = sl * u;", "y = oracle_silu(u) * g;")],
 }
 
 
@@ -34,6 +36,9 @@ def test_pins_catch_planted_mistake(name, tmp_path):
         src = src.replace(old, new)
     if name == "id_padding_ignored":
         src = src.replace("W + ((int64_t)e * N + n) * row_bytes", "W + ((int64_t)(e < 0 ? 0 : e) * N + n) * row_bytes")
+        for t in ("Wg", "Wu"):
+            src = src.replace(f"{t} + ((int64_t)e * N + n) * row_bytes",
+                              f"{t} + ((int64_t)(e < 0 ? 0 : e) * N + n) * row_bytes")
     c = tmp_path / "mutant.c"
     c.write_text(src)
     so = tmp_path / "libmutant.so"

@@ -200,6 +200,50 @@ def test_qmv_id_rejects_out_of_range_id(oracle_lib):
                           np.zeros(K, np.float32), K, 0)
 
 
+# --- fused gate+up: silu and the product ------------------------------------------------
+
+def test_silu_closed_forms(oracle_lib):
+    """silu(z) = z * logistic(z): logistic(0) = 1/2, logistic(1) = e/(1+e), logistic(2) =
+    e^2/(1+e^2) (textbook values); silu(z) - silu(-z) = z because logistic(z) +
+    logistic(-z) = 1; silu(z) -> z for large z and -> 0 (from below) for very negative z."""
+    import math
+    assert oracle_lib.silu(0.0) == 0.0
+    assert oracle_lib.silu(1.0) == pytest.approx(0.7310585786300049, rel=1e-15, abs=0)
+    assert oracle_lib.silu(2.0) == pytest.approx(2 * 0.8807970779778823, rel=1e-15, abs=0)
+    assert oracle_lib.silu(-1.0) == pytest.approx(-0.2689414213699951, rel=1e-15, abs=0)
+    for z in (0.25, 1.0, 3.5, 7.0, 20.0):
+        assert oracle_lib.silu(z) - oracle_lib.silu(-z) == pytest.approx(z, rel=1e-14, abs=0)
+    assert oracle_lib.silu(60.0) == 60.0
+    assert -1e-20 < oracle_lib.silu(-60.0) < 0
+    assert oracle_lib.silu(-2.0) == pytest.approx(-2 / (1 + math.e ** 2), rel=1e-15, abs=0)
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0"])
+def test_gate_up_bruteforce(oracle_lib, fmt):
+    """Fused gate+up against the NumPy brute force: silu(Wg x) * (Wu x) per slot, padding
+    slots zero, and the tolerance scale is at least |y| * 1e-3 and zero for padding."""
+    E, N, K, T, top_k = 4, 5, 96, 3, 2
+    enc = gen.encode_q4_0 if fmt == "q4_0" else gen.encode_q8_0
+    Wg = enc(gen.normal((E * N, K), ("gu", "g", fmt), std=0.05)).numpy()
+    Wu = enc(gen.normal((E * N, K), ("gu", "u", fmt), std=0.05)).numpy()
+    ids = np.array([[3, 0], [-1, 2], [1, 3]], np.int32)
+    X = gen.normal((T, top_k, K), ("gu-x", fmt)).numpy()
+    Y, S = oracle_lib.qmv_id_gate_up(fmt, Wg, Wu, E, N, K, ids, X, top_k * K, K)
+    Gd = _npref.dequant(fmt, Wg, E * N, K).reshape(E, N, K)
+    Ud = _npref.dequant(fmt, Wu, E * N, K).reshape(E, N, K)
+    for t in range(T):
+        for s in range(top_k):
+            e = ids[t, s]
+            if e < 0:
+                assert np.all(Y[t, s] == 0) and np.all(S[t, s] == 0)
+                continue
+            x = X[t, s].astype(np.float64)
+            g, u = Gd[e] @ x, Ud[e] @ x
+            yr = g / (1 + np.exp(-g)) * u
+            assert np.all(np.abs(Y[t, s] - yr) <= 1e-12 * (np.abs(yr) + np.abs(g * u) + 1e-300))
+            assert np.all(S[t, s] >= 1e-3 * np.abs(Y[t, s]))
+
+
 # --- activation quantizer: special cases and properties --------------------------------
 
 def _half_away_exact(v: np.float32) -> int:

@@ -58,10 +58,11 @@ def _load():
         lib.oracle_silu.restype = ctypes.c_double
         lib.oracle_quantize_q8_act.argtypes = [P, I64, I64, P, P]
         lib.oracle_qmm_q8_0.argtypes = [P, P, P, I64, I64, I64, P, P, P]
+        lib.oracle_qmm_q4_0.argtypes = [P, P, P, I64, I64, I64, P, P, P]
         lib.oracle_threads.restype = I32
         lib.oracle_set_threads.argtypes = [I32]
         for f in ("oracle_decode_row", "oracle_qmv", "oracle_qmv_id", "oracle_qmv_id_gate_up",
-                  "oracle_quantize_q8_act", "oracle_qmm_q8_0"):
+                  "oracle_quantize_q8_act", "oracle_qmm_q8_0", "oracle_qmm_q4_0"):
             getattr(lib, f).restype = I32
         _lib = lib
     return _lib
@@ -167,4 +168,18 @@ def qmm_q8_0(W, Xq, dx, N: int, K: int, want_isum: bool = False):
     isum = np.empty((M, N, K // 32), np.int32) if want_isum else None
     _check(_load().oracle_qmm_q8_0(_p(Wb), _p(Xq8), _p(dxf), M, N, K, _p(isum), _p(Y), _p(S)),
            "qmm_q8_0")
+    return (Y, S, isum) if want_isum else (Y, S)
+
+
+def qmm_q4_0(W, Xq, dx, N: int, K: int, want_isum: bool = False):
+    """The Q4_0-weight prefill product: Y, S [M][N] and optionally isum [M][N][K/32]."""
+    Wb = _c(W, np.uint8)
+    Xq8 = _c(Xq, np.int8).reshape(-1, K)
+    M = Xq8.shape[0]
+    dxf = _c(dx, np.float32).reshape(M, K // 32)
+    Y = np.empty((M, N), np.float64)
+    S = np.empty((M, N), np.float64)
+    isum = np.empty((M, N, K // 32), np.int32) if want_isum else None
+    _check(_load().oracle_qmm_q4_0(_p(Wb), _p(Xq8), _p(dxf), M, N, K, _p(isum), _p(Y), _p(S)),
+           "qmm_q4_0")
     return (Y, S, isum) if want_isum else (Y, S)

@@ -282,3 +282,40 @@ int oracle_qmm_q8_0(const uint8_t* W, const int8_t* Xq, const float* dx, int64_t
   }
   return 0;
 }
+
+/* Prefill product with Q4_0 weights: the same definition as oracle_qmm_q8_0 with the
+ * weight codes q - 8 (q the nibble; weight j of a block in the low nibble of byte j,
+ * weight j + 16 in the high one):
+ *   isum[m][n][b] = sum_j (q[n][32b+j] - 8) * Xq[m][32b+j]   (exact int32)
+ *   Y[m][n]       = sum_b (double)d_w[n][b] * (double)dx[m][b] * isum[m][n][b]. */
+int oracle_qmm_q4_0(const uint8_t* W, const int8_t* Xq, const float* dx, int64_t M, int64_t N,
+                    int64_t K, int32_t* isum, double* Y, double* S) {
+  if (K % 32 != 0) return -1;
+  const int64_t nb = K / 32;
+  const int64_t row_bytes = nb * 18;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t m = 0; m < M; m++) {
+    for (int64_t n = 0; n < N; n++) {
+      double y = 0.0, sa = 0.0;
+      for (int64_t b = 0; b < nb; b++) {
+        const uint8_t* blk = W + n * row_bytes + b * 18;
+        double dw = oracle_half_to_double((uint16_t)(blk[0] | (blk[1] << 8)));
+        const uint8_t* qs = blk + 2;
+        const int8_t* qx = Xq + m * K + 32 * b;
+        int32_t acc = 0, aabs = 0;
+        for (int j = 0; j < 16; j++) {
+          const int32_t lo = (qs[j] & 0x0f) - 8, hi = ((qs[j] >> 4) & 0x0f) - 8;
+          acc += lo * (int32_t)qx[j] + hi * (int32_t)qx[j + 16];
+          aabs += abs(lo * (int32_t)qx[j]) + abs(hi * (int32_t)qx[j + 16]);
+        }
+        if (isum) isum[(m * N + n) * nb + b] = acc;
+        double scale = dw * (double)dx[m * nb + b];
+        y += scale * (double)acc;
+        sa += fabs(scale) * (double)aabs;
+      }
+      Y[m * N + n] = y;
+      if (S) S[m * N + n] = sa;
+    }
+  }
+  return 0;
+}

@@ -43,3 +43,24 @@ def q8_scales(Wq8, N, K):
     nb = K // 32
     blk = np.asarray(Wq8, np.uint8).reshape(N, nb, 34)
     return blk[:, :, 0:2].copy().view(np.float16)[:, :, 0].astype(np.float64)
+
+
+def q4_codes(Wq4, N, K):
+    """Signed Q4_0 codes [N][nb][32] (nibble - 8): low nibbles are weights 0..15 of a
+    block, high nibbles weights 16..31."""
+    nb = K // 32
+    qs = np.asarray(Wq4, np.uint8).reshape(N, nb, 18)[:, :, 2:]
+    return np.concatenate([qs & 0x0F, qs >> 4], axis=2).astype(np.int64) - 8
+
+
+def q4_scales(Wq4, N, K):
+    nb = K // 32
+    blk = np.asarray(Wq4, np.uint8).reshape(N, nb, 18)
+    return blk[:, :, 0:2].copy().view(np.float16)[:, :, 0].astype(np.float64)
+
+
+def qmm_q4_isum(Wq4, Xq, N, K):
+    """Exact int64 block sums [M][N][nb] of Q4_0 weight codes with int8 activations."""
+    nb = K // 32
+    qx = np.asarray(Xq, np.int8).astype(np.int64).reshape(-1, nb, 32)
+    return np.einsum("mbj,nbj->mnb", qx, q4_codes(Wq4, N, K))

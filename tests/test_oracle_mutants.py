@@ -19,6 +19,10 @@ MUTANTS = {
     "qmm_block_scale_index": [("(double)dx[m * nb + b]", "(double)dx[m * nb]")],
     "qmm_codes_unsigned": [("acc += (int32_t)qw[j] * (int32_t)qx[j];",
                             "acc += (int32_t)(uint8_t)qw[j] * (int32_t)qx[j];")],
+    "qmm_q4_offset_dropped": [("const int32_t lo = (qs[j] & 0x0f) - 8, hi = ((qs[j] >> 4) & 0x0f) - 8;",
+                               "const int32_t lo = (qs[j] & 0x0f), hi = ((qs[j] >> 4) & 0x0f);")],
+    "qmm_q4_halves_swapped": [("lo * (int32_t)qx[j] + hi * (int32_t)qx[j + 16]",
+                               "hi * (int32_t)qx[j] + lo * (int32_t)qx[j + 16]")],
     "act_round_to_even": [("roundf(x[j] / d)", "rintf(x[j] / d)")],
     "act_signed_max": [("float v = fabsf(x[j]);", "float v = x[j];")],
     "id_slot_stride": [("s * x_slot_stride", "t * x_slot_stride")],

@@ -313,6 +313,49 @@ def test_qmm_single_block_is_one_product(oracle_lib):
     assert np.array_equal(Y[0], dw * 0.25 * isum[0, :, 0])
 
 
+@pytest.mark.parametrize("M,N,K", [(3, 4, 96), (2, 5, 64)])
+def test_qmm_q4_bruteforce(oracle_lib, M, N, K):
+    """Q4_0 prefill product: exact block sums against a NumPy decode of the nibbles, and
+    the scaled sum against a dense fp64 contraction."""
+    W = gen.raw_q4_0(N, K, ("qmm4", M, N, K), scales=(0.001, 0.0173, -0.02), codes=(0, 15)).numpy()
+    rng = np.random.default_rng(11)
+    Xq = rng.integers(-127, 128, size=(M, K), dtype=np.int8)
+    dx = (rng.random((M, K // 32)) * 0.05).astype(np.float32)
+    Y, S, isum = oracle_lib.qmm_q4_0(W, Xq, dx, N, K, want_isum=True)
+    iref = _npref.qmm_q4_isum(W, Xq, N, K)
+    assert np.array_equal(isum, iref)
+    dw = _npref.q4_scales(W, N, K)
+    scale = dw[None, :, :] * dx.astype(np.float64)[:, None, :]
+    Yr = np.einsum("mnb,mnb->mn", scale, iref.astype(np.float64))
+    assert np.all(np.abs(Y - Yr) <= 1e-12 * S)
+
+
+def test_qmm_q4_extreme_codes(oracle_lib):
+    """Nibble 0 is the code -8 and nibble 15 the code +7: all-0x00 bytes against all-ones
+    activations give -8 per weight, all-0xFF bytes +7."""
+    K = 64
+    W = gen.raw_q4_0(2, K, ("qmm4x",), scales=(1.0,), codes=(0, 0)).numpy().reshape(2, 2, 18)
+    W[1, :, 2:] = 0xFF
+    Xq = np.ones((1, K), np.int8)
+    dx = np.array([[1.0, 0.5]], np.float32)
+    Y, S, isum = oracle_lib.qmm_q4_0(W.reshape(-1), Xq, dx, 2, K, want_isum=True)
+    assert np.array_equal(isum[0], [[-256, -256], [224, 224]])
+    assert np.array_equal(Y[0], [-256 * 1.5, 224 * 1.5])
+
+
+def test_qmm_q4_matches_qmv_on_dequantized_activations(oracle_lib):
+    """qmm with activations dx*qx equals the fp64 Q4_0 GEMV with them."""
+    M, N, K = 2, 3, 64
+    W = gen.raw_q4_0(N, K, ("qmm4-qmv",), scales=(0.25, 0.5), codes=(0, 15)).numpy()
+    rng = np.random.default_rng(5)
+    Xq = rng.integers(-127, 128, size=(M, K), dtype=np.int8)
+    dx = np.array([[0.5, 2.0], [0.125, 1.0]], np.float32)
+    Y, _ = oracle_lib.qmm_q4_0(W, Xq, dx, N, K)
+    Xd = (Xq.reshape(M, 2, 32) * dx[:, :, None]).reshape(M, K).astype(np.float32)
+    Y2, _ = oracle_lib.qmv("q4_0", W, Xd, N, K)
+    assert np.array_equal(Y, Y2)
+
+
 def test_qmm_matches_qmv_on_dequantized_activations(oracle_lib):
     """qmm with activations dx*qx equals the fp64 product of the Q8_0 weights with them."""
     M, N, K = 2, 3, 64

@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dense27b_q4_0",
-                    choices=["dense27b_q4_0", "dense27b_q8_0", "gemv4096", "moe", "prefill"])
+                    choices=["dense27b_q4_0", "dense27b_q8_0", "gemv4096", "moe", "prefill", "prefill_q4_0"])
     ap.add_argument("--M", type=int, default=1, help="batch for dense27b_q8_0 (1, 4 or 8)")
     ap.add_argument("--layers", type=int, default=64)
     ap.add_argument("--no-graph", action="store_true", help="eager launches instead of a graph")
@@ -385,17 +385,18 @@ def run_moe(args, torch, gen, bqm):
             "by_T": out}
 
 
-def run_prefill(args, torch, gen, bqm):
+def run_prefill(args, torch, gen, bqm, fmt="q8_0"):
     sh = gen.PREFILL_SHAPE
     M, N, K = sh["M"], sh["N"], sh["K"]
     copies = 8
-    mats = [make_matrix("q8_0", N, K, ("prefill", c), torch, gen, bqm) for c in range(copies)]
+    mats = [make_matrix(fmt, N, K, ("prefill", c), torch, gen, bqm) for c in range(copies)]
+    qmm = getattr(bqm, f"qmm_{fmt}")
     X = gen.normal((M, K), ("prefill-x", 0), device="cuda")
     Xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
     dx = torch.empty((M, K // 32), device="cuda")
     Y = torch.empty((M, N), device="cuda")
     bqm.bqm_quantize_q8_act(X, Xq, dx, M, K)
-    launches = [(lambda w=w: bqm.qmm_q8_0(w, Xq, dx, Y, M, N, K)) for w in mats]
+    launches = [(lambda w=w: qmm(w, Xq, dx, Y, M, N, K)) for w in mats]
     qlaunch = [lambda: bqm.bqm_quantize_q8_act(X, Xq, dx, M, K)]
 
     def run():
@@ -413,15 +414,15 @@ def run_prefill(args, torch, gen, bqm):
     # cores): 2 lane operations, against 256 CUs x 64 lanes x 2.4 GHz = 39.3 T per second.
     valu_ops = 2.0 * M * N * (K // 32)
     valu_t = valu_ops / (dur.mean() * 1e-3) / 1e12
-    return {"metric": "prefill qmm_q8_0 int8 TOP/s", "value": round(tops, 2), "unit": "TOP/s",
+    return {"metric": f"prefill qmm_{fmt} int8 TOP/s", "value": round(tops, 2), "unit": "TOP/s",
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8/f32",
             "data": "synthetic",
-            "config": {"workload": "prefill GEMM M=512 K=5120 N=17408, Q8_0 weights, 8 weight copies"},
+            "config": {"workload": f"prefill GEMM M=512 K=5120 N=17408, {fmt.upper()} weights, 8 weight copies"},
             "roofline": {"bound": "alu", "achieved": round(valu_t, 3), "peak": VALU_PEAK_TOPS,
                          "unit": "T lane-op/s", "frac": round(valu_t / VALU_PEAK_TOPS, 4),
-                         "traffic": traffic_from_profiles("qmm_q8_0_prefill"),
-                         "kernel": "k_qmm_q8_0", "avg_launch_us": round(1e3 * float(dur.mean()), 3),
+                         "traffic": traffic_from_profiles(f"qmm_{fmt}_prefill"),
+                         "kernel": f"k_qmm_{fmt}", "avg_launch_us": round(1e3 * float(dur.mean()), 3),
                          "mfma_int8_frac": round(tops / INT8_PEAK_TOPS, 4)},
             "quantize_us": round(1e3 * float(qdur.mean()), 3)}
 
@@ -449,6 +450,8 @@ def main():
         res = run_gemv4096(args, torch, gen, bqm)
     elif wl == "moe":
         res = run_moe(args, torch, gen, bqm)
+    elif wl == "prefill_q4_0":
+        res = run_prefill(args, torch, gen, bqm, "q4_0")
     else:
         res = run_prefill(args, torch, gen, bqm)
     print(json.dumps(res), flush=True)

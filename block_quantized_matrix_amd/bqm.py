@@ -51,6 +51,7 @@ def lib():
         L.qmv_id_gate_up.argtypes = [I, P, P, I, I64, I64, P, I, I, P, I64, I64, P, P]
         L.bqm_quantize_q8_act.argtypes = [P, P, P, I64, I64, P]
         L.qmm_q8_0.argtypes = [P, P, P, P, I64, I64, I64, P]
+        L.qmm_q4_0.argtypes = [P, P, P, P, I64, I64, I64, P]
         L.bqm_chain_workspace_bytes.argtypes = [I]
         L.bqm_chain_workspace_bytes.restype = SZ
         L.bqm_chain_prepare.argtypes = [P, I, P, P]
@@ -61,7 +62,7 @@ def lib():
         L.bqm_strerror.argtypes = [I]
         L.bqm_strerror.restype = ctypes.c_char_p
         for f in ("bqm_repack", "bqm_unpack", "qmv_q4_0", "qmv_q8_0", "qmv_id",
-                  "bqm_quantize_q8_act", "qmm_q8_0"):
+                  "bqm_quantize_q8_act", "qmm_q8_0", "qmm_q4_0"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -133,6 +134,10 @@ def bqm_quantize_q8_act(X, Xq, dx, M: int, K: int, stream=None):
 
 def qmm_q8_0(w_packed, Xq, dx, Y, M: int, N: int, K: int, stream=None):
     _call("qmm_q8_0", _ptr(w_packed), _ptr(Xq), _ptr(dx), _ptr(Y), M, N, K, _stream(stream))
+
+
+def qmm_q4_0(w_packed, Xq, dx, Y, M: int, N: int, K: int, stream=None):
+    _call("qmm_q4_0", _ptr(w_packed), _ptr(Xq), _ptr(dx), _ptr(Y), M, N, K, _stream(stream))
 
 
 class Gemv(ctypes.Structure):

@@ -142,9 +142,9 @@ int bqm_quantize_q8_act(const float* X, int8_t* Xq, float* dx, int64_t M, int64_
   return launch_quantize_q8_act(X, Xq, dx, M, K, stream);
 }
 
-int qmm_q8_0(const void* w_packed, const int8_t* Xq, const float* dx, float* Y, int64_t M,
-             int64_t N, int64_t K, hipStream_t stream) {
-  if (int st = check_shape(BQM_Q8_0, N, K)) return st;
+static int qmm_common(int fmt, const void* w_packed, const int8_t* Xq, const float* dx, float* Y,
+                      int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  if (int st = check_shape(fmt, N, K)) return st;
   if (M < 0 || M > kMaxRows) return BQM_E_SHAPE;
   if (M == 0 || N == 0) return BQM_OK;
   if (!Y) return BQM_E_NULL;
@@ -153,7 +153,18 @@ int qmm_q8_0(const void* w_packed, const int8_t* Xq, const float* dx, float* Y, 
   if (int st = check_ptr(w_packed)) return st;
   if (int st = check_ptr(Xq)) return st;
   if (int st = check_ptr(dx)) return st;
-  return launch_qmm_q8_0(w_packed, Xq, dx, Y, M, N, K, stream);
+  return fmt == BQM_Q4_0 ? launch_qmm_q4_0(w_packed, Xq, dx, Y, M, N, K, stream)
+                         : launch_qmm_q8_0(w_packed, Xq, dx, Y, M, N, K, stream);
+}
+
+int qmm_q8_0(const void* w_packed, const int8_t* Xq, const float* dx, float* Y, int64_t M,
+             int64_t N, int64_t K, hipStream_t stream) {
+  return qmm_common(BQM_Q8_0, w_packed, Xq, dx, Y, M, N, K, stream);
+}
+
+int qmm_q4_0(const void* w_packed, const int8_t* Xq, const float* dx, float* Y, int64_t M,
+             int64_t N, int64_t K, hipStream_t stream) {
+  return qmm_common(BQM_Q4_0, w_packed, Xq, dx, Y, M, N, K, stream);
 }
 
 size_t bqm_chain_workspace_bytes(int n) { return chain_workspace_bytes(n); }

@@ -60,6 +60,8 @@ int launch_quantize_q8_act(const float* X, int8_t* Xq, float* dx, int64_t M, int
                            hipStream_t s);
 int launch_qmm_q8_0(const void* w, const int8_t* Xq, const float* dx, float* Y, int64_t M,
                     int64_t N, int64_t K, hipStream_t s);
+int launch_qmm_q4_0(const void* w, const int8_t* Xq, const float* dx, float* Y, int64_t M,
+                    int64_t N, int64_t K, hipStream_t s);
 int launch_fill(float* y, int64_t n, float v, hipStream_t s);
 int64_t chain_max_k();
 size_t chain_workspace_bytes(int n);

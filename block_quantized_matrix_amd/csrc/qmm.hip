@@ -1,4 +1,5 @@
-// Prefill: activation quantizer and the Q8_0 x Q8-activation product on int8 MFMA, gfx950.
+// Prefill: activation quantizer and the Q8_0 / Q4_0 x Q8-activation product on int8 MFMA,
+// gfx950.  qw is the signed weight code: the int8 of Q8_0, the nibble - 8 of Q4_0.
 //
 //   isum[m][n][b] = sum_{j<32} qw[n][32b+j] * Xq[m][32b+j]        exact int32
 //   Y[m][n]       = sum_b (d_w[n][b] * dx[m][b]) * isum[m][n][b]    fp32, b ascending
@@ -100,12 +101,30 @@ __device__ __forceinline__ u32x4 dw_operand(uint32_t dw_bits) {
   return u32x4{w, w, w, 0u};
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_qmm_q8_0(const int8_t* __restrict__ Wc,   // [N][K]
-                                                       const uint16_t* __restrict__ Wd,  // [N][nb]
-                                                       const int8_t* __restrict__ Xq,    // [M][K]
-                                                       const float* __restrict__ dx,     // [M][nb]
-                                                       float* __restrict__ Y, int M, int N, int nb,
-                                                       int tiles_m, int tiles_n) {
+// Q4_0 codes: a 16-byte block holds weight j in the low nibble of byte j and weight j + 16
+// in the high one.  Each half expands to four signed bytes per word (nibble - 8) without a
+// borrow between bytes: set bit 7, subtract 8, flip bit 7 back.
+__device__ __forceinline__ uint32_t nib_to_i8(uint32_t v) {  // v: four nibbles 0..15
+  return ((v | 0x80808080u) - 0x08080808u) ^ 0x80808080u;
+}
+__device__ __forceinline__ void expand_q4(const u32x4& q, u32x4& lo, u32x4& hi) {
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    lo[i] = nib_to_i8(q[i] & 0x0F0F0F0Fu);
+    hi[i] = nib_to_i8((q[i] >> 4) & 0x0F0F0F0Fu);
+  }
+}
+
+// One workgroup tile of Y.  FMT selects how the weight codes arrive: Q8_0 as int8 rows
+// [N][K]; Q4_0 as 16-byte blocks [N][nb][16], expanded to int8 while they are staged, so
+// that the LDS layout and everything after it are the same for both.
+template <int FMT>
+__device__ __forceinline__ void qmm_tile(const uint8_t* __restrict__ Wc, const uint16_t* __restrict__ Wd,
+                                         const int8_t* __restrict__ Xq, const float* __restrict__ dx,
+                                         float* __restrict__ Y, int M, int N, int nb, int tiles_m,
+                                         int tiles_n) {
+  constexpr bool Q4 = FMT == BQM_Q4_0;
+  constexpr int NPB = Q4 ? 2 : 4;   // 16-byte pieces of weight codes per thread and stage
   __shared__ __attribute__((aligned(16))) int8_t sA[BM * ROWB];
   __shared__ __attribute__((aligned(16))) int8_t sB[BN * ROWB];
   __shared__ u32x4 sXs[BKB * BM + 1];  // dx operands per (block, m); the last: zeros
@@ -134,7 +153,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   // staging: 128 rows x 128 bytes per operand = 1024 16-byte pieces, 4 per thread; 512
   // scales per operand, 2 per thread
-  u32x4 pa0, pa1, pa2, pa3, pb0, pb1, pb2, pb3;
+  // (Q4_0: 128 rows x 4 blocks of 16 bytes, 2 per thread)
+  const int64_t wrow = Q4 ? (int64_t)nb * 16 : (int64_t)K;  // bytes per weight row
+  u32x4 pa0, pa1, pa2, pa3, pb0, pb1, pb2 = {}, pb3 = {};
   float px0, px1;
   uint32_t pw0, pw1;
 #define BQM_FETCH(B0)                                                                          \
@@ -145,13 +166,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     _Pragma("unroll") for (int p = 0; p < 4; p++) {                                            \
       const int piece = tid + p * kThreads, row = piece >> 3, c16 = piece & 7;                 \
       const bool kin = (c16 >> 1) < bn_;                                                       \
-      u32x4 va = {0u, 0u, 0u, 0u}, vb = {0u, 0u, 0u, 0u};                                     \
+      u32x4 va = {0u, 0u, 0u, 0u};                                                             \
       if (kin && m0 + row < M)                                                                 \
         va = *reinterpret_cast<const u32x4*>(Xq + (size_t)(m0 + row) * K + (size_t)(B0) * 32 + c16 * 16); \
-      if (kin && n0 + row < N)                                                                 \
-        vb = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(                       \
-            Wc + (size_t)(n0 + row) * K + (size_t)(B0) * 32 + c16 * 16));                      \
       *pa_[p] = va;                                                                            \
+    }                                                                                          \
+    _Pragma("unroll") for (int p = 0; p < NPB; p++) {                                          \
+      const int piece = tid + p * kThreads;                                                    \
+      const int row = Q4 ? piece >> 2 : piece >> 3, c16 = Q4 ? piece & 3 : piece & 7;          \
+      const int kb_ = Q4 ? c16 : c16 >> 1;                                                     \
+      u32x4 vb = {0u, 0u, 0u, 0u};                                                             \
+      if (kb_ < bn_ && n0 + row < N)                                                           \
+        vb = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(                       \
+            Wc + (size_t)(n0 + row) * wrow + (size_t)(B0) * (Q4 ? 16 : 32) + c16 * 16));       \
       *pb_[p] = vb;                                                                            \
     }                                                                                          \
     float* px_[2] = {&px0, &px1};                                                              \
@@ -175,7 +202,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       for (int p = 0; p < 4; p++) {
         const int piece = tid + p * kThreads, row = piece >> 3, c16 = piece & 7;
         *reinterpret_cast<u32x4*>(sA + row * ROWB + c16 * 16) = pa_[p];
-        *reinterpret_cast<u32x4*>(sB + row * ROWB + c16 * 16) = pb_[p];
+      }
+#pragma unroll
+      for (int p = 0; p < NPB; p++) {
+        const int piece = tid + p * kThreads;
+        if constexpr (Q4) {
+          const int row = piece >> 2, kb = piece & 3;
+          u32x4 lo, hi;
+          expand_q4(pb_[p], lo, hi);
+          *reinterpret_cast<u32x4*>(sB + row * ROWB + kb * 32) = lo;
+          *reinterpret_cast<u32x4*>(sB + row * ROWB + kb * 32 + 16) = hi;
+        } else {
+          const int row = piece >> 3, c16 = piece & 7;
+          *reinterpret_cast<u32x4*>(sB + row * ROWB + c16 * 16) = pb_[p];
+        }
       }
       const float px_[2] = {px0, px1};
       const uint32_t pw_[2] = {pw0, pw1};
@@ -232,6 +272,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
 }
 
+#define BQM_QMM_KERNEL(NAME, FMT)                                                              \
+  __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void NAME( \
+      const uint8_t* __restrict__ Wc, const uint16_t* __restrict__ Wd,                         \
+      const int8_t* __restrict__ Xq, const float* __restrict__ dx, float* __restrict__ Y,      \
+      int M, int N, int nb, int tiles_m, int tiles_n) {                                        \
+    qmm_tile<FMT>(Wc, Wd, Xq, dx, Y, M, N, nb, tiles_m, tiles_n);                              \
+  }
+BQM_QMM_KERNEL(k_qmm_q8_0, BQM_Q8_0)
+BQM_QMM_KERNEL(k_qmm_q4_0, BQM_Q4_0)
+#undef BQM_QMM_KERNEL
+
 }  // namespace
 
 int launch_quantize_q8_act(const float* X, int8_t* Xq, float* dx, int64_t M, int64_t K,
@@ -243,16 +294,27 @@ int launch_quantize_q8_act(const float* X, int8_t* Xq, float* dx, int64_t M, int
   return launch_status();
 }
 
+static int launch_qmm(int fmt, const void* w, const int8_t* Xq, const float* dx, float* Y,
+                      int64_t M, int64_t N, int64_t K, hipStream_t s) {
+  Layout L;
+  layout_of(fmt, N, K, &L);
+  const uint8_t* Wc = static_cast<const uint8_t*>(w);
+  const uint16_t* Wd = reinterpret_cast<const uint16_t*>(Wc + L.scales_off);
+  const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
+  hipLaunchKernelGGL(fmt == BQM_Q4_0 ? k_qmm_q4_0 : k_qmm_q8_0, dim3((unsigned)(tiles_m * tiles_n)),
+                     dim3(kThreads), 0, s, Wc, Wd, Xq, dx, Y, (int)M, (int)N, (int)L.nb, tiles_m,
+                     tiles_n);
+  return launch_status();
+}
+
 int launch_qmm_q8_0(const void* w, const int8_t* Xq, const float* dx, float* Y, int64_t M,
                     int64_t N, int64_t K, hipStream_t s) {
-  Layout L;
-  layout_of(BQM_Q8_0, N, K, &L);
-  const int8_t* Wc = static_cast<const int8_t*>(w);
-  const uint16_t* Wd = reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(w) + L.scales_off);
-  const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
-  hipLaunchKernelGGL(k_qmm_q8_0, dim3((unsigned)(tiles_m * tiles_n)), dim3(kThreads), 0, s, Wc, Wd,
-                     Xq, dx, Y, (int)M, (int)N, (int)L.nb, tiles_m, tiles_n);
-  return launch_status();
+  return launch_qmm(BQM_Q8_0, w, Xq, dx, Y, M, N, K, s);
+}
+
+int launch_qmm_q4_0(const void* w, const int8_t* Xq, const float* dx, float* Y, int64_t M,
+                    int64_t N, int64_t K, hipStream_t s) {
+  return launch_qmm(BQM_Q4_0, w, Xq, dx, Y, M, N, K, s);
 }
 
 }  // namespace bqm

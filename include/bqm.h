@@ -192,6 +192,15 @@ int bqm_quantize_q8_act(const float* X, int8_t* Xq, float* dx, int64_t M, int64_
 int qmm_q8_0(const void* w_packed, const int8_t* Xq, const float* dx, float* Y, int64_t M,
              int64_t N, int64_t K, hipStream_t stream);
 
+/* Prefill product with Q4_0 weights (the pp512 prompt-processing rows of Q4_0 (QAT)
+ * models in the same section of the "llama.cpp 0.9.0" analysis page): the definition of
+ * qmm_q8_0 with qw the nibble - 8 (weight j of a block in the low nibble of code byte j,
+ * weight j + 16 in the high one).  The nibbles are widened to int8 on the way into local
+ * memory, so the integer sums are exact and the scaling is that of qmm_q8_0.
+ * w_packed: packed Q4_0 N x K matrix; the rest as for qmm_q8_0.  Same status codes. */
+int qmm_q4_0(const void* w_packed, const int8_t* Xq, const float* dx, float* Y, int64_t M,
+             int64_t N, int64_t K, hipStream_t stream);
+
 /* Static English text for a status code. */
 const char* bqm_strerror(int status);
 

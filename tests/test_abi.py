@@ -23,7 +23,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("bqm_packed_bytes", "bqm_repack", "bqm_unpack", "qmv_q4_0", "qmv_q8_0", "qmv_id",
-              "qmv_id_gate_up", "bqm_quantize_q8_act", "qmm_q8_0", "bqm_strerror"):
+              "qmv_id_gate_up", "bqm_quantize_q8_act", "qmm_q8_0", "qmm_q4_0", "bqm_strerror"):
         assert n in names
 
 
@@ -98,6 +98,10 @@ def test_host_validation_before_launch():
     assert L.bqm_quantize_q8_act(GOOD, None, GOOD, 4, 64, None) == 1
     assert L.qmm_q8_0(GOOD, GOOD, GOOD, GOOD, 4, 8, 48, None) == 2
     assert L.qmm_q8_0(GOOD, ODD, GOOD, GOOD, 4, 8, 64, None) == 3
+    assert L.qmm_q4_0(GOOD, GOOD, GOOD, GOOD, 4, 8, 48, None) == 2
+    assert L.qmm_q4_0(GOOD, GOOD, GOOD, GOOD, -1, 8, 64, None) == 2
+    assert L.qmm_q4_0(None, GOOD, GOOD, GOOD, 4, 8, 64, None) == 1
+    assert L.qmm_q4_0(GOOD, GOOD, GOOD, ODD, 4, 8, 64, None) == 3
     # repack alignment: interchange needs 2-byte alignment, packed 16
     assert L.bqm_repack(2, P(0x100001), GOOD, 4, 64, None) == 3
     assert L.bqm_repack(2, GOOD, ODD, 4, 64, None) == 3
@@ -112,6 +116,7 @@ def test_empty_sizes_are_no_ops():
     assert L.qmv_id_gate_up(2, None, None, 4, 8, 64, None, 0, 8, None, 64, 0, None, None) == 0
     assert L.bqm_quantize_q8_act(None, None, None, 0, 64, None) == 0
     assert L.qmm_q8_0(None, None, None, None, 0, 8, 64, None) == 0
+    assert L.qmm_q4_0(None, None, None, None, 4, 0, 64, None) == 0
     assert L.bqm_repack(2, None, None, 0, 64, None) == 0
     assert L.bqm_unpack(8, None, None, 4, 0, None) == 0
 

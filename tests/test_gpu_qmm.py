@@ -51,72 +51,101 @@ def test_quantize_q8_act_special_blocks():
     assert list(host(Xq)[0, 32:38]) == [127, 64, -1, 3, -3, 0]
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (5, 37, 96), (130, 129, 160), (256, 300, 1056)])
-def test_qmm_parity_small(M, N, K):
-    say("qmm small", M, N, K)
-    Wi = weights("q8_0", N, K, ("qmm", M, N, K))
+FMTS = ["q8_0", "q4_0"]
+
+
+def qmm(fmt):
+    return getattr(bqm, f"qmm_{fmt}")
+
+
+def qmm_oracle(fmt):
+    return getattr(oracle, f"qmm_{fmt}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (5, 37, 96), (130, 129, 160), (256, 300, 1056),
+                                   (129, 131, 4128)])
+def test_qmm_parity_small(fmt, M, N, K):
+    say("qmm small", fmt, M, N, K)
+    Wi = weights(fmt, N, K, ("qmm", M, N, K))
     X = gen.normal((M, K), ("qmm-x", M, N, K), device=DEV)
     Xq, dx = quantize(X, M, K)
     Y = torch.full((M, N), float("nan"), device=DEV)
-    bqm.qmm_q8_0(packed("q8_0", Wi, N, K), Xq, dx, Y, M, N, K)
-    Yr, S = oracle.qmm_q8_0(host(Wi), host(Xq), host(dx), N, K)
-    check_close(host(Y), Yr, S, f"qmm {M}x{N}x{K}")
+    qmm(fmt)(packed(fmt, Wi, N, K), Xq, dx, Y, M, N, K)
+    Yr, S = qmm_oracle(fmt)(host(Wi), host(Xq), host(dx), N, K)
+    check_close(host(Y), Yr, S, f"qmm {fmt} {M}x{N}x{K}")
 
 
-def _exact_probe(M, N, K, rows=None):
-    """qw, qx in [-8, 8], dw, dx in {0.5, 1, 2}: the block sums are exact integers and so is
-    every fp32 step after them, so the output equals the oracle bit for bit; a single
-    wrong integer block sum changes it."""
-    Wi = gen.raw_q8_0(N, K, ("qmm-probe", N, K), codes=(-8, 8), device=DEV)
+def _exact_probe(fmt, M, N, K, rows=None):
+    """qw in [-8, 8] (Q8_0) or every nibble (Q4_0: [-8, 7]), qx in [-8, 8], dw, dx in
+    {0.5, 1, 2}: the block sums are exact integers and so is every fp32 step after them, so
+    the output equals the oracle bit for bit; a single wrong integer block sum changes it."""
+    if fmt == "q8_0":
+        Wi = gen.raw_q8_0(N, K, ("qmm-probe", N, K), codes=(-8, 8), device=DEV)
+    else:
+        Wi = gen.raw_q4_0(N, K, ("qmm-probe4", N, K), codes=(0, 15), device=DEV)
     Xq = gen.small_int((M, K), ("qmm-probe-x", M, K), device=DEV, dtype=torch.int32).to(torch.int8)
     pick = gen.small_int((M, K // 32), ("qmm-probe-dx", M, K), 0, 2, device=DEV, dtype=torch.int32)
     dx = torch.tensor([0.5, 1.0, 2.0], device=DEV)[pick.long()]
     Y = torch.empty((M, N), device=DEV)
-    bqm.qmm_q8_0(packed("q8_0", Wi, N, K), Xq, dx, Y, M, N, K)
+    qmm(fmt)(packed(fmt, Wi, N, K), Xq, dx, Y, M, N, K)
     Wh = host(Wi).reshape(N, -1)
     if rows is not None:
         Wh = Wh[rows]
-    Yr, _ = oracle.qmm_q8_0(Wh, host(Xq), host(dx), Wh.shape[0], K)
+    Yr, _ = qmm_oracle(fmt)(Wh, host(Xq), host(dx), Wh.shape[0], K)
     yg = host(Y) if rows is None else host(Y)[:, rows]
     assert np.array_equal(yg.astype(np.float64), Yr)
 
 
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("M,N,K", [(3, 5, 64), (130, 129, 544), (128, 256, 5120)])
-def test_qmm_exact_probe(M, N, K):
-    say("qmm exact", M, N, K)
-    _exact_probe(M, N, K)
+def test_qmm_exact_probe(fmt, M, N, K):
+    say("qmm exact", fmt, M, N, K)
+    _exact_probe(fmt, M, N, K)
 
 
-def test_qmm_exact_probe_prefill_shape():
+@pytest.mark.parametrize("fmt", FMTS)
+def test_qmm_exact_probe_prefill_shape(fmt):
     """The full 512 x 17408 x 5120 prefill shape, sampled output columns, bit exact."""
-    say("qmm exact full shape")
+    say("qmm exact full shape", fmt)
     sh = gen.PREFILL_SHAPE
     rows = np.unique(np.random.default_rng(1).integers(0, sh["N"], 48))
-    _exact_probe(sh["M"], sh["N"], sh["K"], rows)
+    _exact_probe(fmt, sh["M"], sh["N"], sh["K"], rows)
 
 
-def test_qmm_prefill_shape():
-    """Prefill GEMM: M=512 tokens, K=5120, N=17408, Q8_0 weights from N(0, 0.02), activations
-    N(0, 1) quantized per block; sampled output columns against the oracle."""
+@pytest.mark.parametrize("fmt", FMTS)
+def test_qmm_prefill_shape(fmt):
+    """Prefill GEMM: M=512 tokens, K=5120, N=17408, weights from N(0, 0.02) quantized to the
+    format, activations N(0, 1) quantized per block; sampled output columns against the
+    oracle."""
     sh = gen.PREFILL_SHAPE
     M, N, K = sh["M"], sh["N"], sh["K"]
-    say("qmm prefill shape")
-    Wi = weights("q8_0", N, K, ("prefill", 0))
+    say("qmm prefill shape", fmt)
+    Wi = weights(fmt, N, K, ("prefill", 0))
     X = gen.normal((M, K), ("prefill-x", 0), device=DEV)
     Xq, dx = quantize(X, M, K)
     Y = torch.empty((M, N), device=DEV)
-    bqm.qmm_q8_0(packed("q8_0", Wi, N, K), Xq, dx, Y, M, N, K)
+    qmm(fmt)(packed(fmt, Wi, N, K), Xq, dx, Y, M, N, K)
     rows = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(2).integers(0, N, 64)]))
-    Yr, S = oracle.qmm_q8_0(host(Wi).reshape(N, -1)[rows], host(Xq), host(dx), len(rows), K)
-    check_close(host(Y)[:, rows], Yr, S, "prefill")
+    Yr, S = qmm_oracle(fmt)(host(Wi).reshape(N, -1)[rows], host(Xq), host(dx), len(rows), K)
+    check_close(host(Y)[:, rows], Yr, S, f"prefill {fmt}")
 
 
-def test_qmm_deterministic():
+@pytest.mark.parametrize("fmt", FMTS)
+def test_qmm_deterministic(fmt):
     M, N, K = 256, 384, 2048
-    Wp = packed("q8_0", weights("q8_0", N, K, ("qmm-det",)), N, K)
+    Wp = packed(fmt, weights(fmt, N, K, ("qmm-det",)), N, K)
     Xq, dx = quantize(gen.normal((M, K), ("qmm-det-x",), device=DEV), M, K)
     Y1 = torch.empty((M, N), device=DEV)
     Y2 = torch.empty((M, N), device=DEV)
-    bqm.qmm_q8_0(Wp, Xq, dx, Y1, M, N, K)
-    bqm.qmm_q8_0(Wp, Xq, dx, Y2, M, N, K)
+    qmm(fmt)(Wp, Xq, dx, Y1, M, N, K)
+    qmm(fmt)(Wp, Xq, dx, Y2, M, N, K)
     assert torch.equal(Y1, Y2)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_qmm_empty_k_writes_zeros(fmt):
+    M, N = 3, 70
+    Y = torch.full((M, N), float("nan"), device=DEV)
+    qmm(fmt)(None, None, None, Y, M, N, 0)
+    assert torch.count_nonzero(Y).item() == 0

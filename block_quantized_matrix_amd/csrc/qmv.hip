@@ -85,6 +85,16 @@ template <> struct Codes<FQ8> { u32x4 a, b; };
 constexpr int kP1Waves = 16;  // waves of a workgroup (8 for the widest batch: registers)
 constexpr int kBlkLds = 144;  // LDS bytes per staged block
 constexpr int kChainMaxM = 8;
+// A row's blocks are taken by a group of kG lanes (lane g: blocks g, g + kG, ...), kGpw
+// groups per wave.  Narrow groups are faster on every shape measured (16 lanes against the
+// 64 or 32 that leave as few idle lanes, e.g. 4096 x 4096 Q4_0: +18 %): a row's sum is
+// reduced over fewer lanes and once per more blocks, and the lanes of a wave read fewer
+// distinct staged input blocks per step (LDS broadcasts the rest).
+#ifndef BQM_LG2G
+#define BQM_LG2G 4
+#endif
+constexpr int kLg2G = BQM_LG2G, kG = 1 << kLg2G, kGpw = 64 >> kLg2G;
+static_assert(kLg2G >= 3 && kLg2G <= 4, "group_sum covers 8 or 16 lanes");
 
 // One block of codes against MM staged input blocks (input m at xb + m * mstride bytes):
 // c[m] = sum_j code_j * x_mj in chain order (positions 0..15, then 16..31).
@@ -147,13 +157,11 @@ __device__ __forceinline__ float dpp(float v) {
                                                                __builtin_bit_cast(int, v), CTRL, 0xF,
                                                                0xF, false));
 }
-__device__ __forceinline__ float group_sum_rt(float v, int lg2G) {
+__device__ __forceinline__ float group_sum(float v) {
   v = v + dpp<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
   v = v + dpp<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
   v = v + dpp<0x141>(v);  // row_half_mirror: the other quad of the 8
-  v = v + dpp<0x140>(v);  // row_mirror: the other 8 of the 16
-  if (lg2G >= 5) v = v + __shfl_xor(v, 16, 64);
-  if (lg2G >= 6) v = v + __shfl_xor(v, 32, 64);
+  if constexpr (kLg2G >= 4) v = v + dpp<0x140>(v);  // row_mirror: the other 8 of the 16
   return v;
 }
 
@@ -250,8 +258,8 @@ struct Stage {
   const uint16_t* scales2;
   const float* x;
   float* y;
-  int nrows, nb, nbc, kb0, lg2G, G, gpw, ns, S, start, end, M, xstride, ystride, nchunks, lo;
-  bool ragged, wait, first, last;
+  int nrows, nb, nbc, kb0, ns, S, start, end, M, xstride, ystride, nchunks, lo;
+  bool wait, first, last;
 };
 
 // __builtin_amdgcn_readfirstlane is 32 bits wide: a 64-bit value takes two.
@@ -269,19 +277,10 @@ __device__ __forceinline__ void stage_chunk(int c, int kc, int wave, int wait, S
   s.first = c == 0;
   s.last = c == s.nchunks - 1;
   s.wait = wait != 0 && c == 0;
-  // lane group: the width among 64/32/16 that leaves the fewest idle lanes in a row
-  const int w64 = (-s.nbc) & 63, w32 = (-s.nbc) & 31, w16 = (-s.nbc) & 15;
-  int lg2 = 6;
-  if (w32 < w64) lg2 = 5;
-  if (w16 < (lg2 == 6 ? w64 : w32)) lg2 = 4;
-  s.lg2G = lg2;
-  s.G = 1 << lg2;
-  s.gpw = 64 >> lg2;
-  s.ragged = (s.nbc & (s.G - 1)) != 0;
-  s.ns = (s.nbc + s.G - 1) >> lg2;
-  // tiles of RT * gpw rows, ns steps each, in row order; the waves take equal contiguous
+  s.ns = (s.nbc + kG - 1) >> kLg2G;
+  // tiles of RT * kGpw rows, ns steps each, in row order; the waves take equal contiguous
   // ranges of the tile-major step sequence (a tile may be split between waves)
-  const int ntiles = (s.nrows + RT * s.gpw - 1) / (RT * s.gpw);
+  const int ntiles = (s.nrows + RT * kGpw - 1) / (RT * kGpw);
   s.S = ntiles * s.ns;
   s.start = (wave * s.S) >> LGW;
   s.end = ((wave + 1) * s.S) >> LGW;
@@ -400,7 +399,7 @@ struct ChainLds {
 __host__ __device__ inline ChainLds chain_lds(int n, int mm, int r, int pacc_rows, int kc) {
   ChainLds L;
   L.part = (n * 64 + 15) & ~15;
-  L.done = L.part + kP1Waves * 2 * 4 * r * mm * 4;
+  L.done = L.part + kP1Waves * 2 * kGpw * r * mm * 4;
   L.pacc = L.done + kP1Waves * 4;
   L.x = L.pacc + ((pacc_rows * mm * 4 + 15) & ~15);
   L.total = L.x + mm * kc * kBlkLds;
@@ -625,8 +624,8 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
   uint32_t vc1 = kOob, vs1 = kOob, vcl1 = kOob, vsl1 = kOob;
   int ig = 0, ilg = 0;
   auto tile_offsets = [&]() {
-    const bool past_k = ((si.ns - 1) << si.lg2G) + ig >= si.nbc;
-    const int row = it * RT * si.gpw + ilg;
+    const bool past_k = ((si.ns - 1) << kLg2G) + ig >= si.nbc;
+    const int row = it * RT * kGpw + ilg;
     const bool ok0 = row < si.nrows;  // rows past the range read zeros
     vc0 = ok0 ? ((uint32_t)ilg * si.nb + ig) * CB : kOob;
     vs0 = ok0 ? ((uint32_t)ilg * si.nb + ig) * 2 : kOob;
@@ -638,9 +637,9 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
       vcl1 = vcl0;
       vsl1 = vsl0;
     } else if constexpr (R == 2) {
-      const bool ok1 = row + si.gpw < si.nrows;
-      vc1 = ok1 ? ((uint32_t)(si.gpw + ilg) * si.nb + ig) * CB : kOob;
-      vs1 = ok1 ? ((uint32_t)(si.gpw + ilg) * si.nb + ig) * 2 : kOob;
+      const bool ok1 = row + kGpw < si.nrows;
+      vc1 = ok1 ? ((uint32_t)(kGpw + ilg) * si.nb + ig) * CB : kOob;
+      vs1 = ok1 ? ((uint32_t)(kGpw + ilg) * si.nb + ig) * 2 : kOob;
       vcl1 = past_k ? kOob : vc1;
       vsl1 = past_k ? kOob : vs1;
     }
@@ -673,8 +672,8 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
         rs2 = __builtin_amdgcn_make_buffer_rsrc((void*)si.scales2, (short)0,
                                                 (int)((uint32_t)si.nrows * si.nb * 2 + 2), 0x00020000);
       }
-      ig = lane & (si.G - 1);
-      ilg = lane >> si.lg2G;
+      ig = lane & (kG - 1);
+      ilg = lane >> kLg2G;
       it = si.start / si.ns;
       ij = si.start - it * si.ns;
       tile_offsets();
@@ -687,7 +686,7 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
     // the loads duplicated): one load sequence for real and padding steps.  Once the range
     // is done the lane offsets are past the descriptor: zeros, no memory traffic.
     const uint32_t live = ireal > 0 ? 1u : 0u;
-    const uint32_t so = ((uint32_t)(it * RT * si.gpw) * si.nb + (uint32_t)si.kb0 + (uint32_t)(ij << si.lg2G)) * live;
+    const uint32_t so = ((uint32_t)(it * RT * kGpw) * si.nb + (uint32_t)si.kb0 + (uint32_t)(ij << kLg2G)) * live;
     const uint32_t lm = 0u - (uint32_t)(ij == si.ns - 1);  // all ones at a tile's last step
 #pragma unroll
     for (int r = 0; r < R; r++) {
@@ -771,8 +770,8 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
     cpad = (creal + P - 1) / P * P;
     ct = sc.start / sc.ns;
     cj = sc.start - ct * sc.ns;
-    cg = lane & (sc.G - 1);
-    clg = lane >> sc.lg2G;
+    cg = lane & (kG - 1);
+    clg = lane >> kLg2G;
     __syncthreads();
     // x comes through agent-coherent loads (other workgroups may have written it), 16
     // bytes per lane: a pass of a wave stages 8 whole blocks of one input.  Up to 4 passes'
@@ -833,7 +832,7 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
     }
     __syncthreads();
     lds_lane = xlds + cg * kBlkLds;
-    lds_last = ((sc.ns - 1) << sc.lg2G) + cg < sc.nbc ? lds_lane + (sc.ns - 1) * (sc.G * kBlkLds)
+    lds_last = ((sc.ns - 1) << kLg2G) + cg < sc.nbc ? lds_lane + (sc.ns - 1) * (kG * kBlkLds)
                                                       : xlds + (sc.nbc - 1) * kBlkLds;  // its d is 0
     return true;
   };
@@ -844,7 +843,7 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
 #pragma unroll
       for (int p = 0; p < P; p++) {
         if (creal > 0) {  // uniform: a real step of this wave
-          const char* xb = cj == sc.ns - 1 ? lds_last : lds_lane + cj * (sc.G * kBlkLds);
+          const char* xb = cj == sc.ns - 1 ? lds_last : lds_lane + cj * (kG * kBlkLds);
           float sxm[MM];
 #pragma unroll
           for (int m = 0; m < MM; m++) sxm[m] = *reinterpret_cast<const float*>(xb + m * mstride + 128);
@@ -878,20 +877,20 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
 #pragma unroll
             for (int r = 0; r < R; r++)
 #pragma unroll
-              for (int m = 0; m < MM; m++) v[r][m] = group_sum_rt(acc[r][m], sc.lg2G);
+              for (int m = 0; m < MM; m++) v[r][m] = group_sum(acc[r][m]);
             // waves holding the tile: the wave of step s is (NW s + NW - 1) / S; when S < NW
             // each non-empty wave holds one step
             const int t0 = ct * sc.ns, t1 = t0 + sc.ns;
             const int w0 = (NW * t0 + NW - 1) / sc.S, wl = (NW * (t1 - 1) + NW - 1) / sc.S;
             const int parts = sc.S >= NW ? wl - w0 + 1 : sc.ns;
             bool put = parts == 1;
-            if (!put) {  // rows of the tile: r * gpw + clg, fewer than 4 R
-              float* mine = part + ((wave * 2 + (t0 >= sc.start ? 1 : 0)) * 4 * R + clg) * MM;
+            if (!put) {  // rows of the tile: r * kGpw + clg
+              float* mine = part + ((wave * 2 + (t0 >= sc.start ? 1 : 0)) * kGpw * R + clg) * MM;
               if (cg == 0) {
 #pragma unroll
                 for (int r = 0; r < R; r++)
 #pragma unroll
-                  for (int m = 0; m < MM; m++) mine[r * sc.gpw * MM + m] = v[r][m];
+                  for (int m = 0; m < MM; m++) mine[r * kGpw * MM + m] = v[r][m];
               }
               asm volatile("" ::: "memory");
               int before = 0;
@@ -902,7 +901,7 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
               if (before == parts - 1) {  // the last part in: every part is in `part`
 #pragma unroll
                 for (int r = 0; r < R; r++) {
-                  const float* p0 = part + ((w0 * 2 + 1) * 4 * R + r * sc.gpw + clg) * MM;
+                  const float* p0 = part + ((w0 * 2 + 1) * kGpw * R + r * kGpw + clg) * MM;
 #pragma unroll
                   for (int m = 0; m < MM; m++) v[r][m] = p0[m];
                 }
@@ -910,7 +909,7 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
                   if (sc.S >= NW || ((u * sc.S) >> LGW) < (((u + 1) * sc.S) >> LGW)) {
 #pragma unroll
                     for (int r = 0; r < R; r++) {
-                      const float* pu = part + ((u * 2) * 4 * R + r * sc.gpw + clg) * MM;
+                      const float* pu = part + ((u * 2) * kGpw * R + r * kGpw + clg) * MM;
 #pragma unroll
                       for (int m = 0; m < MM; m++) v[r][m] = v[r][m] + pu[m];
                     }
@@ -922,7 +921,7 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
 #pragma unroll
             for (int r = 0; r < R; r++) {
               // the output row (gate+up form: both of the lane's rows are row n)
-              const int row = GU ? ct * sc.gpw + clg : ct * R * sc.gpw + r * sc.gpw + clg;
+              const int row = GU ? ct * kGpw + clg : ct * R * kGpw + r * kGpw + clg;
               if (put && cg == 0 && row < sc.nrows) {
                 bool store = true;
                 if (sc.nchunks > 1) {  // chunk sums, added in chunk order

@@ -25,7 +25,7 @@ import torch
 
 __all__ = [
     "QK", "Q4_0_BLOCK_BYTES", "Q8_0_BLOCK_BYTES", "seed_of", "normal", "round_half_away",
-    "encode_q4_0", "encode_q8_0", "raw_q4_0", "raw_q8_0", "small_int", "router_ids",
+    "encode_q4_0", "encode_q8_0", "raw_q4_0", "raw_q8_0", "small_int", "router_ids", "router_weights",
     "DENSE27B_LAYERS", "DENSE27B_SHAPES", "DENSE27B_FUSED_SHAPES", "MOE_SHAPE", "PREFILL_SHAPE",
     "block_bytes",
 ]
@@ -167,6 +167,16 @@ def small_int(shape, key, lo: int = -8, hi: int = 8, device="cpu", dtype=torch.f
     """Integers uniform in [lo, hi] (as fp32 by default)."""
     return torch.randint(lo, hi + 1, tuple(shape), generator=_gen(key, device), device=device,
                          dtype=torch.int32).to(dtype)
+
+
+def router_weights(T: int, top_k: int, key) -> np.ndarray:
+    """Router weights [T, top_k] fp32: a softmax over top_k N(0, 1) draws per token, so
+    each token's weights are positive and sum to about 1 (the usual normalised top-k
+    gating; the pages give no weights of their own)."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed_of(*key) & 0xFFFFFFFF, 7]))
+    z = rng.standard_normal((T, top_k))
+    e = np.exp(z - z.max(axis=1, keepdims=True))
+    return np.ascontiguousarray((e / e.sum(axis=1, keepdims=True)).astype(np.float32))
 
 
 def router_ids(T: int, E: int, top_k: int, key, s: float = 1.1) -> np.ndarray:

@@ -59,9 +59,10 @@ def _load():
         lib.oracle_quantize_q8_act.argtypes = [P, I64, I64, P, P]
         lib.oracle_qmm_q8_0.argtypes = [P, P, P, I64, I64, I64, P, P, P]
         lib.oracle_qmm_q4_0.argtypes = [P, P, P, I64, I64, I64, P, P, P]
+        lib.oracle_qmv_id_sum.argtypes = [I32, P, I64, I64, I64, P, P, I64, I64, P, I64, I64, P, P]
         lib.oracle_threads.restype = I32
         lib.oracle_set_threads.argtypes = [I32]
-        for f in ("oracle_decode_row", "oracle_qmv", "oracle_qmv_id", "oracle_qmv_id_gate_up",
+        for f in ("oracle_decode_row", "oracle_qmv", "oracle_qmv_id", "oracle_qmv_id_gate_up", "oracle_qmv_id_sum",
                   "oracle_quantize_q8_act", "oracle_qmm_q8_0", "oracle_qmm_q4_0"):
             getattr(lib, f).restype = I32
         _lib = lib
@@ -123,6 +124,23 @@ def qmv_id(fmt: str, W, E: int, N: int, K: int, ids, X, x_tok_stride: int, x_slo
     S = np.empty((T, top_k, N), np.float64)
     _check(_load().oracle_qmv_id(FMT[fmt], _p(Wb), E, N, K, _p(ids32), T, top_k, _p(Xf),
                                  x_tok_stride, x_slot_stride, _p(Y), _p(S)), "qmv_id")
+    return Y, S
+
+
+def qmv_id_sum(fmt: str, W, E: int, N: int, K: int, ids, weights, X, x_tok_stride: int,
+               x_slot_stride: int):
+    """Y, S [T][N]: the router-weighted sum over each token's routed experts."""
+    Wb = _c(W, np.uint8)
+    ids32 = _c(ids, np.int32)
+    T, top_k = ids32.shape
+    wf = _c(weights, np.float32).reshape(T, top_k)
+    Xf = _c(X, np.float32).reshape(-1)
+    assert Wb.size == E * N * (K // 32) * BLOCK_BYTES[fmt]
+    Y = np.empty((T, N), np.float64)
+    S = np.empty((T, N), np.float64)
+    _check(_load().oracle_qmv_id_sum(FMT[fmt], _p(Wb), E, N, K, _p(ids32), _p(wf), T, top_k,
+                                     _p(Xf), x_tok_stride, x_slot_stride, _p(Y), _p(S)),
+           "qmv_id_sum")
     return Y, S
 
 

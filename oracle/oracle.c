@@ -159,6 +159,49 @@ int oracle_qmv_id(int fmt, const uint8_t* W, int64_t E, int64_t N, int64_t K,
   return err;
 }
 
+/* Output of a mixture-of-experts layer over the routed experts: for token t and row n,
+ *     Y[t][n] = sum_s weights[t][s] * (sum_k W[e][n][k] x_ts[k]),   e = ids[t][s] >= 0,
+ * each expert product in double over the exactly dequantized weights in index order, the
+ * slots added in order; a padding slot (negative id) adds nothing.  S[t][n] =
+ * sum_s |weights[t][s]| * sum_k |W[e][n][k] x_ts[k]|, the tolerance scale. */
+int oracle_qmv_id_sum(int fmt, const uint8_t* W, int64_t E, int64_t N, int64_t K,
+                      const int32_t* ids, const float* weights, int64_t T, int64_t top_k,
+                      const float* X, int64_t x_tok_stride, int64_t x_slot_stride, double* Y,
+                      double* S) {
+  if (K % 32 != 0 || (fmt != ORACLE_Q4_0 && fmt != ORACLE_Q8_0)) return -1;
+  const int64_t row_bytes = (K / 32) * block_bytes(fmt);
+  for (int64_t i = 0; i < T * top_k; i++)
+    if (ids[i] >= E) return -3;
+  int err = 0;
+#pragma omp parallel for collapse(2) schedule(dynamic, 4)
+  for (int64_t t = 0; t < T; t++) {
+    for (int64_t n = 0; n < N; n++) {
+      double y = 0.0, sa = 0.0;
+      double* w = (double*)malloc((size_t)(K > 0 ? K : 1) * sizeof(double));
+      if (!w) { err = -2; continue; }
+      for (int64_t s = 0; s < top_k; s++) {
+        const int32_t e = ids[t * top_k + s];
+        if (e < 0) continue;
+        oracle_decode_row(fmt, W + ((int64_t)e * N + n) * row_bytes, K, w);
+        const float* x = X + t * x_tok_stride + s * x_slot_stride;
+        double ys = 0.0, ss = 0.0;
+        for (int64_t k = 0; k < K; k++) {
+          double p = w[k] * (double)x[k];
+          ys += p;
+          ss += fabs(p);
+        }
+        const double r = (double)weights[t * top_k + s];
+        y += r * ys;
+        sa += fabs(r) * ss;
+      }
+      free(w);
+      Y[t * N + n] = y;
+      if (S) S[t * N + n] = sa;
+    }
+  }
+  return err;
+}
+
 /* silu(z) = z / (1 + e^-z), in double precision. */
 double oracle_silu(double z) { return z / (1.0 + exp(-z)); }
 

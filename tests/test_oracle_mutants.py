@@ -27,6 +27,8 @@ MUTANTS = {
     "act_signed_max": [("float v = fabsf(x[j]);", "float v = x[j];")],
     "id_slot_stride": [("s * x_slot_stride", "t * x_slot_stride")],
     "id_padding_ignored": [("if (e >= 0) {", "if (1) { const int32_t ee = e < 0 ? 0 : e; (void)ee;")],
+    "sum_unweighted": [("y += r * ys;", "y += ys;")],
+    "sum_weight_index": [("(double)weights[t * top_k + s]", "(double)weights[s]")],
     "silu_sign": [("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));")],
     "gate_up_swapped": [("y = sl * u;", "y = oracle_silu(u) * g;")],
 }

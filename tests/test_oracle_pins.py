@@ -200,6 +200,52 @@ def test_qmv_id_rejects_out_of_range_id(oracle_lib):
                           np.zeros(K, np.float32), K, 0)
 
 
+# --- router-weighted sum over each token's experts ---------------------------------------
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0"])
+def test_qmv_id_sum_bruteforce(oracle_lib, fmt):
+    """Y[t] = sum_s w[t][s] * W[e_ts] x_ts against a dense NumPy product per slot, with a
+    padding slot and one expert chosen twice by the same token."""
+    E, N, K, T, top_k = 5, 6, 96, 3, 3
+    enc = gen.encode_q4_0 if fmt == "q4_0" else gen.encode_q8_0
+    W = enc(gen.normal((E * N, K), ("idsum", fmt), std=0.05)).numpy()
+    ids = np.array([[3, 0, 3], [-1, 4, 2], [1, 3, 0]], np.int32)
+    w = gen.router_weights(T, top_k, ("idsum-w", fmt))
+    X = gen.normal((T, top_k, K), ("idsum-x", fmt)).numpy()
+    Y, S = oracle_lib.qmv_id_sum(fmt, W, E, N, K, ids, w, X, top_k * K, K)
+    Wd = _npref.dequant(fmt, W, E * N, K).reshape(E, N, K)
+    for t in range(T):
+        yr = np.zeros(N)
+        sr = np.zeros(N)
+        for s in range(top_k):
+            e = ids[t, s]
+            if e < 0:
+                continue
+            x = X[t, s].astype(np.float64)
+            yr += float(w[t, s]) * (Wd[e] @ x)
+            sr += abs(float(w[t, s])) * (np.abs(Wd[e]) @ np.abs(x))
+        assert np.all(np.abs(Y[t] - yr) <= 1e-12 * sr)
+        assert np.allclose(S[t], sr, rtol=1e-12, atol=0)
+
+
+def test_qmv_id_sum_one_hot_and_scaling(oracle_lib):
+    """One-hot weights pick one slot's expert product (equal to qmv_id's row bit for bit);
+    doubling every weight doubles every output bit for bit; all-padding tokens give 0."""
+    E, N, K, T, top_k = 4, 5, 64, 3, 2
+    W = gen.encode_q4_0(gen.normal((E * N, K), ("idsum1",), std=0.05)).numpy()
+    ids = np.array([[2, 1], [0, 3], [-1, -1]], np.int32)
+    X = gen.normal((T, top_k, K), ("idsum1-x",)).numpy()
+    Yid, _ = oracle_lib.qmv_id("q4_0", W, E, N, K, ids, X, top_k * K, K)
+    onehot = np.array([[0, 1], [1, 0], [1, 0]], np.float32)
+    Y, S = oracle_lib.qmv_id_sum("q4_0", W, E, N, K, ids, onehot, X, top_k * K, K)
+    assert np.array_equal(Y[0], Yid[0, 1]) and np.array_equal(Y[1], Yid[1, 0])
+    assert np.all(Y[2] == 0) and np.all(S[2] == 0)
+    w = gen.router_weights(T, top_k, ("idsum1-w",))
+    Y1, _ = oracle_lib.qmv_id_sum("q4_0", W, E, N, K, ids, w, X, top_k * K, K)
+    Y2, _ = oracle_lib.qmv_id_sum("q4_0", W, E, N, K, ids, 2 * w, X, top_k * K, K)
+    assert np.array_equal(Y2, 2 * Y1)
+
+
 # --- fused gate+up: silu and the product ------------------------------------------------
 
 def test_silu_closed_forms(oracle_lib):

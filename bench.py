@@ -313,6 +313,9 @@ def run_moe(args, torch, gen, bqm):
             yd = torch.empty((T, top_k, H), device="cuda")
             uniq = len(np.unique(ids.cpu().numpy()))
             layers.append((gate, up, down, ids, x, xd, yg, yu, yd, uniq))
+        # router weights and the layer outputs of the down projection with the weighted sum
+        rws = [torch.from_numpy(gen.router_weights(T, top_k, ("moe-w", l, T))).cuda() for l in range(n_layers)]
+        youts = [torch.empty((T, H), device="cuda") for _ in range(n_layers)]
 
         def run():
             for gate, up, down, ids, x, xd, yg, yu, yd, _ in layers:
@@ -355,6 +358,26 @@ def run_moe(args, torch, gen, bqm):
             fbytes.append(2 * uniq * weight_bytes("q4_0", F, H) + 4 * (T * H + T * top_k * F))
         fdur = per_launch_ms(flaunch, torch)
         f_achieved = sum(fbytes) / (fdur.sum() * 1e-3) / 1e9
+
+        # the whole layer fused: gate+up in one pass, then down with the router-weighted
+        # sum over each token's experts (its output per token) in one launch
+        def run_layer():
+            for l, (gate, up, down, ids, x, xd, yg, yu, yd, _) in enumerate(layers):
+                bqm.qmv_id_gate_up("q4_0", gate, up, E, F, H, ids, T, top_k, x, H, 0, yg)
+                bqm.qmv_id_sum("q4_0", down, E, H, F, ids, rws[l], T, top_k, yg, top_k * F, F, yd,
+                               youts[l])
+
+        ms_l = time_steps(run_layer, args.steps, args.warmup, torch, not args.no_graph)
+        abytes_l = n_layers * 4 * (T * H + 2 * T * top_k * F + 2 * T * top_k * H + T * H)
+        gbs_l = (ubytes + abytes_l) / (ms_l * 1e-3) / 1e9
+        slaunch, sbytes = [], []
+        for l, (gate, up, down, ids, x, xd, yg, yu, yd, uniq) in enumerate(layers):
+            slaunch.append(lambda w=down, i=ids, r=rws[l], x=yg, y=yd, o=youts[l]:
+                           bqm.qmv_id_sum("q4_0", w, E, H, F, i, r, T, top_k, x, top_k * F, F, y, o))
+            # expert rows, inputs, the weighted slot rows written and read back, the sums
+            sbytes.append(uniq * weight_bytes("q4_0", H, F) + 4 * (T * top_k * F + 2 * T * top_k * H + T * H))
+        sdur = per_launch_ms(slaunch, torch)
+        s_achieved = sum(sbytes) / (sdur.sum() * 1e-3) / 1e9
         out.append({"T": T, "ms_per_layer": round(ms / n_layers, 4),
                     "unique_experts_per_layer": [L[-1] for L in layers],
                     "gbs_unique_bytes": round(gbs, 1), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
@@ -372,8 +395,18 @@ def run_moe(args, torch, gen, bqm):
                                      "unit": "GB/s", "frac": round(f_achieved / HBM_PEAK_GBS, 4),
                                      "traffic": traffic_from_profiles(f"qmv_id_gate_up_q4_0_moe_t{T}"),
                                      "kernel": "k_qmv_chain gate+up form (qmv_id_gate_up)",
-                                     "avg_launch_us": round(1e3 * float(fdur.mean()), 3)}}})
-        del layers
+                                     "avg_launch_us": round(1e3 * float(fdur.mean()), 3)}},
+                    "fused_layer": {
+                        "what": "qmv_id_gate_up, then qmv_id_sum (down + router-weighted slot sum)",
+                        "ms_per_layer": round(ms_l / n_layers, 4), "gbs_unique_bytes": round(gbs_l, 1),
+                        "pct_of_hbm_peak": round(100 * gbs_l / HBM_PEAK_GBS, 2),
+                        "layer_tok_s": round(T * n_layers / (ms_l * 1e-3), 1),
+                        "roofline": {"bound": "hbm", "achieved": round(s_achieved, 1), "peak": HBM_PEAK_GBS,
+                                     "unit": "GB/s", "frac": round(s_achieved / HBM_PEAK_GBS, 4),
+                                     "traffic": traffic_from_profiles(f"qmv_id_sum_q4_0_moe_t{T}"),
+                                     "kernel": "qmv_id_sum: k_qmv_chain indexed form (weighted rows) + k_slot_sum",
+                                     "avg_launch_us": round(1e3 * float(sdur.mean()), 3)}}})
+        del layers, rws, youts
         torch.cuda.empty_cache()
     return {"metric": "MoE qmv_id achieved HBM GB/s over unique-expert bytes", "value": out[0]["gbs_unique_bytes"],
             "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,

@@ -49,6 +49,7 @@ def lib():
         L.qmv_q8_0.argtypes = [P, P, P, I, I64, I64, P]
         L.qmv_id.argtypes = [I, P, I, I64, I64, P, I, I, P, I64, I64, P, P]
         L.qmv_id_gate_up.argtypes = [I, P, P, I, I64, I64, P, I, I, P, I64, I64, P, P]
+        L.qmv_id_sum.argtypes = [I, P, I, I64, I64, P, P, I, I, P, I64, I64, P, P, P]
         L.bqm_quantize_q8_act.argtypes = [P, P, P, I64, I64, P]
         L.qmm_q8_0.argtypes = [P, P, P, P, I64, I64, I64, P]
         L.qmm_q4_0.argtypes = [P, P, P, P, I64, I64, I64, P]
@@ -120,6 +121,12 @@ def qmv_id(fmt, w_packed, E: int, N: int, K: int, ids, T: int, top_k: int, X,
            x_tok_stride: int, x_slot_stride: int, Y, stream=None):
     _call("qmv_id", _fmt(fmt), _ptr(w_packed), E, N, K, _ptr(ids), T, top_k, _ptr(X),
           x_tok_stride, x_slot_stride, _ptr(Y), _stream(stream))
+
+
+def qmv_id_sum(fmt, w_packed, E: int, N: int, K: int, ids, weights, T: int, top_k: int, X,
+               x_tok_stride: int, x_slot_stride: int, Y_slots, Y, stream=None):
+    _call("qmv_id_sum", _fmt(fmt), _ptr(w_packed), E, N, K, _ptr(ids), _ptr(weights), T, top_k,
+          _ptr(X), x_tok_stride, x_slot_stride, _ptr(Y_slots), _ptr(Y), _stream(stream))
 
 
 def qmv_id_gate_up(fmt, w_gate, w_up, E: int, N: int, K: int, ids, T: int, top_k: int, X,

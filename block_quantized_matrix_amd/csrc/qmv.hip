@@ -184,6 +184,7 @@ struct IdxArgs {
   const uint16_t* up_scales;  // ... and scales; the gate tensor is `one.w`
   int E, TS, top_k;        // experts; slots T * top_k; slots per token
   int64_t xts, xss;        // input strides (floats) per token and per slot
+  const float* rw;         // indexed form: router weights [T][top_k] the rows are scaled by, or null
 };
 
 struct ChainArgs {
@@ -737,6 +738,9 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
   const char* lds_last = xlds;   // ... its block at the tile's last step (past K: the last block)
   int cg = 0, clg = 0;
   float acc[R][MM];
+  float wslot[MM];  // weighted-sum form: the router weights of the current group's slots
+#pragma unroll
+  for (int m = 0; m < MM; m++) wslot[m] = 1.0f;
 #pragma unroll
   for (int r = 0; r < R; r++)
 #pragma unroll
@@ -779,6 +783,12 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
     // order over the values as staged (Q4_0 positions 16..31 divided by 16, multiplied back
     // exactly); a wave's LDS accesses complete in order, so its own stores are visible to
     // its reads.  Inputs m >= M are staged as zeros (their results are not stored).
+    if constexpr (IDX && !GU) {  // read here, off the store path (the staging waits anyway)
+      if (a.ix.rw) {
+#pragma unroll
+        for (int m = 0; m < MM; m++) wslot[m] = m < sc.M ? a.ix.rw[slot_of(sc, m)] : 0.0f;
+      }
+    }
     const int nch = sc.nbc * 8;
 #pragma unroll
     for (int m = 0; m < MM; m++) {
@@ -938,12 +948,15 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
                   for (int m = 0; m < MM; m++)
                     if (m < sc.M) {  // agent-coherent: a later GEMV may read it
                       float out = v[r][m];
+                      const int ts = slot_of(sc, m);
                       if constexpr (GU) {  // silu(g) * u, g the gate row's sum
                         const float g = v[0][m];
                         out = g / (1.0f + expf(-g)) * v[1][m];
+                      } else if constexpr (IDX) {
+                        if (a.ix.rw) out = out * wslot[m];  // router weight of the slot
                       }
                       __hip_atomic_store((__attribute__((address_space(1))) float*)sc.y +
-                                             (int64_t)slot_of(sc, m) * sc.ystride + row,
+                                             (int64_t)ts * sc.ystride + row,
                                          out, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     }
                 }
@@ -1098,7 +1111,7 @@ int launch_chain(int fmt, int mm, const GemvDesc* descs, const int64_t* seg, con
   a.kc = kc;
   a.pacc_rows = pacc_rows;
   a.sync = sync;
-  if (ix) a.ix = *ix; else a.ix = IdxArgs{nullptr, nullptr, nullptr, nullptr, 0, 0, 0, 0, 0};
+  if (ix) a.ix = *ix; else a.ix = IdxArgs{nullptr, nullptr, nullptr, nullptr, 0, 0, 0, 0, 0, nullptr};
   const int mode = ix ? (ix->up ? 2 : 1) : 0;
   ChainKernel k = chain_kernel(fmt, mm, mode);
   // per kernel: 1 = its static LDS fits the reserve, -1 = it does not
@@ -1250,7 +1263,7 @@ int launch_qmv(int fmt, const void* w, const float* X, float* Y, int M, int64_t 
 // and up row n of the expert, and the output is silu(gate) * up.
 static int launch_id(int fmt, const void* w, const void* w_up, int E, int64_t N, int64_t K,
               const int32_t* ids, int T, int top_k, const float* X, int64_t xts, int64_t xss,
-              float* Y, hipStream_t s) {
+              float* Y, hipStream_t s, const float* rw = nullptr) {
   const int TS = T * top_k;
   Layout L;
   layout_of(fmt, (int64_t)E * N, K, &L);
@@ -1270,7 +1283,7 @@ static int launch_id(int fmt, const void* w, const void* w_up, int E, int64_t N,
   const uint8_t* up = static_cast<const uint8_t*>(w_up);
   const IdxArgs ix{ids, reinterpret_cast<const uint16_t*>(codes + L.scales_off), up,
                    up ? reinterpret_cast<const uint16_t*>(up + L.scales_off) : nullptr,
-                   E, TS, top_k, xts, xss};
+                   E, TS, top_k, xts, xss, rw};
   const GemvDesc d{codes, X, Y, N, K, fmt, 0, 1, 0};
   return launch_chain(fmt, mm, nullptr, nullptr, &d, 1, kc, pacc_rows, nullptr, false, s, &ix);
 }
@@ -1284,6 +1297,37 @@ int launch_qmv_id_gate_up(int fmt, const void* w_gate, const void* w_up, int E, 
                           const int32_t* ids, int T, int top_k, const float* X, int64_t xts,
                           int64_t xss, float* Y, hipStream_t s) {
   return launch_id(fmt, w_gate, w_up, E, N, K, ids, T, top_k, X, xts, xss, Y, s);
+}
+
+// Y[t][n] = sum over s < top_k of Y_slots[t][s][n], s ascending, fp32: one thread per (t, n),
+// the slots' loads in flight together, eight at a time.
+__global__ __launch_bounds__(256) void k_slot_sum(const float* __restrict__ ys, float* __restrict__ y,
+                                                  int64_t N, int64_t TN, int top_k) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= TN) return;
+  const int64_t t = i / N, n = i - t * N;
+  const float* p = ys + t * top_k * N + n;
+  float sum = 0.0f;
+  for (int kb = 0; kb < top_k; kb += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) v[j] = kb + j < top_k ? p[(int64_t)(kb + j) * N] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; j++)
+      if (kb + j < top_k) sum = kb + j == 0 ? v[j] : sum + v[j];
+  }
+  y[i] = sum;
+}
+
+int launch_qmv_id_sum(int fmt, const void* w, int E, int64_t N, int64_t K, const int32_t* ids,
+                      const float* rw, int T, int top_k, const float* X, int64_t xts, int64_t xss,
+                      float* Y_slots, float* Y, hipStream_t s) {
+  if (int st = launch_id(fmt, w, nullptr, E, N, K, ids, T, top_k, X, xts, xss, Y_slots, s, rw))
+    return st;
+  const int64_t TN = (int64_t)T * N;
+  hipLaunchKernelGGL(k_slot_sum, dim3((unsigned)((TN + 255) / 256)), dim3(256), 0, s, Y_slots, Y, N,
+                     TN, top_k);
+  return launch_status();
 }
 
 }  // namespace bqm

@@ -126,6 +126,24 @@ int qmv_id_gate_up(int fmt, const void* w_gate, const void* w_up, int E, int64_t
                    const int32_t* ids, int T, int top_k, const float* X, int64_t x_tok_stride,
                    int64_t x_slot_stride, float* Y, hipStream_t stream);
 
+/* Expert-indexed GEMV with the router-weighted sum over each token's slots: the output of
+ * a mixture-of-experts feed-forward layer (the top-k routed experts of the page
+ * "ik_llama.cpp 老工作站多 GPU 部署 Qwen3-235B-A22B 实战指南" (nxmr.cn), background
+ * section), its small decode-time steps merged as the "llama.cpp-v100" README
+ * (shadowgraph.io) describes in its kernels-and-runtime list: the weighting is done in the
+ * product's store, the sum by one small kernel after it.  Read as
+ *     Y_slots[t][s][n] = weights[t][s] * sum_k dequant(W)[e][n][k] * x_ts[k]
+ *     Y[t][n]          = sum_{s < top_k} Y_slots[t][s][n]     (fp32, s ascending)
+ * with e, x_ts, padding and out-of-range ids as in qmv_id: a padding slot's row is 0 (it
+ * adds 0), an id >= E gives a NaN row (Y[t][n] is NaN).  Deterministic.
+ * weights: fp32 [T][top_k], 4-byte aligned.  Y_slots: fp32 [T][top_k][N] (device memory
+ * the caller owns; written as qmv_id's Y, scaled by the weights).  Y: fp32 [T][N], 16-byte
+ * aligned, not overlapping Y_slots.  top_k = 0 writes Y = 0.  Limits and status codes as
+ * qmv_id; a null or misaligned weights pointer: BQM_E_NULL / BQM_E_ALIGN. */
+int qmv_id_sum(int fmt, const void* w_packed, int E, int64_t N, int64_t K, const int32_t* ids,
+               const float* weights, int T, int top_k, const float* X, int64_t x_tok_stride,
+               int64_t x_slot_stride, float* Y_slots, float* Y, hipStream_t stream);
+
 /* ---- chains of GEMVs in one launch ----------------------------------------------------
  * Decode runs one GEMV after another, each reading the previous one's output (through
  * the layers' other operations); launching them one by one pays a kernel start and drain

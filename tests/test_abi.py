@@ -23,7 +23,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("bqm_packed_bytes", "bqm_repack", "bqm_unpack", "qmv_q4_0", "qmv_q8_0", "qmv_id",
-              "qmv_id_gate_up", "bqm_quantize_q8_act", "qmm_q8_0", "qmm_q4_0", "bqm_strerror"):
+              "qmv_id_gate_up", "qmv_id_sum", "bqm_quantize_q8_act", "qmm_q8_0", "qmm_q4_0", "bqm_strerror"):
         assert n in names
 
 
@@ -93,6 +93,14 @@ def test_host_validation_before_launch():
     assert L.qmv_id_gate_up(2, GOOD, ODD, 4, 8, 64, GOOD, 1, 2, GOOD, 64, 0, GOOD, None) == 3
     assert L.qmv_id_gate_up(2, None, GOOD, 4, 8, 64, GOOD, 1, 2, GOOD, 64, 0, GOOD, None) == 1
     assert L.qmv_id_gate_up(2, GOOD, GOOD, 4, 8, 64, GOOD, 1, 2, GOOD, 66, 0, GOOD, None) == 3
+    # qmv_id_sum: qmv_id's checks, then Y, the weights and the counters
+    assert L.qmv_id_sum(5, GOOD, 4, 8, 64, GOOD, GOOD, 1, 2, GOOD, 64, 0, GOOD, GOOD, None) == 4
+    assert L.qmv_id_sum(2, GOOD, 4, 8, 64, GOOD, GOOD, 65, 2, GOOD, 64, 0, GOOD, GOOD, None) == 2
+    assert L.qmv_id_sum(2, GOOD, 4, 8, 64, GOOD, GOOD, 1, 2, GOOD, 64, 0, GOOD, None, None) == 1
+    assert L.qmv_id_sum(2, GOOD, 4, 8, 64, GOOD, GOOD, 1, 2, GOOD, 64, 0, GOOD, ODD, None) == 3
+    assert L.qmv_id_sum(2, GOOD, 4, 8, 64, GOOD, None, 1, 2, GOOD, 64, 0, GOOD, GOOD, None) == 1
+    assert L.qmv_id_sum(2, GOOD, 4, 8, 64, GOOD, P(0x100002), 1, 2, GOOD, 64, 0, GOOD, GOOD, None) == 3
+    assert L.qmv_id_sum(2, GOOD, 4, 8, 64, None, GOOD, 1, 2, GOOD, 64, 0, GOOD, GOOD, None) == 1
     # quantizer and qmm
     assert L.bqm_quantize_q8_act(GOOD, GOOD, GOOD, 4, 40, None) == 2
     assert L.bqm_quantize_q8_act(GOOD, None, GOOD, 4, 64, None) == 1
@@ -114,6 +122,7 @@ def test_empty_sizes_are_no_ops():
     assert L.qmv_q4_0(None, None, None, 1, 0, 64, None) == 0
     assert L.qmv_id(2, None, 4, 8, 64, None, 0, 8, None, 64, 0, None, None) == 0
     assert L.qmv_id_gate_up(2, None, None, 4, 8, 64, None, 0, 8, None, 64, 0, None, None) == 0
+    assert L.qmv_id_sum(2, None, 4, 8, 64, None, None, 0, 8, None, 64, 0, None, None, None) == 0
     assert L.bqm_quantize_q8_act(None, None, None, 0, 64, None) == 0
     assert L.qmm_q8_0(None, None, None, None, 0, 8, 64, None) == 0
     assert L.qmm_q4_0(None, None, None, None, 4, 0, 64, None) == 0

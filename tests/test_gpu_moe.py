@@ -259,3 +259,122 @@ def test_gate_up_empty_k_and_matches_separate_calls():
     sep = host(torch.nn.functional.silu(Yg) * Yu).astype(np.float64)
     check_close(host(Yf), sep, S, "fused vs separate")
     check_close(host(Yf), Yr, S, "fused vs oracle")
+
+
+# --- router-weighted sum over each token's slots -------------------------------------------
+
+def run_sum(fmt, E, N, K, ids_np, X, xts, xss, key, w_np=None):
+    T, top_k = ids_np.shape
+    Wi = weights(fmt, E * N, K, key)
+    Wp = packed(fmt, Wi, E * N, K)
+    if w_np is None:
+        w_np = gen.router_weights(T, top_k, key + ("w",))
+    ids = torch.from_numpy(ids_np).to(DEV)
+    w = torch.from_numpy(w_np).to(DEV)
+    Ys = torch.full((T, top_k, N), -7.0, device=DEV)
+    Y = torch.full((T, N), -7.0, device=DEV)
+    bqm.qmv_id_sum(fmt, Wp, E, N, K, ids, w, T, top_k, X, xts, xss, Ys, Y)
+    ids_ok = np.where(ids_np >= E, -1, ids_np).astype(np.int32)
+    Yr, S = oracle.qmv_id_sum(fmt, host(Wi), E, N, K, ids_ok, w_np, host(X).reshape(-1), xts, xss)
+    Yid, Sid = oracle.qmv_id(fmt, host(Wi), E, N, K, ids_ok, host(X).reshape(-1), xts, xss)
+    return host(Ys), host(Y), Yr, S, Yid, Sid, w_np
+
+
+def slot_sum_fp32(ys, ids_np, E):
+    """The weighted sum as the kernel defines it: fp32, slots in order, padding 0, bad NaN."""
+    T, top_k, N = ys.shape
+    out = np.zeros((T, N), np.float32)
+    for t in range(T):
+        acc = None
+        for s in range(top_k):
+            e = ids_np[t, s]
+            v = np.full(N, np.nan, np.float32) if e >= E else (np.zeros(N, np.float32) if e < 0 else ys[t, s])
+            acc = v.copy() if acc is None else (acc + v).astype(np.float32)
+        out[t] = acc
+    return out
+
+
+def check_sum(ys, y, Yr, S, Yid, Sid, w_np, ids_np, E, what):
+    T, top_k = ids_np.shape
+    valid = (ids_np >= 0) & (ids_np < E)
+    wb = w_np.astype(np.float64)[:, :, None]
+    check_close(ys[valid], (wb * Yid)[valid], (np.abs(wb) * Sid)[valid], what + " slots")
+    assert np.array_equal(y.view(np.uint32), slot_sum_fp32(ys, ids_np, E).view(np.uint32)), what
+    ok = ~np.any(ids_np >= E, axis=1)
+    check_close(y[ok], Yr[ok], S[ok], what)
+    assert np.all(np.isnan(y[~ok]))
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0"])
+@pytest.mark.parametrize("E,N,K", [(5, 37, 96), (3, 300, 1536), (9, 130, 4096)])
+def test_qmv_id_sum_small(fmt, E, N, K):
+    say("qmv_id_sum small", fmt, E, N, K)
+    ids = np.array([[3, 0, 4], [-1, 4, 2], [1, 3, -1], [0, 0, 4]], np.int32) % max(E, 1)
+    ids[1, 0] = -1
+    ids[2, 2] = -1
+    T, top_k = ids.shape
+    X = gen.normal((T, top_k, K), ("sum-x", K), device=DEV)
+    r = run_sum(fmt, E, N, K, ids, X, top_k * K, K, ("sum", fmt, E, N, K))
+    check_sum(*r, ids, E, f"qmv_id_sum {fmt} {E}x{N}x{K}")
+
+
+@pytest.mark.parametrize("T", [1, 16])
+def test_qmv_id_sum_moe_down(T):
+    """The MoE layer's down projection (4096 x 1536 per expert, 128 experts, top-8) with
+    the router weights: the layer's output per token."""
+    sh = gen.MOE_SHAPE
+    E, top_k, N, K = sh["E"], sh["top_k"], sh["hidden"], sh["ffn"]
+    ids = gen.router_ids(T, E, top_k, ("moe-router", T))
+    X = gen.normal((T, top_k, K), ("sum-moe-x", T), device=DEV)
+    say("qmv_id_sum moe down", T)
+    r = run_sum("q4_0", E, N, K, ids, X, top_k * K, K, ("sum-moe",))
+    check_sum(*r, ids, E, f"moe down sum T={T}")
+
+
+def test_qmv_id_sum_bad_ids_empty_k_and_no_slots():
+    """An id >= E makes its token's sum NaN; K = 0 gives 0 for tokens with valid slots;
+    top_k = 0 gives 0 everywhere."""
+    E, N, K = 3, 70, 64
+    ids = np.array([[0, 3], [2, -1], [-1, -1]], np.int32)
+    X = gen.normal((3, 2, K), ("sum-bad-x",), device=DEV)
+    r = run_sum("q4_0", E, N, K, ids, X, 2 * K, K, ("sum-bad",))
+    check_sum(*r, ids, E, "bad ids")
+    y = r[1]
+    assert np.all(np.isnan(y[0])) and np.all(y[2] == 0)
+    idd = torch.from_numpy(ids).to(DEV)
+    w = torch.ones((3, 2), device=DEV)
+    W = torch.zeros(256, dtype=torch.uint8, device=DEV)
+    Ys = torch.full((3, 2, N), -7.0, device=DEV)
+    Y = torch.full((3, N), -7.0, device=DEV)
+    bqm.qmv_id_sum("q4_0", W, E, N, 0, idd, w, 3, 2, X, 0, 0, Ys, Y)
+    y = host(Y)
+    assert np.all(np.isnan(y[0])) and np.all(y[1] == 0) and np.all(y[2] == 0)
+    Y.fill_(-7.0)
+    bqm.qmv_id_sum("q4_0", W, E, N, 64, idd, w, 3, 0, X, 0, 0, Ys, Y)
+    assert torch.count_nonzero(Y).item() == 0
+
+
+def test_qmv_id_sum_maximum_slots_and_repeat():
+    """T = 64 tokens x top_k = 32 over crowded experts (the slot limits), with padding; two
+    calls in a row give bit-identical outputs."""
+    E, N, K, T, top_k = 256, 200, 128, bqm.QMV_ID_MAX_T, bqm.QMV_ID_MAX_TOPK
+    rng = np.random.default_rng(11)
+    ids = (rng.integers(0, 16, size=(T, top_k)) * 16).astype(np.int32)
+    ids[1::7, 2] = -1
+    X = gen.normal((T, top_k, K), ("sum-max-x",), device=DEV)
+    say("qmv_id_sum max slots")
+    r1 = run_sum("q4_0", E, N, K, ids, X, top_k * K, K, ("sum-max",))
+    check_sum(*r1, ids, E, "max slots")
+    r2 = run_sum("q4_0", E, N, K, ids, X, top_k * K, K, ("sum-max",))
+    assert np.array_equal(r1[1].view(np.uint32), r2[1].view(np.uint32))
+
+
+def test_qmv_id_sum_matches_weighted_qmv_id():
+    """The fused sum equals the fp32 slot sum of qmv_id's rows times the weights, to the
+    tolerance, for a ragged N (not a multiple of 64) and long K (chunked)."""
+    E, N, K, T, top_k = 6, 1000, 16384, 3, 4
+    ids = gen.router_ids(T, E, top_k, ("sum-vs",))
+    X = gen.normal((T, top_k, K), ("sum-vs-x",), device=DEV)
+    say("qmv_id_sum vs qmv_id")
+    r = run_sum("q8_0", E, N, K, ids, X, top_k * K, K, ("sum-vs",))
+    check_sum(*r, ids, E, "vs qmv_id")

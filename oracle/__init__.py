@@ -60,10 +60,11 @@ def _load():
         lib.oracle_qmm_q8_0.argtypes = [P, P, P, I64, I64, I64, P, P, P]
         lib.oracle_qmm_q4_0.argtypes = [P, P, P, I64, I64, I64, P, P, P]
         lib.oracle_qmv_id_sum.argtypes = [I32, P, I64, I64, I64, P, P, I64, I64, P, I64, I64, P, P]
+        lib.oracle_qmm_id.argtypes = [I32, P, I64, I64, I64, P, I64, I64, P, P, I64, I64, P, P]
         lib.oracle_threads.restype = I32
         lib.oracle_set_threads.argtypes = [I32]
         for f in ("oracle_decode_row", "oracle_qmv", "oracle_qmv_id", "oracle_qmv_id_gate_up", "oracle_qmv_id_sum",
-                  "oracle_quantize_q8_act", "oracle_qmm_q8_0", "oracle_qmm_q4_0"):
+                  "oracle_quantize_q8_act", "oracle_qmm_q8_0", "oracle_qmm_q4_0", "oracle_qmm_id"):
             getattr(lib, f).restype = I32
         _lib = lib
     return _lib
@@ -201,3 +202,18 @@ def qmm_q4_0(W, Xq, dx, N: int, K: int, want_isum: bool = False):
     _check(_load().oracle_qmm_q4_0(_p(Wb), _p(Xq8), _p(dxf), M, N, K, _p(isum), _p(Y), _p(S)),
            "qmm_q4_0")
     return (Y, S, isum) if want_isum else (Y, S)
+
+
+def qmm_id(fmt: str, W, E: int, N: int, K: int, ids, Xq, dx, x_tok_rows: int, x_slot_rows: int):
+    """Y, S [T][top_k][N] of the expert-indexed prefill product (negative id -> zero row)."""
+    Wb = _c(W, np.uint8)
+    ids32 = _c(ids, np.int32)
+    T, top_k = ids32.shape
+    Xq8 = _c(Xq, np.int8).reshape(-1, K)
+    dxf = _c(dx, np.float32).reshape(Xq8.shape[0], K // 32)
+    assert Wb.size == E * N * (K // 32) * BLOCK_BYTES[fmt]
+    Y = np.empty((T, top_k, N), np.float64)
+    S = np.empty((T, top_k, N), np.float64)
+    _check(_load().oracle_qmm_id(FMT[fmt], _p(Wb), E, N, K, _p(ids32), T, top_k, _p(Xq8), _p(dxf),
+                                 x_tok_rows, x_slot_rows, _p(Y), _p(S)), "qmm_id")
+    return Y, S

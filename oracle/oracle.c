@@ -362,3 +362,37 @@ int oracle_qmm_q4_0(const uint8_t* W, const int8_t* Xq, const float* dx, int64_t
   }
   return 0;
 }
+
+/* Expert-indexed prefill product (the prefill counterpart of oracle_qmv_id): for slot
+ * (t, s) with expert e = ids[t][s] >= 0 and input row r = t * x_tok_rows + s * x_slot_rows
+ * of the quantized activations, the prefill product of that one row with expert e's
+ * N x K matrix (oracle_qmm_q8_0 / oracle_qmm_q4_0 with M = 1):
+ *   Y[t][s][n] = sum_b d_w[e][n][b] * dx[r][b] * sum_j qw[e][n][32b+j] * Xq[r][32b+j].
+ * A padding slot (negative id) gives a zero row; an id >= E is rejected. */
+int oracle_qmm_id(int fmt, const uint8_t* W, int64_t E, int64_t N, int64_t K, const int32_t* ids,
+                  int64_t T, int64_t top_k, const int8_t* Xq, const float* dx, int64_t x_tok_rows,
+                  int64_t x_slot_rows, double* Y, double* S) {
+  if (K % 32 != 0 || (fmt != ORACLE_Q4_0 && fmt != ORACLE_Q8_0)) return -1;
+  const int64_t nb = K / 32, row_bytes = nb * block_bytes(fmt);
+  for (int64_t i = 0; i < T * top_k; i++)
+    if (ids[i] >= E) return -3;
+  for (int64_t ts = 0; ts < T * top_k; ts++) {
+    const int64_t t = ts / top_k, s = ts % top_k;
+    const int32_t e = ids[ts];
+    double* y = Y + ts * N;
+    double* sa = S ? S + ts * N : NULL;
+    if (e < 0) {
+      for (int64_t n = 0; n < N; n++) {
+        y[n] = 0.0;
+        if (sa) sa[n] = 0.0;
+      }
+      continue;
+    }
+    const int64_t r = t * x_tok_rows + s * x_slot_rows;
+    const uint8_t* We = W + (int64_t)e * N * row_bytes;
+    const int st = fmt == ORACLE_Q8_0 ? oracle_qmm_q8_0(We, Xq + r * K, dx + r * nb, 1, N, K, NULL, y, sa)
+                                      : oracle_qmm_q4_0(We, Xq + r * K, dx + r * nb, 1, N, K, NULL, y, sa);
+    if (st != 0) return st;
+  }
+  return 0;
+}

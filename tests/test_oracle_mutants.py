@@ -23,6 +23,9 @@ MUTANTS = {
                                "const int32_t lo = (qs[j] & 0x0f), hi = ((qs[j] >> 4) & 0x0f);")],
     "qmm_q4_halves_swapped": [("lo * (int32_t)qx[j] + hi * (int32_t)qx[j + 16]",
                                "hi * (int32_t)qx[j] + lo * (int32_t)qx[j + 16]")],
+    "qmm_id_slot_row": [("const int64_t r = t * x_tok_rows + s * x_slot_rows;",
+                         "const int64_t r = t * x_tok_rows;")],
+    "qmm_id_expert_offset": [("W + (int64_t)e * N * row_bytes;", "W + (int64_t)e * row_bytes;")],
     "act_round_to_even": [("roundf(x[j] / d)", "rintf(x[j] / d)")],
     "act_signed_max": [("float v = fabsf(x[j]);", "float v = x[j];")],
     "id_slot_stride": [("s * x_slot_stride", "t * x_slot_stride")],

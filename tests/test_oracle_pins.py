@@ -402,6 +402,37 @@ def test_qmm_q4_matches_qmv_on_dequantized_activations(oracle_lib):
     assert np.array_equal(Y, Y2)
 
 
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_0"])
+@pytest.mark.parametrize("rows", ["broadcast", "per_slot"])
+def test_qmm_id_bruteforce(oracle_lib, fmt, rows):
+    """Expert-indexed prefill product: per slot, exact block sums of the selected expert's
+    codes with the slot's input row (NumPy decode), scaled in fp64; padding slots 0."""
+    E, N, K, T, top_k = 4, 5, 96, 3, 2
+    raw = gen.raw_q8_0 if fmt == "q8_0" else gen.raw_q4_0
+    codes = (-127, 127) if fmt == "q8_0" else (0, 15)
+    W = raw(E * N, K, ("qmmid", fmt), scales=(0.001, 0.0173, -0.02), codes=codes).numpy()
+    ids = np.array([[3, 0], [-1, 2], [1, 3]], np.int32)
+    nrows, xt, xs = (T, 1, 0) if rows == "broadcast" else (T * top_k, top_k, 1)
+    rng = np.random.default_rng(13)
+    Xq = rng.integers(-127, 128, size=(nrows, K), dtype=np.int8)
+    dx = (rng.random((nrows, K // 32)) * 0.05).astype(np.float32)
+    Y, S = oracle_lib.qmm_id(fmt, W, E, N, K, ids, Xq, dx, xt, xs)
+    nb = K // 32
+    bb = 34 if fmt == "q8_0" else 18
+    for t in range(T):
+        for s in range(top_k):
+            e = ids[t, s]
+            if e < 0:
+                assert np.all(Y[t, s] == 0) and np.all(S[t, s] == 0)
+                continue
+            r = t * xt + s * xs
+            We = W.reshape(E, N * nb * bb)[e]
+            isum = (_npref.qmm_isum if fmt == "q8_0" else _npref.qmm_q4_isum)(We, Xq[r:r + 1], N, K)[0]
+            dw = (_npref.q8_scales if fmt == "q8_0" else _npref.q4_scales)(We, N, K)
+            yr = (dw * dx[r].astype(np.float64)[None, :] * isum).sum(axis=1)
+            assert np.all(np.abs(Y[t, s] - yr) <= 1e-12 * S[t, s])
+
+
 def test_qmm_matches_qmv_on_dequantized_activations(oracle_lib):
     """qmm with activations dx*qx equals the fp64 product of the Q8_0 weights with them."""
     M, N, K = 2, 3, 64

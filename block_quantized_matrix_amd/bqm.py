@@ -21,6 +21,7 @@ Q8_0 = 8
 FMT = {"q4_0": Q4_0, "q8_0": Q8_0}
 QMV_MAX_M = 8
 QMV_ID_MAX_T = 64
+QMM_ID_MAX_T = 16384
 QMV_ID_MAX_TOPK = 32
 QMV_ID_MAX_E = 4096
 
@@ -53,6 +54,7 @@ def lib():
         L.bqm_quantize_q8_act.argtypes = [P, P, P, I64, I64, P]
         L.qmm_q8_0.argtypes = [P, P, P, P, I64, I64, I64, P]
         L.qmm_q4_0.argtypes = [P, P, P, P, I64, I64, I64, P]
+        L.qmm_id.argtypes = [I, P, I, I64, I64, P, I, I, P, P, I64, I64, P, P]
         L.bqm_chain_workspace_bytes.argtypes = [I]
         L.bqm_chain_workspace_bytes.restype = SZ
         L.bqm_chain_prepare.argtypes = [P, I, P, P]
@@ -145,6 +147,12 @@ def qmm_q8_0(w_packed, Xq, dx, Y, M: int, N: int, K: int, stream=None):
 
 def qmm_q4_0(w_packed, Xq, dx, Y, M: int, N: int, K: int, stream=None):
     _call("qmm_q4_0", _ptr(w_packed), _ptr(Xq), _ptr(dx), _ptr(Y), M, N, K, _stream(stream))
+
+
+def qmm_id(fmt, w_packed, E: int, N: int, K: int, ids, T: int, top_k: int, Xq, dx,
+           x_tok_rows: int, x_slot_rows: int, Y, stream=None):
+    _call("qmm_id", _fmt(fmt), _ptr(w_packed), E, N, K, _ptr(ids), T, top_k, _ptr(Xq), _ptr(dx),
+          x_tok_rows, x_slot_rows, _ptr(Y), _stream(stream))
 
 
 class Gemv(ctypes.Structure):

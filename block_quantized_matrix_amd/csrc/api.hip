@@ -184,6 +184,30 @@ int qmm_q4_0(const void* w_packed, const int8_t* Xq, const float* dx, float* Y, 
   return qmm_common(BQM_Q4_0, w_packed, Xq, dx, Y, M, N, K, stream);
 }
 
+int qmm_id(int fmt, const void* w_packed, int E, int64_t N, int64_t K, const int32_t* ids, int T,
+           int top_k, const int8_t* Xq, const float* dx, int64_t x_tok_rows, int64_t x_slot_rows,
+           float* Y, hipStream_t stream) {
+  if (E < 0 || T < 0 || top_k < 0 || T > BQM_QMM_ID_MAX_T || top_k > BQM_QMV_ID_MAX_TOPK ||
+      E > BQM_QMV_ID_MAX_E)
+    return BQM_E_SHAPE;
+  if (N < 0 || (int64_t)E * N > kMaxRows) return BQM_E_SHAPE;
+  if (int st = check_shape(fmt, (int64_t)E * N, K)) return st;
+  if (x_tok_rows < 0 || x_slot_rows < 0) return BQM_E_SHAPE;
+  if (T > 0 && top_k > 0 &&
+      (int64_t)(T - 1) * x_tok_rows + (int64_t)(top_k - 1) * x_slot_rows >= ((int64_t)1 << 31))
+    return BQM_E_SHAPE;
+  if (T == 0 || top_k == 0 || N == 0) return BQM_OK;
+  if (!Y || !ids) return BQM_E_NULL;
+  if (!aligned16(Y) || !aligned16(ids)) return BQM_E_ALIGN;
+  if (K > 0 && E > 0) {
+    if (int st = check_ptr(w_packed)) return st;
+    if (int st = check_ptr(Xq)) return st;
+    if (int st = check_ptr(dx)) return st;
+  }
+  return launch_qmm_id(fmt, w_packed, E, N, K, ids, T, top_k, Xq, dx, x_tok_rows, x_slot_rows, Y,
+                       stream);
+}
+
 size_t bqm_chain_workspace_bytes(int n) { return chain_workspace_bytes(n); }
 
 int bqm_chain_prepare(const bqm_gemv* descs, int n, void* workspace, hipStream_t stream) {

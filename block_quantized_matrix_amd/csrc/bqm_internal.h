@@ -65,6 +65,9 @@ int launch_qmm_q8_0(const void* w, const int8_t* Xq, const float* dx, float* Y, 
                     int64_t N, int64_t K, hipStream_t s);
 int launch_qmm_q4_0(const void* w, const int8_t* Xq, const float* dx, float* Y, int64_t M,
                     int64_t N, int64_t K, hipStream_t s);
+int launch_qmm_id(int fmt, const void* w, int E, int64_t N, int64_t K, const int32_t* ids, int T,
+                  int top_k, const int8_t* Xq, const float* dx, int64_t x_tok_rows,
+                  int64_t x_slot_rows, float* Y, hipStream_t s);
 int launch_fill(float* y, int64_t n, float v, hipStream_t s);
 int64_t chain_max_k();
 size_t chain_workspace_bytes(int n);

@@ -115,60 +115,58 @@ __device__ __forceinline__ void expand_q4(const u32x4& q, u32x4& lo, u32x4& hi) 
   }
 }
 
-// One workgroup tile of Y.  FMT selects how the weight codes arrive: Q8_0 as int8 rows
-// [N][K]; Q4_0 as 16-byte blocks [N][nb][16], expanded to int8 while they are staged, so
-// that the LDS layout and everything after it are the same for both.
-template <int FMT>
-__device__ __forceinline__ void qmm_tile(const uint8_t* __restrict__ Wc, const uint16_t* __restrict__ Wd,
+// One workgroup tile of Y: TBM = 64 MI rows (m) by BN columns (n).  FMT selects how the
+// weight codes arrive: Q8_0 as int8 rows [N][K]; Q4_0 as 16-byte blocks [N][nb][16],
+// expanded to int8 while they are staged, so that the LDS layout and everything after it
+// are the same for both.  Rows: dense (GATHER false), tile row r is input and output row
+// m0 + r (< M); gathered, tile row r reads input row xrow[r] and writes output row yrow[r]
+// (LDS tables, -1 past the tile's rows).
+template <int FMT, int MI, bool GATHER>
+__device__ __forceinline__ void qmm_core(const uint8_t* __restrict__ Wc, const uint16_t* __restrict__ Wd,
                                          const int8_t* __restrict__ Xq, const float* __restrict__ dx,
-                                         float* __restrict__ Y, int M, int N, int nb, int tiles_m,
-                                         int tiles_n) {
+                                         float* __restrict__ Y, int N, int nb, int n0, int m0, int M,
+                                         const int* xrow, const int* yrow, int8_t* sA, int8_t* sB,
+                                         u32x4* sXs, u32x4* sWs) {
   constexpr bool Q4 = FMT == BQM_Q4_0;
-  constexpr int NPB = Q4 ? 2 : 4;   // 16-byte pieces of weight codes per thread and stage
-  __shared__ __attribute__((aligned(16))) int8_t sA[BM * ROWB];
-  __shared__ __attribute__((aligned(16))) int8_t sB[BN * ROWB];
-  __shared__ u32x4 sXs[BKB * BM + 1];  // dx operands per (block, m); the last: zeros
-  __shared__ u32x4 sWs[BKB * BN];      // dw operands per (block, n)
-
-  // Workgroups are dealt round-robin to the eight XCDs; give the workgroups of one XCD
-  // neighbouring tiles (all m-tiles of a few n-tiles) so they share W rows in that L2.
-  const int nwg = tiles_m * tiles_n;
-  const int bid = blockIdx.x;
-  int tile = bid;
-  if (nwg % 8 == 0) tile = (bid % 8) * (nwg / 8) + bid / 8;
-  const int tm = tile % tiles_m, tn = tile / tiles_m;
-  const int m0 = tm * BM, n0 = tn * BN;
+  constexpr int TBM = 64 * MI;
+  constexpr int PA = TBM * 8 / kThreads;    // 16-byte pieces of activation codes per thread and stage
+  constexpr int QX = BKB * TBM / kThreads;  // activation scales per thread and stage
+  constexpr int NPB = Q4 ? 2 : 4;           // 16-byte pieces of weight codes per thread and stage
+  static_assert(PA >= 1 && PA <= 4 && QX >= 1 && QX <= 2, "tile shape");
   const int K = nb * 32;
-
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = (wave & 1) * 64, wn = (wave >> 1) * 64;
+  const int wm = (wave & 1) * 32 * MI, wn = (wave >> 1) * 64;
   const int l32 = lane & 31, lh = lane >> 5;
-  if (tid == 0) sXs[BKB * BM] = u32x4{0u, 0u, 0u, 0u};
+  if (tid == 0) sXs[BKB * TBM] = u32x4{0u, 0u, 0u, 0u};
+  // input row of tile row r, or -1
+  auto in_row = [&](int r) -> int {
+    if constexpr (GATHER) return xrow[r];
+    else return m0 + r < M ? m0 + r : -1;
+  };
 
-  f32x16 acc[2][2];
+  f32x16 acc[MI][2];
 #pragma unroll
-  for (int i = 0; i < 2; i++)
+  for (int i = 0; i < MI; i++)
 #pragma unroll
     for (int j = 0; j < 2; j++) acc[i][j] = f32x16{};
 
-  // staging: 128 rows x 128 bytes per operand = 1024 16-byte pieces, 4 per thread; 512
-  // scales per operand, 2 per thread
-  // (Q4_0: 128 rows x 4 blocks of 16 bytes, 2 per thread)
+  // staging per stage: TBM rows x 128 bytes of activation codes, BN rows x 128 bytes of
+  // weight codes (Q4_0: BN rows x 4 blocks of 16 bytes), BKB x (TBM + BN) scales
   const int64_t wrow = Q4 ? (int64_t)nb * 16 : (int64_t)K;  // bytes per weight row
-  u32x4 pa0, pa1, pa2, pa3, pb0, pb1, pb2 = {}, pb3 = {};
-  float px0, px1;
+  u32x4 pa0, pa1, pa2 = {}, pa3 = {}, pb0, pb1, pb2 = {}, pb3 = {};
+  float px0, px1 = 0.f;
   uint32_t pw0, pw1;
 #define BQM_FETCH(B0)                                                                          \
   {                                                                                            \
     const int bn_ = min(BKB, nb - (B0));                                                       \
     u32x4* pa_[4] = {&pa0, &pa1, &pa2, &pa3};                                                  \
     u32x4* pb_[4] = {&pb0, &pb1, &pb2, &pb3};                                                  \
-    _Pragma("unroll") for (int p = 0; p < 4; p++) {                                            \
+    _Pragma("unroll") for (int p = 0; p < PA; p++) {                                           \
       const int piece = tid + p * kThreads, row = piece >> 3, c16 = piece & 7;                 \
-      const bool kin = (c16 >> 1) < bn_;                                                       \
+      const int xr = in_row(row);                                                              \
       u32x4 va = {0u, 0u, 0u, 0u};                                                             \
-      if (kin && m0 + row < M)                                                                 \
-        va = *reinterpret_cast<const u32x4*>(Xq + (size_t)(m0 + row) * K + (size_t)(B0) * 32 + c16 * 16); \
+      if ((c16 >> 1) < bn_ && xr >= 0)                                                         \
+        va = *reinterpret_cast<const u32x4*>(Xq + (size_t)xr * K + (size_t)(B0) * 32 + c16 * 16); \
       *pa_[p] = va;                                                                            \
     }                                                                                          \
     _Pragma("unroll") for (int p = 0; p < NPB; p++) {                                          \
@@ -183,11 +181,14 @@ __device__ __forceinline__ void qmm_tile(const uint8_t* __restrict__ Wc, const u
     }                                                                                          \
     float* px_[2] = {&px0, &px1};                                                              \
     uint32_t* pw_[2] = {&pw0, &pw1};                                                           \
+    _Pragma("unroll") for (int q = 0; q < QX; q++) {                                           \
+      const int e = tid + q * kThreads, kb = e / TBM, r = e % TBM;                             \
+      const int xr = in_row(r);                                                                \
+      *px_[q] = (kb < bn_ && xr >= 0) ? dx[(size_t)xr * nb + (B0) + kb] : 0.f;                 \
+    }                                                                                          \
     _Pragma("unroll") for (int q = 0; q < 2; q++) {                                            \
       const int e = tid + q * kThreads, kb = e >> 7, r = e & 127;                              \
-      const bool kin = kb < bn_;                                                               \
-      *px_[q] = (kin && m0 + r < M) ? dx[(size_t)(m0 + r) * nb + (B0) + kb] : 0.f;             \
-      *pw_[q] = (kin && n0 + r < N) ? (uint32_t)Wd[(size_t)(n0 + r) * nb + (B0) + kb] : 0u;   \
+      *pw_[q] = (kb < bn_ && n0 + r < N) ? (uint32_t)Wd[(size_t)(n0 + r) * nb + (B0) + kb] : 0u; \
     }                                                                                          \
   }
 
@@ -199,7 +200,7 @@ __device__ __forceinline__ void qmm_tile(const uint8_t* __restrict__ Wc, const u
       const u32x4 pa_[4] = {pa0, pa1, pa2, pa3};
       const u32x4 pb_[4] = {pb0, pb1, pb2, pb3};
 #pragma unroll
-      for (int p = 0; p < 4; p++) {
+      for (int p = 0; p < PA; p++) {
         const int piece = tid + p * kThreads, row = piece >> 3, c16 = piece & 7;
         *reinterpret_cast<u32x4*>(sA + row * ROWB + c16 * 16) = pa_[p];
       }
@@ -220,33 +221,31 @@ __device__ __forceinline__ void qmm_tile(const uint8_t* __restrict__ Wc, const u
       const float px_[2] = {px0, px1};
       const uint32_t pw_[2] = {pw0, pw1};
 #pragma unroll
-      for (int q = 0; q < 2; q++) {
-        const int e = tid + q * kThreads;  // = kb * 128 + r
-        sXs[e] = dx_operand(px_[q]);
-        sWs[e] = dw_operand(pw_[q]);
-      }
+      for (int q = 0; q < QX; q++) sXs[tid + q * kThreads] = dx_operand(px_[q]);  // kb * TBM + r
+#pragma unroll
+      for (int q = 0; q < 2; q++) sWs[tid + q * kThreads] = dw_operand(pw_[q]);  // kb * BN + r
     }
     __syncthreads();
     if (b0 + BKB < nb) BQM_FETCH(b0 + BKB)  // in flight while this stage is computed
 
     for (int kb = 0; kb < bn; kb++) {
-      i32x4 a[2], bq[2];
-      bf16x8 as[2], bs[2];
+      i32x4 a[MI], bq[2];
+      bf16x8 as[MI], bs[2];
 #pragma unroll
-      for (int i = 0; i < 2; i++) {
+      for (int i = 0; i < MI; i++) {
         a[i] = *reinterpret_cast<const i32x4*>(sA + (wm + i * 32 + l32) * ROWB + kb * 32 + lh * 16);
         // lanes 32..63 hold k = 8..15 of the scale product: zeros
-        const u32x4* p = lh ? &sXs[BKB * BM] : &sXs[kb * BM + wm + i * 32 + l32];
+        const u32x4* p = lh ? &sXs[BKB * TBM] : &sXs[kb * TBM + wm + i * 32 + l32];
         as[i] = __builtin_bit_cast(bf16x8, *p);
       }
 #pragma unroll
       for (int j = 0; j < 2; j++) {
         bq[j] = *reinterpret_cast<const i32x4*>(sB + (wn + j * 32 + l32) * ROWB + kb * 32 + lh * 16);
-        const u32x4* p = lh ? &sXs[BKB * BM] : &sWs[kb * BN + wn + j * 32 + l32];
+        const u32x4* p = lh ? &sXs[BKB * TBM] : &sWs[kb * BN + wn + j * 32 + l32];
         bs[j] = __builtin_bit_cast(bf16x8, *p);
       }
 #pragma unroll
-      for (int i = 0; i < 2; i++)
+      for (int i = 0; i < MI; i++)
 #pragma unroll
         for (int j = 0; j < 2; j++) {
           const i32x16 isum = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], bq[j], i32x16{}, 0, 0, 0);
@@ -260,16 +259,143 @@ __device__ __forceinline__ void qmm_tile(const uint8_t* __restrict__ Wc, const u
 
   // a lane's 16 results of a 32 x 32 tile: rows 8 (r / 4) + 4 lh + r % 4, column l32
 #pragma unroll
-  for (int i = 0; i < 2; i++)
+  for (int i = 0; i < MI; i++)
 #pragma unroll
     for (int j = 0; j < 2; j++) {
       const int n = n0 + wn + j * 32 + l32;
 #pragma unroll
       for (int r = 0; r < 16; r++) {
-        const int m = m0 + wm + i * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
-        if (m < M && n < N) Y[(size_t)m * N + n] = acc[i][j][r];
+        const int tr = wm + i * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
+        if constexpr (GATHER) {
+          const int yr = yrow[tr];
+          if (yr >= 0 && n < N) Y[(size_t)yr * N + n] = acc[i][j][r];
+        } else {
+          const int m = m0 + tr;
+          if (m < M && n < N) Y[(size_t)m * N + n] = acc[i][j][r];
+        }
       }
     }
+}
+
+template <int FMT>
+__device__ __forceinline__ void qmm_dense(const uint8_t* __restrict__ Wc, const uint16_t* __restrict__ Wd,
+                                          const int8_t* __restrict__ Xq, const float* __restrict__ dx,
+                                          float* __restrict__ Y, int M, int N, int nb, int tiles_m,
+                                          int tiles_n) {
+  __shared__ __attribute__((aligned(16))) int8_t sA[BM * ROWB];
+  __shared__ __attribute__((aligned(16))) int8_t sB[BN * ROWB];
+  __shared__ u32x4 sXs[BKB * BM + 1];  // dx operands per (block, m); the last: zeros
+  __shared__ u32x4 sWs[BKB * BN];      // dw operands per (block, n)
+  // Workgroups are dealt round-robin to the eight XCDs; give the workgroups of one XCD
+  // neighbouring tiles (all m-tiles of a few n-tiles) so they share W rows in that L2.
+  const int nwg = tiles_m * tiles_n;
+  const int bid = blockIdx.x;
+  int tile = bid;
+  if (nwg % 8 == 0) tile = (bid % 8) * (nwg / 8) + bid / 8;
+  const int tm = tile % tiles_m, tn = tile / tiles_m;
+  qmm_core<FMT, BM / 64, false>(Wc, Wd, Xq, dx, Y, N, nb, tn * BN, tm * BM, M, nullptr, nullptr,
+                                sA, sB, sXs, sWs);
+}
+
+// Exclusive prefix sum of v over the workgroup's threads (thread order).
+__device__ __forceinline__ int block_exclusive_scan(int v, int* wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(x, o, 64);
+    if (lane >= o) x += u;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; w++) base += wsum[w];
+  __syncthreads();
+  return base + x - v;
+}
+
+// Expert-indexed prefill product.  Every workgroup counts the slots per expert; the
+// experts' row tiles (ceil(count / kIdTBM) each, experts ascending, the slots of an expert
+// in index order) are numbered, and workgroup b takes row tile b / tiles_n, column tile
+// b % tiles_n; workgroups past the last row tile only take part in the padding fill.
+constexpr int kIdMI = 1, kIdTBM = 64 * kIdMI;
+
+template <int FMT>
+__device__ __forceinline__ void qmm_indexed(const uint8_t* __restrict__ Wc, const uint16_t* __restrict__ Wd,
+                                            const int8_t* __restrict__ Xq, const float* __restrict__ dx,
+                                            const int32_t* __restrict__ ids, float* __restrict__ Y,
+                                            int E, int N, int nb, int TS, int top_k, int xtr, int xsr,
+                                            int tiles_n) {
+  __shared__ __attribute__((aligned(16))) int8_t sA[kIdTBM * ROWB];
+  __shared__ __attribute__((aligned(16))) int8_t sB[BN * ROWB];  // first: per-expert counts
+  __shared__ u32x4 sXs[BKB * kIdTBM + 1];
+  __shared__ u32x4 sWs[BKB * BN];
+  __shared__ int xrow[kIdTBM], yrow[kIdTBM];
+  __shared__ int wsum[kThreads / 64];
+  __shared__ int tile_e, tile_m0;
+  const int tid = threadIdx.x;
+  // rows of slots that no tile computes, each by one workgroup: a padding slot (negative
+  // id) gives zeros, an id >= E NaN
+  for (int i = blockIdx.x; i < TS; i += gridDim.x) {
+    const int e = ids[i];
+    if (e >= 0 && e < E) continue;
+    const float v = e < 0 ? 0.0f : __builtin_nanf("");
+    for (int n = tid; n < N; n += kThreads) Y[(size_t)i * N + n] = v;
+  }
+  int* cnt = reinterpret_cast<int*>(sB);
+  for (int e = tid; e < E; e += kThreads) cnt[e] = 0;
+  if (tid == 0) tile_e = -1;
+  __syncthreads();
+  for (int i = tid; i < TS; i += kThreads) {
+    const int e = ids[i];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  // find this workgroup's row tile: thread t holds experts [e0, e1) and their tile count
+  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
+  const int per = (E + kThreads - 1) / kThreads;
+  const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
+  int mine = 0;
+  for (int e = e0; e < e1; e++) mine += (cnt[e] + kIdTBM - 1) / kIdTBM;
+  const int first = block_exclusive_scan(mine, wsum);
+  if (tm >= first && tm < first + mine) {
+    int t = first;
+    for (int e = e0; e < e1; e++) {
+      const int k = (cnt[e] + kIdTBM - 1) / kIdTBM;
+      if (tm < t + k) {
+        tile_e = e;
+        tile_m0 = (tm - t) * kIdTBM;
+        break;
+      }
+      t += k;
+    }
+  }
+  for (int r = tid; r < kIdTBM; r += kThreads) xrow[r] = yrow[r] = -1;
+  __syncthreads();
+  const int e = tile_e;
+  if (e < 0) return;  // past the last row tile (uniform)
+  const int m0 = tile_m0;
+  // the expert's slots of ranks m0 .. m0 + kIdTBM - 1 (rank: place among its slots in index
+  // order); thread t scans slots [s0, s1)
+  const int sper = (TS + kThreads - 1) / kThreads;
+  const int s0 = min(TS, tid * sper), s1 = min(TS, s0 + sper);
+  int c = 0;
+  for (int i = s0; i < s1; i++) c += ids[i] == e;
+  int rank = block_exclusive_scan(c, wsum);
+  for (int i = s0; i < s1; i++)
+    if (ids[i] == e) {
+      const int r = rank - m0;
+      if (r >= 0 && r < kIdTBM) {
+        const int t = i / top_k;
+        xrow[r] = t * xtr + (i - t * top_k) * xsr;
+        yrow[r] = i;
+      }
+      ++rank;
+    }
+  __syncthreads();
+  const int64_t wrow = FMT == BQM_Q4_0 ? (int64_t)nb * 16 : (int64_t)nb * 32;
+  qmm_core<FMT, kIdMI, true>(Wc + (int64_t)e * N * wrow, Wd + (int64_t)e * N * nb, Xq, dx, Y, N, nb,
+                             tn * BN, 0, 0, xrow, yrow, sA, sB, sXs, sWs);
 }
 
 #define BQM_QMM_KERNEL(NAME, FMT)                                                              \
@@ -277,11 +403,23 @@ __device__ __forceinline__ void qmm_tile(const uint8_t* __restrict__ Wc, const u
       const uint8_t* __restrict__ Wc, const uint16_t* __restrict__ Wd,                         \
       const int8_t* __restrict__ Xq, const float* __restrict__ dx, float* __restrict__ Y,      \
       int M, int N, int nb, int tiles_m, int tiles_n) {                                        \
-    qmm_tile<FMT>(Wc, Wd, Xq, dx, Y, M, N, nb, tiles_m, tiles_n);                              \
+    qmm_dense<FMT>(Wc, Wd, Xq, dx, Y, M, N, nb, tiles_m, tiles_n);                             \
   }
 BQM_QMM_KERNEL(k_qmm_q8_0, BQM_Q8_0)
 BQM_QMM_KERNEL(k_qmm_q4_0, BQM_Q4_0)
 #undef BQM_QMM_KERNEL
+
+#define BQM_QMM_ID_KERNEL(NAME, FMT)                                                           \
+  __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void NAME( \
+      const uint8_t* __restrict__ Wc, const uint16_t* __restrict__ Wd,                         \
+      const int8_t* __restrict__ Xq, const float* __restrict__ dx,                             \
+      const int32_t* __restrict__ ids, float* __restrict__ Y, int E, int N, int nb, int TS,    \
+      int top_k, int xtr, int xsr, int tiles_n) {                                              \
+    qmm_indexed<FMT>(Wc, Wd, Xq, dx, ids, Y, E, N, nb, TS, top_k, xtr, xsr, tiles_n);          \
+  }
+BQM_QMM_ID_KERNEL(k_qmm_id_q8_0, BQM_Q8_0)
+BQM_QMM_ID_KERNEL(k_qmm_id_q4_0, BQM_Q4_0)
+#undef BQM_QMM_ID_KERNEL
 
 }  // namespace
 
@@ -315,6 +453,25 @@ int launch_qmm_q8_0(const void* w, const int8_t* Xq, const float* dx, float* Y, 
 int launch_qmm_q4_0(const void* w, const int8_t* Xq, const float* dx, float* Y, int64_t M,
                     int64_t N, int64_t K, hipStream_t s) {
   return launch_qmm(BQM_Q4_0, w, Xq, dx, Y, M, N, K, s);
+}
+
+int launch_qmm_id(int fmt, const void* w, int E, int64_t N, int64_t K, const int32_t* ids, int T,
+                  int top_k, const int8_t* Xq, const float* dx, int64_t x_tok_rows,
+                  int64_t x_slot_rows, float* Y, hipStream_t s) {
+  Layout L;
+  layout_of(fmt, (int64_t)E * N, K, &L);
+  const uint8_t* Wc = static_cast<const uint8_t*>(w);
+  const uint16_t* Wd = reinterpret_cast<const uint16_t*>(Wc + L.scales_off);
+  const int TS = T * top_k;
+  const int tiles_n = (int)((N + BN - 1) / BN);
+  // row tiles: at most one partial tile per expert that has slots, plus the full ones
+  const int64_t max_tm = (TS < E ? TS : E) + (TS + kIdTBM - 1) / kIdTBM;
+  const int64_t grid = max_tm * tiles_n;
+  if (grid >= ((int64_t)1 << 31)) return BQM_E_SHAPE;
+  hipLaunchKernelGGL(fmt == BQM_Q4_0 ? k_qmm_id_q4_0 : k_qmm_id_q8_0, dim3((unsigned)grid),
+                     dim3(kThreads), 0, s, Wc, Wd, Xq, dx, ids, Y, E, (int)N, (int)L.nb, TS, top_k,
+                     (int)x_tok_rows, (int)x_slot_rows, tiles_n);
+  return launch_status();
 }
 
 }  // namespace bqm

@@ -26,7 +26,7 @@ import torch
 __all__ = [
     "QK", "Q4_0_BLOCK_BYTES", "Q8_0_BLOCK_BYTES", "seed_of", "normal", "round_half_away",
     "encode_q4_0", "encode_q8_0", "raw_q4_0", "raw_q8_0", "small_int", "router_ids", "router_weights",
-    "DENSE27B_LAYERS", "DENSE27B_SHAPES", "DENSE27B_FUSED_SHAPES", "MOE_SHAPE", "PREFILL_SHAPE",
+    "DENSE27B_LAYERS", "DENSE27B_SHAPES", "DENSE27B_FUSED_SHAPES", "MOE_SHAPE", "MOE_PREFILL_T", "PREFILL_SHAPE",
     "block_bytes",
 ]
 
@@ -46,6 +46,8 @@ DENSE27B_FUSED_SHAPES = (
 )
 # 128-expert MoE layer: gate/up 4096 -> 1536 and down 1536 -> 4096 per expert, top-8.
 MOE_SHAPE = dict(E=128, top_k=8, hidden=4096, ffn=1536)
+# MoE prefill: the MoE layer's experts over a 512-token prompt.
+MOE_PREFILL_T = 512
 # Prefill GEMM: 512 tokens through a 5120 -> 17408 projection.
 PREFILL_SHAPE = dict(M=512, K=5120, N=17408)
 

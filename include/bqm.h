@@ -67,6 +67,8 @@ typedef enum { BQM_Q4_0 = 2, BQM_Q8_0 = 8 } bqm_fmt;
 #define BQM_QMV_ID_MAX_T 64
 #define BQM_QMV_ID_MAX_TOPK 32
 #define BQM_QMV_ID_MAX_E 4096
+/* Token limit of qmm_id (top_k and E as for qmv_id). */
+#define BQM_QMM_ID_MAX_T 16384
 
 /* Bytes of the packed layout of a rows x K matrix in format fmt (0 for an unknown
  * format or a K that is not a multiple of 32).  Host function, no device work. */
@@ -218,6 +220,23 @@ int qmm_q8_0(const void* w_packed, const int8_t* Xq, const float* dx, float* Y, 
  * w_packed: packed Q4_0 N x K matrix; the rest as for qmm_q8_0.  Same status codes. */
 int qmm_q4_0(const void* w_packed, const int8_t* Xq, const float* dx, float* Y, int64_t M,
              int64_t N, int64_t K, hipStream_t stream);
+
+/* Expert-indexed prefill product: the prefill expert matmul of the "llama.cpp-v100" README
+ * (shadowgraph.io), kernels-and-runtime list, with qmv_id's routing (mul_mat_id, page
+ * "ik_llama.cpp 老工作站多 GPU 部署 Qwen3-235B-A22B 实战指南" (nxmr.cn)):
+ *     e = ids[t][s],  r = t * x_tok_rows + s * x_slot_rows,
+ *     Y[t][s][n] = sum_b d_w[e][n][b] * dx[r][b] * sum_j qw[e][n][32b+j] * Xq[r][32b+j]
+ * i.e. qmm_q8_0 / qmm_q4_0 of input row r with expert e's matrix, integer block sums exact,
+ * the scaling as in qmm_q8_0.  The slots of each expert are gathered into row tiles (in
+ * slot order), so each expert's rows are streamed once per 64 of its slots.
+ * w_packed: expert tensor of format fmt packed as ONE matrix of E*N rows.  ids: int32
+ * [T][top_k].  Xq, dx: quantized activations from bqm_quantize_q8_act, rows as indexed
+ * above (x_tok_rows = 1, x_slot_rows = 0: one row per token; top_k, 1: one per slot).
+ * Y: fp32 [T][top_k][N].  Padding slots (negative id) give zero rows, ids >= E NaN rows.
+ * Limits: T <= BQM_QMM_ID_MAX_T, top_k <= 32, E <= 4096, input rows below 2^31. */
+int qmm_id(int fmt, const void* w_packed, int E, int64_t N, int64_t K, const int32_t* ids, int T,
+           int top_k, const int8_t* Xq, const float* dx, int64_t x_tok_rows, int64_t x_slot_rows,
+           float* Y, hipStream_t stream);
 
 /* Static English text for a status code. */
 const char* bqm_strerror(int status);

@@ -23,7 +23,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("bqm_packed_bytes", "bqm_repack", "bqm_unpack", "qmv_q4_0", "qmv_q8_0", "qmv_id",
-              "qmv_id_gate_up", "qmv_id_sum", "bqm_quantize_q8_act", "qmm_q8_0", "qmm_q4_0", "bqm_strerror"):
+              "qmv_id_gate_up", "qmv_id_sum", "bqm_quantize_q8_act", "qmm_q8_0", "qmm_q4_0", "qmm_id", "bqm_strerror"):
         assert n in names
 
 
@@ -110,6 +110,18 @@ def test_host_validation_before_launch():
     assert L.qmm_q4_0(GOOD, GOOD, GOOD, GOOD, -1, 8, 64, None) == 2
     assert L.qmm_q4_0(None, GOOD, GOOD, GOOD, 4, 8, 64, None) == 1
     assert L.qmm_q4_0(GOOD, GOOD, GOOD, ODD, 4, 8, 64, None) == 3
+    # qmm_id: limits, strides, pointers
+    assert L.qmm_id(5, GOOD, 4, 8, 64, GOOD, 1, 2, GOOD, GOOD, 1, 0, GOOD, None) == 4
+    assert L.qmm_id(2, GOOD, 4, 8, 64, GOOD, 16385, 2, GOOD, GOOD, 1, 0, GOOD, None) == 2
+    assert L.qmm_id(2, GOOD, 4, 8, 64, GOOD, 1, 33, GOOD, GOOD, 1, 0, GOOD, None) == 2
+    assert L.qmm_id(2, GOOD, 4097, 8, 64, GOOD, 1, 2, GOOD, GOOD, 1, 0, GOOD, None) == 2
+    assert L.qmm_id(2, GOOD, 4, 8, 48, GOOD, 1, 2, GOOD, GOOD, 1, 0, GOOD, None) == 2
+    assert L.qmm_id(2, GOOD, 4, 8, 64, GOOD, 2, 2, GOOD, GOOD, 1 << 31, 0, GOOD, None) == 2
+    assert L.qmm_id(2, GOOD, 4, 8, 64, GOOD, 1, 2, GOOD, GOOD, -1, 0, GOOD, None) == 2
+    assert L.qmm_id(2, GOOD, 4, 8, 64, None, 1, 2, GOOD, GOOD, 1, 0, GOOD, None) == 1
+    assert L.qmm_id(2, None, 4, 8, 64, GOOD, 1, 2, GOOD, GOOD, 1, 0, GOOD, None) == 1
+    assert L.qmm_id(2, GOOD, 4, 8, 64, GOOD, 1, 2, GOOD, GOOD, 1, 0, ODD, None) == 3
+    assert L.qmm_id(2, ODD, 4, 8, 64, GOOD, 1, 2, GOOD, GOOD, 1, 0, GOOD, None) == 3
     # repack alignment: interchange needs 2-byte alignment, packed 16
     assert L.bqm_repack(2, P(0x100001), GOOD, 4, 64, None) == 3
     assert L.bqm_repack(2, GOOD, ODD, 4, 64, None) == 3
@@ -126,6 +138,7 @@ def test_empty_sizes_are_no_ops():
     assert L.bqm_quantize_q8_act(None, None, None, 0, 64, None) == 0
     assert L.qmm_q8_0(None, None, None, None, 0, 8, 64, None) == 0
     assert L.qmm_q4_0(None, None, None, None, 4, 0, 64, None) == 0
+    assert L.qmm_id(2, None, 4, 8, 64, None, 0, 2, None, None, 1, 0, None, None) == 0
     assert L.bqm_repack(2, None, None, 0, 64, None) == 0
     assert L.bqm_unpack(8, None, None, 4, 0, None) == 0
 

@@ -149,3 +149,99 @@ def test_qmm_empty_k_writes_zeros(fmt):
     Y = torch.full((M, N), float("nan"), device=DEV)
     qmm(fmt)(None, None, None, Y, M, N, 0)
     assert torch.count_nonzero(Y).item() == 0
+
+
+# --- expert-indexed prefill product ----------------------------------------------------------
+
+def run_qmm_id(fmt, E, N, K, ids_np, rows, key, sample=None, exact=False):
+    """qmm_id against the oracle; rows: 'broadcast' (one input row per token) or 'per_slot'.
+    sample: slots to check (the oracle computes only those; others are given as padding)."""
+    T, top_k = ids_np.shape
+    if exact:
+        Wi = (gen.raw_q8_0(E * N, K, key, codes=(-8, 8), device=DEV) if fmt == "q8_0"
+              else gen.raw_q4_0(E * N, K, key, codes=(0, 15), device=DEV))
+    else:
+        Wi = weights(fmt, E * N, K, key)
+    Wp = packed(fmt, Wi, E * N, K)
+    nrows, xt, xs = (T, 1, 0) if rows == "broadcast" else (T * top_k, top_k, 1)
+    if exact:
+        Xq = gen.small_int((nrows, K), key + ("x",), device=DEV, dtype=torch.int32).to(torch.int8)
+        pick = gen.small_int((nrows, K // 32), key + ("dx",), 0, 2, device=DEV, dtype=torch.int32)
+        dx = torch.tensor([0.5, 1.0, 2.0], device=DEV)[pick.long()]
+    else:
+        Xq, dx = quantize(gen.normal((nrows, K), key + ("x",), device=DEV), nrows, K)
+    ids = torch.from_numpy(ids_np).to(DEV)
+    Y = torch.full((T, top_k, N), -7.0, device=DEV)
+    bqm.qmm_id(fmt, Wp, E, N, K, ids, T, top_k, Xq, dx, xt, xs, Y)
+    ids_or = np.where(ids_np >= E, -1, ids_np).astype(np.int32)
+    if sample is not None:
+        keep = np.zeros(T * top_k, bool)
+        keep[sample] = True
+        ids_or = np.where(keep.reshape(T, top_k), ids_or, -1).astype(np.int32)
+    Yr, S = oracle.qmm_id(fmt, host(Wi), E, N, K, ids_or, host(Xq), host(dx), xt, xs)
+    return host(Y), Yr, S
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("rows", ["broadcast", "per_slot"])
+@pytest.mark.parametrize("E,N,K", [(5, 37, 96), (3, 300, 1056), (9, 129, 4128)])
+def test_qmm_id_small(fmt, rows, E, N, K):
+    say("qmm_id small", fmt, rows, E, N, K)
+    ids = np.array([[3, 0, 4], [-1, 4, 2], [1, 3, -1], [0, 2, 4], [4, 4, 1]], np.int32) % E
+    ids[1, 0] = -1
+    ids[2, 2] = -1
+    y, Yr, S = run_qmm_id(fmt, E, N, K, ids, rows, ("qmmid", fmt, rows, E, N, K))
+    check_close(y, Yr, S, f"qmm_id {fmt} {rows}")
+    assert np.all(y[1, 0] == 0) and np.all(y[2, 2] == 0)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_qmm_id_exact_probe_and_many_slots_per_expert(fmt):
+    """Integer-valued inputs (bit exact against the oracle), 300 tokens over 3 experts with
+    one of them taking most slots: row tiles of 64 slots, several per expert, the last
+    partial; bad ids give NaN rows."""
+    E, N, K, T, top_k = 3, 200, 544, 300, 2
+    ids = np.stack([np.zeros(T, np.int32), (np.arange(T) % 3).astype(np.int32)], axis=1)
+    ids[5, 1] = -1
+    ids[7, 1] = E + 2
+    say("qmm_id exact", fmt)
+    y, Yr, S = run_qmm_id(fmt, E, N, K, ids, "per_slot", ("qmmid-x", fmt), exact=True)
+    bad = ids >= E
+    assert np.all(np.isnan(y[bad]))
+    assert np.array_equal(y[~bad].astype(np.float64), Yr[~bad])
+
+
+@pytest.mark.parametrize("proj", ["gate", "down"])
+def test_qmm_id_moe_prefill(proj):
+    """The MoE layer over a 512-token prompt (128 experts, top-8, skewed router), gate
+    (4096 -> 1536, one input per token) or down (1536 -> 4096, one input per slot); 96
+    sampled slots against the oracle, padding and every other slot present."""
+    sh = gen.MOE_SHAPE
+    E, top_k, T = sh["E"], sh["top_k"], gen.MOE_PREFILL_T
+    N, K = (sh["ffn"], sh["hidden"]) if proj == "gate" else (sh["hidden"], sh["ffn"])
+    ids = gen.router_ids(T, E, top_k, ("moe-prefill-router",))
+    sample = np.unique(np.random.default_rng(3).integers(0, T * top_k, 96))
+    say("qmm_id moe prefill", proj, "busiest expert", int(np.bincount(ids.ravel()).max()))
+    y, Yr, S = run_qmm_id("q4_0", E, N, K, ids, "broadcast" if proj == "gate" else "per_slot",
+                          ("qmmid-moe", proj), sample=sample)
+    ys = y.reshape(T * top_k, N)[sample]
+    check_close(ys, Yr.reshape(T * top_k, N)[sample], S.reshape(T * top_k, N)[sample],
+                f"qmm_id moe prefill {proj}")
+
+
+def test_qmm_id_deterministic_and_empty_k():
+    E, N, K, T, top_k = 16, 256, 1024, 40, 4
+    ids = torch.from_numpy(gen.router_ids(T, E, top_k, ("qmmid-det",))).to(DEV)
+    Wp = packed("q8_0", weights("q8_0", E * N, K, ("qmmid-det",)), E * N, K)
+    Xq, dx = quantize(gen.normal((T, K), ("qmmid-det-x",), device=DEV), T, K)
+    Y1 = torch.empty((T, top_k, N), device=DEV)
+    Y2 = torch.empty((T, top_k, N), device=DEV)
+    bqm.qmm_id("q8_0", Wp, E, N, K, ids, T, top_k, Xq, dx, 1, 0, Y1)
+    bqm.qmm_id("q8_0", Wp, E, N, K, ids, T, top_k, Xq, dx, 1, 0, Y2)
+    assert torch.equal(Y1, Y2)
+    idk = torch.tensor([[0, -1], [2, 5]], dtype=torch.int32, device=DEV)
+    Y = torch.full((2, 2, 24), -7.0, device=DEV)
+    bqm.qmm_id("q4_0", torch.zeros(256, dtype=torch.uint8, device=DEV), 3, 24, 0, idk, 2, 2,
+               torch.zeros(64, dtype=torch.int8, device=DEV), torch.zeros(16, device=DEV), 1, 0, Y)
+    y = host(Y)
+    assert np.all(y[0] == 0) and np.all(y[1, 0] == 0) and np.all(np.isnan(y[1, 1]))

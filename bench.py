@@ -39,7 +39,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dense27b_q4_0",
-                    choices=["dense27b_q4_0", "dense27b_q8_0", "gemv4096", "moe", "prefill", "prefill_q4_0"])
+                    choices=["dense27b_q4_0", "dense27b_q8_0", "gemv4096", "moe", "prefill", "prefill_q4_0",
+                             "prefill_moe"])
     ap.add_argument("--M", type=int, default=1, help="batch for dense27b_q8_0 (1, 4 or 8)")
     ap.add_argument("--layers", type=int, default=64)
     ap.add_argument("--no-graph", action="store_true", help="eager launches instead of a graph")
@@ -460,6 +461,68 @@ def run_prefill(args, torch, gen, bqm, fmt="q8_0"):
             "quantize_us": round(1e3 * float(qdur.mean()), 3)}
 
 
+def run_prefill_moe(args, torch, gen, bqm):
+    """The MoE layer over a 512-token prompt: gate and up (4096 -> 1536, one input row per
+    token) and down (1536 -> 4096, one input row per slot) through qmm_id, Q4_0 experts."""
+    sh = gen.MOE_SHAPE
+    E, top_k, H, F, T = sh["E"], sh["top_k"], sh["hidden"], sh["ffn"], gen.MOE_PREFILL_T
+    n_layers = 4   # distinct layers (4 x 1.36 GB of experts) cycled
+    layers = []
+    for l in range(n_layers):
+        gate = make_matrix("q4_0", E * F, H, ("moep", l, "gate"), torch, gen, bqm)
+        up = make_matrix("q4_0", E * F, H, ("moep", l, "up"), torch, gen, bqm)
+        down = make_matrix("q4_0", E * H, F, ("moep", l, "down"), torch, gen, bqm)
+        ids_np = gen.router_ids(T, E, top_k, ("moep-ids", l))
+        ids = torch.from_numpy(ids_np).cuda()
+        x = gen.normal((T, H), ("moep-x", l), device="cuda")
+        xq = torch.empty((T, H), dtype=torch.int8, device="cuda")
+        xdx = torch.empty((T, H // 32), device="cuda")
+        bqm.bqm_quantize_q8_act(x, xq, xdx, T, H)
+        h = gen.normal((T * top_k, F), ("moep-h", l), device="cuda")
+        hq = torch.empty((T * top_k, F), dtype=torch.int8, device="cuda")
+        hdx = torch.empty((T * top_k, F // 32), device="cuda")
+        bqm.bqm_quantize_q8_act(h, hq, hdx, T * top_k, F)
+        yg = torch.empty((T, top_k, F), device="cuda")
+        yu = torch.empty((T, top_k, F), device="cuda")
+        yd = torch.empty((T, top_k, H), device="cuda")
+        counts = np.bincount(ids_np.ravel(), minlength=E)
+        layers.append((gate, up, down, ids, xq, xdx, hq, hdx, yg, yu, yd, counts))
+
+    def run():
+        for gate, up, down, ids, xq, xdx, hq, hdx, yg, yu, yd, _ in layers:
+            bqm.qmm_id("q4_0", gate, E, F, H, ids, T, top_k, xq, xdx, 1, 0, yg)
+            bqm.qmm_id("q4_0", up, E, F, H, ids, T, top_k, xq, xdx, 1, 0, yu)
+            bqm.qmm_id("q4_0", down, E, H, F, ids, T, top_k, hq, hdx, top_k, 1, yd)
+
+    ms = time_steps(run, args.steps, args.warmup, torch, not args.no_graph)
+    launches = []
+    for gate, up, down, ids, xq, xdx, hq, hdx, yg, yu, yd, _ in layers:
+        launches += [lambda w=gate, i=ids, a=xq, d=xdx, y=yg: bqm.qmm_id("q4_0", w, E, F, H, i, T, top_k, a, d, 1, 0, y),
+                     lambda w=up, i=ids, a=xq, d=xdx, y=yu: bqm.qmm_id("q4_0", w, E, F, H, i, T, top_k, a, d, 1, 0, y),
+                     lambda w=down, i=ids, a=hq, d=hdx, y=yd: bqm.qmm_id("q4_0", w, E, H, F, i, T, top_k, a, d, top_k, 1, y)]
+    dur = per_launch_ms(launches, torch)
+    slots = T * top_k
+    ops = n_layers * 3 * 2.0 * slots * F * H           # useful int8 operations, all launches
+    tops = ops / (dur.sum() * 1e-3) / 1e12
+    valu = n_layers * 3 * 2.0 * slots * F * (H // 32)  # 2 lane-ops per (slot, n, block): same count
+    valu_t = valu / (dur.sum() * 1e-3) / 1e12
+    tiles = [int(np.sum((L[-1] + 63) // 64)) for L in layers]   # 64-row tiles of the kernel
+    return {"metric": "MoE prefill qmm_id int8 TOP/s", "value": round(tops, 2), "unit": "TOP/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8/f32",
+            "data": "synthetic",
+            "config": {"workload": "128-expert MoE layer (gate/up 4096->1536, down 1536->4096, Q4_0, top-8) "
+                                   "over a 512-token prompt, 4 distinct layers per step"},
+            "ms_per_layer": round(ms / n_layers, 4),
+            "busiest_expert_slots": [int(L[-1].max()) for L in layers],
+            "row_tile_fill": round(slots / (64.0 * float(np.mean(tiles))), 3),
+            "roofline": {"bound": "alu", "achieved": round(valu_t, 3), "peak": VALU_PEAK_TOPS,
+                         "unit": "T lane-op/s", "frac": round(valu_t / VALU_PEAK_TOPS, 4),
+                         "traffic": traffic_from_profiles("qmm_id_q4_0_moe_prefill"),
+                         "kernel": "k_qmm_id_q4_0", "avg_launch_us": round(1e3 * float(dur.mean()), 3),
+                         "mfma_int8_frac": round(tops / INT8_PEAK_TOPS, 4)}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -485,6 +548,8 @@ def main():
         res = run_moe(args, torch, gen, bqm)
     elif wl == "prefill_q4_0":
         res = run_prefill(args, torch, gen, bqm, "q4_0")
+    elif wl == "prefill_moe":
+        res = run_prefill_moe(args, torch, gen, bqm)
     else:
         res = run_prefill(args, torch, gen, bqm)
     print(json.dumps(res), flush=True)

@@ -115,27 +115,30 @@ __device__ __forceinline__ void expand_q4(const u32x4& q, u32x4& lo, u32x4& hi) 
   }
 }
 
-// One workgroup tile of Y: TBM = 64 MI rows (m) by BN columns (n).  FMT selects how the
+// One workgroup tile of Y: TBM = 32 WGM TI rows (m) by BN columns (n); the four waves form
+// a WGM x (4 / WGM) grid, each wave TI x TJ MFMA tiles of 32 x 32.  FMT selects how the
 // weight codes arrive: Q8_0 as int8 rows [N][K]; Q4_0 as 16-byte blocks [N][nb][16],
 // expanded to int8 while they are staged, so that the LDS layout and everything after it
 // are the same for both.  Rows: dense (GATHER false), tile row r is input and output row
 // m0 + r (< M); gathered, tile row r reads input row xrow[r] and writes output row yrow[r]
 // (LDS tables, -1 past the tile's rows).
-template <int FMT, int MI, bool GATHER>
+template <int FMT, int WGM, int TI, int TJ, bool GATHER>
 __device__ __forceinline__ void qmm_core(const uint8_t* __restrict__ Wc, const uint16_t* __restrict__ Wd,
                                          const int8_t* __restrict__ Xq, const float* __restrict__ dx,
                                          float* __restrict__ Y, int N, int nb, int n0, int m0, int M,
                                          const int* xrow, const int* yrow, int8_t* sA, int8_t* sB,
                                          u32x4* sXs, u32x4* sWs) {
   constexpr bool Q4 = FMT == BQM_Q4_0;
-  constexpr int TBM = 64 * MI;
+  constexpr int TBM = 32 * WGM * TI;
   constexpr int PA = TBM * 8 / kThreads;    // 16-byte pieces of activation codes per thread and stage
-  constexpr int QX = BKB * TBM / kThreads;  // activation scales per thread and stage
+  constexpr int NXS = BKB * TBM;            // activation scales per stage ...
+  constexpr int QX = (NXS + kThreads - 1) / kThreads;  // ... per thread
   constexpr int NPB = Q4 ? 2 : 4;           // 16-byte pieces of weight codes per thread and stage
   static_assert(PA >= 1 && PA <= 4 && QX >= 1 && QX <= 2, "tile shape");
+  static_assert((4 / WGM) * 32 * TJ == BN, "the waves cover the BN columns");
   const int K = nb * 32;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = (wave & 1) * 32 * MI, wn = (wave >> 1) * 64;
+  const int wm = (wave % WGM) * 32 * TI, wn = (wave / WGM) * 32 * TJ;
   const int l32 = lane & 31, lh = lane >> 5;
   if (tid == 0) sXs[BKB * TBM] = u32x4{0u, 0u, 0u, 0u};
   // input row of tile row r, or -1
@@ -144,11 +147,11 @@ __device__ __forceinline__ void qmm_core(const uint8_t* __restrict__ Wc, const u
     else return m0 + r < M ? m0 + r : -1;
   };
 
-  f32x16 acc[MI][2];
+  f32x16 acc[TI][TJ];
 #pragma unroll
-  for (int i = 0; i < MI; i++)
+  for (int i = 0; i < TI; i++)
 #pragma unroll
-    for (int j = 0; j < 2; j++) acc[i][j] = f32x16{};
+    for (int j = 0; j < TJ; j++) acc[i][j] = f32x16{};
 
   // staging per stage: TBM rows x 128 bytes of activation codes, BN rows x 128 bytes of
   // weight codes (Q4_0: BN rows x 4 blocks of 16 bytes), BKB x (TBM + BN) scales
@@ -183,7 +186,7 @@ __device__ __forceinline__ void qmm_core(const uint8_t* __restrict__ Wc, const u
     uint32_t* pw_[2] = {&pw0, &pw1};                                                           \
     _Pragma("unroll") for (int q = 0; q < QX; q++) {                                           \
       const int e = tid + q * kThreads, kb = e / TBM, r = e % TBM;                             \
-      const int xr = in_row(r);                                                                \
+      const int xr = e < NXS ? in_row(r) : -1;                                                 \
       *px_[q] = (kb < bn_ && xr >= 0) ? dx[(size_t)xr * nb + (B0) + kb] : 0.f;                 \
     }                                                                                          \
     _Pragma("unroll") for (int q = 0; q < 2; q++) {                                            \
@@ -221,7 +224,8 @@ __device__ __forceinline__ void qmm_core(const uint8_t* __restrict__ Wc, const u
       const float px_[2] = {px0, px1};
       const uint32_t pw_[2] = {pw0, pw1};
 #pragma unroll
-      for (int q = 0; q < QX; q++) sXs[tid + q * kThreads] = dx_operand(px_[q]);  // kb * TBM + r
+      for (int q = 0; q < QX; q++)
+        if (tid + q * kThreads < NXS) sXs[tid + q * kThreads] = dx_operand(px_[q]);  // kb * TBM + r
 #pragma unroll
       for (int q = 0; q < 2; q++) sWs[tid + q * kThreads] = dw_operand(pw_[q]);  // kb * BN + r
     }
@@ -229,25 +233,25 @@ __device__ __forceinline__ void qmm_core(const uint8_t* __restrict__ Wc, const u
     if (b0 + BKB < nb) BQM_FETCH(b0 + BKB)  // in flight while this stage is computed
 
     for (int kb = 0; kb < bn; kb++) {
-      i32x4 a[MI], bq[2];
-      bf16x8 as[MI], bs[2];
+      i32x4 a[TI], bq[TJ];
+      bf16x8 as[TI], bs[TJ];
 #pragma unroll
-      for (int i = 0; i < MI; i++) {
+      for (int i = 0; i < TI; i++) {
         a[i] = *reinterpret_cast<const i32x4*>(sA + (wm + i * 32 + l32) * ROWB + kb * 32 + lh * 16);
         // lanes 32..63 hold k = 8..15 of the scale product: zeros
         const u32x4* p = lh ? &sXs[BKB * TBM] : &sXs[kb * TBM + wm + i * 32 + l32];
         as[i] = __builtin_bit_cast(bf16x8, *p);
       }
 #pragma unroll
-      for (int j = 0; j < 2; j++) {
+      for (int j = 0; j < TJ; j++) {
         bq[j] = *reinterpret_cast<const i32x4*>(sB + (wn + j * 32 + l32) * ROWB + kb * 32 + lh * 16);
         const u32x4* p = lh ? &sXs[BKB * TBM] : &sWs[kb * BN + wn + j * 32 + l32];
         bs[j] = __builtin_bit_cast(bf16x8, *p);
       }
 #pragma unroll
-      for (int i = 0; i < MI; i++)
+      for (int i = 0; i < TI; i++)
 #pragma unroll
-        for (int j = 0; j < 2; j++) {
+        for (int j = 0; j < TJ; j++) {
           const i32x16 isum = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], bq[j], i32x16{}, 0, 0, 0);
           const f32x16 sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as[i], bs[j], f32x16{}, 0, 0, 0);
 #pragma unroll
@@ -259,9 +263,9 @@ __device__ __forceinline__ void qmm_core(const uint8_t* __restrict__ Wc, const u
 
   // a lane's 16 results of a 32 x 32 tile: rows 8 (r / 4) + 4 lh + r % 4, column l32
 #pragma unroll
-  for (int i = 0; i < MI; i++)
+  for (int i = 0; i < TI; i++)
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
+    for (int j = 0; j < TJ; j++) {
       const int n = n0 + wn + j * 32 + l32;
 #pragma unroll
       for (int r = 0; r < 16; r++) {
@@ -293,8 +297,8 @@ __device__ __forceinline__ void qmm_dense(const uint8_t* __restrict__ Wc, const 
   int tile = bid;
   if (nwg % 8 == 0) tile = (bid % 8) * (nwg / 8) + bid / 8;
   const int tm = tile % tiles_m, tn = tile / tiles_m;
-  qmm_core<FMT, BM / 64, false>(Wc, Wd, Xq, dx, Y, N, nb, tn * BN, tm * BM, M, nullptr, nullptr,
-                                sA, sB, sXs, sWs);
+  qmm_core<FMT, 2, BM / 64, 2, false>(Wc, Wd, Xq, dx, Y, N, nb, tn * BN, tm * BM, M, nullptr,
+                                      nullptr, sA, sB, sXs, sWs);
 }
 
 // Exclusive prefix sum of v over the workgroup's threads (thread order).
@@ -318,7 +322,15 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum) {
 // experts' row tiles (ceil(count / kIdTBM) each, experts ascending, the slots of an expert
 // in index order) are numbered, and workgroup b takes row tile b / tiles_n, column tile
 // b % tiles_n; workgroups past the last row tile only take part in the padding fill.
-constexpr int kIdMI = 1, kIdTBM = 64 * kIdMI;
+#ifndef BQM_QMM_ID_ROWS
+#define BQM_QMM_ID_ROWS 64
+#endif
+// Row tile of the indexed product.  64 rows (waves 2 x 2, each 1 x 2 MFMA tiles), three
+// workgroups per CU: measured on the 512-token MoE prefill, 185 TOP/s against 161 with two
+// workgroups per CU and 143-164 with 32-row tiles (waves 1 x 4, one MFMA tile each: fewer
+// padded rows, but twice the weight staging per output).
+constexpr int kIdTBM = BQM_QMM_ID_ROWS;
+constexpr int kIdWGM = kIdTBM == 32 ? 1 : 2, kIdTJ = kIdTBM == 32 ? 1 : 2;
 
 template <int FMT>
 __device__ __forceinline__ void qmm_indexed(const uint8_t* __restrict__ Wc, const uint16_t* __restrict__ Wd,
@@ -394,8 +406,8 @@ __device__ __forceinline__ void qmm_indexed(const uint8_t* __restrict__ Wc, cons
     }
   __syncthreads();
   const int64_t wrow = FMT == BQM_Q4_0 ? (int64_t)nb * 16 : (int64_t)nb * 32;
-  qmm_core<FMT, kIdMI, true>(Wc + (int64_t)e * N * wrow, Wd + (int64_t)e * N * nb, Xq, dx, Y, N, nb,
-                             tn * BN, 0, 0, xrow, yrow, sA, sB, sXs, sWs);
+  qmm_core<FMT, kIdWGM, 1, kIdTJ, true>(Wc + (int64_t)e * N * wrow, Wd + (int64_t)e * N * nb, Xq, dx,
+                                        Y, N, nb, tn * BN, 0, 0, xrow, yrow, sA, sB, sXs, sWs);
 }
 
 #define BQM_QMM_KERNEL(NAME, FMT)                                                              \
@@ -409,8 +421,12 @@ BQM_QMM_KERNEL(k_qmm_q8_0, BQM_Q8_0)
 BQM_QMM_KERNEL(k_qmm_q4_0, BQM_Q4_0)
 #undef BQM_QMM_KERNEL
 
+#ifndef BQM_QMM_ID_WAVES
+#define BQM_QMM_ID_WAVES 3  // waves per SIMD (workgroups per CU) the indexed kernel is built for
+#endif
 #define BQM_QMM_ID_KERNEL(NAME, FMT)                                                           \
-  __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void NAME( \
+  __global__ __launch_bounds__(kThreads)                                                       \
+  __attribute__((amdgpu_waves_per_eu(BQM_QMM_ID_WAVES, BQM_QMM_ID_WAVES))) void NAME(          \
       const uint8_t* __restrict__ Wc, const uint16_t* __restrict__ Wd,                         \
       const int8_t* __restrict__ Xq, const float* __restrict__ dx,                             \
       const int32_t* __restrict__ ids, float* __restrict__ Y, int E, int N, int nb, int TS,    \

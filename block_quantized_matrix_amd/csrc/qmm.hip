@@ -70,7 +70,17 @@ __global__ __launch_bounds__(kThreads) void k_quantize_q8_act(const float4* __re
 // one bf16 MFMA with K = 6 used terms, dx split exactly into three truncated bf16 parts
 // and dw (fp16, 11 significant bits) into two, every partial product exact in fp32.
 // Per element and block the vector units then do one conversion and one FMA.
-constexpr int BM = 128, BN = 128, BKB = 4;     // BKB blocks of 32 per stage
+// Row tile of the dense product and workgroups per CU: 64 rows (waves 2 x 2, each 1 x 2
+// MFMA tiles, 156-158 VGPRs) let three workgroups share a CU, which hides more of each
+// wave's MFMA-to-epilogue latency than a 128-row tile's reuse saves (512 x 5120 x 17408:
+// Q8_0 392 -> 426 TOP/s, Q4_0 393 -> 445 against 128 rows with two per CU).
+#ifndef BQM_QMM_ROWS
+#define BQM_QMM_ROWS 64
+#endif
+#ifndef BQM_QMM_WAVES
+#define BQM_QMM_WAVES 3
+#endif
+constexpr int BM = BQM_QMM_ROWS, BN = 128, BKB = 4;  // BKB blocks of 32 per stage
 constexpr int ROWB = BKB * 32 + 16;            // LDS row stride in bytes (padding vs conflicts)
 
 // v = hi + mid + lo exactly, each a truncated bf16 (returned as its 16 bits)
@@ -297,8 +307,9 @@ __device__ __forceinline__ void qmm_dense(const uint8_t* __restrict__ Wc, const 
   int tile = bid;
   if (nwg % 8 == 0) tile = (bid % 8) * (nwg / 8) + bid / 8;
   const int tm = tile % tiles_m, tn = tile / tiles_m;
-  qmm_core<FMT, 2, BM / 64, 2, false>(Wc, Wd, Xq, dx, Y, N, nb, tn * BN, tm * BM, M, nullptr,
-                                      nullptr, sA, sB, sXs, sWs);
+  constexpr int WGM = BM == 32 ? 1 : 2;  // waves along m; each covers 128 / (4 / WGM) columns
+  qmm_core<FMT, WGM, BM / (32 * WGM), WGM, false>(Wc, Wd, Xq, dx, Y, N, nb, tn * BN, tm * BM, M,
+                                                  nullptr, nullptr, sA, sB, sXs, sWs);
 }
 
 // Exclusive prefix sum of v over the workgroup's threads (thread order).
@@ -411,7 +422,8 @@ __device__ __forceinline__ void qmm_indexed(const uint8_t* __restrict__ Wc, cons
 }
 
 #define BQM_QMM_KERNEL(NAME, FMT)                                                              \
-  __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void NAME( \
+  __global__ __launch_bounds__(kThreads)                                                       \
+  __attribute__((amdgpu_waves_per_eu(BQM_QMM_WAVES, BQM_QMM_WAVES))) void NAME(                \
       const uint8_t* __restrict__ Wc, const uint16_t* __restrict__ Wd,                         \
       const int8_t* __restrict__ Xq, const float* __restrict__ dx, float* __restrict__ Y,      \
       int M, int N, int nb, int tiles_m, int tiles_n) {                                        \

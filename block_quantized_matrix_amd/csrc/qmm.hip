@@ -135,22 +135,25 @@ __device__ __forceinline__ void expand_q4(const u32x4& q, u32x4& lo, u32x4& hi) 
 template <int FMT, int WGM, int TI, int TJ, bool GATHER>
 __device__ __forceinline__ void qmm_core(const uint8_t* __restrict__ Wc, const uint16_t* __restrict__ Wd,
                                          const int8_t* __restrict__ Xq, const float* __restrict__ dx,
-                                         float* __restrict__ Y, int N, int nb, int n0, int m0, int M,
-                                         const int* xrow, const int* yrow, int8_t* sA, int8_t* sB,
-                                         u32x4* sXs, u32x4* sWs) {
+                                         int64_t x_rows, float* __restrict__ Y, int N, int nb, int n0,
+                                         int m0, int M, const int* xrow, const int* yrow, int8_t* sA,
+                                         int8_t* sB, u32x4* sXs, u32x4* sWs) {
   constexpr bool Q4 = FMT == BQM_Q4_0;
   constexpr int TBM = 32 * WGM * TI;
   constexpr int PA = TBM * 8 / kThreads;    // 16-byte pieces of activation codes per thread and stage
   constexpr int NXS = BKB * TBM;            // activation scales per stage ...
   constexpr int QX = (NXS + kThreads - 1) / kThreads;  // ... per thread
   constexpr int NPB = Q4 ? 2 : 4;           // 16-byte pieces of weight codes per thread and stage
+  constexpr uint32_t kOob = 0x80000000u;    // a buffer offset past every descriptor: reads 0
   static_assert(PA >= 1 && PA <= 4 && QX >= 1 && QX <= 2, "tile shape");
   static_assert((4 / WGM) * 32 * TJ == BN, "the waves cover the BN columns");
   const int K = nb * 32;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = (wave % WGM) * 32 * TI, wn = (wave / WGM) * 32 * TJ;
   const int l32 = lane & 31, lh = lane >> 5;
-  if (tid == 0) sXs[BKB * TBM] = u32x4{0u, 0u, 0u, 0u};
+  // dx operands in LDS as [BKB][2][TBM]: the second half stays zero (lanes 32..63 of the
+  // scale product's A operand hold its k = 8..15, which must be zero)
+  for (int e = tid; e < NXS; e += kThreads) sXs[(e / TBM * 2 + 1) * TBM + e % TBM] = u32x4{0u, 0u, 0u, 0u};
   // input row of tile row r, or -1
   auto in_row = [&](int r) -> int {
     if constexpr (GATHER) return xrow[r];
@@ -163,113 +166,129 @@ __device__ __forceinline__ void qmm_core(const uint8_t* __restrict__ Wc, const u
 #pragma unroll
     for (int j = 0; j < TJ; j++) acc[i][j] = f32x16{};
 
-  // staging per stage: TBM rows x 128 bytes of activation codes, BN rows x 128 bytes of
-  // weight codes (Q4_0: BN rows x 4 blocks of 16 bytes), BKB x (TBM + BN) scales
+  // Loads go through buffer descriptors: each lane's offset is fixed for the whole K loop
+  // (row and place in the stage), the stage's block offset is a scalar.  A lane's piece
+  // past the rows, or (last stage) past K, reads zeros through an offset past the
+  // descriptor; every other access lies inside the operand by construction.
   const int64_t wrow = Q4 ? (int64_t)nb * 16 : (int64_t)K;  // bytes per weight row
-  u32x4 pa0, pa1, pa2 = {}, pa3 = {}, pb0, pb1, pb2 = {}, pb3 = {};
-  float px0, px1 = 0.f;
-  uint32_t pw0, pw1;
-#define BQM_FETCH(B0)                                                                          \
-  {                                                                                            \
-    const int bn_ = min(BKB, nb - (B0));                                                       \
-    u32x4* pa_[4] = {&pa0, &pa1, &pa2, &pa3};                                                  \
-    u32x4* pb_[4] = {&pb0, &pb1, &pb2, &pb3};                                                  \
-    _Pragma("unroll") for (int p = 0; p < PA; p++) {                                           \
-      const int piece = tid + p * kThreads, row = piece >> 3, c16 = piece & 7;                 \
-      const int xr = in_row(row);                                                              \
-      u32x4 va = {0u, 0u, 0u, 0u};                                                             \
-      if ((c16 >> 1) < bn_ && xr >= 0)                                                         \
-        va = *reinterpret_cast<const u32x4*>(Xq + (size_t)xr * K + (size_t)(B0) * 32 + c16 * 16); \
-      *pa_[p] = va;                                                                            \
-    }                                                                                          \
-    _Pragma("unroll") for (int p = 0; p < NPB; p++) {                                          \
-      const int piece = tid + p * kThreads;                                                    \
-      const int row = Q4 ? piece >> 2 : piece >> 3, c16 = Q4 ? piece & 3 : piece & 7;          \
-      const int kb_ = Q4 ? c16 : c16 >> 1;                                                     \
-      u32x4 vb = {0u, 0u, 0u, 0u};                                                             \
-      if (kb_ < bn_ && n0 + row < N)                                                           \
-        vb = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(                       \
-            Wc + (size_t)(n0 + row) * wrow + (size_t)(B0) * (Q4 ? 16 : 32) + c16 * 16));       \
-      *pb_[p] = vb;                                                                            \
-    }                                                                                          \
-    float* px_[2] = {&px0, &px1};                                                              \
-    uint32_t* pw_[2] = {&pw0, &pw1};                                                           \
-    _Pragma("unroll") for (int q = 0; q < QX; q++) {                                           \
-      const int e = tid + q * kThreads, kb = e / TBM, r = e % TBM;                             \
-      const int xr = e < NXS ? in_row(r) : -1;                                                 \
-      *px_[q] = (kb < bn_ && xr >= 0) ? dx[(size_t)xr * nb + (B0) + kb] : 0.f;                 \
-    }                                                                                          \
-    _Pragma("unroll") for (int q = 0; q < 2; q++) {                                            \
-      const int e = tid + q * kThreads, kb = e >> 7, r = e & 127;                              \
-      *pw_[q] = (kb < bn_ && n0 + r < N) ? (uint32_t)Wd[(size_t)(n0 + r) * nb + (B0) + kb] : 0u; \
-    }                                                                                          \
+  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc((void*)Xq, (short)0, (int)(x_rows * K), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rX = __builtin_amdgcn_make_buffer_rsrc((void*)dx, (short)0, (int)(x_rows * nb * 4), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc((void*)Wc, (short)0, (int)(N * wrow), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc((void*)Wd, (short)0, (int)((int64_t)N * nb * 2), 0x00020000);
+  uint32_t oA[PA], oB[NPB], oX[QX], oW[2];
+  int bA[PA], bB[NPB], bX[QX], bW[2];  // block of the stage each piece belongs to
+#pragma unroll
+  for (int p = 0; p < PA; p++) {
+    const int piece = tid + p * kThreads, row = piece >> 3, c16 = piece & 7;
+    const int xr = in_row(row);
+    oA[p] = xr >= 0 ? (uint32_t)xr * (uint32_t)K + c16 * 16 : kOob;
+    bA[p] = c16 >> 1;
+  }
+#pragma unroll
+  for (int p = 0; p < NPB; p++) {
+    const int piece = tid + p * kThreads;
+    const int row = Q4 ? piece >> 2 : piece >> 3, c16 = Q4 ? piece & 3 : piece & 7;
+    oB[p] = n0 + row < N ? (uint32_t)((n0 + row) * wrow) + c16 * 16 : kOob;
+    bB[p] = Q4 ? c16 : c16 >> 1;
+  }
+#pragma unroll
+  for (int q = 0; q < QX; q++) {
+    const int e = tid + q * kThreads, kb = e / TBM, r = e % TBM;
+    const int xr = e < NXS ? in_row(r) : -1;
+    oX[q] = xr >= 0 ? ((uint32_t)xr * (uint32_t)nb + kb) * 4u : kOob;
+    bX[q] = kb;
+  }
+#pragma unroll
+  for (int q = 0; q < 2; q++) {
+    const int e = tid + q * kThreads, kb = e >> 7, r = e & 127;
+    oW[q] = n0 + r < N ? ((uint32_t)(n0 + r) * (uint32_t)nb + kb) * 2u : kOob;
+    bW[q] = kb;
   }
 
-  BQM_FETCH(0)
+  u32x4 pa[PA], pb[NPB];
+  uint32_t px[QX], pw[2];
+  auto fetch = [&](int b0) {
+    const int bn_ = min(BKB, nb - b0);
+    const bool full = bn_ == BKB;
+#pragma unroll
+    for (int p = 0; p < PA; p++)
+      pa[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                  rA, full || bA[p] < bn_ ? oA[p] : kOob, b0 * 32, 0));
+#pragma unroll
+    for (int p = 0; p < NPB; p++)
+      pb[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                  rB, full || bB[p] < bn_ ? oB[p] : kOob, b0 * (Q4 ? 16 : 32), 0));
+#pragma unroll
+    for (int q = 0; q < QX; q++)
+      px[q] = __builtin_amdgcn_raw_buffer_load_b32(rX, full || bX[q] < bn_ ? oX[q] : kOob, b0 * 4, 0);
+#pragma unroll
+    for (int q = 0; q < 2; q++)
+      pw[q] = (uint32_t)__builtin_bit_cast(uint16_t, __builtin_amdgcn_raw_buffer_load_b16(
+                  rW, full || bW[q] < bn_ ? oW[q] : kOob, b0 * 2, 0));
+  };
+
+  fetch(0);
   for (int b0 = 0; b0 < nb; b0 += BKB) {
     const int bn = min(BKB, nb - b0);
     __syncthreads();  // every wave is done with the previous stage
-    {
-      const u32x4 pa_[4] = {pa0, pa1, pa2, pa3};
-      const u32x4 pb_[4] = {pb0, pb1, pb2, pb3};
 #pragma unroll
-      for (int p = 0; p < PA; p++) {
-        const int piece = tid + p * kThreads, row = piece >> 3, c16 = piece & 7;
-        *reinterpret_cast<u32x4*>(sA + row * ROWB + c16 * 16) = pa_[p];
-      }
-#pragma unroll
-      for (int p = 0; p < NPB; p++) {
-        const int piece = tid + p * kThreads;
-        if constexpr (Q4) {
-          const int row = piece >> 2, kb = piece & 3;
-          u32x4 lo, hi;
-          expand_q4(pb_[p], lo, hi);
-          *reinterpret_cast<u32x4*>(sB + row * ROWB + kb * 32) = lo;
-          *reinterpret_cast<u32x4*>(sB + row * ROWB + kb * 32 + 16) = hi;
-        } else {
-          const int row = piece >> 3, c16 = piece & 7;
-          *reinterpret_cast<u32x4*>(sB + row * ROWB + c16 * 16) = pb_[p];
-        }
-      }
-      const float px_[2] = {px0, px1};
-      const uint32_t pw_[2] = {pw0, pw1};
-#pragma unroll
-      for (int q = 0; q < QX; q++)
-        if (tid + q * kThreads < NXS) sXs[tid + q * kThreads] = dx_operand(px_[q]);  // kb * TBM + r
-#pragma unroll
-      for (int q = 0; q < 2; q++) sWs[tid + q * kThreads] = dw_operand(pw_[q]);  // kb * BN + r
+    for (int p = 0; p < PA; p++) {
+      const int piece = tid + p * kThreads, row = piece >> 3, c16 = piece & 7;
+      *reinterpret_cast<u32x4*>(sA + row * ROWB + c16 * 16) = pa[p];
     }
+#pragma unroll
+    for (int p = 0; p < NPB; p++) {
+      const int piece = tid + p * kThreads;
+      if constexpr (Q4) {
+        const int row = piece >> 2, kb = piece & 3;
+        u32x4 lo, hi;
+        expand_q4(pb[p], lo, hi);
+        *reinterpret_cast<u32x4*>(sB + row * ROWB + kb * 32) = lo;
+        *reinterpret_cast<u32x4*>(sB + row * ROWB + kb * 32 + 16) = hi;
+      } else {
+        const int row = piece >> 3, c16 = piece & 7;
+        *reinterpret_cast<u32x4*>(sB + row * ROWB + c16 * 16) = pb[p];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < QX; q++) {
+      const int e = tid + q * kThreads;  // = kb * TBM + r
+      if (e < NXS) sXs[(e / TBM * 2) * TBM + e % TBM] = dx_operand(__uint_as_float(px[q]));
+    }
+#pragma unroll
+    for (int q = 0; q < 2; q++) sWs[tid + q * kThreads] = dw_operand(pw[q]);  // kb * BN + r
     __syncthreads();
-    if (b0 + BKB < nb) BQM_FETCH(b0 + BKB)  // in flight while this stage is computed
+    if (b0 + BKB < nb) fetch(b0 + BKB);  // in flight while this stage is computed
 
-    for (int kb = 0; kb < bn; kb++) {
-      i32x4 a[TI], bq[TJ];
-      bf16x8 as[TI], bs[TJ];
+    // unrolled over the stage's blocks, so every LDS read has an immediate offset
 #pragma unroll
-      for (int i = 0; i < TI; i++) {
-        a[i] = *reinterpret_cast<const i32x4*>(sA + (wm + i * 32 + l32) * ROWB + kb * 32 + lh * 16);
-        // lanes 32..63 hold k = 8..15 of the scale product: zeros
-        const u32x4* p = lh ? &sXs[BKB * TBM] : &sXs[kb * TBM + wm + i * 32 + l32];
-        as[i] = __builtin_bit_cast(bf16x8, *p);
-      }
+    for (int kb = 0; kb < BKB; kb++) {
+      if (kb < bn) {
+        i32x4 a[TI], bq[TJ];
+        bf16x8 as[TI], bs[TJ];
 #pragma unroll
-      for (int j = 0; j < TJ; j++) {
-        bq[j] = *reinterpret_cast<const i32x4*>(sB + (wn + j * 32 + l32) * ROWB + kb * 32 + lh * 16);
-        const u32x4* p = lh ? &sXs[BKB * TBM] : &sWs[kb * BN + wn + j * 32 + l32];
-        bs[j] = __builtin_bit_cast(bf16x8, *p);
-      }
-#pragma unroll
-      for (int i = 0; i < TI; i++)
+        for (int i = 0; i < TI; i++) {
+          a[i] = *reinterpret_cast<const i32x4*>(sA + (wm + i * 32 + l32) * ROWB + kb * 32 + lh * 16);
+          as[i] = __builtin_bit_cast(bf16x8, sXs[(kb * 2 + lh) * TBM + wm + i * 32 + l32]);
+        }
 #pragma unroll
         for (int j = 0; j < TJ; j++) {
-          const i32x16 isum = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], bq[j], i32x16{}, 0, 0, 0);
-          const f32x16 sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as[i], bs[j], f32x16{}, 0, 0, 0);
-#pragma unroll
-          for (int r = 0; r < 16; r++) acc[i][j][r] = fmaf(sc[r], (float)isum[r], acc[i][j][r]);
+          bq[j] = *reinterpret_cast<const i32x4*>(sB + (wn + j * 32 + l32) * ROWB + kb * 32 + lh * 16);
+          // lanes 32..63 read the same operand row: it meets the zero half of A
+          bs[j] = __builtin_bit_cast(bf16x8, sWs[kb * BN + wn + j * 32 + l32]);
         }
+#pragma unroll
+        for (int i = 0; i < TI; i++)
+#pragma unroll
+          for (int j = 0; j < TJ; j++) {
+            const i32x16 isum = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], bq[j], i32x16{}, 0, 0, 0);
+            const f32x16 sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as[i], bs[j], f32x16{}, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[i][j][r] = fmaf(sc[r], (float)isum[r], acc[i][j][r]);
+          }
+      }
     }
   }
-#undef BQM_FETCH
 
   // a lane's 16 results of a 32 x 32 tile: rows 8 (r / 4) + 4 lh + r % 4, column l32
 #pragma unroll
@@ -298,7 +317,7 @@ __device__ __forceinline__ void qmm_dense(const uint8_t* __restrict__ Wc, const 
                                           int tiles_n) {
   __shared__ __attribute__((aligned(16))) int8_t sA[BM * ROWB];
   __shared__ __attribute__((aligned(16))) int8_t sB[BN * ROWB];
-  __shared__ u32x4 sXs[BKB * BM + 1];  // dx operands per (block, m); the last: zeros
+  __shared__ u32x4 sXs[BKB * 2 * BM];  // dx operands per (block, m), each block's zero half after it
   __shared__ u32x4 sWs[BKB * BN];      // dw operands per (block, n)
   // Workgroups are dealt round-robin to the eight XCDs; give the workgroups of one XCD
   // neighbouring tiles (all m-tiles of a few n-tiles) so they share W rows in that L2.
@@ -308,8 +327,8 @@ __device__ __forceinline__ void qmm_dense(const uint8_t* __restrict__ Wc, const 
   if (nwg % 8 == 0) tile = (bid % 8) * (nwg / 8) + bid / 8;
   const int tm = tile % tiles_m, tn = tile / tiles_m;
   constexpr int WGM = BM == 32 ? 1 : 2;  // waves along m; each covers 128 / (4 / WGM) columns
-  qmm_core<FMT, WGM, BM / (32 * WGM), WGM, false>(Wc, Wd, Xq, dx, Y, N, nb, tn * BN, tm * BM, M,
-                                                  nullptr, nullptr, sA, sB, sXs, sWs);
+  qmm_core<FMT, WGM, BM / (32 * WGM), WGM, false>(Wc, Wd, Xq, dx, M, Y, N, nb, tn * BN, tm * BM,
+                                                  M, nullptr, nullptr, sA, sB, sXs, sWs);
 }
 
 // Exclusive prefix sum of v over the workgroup's threads (thread order).
@@ -348,10 +367,11 @@ __device__ __forceinline__ void qmm_indexed(const uint8_t* __restrict__ Wc, cons
                                             const int8_t* __restrict__ Xq, const float* __restrict__ dx,
                                             const int32_t* __restrict__ ids, float* __restrict__ Y,
                                             int E, int N, int nb, int TS, int top_k, int xtr, int xsr,
+                                            int64_t x_rows,
                                             int tiles_n) {
   __shared__ __attribute__((aligned(16))) int8_t sA[kIdTBM * ROWB];
   __shared__ __attribute__((aligned(16))) int8_t sB[BN * ROWB];  // first: per-expert counts
-  __shared__ u32x4 sXs[BKB * kIdTBM + 1];
+  __shared__ u32x4 sXs[BKB * 2 * kIdTBM];
   __shared__ u32x4 sWs[BKB * BN];
   __shared__ int xrow[kIdTBM], yrow[kIdTBM];
   __shared__ int wsum[kThreads / 64];
@@ -418,7 +438,7 @@ __device__ __forceinline__ void qmm_indexed(const uint8_t* __restrict__ Wc, cons
   __syncthreads();
   const int64_t wrow = FMT == BQM_Q4_0 ? (int64_t)nb * 16 : (int64_t)nb * 32;
   qmm_core<FMT, kIdWGM, 1, kIdTJ, true>(Wc + (int64_t)e * N * wrow, Wd + (int64_t)e * N * nb, Xq, dx,
-                                        Y, N, nb, tn * BN, 0, 0, xrow, yrow, sA, sB, sXs, sWs);
+                                        x_rows, Y, N, nb, tn * BN, 0, 0, xrow, yrow, sA, sB, sXs, sWs);
 }
 
 #define BQM_QMM_KERNEL(NAME, FMT)                                                              \
@@ -442,8 +462,8 @@ BQM_QMM_KERNEL(k_qmm_q4_0, BQM_Q4_0)
       const uint8_t* __restrict__ Wc, const uint16_t* __restrict__ Wd,                         \
       const int8_t* __restrict__ Xq, const float* __restrict__ dx,                             \
       const int32_t* __restrict__ ids, float* __restrict__ Y, int E, int N, int nb, int TS,    \
-      int top_k, int xtr, int xsr, int tiles_n) {                                              \
-    qmm_indexed<FMT>(Wc, Wd, Xq, dx, ids, Y, E, N, nb, TS, top_k, xtr, xsr, tiles_n);          \
+      int top_k, int xtr, int xsr, int64_t x_rows, int tiles_n) {                              \
+    qmm_indexed<FMT>(Wc, Wd, Xq, dx, ids, Y, E, N, nb, TS, top_k, xtr, xsr, x_rows, tiles_n);  \
   }
 BQM_QMM_ID_KERNEL(k_qmm_id_q8_0, BQM_Q8_0)
 BQM_QMM_ID_KERNEL(k_qmm_id_q4_0, BQM_Q4_0)
@@ -460,8 +480,16 @@ int launch_quantize_q8_act(const float* X, int8_t* Xq, float* dx, int64_t M, int
   return launch_status();
 }
 
+// The kernels address each operand through a buffer descriptor with 32-bit offsets.
+static bool fits_descriptors(int fmt, int64_t x_rows, int64_t N, int64_t K) {
+  const int64_t lim = (int64_t)1 << 31;
+  const int64_t wrow = fmt == BQM_Q4_0 ? K / 2 : K;  // code bytes per weight row
+  return x_rows * K < lim && x_rows * (K / 32) * 4 < lim && N * wrow < lim && N * (K / 32) * 2 < lim;
+}
+
 static int launch_qmm(int fmt, const void* w, const int8_t* Xq, const float* dx, float* Y,
                       int64_t M, int64_t N, int64_t K, hipStream_t s) {
+  if (!fits_descriptors(fmt, M, N, K)) return BQM_E_SHAPE;
   Layout L;
   layout_of(fmt, N, K, &L);
   const uint8_t* Wc = static_cast<const uint8_t*>(w);
@@ -495,10 +523,12 @@ int launch_qmm_id(int fmt, const void* w, int E, int64_t N, int64_t K, const int
   // row tiles: at most one partial tile per expert that has slots, plus the full ones
   const int64_t max_tm = (TS < E ? TS : E) + (TS + kIdTBM - 1) / kIdTBM;
   const int64_t grid = max_tm * tiles_n;
-  if (grid >= ((int64_t)1 << 31)) return BQM_E_SHAPE;
+  // input rows the slots can address: row (T - 1) x_tok_rows + (top_k - 1) x_slot_rows at most
+  const int64_t x_rows = (int64_t)(T - 1) * x_tok_rows + (int64_t)(top_k - 1) * x_slot_rows + 1;
+  if (grid >= ((int64_t)1 << 31) || !fits_descriptors(fmt, x_rows, N, K)) return BQM_E_SHAPE;
   hipLaunchKernelGGL(fmt == BQM_Q4_0 ? k_qmm_id_q4_0 : k_qmm_id_q8_0, dim3((unsigned)grid),
                      dim3(kThreads), 0, s, Wc, Wd, Xq, dx, ids, Y, E, (int)N, (int)L.nb, TS, top_k,
-                     (int)x_tok_rows, (int)x_slot_rows, tiles_n);
+                     (int)x_tok_rows, (int)x_slot_rows, x_rows, tiles_n);
   return launch_status();
 }
 

@@ -386,6 +386,8 @@ __device__ __forceinline__ bool grid_barrier(uint32_t* ws, uint32_t epoch, bool*
   return *lds_ok;
 }
 
+// Largest batch class (slots per group) of the indexed form.
+constexpr int kIdMaxClass = 4;
 // Slots of the indexed form, at most (its tables are built in LDS).
 constexpr int kIdMaxSlots = BQM_QMV_ID_MAX_T * BQM_QMV_ID_MAX_TOPK;
 // LDS rows (64 bytes) the indexed form's tables take: per-expert counts (E + 1), the slots
@@ -1257,9 +1259,9 @@ int launch_qmv(int fmt, const void* w, const float* X, float* Y, int M, int64_t 
 }
 
 // Expert-indexed GEMV: the chain kernel's indexed form, with E * N rows as one matrix.  The
-// batch class is that of min(T, 8): one token usually adds at most one slot to an expert,
-// so up to 8 tokens stream each selected expert once; an expert with more slots is
-// streamed once per group of 8.  With `w_up`, the gate+up form: each lane takes gate row n
+// batch class is that of min(T, 4): one token usually adds at most one slot to an expert,
+// so up to 4 tokens stream each selected expert once; an expert with more slots is
+// streamed once per group of 4.  With `w_up`, the gate+up form: each lane takes gate row n
 // and up row n of the expert, and the output is silu(gate) * up.
 static int launch_id(int fmt, const void* w, const void* w_up, int E, int64_t N, int64_t K,
               const int32_t* ids, int T, int top_k, const float* X, int64_t xts, int64_t xss,
@@ -1268,7 +1270,11 @@ static int launch_id(int fmt, const void* w, const void* w_up, int E, int64_t N,
   Layout L;
   layout_of(fmt, (int64_t)E * N, K, &L);
   const int CB = fmt == BQM_Q4_0 ? 16 : 32;
-  const int mm = m_class(T < kChainMaxM ? T : kChainMaxM);
+  // Groups of at most 4 slots (batch class 4, 16 waves): with top-8 routing an expert
+  // rarely gets more than a few of T tokens, so a class-8 group mostly computes empty
+  // inputs on half the waves (128-expert MoE layer, T = 16: 0.271 -> 0.183 ms per layer;
+  // class 2 re-reads the popular experts too often: 0.190).
+  const int mm = m_class(T < kIdMaxClass ? T : kIdMaxClass);
   const int cus = cu_count();
   // a workgroup's rows of one group: its share of the groups' rows (at most TS groups of N)
   int64_t rows = ((int64_t)TS * N + cus - 1) / cus;

@@ -105,7 +105,7 @@ def test_qmv_id_deterministic():
 @pytest.mark.parametrize("fmt", ["q4_0", "q8_0"])
 @pytest.mark.parametrize("T", [2, 3, 5, 8])
 def test_qmv_id_batch_classes(fmt, T):
-    """T tokens run in the batch class of min(T, 8) (2, 4, 8, 8): groups of every size,
+    """T tokens run in the batch class of min(T, 4) (2, 4, 4, 4): groups of every size,
     some shorter than the class, with padding slots among them."""
     E, N, K, top_k = 6, 130, 1184, 3
     ids = gen.router_ids(T, E, top_k, ("cls-router", T))

@@ -79,9 +79,11 @@ template <> struct Codes<FQ8> { u32x4 a, b; };
 //    the next GEMV do not depend on its input, so they stream while the workgroup waits for
 //    the previous GEMV's outputs (device-wide barrier) and stages the new x.
 // Arithmetic per block and row: 8 ANDs (Q8_0: XORs) and 32 v_cvt_f32_ubyte, shared by the
-// M inputs; per input 32 FMAs in one chain, then r = chain - 8 * sum(x) (Q8_0: - 128 *
-// sum(x)) and acc += d * r (v_fma_mix: d stays fp16).  The chain and the block sum follow
-// the same order and 8, 128 and 1/16 are powers of two, so neutral codes give exactly zero.
+// M inputs; per input the block's products summed by multiply-adds (batches 1 and 2: eight
+// chains of four and a fixed tree over them; wider batches: one chain of 32), then
+// r = sum - 8 * sum(x) (Q8_0: - 128 * sum(x)) and acc += d * r (v_fma_mix: d stays fp16).
+// The products and the block sum of x follow the same order and 8, 128 and 1/16 are powers
+// of two, so neutral codes give exactly zero.
 constexpr int kP1Waves = 16;  // waves of a workgroup (8 for the widest batch: registers)
 constexpr int kBlkLds = 144;  // LDS bytes per staged block
 constexpr int kChainMaxM = 8;
@@ -96,11 +98,83 @@ constexpr int kChainMaxM = 8;
 constexpr int kLg2G = BQM_LG2G, kG = 1 << kLg2G, kGpw = 64 >> kLg2G;
 static_assert(kLg2G >= 3 && kLg2G <= 4, "group_sum covers 8 or 16 lanes");
 
+// Order of a block's sums (batches 1 and 2).  A block is eight chunks of four positions
+// (the 16-byte pieces of its staged input); a chunk's sum runs over its four positions in
+// order, and the block's sum is the tree ((c0 + c1) + (c2 + c3)) + ((c4 + c5) + (c6 + c7)).
+// The code chains below and the block sums of the staged inputs both follow it, so that
+// codes all equal to the offset give exactly zero; the tree lets eight lanes form a block's
+// input sum in three steps (the sum in position order took one lane 32 steps: 3 % of the
+// 27B Q4_0 pass).
+template <int K, int MM>
+__device__ __forceinline__ void tree_add(const float (&ck)[MM], float (&pr)[MM], float (&qd)[MM],
+                                         float (&hf)[MM], float (&c)[MM]) {
+#pragma unroll
+  for (int m = 0; m < MM; m++) {
+    if constexpr (K % 2 == 0) pr[m] = ck[m];
+    else pr[m] = pr[m] + ck[m];
+    if constexpr (K % 4 == 1) qd[m] = pr[m];
+    if constexpr (K % 4 == 3) qd[m] = qd[m] + pr[m];
+    if constexpr (K == 3) hf[m] = qd[m];
+    if constexpr (K == 7) c[m] = hf[m] + qd[m];
+  }
+}
+
 // One block of codes against MM staged input blocks (input m at xb + m * mstride bytes):
-// c[m] = sum_j code_j * x_mj in chain order (positions 0..15, then 16..31).
+// c[m] = sum_j code_j * x_mj in the order above (positions 0..15, then 16..31).
 template <int FMT, int MM>
-__device__ __forceinline__ void chain_block(const Codes<FMT>& q, const char* xb, int mstride,
-                                            float (&c)[MM]) {
+__device__ __forceinline__ void chain_block_tree(const Codes<FMT>& q, const char* xb, int mstride,
+                                                 float (&c)[MM]) {
+  auto xm = [&](int m, int k) { return *reinterpret_cast<const f32x4*>(xb + m * mstride + k * 16); };
+  float ck[MM], pr[MM], qd[MM], hf[MM];
+  auto chunk = [&](uint32_t u, int k) {  // the four codes in u's bytes against chunk k
+    const float v0 = ub(u, 0), v1 = ub(u, 1), v2 = ub(u, 2), v3 = ub(u, 3);
+#pragma unroll
+    for (int m = 0; m < MM; m++) {
+      const f32x4 a = xm(m, k);
+      ck[m] = v0 * a.x;
+      ck[m] = fmaf(v1, a.y, ck[m]); ck[m] = fmaf(v2, a.z, ck[m]); ck[m] = fmaf(v3, a.w, ck[m]);
+    }
+  };
+  if constexpr (FMT == FQ4) {
+    uint32_t l[4], h[4];
+    const uint32_t w[4] = {q.a.x, q.a.y, q.a.z, q.a.w};
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      l[k] = w[k] & 0x0F0F0F0Fu;
+      h[k] = w[k] & 0xF0F0F0F0u;  // 16 * high nibble, in place
+      asm("" : "+v"(l[k]), "+v"(h[k]));  // keep the conversions as v_cvt_f32_ubyte{0..3}
+    }
+    chunk(l[0], 0); tree_add<0>(ck, pr, qd, hf, c);
+    chunk(l[1], 1); tree_add<1>(ck, pr, qd, hf, c);
+    chunk(l[2], 2); tree_add<2>(ck, pr, qd, hf, c);
+    chunk(l[3], 3); tree_add<3>(ck, pr, qd, hf, c);
+    chunk(h[0], 4); tree_add<4>(ck, pr, qd, hf, c);
+    chunk(h[1], 5); tree_add<5>(ck, pr, qd, hf, c);
+    chunk(h[2], 6); tree_add<6>(ck, pr, qd, hf, c);
+    chunk(h[3], 7); tree_add<7>(ck, pr, qd, hf, c);
+  } else {
+    uint32_t u[8] = {q.a.x, q.a.y, q.a.z, q.a.w, q.b.x, q.b.y, q.b.z, q.b.w};
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      u[k] ^= 0x80808080u;  // q + 128 as unsigned bytes
+      asm("" : "+v"(u[k]));
+    }
+    chunk(u[0], 0); tree_add<0>(ck, pr, qd, hf, c);
+    chunk(u[1], 1); tree_add<1>(ck, pr, qd, hf, c);
+    chunk(u[2], 2); tree_add<2>(ck, pr, qd, hf, c);
+    chunk(u[3], 3); tree_add<3>(ck, pr, qd, hf, c);
+    chunk(u[4], 4); tree_add<4>(ck, pr, qd, hf, c);
+    chunk(u[5], 5); tree_add<5>(ck, pr, qd, hf, c);
+    chunk(u[6], 6); tree_add<6>(ck, pr, qd, hf, c);
+    chunk(u[7], 7); tree_add<7>(ck, pr, qd, hf, c);
+  }
+}
+
+// The same with the sums in plain position order (the wider batches: their registers do
+// not hold the tree's partial sums for every input).
+template <int FMT, int MM>
+__device__ __forceinline__ void chain_block_seq(const Codes<FMT>& q, const char* xb, int mstride,
+                                                float (&c)[MM]) {
   auto xm = [&](int m, int k) { return *reinterpret_cast<const f32x4*>(xb + m * mstride + k * 16); };
   if constexpr (FMT == FQ4) {
     uint32_t l[4], h[4];
@@ -148,9 +222,19 @@ __device__ __forceinline__ void chain_block(const Codes<FMT>& q, const char* xb,
   }
 }
 
-// Sum over the lane group of 16, 32 or 64 lanes holding one row (every lane gets the sum):
-// DPP exchanges within 16-lane rows, then cross-row exchanges.  The partners of each step
-// add the same two values, so all lanes hold bitwise the same result.
+// Batches 1 and 2 sum in the tree order, wider ones in position order.
+template <int MM>
+constexpr bool kTreeOrder = MM <= 2;
+template <int FMT, int MM>
+__device__ __forceinline__ void chain_block(const Codes<FMT>& q, const char* xb, int mstride,
+                                            float (&c)[MM]) {
+  if constexpr (kTreeOrder<MM>) chain_block_tree<FMT, MM>(q, xb, mstride, c);
+  else chain_block_seq<FMT, MM>(q, xb, mstride, c);
+}
+
+// Sum over the lane group of 16 (or 8) lanes holding one row (every lane gets the sum): DPP
+// exchanges within the 16-lane row.  The partners of each step add the same two values, so
+// all lanes hold bitwise the same result.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v),
@@ -822,22 +906,36 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
             f32x4 w = v[q];
             if (FMT == FQ4 && i >= 4) w = w * 0.0625f;
             if (c < nch) *reinterpret_cast<f32x4*>(xm + blk * kBlkLds + i * 16) = w;
-            asm volatile("" ::: "memory");
-            const int b = (c0 >> 3) + lane;
-            if (lane < 8 && b < sc.nbc) {
-              const f32x4* xl = reinterpret_cast<const f32x4*>(xm + b * kBlkLds);
-              float s = xl[0].x;
-              s = s + xl[0].y; s = s + xl[0].z; s = s + xl[0].w;
+            if constexpr (kTreeOrder<MM>) {
+              // the block's input sum in the chains' order: this lane's chunk as staged
+              // (Q4_0 high chunks multiplied back by 16, exact), then pairs, quads and
+              // halves of the block's eight lanes (lanes past the end hold zeros)
+              const float mu = FMT == FQ4 && i >= 4 ? 16.0f : 1.0f;
+              float sx = w.x * mu;
+              sx = sx + w.y * mu; sx = sx + w.z * mu; sx = sx + w.w * mu;
+              sx = sx + dpp<0xB1>(sx);   // lane ^ 1
+              sx = sx + dpp<0x4E>(sx);   // lane ^ 2
+              sx = sx + dpp<0x141>(sx);  // the other quad of the eight
+              if (i == 0 && c < nch) *reinterpret_cast<float*>(xm + blk * kBlkLds + 128) = sx;
+            } else {
+              // position order: one lane per block, over the values as staged
+              asm volatile("" ::: "memory");
+              const int b = (c0 >> 3) + lane;
+              if (lane < 8 && b < sc.nbc) {
+                const f32x4* xl = reinterpret_cast<const f32x4*>(xm + b * kBlkLds);
+                float sx = xl[0].x;
+                sx = sx + xl[0].y; sx = sx + xl[0].z; sx = sx + xl[0].w;
 #pragma unroll
-              for (int k = 1; k < 4; k++) { s = s + xl[k].x; s = s + xl[k].y; s = s + xl[k].z; s = s + xl[k].w; }
-              const float mu = FMT == FQ4 ? 16.0f : 1.0f;
+                for (int k = 1; k < 4; k++) { sx = sx + xl[k].x; sx = sx + xl[k].y; sx = sx + xl[k].z; sx = sx + xl[k].w; }
+                const float mu = FMT == FQ4 ? 16.0f : 1.0f;
 #pragma unroll
-              for (int k = 4; k < 8; k++) {
-                s = s + xl[k].x * mu; s = s + xl[k].y * mu; s = s + xl[k].z * mu; s = s + xl[k].w * mu;
+                for (int k = 4; k < 8; k++) {
+                  sx = sx + xl[k].x * mu; sx = sx + xl[k].y * mu; sx = sx + xl[k].z * mu; sx = sx + xl[k].w * mu;
+                }
+                *reinterpret_cast<float*>(xm + b * kBlkLds + 128) = sx;
               }
-              *reinterpret_cast<float*>(xm + b * kBlkLds + 128) = s;
+              asm volatile("" ::: "memory");
             }
-            asm volatile("" ::: "memory");
           }
         }
       }

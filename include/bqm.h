@@ -208,7 +208,9 @@ int bqm_quantize_q8_act(const float* X, int8_t* Xq, float* dx, int64_t M, int64_
  * The scale product d_w * dx comes from the matrix cores as an fp32 sum of six exact
  * partial products (d_w and dx split into bf16 parts); it may differ from the correctly
  * rounded product in the last bits, well within the float tolerance.
- * w_packed: packed Q8_0 N x K matrix.  Xq, dx: from bqm_quantize_q8_act.  Y: fp32 [M][N]. */
+ * w_packed: packed Q8_0 N x K matrix.  Xq, dx: from bqm_quantize_q8_act.  Y: fp32 [M][N].
+ * Operands are addressed with 32-bit offsets: M*K or N*K code bytes of 2 GiB or more give
+ * BQM_E_SHAPE. */
 int qmm_q8_0(const void* w_packed, const int8_t* Xq, const float* dx, float* Y, int64_t M,
              int64_t N, int64_t K, hipStream_t stream);
 
@@ -233,7 +235,8 @@ int qmm_q4_0(const void* w_packed, const int8_t* Xq, const float* dx, float* Y, 
  * [T][top_k].  Xq, dx: quantized activations from bqm_quantize_q8_act, rows as indexed
  * above (x_tok_rows = 1, x_slot_rows = 0: one row per token; top_k, 1: one per slot).
  * Y: fp32 [T][top_k][N].  Padding slots (negative id) give zero rows, ids >= E NaN rows.
- * Limits: T <= BQM_QMM_ID_MAX_T, top_k <= 32, E <= 4096, input rows below 2^31. */
+ * Limits: T <= BQM_QMM_ID_MAX_T, top_k <= 32, E <= 4096; the input rows the slots address,
+ * and one expert's codes, below 2 GiB (else BQM_E_SHAPE). */
 int qmm_id(int fmt, const void* w_packed, int E, int64_t N, int64_t K, const int32_t* ids, int T,
            int top_k, const int8_t* Xq, const float* dx, int64_t x_tok_rows, int64_t x_slot_rows,
            float* Y, hipStream_t stream);

@@ -122,6 +122,11 @@ def test_host_validation_before_launch():
     assert L.qmm_id(2, None, 4, 8, 64, GOOD, 1, 2, GOOD, GOOD, 1, 0, GOOD, None) == 1
     assert L.qmm_id(2, GOOD, 4, 8, 64, GOOD, 1, 2, GOOD, GOOD, 1, 0, ODD, None) == 3
     assert L.qmm_id(2, ODD, 4, 8, 64, GOOD, 1, 2, GOOD, GOOD, 1, 0, GOOD, None) == 3
+    # prefill operands are addressed with 32-bit offsets: 2 GiB of activations or of one
+    # matrix's codes is refused before any launch
+    assert L.qmm_q8_0(GOOD, GOOD, GOOD, GOOD, 1 << 17, 8, 1 << 14, None) == 2
+    assert L.qmm_q8_0(GOOD, GOOD, GOOD, GOOD, 4, 1 << 17, 1 << 14, None) == 2
+    assert L.qmm_id(2, GOOD, 4, 8, 1 << 14, GOOD, 16384, 32, GOOD, GOOD, 32, 1, GOOD, None) == 2
     # repack alignment: interchange needs 2-byte alignment, packed 16
     assert L.bqm_repack(2, P(0x100001), GOOD, 4, 64, None) == 3
     assert L.bqm_repack(2, GOOD, ODD, 4, 64, None) == 3

@@ -22,8 +22,9 @@
  *
  * Conventions shared by every call:
  *   - Pointers are DEVICE pointers unless stated; the caller owns all memory.  The
- *     library allocates nothing, frees nothing and never synchronizes: work is queued
- *     on `stream` (a HIP stream; 0 = the null stream) and the call returns.
+ *     library allocates nothing and frees nothing; work is queued on `stream` (a HIP
+ *     stream; 0 = the null stream) and the call returns without synchronizing (only
+ *     bqm_chain_prepare and bqm_chain_status wait, as their entries say).
  *   - Argument errors are found on the host before anything is launched: the call
  *     returns a non-zero bqm_status and leaves every output untouched.  A failed launch
  *     returns BQM_E_LAUNCH.  Faults inside a kernel surface at the caller's next
@@ -31,8 +32,8 @@
  *   - Sizes may be zero (nothing is launched, except that N > 0 with K = 0 writes
  *     zeros, the value of an empty sum).  K must be a multiple of 32.
  *   - Pointers passed to the products must be 16-byte aligned (torch allocations are).
- *   - Outputs must not alias inputs.  Results are deterministic: no atomics, a fixed
- *     summation order, the same bits on every run with the same launch.
+ *   - Outputs must not alias inputs.  Results are deterministic: no atomic updates of
+ *     data, a fixed summation order, the same bits on every run with the same launch.
  *   - Floating-point outputs are fp32 and satisfy, per output,
  *         |y - y_exact| <= 1e-3 * sum_i |w_i * x_i|
  *     (y_exact in exact arithmetic); integer and byte outputs are exact.

@@ -160,6 +160,10 @@ __device__ __forceinline__ void qmm_core(const uint8_t* __restrict__ Wc, const u
     else return m0 + r < M ? m0 + r : -1;
   };
 
+  // Gathered rows fill a tile from its first row, so a wave whose first row has no input
+  // row has nothing to compute (it still loads and stages its pieces for the other waves).
+  const bool live = !GATHER || __builtin_amdgcn_readfirstlane(in_row(wm)) >= 0;
+
   f32x16 acc[TI][TJ];
 #pragma unroll
   for (int i = 0; i < TI; i++)
@@ -263,7 +267,7 @@ __device__ __forceinline__ void qmm_core(const uint8_t* __restrict__ Wc, const u
     // unrolled over the stage's blocks, so every LDS read has an immediate offset
 #pragma unroll
     for (int kb = 0; kb < BKB; kb++) {
-      if (kb < bn) {
+      if (kb < bn && live) {
         i32x4 a[TI], bq[TJ];
         bf16x8 as[TI], bs[TJ];
 #pragma unroll

@@ -240,6 +240,20 @@ def run_dense(args, torch, gen, bqm, fmt="q4_0"):
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": kernel, "avg_launch_us": launch_us},
     }
+    # The vector-ALU ceiling: each weight takes at least M fp32 multiply-adds (one per input
+    # row; packed fp32 is not used) and one code conversion.  Where that ceiling is below
+    # the HBM one (Q8_0 at M = 8), it is the binding roofline and is reported as such.
+    nweights = sum(N * K for _, N, K in mats)
+    lane_ops = nweights * (M + 1)
+    alu_ceiling_gbs = VALU_PEAK_TOPS * 1e12 / (M + 1) * (wbytes / nweights) / 1e9
+    res["alu_ceiling_gbs"] = round(alu_ceiling_gbs, 1)
+    res["hbm_frac"] = round(achieved / HBM_PEAK_GBS, 4)
+    if alu_ceiling_gbs < HBM_PEAK_GBS:
+        valu_t = lane_ops / (float(dur.mean() if use_chain else dur.sum()) * 1e-3) / 1e12
+        res["roofline"] = {"bound": "alu", "achieved": round(valu_t, 3), "peak": round(VALU_PEAK_TOPS, 4),
+                           "unit": "T lane-op/s", "frac": round(valu_t / VALU_PEAK_TOPS, 4),
+                           "traffic": traffic, "kernel": kernel, "avg_launch_us": launch_us,
+                           "hbm_gbs": round(achieved, 1)}
     if fmt == "q8_0":
         res["equiv_tok_s_aggregate"] = round(M * 1e3 / ms, 2)
     if not args.no_cpu:

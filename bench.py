@@ -136,13 +136,13 @@ def traffic_from_profiles(kernel_key):
 
 # --------------------------------------------------------------------- CPU baseline
 
-def cpu_baseline(fmt, shapes, key_of, seconds, torch, gen, unit="GB/s", M=1):
+def cpu_baseline(fmt, shapes, key_of, seconds, torch, gen, unit="GB/s", M=1, limit=64, what="layers"):
     """The oracle (never tuned) on the host cores, on whole layers of the same stream until
     about `seconds` of work is done; rate in the metric's unit over the same bytes."""
     import oracle
     oracle.build(force=False)
     done_bytes, t_used, layers = 0, 0.0, 0
-    while t_used < seconds and layers < 64:
+    while t_used < seconds and layers < limit:
         for name, N, K in shapes:
             wi = (gen.encode_q4_0 if fmt == "q4_0" else gen.encode_q8_0)(
                 gen.normal((N, K), key_of(layers, name), std=0.02, device="cuda"))
@@ -155,8 +155,94 @@ def cpu_baseline(fmt, shapes, key_of, seconds, torch, gen, unit="GB/s", M=1):
         layers += 1
     return {"value": round(done_bytes / t_used / 1e9, 4), "unit": unit, "cores": oracle.threads(),
             "kind": "oracle",
-            "sample": f"{layers} of the 64 layers ({len(shapes)} GEMVs each), full rows, "
+            "sample": f"{layers} of the {limit} {what} ({len(shapes)} GEMVs each), full rows, "
                       f"{t_used:.1f} s of oracle time"}
+
+
+def _host_blocks(fmt, N, K, key, gen):
+    """Interchange blocks of the seeded weights (the same draws as make_matrix), on the host."""
+    w = gen.normal((N, K), key, std=0.02, device="cuda")
+    wi = gen.encode_q4_0(w) if fmt == "q4_0" else gen.encode_q8_0(w)
+    del w
+    return wi.cpu().numpy()
+
+
+def cpu_baseline_moe(T, E, top_k, H, F, seconds, gen):
+    """The oracle's expert-indexed GEMV (gate, up, down of one layer, the definition: every
+    slot's rows in turn) on the host cores; GB/s over the same unique-expert and activation
+    bytes as the GPU figure."""
+    import oracle
+    oracle.build(force=False)
+    gate = _host_blocks("q4_0", E * F, H, ("moe", 0, "gate"), gen)
+    up = _host_blocks("q4_0", E * F, H, ("moe", 0, "up"), gen)
+    down = _host_blocks("q4_0", E * H, F, ("moe", 0, "down"), gen)
+    ids = gen.router_ids(T, E, top_k, ("moe-ids", 0, T))
+    x = gen.normal((T, H), ("moe-x", 0, T), device="cuda").cpu().numpy()
+    xd = gen.normal((T, top_k, F), ("moe-xd", 0, T), device="cuda").cpu().numpy()
+    uniq = len(np.unique(ids))
+    per = uniq * (weight_bytes("q4_0", F, H) * 2 + weight_bytes("q4_0", H, F)) + \
+        4 * (2 * T * H + 2 * T * top_k * F + T * top_k * F + T * top_k * H)
+    done, t_used, reps = 0, 0.0, 0
+    while t_used < seconds and reps < 64:
+        t = time.perf_counter()
+        oracle.qmv_id("q4_0", gate, E, F, H, ids, x, H, 0)
+        oracle.qmv_id("q4_0", up, E, F, H, ids, x, H, 0)
+        oracle.qmv_id("q4_0", down, E, H, F, ids, xd, top_k * F, F)
+        t_used += time.perf_counter() - t
+        done += per
+        reps += 1
+    return {"value": round(done / t_used / 1e9, 4), "unit": "GB/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"layer 0 of 8 at T = {T} (gate, up, down; {uniq} unique experts), "
+                      f"{reps} passes, {t_used:.1f} s of oracle time"}
+
+
+def cpu_baseline_qmm(fmt, M, N, K, key, xkey, seconds, gen):
+    """The oracle's prefill product (int32 block sums, fp64 rescale) on the host cores over
+    leading row ranges of the same weights, until about `seconds` of work; int8 TOP/s."""
+    import oracle
+    oracle.build(force=False)
+    W = _host_blocks(fmt, N, K, key, gen).reshape(N, -1)
+    X = gen.normal((M, K), xkey, device="cuda").cpu().numpy()
+    Xq, dx = oracle.quantize_q8_act(X, K)   # the oracle's own quantizer
+    fn = oracle.qmm_q4_0 if fmt == "q4_0" else oracle.qmm_q8_0
+    rows, t_used, chunk = 0, 0.0, 64
+    while t_used < seconds and rows < N:
+        n = min(chunk, N - rows)
+        t = time.perf_counter()
+        fn(W[rows:rows + n], Xq, dx, n, K)
+        t_used += time.perf_counter() - t
+        rows += n
+        chunk = min(4 * chunk, 1024)
+    return {"value": round(2.0 * M * rows * K / t_used / 1e12, 6), "unit": "TOP/s",
+            "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"output columns 0..{rows - 1} of {N} (all {M} rows, K = {K}), "
+                      f"{t_used:.1f} s of oracle time"}
+
+
+def cpu_baseline_qmm_id(E, top_k, H, F, T, seconds, gen):
+    """The oracle's expert-indexed prefill product (gate projection of layer 0) on the host
+    cores, over the first rows of every expert, until about `seconds` of work; TOP/s of
+    useful int8 products."""
+    import oracle
+    oracle.build(force=False)
+    gate = _host_blocks("q4_0", E * F, H, ("moep", 0, "gate"), gen).reshape(E, F, -1)
+    ids = gen.router_ids(T, E, top_k, ("moep-ids", 0))
+    x = gen.normal((T, H), ("moep-x", 0), device="cuda").cpu().numpy()
+    xq, xdx = oracle.quantize_q8_act(x, H)
+    n, t_used = 8, 0.0
+    while True:
+        Wn = np.ascontiguousarray(gate[:, :n])
+        t = time.perf_counter()
+        oracle.qmm_id("q4_0", Wn, E, n, H, ids, xq, xdx, 1, 0)
+        t_used = time.perf_counter() - t
+        if t_used >= seconds / 4 or n >= F:
+            break
+        n = min(F, n * 4)
+    return {"value": round(2.0 * T * top_k * n * H / t_used / 1e12, 6), "unit": "TOP/s",
+            "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"gate projection of layer 0, output rows 0..{n - 1} of {F} of every expert, "
+                      f"all {T * top_k} slots, {t_used:.1f} s of oracle time"}
 
 
 # --------------------------------------------------------------------- workloads
@@ -306,7 +392,10 @@ def run_gemv4096(args, torch, gen, bqm):
                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                          "traffic": traffic_from_profiles("qmv_chain_q4_0_gemv4096"),
                          "kernel": "k_qmv_chain (Q4_0, M=1, 64 GEMVs per launch)",
-                         "avg_launch_us": round(1e3 * float(dur.mean()), 3)}}
+                         "avg_launch_us": round(1e3 * float(dur.mean()), 3)},
+            **({} if args.no_cpu else {"cpu_baseline": cpu_baseline(
+                "q4_0", [("w", N, K)], lambda c, n: ("gemv4096", c), args.cpu_seconds, torch, gen,
+                limit=copies, what="weight copies")})}
 
 
 def run_moe(args, torch, gen, bqm):
@@ -423,6 +512,9 @@ def run_moe(args, torch, gen, bqm):
                                      "avg_launch_us": round(1e3 * float(sdur.mean()), 3)}}})
         del layers, rws, youts
         torch.cuda.empty_cache()
+        if not args.no_cpu:
+            say(f"timing the oracle on the host (T = {T}) ...")
+            out[-1]["cpu_baseline"] = cpu_baseline_moe(T, E, top_k, H, F, args.cpu_seconds / 2, gen)
     return {"metric": "MoE qmv_id achieved HBM GB/s over unique-expert bytes", "value": out[0]["gbs_unique_bytes"],
             "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": out[0]["ms_per_layer"] * n_layers, "higher_is_better": True,
@@ -430,6 +522,7 @@ def run_moe(args, torch, gen, bqm):
             "config": {"workload": "128-expert MoE layer (gate/up 4096->1536, down 1536->4096, Q4_0, top-8), "
                                    "8 distinct layers per step"},
             "roofline": out[0]["roofline"],
+            **({} if args.no_cpu else {"cpu_baseline": out[0]["cpu_baseline"]}),
             "by_T": out}
 
 
@@ -472,7 +565,9 @@ def run_prefill(args, torch, gen, bqm, fmt="q8_0"):
                          "traffic": traffic_from_profiles(f"qmm_{fmt}_prefill"),
                          "kernel": f"k_qmm_{fmt}", "avg_launch_us": round(1e3 * float(dur.mean()), 3),
                          "mfma_int8_frac": round(tops / INT8_PEAK_TOPS, 4)},
-            "quantize_us": round(1e3 * float(qdur.mean()), 3)}
+            "quantize_us": round(1e3 * float(qdur.mean()), 3),
+            **({} if args.no_cpu else {"cpu_baseline": cpu_baseline_qmm(
+                fmt, M, N, K, ("prefill", 0), ("prefill-x", 0), args.cpu_seconds, gen)})}
 
 
 def run_prefill_moe(args, torch, gen, bqm):
@@ -534,7 +629,9 @@ def run_prefill_moe(args, torch, gen, bqm):
                          "unit": "T lane-op/s", "frac": round(valu_t / VALU_PEAK_TOPS, 4),
                          "traffic": traffic_from_profiles("qmm_id_q4_0_moe_prefill"),
                          "kernel": "k_qmm_id_q4_0", "avg_launch_us": round(1e3 * float(dur.mean()), 3),
-                         "mfma_int8_frac": round(tops / INT8_PEAK_TOPS, 4)}}
+                         "mfma_int8_frac": round(tops / INT8_PEAK_TOPS, 4)},
+            **({} if args.no_cpu else {"cpu_baseline": cpu_baseline_qmm_id(
+                E, top_k, H, F, T, args.cpu_seconds, gen)})}
 
 
 def main():

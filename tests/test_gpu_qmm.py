@@ -245,3 +245,25 @@ def test_qmm_id_deterministic_and_empty_k():
                torch.zeros(64, dtype=torch.int8, device=DEV), torch.zeros(16, device=DEV), 1, 0, Y)
     y = host(Y)
     assert np.all(y[0] == 0) and np.all(y[1, 0] == 0) and np.all(np.isnan(y[1, 1]))
+
+
+@pytest.mark.parametrize("T,top_k", [(bqm.QMM_ID_MAX_T, 2), (64, 32)])
+def test_qmm_id_at_the_limits(T, top_k):
+    """The largest token count (and the largest top-k) over the most experts, with short
+    rows: every workgroup counts T * top_k ids; a sample of slots against the oracle, and
+    the out-of-range ids (negative: zeros; >= E: NaN) checked everywhere."""
+    E, N, K = bqm.QMV_ID_MAX_E, 64, 32
+    rng = np.random.default_rng(11)
+    ids = rng.integers(0, E, (T, top_k)).astype(np.int32)
+    ids[0, 0] = -1
+    ids[1, -1] = E
+    ids[T - 1, 0] = E + 7
+    sample = np.unique(np.concatenate([rng.integers(0, T * top_k, 160), [0, T * top_k - 1]]))
+    say("qmm_id limits", T, top_k, E)
+    y, Yr, S = run_qmm_id("q8_0", E, N, K, ids, "per_slot", ("qmmid-lim", T, top_k), sample=sample)
+    flat, valid = y.reshape(T * top_k, N), (ids >= 0) & (ids < E)
+    keep = valid.ravel()[sample]
+    check_close(flat[sample][keep], Yr.reshape(T * top_k, N)[sample][keep],
+                S.reshape(T * top_k, N)[sample][keep], "qmm_id at the limits")
+    assert np.all(y[0, 0] == 0)
+    assert np.all(np.isnan(y[1, -1])) and np.all(np.isnan(y[T - 1, 0]))

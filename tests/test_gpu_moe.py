@@ -210,6 +210,25 @@ def test_gate_up_batch_classes(fmt, T):
     check_close(y[~bad], Yr[~bad], S[~bad], f"gate_up {fmt} T={T}")
 
 
+def test_gate_up_maximum_slots_and_experts():
+    """The gate+up form at the limits: T = 64 tokens x top_k = 32 slots over E = 4096
+    experts, crowded onto 64 of them, with padding and out-of-range ids mixed in."""
+    from block_quantized_matrix_amd import bqm as b
+    E, N, K, T, top_k = b.QMV_ID_MAX_E, 8, 64, b.QMV_ID_MAX_T, b.QMV_ID_MAX_TOPK
+    rng = np.random.default_rng(17)
+    ids = rng.integers(0, 64, size=(T, top_k)).astype(np.int32) * 64
+    ids[::3, 5] = rng.integers(0, E, size=ids[::3, 5].shape)
+    ids[1::7, 2] = -1
+    ids[2::9, 9] = E + 5
+    X = gen.normal((T, K), ("gu-max-x",), device=DEV)
+    say("gate_up max slots")
+    y, Yr, S = run_gate_up("q4_0", E, N, K, ids, X, K, 0, ("gu-max",))
+    bad = ids >= E
+    assert np.all(np.isnan(y[bad]))
+    assert np.all(y[ids < 0] == 0)
+    check_close(y[~bad], Yr[~bad], S[~bad], "gate_up max slots")
+
+
 @pytest.mark.parametrize("T,K", [(16, 16384), (1, 32768)])
 def test_gate_up_long_k_is_chunked(T, K):
     """Chunked K: each output row keeps two partial sums (gate and up) across the chunks."""

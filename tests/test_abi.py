@@ -5,8 +5,6 @@ import ctypes
 import os
 import re
 
-import pytest
-
 from block_quantized_matrix_amd import bqm
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))

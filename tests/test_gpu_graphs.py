@@ -1,6 +1,5 @@
 """The entry points captured in a HIP graph (as the benchmark runs them): every replay, with
 eager work and synchronizations between replays, gives the eager result bit for bit."""
-import numpy as np
 import pytest
 import torch
 

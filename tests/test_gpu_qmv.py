@@ -81,7 +81,7 @@ def test_qmv_exact_probe(fmt, M, N, K):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("M", [1, 3])
+@pytest.mark.parametrize("M", [1, 2, 3, 8])  # every batch class (1, 2, 4, 8) and sum order
 def test_qmv_invariants(fmt, M):
     N, K = 96, 5120
     say("qmv invariants", fmt, M)

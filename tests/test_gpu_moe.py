@@ -397,3 +397,23 @@ def test_qmv_id_sum_matches_weighted_qmv_id():
     say("qmv_id_sum vs qmv_id")
     r = run_sum("q8_0", E, N, K, ids, X, top_k * K, K, ("sum-vs",))
     check_sum(*r, ids, E, "vs qmv_id")
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0"])
+@pytest.mark.parametrize("T", [1, 2, 5])  # batch classes 1, 2 and 4
+def test_indexed_neutral_codes_give_exact_zeros(fmt, T):
+    """Codes all equal to the format's offset give exactly zero for any scale and input, in
+    the indexed form and (silu(0) * 0) the gate+up form."""
+    E, N, K, top_k = 4, 40, 4096, 2
+    bb = gen.block_bytes(fmt)
+    Wn = weights(fmt, E * N, K, ("neutral", fmt)).reshape(E * N, K // 32, bb).clone()
+    Wn[:, :, 2:] = 0x88 if fmt == "q4_0" else 0
+    Wp = packed(fmt, Wn.reshape(E * N, -1), E * N, K)
+    ids = torch.from_numpy(gen.router_ids(T, E, top_k, ("neutral-ids", T))).to(DEV)
+    X = gen.normal((T, K), ("neutral-x", T), device=DEV)
+    Y = torch.full((T, top_k, N), float("nan"), device=DEV)
+    bqm.qmv_id(fmt, Wp, E, N, K, ids, T, top_k, X, K, 0, Y)
+    assert torch.all(Y == 0)
+    Y.fill_(float("nan"))
+    bqm.qmv_id_gate_up(fmt, Wp, Wp, E, N, K, ids, T, top_k, X, K, 0, Y)
+    assert torch.all(Y == 0)

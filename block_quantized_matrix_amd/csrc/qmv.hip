@@ -559,7 +559,7 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
   constexpr int CB = FMT == FQ4 ? 16 : 32;     // code bytes per block
   constexpr uint32_t kOob = 0x80000000u;       // lane offset past every descriptor: reads 0
   constexpr int LOADS = R * (FMT == FQ4 ? 2 : 3);  // loads per step (R rows)
-  constexpr bool kPrioFeedback = MM == 1 && !IDX;
+  constexpr bool kPrioFeedback = MM == 1;
   __shared__ bool lds_ok;
   __shared__ uint32_t lds_epoch;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1046,8 +1046,9 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
           // waves of a workgroup finish microseconds later and the whole workgroup waits
           // for them.  Each wave's issue priority follows the share of its steps still
           // left: a wave that falls behind keeps a higher priority than those ahead of it.
-          // (Measured: 8% faster on the dependent batch-1 chain; far slower for wider
-          // batches and the indexed form, which keep the default.)
+          // (Measured: 8% faster on the dependent batch-1 chain, 2-4% on the indexed form's
+          // batch-1 groups (MoE decode at T = 1); far slower for wider batches, which keep
+          // the default.)
           if constexpr (kPrioFeedback) {  // quarter of the steps left: 3 .. 0 (no division)
             const int c4 = 4 * creal;
             if (c4 >= 3 * creal0) __builtin_amdgcn_s_setprio(3);

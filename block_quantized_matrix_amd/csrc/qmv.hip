@@ -559,7 +559,7 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
   constexpr int CB = FMT == FQ4 ? 16 : 32;     // code bytes per block
   constexpr uint32_t kOob = 0x80000000u;       // lane offset past every descriptor: reads 0
   constexpr int LOADS = R * (FMT == FQ4 ? 2 : 3);  // loads per step (R rows)
-  constexpr bool kPrioFeedback = MM == 1;
+  constexpr bool kPrioFeedback = MM == 1 || (MM == 2 && !IDX);
   __shared__ bool lds_ok;
   __shared__ uint32_t lds_epoch;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1046,8 +1046,9 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
           // waves of a workgroup finish microseconds later and the whole workgroup waits
           // for them.  Each wave's issue priority follows the share of its steps still
           // left: a wave that falls behind keeps a higher priority than those ahead of it.
-          // (Measured: 8% faster on the dependent batch-1 chain, 2-4% on the indexed form's
-          // batch-1 groups (MoE decode at T = 1); far slower for wider batches, which keep
+          // (Measured: 8% faster on the dependent batch-1 chain, 3% at batch 2, 2-4% on the
+          // indexed form's batch-1 groups (MoE decode at T = 1); 4-6 times slower for the
+          // chain at batches 4 and 8 and 3.5 times for the indexed form's class 4, which keep
           // the default.)
           if constexpr (kPrioFeedback) {  // quarter of the steps left: 3 .. 0 (no division)
             const int c4 = 4 * creal;

@@ -417,3 +417,20 @@ def test_indexed_neutral_codes_give_exact_zeros(fmt, T):
     Y.fill_(float("nan"))
     bqm.qmv_id_gate_up(fmt, Wp, Wp, E, N, K, ids, T, top_k, X, K, 0, Y)
     assert torch.all(Y == 0)
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0"])
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 16])  # batch classes 1, 2, 2, 4, 4
+def test_qmv_id_sum_batch_classes(fmt, T):
+    """The router-weighted form at every batch class the indexed GEMV picks, with a padding
+    slot and (T > 1) an out-of-range id: weighted slot rows against the oracle, the sums bit
+    for bit against the slot rows added in slot order."""
+    E, N, K, top_k = 6, 130, 1184, 3
+    ids = gen.router_ids(T, E, top_k, ("sum-classes", T))
+    ids[0, 1] = -1
+    if T > 1:
+        ids[1, 2] = E + 1
+    X = gen.normal((T, top_k, K), ("sum-classes-x", T, fmt), device=DEV)
+    say("qmv_id_sum classes", fmt, T)
+    ys, y, Yr, S, Yid, Sid, w_np = run_sum(fmt, E, N, K, ids, X, top_k * K, K, ("sum-cl", fmt, T))
+    check_sum(ys, y, Yr, S, Yid, Sid, w_np, ids, E, f"qmv_id_sum classes {fmt} T={T}")

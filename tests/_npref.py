@@ -64,3 +64,34 @@ def qmm_q4_isum(Wq4, Xq, N, K):
     nb = K // 32
     qx = np.asarray(Xq, np.int8).astype(np.int64).reshape(-1, nb, 32)
     return np.einsum("mbj,nbj->mnb", qx, q4_codes(Wq4, N, K))
+
+
+def q8_codes(Wq8, N, K):
+    """Signed Q8_0 codes [N][nb][32]."""
+    nb = K // 32
+    return np.asarray(Wq8, np.uint8).reshape(N, nb, 34)[:, :, 2:].view(np.int8).astype(np.int64)
+
+
+def qmm_scale(fmt, W, Xq, dx, N, K):
+    """Tolerance scale of the prefill product, from its definition:
+    S[m][n] = sum_b |d_w[n][b] * dx[m][b]| * sum_j |qw[n][32b+j] * qx[m][32b+j]|,
+    with the absolute block sums formed as one dense integer contraction per block."""
+    nb = K // 32
+    codes = q8_codes(W, N, K) if fmt == "q8_0" else q4_codes(W, N, K)       # [N][nb][32]
+    dw = q8_scales(W, N, K) if fmt == "q8_0" else q4_scales(W, N, K)        # [N][nb]
+    qx = np.asarray(Xq, np.int8).astype(np.int64).reshape(-1, nb, 32)      # [M][nb][32]
+    aisum = np.einsum("mbj,nbj->mnb", np.abs(qx), np.abs(codes)).astype(np.float64)
+    scale = np.abs(dw)[None, :, :] * np.abs(np.asarray(dx, np.float32).astype(np.float64))[:, None, :]
+    return (scale * aisum).sum(axis=2)
+
+
+def silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def gate_up_scale(g, u, Sg, Su):
+    """Tolerance scale of silu(g) * u when g and u each carry an error within 1e-3 of
+    their own scales Sg, Su: the bound of the first-order expansion with |silu'| <= 1.1,
+    term by term, plus 1e-3 |y| for evaluating silu and the product in single precision."""
+    y = silu(g) * u
+    return 1.1 * Sg * (np.abs(u) + 1e-3 * Su) + np.abs(silu(g)) * Su + 1e-3 * np.abs(y)

@@ -34,6 +34,22 @@ MUTANTS = {
     "sum_weight_index": [("(double)weights[t * top_k + s]", "(double)weights[s]")],
     "silu_sign": [("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));")],
     "gate_up_swapped": [("y = sl * u;", "y = oracle_silu(u) * g;")],
+    # the tolerance scales S, which set the acceptance bar of the GPU parity tests
+    "qmv_scale_x10": [("        s += fabs(p);", "        s += 10 * fabs(p);")],
+    "id_scale_x10": [("sa += fabs(p);", "sa += 10 * fabs(p);")],
+    "sum_scale_weight_signed": [("sa += fabs(r) * ss;", "sa += r * ss;")],
+    "qmm_scale_x10": [("sa += fabs(scale) * (double)aabs;", "sa += 10 * fabs(scale) * (double)aabs;")],
+    "qmm_scale_signed": [("sa += fabs(scale) * (double)aabs;", "sa += scale * (double)aabs;")],
+    "qmm_scale_abs_sums_multiplied": [
+        ("int32_t acc = 0, aabs = 0;", "int32_t acc = 0, aabs = 0, aw = 0, ax = 0;"),
+        ("aabs += abs((int32_t)qw[j] * (int32_t)qx[j]);",
+         "aw += abs((int32_t)qw[j]); ax += abs((int32_t)qx[j]); aabs = aw * ax;")],
+    "gate_up_scale_gate_term_dropped": [
+        ("sy = 1.1 * sg * (fabs(u) + 1e-3 * su) + fabs(sl) * su + 1e-3 * fabs(y);",
+         "sy = fabs(sl) * su + 1e-3 * fabs(y);")],
+    "gate_up_scale_x10": [
+        ("sy = 1.1 * sg * (fabs(u) + 1e-3 * su) + fabs(sl) * su + 1e-3 * fabs(y);",
+         "sy = 10 * (1.1 * sg * (fabs(u) + 1e-3 * su) + fabs(sl) * su + 1e-3 * fabs(y));")],
 }
 
 

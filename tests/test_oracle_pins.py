@@ -189,6 +189,7 @@ def test_qmv_id_bruteforce(oracle_lib, x_slot_stride):
             yr = Wd[e] @ x
             sr = np.abs(Wd[e]) @ np.abs(x)
             assert np.all(np.abs(Y[t, s] - yr) <= 1e-12 * sr)
+            assert np.all(sr > 0) and np.allclose(S[t, s], sr, rtol=1e-12, atol=0)
 
 
 def test_qmv_id_rejects_out_of_range_id(oracle_lib):
@@ -210,6 +211,7 @@ def test_qmv_id_sum_bruteforce(oracle_lib, fmt):
     W = enc(gen.normal((E * N, K), ("idsum", fmt), std=0.05)).numpy()
     ids = np.array([[3, 0, 3], [-1, 4, 2], [1, 3, 0]], np.int32)
     w = gen.router_weights(T, top_k, ("idsum-w", fmt))
+    w[2, 1] = -w[2, 1]  # any fp32 weight is valid; a negative one checks |w| in the scale
     X = gen.normal((T, top_k, K), ("idsum-x", fmt)).numpy()
     Y, S = oracle_lib.qmv_id_sum(fmt, W, E, N, K, ids, w, X, top_k * K, K)
     Wd = _npref.dequant(fmt, W, E * N, K).reshape(E, N, K)
@@ -286,7 +288,8 @@ def test_gate_up_bruteforce(oracle_lib, fmt):
             g, u = Gd[e] @ x, Ud[e] @ x
             yr = g / (1 + np.exp(-g)) * u
             assert np.all(np.abs(Y[t, s] - yr) <= 1e-12 * (np.abs(yr) + np.abs(g * u) + 1e-300))
-            assert np.all(S[t, s] >= 1e-3 * np.abs(Y[t, s]))
+            Sr = _npref.gate_up_scale(g, u, np.abs(Gd[e]) @ np.abs(x), np.abs(Ud[e]) @ np.abs(x))
+            assert np.allclose(S[t, s], Sr, rtol=1e-9, atol=0)
 
 
 # --- activation quantizer: special cases and properties --------------------------------
@@ -346,6 +349,7 @@ def test_qmm_bruteforce(oracle_lib, M, N, K):
     scale = dw[None, :, :] * dx.astype(np.float64)[:, None, :]       # [M][N][nb]
     Yr = np.einsum("mnb,mnb->mn", scale, iref.astype(np.float64))
     assert np.all(np.abs(Y - Yr) <= 1e-12 * S)
+    assert np.allclose(S, _npref.qmm_scale("q8_0", W, Xq, dx, N, K), rtol=1e-12, atol=0)
 
 
 def test_qmm_single_block_is_one_product(oracle_lib):
@@ -373,6 +377,7 @@ def test_qmm_q4_bruteforce(oracle_lib, M, N, K):
     scale = dw[None, :, :] * dx.astype(np.float64)[:, None, :]
     Yr = np.einsum("mnb,mnb->mn", scale, iref.astype(np.float64))
     assert np.all(np.abs(Y - Yr) <= 1e-12 * S)
+    assert np.allclose(S, _npref.qmm_scale("q4_0", W, Xq, dx, N, K), rtol=1e-12, atol=0)
 
 
 def test_qmm_q4_extreme_codes(oracle_lib):
@@ -430,6 +435,8 @@ def test_qmm_id_bruteforce(oracle_lib, fmt, rows):
             dw = (_npref.q8_scales if fmt == "q8_0" else _npref.q4_scales)(We, N, K)
             yr = (dw * dx[r].astype(np.float64)[None, :] * isum).sum(axis=1)
             assert np.all(np.abs(Y[t, s] - yr) <= 1e-12 * S[t, s])
+            Sr = _npref.qmm_scale(fmt, We, Xq[r:r + 1], dx[r:r + 1], N, K)[0]
+            assert np.all(Sr > 0) and np.allclose(S[t, s], Sr, rtol=1e-12, atol=0)
 
 
 def test_qmm_matches_qmv_on_dequantized_activations(oracle_lib):
@@ -443,3 +450,38 @@ def test_qmm_matches_qmv_on_dequantized_activations(oracle_lib):
     Xd = (Xq.reshape(M, 2, 32) * dx[:, :, None]).reshape(M, K).astype(np.float32)  # exact
     Y2, _ = oracle_lib.qmv("q8_0", W, Xd, N, K)
     assert np.array_equal(Y, Y2)
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0"])
+def test_gate_up_scale_exact_inputs(oracle_lib, fmt):
+    """The gate+up tolerance scale, term by term, on inputs where every sum is exact
+    (power-of-two scales, small integer codes and inputs), so both sides see the same g, u,
+    Sg and Su and the scale must agree to rounding: rtol 1e-12."""
+    E, N, K, T, top_k = 3, 7, 128, 2, 2
+    raw = gen.raw_q4_0 if fmt == "q4_0" else gen.raw_q8_0
+    Wg, Wu = raw(E * N, K, ("gus", "g", fmt)).numpy(), raw(E * N, K, ("gus", "u", fmt)).numpy()
+    ids = np.array([[2, 0], [1, -1]], np.int32)
+    X = gen.small_int((T, K), ("gus-x", fmt)).numpy()
+    Y, S = oracle_lib.qmv_id_gate_up(fmt, Wg, Wu, E, N, K, ids, X, K, 0)
+    Gd = _npref.dequant(fmt, Wg, E * N, K).reshape(E, N, K)
+    Ud = _npref.dequant(fmt, Wu, E * N, K).reshape(E, N, K)
+    for t in range(T):
+        for s in range(top_k):
+            e = ids[t, s]
+            if e < 0:
+                continue
+            x = X[t].astype(np.float64)
+            g, u = Gd[e] @ x, Ud[e] @ x
+            Sr = _npref.gate_up_scale(g, u, np.abs(Gd[e]) @ np.abs(x), np.abs(Ud[e]) @ np.abs(x))
+            assert np.allclose(S[t, s], Sr, rtol=1e-12, atol=0)
+            assert np.allclose(Y[t, s], _npref.silu(g) * u, rtol=1e-12, atol=1e-300)
+
+
+def test_qmv_scale_is_sum_of_abs_products(oracle_lib):
+    """The GEMV tolerance scale S = sum |w x| against |W| |x| on signed scales and inputs."""
+    M, N, K = 3, 4, 96
+    W = gen.raw_q8_0(N, K, ("qs",), scales=(0.001, 0.0173, -0.02), codes=(-127, 127)).numpy()
+    X = gen.normal((M, K), ("qs-x",)).numpy()
+    _, S = oracle_lib.qmv("q8_0", W, X, N, K)
+    Wd = _npref.dequant("q8_0", W, N, K)
+    assert np.allclose(S, np.abs(X.astype(np.float64)) @ np.abs(Wd).T, rtol=1e-12, atol=0)

@@ -16,16 +16,12 @@
 // eight neighbouring lanes (eight consecutive blocks) hit eight different bank groups.
 // Long rows are staged in chunks of blocks that fit the LDS budget.
 //
-// Arithmetic, M = 1 (the bandwidth-critical case).  A Q4_0 weight is (n - 8) d.  Per
-// block the kernel accumulates sum n_j x_j with v_cvt_f32_ubyte + FMA (the high nibbles
-// are taken in place, as 16 n, and scaled by 1/16 once per block), and then subtracts
-// 8 * sum_j x_j, a per-block sum computed once in LDS in the *same order* as the FMA
-// chains.  Because 8 (and 1/16) are powers of two the subtraction is exact for an all-8
-// block, so neutral codes give exactly zero, as the definition requires.  Q8_0 does the
-// same with the bias 128 (q ^ 0x80 makes the code an unsigned byte q + 128).
-//
-// Arithmetic, M > 1.  Each weight is dequantized once into a register, exactly:
-// fma(n, d, -8d) has at most 4 + 11 significant bits, and then used for M FMAs.
+// Arithmetic.  Every code becomes its signed value exactly before it meets x (a Q4_0
+// nibble as the binary16 value n - 8 through a mantissa trick, a Q8_0 byte through a
+// sign-extending conversion), and each block's 32 products are summed by fused
+// multiply-adds, then scaled by d: the rounding error of a block stays proportional to
+// sum |(n - 8) d x|, its share of the tolerance scale, and neutral codes give exactly zero.
+// The signed codes of a block are formed once and shared by the M inputs.
 //
 // Reduction: a butterfly of cross-lane shuffles inside the lane group, then one lane
 // stores the row.  No atomics; the summation order is fixed for a given launch shape.
@@ -62,11 +58,10 @@ template <> struct Codes<FQ8> { u32x4 a, b; };
 // 14.2 T weights/s against 39.3 T fp32 lane-ops/s, about 2.8 ops per weight).  One launch
 // runs a chain of GEMVs in order (a single GEMV is a chain of one):
 //  - One 1024-thread workgroup per CU owns, for each GEMV, a contiguous range of rows and
-//    stages that GEMV's M inputs into LDS.  Blocks are 144 bytes apart in LDS: 128 bytes of
-//    x, then the block's x sum; with that stride eight neighbouring blocks start in eight
-//    different 16-byte bank groups, so the per-lane block reads are conflict-free with
-//    immediate offsets.  For Q4_0 the x values that meet the high nibbles are stored
-//    divided by 16 (exact), so one FMA chain takes the nibbles in place (16 n * x / 16).
+//    stages that GEMV's M inputs into LDS.  Blocks are 144 bytes apart in LDS (128 bytes of
+//    x and 16 unused): with that stride eight neighbouring blocks start in eight different
+//    16-byte bank groups, so the per-lane block reads are conflict-free with immediate
+//    offsets.
 //  - When M inputs of K do not fit, a GEMV is walked in chunks of kc blocks of K: the
 //    workgroup stages one chunk of x at a time and keeps each row's partial sums in LDS,
 //    adding the chunks in order.
@@ -78,13 +73,10 @@ template <> struct Codes<FQ8> { u32x4 a, b; };
 //    unrolled by P).  The ring runs ahead across GEMV and chunk boundaries: the weights of
 //    the next GEMV do not depend on its input, so they stream while the workgroup waits for
 //    the previous GEMV's outputs (device-wide barrier) and stages the new x.
-// Arithmetic per block and row: 8 ANDs (Q8_0: XORs) and 32 v_cvt_f32_ubyte, shared by the
-// M inputs; per input the block's products summed by multiply-adds (batches 1 and 2: Q4_0
-// two chains of sixteen, Q8_0 eight chains of four and a fixed tree over them; wider
-// batches: one chain of 32), then
-// r = sum - 8 * sum(x) (Q8_0: - 128 * sum(x)) and acc += d * r (v_fma_mix: d stays fp16).
-// The products and the block sum of x follow the same order and 8, 128 and 1/16 are powers
-// of two, so neutral codes give exactly zero.
+// Arithmetic per block and row (see chain_block): Q4_0 4 shifts, 16 and-ors and 16 packed
+// binary16 subtractions give the 32 signed codes, Q8_0 32 sign-extending conversions; then
+// per input 32 fused multiply-adds (v_fma_mix for the binary16 codes) and acc += d * sum
+// (v_fma_mix again: d stays binary16).
 constexpr int kP1Waves = 16;  // waves of a workgroup (8 for the widest batch: registers)
 constexpr int kBlkLds = 144;  // LDS bytes per staged block
 constexpr int kChainMaxM = 8;
@@ -99,191 +91,139 @@ constexpr int kChainMaxM = 8;
 constexpr int kLg2G = BQM_LG2G, kG = 1 << kLg2G, kGpw = 64 >> kLg2G;
 static_assert(kLg2G >= 3 && kLg2G <= 4, "group_sum covers 8 or 16 lanes");
 
-// Orders of a block's sums.  A block is eight chunks of four positions (the 16-byte pieces
-// of its staged input).  Tree: a chunk's sum runs over its four positions in order, and the
-// block's sum is ((c0 + c1) + (c2 + c3)) + ((c4 + c5) + (c6 + c7)); halves: positions 0..15
-// and 16..31 each in order, then their sum; position order: 0..31.  The code chains below
-// and the block sums of the staged inputs follow the same order, so that codes all equal to
-// the offset give exactly zero.  The tree lets eight lanes form a block's input sum in three
-// steps, halves two lanes in sixteen (the sum in position order took one lane 32 steps: 3 %
-// of the 27B Q4_0 pass); halves take 6 fewer vector operations per block and row than the
-// tree in the chains themselves.
-template <int K, int MM>
-__device__ __forceinline__ void tree_add(const float (&ck)[MM], float (&pr)[MM], float (&qd)[MM],
-                                         float (&hf)[MM], float (&c)[MM]) {
-#pragma unroll
-  for (int m = 0; m < MM; m++) {
-    if constexpr (K % 2 == 0) pr[m] = ck[m];
-    else pr[m] = pr[m] + ck[m];
-    if constexpr (K % 4 == 1) qd[m] = pr[m];
-    if constexpr (K % 4 == 3) qd[m] = qd[m] + pr[m];
-    if constexpr (K == 3) hf[m] = qd[m];
-    if constexpr (K == 7) c[m] = hf[m] + qd[m];
-  }
+// ---- per-block arithmetic ------------------------------------------------------------
+// Each code is turned into its signed value exactly (Q4_0: nibble - 8, Q8_0: the int8 code)
+// before it meets x, and a block's 32 products are summed by fused multiply-adds in a fixed
+// order (chain_block): a product is exact inside its FMA, so the block sum carries at most
+// 32 roundings of partial sums that are each bounded by sum_j |code_j x_j|, the block's
+// share of S = sum |w x|.  (Summing unsigned codes and subtracting the offset times sum x
+// afterwards cancels: its error grows with sum (n + 8)|x| and can swallow a whole
+// near-neutral block.)  All-neutral codes give exactly zero.
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+// The eight nibbles of one Q4_0 code word as four pairs of binary16 values n - 8, with no
+// conversion instruction: OR-ed into the mantissa of 1024.0 (0x6400) a nibble n reads as
+// 1024 + n, and a nibble at bits 4..7 OR-ed into 64.0 (0x5400, mantissa step 1/16) reads as
+// 64 + n; one packed subtraction per pair gives n - 8 exactly.  The pairs then enter
+// v_fma_mix_f32 directly (a binary16 operand widened inside the FMA, x stays fp32).  Byte b
+// of word k holds position 4k + b in its low nibble and 16 + 4k + b in its high nibble, so
+// the pairs hold positions (4k, 4k+2), (4k+1, 4k+3) and the same 16 positions on.
+struct Q4Pairs {
+  h2 l02, l13, h02, h13;
+};
+// mask and magic constants live in registers: a VOP3 and-or takes no literal operand
+struct Q4Consts {
+  uint32_t mlo, mhi, klo, khi;
+};
+__device__ __forceinline__ Q4Consts q4_consts() {
+  Q4Consts c{0x000F000Fu, 0x00F000F0u, 0x64006400u, 0x54005400u};
+  asm("" : "+s"(c.mlo), "+s"(c.mhi), "+v"(c.klo), "+v"(c.khi));
+  return c;
+}
+__device__ __forceinline__ Q4Pairs q4_pairs(uint32_t w, const Q4Consts& k) {
+  const uint32_t s = w >> 8;
+  const h2 lo_off = {(_Float16)1032.0f, (_Float16)1032.0f}, hi_off = {(_Float16)72.0f, (_Float16)72.0f};
+  Q4Pairs p;
+  p.l02 = __builtin_bit_cast(h2, (w & k.mlo) | k.klo) - lo_off;
+  p.l13 = __builtin_bit_cast(h2, (s & k.mlo) | k.klo) - lo_off;
+  p.h02 = __builtin_bit_cast(h2, (w & k.mhi) | k.khi) - hi_off;
+  p.h13 = __builtin_bit_cast(h2, (s & k.mhi) | k.khi) - hi_off;
+  return p;
 }
 
 // One block of codes against MM staged input blocks (input m at xb + m * mstride bytes):
-// c[m] = sum_j code_j * x_mj in the order above (positions 0..15, then 16..31).
+// c[m] = sum_{j < 32} code_j * x_mj by FMA chains in a fixed order.  A word's signed codes
+// are formed once and shared by the MM inputs.  The order only changes which registers stay
+// live (any fixed order meets the bound), so it is picked per format and batch:
+//  - Q4_0, batches 1-2: word-major, one chain: for word k positions 4k..4k+3, then
+//    16+4k..16+4k+3, so a word's pairs die at once;
+//  - Q4_0, batches 4-8: one chain in position order 0..31 (the low nibbles of the four words,
+//    then the high ones), so each input's two staged chunks are not live together;
+//  - Q8_0, batches 1-2: eight chains of four positions (one per 16-byte piece of the staged
+//    input) added as ((c0 + c1) + (c2 + c3)) + ((c4 + c5) + (c6 + c7)): each piece's reads
+//    are used at once (with one or two chains the scheduler hoisted every read and batch 2
+//    with two steps in flight spilled registers);
+//  - Q8_0, batches 4-8: one chain in position order.
 template <int FMT, int MM>
-__device__ __forceinline__ void chain_block_tree(const Codes<FMT>& q, const char* xb, int mstride,
-                                                 float (&c)[MM]) {
-  auto xm = [&](int m, int k) { return *reinterpret_cast<const f32x4*>(xb + m * mstride + k * 16); };
-  float ck[MM], pr[MM], qd[MM], hf[MM];
-  auto chunk = [&](uint32_t u, int k) {  // the four codes in u's bytes against chunk k
-    const float v0 = ub(u, 0), v1 = ub(u, 1), v2 = ub(u, 2), v3 = ub(u, 3);
-#pragma unroll
-    for (int m = 0; m < MM; m++) {
-      const f32x4 a = xm(m, k);
-      ck[m] = v0 * a.x;
-      ck[m] = fmaf(v1, a.y, ck[m]); ck[m] = fmaf(v2, a.z, ck[m]); ck[m] = fmaf(v3, a.w, ck[m]);
-    }
-  };
-  if constexpr (FMT == FQ4) {
-    uint32_t l[4], h[4];
-    const uint32_t w[4] = {q.a.x, q.a.y, q.a.z, q.a.w};
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-      l[k] = w[k] & 0x0F0F0F0Fu;
-      h[k] = w[k] & 0xF0F0F0F0u;  // 16 * high nibble, in place
-      asm("" : "+v"(l[k]), "+v"(h[k]));  // keep the conversions as v_cvt_f32_ubyte{0..3}
-    }
-    chunk(l[0], 0); tree_add<0>(ck, pr, qd, hf, c);
-    chunk(l[1], 1); tree_add<1>(ck, pr, qd, hf, c);
-    chunk(l[2], 2); tree_add<2>(ck, pr, qd, hf, c);
-    chunk(l[3], 3); tree_add<3>(ck, pr, qd, hf, c);
-    chunk(h[0], 4); tree_add<4>(ck, pr, qd, hf, c);
-    chunk(h[1], 5); tree_add<5>(ck, pr, qd, hf, c);
-    chunk(h[2], 6); tree_add<6>(ck, pr, qd, hf, c);
-    chunk(h[3], 7); tree_add<7>(ck, pr, qd, hf, c);
-  } else {
-    uint32_t u[8] = {q.a.x, q.a.y, q.a.z, q.a.w, q.b.x, q.b.y, q.b.z, q.b.w};
-#pragma unroll
-    for (int k = 0; k < 8; k++) {
-      u[k] ^= 0x80808080u;  // q + 128 as unsigned bytes
-      asm("" : "+v"(u[k]));
-    }
-    chunk(u[0], 0); tree_add<0>(ck, pr, qd, hf, c);
-    chunk(u[1], 1); tree_add<1>(ck, pr, qd, hf, c);
-    chunk(u[2], 2); tree_add<2>(ck, pr, qd, hf, c);
-    chunk(u[3], 3); tree_add<3>(ck, pr, qd, hf, c);
-    chunk(u[4], 4); tree_add<4>(ck, pr, qd, hf, c);
-    chunk(u[5], 5); tree_add<5>(ck, pr, qd, hf, c);
-    chunk(u[6], 6); tree_add<6>(ck, pr, qd, hf, c);
-    chunk(u[7], 7); tree_add<7>(ck, pr, qd, hf, c);
-  }
-}
-
-// The same with the sums in plain position order (the wider batches: their registers do
-// not hold the tree's partial sums for every input).
-template <int FMT, int MM>
-__device__ __forceinline__ void chain_block_seq(const Codes<FMT>& q, const char* xb, int mstride,
-                                                float (&c)[MM]) {
+__device__ __forceinline__ void chain_block(const Codes<FMT>& q, const char* xb, int mstride,
+                                            float (&c)[MM]) {
   auto xm = [&](int m, int k) { return *reinterpret_cast<const f32x4*>(xb + m * mstride + k * 16); };
   if constexpr (FMT == FQ4) {
-    uint32_t l[4], h[4];
+    const Q4Consts kc = q4_consts();
     const uint32_t w[4] = {q.a.x, q.a.y, q.a.z, q.a.w};
+    if constexpr (MM <= 2) {
 #pragma unroll
-    for (int k = 0; k < 4; k++) {
-      l[k] = w[k] & 0x0F0F0F0Fu;
-      h[k] = w[k] & 0xF0F0F0F0u;  // 16 * high nibble, in place
-      asm("" : "+v"(l[k]), "+v"(h[k]));  // keep the conversions as v_cvt_f32_ubyte{0..3}
-    }
+      for (int k = 0; k < 4; k++) {
+        const Q4Pairs p = q4_pairs(w[k], kc);
 #pragma unroll
-    for (int k = 0; k < 4; k++) {
-      const float v0 = ub(l[k], 0), v1 = ub(l[k], 1), v2 = ub(l[k], 2), v3 = ub(l[k], 3);
-#pragma unroll
-      for (int m = 0; m < MM; m++) {
-        const f32x4 a = xm(m, k);
-        if (k == 0) c[m] = v0 * a.x; else c[m] = fmaf(v0, a.x, c[m]);
-        c[m] = fmaf(v1, a.y, c[m]); c[m] = fmaf(v2, a.z, c[m]); c[m] = fmaf(v3, a.w, c[m]);
+        for (int m = 0; m < MM; m++) {
+          const f32x4 a = xm(m, k), b = xm(m, k + 4);
+          float t = fmaf((float)p.l02.x, a.x, k == 0 ? 0.0f : c[m]);  // v_fma_mix onto +0 at k = 0
+          t = fmaf((float)p.l13.x, a.y, t);
+          t = fmaf((float)p.l02.y, a.z, t);
+          t = fmaf((float)p.l13.y, a.w, t);
+          t = fmaf((float)p.h02.x, b.x, t);
+          t = fmaf((float)p.h13.x, b.y, t);
+          t = fmaf((float)p.h02.y, b.z, t);
+          c[m] = fmaf((float)p.h13.y, b.w, t);
+        }
       }
-    }
+    } else {
+      Q4Pairs p[4];
 #pragma unroll
-    for (int k = 0; k < 4; k++) {
-      const float v0 = ub(h[k], 0), v1 = ub(h[k], 1), v2 = ub(h[k], 2), v3 = ub(h[k], 3);
+      for (int k = 0; k < 4; k++) p[k] = q4_pairs(w[k], kc);
 #pragma unroll
       for (int m = 0; m < MM; m++) {
-        const f32x4 b = xm(m, k + 4);
-        c[m] = fmaf(v0, b.x, c[m]); c[m] = fmaf(v1, b.y, c[m]);
-        c[m] = fmaf(v2, b.z, c[m]); c[m] = fmaf(v3, b.w, c[m]);
+        float t;
+#pragma unroll
+        for (int k = 0; k < 4; k++) {  // positions 4k .. 4k+3: low nibbles of word k
+          const f32x4 a = xm(m, k);
+          t = fmaf((float)p[k].l02.x, a.x, k == 0 ? 0.0f : t);
+          t = fmaf((float)p[k].l13.x, a.y, t);
+          t = fmaf((float)p[k].l02.y, a.z, t);
+          t = fmaf((float)p[k].l13.y, a.w, t);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; k++) {  // positions 16 + 4k .. : high nibbles of word k
+          const f32x4 b = xm(m, k + 4);
+          t = fmaf((float)p[k].h02.x, b.x, t);
+          t = fmaf((float)p[k].h13.x, b.y, t);
+          t = fmaf((float)p[k].h02.y, b.z, t);
+          t = fmaf((float)p[k].h13.y, b.w, t);
+        }
+        c[m] = t;
       }
     }
   } else {
     const uint32_t w[8] = {q.a.x, q.a.y, q.a.z, q.a.w, q.b.x, q.b.y, q.b.z, q.b.w};
+    constexpr bool kTree = MM <= 2;
+    float pr[MM], qd[MM], hf[MM];  // the tree's partial sums: pair, quad, half
 #pragma unroll
     for (int k = 0; k < 8; k++) {
-      uint32_t u = w[k] ^ 0x80808080u;  // q + 128 as unsigned bytes
-      asm("" : "+v"(u));
-      const float v0 = ub(u, 0), v1 = ub(u, 1), v2 = ub(u, 2), v3 = ub(u, 3);
+      // v_cvt_f32_i32 of a sign-extended byte (SDWA): one instruction per code
+      const float v0 = (float)(int8_t)w[k], v1 = (float)(int8_t)(w[k] >> 8);
+      const float v2 = (float)(int8_t)(w[k] >> 16), v3 = (float)(int8_t)(w[k] >> 24);
 #pragma unroll
       for (int m = 0; m < MM; m++) {
         const f32x4 a = xm(m, k);
-        if (k == 0) c[m] = v0 * a.x; else c[m] = fmaf(v0, a.x, c[m]);
-        c[m] = fmaf(v1, a.y, c[m]); c[m] = fmaf(v2, a.z, c[m]); c[m] = fmaf(v3, a.w, c[m]);
+        float t = k == 0 || kTree ? v0 * a.x : fmaf(v0, a.x, c[m]);
+        t = fmaf(v1, a.y, t);
+        t = fmaf(v2, a.z, t);
+        t = fmaf(v3, a.w, t);
+        if constexpr (kTree) {
+          if (k % 2 == 0) pr[m] = t;
+          else pr[m] = pr[m] + t;
+          if (k % 4 == 1) qd[m] = pr[m];
+          if (k % 4 == 3) qd[m] = qd[m] + pr[m];
+          if (k == 3) hf[m] = qd[m];
+          if (k == 7) c[m] = hf[m] + qd[m];
+        } else {
+          c[m] = t;
+        }
       }
     }
   }
-}
-
-// The same in two chains, positions 0..15 and 16..31 (Q4_0: the low and the high
-// nibbles), each in position order, then their sum: 6 fewer vector operations per block and
-// row than the tree.
-template <int FMT, int MM>
-__device__ __forceinline__ void chain_block_halves(const Codes<FMT>& q, const char* xb, int mstride,
-                                                   float (&c)[MM]) {
-  auto xm = [&](int m, int k) { return *reinterpret_cast<const f32x4*>(xb + m * mstride + k * 16); };
-  float h0[MM], h1[MM];
-  auto chunk = [&](uint32_t u, int k, float (&h)[MM]) {  // chunk k continues its half's chain
-    const float v0 = ub(u, 0), v1 = ub(u, 1), v2 = ub(u, 2), v3 = ub(u, 3);
-#pragma unroll
-    for (int m = 0; m < MM; m++) {
-      const f32x4 a = xm(m, k);
-      float t = k % 4 == 0 ? v0 * a.x : fmaf(v0, a.x, h[m]);
-      t = fmaf(v1, a.y, t); t = fmaf(v2, a.z, t); h[m] = fmaf(v3, a.w, t);
-    }
-  };
-  if constexpr (FMT == FQ4) {
-    uint32_t l[4], h[4];
-    const uint32_t w[4] = {q.a.x, q.a.y, q.a.z, q.a.w};
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-      l[k] = w[k] & 0x0F0F0F0Fu;
-      h[k] = w[k] & 0xF0F0F0F0u;  // 16 * high nibble, in place
-      asm("" : "+v"(l[k]), "+v"(h[k]));  // keep the conversions as v_cvt_f32_ubyte{0..3}
-    }
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-      chunk(l[k], k, h0);
-      chunk(h[k], k + 4, h1);
-    }
-  } else {
-    uint32_t u[8] = {q.a.x, q.a.y, q.a.z, q.a.w, q.b.x, q.b.y, q.b.z, q.b.w};
-#pragma unroll
-    for (int k = 0; k < 8; k++) {
-      u[k] ^= 0x80808080u;  // q + 128 as unsigned bytes
-      asm("" : "+v"(u[k]));
-    }
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-      chunk(u[k], k, h0);
-      chunk(u[k + 4], k + 4, h1);
-    }
-  }
-#pragma unroll
-  for (int m = 0; m < MM; m++) c[m] = h0[m] + h1[m];
-}
-
-// Order of the block sums: batches 1 and 2 of Q4_0 in halves, of Q8_0 in the tree
-// (measured: halves +1.5 % on the 27B Q4_0 pass, -0.6 % on the Q8_0 one); wider batches in
-// position order.  0: position order, 1: tree, 2: halves.
-template <int FMT, int MM>
-constexpr int kSumOrder = MM > 2 ? 0 : FMT == FQ4 ? 2 : 1;
-template <int FMT, int MM>
-__device__ __forceinline__ void chain_block(const Codes<FMT>& q, const char* xb, int mstride,
-                                            float (&c)[MM]) {
-  if constexpr (kSumOrder<FMT, MM> == 1) chain_block_tree<FMT, MM>(q, xb, mstride, c);
-  else if constexpr (kSumOrder<FMT, MM> == 2) chain_block_halves<FMT, MM>(q, xb, mstride, c);
-  else chain_block_seq<FMT, MM>(q, xb, mstride, c);
 }
 
 // Sum over the lane group of 16 (or 8) lanes holding one row (every lane gets the sum): DPP
@@ -889,7 +829,7 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
   // Enter the next (unit, chunk) with rows in this workgroup: wait for earlier outputs
   // where a unit asks (also for a unit with none of its rows here: every workgroup takes
   // part in every wait), then, once all waves finished reading the staged x, stage the new
-  // x and its block sums.  Every wave enters the same (unit, chunk)s, in order.  False when
+  // x.  Every wave enters the same (unit, chunk)s, in order.  False when
   // no unit is left or a wait failed.
   auto enter = [&]() -> bool {
     for (;;) {
@@ -919,10 +859,8 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
     __syncthreads();
     // x comes through agent-coherent loads (other workgroups may have written it), 16
     // bytes per lane: a pass of a wave stages 8 whole blocks of one input.  Up to 4 passes'
-    // loads are issued before any is used.  Then 8 lanes form the blocks' sums in chain
-    // order over the values as staged (Q4_0 positions 16..31 divided by 16, multiplied back
-    // exactly); a wave's LDS accesses complete in order, so its own stores are visible to
-    // its reads.  Inputs m >= M are staged as zeros (their results are not stored).
+    // loads are issued before any is used.  Inputs m >= M are staged as zeros (their
+    // results are not stored).
     if constexpr (IDX && !GU) {  // read here, off the store path (the staging waits anyway)
       if (a.ix.rw) {
 #pragma unroll
@@ -957,58 +895,7 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
           if (c0 < nch) {
             const int c = c0 + lane;
             const int blk = c >> 3, i = c & 7;
-            f32x4 w = v[q];
-            if (FMT == FQ4 && i >= 4) w = w * 0.0625f;
-            if (c < nch) *reinterpret_cast<f32x4*>(xm + blk * kBlkLds + i * 16) = w;
-            if constexpr (kSumOrder<FMT, MM> == 1) {
-              // the block's input sum in the chains' order: this lane's chunk as staged
-              // (Q4_0 high chunks multiplied back by 16, exact), then pairs, quads and
-              // halves of the block's eight lanes (lanes past the end hold zeros)
-              const float mu = FMT == FQ4 && i >= 4 ? 16.0f : 1.0f;
-              float sx = w.x * mu;
-              sx = sx + w.y * mu; sx = sx + w.z * mu; sx = sx + w.w * mu;
-              sx = sx + dpp<0xB1>(sx);   // lane ^ 1
-              sx = sx + dpp<0x4E>(sx);   // lane ^ 2
-              sx = sx + dpp<0x141>(sx);  // the other quad of the eight
-              if (i == 0 && c < nch) *reinterpret_cast<float*>(xm + blk * kBlkLds + 128) = sx;
-            } else if constexpr (kSumOrder<FMT, MM> == 2) {
-              // halves: one lane per half block sums its sixteen values in order (Q4_0
-              // positions 16..31 multiplied back by 16, exact), then the pair adds
-              asm volatile("" ::: "memory");
-              const int b = (c0 >> 3) + (lane >> 1), half = lane & 1;
-              float sx = 0.0f;
-              if (lane < 16 && b < sc.nbc) {
-                const f32x4* xl = reinterpret_cast<const f32x4*>(xm + b * kBlkLds + half * 64);
-                const float mu = FMT == FQ4 && half ? 16.0f : 1.0f;
-                sx = xl[0].x * mu;
-                sx = sx + xl[0].y * mu; sx = sx + xl[0].z * mu; sx = sx + xl[0].w * mu;
-#pragma unroll
-                for (int k = 1; k < 4; k++) {
-                  sx = sx + xl[k].x * mu; sx = sx + xl[k].y * mu; sx = sx + xl[k].z * mu; sx = sx + xl[k].w * mu;
-                }
-              }
-              sx = sx + dpp<0xB1>(sx);  // the other half of the block (lane ^ 1)
-              if (lane < 16 && half == 0 && b < sc.nbc) *reinterpret_cast<float*>(xm + b * kBlkLds + 128) = sx;
-              asm volatile("" ::: "memory");
-            } else {
-              // position order: one lane per block, over the values as staged
-              asm volatile("" ::: "memory");
-              const int b = (c0 >> 3) + lane;
-              if (lane < 8 && b < sc.nbc) {
-                const f32x4* xl = reinterpret_cast<const f32x4*>(xm + b * kBlkLds);
-                float sx = xl[0].x;
-                sx = sx + xl[0].y; sx = sx + xl[0].z; sx = sx + xl[0].w;
-#pragma unroll
-                for (int k = 1; k < 4; k++) { sx = sx + xl[k].x; sx = sx + xl[k].y; sx = sx + xl[k].z; sx = sx + xl[k].w; }
-                const float mu = FMT == FQ4 ? 16.0f : 1.0f;
-#pragma unroll
-                for (int k = 4; k < 8; k++) {
-                  sx = sx + xl[k].x * mu; sx = sx + xl[k].y * mu; sx = sx + xl[k].z * mu; sx = sx + xl[k].w * mu;
-                }
-                *reinterpret_cast<float*>(xm + b * kBlkLds + 128) = sx;
-              }
-              asm volatile("" ::: "memory");
-            }
+            if (c < nch) *reinterpret_cast<f32x4*>(xm + blk * kBlkLds + i * 16) = v[q];
           }
         }
       }
@@ -1027,18 +914,12 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
       for (int p = 0; p < P; p++) {
         if (creal > 0) {  // uniform: a real step of this wave
           const char* xb = cj == sc.ns - 1 ? lds_last : lds_lane + cj * (kG * kBlkLds);
-          float sxm[MM];
-#pragma unroll
-          for (int m = 0; m < MM; m++) sxm[m] = *reinterpret_cast<const float*>(xb + m * mstride + 128);
 #pragma unroll
           for (int r = 0; r < R; r++) {
             float c[MM];
             chain_block<FMT, MM>(ring_q[p][r], xb, mstride, c);
 #pragma unroll
-            for (int m = 0; m < MM; m++) {
-              const float rr = fmaf(FMT == FQ4 ? -8.0f : -128.0f, sxm[m], c[m]);
-              acc[r][m] = fmaf(h2f(ring_d[p][r]), rr, acc[r][m]);
-            }
+            for (int m = 0; m < MM; m++) acc[r][m] = fmaf(h2f(ring_d[p][r]), c[m], acc[r][m]);
           }
           --creal;
           ++cj;
@@ -1213,7 +1094,7 @@ ChainKernel chain_kernel_f(int mm) {
   switch (mm) {
     case 1: return k_qmv_chain<FMT, chain_ring<FMT, 1>(), 1, chain_lgw(1), mode_r(1, MODE), MODE>;
     // two rows per lane: the ring of batch 1 (that of batch 2 would spill)
-    case 2: return k_qmv_chain<FMT, chain_ring<FMT, MODE == 2 ? 1 : 2>(), 2, chain_lgw(2), mode_r(2, MODE), MODE>;
+    case 2: return k_qmv_chain<FMT, chain_ring<FMT, MODE == 2 || FMT == FQ8 ? 1 : 2>(), 2, chain_lgw(2), mode_r(2, MODE), MODE>;
     case 4: return k_qmv_chain<FMT, chain_ring<FMT, 4>(), 4, chain_lgw(4), mode_r(4, MODE), MODE>;
     default: return k_qmv_chain<FMT, chain_ring<FMT, 8>(), 8, chain_lgw(8), mode_r(8, MODE), MODE>;
   }

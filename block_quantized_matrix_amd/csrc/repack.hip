@@ -60,7 +60,11 @@ int launch_repack(int fmt, const void* src, void* dst, int64_t rows, int64_t K, 
   const int pad0_n = (int)(L.scales_off - L.codes_bytes);
   uint8_t* pad1 = base + L.scales_off + nblocks * 2;
   const int pad1_n = (int)(L.total - (L.scales_off + nblocks * 2));
-  int64_t work = nblocks > 256 ? nblocks : 256;  // the padding bytes (< 256 each) too
+  // one thread per block, and enough threads for each padding run (the run after the
+  // scales can exceed 256 bytes: up to 255 of alignment plus the 16-byte slack)
+  int64_t work = nblocks;
+  work = work > pad0_n ? work : pad0_n;
+  work = work > pad1_n ? work : pad1_n;
   const int64_t grid = (work + kThreads - 1) / kThreads;
   uint32_t* codes = reinterpret_cast<uint32_t*>(base);
   uint16_t* scales = reinterpret_cast<uint16_t*>(base + L.scales_off);

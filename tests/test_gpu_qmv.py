@@ -22,7 +22,8 @@ def _oracle():
 # ---- repack / unpack ---------------------------------------------------------------
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("N,K", [(1, 32), (3, 96), (17, 160), (257, 4096), (64, 17408)])
+@pytest.mark.parametrize("N,K", [(1, 32), (3, 96), (17, 160), (121, 32), (249, 32), (257, 4096),
+                                 (64, 17408)])
 def test_repack_roundtrip_bitwise(fmt, N, K):
     say("repack", fmt, N, K)
     bb = gen.block_bytes(fmt)

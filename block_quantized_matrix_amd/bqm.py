@@ -24,6 +24,7 @@ QMV_ID_MAX_T = 64
 QMM_ID_MAX_T = 16384
 QMV_ID_MAX_TOPK = 32
 QMV_ID_MAX_E = 4096
+NOALLOC_SLOT_FLOATS = 1 << 20
 
 _lib = None
 
@@ -51,6 +52,7 @@ def lib():
         L.qmv_id.argtypes = [I, P, I, I64, I64, P, I, I, P, I64, I64, P, P]
         L.qmv_id_gate_up.argtypes = [I, P, P, I, I64, I64, P, I, I, P, I64, I64, P, P]
         L.qmv_id_sum.argtypes = [I, P, I, I64, I64, P, P, I, I, P, I64, I64, P, P, P]
+        L.qmv_id_sum_noalloc.argtypes = [I, P, I, I64, I64, P, P, I, I, P, I64, I64, P, P]
         L.bqm_quantize_q8_act.argtypes = [P, P, P, I64, I64, P]
         L.qmm_q8_0.argtypes = [P, P, P, P, I64, I64, I64, P]
         L.qmm_q4_0.argtypes = [P, P, P, P, I64, I64, I64, P]
@@ -64,8 +66,9 @@ def lib():
             getattr(L, f).restype = I
         L.bqm_strerror.argtypes = [I]
         L.bqm_strerror.restype = ctypes.c_char_p
-        for f in ("bqm_repack", "bqm_unpack", "qmv_q4_0", "qmv_q8_0", "qmv_id",
-                  "bqm_quantize_q8_act", "qmm_q8_0", "qmm_q4_0"):
+        for f in ("bqm_repack", "bqm_unpack", "qmv_q4_0", "qmv_q8_0", "qmv_id", "qmv_id_gate_up",
+                  "qmv_id_sum", "qmv_id_sum_noalloc", "bqm_quantize_q8_act", "qmm_q8_0", "qmm_q4_0",
+                  "qmm_id"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -129,6 +132,12 @@ def qmv_id_sum(fmt, w_packed, E: int, N: int, K: int, ids, weights, T: int, top_
                x_tok_stride: int, x_slot_stride: int, Y_slots, Y, stream=None):
     _call("qmv_id_sum", _fmt(fmt), _ptr(w_packed), E, N, K, _ptr(ids), _ptr(weights), T, top_k,
           _ptr(X), x_tok_stride, x_slot_stride, _ptr(Y_slots), _ptr(Y), _stream(stream))
+
+
+def qmv_id_sum_noalloc(fmt, w_packed, E: int, N: int, K: int, ids, weights, T: int, top_k: int,
+                       X, x_tok_stride: int, x_slot_stride: int, Y, stream=None):
+    _call("qmv_id_sum_noalloc", _fmt(fmt), _ptr(w_packed), E, N, K, _ptr(ids), _ptr(weights), T,
+          top_k, _ptr(X), x_tok_stride, x_slot_stride, _ptr(Y), _stream(stream))
 
 
 def qmv_id_gate_up(fmt, w_gate, w_up, E: int, N: int, K: int, ids, T: int, top_k: int, X,

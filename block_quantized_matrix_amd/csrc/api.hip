@@ -150,6 +150,25 @@ int qmv_id_sum(int fmt, const void* w_packed, int E, int64_t N, int64_t K, const
                            x_slot_stride, Y_slots, Y, stream);
 }
 
+int qmv_id_sum_noalloc(int fmt, const void* w_packed, int E, int64_t N, int64_t K,
+                       const int32_t* ids, const float* weights, int T, int top_k, const float* X,
+                       int64_t x_tok_stride, int64_t x_slot_stride, float* Y, hipStream_t stream) {
+  bool nothing = false;
+  // the same checks as qmv_id_sum, Y standing in for the slot rows' pointer checks
+  if (int st = check_id(fmt, w_packed, nullptr, false, E, N, K, ids, T, top_k, X, x_tok_stride,
+                        x_slot_stride, Y, &nothing))
+    return st;
+  if (T == 0 || N == 0) return BQM_OK;
+  if (!Y) return BQM_E_NULL;
+  if (!aligned16(Y)) return BQM_E_ALIGN;
+  if ((int64_t)T * top_k * N > BQM_NOALLOC_SLOT_FLOATS) return BQM_E_SHAPE;
+  if (top_k == 0) return launch_fill(Y, (int64_t)T * N, 0.0f, stream);  // empty sums
+  if (!weights) return BQM_E_NULL;
+  if ((reinterpret_cast<uintptr_t>(weights) & 3) != 0) return BQM_E_ALIGN;
+  return launch_qmv_id_sum_noalloc(fmt, w_packed, E, N, K, ids, weights, T, top_k, X, x_tok_stride,
+                                   x_slot_stride, Y, stream);
+}
+
 int bqm_quantize_q8_act(const float* X, int8_t* Xq, float* dx, int64_t M, int64_t K,
                         hipStream_t stream) {
   if (M < 0 || K < 0 || K % kQK != 0 || M > kMaxRows || K > ((int64_t)1 << 30)) return BQM_E_SHAPE;

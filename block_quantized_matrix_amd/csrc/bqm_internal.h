@@ -59,6 +59,9 @@ int launch_qmv_id_gate_up(int fmt, const void* w_gate, const void* w_up, int E, 
 int launch_qmv_id_sum(int fmt, const void* w, int E, int64_t N, int64_t K, const int32_t* ids,
                       const float* rw, int T, int top_k, const float* X, int64_t xts, int64_t xss,
                       float* Y_slots, float* Y, hipStream_t s);
+int launch_qmv_id_sum_noalloc(int fmt, const void* w, int E, int64_t N, int64_t K, const int32_t* ids,
+                              const float* rw, int T, int top_k, const float* X, int64_t xts,
+                              int64_t xss, float* Y, hipStream_t s);
 int launch_quantize_q8_act(const float* X, int8_t* Xq, float* dx, int64_t M, int64_t K,
                            hipStream_t s);
 int launch_qmm_q8_0(const void* w, const int8_t* Xq, const float* dx, float* Y, int64_t M,

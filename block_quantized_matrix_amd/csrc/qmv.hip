@@ -1390,4 +1390,40 @@ int launch_qmv_id_sum(int fmt, const void* w, int E, int64_t N, int64_t K, const
   return launch_status();
 }
 
+// ---- the weighted sum without a caller buffer -------------------------------------------
+// For callers that cannot allocate: the weighted slot rows live in a file-scope device array
+// of BQM_NOALLOC_SLOT_FLOATS floats (4 MiB), one copy per GPU, held until the process ends.
+// Its address is a device address only through hipGetSymbolAddress (the array's name in host
+// code is a host-side stand-in), taken once per device with that device current and kept.
+// Every slot row is written by the product before the slot sum reads it, so nothing has to
+// start at zero; calls that overlap in time on one GPU share the array and race.
+static __device__ __align__(256) float scratch[BQM_NOALLOC_SLOT_FLOATS];
+
+namespace {
+std::mutex g_scratch_mutex;
+float* g_scratch_ptr[64] = {};
+
+int scratch_on_current_device(float** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return BQM_E_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return BQM_E_LAUNCH;
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return BQM_OK;
+}
+}  // namespace
+
+int launch_qmv_id_sum_noalloc(int fmt, const void* w, int E, int64_t N, int64_t K, const int32_t* ids,
+                              const float* rw, int T, int top_k, const float* X, int64_t xts,
+                              int64_t xss, float* Y, hipStream_t s) {
+  if ((int64_t)T * top_k * N > BQM_NOALLOC_SLOT_FLOATS) return BQM_E_SHAPE;
+  float* slots = nullptr;
+  if (int st = scratch_on_current_device(&slots)) return st;
+  return launch_qmv_id_sum(fmt, w, E, N, K, ids, rw, T, top_k, X, xts, xss, slots, Y, s);
+}
+
 }  // namespace bqm

@@ -22,7 +22,8 @@
  *
  * Conventions shared by every call:
  *   - Pointers are DEVICE pointers unless stated; the caller owns all memory.  The
- *     library allocates nothing and frees nothing; work is queued on `stream` (a HIP
+ *     library allocates nothing and frees nothing (qmv_id_sum_noalloc keeps its slot rows
+ *     in a fixed device array that is part of the library); work is queued on `stream` (a HIP
  *     stream; 0 = the null stream) and the call returns without synchronizing (only
  *     bqm_chain_prepare and bqm_chain_status wait, as their entries say).
  *   - Argument errors are found on the host before anything is launched: the call
@@ -146,6 +147,20 @@ int qmv_id_gate_up(int fmt, const void* w_gate, const void* w_up, int E, int64_t
 int qmv_id_sum(int fmt, const void* w_packed, int E, int64_t N, int64_t K, const int32_t* ids,
                const float* weights, int T, int top_k, const float* X, int64_t x_tok_stride,
                int64_t x_slot_stride, float* Y_slots, float* Y, hipStream_t stream);
+
+/* qmv_id_sum for callers that cannot allocate device memory (code being captured into a HIP
+ * graph, tight serving loops, harnesses that forbid hipMalloc): the same computation and
+ * results as qmv_id_sum, without the Y_slots argument.  The weighted slot rows are kept in a
+ * device array inside the library, BQM_NOALLOC_SLOT_FLOATS floats (4 MiB) per GPU, held
+ * from the first call on that GPU until the process ends; the call itself allocates
+ * nothing.  T * top_k * N above BQM_NOALLOC_SLOT_FLOATS: BQM_E_SHAPE.  Every call on one GPU
+ * uses that GPU's array: calls that overlap in time on one GPU (other streams, other host
+ * threads) race and must not be issued.  Other arguments, limits and status codes as
+ * qmv_id_sum; BQM_E_LAUNCH also if the array's address cannot be obtained. */
+#define BQM_NOALLOC_SLOT_FLOATS (1 << 20)
+int qmv_id_sum_noalloc(int fmt, const void* w_packed, int E, int64_t N, int64_t K,
+                       const int32_t* ids, const float* weights, int T, int top_k, const float* X,
+                       int64_t x_tok_stride, int64_t x_slot_stride, float* Y, hipStream_t stream);
 
 /* ---- chains of GEMVs in one launch ----------------------------------------------------
  * Decode runs one GEMV after another, each reading the previous one's output (through

@@ -99,6 +99,13 @@ def test_host_validation_before_launch():
     assert L.qmv_id_sum(2, GOOD, 4, 8, 64, GOOD, None, 1, 2, GOOD, 64, 0, GOOD, GOOD, None) == 1
     assert L.qmv_id_sum(2, GOOD, 4, 8, 64, GOOD, P(0x100002), 1, 2, GOOD, 64, 0, GOOD, GOOD, None) == 3
     assert L.qmv_id_sum(2, GOOD, 4, 8, 64, None, GOOD, 1, 2, GOOD, 64, 0, GOOD, GOOD, None) == 1
+    # qmv_id_sum_noalloc: qmv_id_sum's checks, and the slot rows must fit the library's array
+    assert L.qmv_id_sum_noalloc(5, GOOD, 4, 8, 64, GOOD, GOOD, 1, 2, GOOD, 64, 0, GOOD, None) == 4
+    assert L.qmv_id_sum_noalloc(2, GOOD, 4, 8, 64, GOOD, GOOD, 65, 2, GOOD, 64, 0, GOOD, None) == 2
+    assert L.qmv_id_sum_noalloc(2, GOOD, 4, 8, 64, GOOD, GOOD, 1, 2, GOOD, 64, 0, None, None) == 1
+    assert L.qmv_id_sum_noalloc(2, GOOD, 4, 8, 64, GOOD, GOOD, 1, 2, GOOD, 64, 0, ODD, None) == 3
+    assert L.qmv_id_sum_noalloc(2, GOOD, 4, 8, 64, GOOD, None, 1, 2, GOOD, 64, 0, GOOD, None) == 1
+    assert L.qmv_id_sum_noalloc(2, GOOD, 4, 1024, 64, GOOD, GOOD, 64, 32, GOOD, 64, 0, GOOD, None) == 2
     # quantizer and qmm
     assert L.bqm_quantize_q8_act(GOOD, GOOD, GOOD, 4, 40, None) == 2
     assert L.bqm_quantize_q8_act(GOOD, None, GOOD, 4, 64, None) == 1

@@ -4,11 +4,14 @@
 One step = one decoded token's pass over a 27B-dense model's GEMV weight stream: 64 layers,
 each q|k|v (7168 x 5120, the three projections stacked since they read the same input),
 o (5120 x 5120), gate|up (34816 x 5120, stacked likewise) and down (5120 x 17408), all
-Q4_0, batch 1, launched in layer order on one stream and replayed as a HIP graph.  Weights
+Q4_0, batch 1, as ONE chain launch of the 256 GEMVs in layer order, each GEMV waiting
+(device-wide) for all earlier ones, as a decode step's data dependencies require.  Weights
 are seeded N(0, 0.02) draws quantized to Q4_0, inputs N(0, 1), all resident in HBM before
 the timed region.  The headline is achieved HBM GB/s over the algorithmic bytes of the
 stream (packed codes and scales read once, fp32 inputs read, outputs written) and the
-equivalent decode tokens/s (1 / time per pass).
+equivalent decode tokens/s (1 / time per pass).  Reported beside it: the per-step median
+and 10th/90th percentiles, the same GEMVs as one chain without waits (the streaming rate
+alone), and each layer shape's sustained rate over 64 independent copies.
 
 Other workloads (--workload): the single 4096 x 4096 GEMV, the Q8_0 stream at M = 1/4/8,
 the 128-expert MoE layer through qmv_id, and the 512 x 5120 x 17408 prefill GEMM.
@@ -99,6 +102,51 @@ def time_steps(run, steps, warmup, torch, use_graph):
     t1.record()
     torch.cuda.synchronize()
     return t0.elapsed_time(t1) / steps   # ms per step
+
+
+def step_percentiles(run, steps, torch):
+    """Each of `steps` further steps bracketed by its own events: median, 10th and 90th
+    percentile of the per-step time in ms."""
+    cur = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record(cur)
+        run()
+        b.record(cur)
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in ev])
+    return {"median": round(float(np.median(t)), 4), "p10": round(float(np.percentile(t, 10)), 4),
+            "p90": round(float(np.percentile(t, 90)), 4), "n": int(steps)}
+
+
+def chain_of(fmt, M, items, wait, torch, bqm):
+    """Prepare chains over (w, N, K, x, y) items; returns the run function (the workspaces
+    stay alive in its closure).  One chain when it can be planned; a chain without waits whose
+    single segment leaves a workgroup more partial sums than its local memory holds (long K
+    at M >= 4) is split into halves, run back to back."""
+    descs = [bqm.gemv(fmt, w, x, y, N, K, wait=wait and i > 0, M=M) for i, (w, N, K, x, y) in enumerate(items)]
+    ws = torch.zeros(bqm.chain_workspace_bytes(len(descs)), dtype=torch.uint8, device="cuda")
+    try:
+        bqm.bqm_chain_prepare(descs, ws)
+    except bqm.BqmError as e:
+        if e.status != 2 or wait or len(items) < 2:
+            raise
+        h = len(items) // 2
+        parts = [chain_of(fmt, M, items[:h], False, torch, bqm), chain_of(fmt, M, items[h:], False, torch, bqm)]
+
+        def run_parts():
+            for r in parts:
+                r()
+        run_parts.ws = parts[0].ws
+        run_parts.chains = sum(getattr(r, "chains", 1) for r in parts)
+        return run_parts
+
+    def run():
+        bqm.qmv_chain(fmt, M, ws, len(descs))
+    run.ws = ws
+    run.chains = 1
+    return run
 
 
 def per_launch_ms(launches, torch, reps=3):
@@ -293,6 +341,22 @@ def run_dense(args, torch, gen, bqm, fmt="q4_0"):
         kernel = f"k_qmv_chain ({fmt.upper()}, M={M}, {len(descs)} GEMVs per launch)"
         launch_us = round(1e3 * float(dur.mean()), 3)
         kkey = f"qmv_chain_{fmt}_dense27b" if M == 1 else f"qmv_chain_{fmt}_m{M}_dense27b"
+        pct = step_percentiles(run, max(20, args.steps), torch)
+        # diagnostics beside the headline: the same GEMVs with no waits (the stream alone),
+        # and each layer shape's sustained rate over its 64 independent copies
+        items = [(w, N, K, x, y) for (w, N, K), x, y in zip(mats, xs, ys)]
+        run_ind = chain_of(fmt, M, items, False, torch, bqm)
+        ms_ind = time_steps(run_ind, args.steps, args.warmup, torch, False)
+        per_shape = {}
+        for j, (name, N, K) in enumerate(shapes):
+            sub = items[j::len(shapes)]
+            run_s = chain_of(fmt, M, sub, False, torch, bqm)
+            ms_s = time_steps(run_s, max(5, args.steps // 2), 2, torch, False)
+            b = sum(weight_bytes(fmt, N, K) + 4 * M * (N + K) for _ in sub)
+            per_shape[f"{name} {N}x{K}"] = {"copies": len(sub), "ms": round(ms_s, 4),
+                                             "gbs": round(b / (ms_s * 1e-3) / 1e9, 1)}
+        if bqm.bqm_chain_status(run_ind.ws) != 0:
+            raise RuntimeError("independent chain reported an error")
     else:
         ms = time_steps(run_separate, args.steps, args.warmup, torch, not args.no_graph)
         dur = per_launch_ms(launches, torch)
@@ -322,6 +386,12 @@ def run_dense(args, torch, gen, bqm, fmt="q4_0"):
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "equiv_tok_s": round(1e3 / ms, 2),
         "separate_launches_ms_per_step": None if ms_sep is None else round(ms_sep, 4),
+        **({"step_ms": pct,
+            "independent_gemvs": {"ms_per_step": round(ms_ind, 4),
+                                  "gbs": round(total / (ms_ind * 1e-3) / 1e9, 1),
+                                  "chains": run_ind.chains,
+                                  "note": "the same 256 GEMVs as chains without waits"},
+            "per_shape_sustained": per_shape} if use_chain else {}),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": kernel, "avg_launch_us": launch_us},
@@ -379,6 +449,20 @@ def run_gemv4096(args, torch, gen, bqm):
             f()
 
     ms_sep = time_steps(run_sep, max(3, args.steps // 2), 1, torch, not args.no_graph)
+    # single launches, as a caller makes them: 256 calls over the 64 copies, each bracketed
+    # by its own events on the stream it runs on
+    cur = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(256)]
+    for i, (a, b) in enumerate(ev):
+        a.record(cur)
+        launches[i % copies]()
+        b.record(cur)
+    torch.cuda.synchronize()
+    single = np.array([a.elapsed_time(b) for a, b in ev]) * 1e3   # us
+    single_stats = {"n": len(single), "median_us": round(float(np.median(single)), 2),
+                    "p10_us": round(float(np.percentile(single, 10)), 2),
+                    "p90_us": round(float(np.percentile(single, 90)), 2),
+                    "gbs_at_median": round(per / (float(np.median(single)) * 1e-6) / 1e9, 1)}
     return {"metric": "Q4_0 GEMV 4096x4096 sustained GB/s", "value": round(gbs, 2), "unit": "GB/s",
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
@@ -388,6 +472,7 @@ def run_gemv4096(args, torch, gen, bqm):
             "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
             "separate_launches_ms_per_step": round(ms_sep, 4),
             "separate_launches_gbs": round(per * copies / (ms_sep * 1e-3) / 1e9, 1),
+            "single_launch": single_stats,
             "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                          "traffic": traffic_from_profiles("qmv_chain_q4_0_gemv4096"),
@@ -489,7 +574,7 @@ def run_moe(args, torch, gen, bqm):
                     "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                                  "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                                  "traffic": traffic_from_profiles(f"qmv_id_q4_0_moe_t{T}"),
-                                 "kernel": f"k_qmv_chain indexed form (Q4_0, batch class {1 if T == 1 else 8})",
+                                 "kernel": f"k_qmv_chain indexed form (Q4_0, batch class {1 if T == 1 else 2 if T == 2 else 4})",
                                  "avg_launch_us": round(1e3 * float(dur.mean()), 3)},
                     "fused_gate_up": {
                         "ms_per_layer": round(ms_f / n_layers, 4), "gbs_unique_bytes": round(gbs_f, 1),

@@ -16,12 +16,12 @@
 // eight neighbouring lanes (eight consecutive blocks) hit eight different bank groups.
 // Long rows are staged in chunks of blocks that fit the LDS budget.
 //
-// Arithmetic.  Every code becomes its signed value exactly before it meets x (a Q4_0
-// nibble as the binary16 value n - 8 through a mantissa trick, a Q8_0 byte through a
-// sign-extending conversion), and each block's 32 products are summed by fused
-// multiply-adds, then scaled by d: the rounding error of a block stays proportional to
-// sum |(n - 8) d x|, its share of the tolerance scale, and neutral codes give exactly zero.
-// The signed codes of a block are formed once and shared by the M inputs.
+// Arithmetic.  Every code becomes its signed value exactly before it meets x (a Q4_0 nibble
+// as 16 (n - 8) in a byte, a Q8_0 code as is, each through a sign-extending byte
+// conversion), and each block's 32 products are summed by fused multiply-adds, then scaled by
+// d (Q4_0: d / 16): the rounding error of a block stays proportional to sum |(n - 8) d x|, its
+// share of the tolerance scale, and neutral codes give exactly zero.  The signed codes of a
+// block are formed once and shared by the M inputs.
 //
 // Reduction: a butterfly of cross-lane shuffles inside the lane group, then one lane
 // stores the row.  No atomics; the summation order is fixed for a given launch shape.
@@ -73,10 +73,9 @@ template <> struct Codes<FQ8> { u32x4 a, b; };
 //    unrolled by P).  The ring runs ahead across GEMV and chunk boundaries: the weights of
 //    the next GEMV do not depend on its input, so they stream while the workgroup waits for
 //    the previous GEMV's outputs (device-wide barrier) and stages the new x.
-// Arithmetic per block and row (see chain_block): Q4_0 4 shifts, 16 and-ors and 16 packed
-// binary16 subtractions give the 32 signed codes, Q8_0 32 sign-extending conversions; then
-// per input 32 fused multiply-adds (v_fma_mix for the binary16 codes) and acc += d * sum
-// (v_fma_mix again: d stays binary16).
+// Arithmetic per block and row (see chain_block): Q4_0 12 integer ops and 32 sign-extending
+// conversions give the signed codes, Q8_0 32 conversions; then per input 32 fp32 FMAs and
+// acc += d * sum.
 constexpr int kP1Waves = 16;  // waves of a workgroup (8 for the widest batch: registers)
 constexpr int kBlkLds = 144;  // LDS bytes per staged block
 constexpr int kChainMaxM = 8;
@@ -100,110 +99,94 @@ static_assert(kLg2G >= 3 && kLg2G <= 4, "group_sum covers 8 or 16 lanes");
 // afterwards cancels: its error grows with sum (n + 8)|x| and can swallow a whole
 // near-neutral block.)  All-neutral codes give exactly zero.
 
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-
-// The eight nibbles of one Q4_0 code word as four pairs of binary16 values n - 8, with no
-// conversion instruction: OR-ed into the mantissa of 1024.0 (0x6400) a nibble n reads as
-// 1024 + n, and a nibble at bits 4..7 OR-ed into 64.0 (0x5400, mantissa step 1/16) reads as
-// 64 + n; one packed subtraction per pair gives n - 8 exactly.  The pairs then enter
-// v_fma_mix_f32 directly (a binary16 operand widened inside the FMA, x stays fp32).  Byte b
-// of word k holds position 4k + b in its low nibble and 16 + 4k + b in its high nibble, so
-// the pairs hold positions (4k, 4k+2), (4k+1, 4k+3) and the same 16 positions on.
-struct Q4Pairs {
-  h2 l02, l13, h02, h13;
+// Q4_0 codes as bytes holding 16 (n - 8): a nibble n with its top bit flipped, n ^ 8, is the
+// two's complement of n - 8 in four bits, so (w ^ 0x80808080) & 0xF0F0F0F0 leaves the high
+// nibbles (positions 16 + 4k + b of word k) as 16 (n - 8) at the top of their bytes and
+// ((w << 4) ^ 0x80808080) & 0xF0F0F0F0 the low ones (positions 4k + b); one shift and two
+// three-input bit operations (v_bitop3_b32) per word.  A sign-extending byte conversion
+// (v_cvt_f32_i32 with an SDWA byte select) then gives 16 (n - 8) exactly, and the 1/16 goes
+// into the block's scale (d / 16 is exact for every binary16 d).  Measured on gfx950: plain fp32 FMAs issue about twice as
+// fast as v_fma_mix_f32, the packed binary16 ops and the conversions, so this form (3 integer
+// ops and 8 conversions per 8 codes, then plain FMAs) beats binary16 code pairs fed to
+// v_fma_mix from batch 2 on and matches them at batch 1.
+struct Q4Bytes {
+  uint32_t lo, hi;  // byte b: 16 (n - 8) of position 4k + b, and of 16 + 4k + b
 };
-// mask and magic constants live in registers: a VOP3 and-or takes no literal operand
-struct Q4Consts {
-  uint32_t mlo, mhi, klo, khi;
-};
-__device__ __forceinline__ Q4Consts q4_consts() {
-  Q4Consts c{0x000F000Fu, 0x00F000F0u, 0x64006400u, 0x54005400u};
-  asm("" : "+s"(c.mlo), "+s"(c.mhi), "+v"(c.klo), "+v"(c.khi));
-  return c;
+__device__ __forceinline__ Q4Bytes q4_bytes(uint32_t w) {
+  return Q4Bytes{((w << 4) ^ 0x80808080u) & 0xF0F0F0F0u, (w ^ 0x80808080u) & 0xF0F0F0F0u};
 }
-__device__ __forceinline__ Q4Pairs q4_pairs(uint32_t w, const Q4Consts& k) {
-  const uint32_t s = w >> 8;
-  const h2 lo_off = {(_Float16)1032.0f, (_Float16)1032.0f}, hi_off = {(_Float16)72.0f, (_Float16)72.0f};
-  Q4Pairs p;
-  p.l02 = __builtin_bit_cast(h2, (w & k.mlo) | k.klo) - lo_off;
-  p.l13 = __builtin_bit_cast(h2, (s & k.mlo) | k.klo) - lo_off;
-  p.h02 = __builtin_bit_cast(h2, (w & k.mhi) | k.khi) - hi_off;
-  p.h13 = __builtin_bit_cast(h2, (s & k.mhi) | k.khi) - hi_off;
-  return p;
+__device__ __forceinline__ float sbyte(uint32_t v, int b) {
+  return (float)(int8_t)(v >> (8 * b));  // v_cvt_f32_i32 with a sign-extending byte select
 }
 
 // One block of codes against MM staged input blocks (input m at xb + m * mstride bytes):
-// c[m] = sum_{j < 32} code_j * x_mj by FMA chains in a fixed order.  A word's signed codes
-// are formed once and shared by the MM inputs.  The order only changes which registers stay
-// live (any fixed order meets the bound), so it is picked per format and batch:
-//  - Q4_0, batches 1-2: word-major, one chain: for word k positions 4k..4k+3, then
-//    16+4k..16+4k+3, so a word's pairs die at once;
-//  - Q4_0, batches 4-8: one chain in position order 0..31 (the low nibbles of the four words,
-//    then the high ones), so each input's two staged chunks are not live together;
-//  - Q8_0, batches 1-2: eight chains of four positions (one per 16-byte piece of the staged
-//    input) added as ((c0 + c1) + (c2 + c3)) + ((c4 + c5) + (c6 + c7)): each piece's reads
-//    are used at once (with one or two chains the scheduler hoisted every read and batch 2
-//    with two steps in flight spilled registers);
-//  - Q8_0, batches 4-8: one chain in position order.
-template <int FMT, int MM>
+// c[m] = sum_{j < 32} code_j * x_mj (Q4_0: 16 times that) by FMA chains in a fixed order.  A
+// word's signed codes are formed once and shared by the MM inputs.  The order only changes
+// which registers stay live (any fixed order meets the bound), so it is picked per format
+// and batch class:
+//  - batches 1-2: Q4_0 word-major, one chain: for word k positions 4k..4k+3 then
+//    16+4k..16+4k+3, so a word's codes die at once; Q8_0 eight chains of four positions (one
+//    per 16-byte piece of the staged input) added as ((c0 + c1) + (c2 + c3)) + ((c4 + c5) +
+//    (c6 + c7)): each piece's reads are used at once (with one or two chains the scheduler
+//    hoisted every read and batch 2 with two steps in flight spilled registers);
+//  - batches 4-8: one chain in position order 0..31 (Q4_0: the low nibbles of the four words,
+//    then the high ones), so each input's two staged chunks are not live together.
+template <int FMT, int MM, int WIDE = (MM > 2)>  // WIDE: the order of batches 4-8
 __device__ __forceinline__ void chain_block(const Codes<FMT>& q, const char* xb, int mstride,
                                             float (&c)[MM]) {
   auto xm = [&](int m, int k) { return *reinterpret_cast<const f32x4*>(xb + m * mstride + k * 16); };
   if constexpr (FMT == FQ4) {
-    const Q4Consts kc = q4_consts();
     const uint32_t w[4] = {q.a.x, q.a.y, q.a.z, q.a.w};
-    if constexpr (MM <= 2) {
+    if constexpr (!WIDE) {
 #pragma unroll
       for (int k = 0; k < 4; k++) {
-        const Q4Pairs p = q4_pairs(w[k], kc);
+        const Q4Bytes p = q4_bytes(w[k]);
+        const float l0 = sbyte(p.lo, 0), l1 = sbyte(p.lo, 1), l2 = sbyte(p.lo, 2), l3 = sbyte(p.lo, 3);
+        const float h0 = sbyte(p.hi, 0), h1 = sbyte(p.hi, 1), h2 = sbyte(p.hi, 2), h3 = sbyte(p.hi, 3);
 #pragma unroll
         for (int m = 0; m < MM; m++) {
           const f32x4 a = xm(m, k), b = xm(m, k + 4);
-          float t = fmaf((float)p.l02.x, a.x, k == 0 ? 0.0f : c[m]);  // v_fma_mix onto +0 at k = 0
-          t = fmaf((float)p.l13.x, a.y, t);
-          t = fmaf((float)p.l02.y, a.z, t);
-          t = fmaf((float)p.l13.y, a.w, t);
-          t = fmaf((float)p.h02.x, b.x, t);
-          t = fmaf((float)p.h13.x, b.y, t);
-          t = fmaf((float)p.h02.y, b.z, t);
-          c[m] = fmaf((float)p.h13.y, b.w, t);
+          float t = k == 0 ? l0 * a.x : fmaf(l0, a.x, c[m]);
+          t = fmaf(l1, a.y, t);
+          t = fmaf(l2, a.z, t);
+          t = fmaf(l3, a.w, t);
+          t = fmaf(h0, b.x, t);
+          t = fmaf(h1, b.y, t);
+          t = fmaf(h2, b.z, t);
+          c[m] = fmaf(h3, b.w, t);
         }
       }
     } else {
-      Q4Pairs p[4];
+      Q4Bytes p[4];
 #pragma unroll
-      for (int k = 0; k < 4; k++) p[k] = q4_pairs(w[k], kc);
+      for (int k = 0; k < 4; k++) p[k] = q4_bytes(w[k]);
+      float t[MM];
 #pragma unroll
-      for (int m = 0; m < MM; m++) {
-        float t;
+      for (int half = 0; half < 2; half++) {
 #pragma unroll
-        for (int k = 0; k < 4; k++) {  // positions 4k .. 4k+3: low nibbles of word k
-          const f32x4 a = xm(m, k);
-          t = fmaf((float)p[k].l02.x, a.x, k == 0 ? 0.0f : t);
-          t = fmaf((float)p[k].l13.x, a.y, t);
-          t = fmaf((float)p[k].l02.y, a.z, t);
-          t = fmaf((float)p[k].l13.y, a.w, t);
+        for (int k = 0; k < 4; k++) {  // half 0: low nibbles (positions 4k..), 1: high (16 + 4k..)
+          const uint32_t v = half ? p[k].hi : p[k].lo;
+          const float v0 = sbyte(v, 0), v1 = sbyte(v, 1), v2 = sbyte(v, 2), v3 = sbyte(v, 3);
+#pragma unroll
+          for (int m = 0; m < MM; m++) {
+            const f32x4 a = xm(m, k + 4 * half);
+            float u = half == 0 && k == 0 ? v0 * a.x : fmaf(v0, a.x, t[m]);
+            u = fmaf(v1, a.y, u);
+            u = fmaf(v2, a.z, u);
+            t[m] = fmaf(v3, a.w, u);
+          }
         }
-#pragma unroll
-        for (int k = 0; k < 4; k++) {  // positions 16 + 4k .. : high nibbles of word k
-          const f32x4 b = xm(m, k + 4);
-          t = fmaf((float)p[k].h02.x, b.x, t);
-          t = fmaf((float)p[k].h13.x, b.y, t);
-          t = fmaf((float)p[k].h02.y, b.z, t);
-          t = fmaf((float)p[k].h13.y, b.w, t);
-        }
-        c[m] = t;
       }
+#pragma unroll
+      for (int m = 0; m < MM; m++) c[m] = t[m];
     }
   } else {
     const uint32_t w[8] = {q.a.x, q.a.y, q.a.z, q.a.w, q.b.x, q.b.y, q.b.z, q.b.w};
-    constexpr bool kTree = MM <= 2;
+    constexpr bool kTree = !WIDE;
     float pr[MM], qd[MM], hf[MM];  // the tree's partial sums: pair, quad, half
 #pragma unroll
     for (int k = 0; k < 8; k++) {
-      // v_cvt_f32_i32 of a sign-extended byte (SDWA): one instruction per code
-      const float v0 = (float)(int8_t)w[k], v1 = (float)(int8_t)(w[k] >> 8);
-      const float v2 = (float)(int8_t)(w[k] >> 16), v3 = (float)(int8_t)(w[k] >> 24);
+      const float v0 = sbyte(w[k], 0), v1 = sbyte(w[k], 1), v2 = sbyte(w[k], 2), v3 = sbyte(w[k], 3);
 #pragma unroll
       for (int m = 0; m < MM; m++) {
         const f32x4 a = xm(m, k);
@@ -224,6 +207,13 @@ __device__ __forceinline__ void chain_block(const Codes<FMT>& q, const char* xb,
       }
     }
   }
+}
+
+// The block scale as the FMA that applies it takes it: d, or for Q4_0 (whose block sums are
+// 16 times too large) d / 16, exact for every binary16 d.
+template <int FMT>
+__device__ __forceinline__ float block_scale(uint32_t dbits) {
+  return FMT == FQ4 ? h2f(dbits) * 0.0625f : h2f(dbits);
 }
 
 // Sum over the lane group of 16 (or 8) lanes holding one row (every lane gets the sum): DPP
@@ -650,9 +640,15 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
   int u_begin = 0, u_end = n_units;
   int64_t flo = 0, fhi = 0;
   if constexpr (IDX) {
+    // Workgroup b runs on XCD b mod 8; taking the flattened rows in the order of
+    // lb = (b mod 8) * (grid / 8) + b / 8 gives each XCD one contiguous range.  The groups
+    // of an expert are consecutive units, so the workgroups streaming the same expert rows
+    // for its successive groups share an L2 and the rows cross HBM about once.
     const int64_t rows = (int64_t)n_units * a.one.N;
-    flo = (int64_t)blockIdx.x * rows / gridDim.x;
-    fhi = (int64_t)(blockIdx.x + 1) * rows / gridDim.x;
+    const int G = (int)gridDim.x, b = (int)blockIdx.x;
+    const int lb = G % 8 == 0 ? (b % 8) * (G / 8) + b / 8 : b;
+    flo = (int64_t)lb * rows / G;
+    fhi = (int64_t)(lb + 1) * rows / G;
     if (fhi > flo) {
       u_begin = (int)(flo / a.one.N);
       u_end = (int)((fhi - 1) / a.one.N) + 1;
@@ -858,16 +854,16 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
     clg = lane >> kLg2G;
     __syncthreads();
     // x comes through agent-coherent loads (other workgroups may have written it), 16
-    // bytes per lane: a pass of a wave stages 8 whole blocks of one input.  Up to 4 passes'
-    // loads are issued before any is used.  Inputs m >= M are staged as zeros (their
-    // results are not stored).
+    // bytes per lane: a pass of a wave stages 8 whole blocks of each input.  Inputs m >= M
+    // are staged as zeros (their results are not stored).
     if constexpr (IDX && !GU) {  // read here, off the store path (the staging waits anyway)
       if (a.ix.rw) {
 #pragma unroll
         for (int m = 0; m < MM; m++) wslot[m] = m < sc.M ? a.ix.rw[slot_of(sc, m)] : 0.0f;
       }
     }
-    const int nch = sc.nbc * 8;
+    const int nch = sc.nbc * 8;  // 16-byte pieces per input
+    __amdgpu_buffer_rsrc_t rx[MM];
 #pragma unroll
     for (int m = 0; m < MM; m++) {
       int64_t xo = 0;  // input row of entry m (entries m >= M read nothing)
@@ -880,22 +876,35 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
         }
       }
       const float* xrow = sc.x + xo + (int64_t)sc.kb0 * kQK;
-      const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)xrow, (short)0, m < sc.M ? sc.nbc * 128 : 0, 0x00020000);
-      char* xm = xlds + m * mstride;
-      for (int c00 = wave * 64; c00 < nch; c00 += 4 * NT) {
-        f32x4 v[4];
+      rx[m] = __builtin_amdgcn_make_buffer_rsrc((void*)xrow, (short)0, m < sc.M ? sc.nbc * 128 : 0,
+                                                0x00020000);
+    }
+    // Loads per lane in flight taken over the inputs and the passes together: MB inputs at a
+    // time, QC passes each (eight loads; four for the widest batch, whose registers are
+    // spent).  Staging the inputs one after another cost a memory round trip per input after
+    // every wait.
+    constexpr int MB = MM >= 8 ? 4 : MM, QC = MM >= 8 ? 1 : 8 / MM;
 #pragma unroll
-        for (int q = 0; q < 4; q++)  // past the end reads zeros
-          v[q] = __builtin_bit_cast(
-              f32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (c00 + q * NT + lane) * 16, 0, 16));
+    for (int mb = 0; mb < MM; mb += MB) {
+      for (int c00 = wave * 64; c00 < nch; c00 += QC * NT) {
+        f32x4 v[MB][QC];
 #pragma unroll
-        for (int q = 0; q < 4; q++) {
-          const int c0 = c00 + q * NT;
-          if (c0 < nch) {
-            const int c = c0 + lane;
+        for (int q = 0; q < QC; q++)
+#pragma unroll
+          for (int m = 0; m < MB; m++) {  // a pass wholly past the end loads nothing (uniform)
+            v[m][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (c00 + q * NT < nch)  // lanes past the end read zeros
+              v[m][q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      rx[mb + m], (c00 + q * NT + lane) * 16, 0, 16));
+          }
+#pragma unroll
+        for (int q = 0; q < QC; q++) {
+          const int c = c00 + q * NT + lane;
+          if (c < nch) {
             const int blk = c >> 3, i = c & 7;
-            if (c < nch) *reinterpret_cast<f32x4*>(xm + blk * kBlkLds + i * 16) = v[q];
+#pragma unroll
+            for (int m = 0; m < MB; m++)
+              *reinterpret_cast<f32x4*>(xlds + (mb + m) * mstride + blk * kBlkLds + i * 16) = v[m][q];
           }
         }
       }
@@ -918,8 +927,9 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
           for (int r = 0; r < R; r++) {
             float c[MM];
             chain_block<FMT, MM>(ring_q[p][r], xb, mstride, c);
+            const float dsc = block_scale<FMT>(ring_d[p][r]);
 #pragma unroll
-            for (int m = 0; m < MM; m++) acc[r][m] = fmaf(h2f(ring_d[p][r]), c[m], acc[r][m]);
+            for (int m = 0; m < MM; m++) acc[r][m] = fmaf(dsc, c[m], acc[r][m]);
           }
           --creal;
           ++cj;
@@ -1093,10 +1103,13 @@ template <int FMT, int MODE>
 ChainKernel chain_kernel_f(int mm) {
   switch (mm) {
     case 1: return k_qmv_chain<FMT, chain_ring<FMT, 1>(), 1, chain_lgw(1), mode_r(1, MODE), MODE>;
-    // two rows per lane: the ring of batch 1 (that of batch 2 would spill)
-    case 2: return k_qmv_chain<FMT, chain_ring<FMT, MODE == 2 || FMT == FQ8 ? 1 : 2>(), 2, chain_lgw(2), mode_r(2, MODE), MODE>;
+    // batch 2: one step in flight for the chain (R = 1), the batch-1 ring for the indexed
+    // forms (two rows per lane); deeper rings spill registers
+    case 2: return k_qmv_chain<FMT, MODE == 0 ? 1 : chain_ring<FMT, 1>(), 2, chain_lgw(2), mode_r(2, MODE), MODE>;
     case 4: return k_qmv_chain<FMT, chain_ring<FMT, 4>(), 4, chain_lgw(4), mode_r(4, MODE), MODE>;
-    default: return k_qmv_chain<FMT, chain_ring<FMT, 8>(), 8, chain_lgw(8), mode_r(8, MODE), MODE>;
+    default:  // the indexed forms run at most class 4 (launch_id): no class 8 for them
+      if constexpr (MODE != 0) return chain_kernel_f<FMT, MODE>(4);
+      else return k_qmv_chain<FMT, chain_ring<FMT, 8>(), 8, chain_lgw(8), mode_r(8, MODE), MODE>;
   }
 }
 template <int MODE>
@@ -1136,21 +1149,35 @@ int64_t chain_max_k() { return 32768; }
 // Staging plan of a chain: kc (K blocks staged at a time) and the rows of the per-row
 // partial-sum buffer (0 when no GEMV is walked in chunks).  Whole GEMVs are staged when
 // the table, the split-tile parts and M inputs of the longest K fit; otherwise every GEMV
-// longer than kc goes in chunks.  Returns false when even 32-block chunks do not fit.
-bool chain_plan(int n, int mm, int64_t max_nb, int64_t max_rows, int* kc, int* pacc_rows) {
+// longer than kc goes in chunks, and the partial sums are sized for the most rows a
+// workgroup holds of one such GEMV.  `nbs` and `rows`: per GEMV, its blocks per row and the
+// most rows a workgroup holds of it.  Returns false when even 32-block chunks do not fit.
+bool chain_plan(int n, int mm, const int64_t* nbs, const int64_t* rows, int count, int* kc,
+                int* pacc_rows) {
+  int64_t max_nb = 0;
+  for (int i = 0; i < count; i++) max_nb = nbs[i] > max_nb ? nbs[i] : max_nb;
   const int64_t fixed = chain_lds(n, mm, chain_r(mm), 0, 0).total;
   if (fixed + (int64_t)mm * max_nb * kBlkLds <= kP1MaxLds) {
     *kc = (int)max_nb;
     *pacc_rows = 0;
     return true;
   }
-  const int64_t pacc = (max_rows * mm * 4 + 15) & ~int64_t(15);
-  const int64_t room = kP1MaxLds - fixed - pacc;
-  const int64_t k = room / ((int64_t)mm * kBlkLds);
-  if (room <= 0 || k < 32) return false;
-  *kc = (int)(k & ~int64_t(15));  // a multiple of the lane group widths' common factor
-  *pacc_rows = (int)max_rows;
-  return true;
+  // the largest kc (a multiple of 16) whose chunked GEMVs' partial sums fit beside it
+  for (int64_t k = (max_nb - 1) & ~int64_t(15); k >= 32; k -= 16) {
+    int64_t prow = 0;
+    for (int i = 0; i < count; i++)
+      if (nbs[i] > k && rows[i] > prow) prow = rows[i];
+    const int64_t pacc = (prow * mm * 4 + 15) & ~int64_t(15);
+    if (fixed + pacc + (int64_t)mm * k * kBlkLds <= kP1MaxLds) {
+      *kc = (int)k;
+      *pacc_rows = (int)prow;
+      return true;
+    }
+  }
+  return false;
+}
+bool chain_plan(int n, int mm, int64_t nb, int64_t rows, int* kc, int* pacc_rows) {
+  return chain_plan(n, mm, &nb, &rows, 1, kc, pacc_rows);
 }
 
 // Launch a chain (descriptors in device memory, or `one` when descs is null), or with
@@ -1215,14 +1242,12 @@ int chain_prepare(const bqm_gemv* descs, int n, void* ws, hipStream_t s) {
   if (fmt != BQM_Q4_0 && fmt != BQM_Q8_0) return BQM_E_UNSUPPORTED;
   const int CB = fmt == BQM_Q4_0 ? 16 : 32;
   // checks of the descriptors alone first (no HIP call before they pass)
-  int64_t max_nb = 0;
   for (int i = 0; i < n; i++) {
     const bqm_gemv& d = descs[i];
     if (d.fmt != fmt) return BQM_E_UNSUPPORTED;
     if (d.M != M || M < 1 || M > kChainMaxM) return BQM_E_SHAPE;
     if (d.N < 1 || d.N > ((int64_t)1 << 30) || d.K < kQK || d.K % kQK != 0 || d.K > chain_max_k())
       return BQM_E_SHAPE;
-    max_nb = d.K / kQK > max_nb ? d.K / kQK : max_nb;
   }
   for (int i = 0; i < n; i++) {
     const bqm_gemv& d = descs[i];
@@ -1245,18 +1270,19 @@ int chain_prepare(const bqm_gemv* descs, int n, void* ws, hipStream_t s) {
   // ceil(share / nb) for a share of ceil(blocks / workgroups) blocks) stay below 2 GiB
   const int cus = cu_count();
   if (cus > kChainMaxWorkgroups) return BQM_E_UNSUPPORTED;
-  int64_t max_rows = 0;
+  std::vector<int64_t> nbs(n), wrows(n);
   for (int i = 0; i < n; i++) {
     const bqm_gemv& d = descs[i];
     const int64_t nb = d.K / kQK, share = (seg[2 * i + 1] + cus - 1) / cus;
-    int64_t rows = (share + nb - 1) / nb;
+    int64_t rows = (share + nb - 1) / nb;  // rows whose first block is in the share
     rows = rows < d.N ? rows : d.N;
     if ((rows + 1) * nb * CB >= ((int64_t)1 << 31)) return BQM_E_SHAPE;
-    max_rows = rows > max_rows ? rows : max_rows;
+    nbs[i] = nb;
+    wrows[i] = rows;
   }
   const int mm = m_class(M);
   int kc = 0, pacc_rows = 0;
-  if (!chain_plan(n, mm, max_nb, max_rows, &kc, &pacc_rows)) return BQM_E_SHAPE;
+  if (!chain_plan(n, mm, nbs.data(), wrows.data(), n, &kc, &pacc_rows)) return BQM_E_SHAPE;
   uint32_t head[8] = {0, 0, 0, (uint32_t)n, (uint32_t)fmt, (uint32_t)kc, (uint32_t)pacc_rows, (uint32_t)mm};
   char* wsb = static_cast<char*>(ws);
   if (hipMemsetAsync(ws, 0, kChainSyncBytes, s) != hipSuccess ||

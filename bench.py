@@ -32,8 +32,47 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 INT8_PEAK_TOPS = 5000.0         # MI355X dense int8 MFMA, published (POP/s = 5.0e15)
-VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12   # non-packed fp32 lane operations, T/s
-VALU_FP32_PEAK = 157.3         # MI355X fp32 vector TFLOP/s, published (with packed fp32)
+# Vector ALU rates of MI355X.  The published fp32 vector peak, 157.3 TFLOP/s = 256 CUs x
+# 2.4 GHz x 128 FMA lanes per cycle x 2 flops, is the rate of plain fp32 FMAs: 78.65 T lane-ops
+# per second.  Other vector operations (conversions, bit operations, packed binary16,
+# mixed-precision FMAs) issue at 256 x 64 lanes x 2.4 GHz = 39.3 T lane-ops/s.  (Measured on
+# the box with register-only loops: v_fmac_f32 / v_fma_f32 1.33-1.41 wave instructions per CU
+# and cycle at 2.4 GHz, v_cvt_f32_i32 (SDWA), v_cvt_f32_ubyte, v_and_or_b32, v_pk_add_f16 and
+# v_fma_mix_f32 0.81-0.90.)  An ALU roofline prices a kernel's algorithmic FMAs and other
+# operations each at its rate; its 'achieved' figure is in FMA-equivalent lane-ops per second
+# (an other operation counts as two) against the FMA peak.
+FMA_PEAK_TOPS = 157.3 / 2
+VALU_OTHER_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
+
+
+def alu_roofline(fma_ops, other_ops, seconds, kernel, launch_us, **extra):
+    eq = (fma_ops + 2.0 * other_ops) / seconds / 1e12
+    return {"bound": "alu", "achieved": round(eq, 3), "peak": round(FMA_PEAK_TOPS, 3),
+            "unit": "T FMA-equivalent lane-op/s", "frac": round(eq / FMA_PEAK_TOPS, 4), "traffic": None,
+            "kernel": kernel, "avg_launch_us": launch_us, **extra}
+
+
+def alu_seconds(fma_ops, other_ops):
+    return fma_ops / (FMA_PEAK_TOPS * 1e12) + other_ops / (VALU_OTHER_PEAK_TOPS * 1e12)
+
+
+def binding_roofline(hbm_bytes, fma_ops, other_ops, seconds, kernel, launch_us, traffic):
+    """The roofline that binds: HBM (algorithmic bytes at 8 TB/s) or the vector ALU (the
+    algorithmic FMAs and conversions at their rates), whichever takes longer; both fractions
+    (ideal time / measured time) beside it."""
+    t_h = hbm_bytes / (HBM_PEAK_GBS * 1e9)
+    t_a = alu_seconds(fma_ops, other_ops)
+    gbs = hbm_bytes / seconds / 1e9
+    if t_a > t_h:
+        r = alu_roofline(fma_ops, other_ops, seconds, kernel, launch_us, hbm_gbs=round(gbs, 1))
+        r["traffic"] = traffic
+    else:
+        r = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel,
+             "avg_launch_us": launch_us}
+    r["hbm_frac"] = round(t_h / seconds, 4)
+    r["alu_frac"] = round(t_a / seconds, 4)
+    return r
 
 
 def parse():
@@ -397,19 +436,19 @@ def run_dense(args, torch, gen, bqm, fmt="q4_0"):
                      "traffic": traffic, "kernel": kernel, "avg_launch_us": launch_us},
     }
     # The vector-ALU ceiling: each weight takes at least M fp32 multiply-adds (one per input
-    # row; packed fp32 is not used) and one code conversion.  Where that ceiling is below
-    # the HBM one (Q8_0 at M = 8), it is the binding roofline and is reported as such.
+    # row) and one code conversion.  Where that ceiling is below the HBM one it is the
+    # binding roofline and is reported as such.
     nweights = sum(N * K for _, N, K in mats)
-    lane_ops = nweights * (M + 1)
-    alu_ceiling_gbs = VALU_PEAK_TOPS * 1e12 / (M + 1) * (wbytes / nweights) / 1e9
+    t_alu = alu_seconds(M * nweights, nweights)
+    alu_ceiling_gbs = total / t_alu / 1e9
     res["alu_ceiling_gbs"] = round(alu_ceiling_gbs, 1)
     res["hbm_frac"] = round(achieved / HBM_PEAK_GBS, 4)
+    launch_s = float(dur.mean() if use_chain else dur.sum()) * 1e-3
+    res["alu_frac"] = round(t_alu / launch_s, 4)
     if alu_ceiling_gbs < HBM_PEAK_GBS:
-        valu_t = lane_ops / (float(dur.mean() if use_chain else dur.sum()) * 1e-3) / 1e12
-        res["roofline"] = {"bound": "alu", "achieved": round(valu_t, 3), "peak": round(VALU_PEAK_TOPS, 4),
-                           "unit": "T lane-op/s", "frac": round(valu_t / VALU_PEAK_TOPS, 4),
-                           "traffic": traffic, "kernel": kernel, "avg_launch_us": launch_us,
-                           "hbm_gbs": round(achieved, 1)}
+        res["roofline"] = alu_roofline(M * nweights, nweights, launch_s, kernel, launch_us,
+                                       hbm_gbs=round(achieved, 1))
+        res["roofline"]["traffic"] = traffic
     if fmt == "q8_0":
         res["equiv_tok_s_aggregate"] = round(M * 1e3 / ms, 2)
     if not args.no_cpu:
@@ -528,7 +567,11 @@ def run_moe(args, torch, gen, bqm):
             lbytes += [uniq * mat + 4 * (T * H + T * top_k * F)] * 2       # gate, up
             lbytes += [uniq * mat + 4 * (T * top_k * F + T * top_k * H)]   # down
         dur = per_launch_ms(launches, torch)
-        achieved = sum(lbytes) / (dur.sum() * 1e-3) / 1e9
+        # algorithmic vector work: one FMA per (slot, weight), one code conversion per
+        # (selected expert, weight); every expert matrix here has F x H weights
+        W = F * H
+        n_u = sum(L[-1] for L in layers)
+        fma_id, cvt_id = 3.0 * n_layers * T * top_k * W, 3.0 * n_u * W
 
         # the same layer with gate and up fused (one pass over both, silu(gate) * up out):
         # two launches per layer
@@ -546,7 +589,6 @@ def run_moe(args, torch, gen, bqm):
                            bqm.qmv_id_gate_up("q4_0", g, u, E, F, H, i, T, top_k, x, H, 0, y))
             fbytes.append(2 * uniq * weight_bytes("q4_0", F, H) + 4 * (T * H + T * top_k * F))
         fdur = per_launch_ms(flaunch, torch)
-        f_achieved = sum(fbytes) / (fdur.sum() * 1e-3) / 1e9
 
         # the whole layer fused: gate+up in one pass, then down with the router-weighted
         # sum over each token's experts (its output per token) in one launch
@@ -566,35 +608,31 @@ def run_moe(args, torch, gen, bqm):
             # expert rows, inputs, the weighted slot rows written and read back, the sums
             sbytes.append(uniq * weight_bytes("q4_0", H, F) + 4 * (T * top_k * F + 2 * T * top_k * H + T * H))
         sdur = per_launch_ms(slaunch, torch)
-        s_achieved = sum(sbytes) / (sdur.sum() * 1e-3) / 1e9
         out.append({"T": T, "ms_per_layer": round(ms / n_layers, 4),
                     "unique_experts_per_layer": [L[-1] for L in layers],
                     "gbs_unique_bytes": round(gbs, 1), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
                     "layer_tok_s": round(T * n_layers / (ms * 1e-3), 1),
-                    "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                                 "traffic": traffic_from_profiles(f"qmv_id_q4_0_moe_t{T}"),
-                                 "kernel": f"k_qmv_chain indexed form (Q4_0, batch class {1 if T == 1 else 2 if T == 2 else 4})",
-                                 "avg_launch_us": round(1e3 * float(dur.mean()), 3)},
+                    "roofline": binding_roofline(
+                        sum(lbytes), fma_id, cvt_id, float(dur.sum()) * 1e-3,
+                        f"k_qmv_chain indexed form (Q4_0, batch class {1 if T == 1 else 2 if T == 2 else 4})",
+                        round(1e3 * float(dur.mean()), 3), traffic_from_profiles(f"qmv_id_q4_0_moe_t{T}")),
                     "fused_gate_up": {
                         "ms_per_layer": round(ms_f / n_layers, 4), "gbs_unique_bytes": round(gbs_f, 1),
                         "pct_of_hbm_peak": round(100 * gbs_f / HBM_PEAK_GBS, 2),
                         "layer_tok_s": round(T * n_layers / (ms_f * 1e-3), 1),
-                        "roofline": {"bound": "hbm", "achieved": round(f_achieved, 1), "peak": HBM_PEAK_GBS,
-                                     "unit": "GB/s", "frac": round(f_achieved / HBM_PEAK_GBS, 4),
-                                     "traffic": traffic_from_profiles(f"qmv_id_gate_up_q4_0_moe_t{T}"),
-                                     "kernel": "k_qmv_chain gate+up form (qmv_id_gate_up)",
-                                     "avg_launch_us": round(1e3 * float(fdur.mean()), 3)}},
+                        "roofline": binding_roofline(
+                            sum(fbytes), 2.0 * n_layers * T * top_k * W, 2.0 * n_u * W, float(fdur.sum()) * 1e-3,
+                            "k_qmv_chain gate+up form (qmv_id_gate_up)", round(1e3 * float(fdur.mean()), 3),
+                            traffic_from_profiles(f"qmv_id_gate_up_q4_0_moe_t{T}"))},
                     "fused_layer": {
                         "what": "qmv_id_gate_up, then qmv_id_sum (down + router-weighted slot sum)",
                         "ms_per_layer": round(ms_l / n_layers, 4), "gbs_unique_bytes": round(gbs_l, 1),
                         "pct_of_hbm_peak": round(100 * gbs_l / HBM_PEAK_GBS, 2),
                         "layer_tok_s": round(T * n_layers / (ms_l * 1e-3), 1),
-                        "roofline": {"bound": "hbm", "achieved": round(s_achieved, 1), "peak": HBM_PEAK_GBS,
-                                     "unit": "GB/s", "frac": round(s_achieved / HBM_PEAK_GBS, 4),
-                                     "traffic": traffic_from_profiles(f"qmv_id_sum_q4_0_moe_t{T}"),
-                                     "kernel": "qmv_id_sum: k_qmv_chain indexed form (weighted rows) + k_slot_sum",
-                                     "avg_launch_us": round(1e3 * float(sdur.mean()), 3)}}})
+                        "roofline": binding_roofline(
+                            sum(sbytes), 1.0 * n_layers * T * top_k * W, 1.0 * n_u * W, float(sdur.sum()) * 1e-3,
+                            "qmv_id_sum: k_qmv_chain indexed form (weighted rows) + k_slot_sum",
+                            round(1e3 * float(sdur.mean()), 3), traffic_from_profiles(f"qmv_id_sum_q4_0_moe_t{T}"))}})
         del layers, rws, youts
         torch.cuda.empty_cache()
         if not args.no_cpu:
@@ -638,18 +676,16 @@ def run_prefill(args, torch, gen, bqm, fmt="q8_0"):
     # The binding unit is the vector ALU: every (m, n, block) needs its int32 block sum
     # converted and multiply-added with the scale product (which comes from the matrix
     # cores): 2 lane operations, against 256 CUs x 64 lanes x 2.4 GHz = 39.3 T per second.
-    valu_ops = 2.0 * M * N * (K // 32)
-    valu_t = valu_ops / (dur.mean() * 1e-3) / 1e12
+    triples = float(M) * N * (K // 32)   # (m, n, block): one conversion and one FMA each
     return {"metric": f"prefill qmm_{fmt} int8 TOP/s", "value": round(tops, 2), "unit": "TOP/s",
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8/f32",
             "data": "synthetic",
             "config": {"workload": f"prefill GEMM M=512 K=5120 N=17408, {fmt.upper()} weights, 8 weight copies"},
-            "roofline": {"bound": "alu", "achieved": round(valu_t, 3), "peak": VALU_PEAK_TOPS,
-                         "unit": "T lane-op/s", "frac": round(valu_t / VALU_PEAK_TOPS, 4),
-                         "traffic": traffic_from_profiles(f"qmm_{fmt}_prefill"),
-                         "kernel": f"k_qmm_{fmt}", "avg_launch_us": round(1e3 * float(dur.mean()), 3),
-                         "mfma_int8_frac": round(tops / INT8_PEAK_TOPS, 4)},
+            "roofline": {**alu_roofline(triples, triples, float(dur.mean()) * 1e-3, f"k_qmm_{fmt}",
+                                        round(1e3 * float(dur.mean()), 3),
+                                        mfma_int8_frac=round(tops / INT8_PEAK_TOPS, 4)),
+                         "traffic": traffic_from_profiles(f"qmm_{fmt}_prefill")},
             "quantize_us": round(1e3 * float(qdur.mean()), 3),
             **({} if args.no_cpu else {"cpu_baseline": cpu_baseline_qmm(
                 fmt, M, N, K, ("prefill", 0), ("prefill-x", 0), args.cpu_seconds, gen)})}
@@ -698,8 +734,7 @@ def run_prefill_moe(args, torch, gen, bqm):
     slots = T * top_k
     ops = n_layers * 3 * 2.0 * slots * F * H           # useful int8 operations, all launches
     tops = ops / (dur.sum() * 1e-3) / 1e12
-    valu = n_layers * 3 * 2.0 * slots * F * (H // 32)  # 2 lane-ops per (slot, n, block): same count
-    valu_t = valu / (dur.sum() * 1e-3) / 1e12
+    triples = n_layers * 3.0 * slots * F * (H // 32)  # (slot, n, block): one conversion, one FMA
     tiles = [int(np.sum((L[-1] + 63) // 64)) for L in layers]   # 64-row tiles of the kernel
     return {"metric": "MoE prefill qmm_id int8 TOP/s", "value": round(tops, 2), "unit": "TOP/s",
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
@@ -710,11 +745,10 @@ def run_prefill_moe(args, torch, gen, bqm):
             "ms_per_layer": round(ms / n_layers, 4),
             "busiest_expert_slots": [int(L[-1].max()) for L in layers],
             "row_tile_fill": round(slots / (64.0 * float(np.mean(tiles))), 3),
-            "roofline": {"bound": "alu", "achieved": round(valu_t, 3), "peak": VALU_PEAK_TOPS,
-                         "unit": "T lane-op/s", "frac": round(valu_t / VALU_PEAK_TOPS, 4),
-                         "traffic": traffic_from_profiles("qmm_id_q4_0_moe_prefill"),
-                         "kernel": "k_qmm_id_q4_0", "avg_launch_us": round(1e3 * float(dur.mean()), 3),
-                         "mfma_int8_frac": round(tops / INT8_PEAK_TOPS, 4)},
+            "roofline": {**alu_roofline(triples, triples, float(dur.sum()) * 1e-3, "k_qmm_id_q4_0",
+                                        round(1e3 * float(dur.mean()), 3),
+                                        mfma_int8_frac=round(tops / INT8_PEAK_TOPS, 4)),
+                         "traffic": traffic_from_profiles("qmm_id_q4_0_moe_prefill")},
             **({} if args.no_cpu else {"cpu_baseline": cpu_baseline_qmm_id(
                 E, top_k, H, F, T, args.cpu_seconds, gen)})}
 

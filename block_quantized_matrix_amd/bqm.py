@@ -14,7 +14,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libbqm.so")
+# BQM_LIB names another build of the same library (a host-sanitizer build, in the tests)
+LIB_PATH = os.environ.get("BQM_LIB") or os.path.join(_HERE, "libbqm.so")
 
 Q4_0 = 2
 Q8_0 = 8

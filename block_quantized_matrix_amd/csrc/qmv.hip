@@ -27,6 +27,7 @@
 // stores the row.  No atomics; the summation order is fixed for a given launch shape.
 #include "bqm_internal.h"
 
+#include <atomic>
 #include <mutex>
 #include <unordered_map>
 #include <vector>
@@ -1120,17 +1121,19 @@ ChainKernel chain_kernel(int fmt, int mm, int mode) {
   return mode == 2 ? chain_kernel_m<2>(fmt, mm) : mode == 1 ? chain_kernel_m<1>(fmt, mm) : chain_kernel_m<0>(fmt, mm);
 }
 
+// Compute units of the current device, queried once per device (threads racing on the first
+// call store the same value).
 int cu_count() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 }  // namespace
@@ -1197,13 +1200,16 @@ int launch_chain(int fmt, int mm, const GemvDesc* descs, const int64_t* seg, con
   if (ix) a.ix = *ix; else a.ix = IdxArgs{nullptr, nullptr, nullptr, nullptr, 0, 0, 0, 0, 0, nullptr};
   const int mode = ix ? (ix->up ? 2 : 1) : 0;
   ChainKernel k = chain_kernel(fmt, mm, mode);
-  // per kernel: 1 = its static LDS fits the reserve, -1 = it does not
-  static int static_ok[3][2][4] = {};
-  int& ok = static_ok[mode][fmt == BQM_Q4_0 ? 0 : 1][mm == 1 ? 0 : mm == 2 ? 1 : mm == 4 ? 2 : 3];
+  // per kernel: 1 = its static LDS fits the reserve, -1 = it does not (checked once; threads
+  // racing on the first call store the same answer)
+  static std::atomic<int> static_ok[3][2][4];
+  std::atomic<int>& okc = static_ok[mode][fmt == BQM_Q4_0 ? 0 : 1][mm == 1 ? 0 : mm == 2 ? 1 : mm == 4 ? 2 : 3];
+  int ok = okc.load(std::memory_order_relaxed);
   if (ok == 0) {
     hipFuncAttributes fa;
     ok = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(k)) == hipSuccess &&
                  fa.sharedSizeBytes <= (size_t)kP1StaticLds ? 1 : -1;
+    okc.store(ok, std::memory_order_relaxed);
   }
   if (ok < 0) return BQM_E_LAUNCH;
   allow_lds(k, kP1MaxLds);

@@ -35,6 +35,10 @@
  *   - Pointers passed to the products must be 16-byte aligned (torch allocations are).
  *   - Outputs must not alias inputs.  Results are deterministic: no atomic updates of
  *     data, a fixed summation order, the same bits on every run with the same launch.
+ *   - Host-side state, all safe to use from several threads: per device, the compute-unit
+ *     count and the device address of qmv_id_sum_noalloc's array (cached once); per kernel,
+ *     whether its static local memory fits (checked once); per workspace prepared by
+ *     bqm_chain_prepare, whether the chain has a waiting GEMV (under a mutex).
  *   - Floating-point outputs are fp32 and satisfy, per output,
  *         |y - y_exact| <= 1e-3 * sum_i |w_i * x_i|
  *     (y_exact in exact arithmetic); integer and byte outputs are exact.
@@ -165,7 +169,11 @@ int qmv_id_sum_noalloc(int fmt, const void* w_packed, int E, int64_t N, int64_t 
 /* ---- chains of GEMVs in one launch ----------------------------------------------------
  * Decode runs one GEMV after another, each reading the previous one's output (through
  * the layers' other operations); launching them one by one pays a kernel start and drain
- * per GEMV.  A chain runs a list of GEMVs in order in ONE launch: a GEMV marked `wait`
+ * per GEMV.  The pages remove that per-launch cost by capturing decode in graphs and fusing
+ * operators (page "v100llm：专为NVIDIA V100 GPU打造的高性能大模型推理引擎" (zingnex.cn),
+ * section 4) and by merging the many small decode operators ("llama.cpp-v100" README
+ * (shadowgraph.io), kernels-and-runtime list); here the GEMVs of a decode step share one
+ * persistent launch.  A chain runs a list of GEMVs in order in ONE launch: a GEMV marked `wait`
  * starts only after every earlier GEMV of the chain has finished and its outputs are
  * visible device-wide (so its x may be an earlier GEMV's y); the weights of the next GEMV
  * are already streaming while the previous one finishes.  Every GEMV of a chain has the
@@ -210,10 +218,13 @@ int qmv_chain(int fmt, int M, void* workspace, int n, hipStream_t stream);
  * wait timed out (results invalid; prepare again), 2 = fmt/M/n mismatch, -1 = copy failed. */
 int bqm_chain_status(const void* workspace, hipStream_t stream);
 
-/* Activation quantizer for the prefill product, per row m and 32-wide block b, in IEEE
- * single precision:  a = max_j |x_j|;  dx = a / 127 (correctly rounded);  dx == 0 gives
- * all-zero codes and dx = +0; otherwise Xq_j = round_half_away_from_zero(x_j / dx) clamped
- * to [-127, 127].  X: fp32 [M][K];  Xq: int8 [M][K];  dx: fp32 [M][K/32].  Bit exact. */
+/* Activation quantizer for the prefill product.  The prefill kernels the pages describe
+ * work on Q8_0-format blocks ("llama.cpp-v100" README (shadowgraph.io): its SM70 kernels
+ * adapted to Q8_0, computing-kernels item); the activations are read as taking the same
+ * 32-wide int8 block shape with an fp32 scale, per row m and block b, in IEEE single
+ * precision:  a = max_j |x_j|;  dx = a / 127 (correctly rounded);  dx == 0 gives all-zero
+ * codes and dx = +0; otherwise Xq_j = round_half_away_from_zero(x_j / dx) clamped to
+ * [-127, 127].  X: fp32 [M][K];  Xq: int8 [M][K];  dx: fp32 [M][K/32].  Bit exact. */
 int bqm_quantize_q8_act(const float* X, int8_t* Xq, float* dx, int64_t M, int64_t K,
                         hipStream_t stream);
 

@@ -5,16 +5,14 @@
 // around streaming the packed codes from HBM once, at full 16-byte load width, and doing as
 // little VALU work per weight as the format allows.
 //
-// Work mapping.  A row of the matrix is handled by a lane group of G lanes (G = 16, 32 or
-// 64, picked so that K/32 divides evenly where possible); lane g of the group owns blocks
-// g, g+G, g+2G, ... of the row, one whole 32-weight block per 16-byte (Q4_0) or 2x16-byte
-// (Q8_0) load.  A group handles R rows at once, so the activations a lane holds for one
-// block are reused R times.  A 256-thread workgroup therefore covers (256/G)*R rows.
+// Work mapping.  A row of the matrix is handled by a group of 16 lanes; lane g of the group
+// owns blocks g, g+16, g+32, ... of the row, one whole 32-weight block per 16-byte (Q4_0) or
+// 2x16-byte (Q8_0) load.  A lane holds R rows at once (two for most batch sizes), so the
+// inputs it reads from LDS for one block serve R rows.
 //
-// Activations.  X is staged once per workgroup into LDS, 128 bytes (one block) per lane
-// read; the eight 16-byte chunks of block b are stored XOR-swizzled by (b & 7) so that
-// eight neighbouring lanes (eight consecutive blocks) hit eight different bank groups.
-// Long rows are staged in chunks of blocks that fit the LDS budget.
+// Activations.  The M inputs are staged once per workgroup into LDS, one block per 144
+// bytes (128 bytes of x and 16 unused, a stride at which eight neighbouring blocks start in
+// eight different bank groups); rows too long for the LDS budget are staged in chunks.
 //
 // Arithmetic.  Every code becomes its signed value exactly before it meets x (a Q4_0 nibble
 // as 16 (n - 8) in a byte, a Q8_0 code as is, each through a sign-extending byte
@@ -23,8 +21,9 @@
 // share of the tolerance scale, and neutral codes give exactly zero.  The signed codes of a
 // block are formed once and shared by the M inputs.
 //
-// Reduction: a butterfly of cross-lane shuffles inside the lane group, then one lane
-// stores the row.  No atomics; the summation order is fixed for a given launch shape.
+// Reduction: DPP exchanges inside the 16-lane group, then one lane stores the row; a tile
+// split between waves is finished through LDS in wave order.  No atomics on data; the
+// summation order is fixed for a given launch shape.
 #include "bqm_internal.h"
 
 #include <atomic>

@@ -571,7 +571,12 @@ def run_moe(args, torch, gen, bqm):
         # (selected expert, weight); every expert matrix here has F x H weights
         W = F * H
         n_u = sum(L[-1] for L in layers)
-        fma_id, cvt_id = 3.0 * n_layers * T * top_k * W, 3.0 * n_u * W
+        # from 8 tokens on the indexed products run on the matrix cores (the slot products
+        # leave the vector ALU, which keeps one code conversion per weight)
+        mma = T >= 8
+        fma_id, cvt_id = (0.0 if mma else 3.0 * n_layers * T * top_k * W), 3.0 * n_u * W
+        id_kernel = ("k_qmv_id_mma (matrix-core indexed form, Q4_0, groups of up to 16 slots)" if mma else
+                     f"k_qmv_chain indexed form (Q4_0, batch class {1 if T == 1 else 2 if T == 2 else 4})")
 
         # the same layer with gate and up fused (one pass over both, silu(gate) * up out):
         # two launches per layer
@@ -614,15 +619,16 @@ def run_moe(args, torch, gen, bqm):
                     "layer_tok_s": round(T * n_layers / (ms * 1e-3), 1),
                     "roofline": binding_roofline(
                         sum(lbytes), fma_id, cvt_id, float(dur.sum()) * 1e-3,
-                        f"k_qmv_chain indexed form (Q4_0, batch class {1 if T == 1 else 2 if T == 2 else 4})",
-                        round(1e3 * float(dur.mean()), 3), traffic_from_profiles(f"qmv_id_q4_0_moe_t{T}")),
+                        id_kernel, round(1e3 * float(dur.mean()), 3), traffic_from_profiles(f"qmv_id_q4_0_moe_t{T}")),
                     "fused_gate_up": {
                         "ms_per_layer": round(ms_f / n_layers, 4), "gbs_unique_bytes": round(gbs_f, 1),
                         "pct_of_hbm_peak": round(100 * gbs_f / HBM_PEAK_GBS, 2),
                         "layer_tok_s": round(T * n_layers / (ms_f * 1e-3), 1),
                         "roofline": binding_roofline(
-                            sum(fbytes), 2.0 * n_layers * T * top_k * W, 2.0 * n_u * W, float(fdur.sum()) * 1e-3,
-                            "k_qmv_chain gate+up form (qmv_id_gate_up)", round(1e3 * float(fdur.mean()), 3),
+                            sum(fbytes), (0.0 if mma else 2.0 * n_layers * T * top_k * W), 2.0 * n_u * W,
+                            float(fdur.sum()) * 1e-3,
+                            ("k_qmv_id_mma gate+up form (qmv_id_gate_up)" if mma else
+                             "k_qmv_chain gate+up form (qmv_id_gate_up)"), round(1e3 * float(fdur.mean()), 3),
                             traffic_from_profiles(f"qmv_id_gate_up_q4_0_moe_t{T}"))},
                     "fused_layer": {
                         "what": "qmv_id_gate_up, then qmv_id_sum (down + router-weighted slot sum)",
@@ -630,8 +636,10 @@ def run_moe(args, torch, gen, bqm):
                         "pct_of_hbm_peak": round(100 * gbs_l / HBM_PEAK_GBS, 2),
                         "layer_tok_s": round(T * n_layers / (ms_l * 1e-3), 1),
                         "roofline": binding_roofline(
-                            sum(sbytes), 1.0 * n_layers * T * top_k * W, 1.0 * n_u * W, float(sdur.sum()) * 1e-3,
-                            "qmv_id_sum: k_qmv_chain indexed form (weighted rows) + k_slot_sum",
+                            sum(sbytes), (0.0 if mma else 1.0 * n_layers * T * top_k * W), 1.0 * n_u * W,
+                            float(sdur.sum()) * 1e-3,
+                            ("qmv_id_sum: k_qmv_id_mma (weighted rows) + k_slot_sum" if mma else
+                             "qmv_id_sum: k_qmv_chain indexed form (weighted rows) + k_slot_sum"),
                             round(1e3 * float(sdur.mean()), 3), traffic_from_profiles(f"qmv_id_sum_q4_0_moe_t{T}"))}})
         del layers, rws, youts
         torch.cuda.empty_cache()

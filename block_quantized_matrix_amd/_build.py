@@ -23,7 +23,7 @@ FLAGS = [
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-function",
 ]
-SOURCES = ["api.hip", "repack.hip", "qmv.hip", "qmm.hip"]
+SOURCES = ["api.hip", "repack.hip", "qmv.hip", "qmv_mma.hip", "qmm.hip"]
 
 
 def hipcc() -> str:

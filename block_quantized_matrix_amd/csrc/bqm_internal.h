@@ -72,6 +72,10 @@ int launch_qmm_id(int fmt, const void* w, int E, int64_t N, int64_t K, const int
                   int top_k, const int8_t* Xq, const float* dx, int64_t x_tok_rows,
                   int64_t x_slot_rows, float* Y, hipStream_t s);
 int launch_fill(float* y, int64_t n, float v, hipStream_t s);
+int cu_count();
+int launch_id_mma(int fmt, const void* w, const void* w_up, int E, int64_t N, int64_t K,
+                  const int32_t* ids, int T, int top_k, const float* X, int64_t xts, int64_t xss,
+                  float* Y, hipStream_t s, const float* rw);
 int64_t chain_max_k();
 size_t chain_workspace_bytes(int n);
 int chain_prepare(const bqm_gemv* descs, int n, void* ws, hipStream_t s);

@@ -1120,6 +1120,8 @@ ChainKernel chain_kernel(int fmt, int mm, int mode) {
   return mode == 2 ? chain_kernel_m<2>(fmt, mm) : mode == 1 ? chain_kernel_m<1>(fmt, mm) : chain_kernel_m<0>(fmt, mm);
 }
 
+}  // namespace
+
 // Compute units of the current device, queried once per device (threads racing on the first
 // call store the same value).
 int cu_count() {
@@ -1134,8 +1136,6 @@ int cu_count() {
   }
   return n;
 }
-
-}  // namespace
 
 int launch_fill(float* y, int64_t n, float v, hipStream_t s) {
   if (n <= 0) return BQM_OK;
@@ -1343,6 +1343,16 @@ int launch_qmv(int fmt, const void* w, const float* X, float* Y, int M, int64_t 
   return launch_chain(fmt, mm, nullptr, nullptr, &d, 1, kc, pacc_rows, nullptr, false, s);
 }
 
+// Tokens from which the indexed forms run on the matrix cores.  Measured on the 128-expert
+// MoE layer (Q4_0, top-8, skewed routing), per call, matrix cores against the vector form:
+// T = 2 38.6 / 23.9 us, T = 4 42.6 / 37.4, T = 8 51.5 / 51.2 (gate+up 77.8 / 81.9),
+// T = 16 65.8 / 80.0 (gate+up 103 / 137): the matrix-core form has a fixed cost (16 input
+// slots staged, most of them empty at small T) and wins once experts get several groups
+// of 4 slots.
+#ifndef BQM_MMA_MIN_T
+#define BQM_MMA_MIN_T 8
+#endif
+
 // Expert-indexed GEMV: the chain kernel's indexed form, with E * N rows as one matrix.  The
 // batch class is that of min(T, 4): one token usually adds at most one slot to an expert,
 // so up to 4 tokens stream each selected expert once; an expert with more slots is
@@ -1351,6 +1361,12 @@ int launch_qmv(int fmt, const void* w, const float* X, float* Y, int M, int64_t 
 static int launch_id(int fmt, const void* w, const void* w_up, int E, int64_t N, int64_t K,
               const int32_t* ids, int T, int top_k, const float* X, int64_t xts, int64_t xss,
               float* Y, hipStream_t s, const float* rw = nullptr) {
+  // From BQM_MMA_MIN_T tokens on, the matrix-core form: each expert's rows stream once for
+  // up to 16 of its slots and the vector work per weight does not grow with the slots
+  if (T >= BQM_MMA_MIN_T) {
+    const int st = launch_id_mma(fmt, w, w_up, E, N, K, ids, T, top_k, X, xts, xss, Y, s, rw);
+    if (st != BQM_E_UNSUPPORTED) return st;
+  }
   const int TS = T * top_k;
   Layout L;
   layout_of(fmt, (int64_t)E * N, K, &L);

@@ -1,0 +1,562 @@
+// Expert-indexed GEMV on the matrix cores, gfx950.
+//
+// The slots routed to one expert (mul_mat_id, on the page "ik_llama.cpp 老工作站多 GPU 部署
+// Qwen3-235B-A22B 实战指南" (nxmr.cn), background section) all multiply the same expert rows:
+// for a group of up to 16 of them, Y[s][n] = sum_k W[e][n][k] x_s[k] is a 16-column matrix
+// product.  Here each 32-weight block of 16 rows goes through v_mfma_f32_16x16x32_bf16 once
+// for all the group's slots, instead of one fp32 FMA per weight and slot on the vector ALU:
+// the expert's rows stream from HBM once per group of 16 (with T <= 16 tokens, once), and
+// the vector work per weight (code conversion and the block-scale FMA) does not grow with
+// the number of slots.
+//
+// Operands.  MFMA rows i = slots of the group, columns j = 16 expert rows, k = the 32
+// positions of one block (so the block's scale applies to the whole product).  Lane l holds
+// A[i = l % 16][k-group l / 16] and B[k-group][j = l % 16]: 8 values each.  A lane's eight
+// positions are those of one 4-byte word of Q4_0 codes (the low nibbles are positions
+// 4q..4q+3, the high ones 16+4q..16+4q+3) or of 8 bytes of Q8_0 codes (8q..8q+7); the inputs
+// are staged in LDS in the same order.  D[i][j] comes back as 4 values per lane: slots
+// 4 (l / 16) + r, row l % 16.
+//
+// Exactness.  Codes enter as bf16 signed values, exact (Q4_0 as 16 (n - 8), Q8_0 the int8
+// code).  Each fp32 input x, scaled by 2^30 (exact; undone in the block scale), is split
+// into two bf16 parts: x_hi, truncated to 8 significant bits, and x_lo, the remainder
+// (exact in fp32) truncated likewise; the part left out is below 2^-14 |x| for every fp32 x
+// below 2^86 in magnitude (larger inputs can overflow the partial sums).  Products of bf16 values are exact in fp32, so a block sum carries
+// the MFMA's fp32 accumulation error plus at most 2^-14 sum_j |c_j x_j|; then acc += d * sum
+// in fp32 as in the vector kernels, blocks in ascending order.  Total error far below
+// 1e-3 sum |w x|; neutral codes give exactly zero; integer inputs and power-of-two scales
+// give exact results.
+//
+// Work.  Every workgroup (one per compute unit, 16 waves) sorts the slots by expert (a
+// stable counting sort in LDS) and cuts each expert's run into groups of up to 16.  The
+// 16-row tiles of all groups are split evenly over the workgroups.  A workgroup walks its
+// tiles in passes of one group each: it stages the group's inputs (both bf16 parts) for a
+// chunk of K in LDS, its waves compute their tiles over the chunk, and so on along K.  When
+// a pass has fewer tiles than waves, the waves also split each chunk's blocks between them
+// and the partial sums are added through LDS in a fixed order, so results are deterministic.
+#include "bqm_internal.h"
+
+#include <algorithm>
+
+namespace bqm {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+enum { MQ4 = 0, MQ8 = 1 };
+
+constexpr int kMWaves = 16, kMThreads = 64 * kMWaves;
+constexpr int kGroupSlots = 16;                     // slots per group: the MFMA's 16 rows
+constexpr int kXBlk = 2 * 64 * 16;                  // LDS bytes per staged block: 2 parts x 64 lanes x 16 B
+constexpr int kMStaticLds = 1024;
+constexpr int kMMaxLds = 160 * 1024 - kMStaticLds;  // dynamic LDS of a launch
+constexpr uint32_t kOob = 0x80000000u;              // a lane offset past every descriptor: reads 0
+constexpr int kMMaxSlots = BQM_QMV_ID_MAX_T * BQM_QMV_ID_MAX_TOPK;
+constexpr int kJobs = 4;                            // staging jobs per thread whose loads fly together
+
+struct MmaArgs {
+  const uint8_t* codes;    // the (gate) expert tensor: codes of E * N rows ...
+  const uint16_t* scales;  // ... and their scales
+  const uint8_t* codes2;   // gate+up form: the up tensor
+  const uint16_t* scales2;
+  const int32_t* ids;      // [T][top_k]
+  const float* x;
+  float* y;                // [T * top_k][N]
+  const float* rw;         // router weights [T][top_k] the rows are scaled by, or null
+  int E, N, nb, TS, top_k, kc;
+  int64_t xts, xss;        // input strides (floats) per token and per slot
+};
+
+// LDS: the slot table (per-expert counts then starts, E + 1; slots sorted by expert, TS;
+// groups of 3 ints, at most TS), then the staged inputs, whose area also takes the K-split
+// partial sums at the end of a pass.
+__host__ __device__ inline int mma_table_bytes(int E, int TS) { return ((E + 1 + 4 * TS) * 4 + 15) & ~15; }
+// Tiles per wave in a pass (their loads, two quads in flight, and sums fit 128 registers).
+__host__ __device__ constexpr int mma_tpw(bool q4, bool gu) { return q4 ? (gu ? 2 : 4) : (gu ? 1 : 2); }
+// The K-split partial sums at most: every wave but those of the first share, TPW tiles of
+// 16 x 16 floats per tensor each.
+__host__ __device__ constexpr int mma_part_bytes(bool q4, bool gu) {
+  return (kMWaves - 1) * mma_tpw(q4, gu) * (gu ? 2 : 1) * 1024;
+}
+
+__device__ __forceinline__ float h2f(uint32_t bits) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+__device__ __forceinline__ float sbyte(uint32_t v, int b) {
+  return (float)(int8_t)(v >> (8 * b));  // v_cvt_f32_i32 with a sign-extending byte select
+}
+// Two floats whose low 16 bits are zero (exact bf16 values) -> one bf16 pair, f0 low.
+__device__ __forceinline__ uint32_t bf_pair(float f0, float f1) {
+  return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f1), __builtin_bit_cast(uint32_t, f0),
+                               0x07060302u);
+}
+// One word of Q4_0 codes (bytes 4q..4q+3 of a block) -> the B operand: 16 (n - 8) of the low
+// nibbles (positions 4q..4q+3), then of the high ones (16+4q..16+4q+3).  n ^ 8 is n - 8 in
+// four-bit two's complement; placed at the top of a byte it reads as 16 (n - 8).
+__device__ __forceinline__ bf16x8 q4_operand(uint32_t w) {
+  const uint32_t lo = ((w << 4) ^ 0x80808080u) & 0xF0F0F0F0u;
+  const uint32_t hi = (w ^ 0x80808080u) & 0xF0F0F0F0u;
+  const u32x4 v{bf_pair(sbyte(lo, 0), sbyte(lo, 1)), bf_pair(sbyte(lo, 2), sbyte(lo, 3)),
+                bf_pair(sbyte(hi, 0), sbyte(hi, 1)), bf_pair(sbyte(hi, 2), sbyte(hi, 3))};
+  return __builtin_bit_cast(bf16x8, v);
+}
+// Eight Q8_0 codes (bytes 8q..8q+7 of a block) -> the B operand.
+__device__ __forceinline__ bf16x8 q8_operand(uint32_t w0, uint32_t w1) {
+  const u32x4 v{bf_pair(sbyte(w0, 0), sbyte(w0, 1)), bf_pair(sbyte(w0, 2), sbyte(w0, 3)),
+                bf_pair(sbyte(w1, 0), sbyte(w1, 1)), bf_pair(sbyte(w1, 2), sbyte(w1, 3))};
+  return __builtin_bit_cast(bf16x8, v);
+}
+// Inputs enter scaled by 2^kXShift (exact), which lifts every fp32 subnormal into the
+// range where the two bf16 parts keep all but 2^-14 of it (a bf16 part cannot hold a value
+// below 2^-133, and the smallest fp32 subnormal is 2^-149); the block scale carries
+// 2^-kXShift back.  The price: |x| must stay below 2^86 for the partial sums (codes up to
+// 128 = 2^7 times 32 terms) to stay below fp32's limit.
+constexpr int kXShift = 30;
+// x -> (x_hi, x_lo) bits of x * 2^kXShift: truncated to bf16, and the exact remainder
+// truncated to bf16 (zero when x is not finite: x_hi carries the infinity or NaN).
+__device__ __forceinline__ void split(float x, uint32_t& hi, uint32_t& lo) {
+  const float f = x * 0x1p30f;
+  static_assert(kXShift == 30, "the literal above");
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  hi = u & 0xFFFF0000u;
+  const float r = f - __builtin_bit_cast(float, hi);
+  lo = __builtin_isfinite(f) ? __builtin_bit_cast(uint32_t, r) & 0xFFFF0000u : 0u;
+}
+
+template <int FMT, bool GU>
+__global__ __launch_bounds__(kMThreads) void k_qmv_id_mma(MmaArgs a) {
+  constexpr int CB = FMT == MQ4 ? 16 : 32;         // code bytes per block
+  constexpr int LW = FMT == MQ4 ? 1 : 2;           // 16-byte code loads per lane, tile and quad
+  constexpr int NG = GU ? 2 : 1;                   // tensors (gate+up: two)
+  constexpr int TPW = mma_tpw(FMT == MQ4, GU);
+  extern __shared__ float4 smem[];
+  char* lds = reinterpret_cast<char*>(smem);
+  __shared__ int s_ng;
+  __shared__ int s_scan[2 * kMWaves];
+  __shared__ int64_t s_xoff[kGroupSlots];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int E = a.E, TS = a.TS, N = a.N, nb = a.nb;
+  int* cnt = reinterpret_cast<int*>(lds);
+  int* srt = cnt + E + 1;
+  int* grp = srt + TS;
+  char* xl = lds + mma_table_bytes(E, TS);
+
+  // ---- slots grouped by expert: a stable counting sort (bucket E: ids out of range) ----
+  for (int e = tid; e <= E; e += kMThreads) cnt[e] = 0;
+  __syncthreads();
+  constexpr int SPT = (kMMaxSlots + kMThreads - 1) / kMThreads;
+  int key[SPT], pos[SPT];
+#pragma unroll
+  for (int k = 0; k < SPT; k++) {
+    const int i = tid + k * kMThreads;
+    key[k] = E;
+    pos[k] = 0;
+    if (i < TS) {
+      const int e = a.ids[i];
+      key[k] = e >= 0 && e < E ? e : E;
+      pos[k] = atomicAdd(&cnt[key[k]], 1);
+    }
+  }
+  __syncthreads();
+  {
+    // exclusive scans over e = 0..E of the slot counts and the group counts; thread t owns
+    // entries [t * per, (t + 1) * per)
+    const int per = (E + 1 + kMThreads - 1) / kMThreads;
+    const int e0 = min(E + 1, tid * per), e1 = min(E + 1, e0 + per);
+    int ls = 0, lg = 0;
+    for (int e = e0; e < e1; e++) {
+      const int c = cnt[e];
+      ls += c;
+      lg += e < E ? (c + kGroupSlots - 1) / kGroupSlots : 0;
+    }
+    int is = ls, ig = lg;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(is, o, 64), v = __shfl_up(ig, o, 64);
+      if (lane >= o) {
+        is += u;
+        ig += v;
+      }
+    }
+    if (lane == 63) {
+      s_scan[2 * wave] = is;
+      s_scan[2 * wave + 1] = ig;
+    }
+    __syncthreads();
+    int s0 = is - ls, g0 = ig - lg;
+    for (int w = 0; w < wave; w++) {
+      s0 += s_scan[2 * w];
+      g0 += s_scan[2 * w + 1];
+    }
+    for (int e = e0; e < e1; e++) {
+      const int c = cnt[e];
+      cnt[e] = s0;
+      if (e < E)
+        for (int j = 0; j < c; j += kGroupSlots) {
+          grp[3 * g0] = e;
+          grp[3 * g0 + 1] = s0 + j;
+          grp[3 * g0 + 2] = min(kGroupSlots, c - j);
+          g0++;
+        }
+      s0 += c;
+    }
+    if (tid == kMThreads - 1) s_ng = g0;
+  }
+  __syncthreads();
+  // each slot at the place its counting atomic returned, then at its rank by index in its run
+#pragma unroll
+  for (int k = 0; k < SPT; k++) {
+    const int i = tid + k * kMThreads;
+    if (i < TS && key[k] < E) srt[cnt[key[k]] + pos[k]] = i;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < SPT; k++) {
+    const int i = tid + k * kMThreads;
+    if (i < TS && key[k] < E) {
+      const int q0 = cnt[key[k]], q1 = cnt[key[k] + 1];
+      int r = q0;
+      for (int q = q0; q < q1; q++) r += srt[q] < i;
+      pos[k] = r;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < SPT; k++) {
+    const int i = tid + k * kMThreads;
+    if (i < TS && key[k] < E) srt[pos[k]] = i;
+  }
+  __syncthreads();
+  const int ng = s_ng;
+
+  // rows of slots that no group computes, each by one workgroup: a negative id gives zeros,
+  // an id >= E NaN; with K = 0 every valid slot's sums are empty (zeros)
+  for (int ts = blockIdx.x; ts < TS; ts += gridDim.x) {
+    const int e = a.ids[ts];
+    const bool valid = e >= 0 && e < E;
+    if (valid && nb > 0) continue;
+    const float v = valid || e < 0 ? 0.0f : __builtin_nanf("");
+    for (int n = tid; n < N; n += kMThreads) a.y[(int64_t)ts * N + n] = v;
+  }
+  if (nb == 0 || ng == 0) return;
+
+  // ---- this workgroup's tiles ----
+  const int tpg = (N + 15) >> 4;  // 16-row tiles per group
+  const int64_t tt = (int64_t)ng * tpg;
+  const int64_t t_end = tt * (blockIdx.x + 1) / gridDim.x;
+  const int j = lane & 15, q = lane >> 4;
+  for (int64_t t = tt * blockIdx.x / gridDim.x; t < t_end;) {
+    const int g = (int)(t / tpg), ta = (int)(t - (int64_t)g * tpg);
+    const int64_t left = t_end - t;
+    int nt = tpg - ta;
+    if (left < nt) nt = (int)left;
+    if (nt > kMWaves * TPW) nt = kMWaves * TPW;
+    t += nt;
+    const int e = grp[3 * g], s0 = grp[3 * g + 1], c = grp[3 * g + 2];
+    // The pass's tiles in sets of TPW, one set per wave; with fewer sets than waves the waves
+    // also split each chunk's blocks into KS shares: wave w takes set w % TSN, share w / TSN
+    // (waves past TSN * KS only help stage the inputs).  Every busy wave then holds TPW tiles'
+    // loads in flight.
+    const int TSN = (nt + TPW - 1) / TPW, KS = kMWaves / TSN;
+    const int tsi = wave % TSN, ks = wave / TSN;
+    const int mt = ks < KS ? min(TPW, nt - tsi * TPW) : 0;  // this wave's tiles
+    const int tb = ta + tsi * TPW;                          // its first tile
+    // the group's input rows (slot si: token * xts + slot * xss floats into x), read by the
+    // staging after the barrier that follows (the previous pass read them before two)
+    if (tid < c) {
+      const int ts = srt[s0 + tid];
+      const int tok = ts / a.top_k, sl = ts - tok * a.top_k;
+      s_xoff[tid] = tok * a.xts + sl * a.xss;
+    }
+    const int64_t erow = (int64_t)e * N;
+    const uint32_t ecb = (uint32_t)N * (uint32_t)nb * CB;  // one expert's code bytes (< 2^31)
+    __amdgpu_buffer_rsrc_t rc[NG], rs[NG];
+    rc[0] = __builtin_amdgcn_make_buffer_rsrc((void*)(a.codes + erow * nb * CB), (short)0, (int)ecb, 0x00020000);
+    rs[0] = __builtin_amdgcn_make_buffer_rsrc((void*)(a.scales + erow * nb), (short)0, (int)((uint32_t)N * nb * 2),
+                                              0x00020000);
+    if constexpr (GU) {
+      rc[1] = __builtin_amdgcn_make_buffer_rsrc((void*)(a.codes2 + erow * nb * CB), (short)0, (int)ecb, 0x00020000);
+      rs[1] = __builtin_amdgcn_make_buffer_rsrc((void*)(a.scales2 + erow * nb), (short)0,
+                                                (int)((uint32_t)N * nb * 2), 0x00020000);
+    }
+    // lane offsets of its row in each of its tiles: codes (its word or two of a block) and
+    // scales; rows past N and tiles the wave does not have read zeros
+    uint32_t vc[TPW], vs[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; i++) {
+      const int n = (tb + i) * 16 + j;
+      const bool ok = i < mt && n < N;
+      vc[i] = ok ? (uint32_t)n * (uint32_t)nb * CB + (uint32_t)q * 16 : kOob;
+      vs[i] = ok ? (uint32_t)n * (uint32_t)nb * 2 : kOob;
+    }
+    float acc[TPW][NG][4];
+#pragma unroll
+    for (int i = 0; i < TPW; i++)
+#pragma unroll
+      for (int h = 0; h < NG; h++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) acc[i][h][r] = 0.0f;
+
+    // One quad (4 blocks) of a wave's tiles: 16-byte code loads and the 4 scales of each tile
+    // and tensor.  A load covers 64 contiguous bytes of each of the tile's 16 rows (lane
+    // group q: Q4_0 block q of the quad; Q8_0 half q % 2 of block q / 2, twice), so every
+    // load instruction reads whole 64-byte pieces; lane exchanges then give each lane group
+    // its word (Q4_0) or 8 bytes (Q8_0) of every block.
+    struct Quad {
+      u32x4 c[TPW][NG][LW];
+      u32x2 s[TPW][NG];
+    };
+    // issue a quad's loads; `live` false: offsets past the descriptors, nothing is read
+    auto issue = [&](Quad& Qd, int kb, bool live) {
+      const uint32_t m = live ? 0u : kOob;
+#pragma unroll
+      for (int i = 0; i < TPW; i++)
+#pragma unroll
+        for (int h = 0; h < NG; h++) {
+#pragma unroll
+          for (int w = 0; w < LW; w++)
+            Qd.c[i][h][w] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc[h], (vc[i] | m) + w * 64, kb * CB, 0));
+          Qd.s[i][h] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs[h], vs[i] | m, kb * 2, 0));
+        }
+    };
+    // v_permlane32_swap: rows 2-3 (lanes 32-63) of a <-> rows 0-1 of b; v_permlane16_swap:
+    // rows 1 and 3 of a <-> rows 0 and 2 of b (a row is 16 lanes)
+    auto swap32 = [](uint32_t& x, uint32_t& y) {
+      const auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+      x = r[0];
+      y = r[1];
+    };
+    auto swap16 = [](uint32_t& x, uint32_t& y) {
+      const auto r = __builtin_amdgcn_permlane16_swap(x, y, false, false);
+      x = r[0];
+      y = r[1];
+    };
+    // Q4_0: lane group q holds words 0-3 of block q; afterwards word u of lane group q is word
+    // q of block u (a 4 x 4 transpose between the lane groups and the words).  Q8_0, each of
+    // the two loads: lane group g holds bytes 16 (g % 2) .. + 16 of block g / 2 as words 0-3;
+    // afterwards words 0-1 of lane group q are bytes 8q .. 8q + 8 of the first block, words
+    // 2-3 those of the second.
+    auto exchange = [&](u32x4& v) {
+      uint32_t r0 = v.x, r1 = v.y, r2 = v.z, r3 = v.w;
+      if constexpr (FMT == MQ4) {
+        swap32(r0, r2);
+        swap32(r1, r3);
+        swap16(r0, r1);
+        swap16(r2, r3);
+      } else {
+        swap16(r0, r2);
+        swap16(r1, r3);
+        swap32(r0, r2);
+        swap32(r1, r3);
+      }
+      v = u32x4{r0, r1, r2, r3};
+    };
+    // a quad's products: block u of the chunk-local quad `ql`
+    auto consume = [&](Quad& Qd, int ql) {
+#pragma unroll
+      for (int i = 0; i < TPW; i++)
+#pragma unroll
+        for (int h = 0; h < NG; h++)
+#pragma unroll
+          for (int w = 0; w < LW; w++) exchange(Qd.c[i][h][w]);
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const int bl = 4 * ql + u;
+        const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(xl + (bl * 128 + lane) * 16);
+        const bf16x8 alo = *reinterpret_cast<const bf16x8*>(xl + (bl * 128 + 64 + lane) * 16);
+        // every tile of the set, also those past the pass's end (whose codes and scales read
+        // as zeros): no branches, so the tiles' products and sums interleave
+        f32x4 d[TPW][NG];
+#pragma unroll
+        for (int i = 0; i < TPW; i++)
+#pragma unroll
+          for (int h = 0; h < NG; h++) {
+            const u32x4& v = Qd.c[i][h][FMT == MQ4 ? 0 : u >> 1];
+            const bf16x8 b = FMT == MQ4 ? q4_operand(v[u]) : q8_operand(v[2 * (u & 1)], v[2 * (u & 1) + 1]);
+            d[i][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            d[i][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, b, d[i][h], 0, 0, 0);
+          }
+#pragma unroll
+        for (int i = 0; i < TPW; i++)
+#pragma unroll
+          for (int h = 0; h < NG; h++) {
+            const uint32_t sw = (u & 2) ? Qd.s[i][h].y : Qd.s[i][h].x;
+            // d, times 1/16 for the Q4_0 codes' 16 (n - 8), times 2^-kXShift for the inputs
+            const float sc = h2f((u & 1) ? sw >> 16 : sw) * (FMT == MQ4 ? 0x1p-34f : 0x1p-30f);
+#pragma unroll
+            for (int r = 0; r < 4; r++) acc[i][h][r] = fmaf(sc, d[i][h][r], acc[i][h][r]);
+          }
+      }
+    };
+
+    for (int kb0 = 0; kb0 < nb; kb0 += a.kc) {
+      const int kcb = min(a.kc, nb - kb0);  // a multiple of 4, as nb and kc are
+      const int nq = kcb >> 2;
+      const int q0 = ks < KS ? nq * ks / KS : 0, q1 = ks < KS ? nq * (ks + 1) / KS : 0;
+      Quad QA, QB;
+      // the first quad's weights do not depend on the inputs: fetch them across the staging
+      issue(QA, kb0 + 4 * q0, q0 < q1);
+      __syncthreads();  // the previous chunk's inputs are no longer read
+      // stage the group's inputs for blocks kb0 .. kb0 + kcb: per (block, lane) both parts;
+      // a thread's jobs in rounds of kJobs, each round's loads in flight together
+      for (int jb0 = 0; jb0 < kcb * 64; jb0 += kJobs * kMThreads) {
+        f32x4 v[kJobs][2];
+#pragma unroll
+        for (int r = 0; r < kJobs; r++) {
+          const int jb = jb0 + r * kMThreads + tid;
+          const int bl = jb >> 6, ln = jb & 63, si = ln & 15, sq = ln >> 4;
+          v[r][0] = v[r][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (jb < kcb * 64 && si < c) {
+            const float* xr = a.x + s_xoff[si] + (int64_t)(kb0 + bl) * 32;
+            v[r][0] = *reinterpret_cast<const f32x4*>(xr + (FMT == MQ4 ? 4 * sq : 8 * sq));
+            v[r][1] = *reinterpret_cast<const f32x4*>(xr + (FMT == MQ4 ? 16 + 4 * sq : 8 * sq + 4));
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < kJobs; r++) {
+          const int jb = jb0 + r * kMThreads + tid;
+          if (jb < kcb * 64) {
+            const int bl = jb >> 6, ln = jb & 63;
+            const float f[8] = {v[r][0].x, v[r][0].y, v[r][0].z, v[r][0].w,
+                                v[r][1].x, v[r][1].y, v[r][1].z, v[r][1].w};
+            uint32_t hb[8], lb[8];
+#pragma unroll
+            for (int k = 0; k < 8; k++) split(f[k], hb[k], lb[k]);
+            *reinterpret_cast<u32x4*>(xl + (bl * 128 + ln) * 16) =
+                u32x4{(hb[1] & 0xFFFF0000u) | (hb[0] >> 16), (hb[3] & 0xFFFF0000u) | (hb[2] >> 16),
+                      (hb[5] & 0xFFFF0000u) | (hb[4] >> 16), (hb[7] & 0xFFFF0000u) | (hb[6] >> 16)};
+            *reinterpret_cast<u32x4*>(xl + (bl * 128 + 64 + ln) * 16) =
+                u32x4{(lb[1] & 0xFFFF0000u) | (lb[0] >> 16), (lb[3] & 0xFFFF0000u) | (lb[2] >> 16),
+                      (lb[5] & 0xFFFF0000u) | (lb[4] >> 16), (lb[7] & 0xFFFF0000u) | (lb[6] >> 16)};
+          }
+        }
+      }
+      __syncthreads();
+      // two quads in flight: the loads of the next are issued before the products of this one
+      for (int qd = q0; qd < q1; qd += 2) {
+        issue(QB, kb0 + 4 * (qd + 1), qd + 1 < q1);
+        consume(QA, qd);
+        issue(QA, kb0 + 4 * (qd + 2), qd + 2 < q1);
+        if (qd + 1 < q1) consume(QB, qd + 1);
+      }
+    }
+
+    // K split between waves: the shares after the first go through LDS (the staging area,
+    // free once every wave is past the last chunk) and are added to the first share's sums in
+    // share order
+    if (KS > 1) {
+      float* part = reinterpret_cast<float*>(xl);
+      __syncthreads();
+      if (ks > 0 && mt > 0) {
+#pragma unroll
+        for (int i = 0; i < TPW; i++)
+          if (i < mt)
+#pragma unroll
+            for (int h = 0; h < NG; h++)
+              *reinterpret_cast<f32x4*>(part + ((((ks - 1) * TSN + tsi) * TPW + i) * NG + h) * 256 + lane * 4) =
+                  f32x4{acc[i][h][0], acc[i][h][1], acc[i][h][2], acc[i][h][3]};
+      }
+      __syncthreads();
+      if (ks == 0 && mt > 0) {
+        for (int kk = 1; kk < KS; kk++) {
+#pragma unroll
+          for (int i = 0; i < TPW; i++)
+            if (i < mt)
+#pragma unroll
+              for (int h = 0; h < NG; h++) {
+                const f32x4 v = *reinterpret_cast<const f32x4*>(
+                    part + ((((kk - 1) * TSN + tsi) * TPW + i) * NG + h) * 256 + lane * 4);
+                acc[i][h][0] += v.x;
+                acc[i][h][1] += v.y;
+                acc[i][h][2] += v.z;
+                acc[i][h][3] += v.w;
+              }
+        }
+      }
+    }
+    // store: lane (j, q) holds row j of each tile for slots 4q .. 4q + 3 of the group
+    if (ks == 0) {
+#pragma unroll
+      for (int i = 0; i < TPW; i++) {
+        const int n = (tb + i) * 16 + j;
+        if (i < mt && n < N) {
+#pragma unroll
+          for (int r = 0; r < 4; r++) {
+            const int si = 4 * q + r;
+            if (si < c) {
+              const int ts = srt[s0 + si];
+              float v = acc[i][0][r];
+              if constexpr (GU) v = v / (1.0f + expf(-v)) * acc[i][NG - 1][r];  // silu(g) * u
+              if (a.rw) v *= a.rw[ts];
+              a.y[(int64_t)ts * N + n] = v;
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+using MmaKernel = void (*)(MmaArgs);
+MmaKernel mma_kernel(int fmt, bool gu) {
+  if (fmt == BQM_Q4_0) return gu ? k_qmv_id_mma<MQ4, true> : k_qmv_id_mma<MQ4, false>;
+  return gu ? k_qmv_id_mma<MQ8, true> : k_qmv_id_mma<MQ8, false>;
+}
+
+}  // namespace
+
+// The matrix-core form of the expert-indexed GEMV (plain, router-weighted with `rw`, or
+// gate+up with `w_up`).  Returns BQM_E_UNSUPPORTED when the shape does not suit it (K not a
+// multiple of 128, an expert of 2 GiB of codes or more, or the slot table leaving no room
+// for a chunk of inputs); the caller then uses the vector form.
+int launch_id_mma(int fmt, const void* w, const void* w_up, int E, int64_t N, int64_t K,
+                  const int32_t* ids, int T, int top_k, const float* X, int64_t xts, int64_t xss,
+                  float* Y, hipStream_t s, const float* rw) {
+  const int64_t nb = K / kQK;
+  if (nb % 4 != 0) return BQM_E_UNSUPPORTED;
+  const int CB = fmt == BQM_Q4_0 ? 16 : 32;
+  if (N * nb * CB >= ((int64_t)1 << 31)) return BQM_E_UNSUPPORTED;
+  const int TS = T * top_k;
+  const bool gu = w_up != nullptr;
+  const int fixed = mma_table_bytes(E, TS);
+  int64_t kc = (kMMaxLds - fixed) / kXBlk;
+  kc &= ~int64_t(3);
+  if (kc > nb) kc = nb < 4 ? 4 : nb;
+  // the staging area also holds the K-split partial sums
+  const int64_t xbytes = std::max<int64_t>(kc * kXBlk, mma_part_bytes(fmt == BQM_Q4_0, gu));
+  if (fixed + xbytes > kMMaxLds) return BQM_E_UNSUPPORTED;
+  Layout L;
+  layout_of(fmt, (int64_t)E * N, K, &L);
+  const uint8_t* codes = static_cast<const uint8_t*>(w);
+  const uint8_t* up = static_cast<const uint8_t*>(w_up);
+  MmaArgs a;
+  a.codes = codes;
+  a.scales = reinterpret_cast<const uint16_t*>(codes + L.scales_off);
+  a.codes2 = up;
+  a.scales2 = up ? reinterpret_cast<const uint16_t*>(up + L.scales_off) : nullptr;
+  a.ids = ids;
+  a.x = X;
+  a.y = Y;
+  a.rw = rw;
+  a.E = E;
+  a.N = (int)N;
+  a.nb = (int)nb;
+  a.TS = TS;
+  a.top_k = top_k;
+  a.kc = (int)kc;
+  a.xts = xts;
+  a.xss = xss;
+  MmaKernel k = mma_kernel(fmt, gu);
+  const int lds = fixed + (int)xbytes;
+  if (lds > 64 * 1024)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  hipLaunchKernelGGL(k, dim3((unsigned)cu_count()), dim3(kMThreads), lds, s, a);
+  return launch_status();
+}
+
+}  // namespace bqm

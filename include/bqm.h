@@ -112,7 +112,10 @@ int qmv_q8_0(const void* w_packed, const float* X, float* Y, int M, int64_t N, i
  * slot its own input (down projection).  A negative id marks a padding slot: its Y row is
  * written with zeros.  An id >= E is a contract violation: its Y row is filled with NaN
  * and nothing outside the arrays is read.  Each selected expert's rows are streamed once
- * per group of up to 4 of the slots routed to it.
+ * per group of the slots routed to it: groups of up to 4 (fp32 vector products), or from
+ * T >= 8 tokens with K a multiple of 128 groups of up to 16 (bf16 matrix-core products with
+ * each input split into two bf16 parts but for a remainder below 2^-14 |x|; the result
+ * meets the same 1e-3 * sum |w x| bound for inputs below 2^86 in magnitude).
  * w_packed: the expert tensor packed as ONE matrix of E*N rows (bqm_repack with
  * rows = E*N).  ids: int32 [T][top_k], device memory.  Y: fp32 [T][top_k][N].
  * fmt: BQM_Q4_0 or BQM_Q8_0.  Limits: T <= 64, top_k <= 32, E <= 4096. */
@@ -126,8 +129,8 @@ int qmv_id(int fmt, const void* w_packed, int E, int64_t N, int64_t K, const int
  * of the models it runs:
  *     g = W_gate[e] x_ts,  u = W_up[e] x_ts,  Y[t][s][n] = silu(g[n]) * u[n],
  *     silu(z) = z / (1 + exp(-z))
- * One pass: each selected expert's gate and up rows are streamed once for all its slots
- * (in groups of up to 4), both sums share every input read.  w_gate and w_up: two expert
+ * One pass: each selected expert's gate and up rows are streamed once per group of its
+ * slots (groups as for qmv_id), both sums share every input read.  w_gate and w_up: two expert
  * tensors of the same format and shape, each packed as one matrix of E*N rows.  Everything
  * else (ids, strides, padding and out-of-range ids, limits, errors) as qmv_id. */
 int qmv_id_gate_up(int fmt, const void* w_gate, const void* w_up, int E, int64_t N, int64_t K,

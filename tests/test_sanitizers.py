@@ -68,7 +68,7 @@ def test_library_host_code_under_sanitizers(tmp_path):
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-ffp-contract=off",
              "-fhip-fp32-correctly-rounded-divide-sqrt", "-mllvm", "-amdgpu-mfma-vgpr-form=1", *san]
     procs, objs = [], []
-    for src in ("api", "repack", "qmv", "qmm"):
+    for src in ("api", "repack", "qmv", "qmv_mma", "qmm"):
         obj = str(tmp_path / f"{src}.o")
         objs.append(obj)
         procs.append(subprocess.Popen([hipcc, *flags, "-c", os.path.join(CSRC, f"{src}.hip"), "-o", obj],

@@ -437,11 +437,15 @@ __global__ __launch_bounds__(kMThreads) void k_qmv_id_mma(MmaArgs a) {
         }
       }
       __syncthreads();
-      // two quads in flight: the loads of the next are issued before the products of this one
+      // Quads in pairs, both issued before either is used: a pair covers whole 128-byte lines
+      // of each row.  Issuing one quad ahead of its products instead requested the second
+      // half of a line while the first was still in flight, and more lines crossed HBM twice
+      // (measured on the MoE layer at T = 16: reads 1.66x -> 1.45x the algorithmic bytes,
+      // 66.7 -> 64.4 us per call; gate+up 102.9 -> 98.4 us).
       for (int qd = q0; qd < q1; qd += 2) {
+        if (qd > q0) issue(QA, kb0 + 4 * qd, true);  // the first pair's was issued above
         issue(QB, kb0 + 4 * (qd + 1), qd + 1 < q1);
         consume(QA, qd);
-        issue(QA, kb0 + 4 * (qd + 2), qd + 2 < q1);
         if (qd + 1 < q1) consume(QB, qd + 1);
       }
     }

@@ -25,6 +25,7 @@
 // split between waves is finished through LDS in wave order.  No atomics on data; the
 // summation order is fixed for a given launch shape.
 #include "bqm_internal.h"
+#include "slot_groups.h"
 
 #include <atomic>
 #include <mutex>
@@ -456,8 +457,6 @@ __device__ __forceinline__ bool grid_barrier(uint32_t* ws, uint32_t epoch, bool*
 
 // Largest batch class (slots per group) of the indexed form.
 constexpr int kIdMaxClass = 4;
-// Slots of the indexed form, at most (its tables are built in LDS).
-constexpr int kIdMaxSlots = BQM_QMV_ID_MAX_T * BQM_QMV_ID_MAX_TOPK;
 // LDS rows (64 bytes) the indexed form's tables take: per-expert counts (E + 1), the slots
 // grouped by expert (TS) and the groups (3 ints each, at most TS).
 __host__ __device__ inline int idx_table_rows(int E, int TS) { return (4 * (E + 1) + 16 * TS + 63) / 64; }
@@ -521,94 +520,9 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
   __shared__ int scan_w[2 * NW];
   Stage ibase;  // indexed form: expert 0, bases
   if constexpr (IDX) {
-    // Counting sort of the slots by expert (bucket E: invalid ids), stable: within an
-    // expert's run the slots are in index order, so every workgroup forms the same groups
-    // (the workgroups split a group's rows between them).  Each run is cut into groups of
-    // at most MM slots.
-    const int E = a.ix.E;
-    for (int e = tid; e <= E; e += NT) cnt[e] = 0;
-    __syncthreads();
-    constexpr int SPT = (kIdMaxSlots + NT - 1) / NT;
-    int key[SPT], pos[SPT];
-#pragma unroll
-    for (int k = 0; k < SPT; k++) {
-      const int i = tid + k * NT;
-      key[k] = E;
-      pos[k] = 0;
-      if (i < TS) {
-        const int e = a.ix.ids[i];
-        key[k] = e >= 0 && e < E ? e : E;
-        pos[k] = atomicAdd(&cnt[key[k]], 1);
-      }
-    }
-    __syncthreads();
-    // exclusive scans over e = 0..E of the slot counts and of the group counts; thread t
-    // owns entries [t * per, (t + 1) * per)
-    const int per = (E + 1 + NT - 1) / NT;
-    const int e0 = min(E + 1, tid * per), e1 = min(E + 1, e0 + per);
-    int ls = 0, lg = 0;
-    for (int e = e0; e < e1; e++) {
-      const int c = cnt[e];
-      ls += c;
-      lg += e < E ? (c + MM - 1) / MM : 0;
-    }
-    int is = ls, ig = lg;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int u = __shfl_up(is, o, 64), v = __shfl_up(ig, o, 64);
-      if (lane >= o) {
-        is += u;
-        ig += v;
-      }
-    }
-    if (lane == 63) {
-      scan_w[2 * wave] = is;
-      scan_w[2 * wave + 1] = ig;
-    }
-    __syncthreads();
-    int s0 = is - ls, g0 = ig - lg;
-    for (int w = 0; w < wave; w++) {
-      s0 += scan_w[2 * w];
-      g0 += scan_w[2 * w + 1];
-    }
-    for (int e = e0; e < e1; e++) {
-      const int c = cnt[e];
-      cnt[e] = s0;
-      if (e < E)
-        for (int j = 0; j < c; j += MM) {
-          groups[3 * g0] = e;
-          groups[3 * g0 + 1] = s0 + j;
-          groups[3 * g0 + 2] = min(MM, c - j);
-          g0++;
-        }
-      s0 += c;
-    }
-    if (tid == NT - 1) lds_units = g0;
-    __syncthreads();
-    // each slot at the place its counting atomic returned (an order that differs between
-    // workgroups), then at its rank by index within its run
-#pragma unroll
-    for (int k = 0; k < SPT; k++) {
-      const int i = tid + k * NT;
-      if (i < TS && key[k] < E) srt[cnt[key[k]] + pos[k]] = i;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < SPT; k++) {
-      const int i = tid + k * NT;
-      if (i < TS && key[k] < E) {
-        const int q0 = cnt[key[k]], q1 = cnt[key[k] + 1];
-        int r = q0;
-        for (int q = q0; q < q1; q++) r += srt[q] < i;
-        pos[k] = r;
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < SPT; k++) {
-      const int i = tid + k * NT;
-      if (i < TS && key[k] < E) srt[pos[k]] = i;
-    }
+    // the slots grouped by expert, groups of at most MM slots (srt is first read after the
+    // barrier below)
+    group_slots<NT, MM, false>(a.ix.ids, a.ix.E, TS, cnt, srt, groups, scan_w, &lds_units);
     const int N = (int)a.one.N, nb = (int)(a.one.K >> 5);
     ibase.codes = a.one.w;
     ibase.scales = a.ix.scales;

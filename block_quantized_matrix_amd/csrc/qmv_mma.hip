@@ -27,14 +27,15 @@
 // 1e-3 sum |w x|; neutral codes give exactly zero; integer inputs and power-of-two scales
 // give exact results.
 //
-// Work.  Every workgroup (one per compute unit, 16 waves) sorts the slots by expert (a
-// stable counting sort in LDS) and cuts each expert's run into groups of up to 16.  The
+// Work.  Every workgroup (one per compute unit, 16 waves) sorts the slots by expert (the
+// stable counting sort of slot_groups.h) and cuts each expert's run into groups of up to 16.  The
 // 16-row tiles of all groups are split evenly over the workgroups.  A workgroup walks its
 // tiles in passes of one group each: it stages the group's inputs (both bf16 parts) for a
 // chunk of K in LDS, its waves compute their tiles over the chunk, and so on along K.  When
 // a pass has fewer tiles than waves, the waves also split each chunk's blocks between them
 // and the partial sums are added through LDS in a fixed order, so results are deterministic.
 #include "bqm_internal.h"
+#include "slot_groups.h"
 
 #include <algorithm>
 
@@ -54,7 +55,6 @@ constexpr int kXBlk = 2 * 64 * 16;                  // LDS bytes per staged bloc
 constexpr int kMStaticLds = 1024;
 constexpr int kMMaxLds = 160 * 1024 - kMStaticLds;  // dynamic LDS of a launch
 constexpr uint32_t kOob = 0x80000000u;              // a lane offset past every descriptor: reads 0
-constexpr int kMMaxSlots = BQM_QMV_ID_MAX_T * BQM_QMV_ID_MAX_TOPK;
 constexpr int kJobs = 4;                            // staging jobs per thread whose loads fly together
 
 struct MmaArgs {
@@ -145,92 +145,8 @@ __global__ __launch_bounds__(kMThreads) void k_qmv_id_mma(MmaArgs a) {
   int* grp = srt + TS;
   char* xl = lds + mma_table_bytes(E, TS);
 
-  // ---- slots grouped by expert: a stable counting sort (bucket E: ids out of range) ----
-  for (int e = tid; e <= E; e += kMThreads) cnt[e] = 0;
-  __syncthreads();
-  constexpr int SPT = (kMMaxSlots + kMThreads - 1) / kMThreads;
-  int key[SPT], pos[SPT];
-#pragma unroll
-  for (int k = 0; k < SPT; k++) {
-    const int i = tid + k * kMThreads;
-    key[k] = E;
-    pos[k] = 0;
-    if (i < TS) {
-      const int e = a.ids[i];
-      key[k] = e >= 0 && e < E ? e : E;
-      pos[k] = atomicAdd(&cnt[key[k]], 1);
-    }
-  }
-  __syncthreads();
-  {
-    // exclusive scans over e = 0..E of the slot counts and the group counts; thread t owns
-    // entries [t * per, (t + 1) * per)
-    const int per = (E + 1 + kMThreads - 1) / kMThreads;
-    const int e0 = min(E + 1, tid * per), e1 = min(E + 1, e0 + per);
-    int ls = 0, lg = 0;
-    for (int e = e0; e < e1; e++) {
-      const int c = cnt[e];
-      ls += c;
-      lg += e < E ? (c + kGroupSlots - 1) / kGroupSlots : 0;
-    }
-    int is = ls, ig = lg;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int u = __shfl_up(is, o, 64), v = __shfl_up(ig, o, 64);
-      if (lane >= o) {
-        is += u;
-        ig += v;
-      }
-    }
-    if (lane == 63) {
-      s_scan[2 * wave] = is;
-      s_scan[2 * wave + 1] = ig;
-    }
-    __syncthreads();
-    int s0 = is - ls, g0 = ig - lg;
-    for (int w = 0; w < wave; w++) {
-      s0 += s_scan[2 * w];
-      g0 += s_scan[2 * w + 1];
-    }
-    for (int e = e0; e < e1; e++) {
-      const int c = cnt[e];
-      cnt[e] = s0;
-      if (e < E)
-        for (int j = 0; j < c; j += kGroupSlots) {
-          grp[3 * g0] = e;
-          grp[3 * g0 + 1] = s0 + j;
-          grp[3 * g0 + 2] = min(kGroupSlots, c - j);
-          g0++;
-        }
-      s0 += c;
-    }
-    if (tid == kMThreads - 1) s_ng = g0;
-  }
-  __syncthreads();
-  // each slot at the place its counting atomic returned, then at its rank by index in its run
-#pragma unroll
-  for (int k = 0; k < SPT; k++) {
-    const int i = tid + k * kMThreads;
-    if (i < TS && key[k] < E) srt[cnt[key[k]] + pos[k]] = i;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < SPT; k++) {
-    const int i = tid + k * kMThreads;
-    if (i < TS && key[k] < E) {
-      const int q0 = cnt[key[k]], q1 = cnt[key[k] + 1];
-      int r = q0;
-      for (int q = q0; q < q1; q++) r += srt[q] < i;
-      pos[k] = r;
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < SPT; k++) {
-    const int i = tid + k * kMThreads;
-    if (i < TS && key[k] < E) srt[pos[k]] = i;
-  }
-  __syncthreads();
+  // the slots grouped by expert, groups of up to 16
+  group_slots<kMThreads, kGroupSlots>(a.ids, E, TS, cnt, srt, grp, s_scan, &s_ng);
   const int ng = s_ng;
 
   // rows of slots that no group computes, each by one workgroup: a negative id gives zeros,

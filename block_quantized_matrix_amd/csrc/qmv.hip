@@ -1004,8 +1004,14 @@ constexpr int chain_ring() {
 // log2 of the waves per workgroup: 16 waves, or 8 for the widest batch, whose sums need
 // more than the 128 registers a lane has when 16 waves share a CU (measured on the 27B
 // Q8_0 pass: M = 4 is fastest with 16 waves and one row per lane, M = 8 with 8 waves and
-// two rows per lane)
-constexpr int chain_lgw(int mm) { return mm >= BQM_CHAIN_MM_WIDE ? 3 : 4; }
+// two rows per lane).  The indexed forms (mode 1, 2) at batch classes 1 and 2 take 8 waves:
+// their calls are small (T = 1: 28 MB per MoE projection, ≈ 110 KB per workgroup) and a
+// lighter workgroup starts and drains sooner (per call on the 128-expert MoE layer, 8 against
+// 16 waves: T = 1 qmv_id 13.5 / 15.4 us, gate+up 18.8 / 18.8; T = 2 24.2 / 23.9, gate+up
+// 32.8 / 34.8; class 4 keeps 16: T = 4 38.2 / 37.4, gate+up 61.2 / 57.3)
+constexpr int chain_lgw(int mm, int mode = 0) {
+  return (mode != 0 && mm <= 2) || mm >= BQM_CHAIN_MM_WIDE ? 3 : 4;
+}
 // rows per lane: one read of the staged inputs serves the codes of two rows, halving the
 // LDS reads per weight byte (batch 1: 8 bytes of x per Q4_0 code byte otherwise; measured
 // +6% on the 27B Q4_0 pass, +6% on the 27B Q8_0 pass at M = 4) and, for the widest batch,
@@ -1016,14 +1022,14 @@ constexpr int mode_r(int mm, int mode) { return mode == 2 ? 2 : chain_r(mm); }
 template <int FMT, int MODE>
 ChainKernel chain_kernel_f(int mm) {
   switch (mm) {
-    case 1: return k_qmv_chain<FMT, chain_ring<FMT, 1>(), 1, chain_lgw(1), mode_r(1, MODE), MODE>;
+    case 1: return k_qmv_chain<FMT, chain_ring<FMT, 1>(), 1, chain_lgw(1, MODE), mode_r(1, MODE), MODE>;
     // batch 2: one step in flight for the chain (R = 1), the batch-1 ring for the indexed
     // forms (two rows per lane); deeper rings spill registers
-    case 2: return k_qmv_chain<FMT, MODE == 0 ? 1 : chain_ring<FMT, 1>(), 2, chain_lgw(2), mode_r(2, MODE), MODE>;
-    case 4: return k_qmv_chain<FMT, chain_ring<FMT, 4>(), 4, chain_lgw(4), mode_r(4, MODE), MODE>;
+    case 2: return k_qmv_chain<FMT, MODE == 0 ? 1 : chain_ring<FMT, 1>(), 2, chain_lgw(2, MODE), mode_r(2, MODE), MODE>;
+    case 4: return k_qmv_chain<FMT, chain_ring<FMT, 4>(), 4, chain_lgw(4, MODE), mode_r(4, MODE), MODE>;
     default:  // the indexed forms run at most class 4 (launch_id): no class 8 for them
       if constexpr (MODE != 0) return chain_kernel_f<FMT, MODE>(4);
-      else return k_qmv_chain<FMT, chain_ring<FMT, 8>(), 8, chain_lgw(8), mode_r(8, MODE), MODE>;
+      else return k_qmv_chain<FMT, chain_ring<FMT, 8>(), 8, chain_lgw(8, MODE), mode_r(8, MODE), MODE>;
   }
 }
 template <int MODE>
@@ -1127,7 +1133,7 @@ int launch_chain(int fmt, int mm, const GemvDesc* descs, const int64_t* seg, con
   if (ok < 0) return BQM_E_LAUNCH;
   allow_lds(k, kP1MaxLds);
   const int grid = cu_count();
-  const int threads = 64 << chain_lgw(mm);
+  const int threads = 64 << chain_lgw(mm, mode);
   if (coop) {
     // workgroups wait for each other: they must all be resident at once
     void* args[] = {&a};

@@ -196,3 +196,20 @@ def test_mma_deterministic():
     bqm.qmv_id("q4_0", Wp, E, N, K, ids, T, top_k, X, K, 0, Y1)
     bqm.qmv_id("q4_0", Wp, E, N, K, ids, T, top_k, X, K, 0, Y2)
     assert torch.equal(Y1, Y2)
+
+
+def test_mma_q8_code_minus_128():
+    """Q8_0 code -128 (accepted on read) through the matrix cores, exact probe: codes in
+    [-128, 127] with -128 in every block, integer inputs, power-of-two scales."""
+    T, E, N, K, top_k = 16, 4, 48, 1024, 2
+    rng = np.random.default_rng(13)
+    codes = rng.integers(-128, 128, (E * N, K // 32, 32))
+    codes[:, :, 7] = -128
+    d = rng.choice([0.5, 1.0, 2.0], (E * N, K // 32)).astype(np.float16)
+    W = np.concatenate([d.view(np.uint8).reshape(E * N, K // 32, 2),
+                        codes.astype(np.int8).view(np.uint8)], axis=2).reshape(E * N, -1)
+    ids = _ids(T, E, top_k, ("mma-m128-router",))
+    X = gen.small_int((T, K), ("mma-m128-x",), device=DEV)
+    say("mma q8 code -128")
+    y, Yr, _ = _run_id("q8_0", torch.from_numpy(W).to(DEV), E, N, K, ids, X, K, 0)
+    assert np.array_equal(y.astype(np.float64), Yr)

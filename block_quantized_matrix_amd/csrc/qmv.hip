@@ -399,15 +399,18 @@ __device__ __forceinline__ void load_unit(const int* groups, const Stage& base, 
   stage_chunk<LGW, R, GU ? 1 : R>(c, kc, wave, 0, s);
 }
 
-// Device-wide barrier between the GEMVs of a chain.  Workspace words: [0] release epoch,
-// [2] error, [3] n, [4] format, [5] kc, [6] partial-sum rows, [7] M class; then one arrival
-// flag per workgroup, each on its own 128-byte line (no contended atomic).  Workgroup 0
-// waits for every flag to reach the barrier's epoch and then publishes it in the release
-// word, which the others wait for.  Data crossing the barrier (the outputs y and the next
-// inputs x) is written and read with agent-coherent (sc1) accesses, so no L2-wide
-// write-back or invalidation is needed; the outputs must only have landed before a
-// workgroup arrives (see the wait below).  Every wait is bounded: on timeout the error
-// word is set and all workgroups leave.
+// Device-wide barrier between the GEMVs of a chain.  Workspace words: [0] the last epoch
+// (read at the start of a launch), [2] error, [3] n, [4] format, [5] kc, [6] partial-sum rows,
+// [7] M class; then one arrival flag per workgroup, each on its own 128-byte line (no
+// contended atomic).  Every workgroup writes the barrier's epoch to its flag and waits until
+// all flags have reached it, one thread per flag.  (Workgroup 0 gathering the flags and
+// publishing one release word for the others to poll took a memory round trip more: the
+// dependent 27B Q4_0 pass 3-4 % slower, Q8_0 M = 4 2.5 %.  Polling all flags when they were
+// packed into a few lines was slower than both: every line had 256 pollers.)  Data crossing
+// the barrier (the outputs y and the next inputs x) is written and read with agent-coherent
+// (sc1) accesses, so no L2-wide write-back or invalidation is needed; the outputs must only
+// have landed before a workgroup arrives (see the wait below).  Every wait is bounded: on
+// timeout the error word is set and all workgroups leave.
 constexpr int kChainHeaderWords = 64;      // 256 bytes
 constexpr int kFlagStrideWords = 32;       // 128 bytes
 constexpr int kChainMaxWorkgroups = 512;
@@ -430,26 +433,24 @@ __device__ __forceinline__ bool grid_barrier(uint32_t* ws, uint32_t epoch, bool*
   __builtin_amdgcn_s_waitcnt(0x0F70 | LOADS);  // vmcnt(LOADS); expcnt, lgkmcnt: no wait
   __syncthreads();
   uint32_t* flags = ws + kChainHeaderWords;
-  if (threadIdx.x == 0) st_agent(flags + blockIdx.x * kFlagStrideWords, epoch);
-  if (blockIdx.x == 0) {
-    for (uint32_t b = threadIdx.x; b < gridDim.x; b += blockDim.x) {
-      uint32_t spins = 0;
-      while (ld_agent(flags + b * kFlagStrideWords) != epoch) {
-        if (++spins > kSpinLimit || ld_agent(ws + 2) != 0) { st_agent(ws + 2, 1u); break; }
-        __builtin_amdgcn_s_sleep(1);
-      }
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) st_agent(ws, epoch);
-  }
   if (threadIdx.x == 0) {
+    st_agent(flags + blockIdx.x * kFlagStrideWords, epoch);
+    *lds_ok = true;
+  }
+  __syncthreads();
+  // every workgroup waits for every flag (one thread per flag)
+  for (uint32_t b = threadIdx.x; b < gridDim.x; b += blockDim.x) {
     uint32_t spins = 0;
-    bool ok = true;
-    while (ld_agent(ws) != epoch) {
-      if (++spins > kSpinLimit || ld_agent(ws + 2) != 0) { st_agent(ws + 2, 1u); ok = false; break; }
+    // a workgroup past this barrier may already have arrived at the next: epochs only grow
+    while ((int32_t)(ld_agent(flags + b * kFlagStrideWords) - epoch) < 0) {
+      if (++spins > kSpinLimit || ld_agent(ws + 2) != 0) { st_agent(ws + 2, 1u); *lds_ok = false; break; }
       __builtin_amdgcn_s_sleep(1);
     }
-    *lds_ok = ok && ld_agent(ws + 2) == 0;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if (blockIdx.x == 0) st_agent(ws, epoch);  // the epoch the next launch starts from
+    *lds_ok = *lds_ok && ld_agent(ws + 2) == 0;
   }
   __syncthreads();
   return *lds_ok;

@@ -743,7 +743,9 @@ def run_prefill_moe(args, torch, gen, bqm):
     ops = n_layers * 3 * 2.0 * slots * F * H           # useful int8 operations, all launches
     tops = ops / (dur.sum() * 1e-3) / 1e12
     triples = n_layers * 3.0 * slots * F * (H // 32)  # (slot, n, block): one conversion, one FMA
-    tiles = [int(np.sum((L[-1] + 63) // 64)) for L in layers]   # 64-row tiles of the kernel
+    # the kernel's row tiles: 64 slots of an expert while more than 32 are left, then 32
+    tall = [int(np.sum(L[-1] // 64 + (L[-1] % 64 > 32))) for L in layers]
+    short = [int(np.sum((L[-1] % 64 > 0) & (L[-1] % 64 <= 32))) for L in layers]
     return {"metric": "MoE prefill qmm_id int8 TOP/s", "value": round(tops, 2), "unit": "TOP/s",
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8/f32",
@@ -752,7 +754,7 @@ def run_prefill_moe(args, torch, gen, bqm):
                                    "over a 512-token prompt, 4 distinct layers per step"},
             "ms_per_layer": round(ms / n_layers, 4),
             "busiest_expert_slots": [int(L[-1].max()) for L in layers],
-            "row_tile_fill": round(slots / (64.0 * float(np.mean(tiles))), 3),
+            "row_tile_fill": round(slots / float(np.mean([64 * a + 32 * b for a, b in zip(tall, short)])), 3),
             "roofline": {**alu_roofline(triples, triples, float(dur.sum()) * 1e-3, "k_qmm_id_q4_0",
                                         round(1e3 * float(dur.mean()), 3),
                                         mfma_int8_frac=round(tops / INT8_PEAK_TOPS, 4)),

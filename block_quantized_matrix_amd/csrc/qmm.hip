@@ -112,16 +112,18 @@ __device__ __forceinline__ u32x4 dw_operand(uint32_t dw_bits) {
 }
 
 // Q4_0 codes: a 16-byte block holds weight j in the low nibble of byte j and weight j + 16
-// in the high one.  Each half expands to four signed bytes per word (nibble - 8) without a
-// borrow between bytes: set bit 7, subtract 8, flip bit 7 back.
-__device__ __forceinline__ uint32_t nib_to_i8(uint32_t v) {  // v: four nibbles 0..15
-  return ((v | 0x80808080u) - 0x08080808u) ^ 0x80808080u;
-}
+// in the high one.  Each nibble becomes the int8 16 (n - 8), four to a word with no carry
+// between bytes: flipping bit 3 of a nibble gives n - 8 as a 4-bit two's complement number,
+// which read as the high half of a byte (the high nibble masked in place, the low one
+// shifted up) is the int8 16 (n - 8).  The sums come out 16 times too large (exactly: at most
+// 2^19 in magnitude); the epilogue takes the factor out.
+constexpr uint32_t kQ4Flip = 0x88888888u, kHighNibbles = 0xF0F0F0F0u;
 __device__ __forceinline__ void expand_q4(const u32x4& q, u32x4& lo, u32x4& hi) {
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    lo[i] = nib_to_i8(q[i] & 0x0F0F0F0Fu);
-    hi[i] = nib_to_i8((q[i] >> 4) & 0x0F0F0F0Fu);
+    const uint32_t v = q[i] ^ kQ4Flip;
+    lo[i] = (v << 4) & kHighNibbles;
+    hi[i] = v & kHighNibbles;
   }
 }
 
@@ -131,8 +133,10 @@ __device__ __forceinline__ void expand_q4(const u32x4& q, u32x4& lo, u32x4& hi) 
 // expanded to int8 while they are staged, so that the LDS layout and everything after it
 // are the same for both.  Rows: dense (GATHER false), tile row r is input and output row
 // m0 + r (< M); gathered, tile row r reads input row xrow[r] and writes output row yrow[r]
-// (LDS tables, -1 past the tile's rows).
-template <int FMT, int WGM, int TI, int TJ, bool GATHER>
+// (LDS tables, -1 past the tile's rows).  NQ < 4: only the first 8 NQ rows of each MFMA
+// tile hold inputs, and the rescale skips the rest of a lane's results (rows 8 q .. 8 q + 7
+// are its results 4 q .. 4 q + 3).
+template <int FMT, int WGM, int TI, int TJ, bool GATHER, int NQ = 4>
 __device__ __forceinline__ void qmm_core(const uint8_t* __restrict__ Wc, const uint16_t* __restrict__ Wd,
                                          const int8_t* __restrict__ Xq, const float* __restrict__ dx,
                                          int64_t x_rows, float* __restrict__ Y, int N, int nb, int n0,
@@ -209,36 +213,39 @@ __device__ __forceinline__ void qmm_core(const uint8_t* __restrict__ Wc, const u
     bW[q] = kb;
   }
 
-  u32x4 pa[PA], pb[NPB];
-  uint32_t px[QX], pw[2];
-  auto fetch = [&](int b0) {
+  // two register sets of staged pieces: the loads of stage s + 2 are issued while stage s is
+  // computed, stage s + 1's already in flight
+  u32x4 pa[2][PA], pb[2][NPB];
+  uint32_t px[2][QX], pw[2][2];
+  auto fetch = [&](auto SET, int b0) {
+    constexpr int S = decltype(SET)::value;
     const int bn_ = min(BKB, nb - b0);
     const bool full = bn_ == BKB;
 #pragma unroll
     for (int p = 0; p < PA; p++)
-      pa[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                  rA, full || bA[p] < bn_ ? oA[p] : kOob, b0 * 32, 0));
+      pa[S][p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                     rA, full || bA[p] < bn_ ? oA[p] : kOob, b0 * 32, 0));
 #pragma unroll
     for (int p = 0; p < NPB; p++)
-      pb[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                  rB, full || bB[p] < bn_ ? oB[p] : kOob, b0 * (Q4 ? 16 : 32), 0));
+      pb[S][p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                     rB, full || bB[p] < bn_ ? oB[p] : kOob, b0 * (Q4 ? 16 : 32), 0));
 #pragma unroll
     for (int q = 0; q < QX; q++)
-      px[q] = __builtin_amdgcn_raw_buffer_load_b32(rX, full || bX[q] < bn_ ? oX[q] : kOob, b0 * 4, 0);
+      px[S][q] = __builtin_amdgcn_raw_buffer_load_b32(rX, full || bX[q] < bn_ ? oX[q] : kOob, b0 * 4, 0);
 #pragma unroll
     for (int q = 0; q < 2; q++)
-      pw[q] = (uint32_t)__builtin_bit_cast(uint16_t, __builtin_amdgcn_raw_buffer_load_b16(
-                  rW, full || bW[q] < bn_ ? oW[q] : kOob, b0 * 2, 0));
+      pw[S][q] = (uint32_t)__builtin_bit_cast(uint16_t, __builtin_amdgcn_raw_buffer_load_b16(
+                     rW, full || bW[q] < bn_ ? oW[q] : kOob, b0 * 2, 0));
   };
 
-  fetch(0);
-  for (int b0 = 0; b0 < nb; b0 += BKB) {
+  auto stage = [&](auto SET, int b0) {
+    constexpr int S = decltype(SET)::value;
     const int bn = min(BKB, nb - b0);
     __syncthreads();  // every wave is done with the previous stage
 #pragma unroll
     for (int p = 0; p < PA; p++) {
       const int piece = tid + p * kThreads, row = piece >> 3, c16 = piece & 7;
-      *reinterpret_cast<u32x4*>(sA + row * ROWB + c16 * 16) = pa[p];
+      *reinterpret_cast<u32x4*>(sA + row * ROWB + c16 * 16) = pa[S][p];
     }
 #pragma unroll
     for (int p = 0; p < NPB; p++) {
@@ -246,23 +253,23 @@ __device__ __forceinline__ void qmm_core(const uint8_t* __restrict__ Wc, const u
       if constexpr (Q4) {
         const int row = piece >> 2, kb = piece & 3;
         u32x4 lo, hi;
-        expand_q4(pb[p], lo, hi);
+        expand_q4(pb[S][p], lo, hi);
         *reinterpret_cast<u32x4*>(sB + row * ROWB + kb * 32) = lo;
         *reinterpret_cast<u32x4*>(sB + row * ROWB + kb * 32 + 16) = hi;
       } else {
         const int row = piece >> 3, c16 = piece & 7;
-        *reinterpret_cast<u32x4*>(sB + row * ROWB + c16 * 16) = pb[p];
+        *reinterpret_cast<u32x4*>(sB + row * ROWB + c16 * 16) = pb[S][p];
       }
     }
 #pragma unroll
     for (int q = 0; q < QX; q++) {
       const int e = tid + q * kThreads;  // = kb * TBM + r
-      if (e < NXS) sXs[(e / TBM * 2) * TBM + e % TBM] = dx_operand(__uint_as_float(px[q]));
+      if (e < NXS) sXs[(e / TBM * 2) * TBM + e % TBM] = dx_operand(__uint_as_float(px[S][q]));
     }
 #pragma unroll
-    for (int q = 0; q < 2; q++) sWs[tid + q * kThreads] = dw_operand(pw[q]);  // kb * BN + r
+    for (int q = 0; q < 2; q++) sWs[tid + q * kThreads] = dw_operand(pw[S][q]);  // kb * BN + r
     __syncthreads();
-    if (b0 + BKB < nb) fetch(b0 + BKB);  // in flight while this stage is computed
+    if (b0 + 2 * BKB < nb) fetch(SET, b0 + 2 * BKB);
 
     // unrolled over the stage's blocks, so every LDS read has an immediate offset
 #pragma unroll
@@ -287,14 +294,28 @@ __device__ __forceinline__ void qmm_core(const uint8_t* __restrict__ Wc, const u
           for (int j = 0; j < TJ; j++) {
             const i32x16 isum = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], bq[j], i32x16{}, 0, 0, 0);
             const f32x16 sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as[i], bs[j], f32x16{}, 0, 0, 0);
+            // a lane's results r = 4 q .. 4 q + 3 lie in the tile's rows 8 q .. 8 q + 7
 #pragma unroll
-            for (int r = 0; r < 16; r++) acc[i][j][r] = fmaf(sc[r], (float)isum[r], acc[i][j][r]);
+            for (int r = 0; r < 4 * NQ; r++) acc[i][j][r] = fmaf(sc[r], (float)isum[r], acc[i][j][r]);
           }
       }
     }
+  };
+
+  using Set0 = std::integral_constant<int, 0>;
+  using Set1 = std::integral_constant<int, 1>;
+  fetch(Set0{}, 0);
+  if (BKB < nb) fetch(Set1{}, BKB);
+  for (int b0 = 0; b0 < nb; b0 += 2 * BKB) {
+    stage(Set0{}, b0);
+    if (b0 + BKB < nb) stage(Set1{}, b0 + BKB);
   }
 
-  // a lane's 16 results of a 32 x 32 tile: rows 8 (r / 4) + 4 lh + r % 4, column l32
+  // a lane's 16 results of a 32 x 32 tile: rows 8 (r / 4) + 4 lh + r % 4, column l32.  Q4_0
+  // sums carry the factor 16 of the expanded codes: every rounding step above saw exactly 16
+  // times the values of the unscaled sums, so the product with 1/16 is the unscaled result
+  // (outside fp32's subnormal range, where the scaled sums kept more bits)
+  constexpr float kOut = Q4 ? 0.0625f : 1.0f;
 #pragma unroll
   for (int i = 0; i < TI; i++)
 #pragma unroll
@@ -305,10 +326,10 @@ __device__ __forceinline__ void qmm_core(const uint8_t* __restrict__ Wc, const u
         const int tr = wm + i * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
         if constexpr (GATHER) {
           const int yr = yrow[tr];
-          if (yr >= 0 && n < N) Y[(size_t)yr * N + n] = acc[i][j][r];
+          if (yr >= 0 && n < N) Y[(size_t)yr * N + n] = acc[i][j][r] * kOut;
         } else {
           const int m = m0 + tr;
-          if (m < M && n < N) Y[(size_t)m * N + n] = acc[i][j][r];
+          if (m < M && n < N) Y[(size_t)m * N + n] = acc[i][j][r] * kOut;
         }
       }
     }
@@ -352,19 +373,57 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum) {
   return base + x - v;
 }
 
-// Expert-indexed prefill product.  Every workgroup counts the slots per expert; the
-// experts' row tiles (ceil(count / kIdTBM) each, experts ascending, the slots of an expert
-// in index order) are numbered, and workgroup b takes row tile b / tiles_n, column tile
-// b % tiles_n; workgroups past the last row tile only take part in the padding fill.
-#ifndef BQM_QMM_ID_ROWS
-#define BQM_QMM_ID_ROWS 64
-#endif
-// Row tile of the indexed product.  64 rows (waves 2 x 2, each 1 x 2 MFMA tiles), three
-// workgroups per CU: measured on the 512-token MoE prefill, 185 TOP/s against 161 with two
-// workgroups per CU and 143-164 with 32-row tiles (waves 1 x 4, one MFMA tile each: fewer
-// padded rows, but twice the weight staging per output).
-constexpr int kIdTBM = BQM_QMM_ID_ROWS;
-constexpr int kIdWGM = kIdTBM == 32 ? 1 : 2, kIdTJ = kIdTBM == 32 ? 1 : 2;
+// Exclusive prefix sums of u and v over the workgroup's threads (thread order), and their
+// totals.
+__device__ __forceinline__ void block_exclusive_scan2(int& u, int& v, int* wsum, int& tu, int& tv) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = u, y = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int p = __shfl_up(x, o, 64), q = __shfl_up(y, o, 64);
+    if (lane >= o) {
+      x += p;
+      y += q;
+    }
+  }
+  if (lane == 63) {
+    wsum[2 * wave] = x;
+    wsum[2 * wave + 1] = y;
+  }
+  __syncthreads();
+  int bu = 0, bv = 0;
+  tu = tv = 0;
+  for (int w = 0; w < kThreads / 64; w++) {
+    if (w < wave) {
+      bu += wsum[2 * w];
+      bv += wsum[2 * w + 1];
+    }
+    tu += wsum[2 * w];
+    tv += wsum[2 * w + 1];
+  }
+  __syncthreads();
+  u = bu + x - u;
+  v = bv + y - v;
+}
+
+// Expert-indexed prefill product.  Every workgroup counts the slots per expert and cuts each
+// expert's slots (in index order) into row tiles: tall tiles of kIdTall slots while more
+// than kIdShort are left, then one short tile of kIdShort for a remainder that fits one.
+// The tall tiles of all experts are numbered first (experts ascending), then the short
+// ones; workgroup b takes row tile b / tiles_n, column tile b % tiles_n, and workgroups past
+// the last row tile only take part in the padding fill.  A tall tile runs its four waves
+// as 2 x 2 (each 32 rows x 64 columns), a short one as 1 x 4 (each 32 x 32): measured on
+// the 512-token MoE prefill (128 experts, top-8, a skewed router: half the experts hold two
+// slots or fewer, the busiest about 500), a short remainder in a tall tile left the two
+// waves of its empty half with nothing to compute, and 32-row tiles throughout (waves
+// 1 x 4) lost on the busy experts' reuse of each weight tile.
+constexpr int kIdTall = 64, kIdShort = 32;
+constexpr int kIdChunk = 16;  // slot ids a thread loads at once
+// A short tile holding at most kIdFew slots (most of the rarely chosen experts' tiles) rescales
+// only the MFMA results of its first kIdFew rows: a separate instantiation, since a branch per
+// row group inside the block loop cost more than it saved (it splits the MFMA and VALU
+// stream the compiler interleaves).
+constexpr int kIdFew = 8;
 
 template <int FMT>
 __device__ __forceinline__ void qmm_indexed(const uint8_t* __restrict__ Wc, const uint16_t* __restrict__ Wd,
@@ -373,76 +432,139 @@ __device__ __forceinline__ void qmm_indexed(const uint8_t* __restrict__ Wc, cons
                                             int E, int N, int nb, int TS, int top_k, int xtr, int xsr,
                                             int64_t x_rows,
                                             int tiles_n) {
-  __shared__ __attribute__((aligned(16))) int8_t sA[kIdTBM * ROWB];
+  __shared__ __attribute__((aligned(16))) int8_t sA[kIdTall * ROWB];
   __shared__ __attribute__((aligned(16))) int8_t sB[BN * ROWB];  // first: per-expert counts
-  __shared__ u32x4 sXs[BKB * 2 * kIdTBM];
+  __shared__ u32x4 sXs[BKB * 2 * kIdTall];
   __shared__ u32x4 sWs[BKB * BN];
-  __shared__ int xrow[kIdTBM], yrow[kIdTBM];
-  __shared__ int wsum[kThreads / 64];
-  __shared__ int tile_e, tile_m0;
+  __shared__ int xrow[kIdTall], yrow[kIdTall];
+  __shared__ int wsum[2 * (kThreads / 64)];
+  __shared__ int tile_e, tile_m0, tile_h, tile_rows;
   const int tid = threadIdx.x;
-  // rows of slots that no tile computes, each by one workgroup: a padding slot (negative
-  // id) gives zeros, an id >= E NaN
-  for (int i = blockIdx.x; i < TS; i += gridDim.x) {
-    const int e = ids[i];
-    if (e >= 0 && e < E) continue;
-    const float v = e < 0 ? 0.0f : __builtin_nanf("");
-    for (int n = tid; n < N; n += kThreads) Y[(size_t)i * N + n] = v;
+  // Thread t owns the slots [s0, s1).  Their ids are read in chunks of kIdChunk through a
+  // buffer descriptor, every load of a chunk issued before the first is used (a slot past the
+  // thread's range reads its neighbour's id, or 0 past TS, and is masked); the first chunk
+  // stays in registers for both passes over the slots.  (Read one at a time, the ids cost
+  // each workgroup two or three dependent round trips per slot it owns: on the 512-token MoE
+  // prefill, a quarter of the kernel's time.)
+  const int sper = (TS + kThreads - 1) / kThreads;
+  const int s0 = min(TS, tid * sper), s1 = min(TS, s0 + sper);
+  const __amdgpu_buffer_rsrc_t rI = __builtin_amdgcn_make_buffer_rsrc((void*)ids, (short)0, TS * 4, 0x00020000);
+  auto load_chunk = [&](int c0, int* v) {
+#pragma unroll
+    for (int k = 0; k < kIdChunk; k++) v[k] = __builtin_amdgcn_raw_buffer_load_b32(rI, (c0 + k) * 4, 0, 0);
+  };
+  int v0[kIdChunk];
+  load_chunk(s0, v0);
+  // rows of slots that no tile computes, each by one workgroup (slots blockIdx.x + j gridDim.x,
+  // their ids read four at a time alongside the chunk): a padding slot (negative id) gives
+  // zeros, an id >= E NaN
+  for (int i0 = blockIdx.x; i0 < TS; i0 += 4 * gridDim.x) {
+    int f[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int64_t i = i0 + (int64_t)j * gridDim.x;
+      f[j] = __builtin_amdgcn_raw_buffer_load_b32(rI, (int)(i < TS ? i : TS) * 4, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int64_t i = i0 + (int64_t)j * gridDim.x;
+      const int e = f[j];
+      if (i >= TS || (e >= 0 && e < E)) continue;
+      const float v = e < 0 ? 0.0f : __builtin_nanf("");
+      for (int n = tid; n < N; n += kThreads) Y[(size_t)i * N + n] = v;
+    }
   }
+  // f(slot, id) for every slot of [s0, s1), in order
+  auto for_slots = [&](auto&& f) {
+#pragma unroll
+    for (int k = 0; k < kIdChunk; k++)
+      if (s0 + k < s1) f(s0 + k, v0[k]);
+    for (int c0 = s0 + kIdChunk; c0 < s1; c0 += kIdChunk) {
+      int v[kIdChunk];
+      load_chunk(c0, v);
+#pragma unroll
+      for (int k = 0; k < kIdChunk; k++)
+        if (c0 + k < s1) f(c0 + k, v[k]);
+    }
+  };
   int* cnt = reinterpret_cast<int*>(sB);
   for (int e = tid; e < E; e += kThreads) cnt[e] = 0;
   if (tid == 0) tile_e = -1;
   __syncthreads();
-  for (int i = tid; i < TS; i += kThreads) {
-    const int e = ids[i];
+  for_slots([&](int, int e) {
     if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
-  }
+  });
   __syncthreads();
-  // find this workgroup's row tile: thread t holds experts [e0, e1) and their tile count
+  // tall and short tiles of an expert with c slots
+  auto tall = [](int c) { return c / kIdTall + (c % kIdTall > kIdShort ? 1 : 0); };
+  auto short_ = [](int c) { const int r = c % kIdTall; return r > 0 && r <= kIdShort ? 1 : 0; };
+  // find this workgroup's row tile: thread t holds experts [e0, e1) and their tile counts
   const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
   const int per = (E + kThreads - 1) / kThreads;
   const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
-  int mine = 0;
-  for (int e = e0; e < e1; e++) mine += (cnt[e] + kIdTBM - 1) / kIdTBM;
-  const int first = block_exclusive_scan(mine, wsum);
-  if (tm >= first && tm < first + mine) {
-    int t = first;
+  int mt = 0, ms = 0;
+  for (int e = e0; e < e1; e++) {
+    mt += tall(cnt[e]);
+    ms += short_(cnt[e]);
+  }
+  int ft = mt, fs = ms, nt, ns;
+  block_exclusive_scan2(ft, fs, wsum, nt, ns);
+  if (tm >= ft && tm < ft + mt) {
+    int t = ft;
     for (int e = e0; e < e1; e++) {
-      const int k = (cnt[e] + kIdTBM - 1) / kIdTBM;
+      const int k = tall(cnt[e]);
       if (tm < t + k) {
         tile_e = e;
-        tile_m0 = (tm - t) * kIdTBM;
+        tile_m0 = (tm - t) * kIdTall;
+        tile_h = kIdTall;
+        tile_rows = min(kIdTall, cnt[e] - tile_m0);
         break;
       }
       t += k;
     }
+  } else if (tm >= nt + fs && tm < nt + fs + ms) {
+    int t = nt + fs;
+    for (int e = e0; e < e1; e++) {
+      if (short_(cnt[e]) && tm == t++) {
+        tile_e = e;
+        tile_m0 = cnt[e] / kIdTall * kIdTall;
+        tile_h = kIdShort;
+        tile_rows = cnt[e] - tile_m0;
+        break;
+      }
+    }
   }
-  for (int r = tid; r < kIdTBM; r += kThreads) xrow[r] = yrow[r] = -1;
+  for (int r = tid; r < kIdTall; r += kThreads) xrow[r] = yrow[r] = -1;
   __syncthreads();
   const int e = tile_e;
   if (e < 0) return;  // past the last row tile (uniform)
-  const int m0 = tile_m0;
-  // the expert's slots of ranks m0 .. m0 + kIdTBM - 1 (rank: place among its slots in index
-  // order); thread t scans slots [s0, s1)
-  const int sper = (TS + kThreads - 1) / kThreads;
-  const int s0 = min(TS, tid * sper), s1 = min(TS, s0 + sper);
+  const int m0 = tile_m0, h = __builtin_amdgcn_readfirstlane(tile_h), rows = __builtin_amdgcn_readfirstlane(tile_rows);
+  // the expert's slots of ranks m0 .. m0 + h - 1 (rank: place among its slots in index order)
   int c = 0;
-  for (int i = s0; i < s1; i++) c += ids[i] == e;
+  for_slots([&](int, int id) { c += id == e; });
   int rank = block_exclusive_scan(c, wsum);
-  for (int i = s0; i < s1; i++)
-    if (ids[i] == e) {
+  for_slots([&](int i, int id) {
+    if (id == e) {
       const int r = rank - m0;
-      if (r >= 0 && r < kIdTBM) {
+      if (r >= 0 && r < h) {
         const int t = i / top_k;
         xrow[r] = t * xtr + (i - t * top_k) * xsr;
         yrow[r] = i;
       }
       ++rank;
     }
+  });
   __syncthreads();
   const int64_t wrow = FMT == BQM_Q4_0 ? (int64_t)nb * 16 : (int64_t)nb * 32;
-  qmm_core<FMT, kIdWGM, 1, kIdTJ, true>(Wc + (int64_t)e * N * wrow, Wd + (int64_t)e * N * nb, Xq, dx,
-                                        x_rows, Y, N, nb, tn * BN, 0, 0, xrow, yrow, sA, sB, sXs, sWs);
+  const uint8_t* We = Wc + (int64_t)e * N * wrow;
+  const uint16_t* De = Wd + (int64_t)e * N * nb;
+  if (h == kIdTall)
+    qmm_core<FMT, 2, 1, 2, true>(We, De, Xq, dx, x_rows, Y, N, nb, tn * BN, 0, 0, xrow, yrow, sA, sB, sXs, sWs);
+  else if (rows > kIdFew)
+    qmm_core<FMT, 1, 1, 1, true>(We, De, Xq, dx, x_rows, Y, N, nb, tn * BN, 0, 0, xrow, yrow, sA, sB, sXs, sWs);
+  else
+    qmm_core<FMT, 1, 1, 1, true, kIdFew / 8>(We, De, Xq, dx, x_rows, Y, N, nb, tn * BN, 0, 0, xrow, yrow, sA, sB,
+                                             sXs, sWs);
 }
 
 #define BQM_QMM_KERNEL(NAME, FMT)                                                              \
@@ -525,7 +647,7 @@ int launch_qmm_id(int fmt, const void* w, int E, int64_t N, int64_t K, const int
   const int TS = T * top_k;
   const int tiles_n = (int)((N + BN - 1) / BN);
   // row tiles: at most one partial tile per expert that has slots, plus the full ones
-  const int64_t max_tm = (TS < E ? TS : E) + (TS + kIdTBM - 1) / kIdTBM;
+  const int64_t max_tm = (TS < E ? TS : E) + (TS + kIdTall - 1) / kIdTall;
   const int64_t grid = max_tm * tiles_n;
   // input rows the slots can address: row (T - 1) x_tok_rows + (top_k - 1) x_slot_rows at most
   const int64_t x_rows = (int64_t)(T - 1) * x_tok_rows + (int64_t)(top_k - 1) * x_slot_rows + 1;

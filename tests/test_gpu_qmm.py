@@ -211,6 +211,24 @@ def test_qmm_id_exact_probe_and_many_slots_per_expert(fmt):
     assert np.array_equal(y[~bad].astype(np.float64), Yr[~bad])
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+def test_qmm_id_exact_probe_tile_heights(fmt):
+    """Bit exact against the oracle with per-expert slot counts on both sides of every cut
+    between row tiles: 64-slot tiles while more than 32 slots are left, one 32-slot tile for
+    a remainder that fits it, rescaling only its first 8 rows when it holds no more (counts
+    1, 8, 9, 31, 32, 33, 63, 64, 65, 72, 73, 96, 97, 128 and none), slots of the experts
+    interleaved in index order."""
+    counts = [1, 8, 9, 31, 32, 33, 63, 64, 0, 65, 72, 73, 96, 97, 128]
+    E, N, K, top_k = len(counts), 160, 288, 2
+    flat = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(counts)])
+    flat = flat[np.random.default_rng(11).permutation(flat.size)]
+    flat = np.concatenate([flat, np.full((-flat.size) % top_k, -1, np.int32)])
+    ids = flat.reshape(-1, top_k)
+    say("qmm_id exact tile heights", fmt, ids.shape)
+    y, Yr, S = run_qmm_id(fmt, E, N, K, ids, "per_slot", ("qmmid-h", fmt), exact=True)
+    assert np.array_equal(y.astype(np.float64), Yr)
+
+
 @pytest.mark.parametrize("proj", ["gate", "down"])
 def test_qmm_id_moe_prefill(proj):
     """The MoE layer over a 512-token prompt (128 experts, top-8, skewed router), gate

@@ -66,16 +66,18 @@ struct MmaArgs {
   const float* x;
   float* y;                // [T * top_k][N]
   const float* rw;         // router weights [T][top_k] the rows are scaled by, or null
-  int E, N, nb, TS, top_k, kc;
+  int E, N, nb, TS, top_k, kc;  // kc: the staging area's bytes / kXBlk
   int64_t xts, xss;        // input strides (floats) per token and per slot
 };
 
 // LDS: the slot table (per-expert counts then starts, E + 1; slots sorted by expert, TS;
-// groups of 3 ints, at most TS), then the staged inputs, whose area also takes the K-split
-// partial sums at the end of a pass.
+// groups of 3 ints, at most TS), then the staging area: a pass's inputs and scales chunk by
+// chunk, and its K-split partial sums at the end.
 __host__ __device__ inline int mma_table_bytes(int E, int TS) { return ((E + 1 + 4 * TS) * 4 + 15) & ~15; }
 // Tiles per wave in a pass (their loads, two quads in flight, and sums fit 128 registers).
 __host__ __device__ constexpr int mma_tpw(bool q4, bool gu) { return q4 ? (gu ? 2 : 4) : (gu ? 1 : 2); }
+// Rows of a pass's scales at most, over both tensors: every wave's tiles.
+__host__ __device__ constexpr int mma_max_rows(bool q4, bool gu) { return kMWaves * mma_tpw(q4, gu) * 16 * (gu ? 2 : 1); }
 // The K-split partial sums at most: every wave but those of the first share, TPW tiles of
 // 16 x 16 floats per tensor each.
 __host__ __device__ constexpr int mma_part_bytes(bool q4, bool gu) {
@@ -199,16 +201,39 @@ __global__ __launch_bounds__(kMThreads) void k_qmv_id_mma(MmaArgs a) {
       rs[1] = __builtin_amdgcn_make_buffer_rsrc((void*)(a.scales2 + erow * nb), (short)0,
                                                 (int)((uint32_t)N * nb * 2), 0x00020000);
     }
-    // lane offsets of its row in each of its tiles: codes (its word or two of a block) and
-    // scales; rows past N and tiles the wave does not have read zeros
-    uint32_t vc[TPW], vs[TPW];
+    // lane offsets of its row in each of its tiles' codes (its word or two of a block); rows
+    // past N and tiles the wave does not have read zeros
+    uint32_t vc[TPW];
 #pragma unroll
     for (int i = 0; i < TPW; i++) {
       const int n = (tb + i) * 16 + j;
       const bool ok = i < mt && n < N;
       vc[i] = ok ? (uint32_t)n * (uint32_t)nb * CB + (uint32_t)q * 16 : kOob;
-      vs[i] = ok ? (uint32_t)n * (uint32_t)nb * 2 : kOob;
     }
+    // The pass's scales are staged in LDS with its inputs, chunk by chunk: R rows (the pass's
+    // tiles) per tensor, each a run of kcp 2-byte scales at a stride of sst bytes.  Read
+    // straight from memory, 8 bytes per row and quad, every row kept a 128-byte scale line
+    // in use for 16 quads: 32 CUs x 16 waves x 64 rows of them, as much as an XCD's L2 holds
+    // while the codes stream through it, and most came back from HBM again and again
+    // (measured on the MoE layer at T = 16: 5x the scale bytes).  Staged, each chunk's scales
+    // of a row are read in one contiguous run.  The chunk (kcp blocks, a multiple of 4) is
+    // the longest that leaves room for both, evened out over the chunks of K; the stride is
+    // twice an odd number of words, so that the 16 rows of one 8-byte read meet 32 distinct
+    // banks.
+    const int R = nt * 16;
+    int kcp = (a.kc * kXBlk - 16 * NG * R) / (kXBlk + 2 * NG * R);
+    kcp = max(4, kcp & ~3);
+    {
+      const int nch = (nb + kcp - 1) / kcp;
+      kcp = min(kcp, (((nb + nch - 1) / nch) + 3) & ~3);
+    }
+    int sdw = kcp / 2 + 2;
+    if (((sdw >> 1) & 1) == 0) sdw += 2;
+    const int sst = 4 * sdw;
+    char* scl = xl + kcp * kXBlk;
+    int srow[TPW];  // this lane's row in the scale area, per tile (tiles it does not have: row 0)
+#pragma unroll
+    for (int i = 0; i < TPW; i++) srow[i] = i < mt ? (tsi * TPW + i) * 16 + j : 0;
     float acc[TPW][NG][4];
 #pragma unroll
     for (int i = 0; i < TPW; i++)
@@ -217,14 +242,13 @@ __global__ __launch_bounds__(kMThreads) void k_qmv_id_mma(MmaArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; r++) acc[i][h][r] = 0.0f;
 
-    // One quad (4 blocks) of a wave's tiles: 16-byte code loads and the 4 scales of each tile
-    // and tensor.  A load covers 64 contiguous bytes of each of the tile's 16 rows (lane
+    // One quad (4 blocks) of a wave's tiles: 16-byte code loads of each tile and tensor (the
+    // scales come from LDS).  A load covers 64 contiguous bytes of each of the tile's 16 rows (lane
     // group q: Q4_0 block q of the quad; Q8_0 half q % 2 of block q / 2, twice), so every
     // load instruction reads whole 64-byte pieces; lane exchanges then give each lane group
     // its word (Q4_0) or 8 bytes (Q8_0) of every block.
     struct Quad {
       u32x4 c[TPW][NG][LW];
-      u32x2 s[TPW][NG];
     };
     // issue a quad's loads; `live` false: offsets past the descriptors, nothing is read
     auto issue = [&](Quad& Qd, int kb, bool live) {
@@ -237,7 +261,6 @@ __global__ __launch_bounds__(kMThreads) void k_qmv_id_mma(MmaArgs a) {
           for (int w = 0; w < LW; w++)
             Qd.c[i][h][w] = __builtin_bit_cast(
                 u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc[h], (vc[i] | m) + w * 64, kb * CB, 0));
-          Qd.s[i][h] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs[h], vs[i] | m, kb * 2, 0));
         }
     };
     // v_permlane32_swap: rows 2-3 (lanes 32-63) of a <-> rows 0-1 of b; v_permlane16_swap:
@@ -274,6 +297,13 @@ __global__ __launch_bounds__(kMThreads) void k_qmv_id_mma(MmaArgs a) {
     };
     // a quad's products: block u of the chunk-local quad `ql`
     auto consume = [&](Quad& Qd, int ql) {
+      // the 4 scales of each tile's row j (lanes of one row read the same 8 bytes)
+      u32x2 sq[TPW][NG];
+#pragma unroll
+      for (int i = 0; i < TPW; i++)
+#pragma unroll
+        for (int h = 0; h < NG; h++)
+          sq[i][h] = *reinterpret_cast<const u32x2*>(scl + (h * R + srow[i]) * sst + 8 * ql);
 #pragma unroll
       for (int i = 0; i < TPW; i++)
 #pragma unroll
@@ -301,7 +331,7 @@ __global__ __launch_bounds__(kMThreads) void k_qmv_id_mma(MmaArgs a) {
         for (int i = 0; i < TPW; i++)
 #pragma unroll
           for (int h = 0; h < NG; h++) {
-            const uint32_t sw = (u & 2) ? Qd.s[i][h].y : Qd.s[i][h].x;
+            const uint32_t sw = (u & 2) ? sq[i][h].y : sq[i][h].x;
             // d, times 1/16 for the Q4_0 codes' 16 (n - 8), times 2^-kXShift for the inputs
             const float sc = h2f((u & 1) ? sw >> 16 : sw) * (FMT == MQ4 ? 0x1p-34f : 0x1p-30f);
 #pragma unroll
@@ -310,8 +340,8 @@ __global__ __launch_bounds__(kMThreads) void k_qmv_id_mma(MmaArgs a) {
       }
     };
 
-    for (int kb0 = 0; kb0 < nb; kb0 += a.kc) {
-      const int kcb = min(a.kc, nb - kb0);  // a multiple of 4, as nb and kc are
+    for (int kb0 = 0; kb0 < nb; kb0 += kcp) {
+      const int kcb = min(kcp, nb - kb0);  // a multiple of 4, as nb and kcp are
       const int nq = kcb >> 2;
       const int q0 = ks < KS ? nq * ks / KS : 0, q1 = ks < KS ? nq * (ks + 1) / KS : 0;
       Quad QA, QB;
@@ -351,6 +381,32 @@ __global__ __launch_bounds__(kMThreads) void k_qmv_id_mma(MmaArgs a) {
                       (lb[5] & 0xFFFF0000u) | (lb[4] >> 16), (lb[7] & 0xFFFF0000u) | (lb[6] >> 16)};
           }
         }
+      }
+      // stage the pass's scales for the chunk: per tensor, row r's kcb scales as 8-byte pieces
+      // (4 blocks each), consecutive pieces of a row to consecutive threads; rows past N read
+      // zeros
+      {
+        const int spr = kcb >> 2, njobs = R * spr;
+#pragma unroll
+        for (int h = 0; h < NG; h++)
+          for (int jb0 = 0; jb0 < njobs; jb0 += kJobs * kMThreads) {
+            u32x2 v[kJobs];
+#pragma unroll
+            for (int r = 0; r < kJobs; r++) {
+              const int jb = jb0 + r * kMThreads + tid;
+              const int row = jb / spr, pc = jb - row * spr, n = ta * 16 + row;
+              const uint32_t off = jb < njobs && n < N ? (uint32_t)n * (uint32_t)nb * 2u + (uint32_t)(kb0 + 4 * pc) * 2u : kOob;
+              v[r] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs[h], off, 0, 0));
+            }
+#pragma unroll
+            for (int r = 0; r < kJobs; r++) {
+              const int jb = jb0 + r * kMThreads + tid;
+              if (jb < njobs) {
+                const int row = jb / spr, pc = jb - row * spr;
+                *reinterpret_cast<u32x2*>(scl + (h * R + row) * sst + 8 * pc) = v[r];
+              }
+            }
+          }
       }
       __syncthreads();
       // Quads in pairs, both issued before either is used: a pair covers whole 128-byte lines
@@ -444,12 +500,13 @@ int launch_id_mma(int fmt, const void* w, const void* w_up, int E, int64_t N, in
   const int TS = T * top_k;
   const bool gu = w_up != nullptr;
   const int fixed = mma_table_bytes(E, TS);
-  int64_t kc = (kMMaxLds - fixed) / kXBlk;
-  kc &= ~int64_t(3);
-  if (kc > nb) kc = nb < 4 ? 4 : nb;
-  // the staging area also holds the K-split partial sums
+  // the staging area: all the LDS the slot table leaves, in units of one block's inputs (a
+  // pass takes its chunks' inputs and scales from it, and the K-split partial sums at the end)
+  const int64_t kc = (kMMaxLds - fixed) / kXBlk;
   const int64_t xbytes = std::max<int64_t>(kc * kXBlk, mma_part_bytes(fmt == BQM_Q4_0, gu));
   if (fixed + xbytes > kMMaxLds) return BQM_E_UNSUPPORTED;
+  // room for a chunk of 4 blocks with the scales of the largest pass
+  if (kc * kXBlk < 4 * kXBlk + 24 * mma_max_rows(fmt == BQM_Q4_0, gu)) return BQM_E_UNSUPPORTED;
   Layout L;
   layout_of(fmt, (int64_t)E * N, K, &L);
   const uint8_t* codes = static_cast<const uint8_t*>(w);

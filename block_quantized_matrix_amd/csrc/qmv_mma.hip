@@ -220,8 +220,15 @@ __global__ __launch_bounds__(kMThreads) void k_qmv_id_mma(MmaArgs a) {
     // the longest that leaves room for both, evened out over the chunks of K; the stride is
     // twice an odd number of words, so that the 16 rows of one 8-byte read meet 32 distinct
     // banks.
+    //
+    // The inputs are staged compactly: per block and bf16 part, the c slots' pieces of the 4
+    // k-groups ([k-group][slot], 16 bytes each), then one zero piece, which the lanes of the
+    // MFMA rows past c read.  (All 16 rows staged, a group of a few slots spent most of the
+    // staging on zeros, and the chunks of K it fitted in were three times as many.)
     const int R = nt * 16;
-    int kcp = (a.kc * kXBlk - 16 * NG * R) / (kXBlk + 2 * NG * R);
+    const int xpp = (4 * c + 1) * 16;  // bytes per block and part
+    const int bxb = 2 * xpp;           // staged input bytes per block
+    int kcp = (a.kc * kXBlk - 16 * NG * R) / (bxb + 2 * NG * R);
     kcp = max(4, kcp & ~3);
     {
       const int nch = (nb + kcp - 1) / kcp;
@@ -230,7 +237,10 @@ __global__ __launch_bounds__(kMThreads) void k_qmv_id_mma(MmaArgs a) {
     int sdw = kcp / 2 + 2;
     if (((sdw >> 1) & 1) == 0) sdw += 2;
     const int sst = 4 * sdw;
-    char* scl = xl + kcp * kXBlk;
+    char* scl = xl + kcp * bxb;
+    // this lane's input piece (slot j, k-group q) in a block's first part (the second is xpp
+    // bytes on); lanes past the group's slots read the zero piece
+    const int xo = j < c ? (q * c + j) * 16 : 4 * c * 16;
     int srow[TPW];  // this lane's row in the scale area, per tile (tiles it does not have: row 0)
 #pragma unroll
     for (int i = 0; i < TPW; i++) srow[i] = i < mt ? (tsi * TPW + i) * 16 + j : 0;
@@ -313,8 +323,9 @@ __global__ __launch_bounds__(kMThreads) void k_qmv_id_mma(MmaArgs a) {
 #pragma unroll
       for (int u = 0; u < 4; u++) {
         const int bl = 4 * ql + u;
-        const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(xl + (bl * 128 + lane) * 16);
-        const bf16x8 alo = *reinterpret_cast<const bf16x8*>(xl + (bl * 128 + 64 + lane) * 16);
+        const char* xb = xl + bl * bxb + xo;
+        const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(xb);
+        const bf16x8 alo = *reinterpret_cast<const bf16x8*>(xb + xpp);
         // every tile of the set, also those past the pass's end (whose codes and scales read
         // as zeros): no branches, so the tiles' products and sums interleave
         f32x4 d[TPW][NG];
@@ -348,16 +359,22 @@ __global__ __launch_bounds__(kMThreads) void k_qmv_id_mma(MmaArgs a) {
       // the first quad's weights do not depend on the inputs: fetch them across the staging
       issue(QA, kb0 + 4 * q0, q0 < q1);
       __syncthreads();  // the previous chunk's inputs are no longer read
-      // stage the group's inputs for blocks kb0 .. kb0 + kcb: per (block, lane) both parts;
-      // a thread's jobs in rounds of kJobs, each round's loads in flight together
-      for (int jb0 = 0; jb0 < kcb * 64; jb0 += kJobs * kMThreads) {
+      // stage the group's inputs for blocks kb0 .. kb0 + kcb: per (block, k-group, slot) both
+      // parts, and each block's zero pieces; a thread's jobs in rounds of kJobs, each round's
+      // loads in flight together
+      for (int b = tid; b < kcb; b += kMThreads) {
+        *reinterpret_cast<u32x4*>(xl + b * bxb + 4 * c * 16) = u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(xl + b * bxb + xpp + 4 * c * 16) = u32x4{0u, 0u, 0u, 0u};
+      }
+      const int njx = kcb * 4 * c;
+      for (int jb0 = 0; jb0 < njx; jb0 += kJobs * kMThreads) {
         f32x4 v[kJobs][2];
 #pragma unroll
         for (int r = 0; r < kJobs; r++) {
           const int jb = jb0 + r * kMThreads + tid;
-          const int bl = jb >> 6, ln = jb & 63, si = ln & 15, sq = ln >> 4;
+          const int bl = jb / (4 * c), pq = jb - bl * 4 * c, sq = pq / c, si = pq - sq * c;
           v[r][0] = v[r][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-          if (jb < kcb * 64 && si < c) {
+          if (jb < njx) {
             const float* xr = a.x + s_xoff[si] + (int64_t)(kb0 + bl) * 32;
             v[r][0] = *reinterpret_cast<const f32x4*>(xr + (FMT == MQ4 ? 4 * sq : 8 * sq));
             v[r][1] = *reinterpret_cast<const f32x4*>(xr + (FMT == MQ4 ? 16 + 4 * sq : 8 * sq + 4));
@@ -366,17 +383,17 @@ __global__ __launch_bounds__(kMThreads) void k_qmv_id_mma(MmaArgs a) {
 #pragma unroll
         for (int r = 0; r < kJobs; r++) {
           const int jb = jb0 + r * kMThreads + tid;
-          if (jb < kcb * 64) {
-            const int bl = jb >> 6, ln = jb & 63;
+          if (jb < njx) {
+            const int bl = jb / (4 * c), pq = jb - bl * 4 * c;  // pq = k-group * c + slot
             const float f[8] = {v[r][0].x, v[r][0].y, v[r][0].z, v[r][0].w,
                                 v[r][1].x, v[r][1].y, v[r][1].z, v[r][1].w};
             uint32_t hb[8], lb[8];
 #pragma unroll
             for (int k = 0; k < 8; k++) split(f[k], hb[k], lb[k]);
-            *reinterpret_cast<u32x4*>(xl + (bl * 128 + ln) * 16) =
+            *reinterpret_cast<u32x4*>(xl + bl * bxb + pq * 16) =
                 u32x4{(hb[1] & 0xFFFF0000u) | (hb[0] >> 16), (hb[3] & 0xFFFF0000u) | (hb[2] >> 16),
                       (hb[5] & 0xFFFF0000u) | (hb[4] >> 16), (hb[7] & 0xFFFF0000u) | (hb[6] >> 16)};
-            *reinterpret_cast<u32x4*>(xl + (bl * 128 + 64 + ln) * 16) =
+            *reinterpret_cast<u32x4*>(xl + bl * bxb + xpp + pq * 16) =
                 u32x4{(lb[1] & 0xFFFF0000u) | (lb[0] >> 16), (lb[3] & 0xFFFF0000u) | (lb[2] >> 16),
                       (lb[5] & 0xFFFF0000u) | (lb[4] >> 16), (lb[7] & 0xFFFF0000u) | (lb[6] >> 16)};
           }
@@ -506,7 +523,7 @@ int launch_id_mma(int fmt, const void* w, const void* w_up, int E, int64_t N, in
   const int64_t xbytes = std::max<int64_t>(kc * kXBlk, mma_part_bytes(fmt == BQM_Q4_0, gu));
   if (fixed + xbytes > kMMaxLds) return BQM_E_UNSUPPORTED;
   // room for a chunk of 4 blocks with the scales of the largest pass
-  if (kc * kXBlk < 4 * kXBlk + 24 * mma_max_rows(fmt == BQM_Q4_0, gu)) return BQM_E_UNSUPPORTED;
+  if (kc * kXBlk < 4 * (kXBlk + 32) + 24 * mma_max_rows(fmt == BQM_Q4_0, gu)) return BQM_E_UNSUPPORTED;
   Layout L;
   layout_of(fmt, (int64_t)E * N, K, &L);
   const uint8_t* codes = static_cast<const uint8_t*>(w);

@@ -42,9 +42,11 @@ def _run_id(fmt, Wi, E, N, K, ids, X, xts, xss):
 # (T, E, N, K, top_k): 16-slot groups of a skewed router; a ragged last row tile (N not a
 # multiple of 16); experts with more than 16 slots (every token on a few experts); one tile
 # per workgroup (K split 16 ways), a few (split 8 or 16 ways), many (split 2 ways); a ragged
-# tile with 4-slot groups; long K in several staged chunks
+# tile with 4-slot groups; long K in several staged chunks; a 15-slot group (one slot is
+# padding) over long K with four tiles per pass (its inputs and scales in four chunks)
 CASES = [(16, 32, 96, 4096, 8), (8, 6, 130, 1152, 3), (64, 4, 40, 256, 2), (8, 2, 16, 2048, 2),
-         (16, 4, 4096, 1024, 2), (16, 40, 4096, 512, 8), (12, 5, 200, 1536, 4), (16, 4, 64, 16384, 2)]
+         (16, 4, 4096, 1024, 2), (16, 40, 4096, 512, 8), (12, 5, 200, 1536, 4), (16, 4, 64, 16384, 2),
+         (16, 1, 16384, 8192, 1)]
 
 
 @pytest.mark.parametrize("fmt", FMTS)

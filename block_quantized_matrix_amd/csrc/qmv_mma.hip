@@ -74,8 +74,9 @@ struct MmaArgs {
 // groups of 3 ints, at most TS), then the staging area: a pass's inputs and scales chunk by
 // chunk, and its K-split partial sums at the end.
 __host__ __device__ inline int mma_table_bytes(int E, int TS) { return ((E + 1 + 4 * TS) * 4 + 15) & ~15; }
-// Tiles per wave in a pass (their loads, two quads in flight, and sums fit 128 registers).
-__host__ __device__ constexpr int mma_tpw(bool q4, bool gu) { return q4 ? (gu ? 2 : 4) : (gu ? 1 : 2); }
+// Tiles per wave in a pass (their loads, two units of 128 bytes per row in flight, and sums
+// fit 128 registers).
+__host__ __device__ constexpr int mma_tpw(bool q4, bool gu) { return (void)q4, gu ? 1 : 2; }
 // Rows of a pass's scales at most, over both tensors: every wave's tiles.
 __host__ __device__ constexpr int mma_max_rows(bool q4, bool gu) { return kMWaves * mma_tpw(q4, gu) * 16 * (gu ? 2 : 1); }
 // The K-split partial sums at most: every wave but those of the first share, TPW tiles of
@@ -228,11 +229,12 @@ __global__ __launch_bounds__(kMThreads) void k_qmv_id_mma(MmaArgs a) {
     const int R = nt * 16;
     const int xpp = (4 * c + 1) * 16;  // bytes per block and part
     const int bxb = 2 * xpp;           // staged input bytes per block
+    constexpr int KQ = FMT == MQ4 ? 8 : 4;  // blocks per 128 bytes of a row: chunks start on lines
     int kcp = (a.kc * kXBlk - 16 * NG * R) / (bxb + 2 * NG * R);
-    kcp = max(4, kcp & ~3);
+    kcp = max(KQ, kcp & ~(KQ - 1));
     {
       const int nch = (nb + kcp - 1) / kcp;
-      kcp = min(kcp, (((nb + nch - 1) / nch) + 3) & ~3);
+      kcp = min(kcp, (((nb + nch - 1) / nch) + KQ - 1) & ~(KQ - 1));
     }
     int sdw = kcp / 2 + 2;
     if (((sdw >> 1) & 1) == 0) sdw += 2;
@@ -353,11 +355,27 @@ __global__ __launch_bounds__(kMThreads) void k_qmv_id_mma(MmaArgs a) {
 
     for (int kb0 = 0; kb0 < nb; kb0 += kcp) {
       const int kcb = min(kcp, nb - kb0);  // a multiple of 4, as nb and kcp are
-      const int nq = kcb >> 2;
-      const int q0 = ks < KS ? nq * ks / KS : 0, q1 = ks < KS ? nq * (ks + 1) / KS : 0;
-      Quad QA, QB;
-      // the first quad's weights do not depend on the inputs: fetch them across the staging
-      issue(QA, kb0 + 4 * q0, q0 < q1);
+      // The chunk's quads in units of 128 bytes of each row (Q4_0: two quads, issued together),
+      // the units split into KS shares; a wave keeps two units of loads in registers and issues
+      // the next into each as soon as its products are taken, so one unit is always in flight.
+      // (Quads issued one ahead of their products asked for the second half of a line while
+      // the first was still in flight, and more lines crossed HBM twice: 1.45x -> 1.66x the
+      // algorithmic bytes on the MoE layer at T = 16.)
+      constexpr int UQ = FMT == MQ4 ? 2 : 1;
+      const int nq = kcb >> 2, nu = (nq + UQ - 1) / UQ;
+      const int u0 = ks < KS ? nu * ks / KS : 0, u1 = ks < KS ? nu * (ks + 1) / KS : 0;
+      Quad UA[UQ], UB[UQ];
+      auto issue_unit = [&](Quad* U, int un, bool live) {
+#pragma unroll
+        for (int sq = 0; sq < UQ; sq++) issue(U[sq], kb0 + 4 * (UQ * un + sq), live && UQ * un + sq < nq);
+      };
+      auto consume_unit = [&](Quad* U, int un) {
+#pragma unroll
+        for (int sq = 0; sq < UQ; sq++)
+          if (UQ * un + sq < nq) consume(U[sq], UQ * un + sq);
+      };
+      // the first unit's weights do not depend on the inputs: fetch them across the staging
+      issue_unit(UA, u0, u0 < u1);
       __syncthreads();  // the previous chunk's inputs are no longer read
       // stage the group's inputs for blocks kb0 .. kb0 + kcb: per (block, k-group, slot) both
       // parts, and each block's zero pieces; a thread's jobs in rounds of kJobs, each round's
@@ -426,16 +444,14 @@ __global__ __launch_bounds__(kMThreads) void k_qmv_id_mma(MmaArgs a) {
           }
       }
       __syncthreads();
-      // Quads in pairs, both issued before either is used: a pair covers whole 128-byte lines
-      // of each row.  Issuing one quad ahead of its products instead requested the second
-      // half of a line while the first was still in flight, and more lines crossed HBM twice
-      // (measured on the MoE layer at T = 16: reads 1.66x -> 1.45x the algorithmic bytes,
-      // 66.7 -> 64.4 us per call; gate+up 102.9 -> 98.4 us).
-      for (int qd = q0; qd < q1; qd += 2) {
-        if (qd > q0) issue(QA, kb0 + 4 * qd, true);  // the first pair's was issued above
-        issue(QB, kb0 + 4 * (qd + 1), qd + 1 < q1);
-        consume(QA, qd);
-        if (qd + 1 < q1) consume(QB, qd + 1);
+      if (u0 + 1 < u1) issue_unit(UB, u0 + 1, true);
+      for (int un = u0; un < u1; un += 2) {
+        consume_unit(UA, un);
+        if (un + 2 < u1) issue_unit(UA, un + 2, true);
+        if (un + 1 < u1) {
+          consume_unit(UB, un + 1);
+          if (un + 3 < u1) issue_unit(UB, un + 3, true);
+        }
       }
     }
 

@@ -981,9 +981,6 @@ void allow_lds(Kern k, size_t bytes) {
 #ifndef BQM_P1_P
 #define BQM_P1_P 4  // blocks in flight per lane (Q4_0; Q8_0 blocks are twice as long: half)
 #endif
-#ifndef BQM_CHAIN_MM_WIDE
-#define BQM_CHAIN_MM_WIDE 8  // batch classes from this one up: 2 rows per lane, 8 waves
-#endif
 constexpr int kP1StaticLds = 1024;                   // reserved for the kernel's own __shared__
 constexpr int kP1MaxLds = 160 * 1024 - kP1StaticLds;  // dynamic LDS of a chain launch
 
@@ -995,29 +992,30 @@ int m_class(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
 // Ring depth: a step of a wider batch computes longer, so fewer steps in flight cover the
 // memory latency, and its registers go to the batch's sums.  Batches 1 and 4 take two
 // rows per lane (two blocks per step), where a shallower ring is best (measured: also less
-// padding at the end of each GEMV's share; batch 4 with two steps would spill).
+// padding at the end of each GEMV's share; batch 4 with two steps would spill); batch 8
+// keeps one step, so that its sums fit 16 waves per CU.
 template <int FMT, int MM>
 constexpr int chain_ring() {
   if (MM == 1) return FMT == FQ4 ? 2 : 1;
-  if (MM == 4) return 1;
+  if (MM == 4 || MM >= 8) return 1;
   return (FMT == FQ4 ? BQM_P1_P : BQM_P1_P / 2) / (MM >= 4 && FMT == FQ4 ? 2 : 1);
 }
-// log2 of the waves per workgroup: 16 waves, or 8 for the widest batch, whose sums need
-// more than the 128 registers a lane has when 16 waves share a CU (measured on the 27B
-// Q8_0 pass: M = 4 is fastest with 16 waves and one row per lane, M = 8 with 8 waves and
-// two rows per lane).  The indexed forms (mode 1, 2) at batch classes 1 and 2 take 8 waves:
-// their calls are small (T = 1: 28 MB per MoE projection, ≈ 110 KB per workgroup) and a
-// lighter workgroup starts and drains sooner (per call on the 128-expert MoE layer, 8 against
-// 16 waves: T = 1 qmv_id 13.5 / 15.4 us, gate+up 18.8 / 18.8; T = 2 24.2 / 23.9, gate+up
-// 32.8 / 34.8; class 4 keeps 16: T = 4 38.2 / 37.4, gate+up 61.2 / 57.3)
-constexpr int chain_lgw(int mm, int mode = 0) {
-  return (mode != 0 && mm <= 2) || mm >= BQM_CHAIN_MM_WIDE ? 3 : 4;
-}
+// log2 of the waves per workgroup: 16 waves.  The indexed forms (mode 1, 2) at batch
+// classes 1 and 2 take 8 waves: their calls are small (T = 1: 28 MB per MoE projection,
+// ≈ 110 KB per workgroup) and a lighter workgroup starts and drains sooner (per call on the
+// 128-expert MoE layer, 8 against 16 waves: T = 1 qmv_id 13.5 / 15.4 us, gate+up 18.8 /
+// 18.8; T = 2 24.2 / 23.9, gate+up 32.8 / 34.8; class 4 keeps 16: T = 4 38.2 / 37.4,
+// gate+up 61.2 / 57.3).
+constexpr int chain_lgw(int mm, int mode = 0) { return mode != 0 && mm <= 2 ? 3 : 4; }
 // rows per lane: one read of the staged inputs serves the codes of two rows, halving the
 // LDS reads per weight byte (batch 1: 8 bytes of x per Q4_0 code byte otherwise; measured
-// +6% on the 27B Q4_0 pass, +6% on the 27B Q8_0 pass at M = 4) and, for the widest batch,
-// sharing the input reads of eight sums; batch 2 keeps one row per lane
-constexpr int chain_r(int mm) { return mm == 2 ? 1 : 2; }
+// +6% on the 27B Q4_0 pass, +6% on the 27B Q8_0 pass at M = 4).  Batch 2 keeps one row per
+// lane, and so does batch 8: two rows of eight sums need more than the 128 registers a lane
+// has when 16 waves share a CU.  Measured on the 27B Q8_0 pass at M = 8, one row per lane,
+// one step in flight and 16 waves against two rows, two steps and 8 waves: the dependent
+// pass 2.10 -> 2.22 TB/s (the waits' ramps are shorter with more waves), the same GEMVs
+// streamed without waits 3.05 -> 2.88 TB/s (two rows share each input read).
+constexpr int chain_r(int mm) { return mm == 2 || mm >= 8 ? 1 : 2; }
 // rows per lane of a mode: the gate+up form always pairs two rows
 constexpr int mode_r(int mm, int mode) { return mode == 2 ? 2 : chain_r(mm); }
 template <int FMT, int MODE>

@@ -520,6 +520,10 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
   __shared__ int lds_units;
   __shared__ int scan_w[2 * NW];
   Stage ibase;  // indexed form: expert 0, bases
+  // the id of this workgroup's first slot in the padding fill below, read now, together with
+  // the ids the slot sort reads (after the sort it would be a memory round trip more)
+  int fill_e0 = 0;
+  if constexpr (IDX) fill_e0 = (int)blockIdx.x < TS ? a.ix.ids[blockIdx.x] : 0;
   if constexpr (IDX) {
     // the slots grouped by expert, groups of at most MM slots (srt is first read after the
     // barrier below)
@@ -559,14 +563,24 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
     // lb = (b mod 8) * (grid / 8) + b / 8 gives each XCD one contiguous range.  The groups
     // of an expert are consecutive units, so the workgroups streaming the same expert rows
     // for its successive groups share an L2 and the rows cross HBM about once.
+    // (floor(lb * rows / G) as q lb + floor(r lb / G) with rows = q G + r: small 32-bit
+    // divisions instead of 64-bit ones, which take a long software sequence)
     const int64_t rows = (int64_t)n_units * a.one.N;
     const int G = (int)gridDim.x, b = (int)blockIdx.x;
     const int lb = G % 8 == 0 ? (b % 8) * (G / 8) + b / 8 : b;
-    flo = (int64_t)lb * rows / G;
-    fhi = (int64_t)(lb + 1) * rows / G;
+    const int64_t q = rows / G;  // one 64-bit division, uniform
+    const int rr = (int)(rows - q * G);
+    flo = q * lb + (rr * lb) / G;
+    fhi = q * (lb + 1) + (rr * (lb + 1)) / G;
     if (fhi > flo) {
-      u_begin = (int)(flo / a.one.N);
-      u_end = (int)((fhi - 1) / a.one.N) + 1;
+      const int N = (int)a.one.N;
+      if (fhi <= 0x7FFFFFFF) {
+        u_begin = (int)flo / N;
+        u_end = ((int)fhi - 1) / N + 1;
+      } else {
+        u_begin = (int)(flo / N);
+        u_end = (int)((fhi - 1) / N) + 1;
+      }
     } else {
       u_end = 0;
     }
@@ -576,7 +590,7 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
     // zeros, an id >= E NaN; with K = 0 every valid slot's sums are empty (zeros)
     const int N = (int)a.one.N;
     for (int ts = blockIdx.x; ts < TS; ts += gridDim.x) {
-      const int e = a.ix.ids[ts];
+      const int e = ts == (int)blockIdx.x ? fill_e0 : a.ix.ids[ts];
       const bool valid = e >= 0 && e < a.ix.E;
       if (valid && n_units > 0) continue;
       const float v = valid || e < 0 ? 0.0f : __builtin_nanf("");

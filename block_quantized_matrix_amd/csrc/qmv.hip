@@ -757,6 +757,7 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
   // x.  Every wave enters the same (unit, chunk)s, in order.  False when
   // no unit is left or a wait failed.
   auto enter = [&]() -> bool {
+    bool waited = false;  // a device-wide wait, which ends with a workgroup barrier, was passed
     for (;;) {
       if (cc + 1 < sc.nchunks) {
         ++cc;
@@ -769,6 +770,7 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
       if (sc.wait && gc > 0 && a.sync) {
         alive = grid_barrier<LOADS>(a.sync, ++epoch, &lds_ok);
         if (!alive) return false;
+        waited = true;
       }
       if (sc.nrows > 0) break;
       cc = sc.nchunks - 1;  // none of its rows here: skip its chunks
@@ -781,7 +783,9 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
     cj = sc.start - ct * sc.ns;
     cg = lane & (kG - 1);
     clg = lane >> kLg2G;
-    __syncthreads();
+    // every wave is done with the staged inputs before they are replaced (after a device-wide
+    // wait they are already)
+    if (!waited) __syncthreads();
     // x comes through agent-coherent loads (other workgroups may have written it), 16
     // bytes per lane: a pass of a wave stages 8 whole blocks of each input.  Inputs m >= M
     // are staged as zeros (their results are not stored).

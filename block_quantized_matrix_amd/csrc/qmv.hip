@@ -427,31 +427,32 @@ __device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v) {
 // at least LOADS loads (its step's refill), and vector memory operations complete in issue
 // order, so vmcnt <= LOADS suffices, while the weights prefetched for the next GEMV may
 // stay in flight.
+// `lds_ok` is set once per launch and only ever cleared.  The error word is read only while
+// a flag keeps a thread waiting, every 64th poll, so that each poll costs one memory round
+// trip and a passing workgroup none at all (reading it after every wait, and after every
+// poll, cost the dependent 27B Q4_0 pass several percent); after a timeout the others
+// still leave within 64 polls of their next wait, and the word reports the launch invalid.
 template <int LOADS>
 __device__ __forceinline__ bool grid_barrier(uint32_t* ws, uint32_t epoch, bool* lds_ok) {
   static_assert(LOADS >= 1 && LOADS <= 15, "vmcnt field");
   __builtin_amdgcn_s_waitcnt(0x0F70 | LOADS);  // vmcnt(LOADS); expcnt, lgkmcnt: no wait
   __syncthreads();
   uint32_t* flags = ws + kChainHeaderWords;
-  if (threadIdx.x == 0) {
-    st_agent(flags + blockIdx.x * kFlagStrideWords, epoch);
-    *lds_ok = true;
-  }
-  __syncthreads();
+  if (threadIdx.x == 0) st_agent(flags + blockIdx.x * kFlagStrideWords, epoch);
   // every workgroup waits for every flag (one thread per flag)
   for (uint32_t b = threadIdx.x; b < gridDim.x; b += blockDim.x) {
     uint32_t spins = 0;
     // a workgroup past this barrier may already have arrived at the next: epochs only grow
     while ((int32_t)(ld_agent(flags + b * kFlagStrideWords) - epoch) < 0) {
-      if (++spins > kSpinLimit || ld_agent(ws + 2) != 0) { st_agent(ws + 2, 1u); *lds_ok = false; break; }
+      if ((++spins & 63u) == 0 && (spins > kSpinLimit || ld_agent(ws + 2) != 0)) {
+        st_agent(ws + 2, 1u);
+        *lds_ok = false;
+        break;
+      }
       __builtin_amdgcn_s_sleep(1);
     }
   }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    if (blockIdx.x == 0) st_agent(ws, epoch);  // the epoch the next launch starts from
-    *lds_ok = *lds_ok && ld_agent(ws + 2) == 0;
-  }
+  if (threadIdx.x == 0 && blockIdx.x == 0) st_agent(ws, epoch);  // the epoch the next launch starts from
   __syncthreads();
   return *lds_ok;
 }
@@ -551,6 +552,7 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
   }
   if (tid < NW) done[tid] = 0;
   if (tid == 0 && a.sync) lds_epoch = ld_agent(a.sync);  // stable until all have arrived once
+  if (tid == 0) lds_ok = true;
   __syncthreads();
   uint32_t epoch = a.sync ? lds_epoch : 0u;
   // units of work: the GEMVs, or (indexed form) the groups; none when K = 0

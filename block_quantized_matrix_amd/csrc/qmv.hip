@@ -25,9 +25,12 @@
 // split between waves is finished through LDS in wave order.  No atomics on data; the
 // summation order is fixed for a given launch shape.
 #include "bqm_internal.h"
+#include "mma_ops.h"
 #include "slot_groups.h"
 
+#include <algorithm>
 #include <atomic>
+#include <type_traits>
 #include <mutex>
 #include <unordered_map>
 #include <vector>
@@ -329,6 +332,7 @@ struct Stage {
   const float* x;
   float* y;
   int nrows, nb, nbc, kb0, ns, S, start, end, M, xstride, ystride, nchunks, lo;
+  int th;                   // matrix-core form: rows per tile
   bool wait, first, last;
 };
 
@@ -982,6 +986,384 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
   }
 }
 
+// ---- the chain on the matrix cores (batches of 3 to 8 inputs) ----------------------------
+// From three inputs on, the fp32 FMAs of a block (one per code and input) outgrow what the
+// vector ALU issues beside the stream (27B Q8_0 pass at M = 8: 12 lane operations per weight,
+// 27 % of HBM).  This form takes the products to the matrix cores, as the expert-indexed
+// form does: every 32-weight block of 16 rows goes through v_mfma_f32_16x16x32_bf16 twice (the
+// two bf16 parts of the inputs) for all M inputs at once, and the vector work per weight (the
+// code conversion and the block-scale FMA) does not grow with M.  Operands and exactness as
+// in mma_ops.h: codes exact, inputs in two bf16 parts of x * 2^30, blocks in ascending order
+// per row (each block sum scaled by d and added in fp32).
+//
+// The chain's structure is kept: per GEMV a workgroup's rows (the same block-balanced split),
+// the device-wide barrier at waits, the inputs staged in LDS per (GEMV, chunk of K), a
+// register ring that runs ahead across GEMVs and chunks.  What changes is the step: a
+// 16-row tile and 128 bytes of each of its rows (Q4_0 eight blocks, Q8_0 four), two 16-byte
+// code loads per lane (lane group q: bytes 16q.. of each 64-byte piece) and one load of the
+// row's scales for the step's blocks, exchanged between the lane groups into the MFMA's
+// operand layout (mma::exchange).  A wave's steps are a contiguous range of the tile-major
+// step sequence, as in the vector form; a tile split between waves is finished in LDS in
+// wave order.  The inputs are staged compactly, per block and part the M inputs' 16-byte
+// pieces of each k-group ([k-group][input]) and one zero piece, which the MFMA rows past M
+// read.  K must be a multiple of 128 (Q8_0) or 256 (Q4_0), so that steps and chunks hold whole
+// 128-byte pieces of a row.
+constexpr int kMcRows = 16;                              // rows of a tile (the MFMA's columns)
+constexpr int kMcMaxM = 8;                               // inputs at most
+constexpr int kMcPartBytes = kP1Waves * 2 * kMcRows * kMcMaxM * 4;  // split-tile parts
+constexpr int kMcClassBit = 0x100;                       // header word 7: a plan for this form
+__host__ __device__ inline int mc_blk_bytes(int M) { return 32 * (4 * M + 1); }
+__host__ __device__ inline ChainLds chain_lds_mc(int n, int M, int pacc_rows, int kc) {
+  ChainLds L;
+  L.part = (n * 64 + 15) & ~15;
+  L.done = L.part + kMcPartBytes;
+  L.pacc = L.done + kP1Waves * 4;
+  L.x = L.pacc + ((pacc_rows * kMcMaxM * 4 + 15) & ~15);
+  L.total = L.x + kc * mc_blk_bytes(M);
+  return L;
+}
+
+// The chunk-dependent values of a stage: steps of 128 bytes per row (UB blocks), the
+// waves' equal contiguous ranges of the tile-major step sequence.  The rows are cut into the
+// fewest tiles of at most 16, all but the last of th rows each, th as even as it gets (20
+// rows: two of 10, not 16 and 4), so that the waves' steps carry equal shares of the rows.
+template <int UB>
+__device__ __forceinline__ void stage_chunk_mc(int c, int kc, int wave, int wait, Stage& s) {
+  s.kb0 = c * kc;
+  s.nbc = min(kc, s.nb - s.kb0);
+  s.first = c == 0;
+  s.last = c == s.nchunks - 1;
+  s.wait = wait != 0 && c == 0;
+  s.ns = s.nbc / UB;
+  const int ntiles = (s.nrows + kMcRows - 1) / kMcRows;
+  s.th = ntiles > 0 ? (s.nrows + ntiles - 1) / ntiles : kMcRows;
+  s.S = ntiles * s.ns;
+  s.start = (wave * s.S) >> 4;
+  s.end = ((wave + 1) * s.S) >> 4;
+}
+
+template <int FMT, int P>
+__global__ __launch_bounds__(1024) void k_qmv_chain_mc(ChainArgs a) {
+  constexpr int NW = 16, NT = 1024;
+  extern __shared__ float4 smem[];
+  constexpr int CB = FMT == FQ4 ? 16 : 32;     // code bytes per block
+  constexpr int UB = FMT == FQ4 ? 8 : 4;       // blocks per step: 128 bytes of a row
+  constexpr uint32_t kOob = 0x80000000u;       // lane offset past every descriptor: reads 0
+  constexpr int LOADS = 3;                     // loads per step: two of codes, one of scales
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  using ScaleRegs = typename std::conditional<FMT == FQ4, u32x4, u32x2>::type;
+  __shared__ bool lds_ok;
+  __shared__ uint32_t lds_epoch;
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (a.sync && (a.sync[3] != (uint32_t)a.n || a.sync[4] != (uint32_t)(FMT == FQ4 ? BQM_Q4_0 : BQM_Q8_0) ||
+                 (a.sync[7] & kMcClassBit) == 0)) {
+    if (blockIdx.x == 0 && tid == 0)
+      __hip_atomic_store(a.sync + 2, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kc = a.sync ? (int)a.sync[5] : a.kc;
+  const int pacc_rows = a.sync ? (int)a.sync[6] : a.pacc_rows;
+  const int M = a.sync ? (int)a.sync[8] : a.one.M;  // inputs of every GEMV of the chain
+  const ChainLds ly = chain_lds_mc(a.n, M, pacc_rows, kc);
+  char* lds = reinterpret_cast<char*>(smem);
+  StageRow* table = reinterpret_cast<StageRow*>(lds);
+  float* part = reinterpret_cast<float*>(lds + ly.part);
+  int* done = reinterpret_cast<int*>(lds + ly.done);
+  float* pacc = reinterpret_cast<float*>(lds + ly.pacc);
+  char* xl = lds + ly.x;
+  const int bxb = mc_blk_bytes(M), xpp = bxb / 2;  // staged bytes per block; per part
+  for (int i = tid; i < a.n; i += NT) {
+    const GemvDesc d = a.descs ? a.descs[i] : a.one;
+    table[i] = a.seg ? make_stage<FMT>(d, a.seg[2 * i], a.seg[2 * i + 1], kc)
+                     : make_stage<FMT>(d, 0, d.N * (d.K >> 5), kc);
+  }
+  if (tid < NW) done[tid] = 0;
+  if (tid == 0 && a.sync) lds_epoch = ld_agent(a.sync);
+  if (tid == 0) lds_ok = true;
+  __syncthreads();
+  uint32_t epoch = a.sync ? lds_epoch : 0u;
+  const int n_units = a.n;
+  // lane (j, q): row j of a tile (MFMA column), k-group / 16-byte piece q
+  const int j = lane & 15, q = lane >> 4;
+  // this lane's A-operand piece in a staged block: input j's k-group q, or the zero piece
+  const int xo = j < M ? (q * M + j) * 16 : 4 * M * 16;
+  auto load = [&](int i, int c, Stage& st) {
+    const StageRow r = table[i];
+    st.codes = reinterpret_cast<const uint8_t*>(uniform64(reinterpret_cast<uint64_t>(r.codes)));
+    st.scales = reinterpret_cast<const uint16_t*>(uniform64(reinterpret_cast<uint64_t>(r.scales)));
+    st.x = reinterpret_cast<const float*>(uniform64(reinterpret_cast<uint64_t>(r.x)));
+    st.y = reinterpret_cast<float*>(uniform64(reinterpret_cast<uint64_t>(r.y)));
+    st.nrows = __builtin_amdgcn_readfirstlane(r.nrows);
+    st.nb = __builtin_amdgcn_readfirstlane(r.nb);
+    st.M = __builtin_amdgcn_readfirstlane(r.M);
+    st.xstride = __builtin_amdgcn_readfirstlane(r.xstride);
+    st.ystride = __builtin_amdgcn_readfirstlane(r.ystride);
+    st.nchunks = __builtin_amdgcn_readfirstlane(r.nchunks);
+    st.lo = 0;
+    stage_chunk_mc<UB>(c, kc, wave, __builtin_amdgcn_readfirstlane(r.wait), st);
+  };
+
+  // ---------------- issue side: P steps ahead (as in the vector form) ----------------
+  int gi = -1, ci = 0;
+  Stage si;
+  si.nchunks = 0;
+  int it = 0, ij = 0, ireal = 0, ipad = 0;
+  __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(nullptr, (short)0, 0, 0x00020000);
+  __amdgpu_buffer_rsrc_t rs = rc;
+  uint32_t vc = kOob, vs = kOob;  // lane offsets of its row in the current tile
+  auto tile_offsets = [&]() {
+    const int row = it * si.th + j;
+    const bool ok = j < si.th && row < si.nrows;  // lanes past the tile's rows read zeros
+    vc = ok ? (uint32_t)j * si.nb * CB + q * 16 : kOob;
+    vs = ok ? (uint32_t)j * si.nb * 2 : kOob;
+  };
+  auto next_issue = [&]() {
+    ireal = 0;
+    ipad = 0;
+    while (ipad == 0) {
+      if (ci + 1 < si.nchunks) {
+        ++ci;
+      } else {
+        if (gi + 1 >= n_units) break;
+        ++gi;
+        ci = 0;
+      }
+      load(gi, ci, si);
+      if (si.nrows == 0) ci = si.nchunks - 1;
+      ireal = si.end - si.start;
+      ipad = (ireal + P - 1) / P * P;
+    }
+    if (ipad > 0) {
+      rc = __builtin_amdgcn_make_buffer_rsrc((void*)si.codes, (short)0,
+                                             (int)((uint32_t)si.nrows * si.nb * CB), 0x00020000);
+      rs = __builtin_amdgcn_make_buffer_rsrc((void*)si.scales, (short)0,
+                                             (int)((uint32_t)si.nrows * si.nb * 2), 0x00020000);
+      it = si.start / si.ns;
+      ij = si.start - it * si.ns;
+      tile_offsets();
+    }
+  };
+  next_issue();
+
+  auto issue = [&](u32x4 (&cq)[2], ScaleRegs& sq) {
+    const uint32_t live = ireal > 0 ? 1u : 0u;
+    // blocks before the step: the tile's rows, the chunk, the step in the tile
+    const uint32_t so = ((uint32_t)(it * si.th) * si.nb + (uint32_t)si.kb0 + (uint32_t)(ij * UB)) * live;
+    cq[0] = __builtin_amdgcn_raw_buffer_load_b128(rc, vc, so * CB, 0);
+    cq[1] = __builtin_amdgcn_raw_buffer_load_b128(rc, vc + 64, so * CB, 0);
+    if constexpr (FMT == FQ4) sq = __builtin_amdgcn_raw_buffer_load_b128(rs, vs, so * 2, 0);
+    else sq = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, vs, so * 2, 0));
+    if (ireal > 0) {
+      if (--ireal == 0) {
+        vc = vs = kOob;
+      } else if (++ij == si.ns) {
+        ij = 0;
+        ++it;
+        tile_offsets();
+      }
+    }
+    if (ipad > 0 && --ipad == 0) next_issue();
+  };
+
+  u32x4 ring_c[P][2];
+  ScaleRegs ring_s[P];
+#pragma unroll
+  for (int p = 0; p < P; p++) issue(ring_c[p], ring_s[p]);
+
+  // ---------------- consume side ----------------
+  int gc = -1, cc = 0;
+  int ct = 0, cj = 0, creal = 0, cpad = 0, creal0 = 1;
+  Stage sc;
+  sc.nchunks = 0;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  bool alive = true;
+  auto enter = [&]() -> bool {
+    bool waited = false;
+    for (;;) {
+      if (cc + 1 < sc.nchunks) {
+        ++cc;
+      } else {
+        if (gc + 1 >= n_units) return false;
+        ++gc;
+        cc = 0;
+      }
+      load(gc, cc, sc);
+      if (sc.wait && gc > 0 && a.sync) {
+        alive = grid_barrier<LOADS>(a.sync, ++epoch, &lds_ok);
+        if (!alive) return false;
+        waited = true;
+      }
+      if (sc.nrows > 0) break;
+      cc = sc.nchunks - 1;
+    }
+    creal = sc.end - sc.start;
+    creal0 = creal > 0 ? creal : 1;
+    __builtin_amdgcn_s_setprio(3);
+    cpad = (creal + P - 1) / P * P;
+    ct = sc.start / sc.ns;
+    cj = sc.start - ct * sc.ns;
+    if (!waited) __syncthreads();
+    // stage the chunk's inputs: per (block, k-group, input) both bf16 parts of 8 inputs,
+    // through agent-coherent loads (other workgroups may have written them); each block's
+    // zero pieces
+    const int nbc = sc.nbc;
+    for (int b = tid; b < nbc; b += NT) {
+      *reinterpret_cast<u32x4*>(xl + b * bxb + 4 * M * 16) = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(xl + b * bxb + xpp + 4 * M * 16) = u32x4{0u, 0u, 0u, 0u};
+    }
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(sc.x + (int64_t)sc.kb0 * kQK), (short)0,
+        (int)(((uint32_t)(M - 1) * (uint32_t)sc.xstride + (uint32_t)nbc * kQK) * 4u), 0x00020000);
+    // jobs (block, k-group, group of four inputs): a job's four loads fly together, and with
+    // at most 1024 jobs (the plan keeps kc so) the staging takes one memory round trip
+    const int MG = (M + 3) >> 2, njx = nbc * 4 * MG;
+#pragma unroll 1
+    for (int jb = tid; jb < njx; jb += NT) {
+      const int kq = jb & 3, t = jb >> 2;
+      const int bl = MG == 2 ? t >> 1 : t, m0 = MG == 2 ? 4 * (t & 1) : 0;
+      // k-group kq: Q4_0 positions 4kq..4kq+3 and 16+4kq..; Q8_0 8kq..8kq+7
+      const uint32_t o0 = ((uint32_t)bl * kQK + (FMT == FQ4 ? 4 * kq : 8 * kq)) * 4u;
+      char* dst = xl + bl * bxb + kq * M * 16;
+      f32x4 v[4][2];
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        v[r][0] = v[r][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (m0 + r < M) {
+          const uint32_t o = o0 + (uint32_t)(m0 + r) * (uint32_t)sc.xstride * 4u;
+          v[r][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, o, 0, 16));
+          v[r][1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  rx, o + (FMT == FQ4 ? 64u : 16u), 0, 16));
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        if (m0 + r < M) {
+          const float f[8] = {v[r][0].x, v[r][0].y, v[r][0].z, v[r][0].w,
+                              v[r][1].x, v[r][1].y, v[r][1].z, v[r][1].w};
+          u32x4 hi, lo;
+          mma::split8(f, hi, lo);
+          *reinterpret_cast<u32x4*>(dst + (m0 + r) * 16) = hi;
+          *reinterpret_cast<u32x4*>(dst + xpp + (m0 + r) * 16) = lo;
+        }
+      }
+    }
+    __syncthreads();
+    return true;
+  };
+
+  bool more = enter();
+  while (more) {
+    if (cpad > 0) {
+#pragma unroll
+      for (int p = 0; p < P; p++) {
+        if (creal > 0) {  // uniform: a real step of this wave
+          mma::exchange<FMT == FQ4>(ring_c[p][0]);
+          mma::exchange<FMT == FQ4>(ring_c[p][1]);
+          const char* xs = xl + (cj * UB) * bxb + xo;
+#pragma unroll
+          for (int u = 0; u < UB; u++) {
+            const mma::bf16x8 ahi = *reinterpret_cast<const mma::bf16x8*>(xs + u * bxb);
+            const mma::bf16x8 alo = *reinterpret_cast<const mma::bf16x8*>(xs + u * bxb + xpp);
+            mma::bf16x8 b;
+            if constexpr (FMT == FQ4) {
+              b = mma::q4_operand(ring_c[p][u >> 2][u & 3]);
+            } else {
+              const u32x4& w = ring_c[p][u >> 1];
+              b = mma::q8_operand(w[2 * (u & 1)], w[2 * (u & 1) + 1]);
+            }
+            f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, b, d, 0, 0, 0);
+            const uint32_t sw = ring_s[p][u >> 1];
+            // d, times 1/16 for the Q4_0 codes' 16 (n - 8), times 2^-30 for the inputs
+            const float s = h2f((u & 1) ? sw >> 16 : sw) * (FMT == FQ4 ? 0x1p-34f : 0x1p-30f);
+#pragma unroll
+            for (int r = 0; r < 4; r++) acc[r] = fmaf(s, d[r], acc[r]);
+          }
+          --creal;
+          ++cj;
+          {  // issue priority from the share of the wave's steps left, as in the vector form
+            // (measured on the dependent 27B Q8_0 pass: M = 8 8.65 -> 8.45 ms, M = 4 6.99 ->
+            // 6.72 ms; the spread between a workgroup's first and last wave on gate_up at M = 4
+            // 20 -> 7.5 us)
+            const int c4 = 4 * creal;
+            if (c4 >= 3 * creal0) __builtin_amdgcn_s_setprio(3);
+            else if (c4 >= 2 * creal0) __builtin_amdgcn_s_setprio(2);
+            else if (c4 >= creal0) __builtin_amdgcn_s_setprio(1);
+            else __builtin_amdgcn_s_setprio(0);
+          }
+          if (cj == sc.ns || creal == 0) {  // this wave's part of the tile is done
+            // lane (j, q) holds row j for inputs 4q .. 4q + 3 (q < 2 for M <= 8)
+            float v[4] = {acc[0], acc[1], acc[2], acc[3]};
+            const int t0 = ct * sc.ns, t1 = t0 + sc.ns;
+            const int w0 = (NW * t0 + NW - 1) / sc.S, wl = (NW * (t1 - 1) + NW - 1) / sc.S;
+            const int parts = sc.S >= NW ? wl - w0 + 1 : sc.ns;
+            bool put = parts == 1;
+            if (!put) {  // [part slot][input][row]
+              float* mine = part + (wave * 2 + (t0 >= sc.start ? 1 : 0)) * (kMcRows * kMcMaxM);
+              if (q < 2) {
+#pragma unroll
+                for (int r = 0; r < 4; r++) mine[(4 * q + r) * kMcRows + j] = v[r];
+              }
+              asm volatile("" ::: "memory");
+              int before = 0;
+              if (lane == 0)
+                before = __hip_atomic_fetch_add(&done[w0], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+              before = __builtin_amdgcn_readfirstlane(before);
+              asm volatile("" ::: "memory");
+              if (before == parts - 1) {
+                if (q < 2) {
+                  const float* p0 = part + (w0 * 2 + 1) * (kMcRows * kMcMaxM);
+#pragma unroll
+                  for (int r = 0; r < 4; r++) v[r] = p0[(4 * q + r) * kMcRows + j];
+                  for (int u = w0 + 1; u <= wl; u++)
+                    if (sc.S >= NW || ((u * sc.S) >> 4) < (((u + 1) * sc.S) >> 4)) {
+                      const float* pu = part + (u * 2) * (kMcRows * kMcMaxM);
+#pragma unroll
+                      for (int r = 0; r < 4; r++) v[r] = v[r] + pu[(4 * q + r) * kMcRows + j];
+                    }
+                }
+                if (lane == 0) done[w0] = 0;
+                put = true;
+              }
+            }
+            const int row = ct * sc.th + j;
+            if (put && q < 2 && j < sc.th && row < sc.nrows) {
+              bool store = true;
+              if (sc.nchunks > 1) {  // chunk sums, added in chunk order
+                float* pa = pacc + row * kMcMaxM + 4 * q;
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                  if (!sc.first) v[r] = pa[r] + v[r];
+                  pa[r] = v[r];
+                }
+                store = sc.last;
+              }
+              if (store) {
+#pragma unroll
+                for (int r = 0; r < 4; r++)
+                  if (4 * q + r < sc.M)  // agent-coherent: a later GEMV may read it
+                    __hip_atomic_store((__attribute__((address_space(1))) float*)sc.y +
+                                           (int64_t)(4 * q + r) * sc.ystride + row,
+                                       v[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              }
+            }
+            asm volatile("" ::: "memory");  // keep the store ahead of this step's loads
+            acc = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (cj == sc.ns) {
+              cj = 0;
+              ++ct;
+            }
+          }
+        }
+        issue(ring_c[p], ring_s[p]);  // refill the slot just consumed
+      }
+      cpad -= P;
+    }
+    if (cpad == 0) more = enter();
+  }
+}
+
 __global__ void k_fill(float* __restrict__ y, int64_t n, float v) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x)
@@ -1180,6 +1562,85 @@ int launch_chain(int fmt, int mm, const GemvDesc* descs, const int64_t* seg, con
   return launch_status();
 }
 
+// The matrix-core chain (k_qmv_chain_mc) takes batches from BQM_MC_MIN_M inputs on, when
+// every GEMV's K holds whole 128-byte pieces of a row.
+// Measured on the dependent 27B Q8_0 pass (ms, this form / the vector form): M = 8 8.45 /
+// 9.87-10.35, M = 4 6.72 / 6.02-6.16 (at M = 4 the vector form issues few enough FMAs, and
+// its input staging is a copy where this form splits every input into two bf16 parts).
+#ifndef BQM_MC_MIN_M
+#define BQM_MC_MIN_M 5
+#endif
+#ifndef BQM_MC_P
+#define BQM_MC_P 2  // steps in flight per wave
+#endif
+static bool mc_eligible(int fmt, int M, int64_t nb) {
+  return M >= BQM_MC_MIN_M && M <= kMcMaxM && nb % (fmt == BQM_Q4_0 ? 8 : 4) == 0;
+}
+// Staging plan of the matrix-core chain, as chain_plan: kc (a multiple of 8 blocks, so that a
+// chunk holds whole steps of either format) and the partial-sum rows.
+static bool chain_plan_mc(int n, int M, const int64_t* nbs, const int64_t* rows, int count, int* kc,
+                   int* pacc_rows) {
+  int64_t max_nb = 0;
+  for (int i = 0; i < count; i++) max_nb = nbs[i] > max_nb ? nbs[i] : max_nb;
+  const int64_t fixed = chain_lds_mc(n, M, 0, 0).total;
+  const int64_t bxb = mc_blk_bytes(M);
+  // at most 1024 staging jobs per chunk (4 per block and group of four inputs): one round
+  const int64_t kmax = 256 / ((M + 3) / 4);
+  if (max_nb <= kmax && fixed + max_nb * bxb <= kP1MaxLds) {
+    *kc = (int)max_nb;
+    *pacc_rows = 0;
+    return true;
+  }
+  for (int64_t k = std::min(max_nb - 1, kmax) & ~int64_t(7); k >= 8; k -= 8) {
+    int64_t prow = 0;
+    for (int i = 0; i < count; i++)
+      if (nbs[i] > k && rows[i] > prow) prow = rows[i];
+    const int64_t pacc = (prow * kMcMaxM * 4 + 15) & ~int64_t(15);
+    if (fixed + pacc + k * bxb <= kP1MaxLds) {
+      *kc = (int)k;
+      *pacc_rows = (int)prow;
+      return true;
+    }
+  }
+  return false;
+}
+template <int FMT>
+static ChainKernel chain_kernel_mc_f() { return k_qmv_chain_mc<FMT, BQM_MC_P>; }
+static int launch_chain_mc(int fmt, const GemvDesc* descs, const int64_t* seg, const GemvDesc* one, int n,
+                    int kc, int pacc_rows, uint32_t* sync, bool coop, hipStream_t s) {
+  ChainArgs a;
+  a.descs = descs;
+  a.seg = seg;
+  if (one) a.one = *one; else a.one = GemvDesc{nullptr, nullptr, nullptr, 0, 0, fmt, 0, 1, 0};
+  a.n = n;
+  a.kc = kc;
+  a.pacc_rows = pacc_rows;
+  a.sync = sync;
+  a.ix = IdxArgs{nullptr, nullptr, nullptr, nullptr, 0, 0, 0, 0, 0, nullptr};
+  ChainKernel k = fmt == BQM_Q4_0 ? chain_kernel_mc_f<FQ4>() : chain_kernel_mc_f<FQ8>();
+  static std::atomic<int> static_ok[2];
+  std::atomic<int>& okc = static_ok[fmt == BQM_Q4_0 ? 0 : 1];
+  int ok = okc.load(std::memory_order_relaxed);
+  if (ok == 0) {
+    hipFuncAttributes fa;
+    ok = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(k)) == hipSuccess &&
+                 fa.sharedSizeBytes <= (size_t)kP1StaticLds ? 1 : -1;
+    okc.store(ok, std::memory_order_relaxed);
+  }
+  if (ok < 0) return BQM_E_LAUNCH;
+  allow_lds(k, kP1MaxLds);
+  const int grid = cu_count();
+  if (coop) {
+    void* args[] = {&a};
+    if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k), dim3(grid), dim3(1024), args,
+                                   kP1MaxLds, s) != hipSuccess)
+      return BQM_E_LAUNCH;
+    return launch_status();
+  }
+  hipLaunchKernelGGL(k, dim3(grid), dim3(1024), kP1MaxLds, s, a);
+  return launch_status();
+}
+
 // ---- chain API.  Workspace: 64 header words {release epoch, -, error, n, fmt, kc,
 // partial-sum rows, M class, ...}, one 128-byte arrival flag per workgroup (at most
 // kChainMaxWorkgroups), then the descriptors, then per descriptor its segment's split
@@ -1191,10 +1652,15 @@ size_t chain_workspace_bytes(int n) {
   return n < 1 ? 0 : (size_t)(kChainSyncBytes + (int64_t)n * (int64_t)(sizeof(GemvDesc) + kSegBytes));
 }
 
-// Whether a prepared workspace's chain has a waiting GEMV (set by chain_prepare; a
-// workspace this process did not prepare is taken to have one).
+// Per prepared workspace (set by chain_prepare): whether its chain has a waiting GEMV, and
+// whether it was planned for the matrix-core form.  A workspace this process did not
+// prepare is taken to have a wait and the vector form (the kernel checks the plan's header
+// and reports a mismatch).
+struct ChainPlan {
+  bool waits, mc;
+};
 static std::mutex g_waits_mutex;
-static std::unordered_map<const void*, bool> g_chain_waits;
+static std::unordered_map<const void*, ChainPlan> g_chain_waits;
 
 int chain_prepare(const bqm_gemv* descs, int n, void* ws, hipStream_t s) {
   const int fmt = descs[0].fmt, M = descs[0].M;
@@ -1240,9 +1706,13 @@ int chain_prepare(const bqm_gemv* descs, int n, void* ws, hipStream_t s) {
     wrows[i] = rows;
   }
   const int mm = m_class(M);
+  bool mc = true;
+  for (int i = 0; i < n; i++) mc = mc && mc_eligible(fmt, M, nbs[i]);
   int kc = 0, pacc_rows = 0;
-  if (!chain_plan(n, mm, nbs.data(), wrows.data(), n, &kc, &pacc_rows)) return BQM_E_SHAPE;
-  uint32_t head[8] = {0, 0, 0, (uint32_t)n, (uint32_t)fmt, (uint32_t)kc, (uint32_t)pacc_rows, (uint32_t)mm};
+  if (mc && !chain_plan_mc(n, M, nbs.data(), wrows.data(), n, &kc, &pacc_rows)) mc = false;
+  if (!mc && !chain_plan(n, mm, nbs.data(), wrows.data(), n, &kc, &pacc_rows)) return BQM_E_SHAPE;
+  uint32_t head[9] = {0, 0, 0, (uint32_t)n, (uint32_t)fmt, (uint32_t)kc, (uint32_t)pacc_rows,
+                      (uint32_t)(mc ? mm | kMcClassBit : mm), (uint32_t)M};
   char* wsb = static_cast<char*>(ws);
   if (hipMemsetAsync(ws, 0, kChainSyncBytes, s) != hipSuccess ||
       hipMemcpyAsync(ws, head, sizeof(head), hipMemcpyHostToDevice, s) != hipSuccess ||
@@ -1255,7 +1725,7 @@ int chain_prepare(const bqm_gemv* descs, int n, void* ws, hipStream_t s) {
   bool waits = false;
   for (int i = 1; i < n; i++) waits = waits || descs[i].wait != 0;
   std::lock_guard<std::mutex> lock(g_waits_mutex);
-  g_chain_waits[ws] = waits;
+  g_chain_waits[ws] = ChainPlan{waits, mc};
   return BQM_OK;
 }
 
@@ -1263,13 +1733,14 @@ int chain_launch(int fmt, int M, void* ws, int n, hipStream_t s) {
   char* wsb = static_cast<char*>(ws);
   const GemvDesc* d = reinterpret_cast<const GemvDesc*>(wsb + kChainSyncBytes);
   const int64_t* seg = reinterpret_cast<const int64_t*>(wsb + kChainSyncBytes + (int64_t)n * sizeof(GemvDesc));
-  bool coop = true;
+  ChainPlan plan{true, false};
   {
     std::lock_guard<std::mutex> lock(g_waits_mutex);
     auto it = g_chain_waits.find(ws);
-    if (it != g_chain_waits.end()) coop = it->second;
+    if (it != g_chain_waits.end()) plan = it->second;
   }
-  return launch_chain(fmt, m_class(M), d, seg, nullptr, n, 0, 0, static_cast<uint32_t*>(ws), coop, s);
+  if (plan.mc) return launch_chain_mc(fmt, d, seg, nullptr, n, 0, 0, static_cast<uint32_t*>(ws), plan.waits, s);
+  return launch_chain(fmt, m_class(M), d, seg, nullptr, n, 0, 0, static_cast<uint32_t*>(ws), plan.waits, s);
 }
 
 int chain_status(const void* ws, hipStream_t s) {
@@ -1292,8 +1763,11 @@ int launch_qmv(int fmt, const void* w, const float* X, float* Y, int M, int64_t 
   const int CB = fmt == BQM_Q4_0 ? 16 : 32;
   if ((rows + 1) * (K / kQK) * CB >= ((int64_t)1 << 31)) return BQM_E_SHAPE;
   int kc = 0, pacc_rows = 0;
-  if (!chain_plan(1, mm, K / kQK, rows, &kc, &pacc_rows)) return BQM_E_SHAPE;
   const GemvDesc d{static_cast<const uint8_t*>(w), X, Y, N, K, fmt, 0, M, 0};
+  const int64_t nb = K / kQK;
+  if (mc_eligible(fmt, M, nb) && chain_plan_mc(1, M, &nb, &rows, 1, &kc, &pacc_rows))
+    return launch_chain_mc(fmt, nullptr, nullptr, &d, 1, kc, pacc_rows, nullptr, false, s);
+  if (!chain_plan(1, mm, nb, rows, &kc, &pacc_rows)) return BQM_E_SHAPE;
   return launch_chain(fmt, mm, nullptr, nullptr, &d, 1, kc, pacc_rows, nullptr, false, s);
 }
 

@@ -35,6 +35,7 @@
 // a pass has fewer tiles than waves, the waves also split each chunk's blocks between them
 // and the partial sums are added through LDS in a fixed order, so results are deterministic.
 #include "bqm_internal.h"
+#include "mma_ops.h"
 #include "slot_groups.h"
 
 #include <algorithm>
@@ -87,46 +88,6 @@ __host__ __device__ constexpr int mma_part_bytes(bool q4, bool gu) {
 
 __device__ __forceinline__ float h2f(uint32_t bits) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
-}
-__device__ __forceinline__ float sbyte(uint32_t v, int b) {
-  return (float)(int8_t)(v >> (8 * b));  // v_cvt_f32_i32 with a sign-extending byte select
-}
-// Two floats whose low 16 bits are zero (exact bf16 values) -> one bf16 pair, f0 low.
-__device__ __forceinline__ uint32_t bf_pair(float f0, float f1) {
-  return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f1), __builtin_bit_cast(uint32_t, f0),
-                               0x07060302u);
-}
-// One word of Q4_0 codes (bytes 4q..4q+3 of a block) -> the B operand: 16 (n - 8) of the low
-// nibbles (positions 4q..4q+3), then of the high ones (16+4q..16+4q+3).  n ^ 8 is n - 8 in
-// four-bit two's complement; placed at the top of a byte it reads as 16 (n - 8).
-__device__ __forceinline__ bf16x8 q4_operand(uint32_t w) {
-  const uint32_t lo = ((w << 4) ^ 0x80808080u) & 0xF0F0F0F0u;
-  const uint32_t hi = (w ^ 0x80808080u) & 0xF0F0F0F0u;
-  const u32x4 v{bf_pair(sbyte(lo, 0), sbyte(lo, 1)), bf_pair(sbyte(lo, 2), sbyte(lo, 3)),
-                bf_pair(sbyte(hi, 0), sbyte(hi, 1)), bf_pair(sbyte(hi, 2), sbyte(hi, 3))};
-  return __builtin_bit_cast(bf16x8, v);
-}
-// Eight Q8_0 codes (bytes 8q..8q+7 of a block) -> the B operand.
-__device__ __forceinline__ bf16x8 q8_operand(uint32_t w0, uint32_t w1) {
-  const u32x4 v{bf_pair(sbyte(w0, 0), sbyte(w0, 1)), bf_pair(sbyte(w0, 2), sbyte(w0, 3)),
-                bf_pair(sbyte(w1, 0), sbyte(w1, 1)), bf_pair(sbyte(w1, 2), sbyte(w1, 3))};
-  return __builtin_bit_cast(bf16x8, v);
-}
-// Inputs enter scaled by 2^kXShift (exact), which lifts every fp32 subnormal into the
-// range where the two bf16 parts keep all but 2^-14 of it (a bf16 part cannot hold a value
-// below 2^-133, and the smallest fp32 subnormal is 2^-149); the block scale carries
-// 2^-kXShift back.  The price: |x| must stay below 2^86 for the partial sums (codes up to
-// 128 = 2^7 times 32 terms) to stay below fp32's limit.
-constexpr int kXShift = 30;
-// x -> (x_hi, x_lo) bits of x * 2^kXShift: truncated to bf16, and the exact remainder
-// truncated to bf16 (zero when x is not finite: x_hi carries the infinity or NaN).
-__device__ __forceinline__ void split(float x, uint32_t& hi, uint32_t& lo) {
-  const float f = x * 0x1p30f;
-  static_assert(kXShift == 30, "the literal above");
-  const uint32_t u = __builtin_bit_cast(uint32_t, f);
-  hi = u & 0xFFFF0000u;
-  const float r = f - __builtin_bit_cast(float, hi);
-  lo = __builtin_isfinite(f) ? __builtin_bit_cast(uint32_t, r) & 0xFFFF0000u : 0u;
 }
 
 template <int FMT, bool GU>
@@ -275,38 +236,6 @@ __global__ __launch_bounds__(kMThreads) void k_qmv_id_mma(MmaArgs a) {
                 u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc[h], (vc[i] | m) + w * 64, kb * CB, 0));
         }
     };
-    // v_permlane32_swap: rows 2-3 (lanes 32-63) of a <-> rows 0-1 of b; v_permlane16_swap:
-    // rows 1 and 3 of a <-> rows 0 and 2 of b (a row is 16 lanes)
-    auto swap32 = [](uint32_t& x, uint32_t& y) {
-      const auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
-      x = r[0];
-      y = r[1];
-    };
-    auto swap16 = [](uint32_t& x, uint32_t& y) {
-      const auto r = __builtin_amdgcn_permlane16_swap(x, y, false, false);
-      x = r[0];
-      y = r[1];
-    };
-    // Q4_0: lane group q holds words 0-3 of block q; afterwards word u of lane group q is word
-    // q of block u (a 4 x 4 transpose between the lane groups and the words).  Q8_0, each of
-    // the two loads: lane group g holds bytes 16 (g % 2) .. + 16 of block g / 2 as words 0-3;
-    // afterwards words 0-1 of lane group q are bytes 8q .. 8q + 8 of the first block, words
-    // 2-3 those of the second.
-    auto exchange = [&](u32x4& v) {
-      uint32_t r0 = v.x, r1 = v.y, r2 = v.z, r3 = v.w;
-      if constexpr (FMT == MQ4) {
-        swap32(r0, r2);
-        swap32(r1, r3);
-        swap16(r0, r1);
-        swap16(r2, r3);
-      } else {
-        swap16(r0, r2);
-        swap16(r1, r3);
-        swap32(r0, r2);
-        swap32(r1, r3);
-      }
-      v = u32x4{r0, r1, r2, r3};
-    };
     // a quad's products: block u of the chunk-local quad `ql`
     auto consume = [&](Quad& Qd, int ql) {
       // the 4 scales of each tile's row j (lanes of one row read the same 8 bytes)
@@ -321,7 +250,7 @@ __global__ __launch_bounds__(kMThreads) void k_qmv_id_mma(MmaArgs a) {
 #pragma unroll
         for (int h = 0; h < NG; h++)
 #pragma unroll
-          for (int w = 0; w < LW; w++) exchange(Qd.c[i][h][w]);
+          for (int w = 0; w < LW; w++) mma::exchange<FMT == MQ4>(Qd.c[i][h][w]);
 #pragma unroll
       for (int u = 0; u < 4; u++) {
         const int bl = 4 * ql + u;
@@ -336,7 +265,7 @@ __global__ __launch_bounds__(kMThreads) void k_qmv_id_mma(MmaArgs a) {
 #pragma unroll
           for (int h = 0; h < NG; h++) {
             const u32x4& v = Qd.c[i][h][FMT == MQ4 ? 0 : u >> 1];
-            const bf16x8 b = FMT == MQ4 ? q4_operand(v[u]) : q8_operand(v[2 * (u & 1)], v[2 * (u & 1) + 1]);
+            const bf16x8 b = FMT == MQ4 ? mma::q4_operand(v[u]) : mma::q8_operand(v[2 * (u & 1)], v[2 * (u & 1) + 1]);
             d[i][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
             d[i][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, b, d[i][h], 0, 0, 0);
           }
@@ -405,15 +334,10 @@ __global__ __launch_bounds__(kMThreads) void k_qmv_id_mma(MmaArgs a) {
             const int bl = jb / (4 * c), pq = jb - bl * 4 * c;  // pq = k-group * c + slot
             const float f[8] = {v[r][0].x, v[r][0].y, v[r][0].z, v[r][0].w,
                                 v[r][1].x, v[r][1].y, v[r][1].z, v[r][1].w};
-            uint32_t hb[8], lb[8];
-#pragma unroll
-            for (int k = 0; k < 8; k++) split(f[k], hb[k], lb[k]);
-            *reinterpret_cast<u32x4*>(xl + bl * bxb + pq * 16) =
-                u32x4{(hb[1] & 0xFFFF0000u) | (hb[0] >> 16), (hb[3] & 0xFFFF0000u) | (hb[2] >> 16),
-                      (hb[5] & 0xFFFF0000u) | (hb[4] >> 16), (hb[7] & 0xFFFF0000u) | (hb[6] >> 16)};
-            *reinterpret_cast<u32x4*>(xl + bl * bxb + xpp + pq * 16) =
-                u32x4{(lb[1] & 0xFFFF0000u) | (lb[0] >> 16), (lb[3] & 0xFFFF0000u) | (lb[2] >> 16),
-                      (lb[5] & 0xFFFF0000u) | (lb[4] >> 16), (lb[7] & 0xFFFF0000u) | (lb[6] >> 16)};
+            u32x4 hi, lo;
+            mma::split8(f, hi, lo);
+            *reinterpret_cast<u32x4*>(xl + bl * bxb + pq * 16) = hi;
+            *reinterpret_cast<u32x4*>(xl + bl * bxb + xpp + pq * 16) = lo;
           }
         }
       }

@@ -377,7 +377,10 @@ def run_dense(args, torch, gen, bqm, fmt="q4_0"):
             raise RuntimeError(f"chain reported error {status}")
         dur = per_launch_ms([run], torch, reps=max(3, args.steps // 2))
         achieved = total / (float(dur.mean()) * 1e-3) / 1e9
-        kernel = f"k_qmv_chain ({fmt.upper()}, M={M}, {len(descs)} GEMVs per launch)"
+        # batches of 5-8 inputs run on the matrix-core form of the chain (every K here is a
+        # multiple of 256)
+        mc = M >= 5
+        kernel = f"{'k_qmv_chain_mc' if mc else 'k_qmv_chain'} ({fmt.upper()}, M={M}, {len(descs)} GEMVs per launch)"
         launch_us = round(1e3 * float(dur.mean()), 3)
         kkey = f"qmv_chain_{fmt}_dense27b" if M == 1 else f"qmv_chain_{fmt}_m{M}_dense27b"
         pct = step_percentiles(run, max(20, args.steps), torch)
@@ -437,17 +440,20 @@ def run_dense(args, torch, gen, bqm, fmt="q4_0"):
     }
     # The vector-ALU ceiling: each weight takes at least M fp32 multiply-adds (one per input
     # row) and one code conversion.  Where that ceiling is below the HBM one it is the
-    # binding roofline and is reported as such.
+    # binding roofline and is reported as such.  On the matrix-core form (batches 5-8) the
+    # products run on the matrix cores, and the vector ALU converts each code once and applies
+    # each block scale once per row and input (M / 32 multiply-adds per weight).
     nweights = sum(N * K for _, N, K in mats)
-    t_alu = alu_seconds(M * nweights, nweights)
+    mc = use_chain and M >= 5
+    t_alu = alu_seconds(M * nweights / 32, nweights) if mc else alu_seconds(M * nweights, nweights)
     alu_ceiling_gbs = total / t_alu / 1e9
     res["alu_ceiling_gbs"] = round(alu_ceiling_gbs, 1)
     res["hbm_frac"] = round(achieved / HBM_PEAK_GBS, 4)
     launch_s = float(dur.mean() if use_chain else dur.sum()) * 1e-3
     res["alu_frac"] = round(t_alu / launch_s, 4)
     if alu_ceiling_gbs < HBM_PEAK_GBS:
-        res["roofline"] = alu_roofline(M * nweights, nweights, launch_s, kernel, launch_us,
-                                       hbm_gbs=round(achieved, 1))
+        res["roofline"] = alu_roofline(M * nweights / 32 if mc else M * nweights, nweights, launch_s,
+                                       kernel, launch_us, hbm_gbs=round(achieved, 1))
         res["roofline"]["traffic"] = traffic
     if fmt == "q8_0":
         res["equiv_tok_s_aggregate"] = round(M * 1e3 / ms, 2)

@@ -125,11 +125,27 @@ __global__ __launch_bounds__(kMThreads) void k_qmv_id_mma(MmaArgs a) {
   if (nb == 0 || ng == 0) return;
 
   // ---- this workgroup's tiles ----
+  // With no more groups than workgroups, each group's tiles go to its own run of workgroups
+  // (group g: workgroups floor(g G / ng) .. floor((g + 1) G / ng) - 1, the tiles split evenly
+  // between them), so a workgroup streams one expert in one pass.  (Split evenly over all
+  // tiles, a workgroup whose share straddled two groups ran two passes, each with its own
+  // staging and sums, and finished 30 us after the others on the MoE layer at T = 16.)  With
+  // more groups than workgroups, the tiles of all groups are split evenly.
   const int tpg = (N + 15) >> 4;  // 16-row tiles per group
   const int64_t tt = (int64_t)ng * tpg;
-  const int64_t t_end = tt * (blockIdx.x + 1) / gridDim.x;
+  const int G = (int)gridDim.x, b = (int)blockIdx.x;
+  int64_t t_begin, t_end;
+  if (ng <= G) {
+    const int g = ((b + 1) * ng + G - 1) / G - 1;  // the largest g with floor(g G / ng) <= b
+    const int w0 = g * G / ng, nw = (g + 1) * G / ng - w0, i = b - w0;
+    t_begin = (int64_t)g * tpg + (int64_t)tpg * i / nw;
+    t_end = (int64_t)g * tpg + (int64_t)tpg * (i + 1) / nw;
+  } else {
+    t_begin = tt * b / G;
+    t_end = tt * (b + 1) / G;
+  }
   const int j = lane & 15, q = lane >> 4;
-  for (int64_t t = tt * blockIdx.x / gridDim.x; t < t_end;) {
+  for (int64_t t = t_begin; t < t_end;) {
     const int g = (int)(t / tpg), ta = (int)(t - (int64_t)g * tpg);
     const int64_t left = t_end - t;
     int nt = tpg - ta;
@@ -341,28 +357,42 @@ __global__ __launch_bounds__(kMThreads) void k_qmv_id_mma(MmaArgs a) {
           }
         }
       }
-      // stage the pass's scales for the chunk: per tensor, row r's kcb scales as 8-byte pieces
-      // (4 blocks each), consecutive pieces of a row to consecutive threads; rows past N read
-      // zeros
+      // stage the pass's scales for the chunk: per tensor, row r's kcb scales as 16-byte pieces
+      // (8 blocks; else 8-byte pieces of 4), consecutive pieces of a
+      // row to consecutive threads, kSJobs rows per thread in flight together (one memory round
+      // trip for up to 8 * 1024 pieces; staged 8 bytes at a time, 4 in flight, a pass of 400
+      // rows took four); rows past N read zeros
       {
-        const int spr = kcb >> 2, njobs = R * spr;
+        constexpr int kSJobs = 8;
+        // 16-byte pieces only where each starts on a 16-byte boundary (nb, kb0, kcb multiples of 8)
+        const bool p16 = ((nb | kb0 | kcb) & 7) == 0;
+        const int pcs = p16 ? kcb >> 3 : kcb >> 2;  // pieces per row
+        const int rpr = kMThreads / pcs;            // rows per round of the threads
+        const int myr = tid / pcs, pc = tid - myr * pcs;
+        const int pbytes = p16 ? 16 : 8;
 #pragma unroll
         for (int h = 0; h < NG; h++)
-          for (int jb0 = 0; jb0 < njobs; jb0 += kJobs * kMThreads) {
-            u32x2 v[kJobs];
+          for (int r0 = 0; r0 < R; r0 += kSJobs * rpr) {
+            u32x4 v[kSJobs];
 #pragma unroll
-            for (int r = 0; r < kJobs; r++) {
-              const int jb = jb0 + r * kMThreads + tid;
-              const int row = jb / spr, pc = jb - row * spr, n = ta * 16 + row;
-              const uint32_t off = jb < njobs && n < N ? (uint32_t)n * (uint32_t)nb * 2u + (uint32_t)(kb0 + 4 * pc) * 2u : kOob;
-              v[r] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs[h], off, 0, 0));
+            for (int k = 0; k < kSJobs; k++) {
+              const int row = r0 + k * rpr + myr, n = ta * 16 + row;
+              const bool ok = myr < rpr && row < R && n < N;
+              const uint32_t off = ok ? (uint32_t)n * (uint32_t)nb * 2u + (uint32_t)(kb0 + pc * (p16 ? 8 : 4)) * 2u : kOob;
+              if (p16) {
+                v[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs[h], off, 0, 0));
+              } else {
+                const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs[h], off, 0, 0));
+                v[k] = u32x4{w.x, w.y, 0u, 0u};
+              }
             }
 #pragma unroll
-            for (int r = 0; r < kJobs; r++) {
-              const int jb = jb0 + r * kMThreads + tid;
-              if (jb < njobs) {
-                const int row = jb / spr, pc = jb - row * spr;
-                *reinterpret_cast<u32x2*>(scl + (h * R + row) * sst + 8 * pc) = v[r];
+            for (int k = 0; k < kSJobs; k++) {
+              const int row = r0 + k * rpr + myr;
+              if (myr < rpr && row < R) {
+                char* dst = scl + (h * R + row) * sst + pbytes * pc;  // 8-byte aligned
+                *reinterpret_cast<u32x2*>(dst) = u32x2{v[k].x, v[k].y};
+                if (p16) *reinterpret_cast<u32x2*>(dst + 8) = u32x2{v[k].z, v[k].w};
               }
             }
           }
@@ -370,6 +400,16 @@ __global__ __launch_bounds__(kMThreads) void k_qmv_id_mma(MmaArgs a) {
       __syncthreads();
       if (u0 + 1 < u1) issue_unit(UB, u0 + 1, true);
       for (int un = u0; un < u1; un += 2) {
+        // issue priority from the share of the wave's units left: a SIMD issues from its
+        // oldest wave first, and without it the waves of a workgroup finished up to 18 us
+        // apart on the MoE layer at T = 16
+        {
+          const int c4 = 4 * (u1 - un), n4 = u1 - u0;
+          if (c4 >= 3 * n4) __builtin_amdgcn_s_setprio(3);
+          else if (c4 >= 2 * n4) __builtin_amdgcn_s_setprio(2);
+          else if (c4 >= n4) __builtin_amdgcn_s_setprio(1);
+          else __builtin_amdgcn_s_setprio(0);
+        }
         consume_unit(UA, un);
         if (un + 2 < u1) issue_unit(UA, un + 2, true);
         if (un + 1 < u1) {

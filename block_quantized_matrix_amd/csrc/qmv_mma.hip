@@ -126,8 +126,7 @@ __global__ __launch_bounds__(kMThreads) void k_qmv_id_mma(MmaArgs a) {
 
   // ---- this workgroup's tiles ----
   // With no more groups than workgroups, each group's tiles go to its own run of workgroups
-  // (group g: workgroups floor(g G / ng) .. floor((g + 1) G / ng) - 1, the tiles split evenly
-  // between them), so a workgroup streams one expert in one pass.  (Split evenly over all
+  // (the tiles split evenly between them), so a workgroup streams one expert in one pass.  (Split evenly over all
   // tiles, a workgroup whose share straddled two groups ran two passes, each with its own
   // staging and sums, and finished 30 us after the others on the MoE layer at T = 16.)  With
   // more groups than workgroups, the tiles of all groups are split evenly.
@@ -136,10 +135,54 @@ __global__ __launch_bounds__(kMThreads) void k_qmv_id_mma(MmaArgs a) {
   const int G = (int)gridDim.x, b = (int)blockIdx.x;
   int64_t t_begin, t_end;
   if (ng <= G) {
-    const int g = ((b + 1) * ng + G - 1) / G - 1;  // the largest g with floor(g G / ng) <= b
-    const int w0 = g * G / ng, nw = (g + 1) * G / ng - w0, i = b - w0;
+    // Each group gets one workgroup, and the G - ng others are shared out by weight: 4 + 2
+    // chunks, the chunks of K its slots' inputs need (estimated at the even share of tiles, at
+    // most 3 counted).  A group of many slots stages its inputs in more chunks, each a memory
+    // round trip more, and its workgroups then take fewer rows.  (Measured on the MoE gate
+    // projection at T = 16, 16 tiles per workgroup: 48-50 us with one chunk, 54-58 with two,
+    // 63 with three, about 2.2 us per tile.)  Group g's workgroups: from g + floor(P_g (G -
+    // ng) / W) to the next group's first, P_g the weights before it, W their sum.
+    {
+      const int nt0 = (int)std::min<int64_t>(kMWaves * TPW, (tt + G - 1) / G);
+      const int R0 = nt0 * 16;
+      constexpr int KQ0 = FMT == MQ4 ? 8 : 4;
+      int wv = 0;  // thread g < ng: group g's weight (ng <= G <= kMThreads)
+      if (tid < ng) {
+        const int c = grp[3 * tid + 2];
+        int kcp = (a.kc * kXBlk - 16 * NG * R0) / (2 * (4 * c + 1) * 16 + 2 * NG * R0);
+        kcp = std::max(KQ0, kcp & ~(KQ0 - 1));
+        wv = 4 + 2 * std::min((nb + kcp - 1) / kcp, 3);
+      }
+      // exclusive prefix of the weights: a scan in each wave, then the waves' totals (s_scan is
+      // free after the sort)
+      int inc = wv;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += u;
+      }
+      if (lane == 63) s_scan[wave] = inc;
+      __syncthreads();
+      int before = 0, W = 0;
+      for (int w = 0; w < kMWaves; w++) {
+        before += w < wave ? s_scan[w] : 0;
+        W += s_scan[w];
+      }
+      if (tid < ng) {  // is this workgroup one of group tid's?  (products below 2^31)
+        const int P = before + inc - wv, E = G - ng;
+        const int f0 = tid + P * E / W, f1 = tid + 1 + (P + wv) * E / W;
+        if (f0 <= b && b < f1) {
+          s_xoff[0] = tid;
+          s_xoff[1] = f0;
+          s_xoff[2] = f1 - f0;
+        }
+      }
+      __syncthreads();
+    }
+    const int g = (int)s_xoff[0], w0 = (int)s_xoff[1], nw = (int)s_xoff[2], i = b - w0;
     t_begin = (int64_t)g * tpg + (int64_t)tpg * i / nw;
     t_end = (int64_t)g * tpg + (int64_t)tpg * (i + 1) / nw;
+    __syncthreads();  // read by every thread before the first pass writes s_xoff
   } else {
     t_begin = tt * b / G;
     t_end = tt * (b + 1) / G;

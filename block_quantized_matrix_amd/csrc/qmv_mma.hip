@@ -109,6 +109,9 @@ __global__ __launch_bounds__(kMThreads) void k_qmv_id_mma(MmaArgs a) {
   int* grp = srt + TS;
   char* xl = lds + mma_table_bytes(E, TS);
 
+  // the id of this workgroup's first slot in the padding fill below, read now, together with
+  // the ids the slot sort reads (after the sort it would be a memory round trip more)
+  const int fill_e0 = (int)blockIdx.x < TS ? a.ids[blockIdx.x] : 0;
   // the slots grouped by expert, groups of up to 16
   group_slots<kMThreads, kGroupSlots>(a.ids, E, TS, cnt, srt, grp, s_scan, &s_ng);
   const int ng = s_ng;
@@ -116,7 +119,7 @@ __global__ __launch_bounds__(kMThreads) void k_qmv_id_mma(MmaArgs a) {
   // rows of slots that no group computes, each by one workgroup: a negative id gives zeros,
   // an id >= E NaN; with K = 0 every valid slot's sums are empty (zeros)
   for (int ts = blockIdx.x; ts < TS; ts += gridDim.x) {
-    const int e = a.ids[ts];
+    const int e = ts == (int)blockIdx.x ? fill_e0 : a.ids[ts];
     const bool valid = e >= 0 && e < E;
     if (valid && nb > 0) continue;
     const float v = valid || e < 0 ? 0.0f : __builtin_nanf("");

@@ -16,8 +16,10 @@ pytestmark = pytest.mark.gpu
 
 FMTS = ["q4_0", "q8_0"]
 QMV = {"q4_0": bqm.qmv_q4_0, "q8_0": bqm.qmv_q8_0}
-# rows: one, ragged tiles, more rows than workgroups; K: one step, whole, chunked, the longest
-SHAPES = [(1, 256), (17, 512), (300, 4096), (70, 17408), (33, 32768), (2049, 1536)]
+# rows: one, ragged tiles, more rows than workgroups; K: one step, whole, chunked, the longest;
+# K = 128 and 384 (whole 128-byte steps of Q8_0 rows; the vector form for Q4_0, whose steps
+# are 256 weights)
+SHAPES = [(1, 256), (17, 512), (300, 4096), (70, 17408), (33, 32768), (2049, 1536), (3, 128), (257, 384)]
 
 
 @pytest.fixture(scope="module", autouse=True)

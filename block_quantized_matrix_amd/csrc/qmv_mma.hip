@@ -138,13 +138,13 @@ __global__ __launch_bounds__(kMThreads) void k_qmv_id_mma(MmaArgs a) {
   const int G = (int)gridDim.x, b = (int)blockIdx.x;
   int64_t t_begin, t_end;
   if (ng <= G) {
-    // Each group gets one workgroup, and the G - ng others are shared out by weight: 4 + 2
-    // chunks, the chunks of K its slots' inputs need (estimated at the even share of tiles, at
-    // most 3 counted).  A group of many slots stages its inputs in more chunks, each a memory
+    // Each group gets a base of workgroups (below), and the others are shared out by weight:
+    // 4 + 2 chunks, the chunks of K its slots' inputs need (estimated at the even share of
+    // tiles, at most 3 counted).  A group of many slots stages its inputs in more chunks, each a memory
     // round trip more, and its workgroups then take fewer rows.  (Measured on the MoE gate
     // projection at T = 16, 16 tiles per workgroup: 48-50 us with one chunk, 54-58 with two,
-    // 63 with three, about 2.2 us per tile.)  Group g's workgroups: from g + floor(P_g (G -
-    // ng) / W) to the next group's first, P_g the weights before it, W their sum.
+    // 63 with three, about 2.2 us per tile.)  Group g's workgroups: from g base + floor(P_g
+    // (G - ng base) / W) to the next group's first, P_g the weights before it, W their sum.
     {
       const int nt0 = (int)std::min<int64_t>(kMWaves * TPW, (tt + G - 1) / G);
       const int R0 = nt0 * 16;
@@ -171,9 +171,15 @@ __global__ __launch_bounds__(kMThreads) void k_qmv_id_mma(MmaArgs a) {
         before += w < wave ? s_scan[w] : 0;
         W += s_scan[w];
       }
+      // every group first gets the workgroups that keep its tiles within one pass (a round of
+      // the waves, kMWaves * TPW tiles), where the grid allows, else one; then its weighted
+      // share of the rest.  (Without the first part, gate+up at T = 16 (16 tiles a pass) gave
+      // some workgroups 17-19 tiles, whose second pass ended the call 27 us after the median.)
+      const int bmin = (tpg + kMWaves * TPW - 1) / (kMWaves * TPW);
+      const int base = (int64_t)ng * bmin <= G ? bmin : 1;
       if (tid < ng) {  // is this workgroup one of group tid's?  (products below 2^31)
-        const int P = before + inc - wv, E = G - ng;
-        const int f0 = tid + P * E / W, f1 = tid + 1 + (P + wv) * E / W;
+        const int P = before + inc - wv, E = G - ng * base;
+        const int f0 = tid * base + P * E / W, f1 = (tid + 1) * base + (P + wv) * E / W;
         if (f0 <= b && b < f1) {
           s_xoff[0] = tid;
           s_xoff[1] = f0;

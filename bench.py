@@ -749,6 +749,13 @@ def run_prefill_moe(args, torch, gen, bqm):
     ops = n_layers * 3 * 2.0 * slots * F * H           # useful int8 operations, all launches
     tops = ops / (dur.sum() * 1e-3) / 1e12
     triples = n_layers * 3.0 * slots * F * (H // 32)  # (slot, n, block): one conversion, one FMA
+    # algorithmic HBM bytes of all launches: each selected expert's weights once, the int8
+    # inputs and their block scales once, the outputs written
+    hbm_bytes = 0
+    for L in layers:
+        U = int(np.sum(L[-1] > 0))
+        hbm_bytes += 2 * (U * F * (H // 32) * 18 + T * H + T * (H // 32) * 4 + slots * F * 4)  # gate, up
+        hbm_bytes += U * H * (F // 32) * 18 + slots * F + slots * (F // 32) * 4 + slots * H * 4  # down
     # the kernel's row tiles: 64 slots of an expert while more than 32 are left, then 32
     tall = [int(np.sum(L[-1] // 64 + (L[-1] % 64 > 32))) for L in layers]
     short = [int(np.sum((L[-1] % 64 > 0) & (L[-1] % 64 <= 32))) for L in layers]
@@ -761,10 +768,13 @@ def run_prefill_moe(args, torch, gen, bqm):
             "ms_per_layer": round(ms / n_layers, 4),
             "busiest_expert_slots": [int(L[-1].max()) for L in layers],
             "row_tile_fill": round(slots / float(np.mean([64 * a + 32 * b for a, b in zip(tall, short)])), 3),
-            "roofline": {**alu_roofline(triples, triples, float(dur.sum()) * 1e-3, "k_qmm_id_q4_0",
-                                        round(1e3 * float(dur.mean()), 3),
-                                        mfma_int8_frac=round(tops / INT8_PEAK_TOPS, 4)),
-                         "traffic": traffic_from_profiles("qmm_id_q4_0_moe_prefill")},
+            # the binding roofline: each selected expert's weights cross HBM once (with
+            # half the experts holding two slots or fewer, the weights take longer at 8 TB/s
+            # than the useful products' vector work takes at its rates), or the vector ALU
+            "roofline": {**binding_roofline(hbm_bytes, triples, triples, float(dur.sum()) * 1e-3,
+                                            "k_qmm_id_q4_0", round(1e3 * float(dur.mean()), 3),
+                                            traffic_from_profiles("qmm_id_q4_0_moe_prefill")),
+                         "mfma_int8_frac": round(tops / INT8_PEAK_TOPS, 4)},
             **({} if args.no_cpu else {"cpu_baseline": cpu_baseline_qmm_id(
                 E, top_k, H, F, T, args.cpu_seconds, gen)})}
 

@@ -189,19 +189,26 @@ def chain_of(fmt, M, items, wait, torch, bqm):
 
 
 def per_launch_ms(launches, torch, reps=3):
-    """Average duration of each launch, bracketed by events on the stream it runs on."""
+    """Average duration of each launch, bracketed by events on the stream it runs on.  A spin
+    kernel ahead of them holds the stream while the host enqueues every launch and event, so
+    that the launches run back to back and a bracket holds a launch's own time on the GPU
+    rather than the host's submission of it to an idle queue (which added 20-30 us to a
+    launch of about 125 us)."""
     cur = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in launches]
-    tot = np.zeros(len(launches))
-    for _ in range(reps):
-        for (a, b), fn in zip(ev, launches):
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in launches] for _ in range(reps)]
+    torch.cuda.synchronize()
+    # about 2.4e6 spin cycles per ms; 0.1 ms of host time per launch and its events, at
+    # least 2 ms
+    torch.cuda._sleep(int(2.4e6 * max(2.0, 0.1 * reps * len(launches))))
+    for r in range(reps):
+        for (a, b), fn in zip(ev[r], launches):
             a.record(cur)
             fn()
             b.record(cur)
-        torch.cuda.synchronize()
-        tot += [a.elapsed_time(b) for a, b in ev]
-    return tot / reps
+    torch.cuda.synchronize()
+    return np.array([sum(ev[r][i][0].elapsed_time(ev[r][i][1]) for r in range(reps)) / reps
+                     for i in range(len(launches))])
 
 
 def traffic_from_profiles(kernel_key):

@@ -280,7 +280,8 @@ struct StageRow {
   int32_t nrows, nb;        // rows of this workgroup; blocks per row
   int32_t wait, M;
   int32_t xstride, ystride; // floats between input rows (K) and between output rows (N)
-  int32_t nchunks, pad;     // chunks of kc blocks
+  int32_t nchunks;          // chunks of kc blocks
+  int32_t next;             // the next GEMV this workgroup enters (see link_units), or n
 };
 static_assert(sizeof(StageRow) == 64, "stage table row");
 
@@ -319,7 +320,7 @@ __device__ __forceinline__ StageRow make_stage(const GemvDesc& d, int64_t sbase,
   st.xstride = (int)d.K;
   st.ystride = N;
   st.nchunks = (nb + kc - 1) / kc;
-  st.pad = 0;
+  st.next = 0;  // set by link_units
   return st;
 }
 
@@ -333,6 +334,7 @@ struct Stage {
   float* y;
   int nrows, nb, nbc, kb0, ns, S, start, end, M, xstride, ystride, nchunks, lo;
   int th;                   // matrix-core form: rows per tile
+  int next;                 // chains: the next GEMV the workgroup enters
   bool wait, first, last;
 };
 
@@ -373,6 +375,7 @@ __device__ __forceinline__ void load_stage(const StageRow* t, int i, int c, int 
   s.xstride = __builtin_amdgcn_readfirstlane(r.xstride);
   s.ystride = __builtin_amdgcn_readfirstlane(r.ystride);
   s.nchunks = __builtin_amdgcn_readfirstlane(r.nchunks);
+  s.next = __builtin_amdgcn_readfirstlane(r.next);
   s.lo = 0;
   stage_chunk<LGW, R>(c, kc, wave, __builtin_amdgcn_readfirstlane(r.wait), s);
 }
@@ -461,6 +464,45 @@ __device__ __forceinline__ bool grid_barrier(uint32_t* ws, uint32_t epoch, bool*
   return *lds_ok;
 }
 
+// The GEMVs of a chain that a workgroup enters: those with rows in its share, and, when the
+// workgroups wait for each other, every waiting one after the first (all take part in each
+// wait).  Walking the whole table instead, one stage read per GEMV on both sides of every
+// wave, cost a chain of 63 independent 4096 x 4096 Q4_0 GEMVs a quarter of its time: each
+// workgroup's share touches one or two of them.  The entered GEMVs are linked once per
+// launch: table[i].next is the first one after i (n if none), first[0] the first of all, so
+// that a step of the walk is a field of the stage row just read (a scan of a bit mask at
+// every step cost the dependent 27B passes 1-2 %: its branches sit before each wait).
+// LDS: mask, one bit per GEMV (64-bit words, at most 64 of them: n <= 4096); first, 64 ints
+// (per word, the first entered GEMV in it or a later word).  Every thread calls it once the
+// table is complete; a barrier must follow.
+__device__ __forceinline__ void link_units(StageRow* table, int n, bool sync, uint64_t* mask, int* first) {
+  const int lane = threadIdx.x & 63;
+  const int nw = (n + 63) >> 6;
+  for (int i0 = threadIdx.x & ~63; i0 < n; i0 += blockDim.x) {
+    const int i = i0 + lane;
+    const bool v = i < n && (table[i].nrows > 0 || (sync && i > 0 && table[i].wait != 0));
+    const uint64_t m = __ballot(v);
+    if (lane == 0) mask[i0 >> 6] = m;
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const uint64_t m = lane < nw ? mask[lane] : 0;
+    int f = m ? lane * 64 + __builtin_ctzll(m) : n;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {  // the minimum over this word and the later ones
+      const int g = __shfl_down(f, o, 64);
+      if (lane + o < 64) f = min(f, g);
+    }
+    first[lane] = f;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int b = i & 63, w1 = (i >> 6) + 1;
+    const uint64_t m = b == 63 ? 0 : mask[i >> 6] >> (b + 1);  // entered GEMVs after i in its word
+    table[i].next = m ? i + 1 + __builtin_ctzll(m) : w1 < 64 ? first[w1] : n;
+  }
+}
+
 // Largest batch class (slots per group) of the indexed form.
 constexpr int kIdMaxClass = 4;
 // LDS rows (64 bytes) the indexed form's tables take: per-expert counts (E + 1), the slots
@@ -470,15 +512,19 @@ __host__ __device__ inline int idx_table_rows(int E, int TS) { return (4 * (E + 
 // Dynamic LDS of a chain launch, in bytes from the start: the stage table, the split-tile
 // parts, their counters, the per-row partial sums of chunked GEMVs, the staged inputs.
 struct ChainLds {
-  int part, done, pacc, x, total;
+  int part, done, pacc, x, mask, first, total;
 };
+// Bytes of link_units' mask for a table of n rows (whole 16 bytes); its 64 ints follow.
+__host__ __device__ inline int unit_mask_bytes(int n) { return ((n + 127) / 128) * 16; }
 __host__ __device__ inline ChainLds chain_lds(int n, int mm, int r, int pacc_rows, int kc) {
   ChainLds L;
   L.part = (n * 64 + 15) & ~15;
   L.done = L.part + kP1Waves * 2 * kGpw * r * mm * 4;
   L.pacc = L.done + kP1Waves * 4;
   L.x = L.pacc + ((pacc_rows * mm * 4 + 15) & ~15);
-  L.total = L.x + mm * kc * kBlkLds;
+  L.mask = L.x + mm * kc * kBlkLds;
+  L.first = L.mask + unit_mask_bytes(n);
+  L.total = L.first + 256;
   return L;
 }
 
@@ -516,6 +562,8 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
   int* done = reinterpret_cast<int*>(lds + ly.done);
   float* pacc = reinterpret_cast<float*>(lds + ly.pacc);
   char* xlds = lds + ly.x;
+  uint64_t* umask = reinterpret_cast<uint64_t*>(lds + ly.mask);
+  int* ufirst = reinterpret_cast<int*>(lds + ly.first);
   const int mstride = kc * kBlkLds;  // bytes between the staged inputs
   // indexed form: per-expert counts, then starts; the valid slots grouped by expert; the
   // groups (expert, first position in srt, slots)
@@ -553,6 +601,8 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
       table[i] = a.seg ? make_stage<FMT>(d, a.seg[2 * i], a.seg[2 * i + 1], kc)
                        : make_stage<FMT>(d, 0, d.N * (d.K >> 5), kc);
     }
+    __syncthreads();
+    link_units(table, a.n, a.sync != nullptr, umask, ufirst);
   }
   if (tid < NW) done[tid] = 0;
   if (tid == 0 && a.sync) lds_epoch = ld_agent(a.sync);  // stable until all have arrived once
@@ -622,6 +672,7 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
 
   // ---------------- issue side: P steps ahead ----------------
   int gi = u_begin - 1, ci = 0;  // unit and chunk being issued
+  const int g_first = IDX ? 0 : __builtin_amdgcn_readfirstlane(ufirst[0]);  // the first GEMV entered
   Stage si;
   si.nchunks = 0;
   int it = 0, ij = 0;        // this wave's tile, step in tile
@@ -663,8 +714,9 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
       if (ci + 1 < si.nchunks) {
         ++ci;
       } else {
-        if (gi + 1 >= u_end) break;
-        ++gi;
+        const int g = IDX ? gi + 1 : gi < 0 ? g_first : si.next;
+        if (g >= u_end) break;
+        gi = g;
         ci = 0;
       }
       load(gi, ci, si);
@@ -768,8 +820,9 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
       if (cc + 1 < sc.nchunks) {
         ++cc;
       } else {
-        if (gc + 1 >= u_end) return false;
-        ++gc;
+        const int g = IDX ? gc + 1 : gc < 0 ? g_first : sc.next;
+        if (g >= u_end) return false;
+        gc = g;
         cc = 0;
       }
       load(gc, cc, sc);
@@ -1019,7 +1072,9 @@ __host__ __device__ inline ChainLds chain_lds_mc(int n, int M, int pacc_rows, in
   L.done = L.part + kMcPartBytes;
   L.pacc = L.done + kP1Waves * 4;
   L.x = L.pacc + ((pacc_rows * kMcMaxM * 4 + 15) & ~15);
-  L.total = L.x + kc * mc_blk_bytes(M);
+  L.mask = L.x + kc * mc_blk_bytes(M);
+  L.first = L.mask + unit_mask_bytes(n);
+  L.total = L.first + 256;
   return L;
 }
 
@@ -1072,12 +1127,16 @@ __global__ __launch_bounds__(1024) void k_qmv_chain_mc(ChainArgs a) {
   int* done = reinterpret_cast<int*>(lds + ly.done);
   float* pacc = reinterpret_cast<float*>(lds + ly.pacc);
   char* xl = lds + ly.x;
+  uint64_t* umask = reinterpret_cast<uint64_t*>(lds + ly.mask);
+  int* ufirst = reinterpret_cast<int*>(lds + ly.first);
   const int bxb = mc_blk_bytes(M), xpp = bxb / 2;  // staged bytes per block; per part
   for (int i = tid; i < a.n; i += NT) {
     const GemvDesc d = a.descs ? a.descs[i] : a.one;
     table[i] = a.seg ? make_stage<FMT>(d, a.seg[2 * i], a.seg[2 * i + 1], kc)
                      : make_stage<FMT>(d, 0, d.N * (d.K >> 5), kc);
   }
+  __syncthreads();
+  link_units(table, a.n, a.sync != nullptr, umask, ufirst);
   if (tid < NW) done[tid] = 0;
   if (tid == 0 && a.sync) lds_epoch = ld_agent(a.sync);
   if (tid == 0) lds_ok = true;
@@ -1100,12 +1159,14 @@ __global__ __launch_bounds__(1024) void k_qmv_chain_mc(ChainArgs a) {
     st.xstride = __builtin_amdgcn_readfirstlane(r.xstride);
     st.ystride = __builtin_amdgcn_readfirstlane(r.ystride);
     st.nchunks = __builtin_amdgcn_readfirstlane(r.nchunks);
+    st.next = __builtin_amdgcn_readfirstlane(r.next);
     st.lo = 0;
     stage_chunk_mc<UB>(c, kc, wave, __builtin_amdgcn_readfirstlane(r.wait), st);
   };
 
   // ---------------- issue side: P steps ahead (as in the vector form) ----------------
   int gi = -1, ci = 0;
+  const int g_first = __builtin_amdgcn_readfirstlane(ufirst[0]);  // the first GEMV entered
   Stage si;
   si.nchunks = 0;
   int it = 0, ij = 0, ireal = 0, ipad = 0;
@@ -1125,8 +1186,9 @@ __global__ __launch_bounds__(1024) void k_qmv_chain_mc(ChainArgs a) {
       if (ci + 1 < si.nchunks) {
         ++ci;
       } else {
-        if (gi + 1 >= n_units) break;
-        ++gi;
+        const int g = gi < 0 ? g_first : si.next;
+        if (g >= n_units) break;
+        gi = g;
         ci = 0;
       }
       load(gi, ci, si);
@@ -1184,8 +1246,9 @@ __global__ __launch_bounds__(1024) void k_qmv_chain_mc(ChainArgs a) {
       if (cc + 1 < sc.nchunks) {
         ++cc;
       } else {
-        if (gc + 1 >= n_units) return false;
-        ++gc;
+        const int g = gc < 0 ? g_first : sc.next;
+        if (g >= n_units) return false;
+        gc = g;
         cc = 0;
       }
       load(gc, cc, sc);
@@ -1385,6 +1448,7 @@ void allow_lds(Kern k, size_t bytes) {
 #endif
 constexpr int kP1StaticLds = 1024;                   // reserved for the kernel's own __shared__
 constexpr int kP1MaxLds = 160 * 1024 - kP1StaticLds;  // dynamic LDS of a chain launch
+static_assert(kP1MaxLds / 64 <= 64 * 64, "link_units: a table that fits holds at most 64 mask words");
 
 using ChainKernel = void (*)(ChainArgs);
 

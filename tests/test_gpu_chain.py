@@ -18,7 +18,8 @@ def _oracle():
 
 def make_chain(fmt, shapes, key, dependent=True, M=1):
     """GEMVs i = 0..n-1 with W_i [N_i][K_i], inputs [M][K_i], outputs [M][N_i]; if
-    dependent, x_{i+1} is y_i (N_i == K_{i+1})."""
+    dependent, x_{i+1} is y_i (N_i == K_{i+1}) and every GEMV after the first waits, else
+    none waits (one segment)."""
     Ws, Wps, xs, ys, descs = [], [], [], [], []
     x = gen.normal((M, shapes[0][1]), key + ("x0",), device=DEV)
     for i, (N, K) in enumerate(shapes):
@@ -28,7 +29,7 @@ def make_chain(fmt, shapes, key, dependent=True, M=1):
             x = gen.normal((M, K), key + ("x", i), device=DEV)
         y = torch.full((M, N), float("nan"), device=DEV)
         Ws.append(Wi); Wps.append(Wp); xs.append(x); ys.append(y)
-        descs.append(bqm.gemv(fmt, Wp, x, y, N, K, wait=i > 0, M=M))
+        descs.append(bqm.gemv(fmt, Wp, x, y, N, K, wait=dependent and i > 0, M=M))
         if dependent:
             x = y
     ws = torch.zeros(bqm.chain_workspace_bytes(len(descs)), dtype=torch.uint8, device=DEV)
@@ -79,6 +80,43 @@ def test_chain_batched_ragged_one_segment(M):
     bqm.qmv_chain("q8_0", M, ws, len(descs))
     assert bqm.bqm_chain_status(ws) == 0
     check_stages("q8_0", shapes, Ws, xs, ys, M=M)
+
+
+@pytest.mark.parametrize("fmt", ["q4_0", "q8_0"])
+@pytest.mark.parametrize("M", [1, 8])
+def test_chain_many_gemvs_in_segments(fmt, M):
+    """150 small GEMVs with waits at 40, 41 and 130 (segments of 40, 1, 89 and 20 GEMVs); a
+    waiting GEMV reads the output of the one before it.  A workgroup's share touches few of
+    a segment's GEMVs (many touch none of the last), so the GEMVs it enters are linked
+    across the 64-GEMV words of its table; every output meets the bar, and a replay gives
+    the same bits."""
+    waits = {40, 41, 130}
+    Ns, Ks = [1, 7, 64, 300, 33], [256, 512, 1024]
+    shapes = []
+    for i in range(150):
+        N, K = Ns[(3 * i) % 5], Ks[i % 3]
+        if i + 1 in waits:
+            N = Ks[(i + 1) % 3]  # the next GEMV reads this output
+        shapes.append((N, K))
+    say("chain many GEMVs", fmt, M)
+    Ws, Wps, xs, ys, descs = [], [], [], [], []  # the descriptors hold raw pointers: keep all alive
+    for i, (N, K) in enumerate(shapes):
+        Wi = weights(fmt, N, K, ("chain-many", fmt, i))
+        Wp = packed(fmt, Wi, N, K)
+        x = ys[i - 1] if i in waits else gen.normal((M, K), ("chain-many-x", fmt, M, i), device=DEV)
+        y = torch.full((M, N), float("nan"), device=DEV)
+        Ws.append(Wi); Wps.append(Wp); xs.append(x); ys.append(y)
+        descs.append(bqm.gemv(fmt, Wp, x, y, N, K, wait=i in waits, M=M))
+    ws = torch.zeros(bqm.chain_workspace_bytes(len(descs)), dtype=torch.uint8, device=DEV)
+    bqm.bqm_chain_prepare(descs, ws)
+    outs = []
+    for _ in range(2):
+        bqm.qmv_chain(fmt, M, ws, len(descs))
+        assert bqm.bqm_chain_status(ws) == 0
+        outs.append([host(y).copy() for y in ys])
+    check_stages(fmt, shapes, Ws, xs, ys, M=M)
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a, b)
 
 
 def test_chain_segments_with_mixed_waits():

@@ -600,9 +600,15 @@ __global__ __launch_bounds__(64 << LGW) void k_qmv_chain(ChainArgs a) {
       const GemvDesc d = a.descs ? a.descs[i] : a.one;
       table[i] = a.seg ? make_stage<FMT>(d, a.seg[2 * i], a.seg[2 * i + 1], kc)
                        : make_stage<FMT>(d, 0, d.N * (d.K >> 5), kc);
+      if (a.n == 1) {  // one GEMV (a single call): entered if it has rows here
+        table[0].next = 1;
+        ufirst[0] = table[0].nrows > 0 ? 0 : 1;
+      }
     }
-    __syncthreads();
-    link_units(table, a.n, a.sync != nullptr, umask, ufirst);
+    if (a.n > 1) {
+      __syncthreads();
+      link_units(table, a.n, a.sync != nullptr, umask, ufirst);
+    }
   }
   if (tid < NW) done[tid] = 0;
   if (tid == 0 && a.sync) lds_epoch = ld_agent(a.sync);  // stable until all have arrived once
@@ -1134,9 +1140,15 @@ __global__ __launch_bounds__(1024) void k_qmv_chain_mc(ChainArgs a) {
     const GemvDesc d = a.descs ? a.descs[i] : a.one;
     table[i] = a.seg ? make_stage<FMT>(d, a.seg[2 * i], a.seg[2 * i + 1], kc)
                      : make_stage<FMT>(d, 0, d.N * (d.K >> 5), kc);
+    if (a.n == 1) {  // one GEMV (a single call): entered if it has rows here
+      table[0].next = 1;
+      ufirst[0] = table[0].nrows > 0 ? 0 : 1;
+    }
   }
-  __syncthreads();
-  link_units(table, a.n, a.sync != nullptr, umask, ufirst);
+  if (a.n > 1) {
+    __syncthreads();
+    link_units(table, a.n, a.sync != nullptr, umask, ufirst);
+  }
   if (tid < NW) done[tid] = 0;
   if (tid == 0 && a.sync) lds_epoch = ld_agent(a.sync);
   if (tid == 0) lds_ok = true;

@@ -87,17 +87,19 @@ def test_chain_batched_ragged_one_segment(M):
 def test_chain_many_gemvs_in_segments(fmt, M):
     """150 small GEMVs with waits at 40, 41 and 130 (segments of 40, 1, 89 and 20 GEMVs); a
     waiting GEMV reads the output of the one before it.  A workgroup's share touches few of
-    a segment's GEMVs (many touch none of the last), so the GEMVs it enters are linked
-    across the 64-GEMV words of its table; every output meets the bar, and a replay gives
-    the same bits."""
+    a segment's GEMVs, and most workgroups hold no row of the last segment (they enter only
+    its wait), so the GEMVs each enters are linked across the 64-GEMV words of its table;
+    every output meets the bar, and a replay gives the same bits."""
     waits = {40, 41, 130}
     Ns, Ks = [1, 7, 64, 300, 33], [256, 512, 1024]
+    # the last segment: 20 GEMVs of 1-7 rows of 256 weights (about 2.5 blocks per workgroup)
+    Kof = [Ks[i % 3] if i < 130 else 256 for i in range(150)]
     shapes = []
     for i in range(150):
-        N, K = Ns[(3 * i) % 5], Ks[i % 3]
+        N = Ns[(3 * i) % 5] if i < 130 else [1, 7, 3][i % 3]
         if i + 1 in waits:
-            N = Ks[(i + 1) % 3]  # the next GEMV reads this output
-        shapes.append((N, K))
+            N = Kof[i + 1]  # the next GEMV reads this output
+        shapes.append((N, Kof[i]))
     say("chain many GEMVs", fmt, M)
     Ws, Wps, xs, ys, descs = [], [], [], [], []  # the descriptors hold raw pointers: keep all alive
     for i, (N, K) in enumerate(shapes):
